@@ -1,0 +1,643 @@
+/*
+ * kvc_oracle.c -- plain, slow CPU oracle for segment-wise two-dimensional
+ * KV-cache compression and for decode attention over the compressed cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package's smoke check
+ * and the benchmark's CPU-baseline leg may load this library.  It shares no
+ * code, header, table or constant with the HIP library; the two are compared
+ * byte for byte (selection, indices, packed layout) and within a tolerance
+ * (attention output).
+ *
+ * Sources (pages, with the passage each step follows):
+ *  [M] "MosaicKV: Serving Long-Context LLM with Dynamic Two-D KV Cache
+ *      Compression" (arXiv 2607.00760), review page: abstract (per-vector
+ *      important elements, strategies chosen per KV segment); Fig. 5 caption
+ *      (segments, strategy generation); Fig. 6 caption, Stage-1 (top-r
+ *      elements of each KV vector), packed KV format, PackedAttention.
+ *  [K] "KARA: Efficient Reasoning LLM Serving via Sliding-Window KV Cache
+ *      Compression" (arXiv 2607.01237), review page: "What carries the
+ *      argument" (keys of a recent window scored by attention accumulated
+ *      from all window queries; Token2Chunk), referee summary (Eqs. 4-5
+ *      bidirectional scoring, Eqs. 6-8 Token2Chunk), free-parameter ledger
+ *      (retention r, window |W|, budget alpha, max length gamma), Fig. 3
+ *      caption (bidirectional weights over all query/key pairs).
+ *
+ * The pages print no equations, so every numerical step below is the reading
+ * stated beside it.  Selection-path arithmetic is IEEE fp32, round to nearest
+ * even, no contraction except explicit fmaf, in exactly the order written;
+ * attention is fp64.
+ *
+ * Parity pins (tests/test_oracle_pins.py) tie each function to closed forms,
+ * brute force or textbook routines.  Token2Chunk's exact rule is not printed
+ * on the pages: its properties are pinned, its parity with the paper is
+ * unpinned.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+#include <omp.h>
+
+#define ORC_D 128           /* head dimension handled by the oracle */
+#define ORC_BLK 64          /* tokens per normalisation partial block */
+
+/* ------------------------------------------------------------------ */
+/* fp32 helpers                                                         */
+/* ------------------------------------------------------------------ */
+static float bf2f(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* log2(e) rounded to fp32, and the Taylor coefficients ln2^k / k!, k=0..7,
+ * each rounded to fp32 (computed here in long double; a pin checks them
+ * against the exactly rounded rationals). */
+static float LOG2E_F;
+static float EXPC[8];
+static int g_init = 0;
+static void orc_init(void) {
+  if (g_init) return;
+  const long double ln2 = 0.693147180559945309417232121458176568L;
+  long double c = 1.0L;
+  for (int k = 0; k < 8; ++k) {
+    EXPC[k] = (float)c;
+    c = c * ln2 / (long double)(k + 1);
+  }
+  LOG2E_F = (float)1.442695040888963407359924681001892137L;
+  g_init = 1;
+}
+
+/* 2^y for y <= 0 by the Taylor series of e^(f ln2) (degree 7, Horner with
+ * fmaf) after splitting y = n + f with n = rint(y), |f| <= 1/2; returns +0
+ * below -125 so that no result is subnormal. */
+static float orc_exp2(float y) {
+  if (!(y >= -125.0f)) return 0.0f;
+  float n = rintf(y);
+  float f = y - n;
+  float p = EXPC[7];
+  for (int k = 6; k >= 0; --k) p = fmaf(p, f, EXPC[k]);
+  return ldexpf(p, (int)n);
+}
+
+/* Pairwise sum over n entries, n a power of two: tree(a) = tree(first half)
+ * + tree(second half). */
+static float tree_pow2(const float* a, int n) {
+  if (n == 1) return a[0];
+  return tree_pow2(a, n / 2) + tree_pow2(a + n / 2, n / 2);
+}
+static int next_pow2(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+/* Pairwise sum of n entries zero-padded to the next power of two. */
+static float tree_any(const float* a, int n) {
+  int np = next_pow2(n < 1 ? 1 : n);
+  float* buf = (float*)calloc((size_t)np, sizeof(float));
+  memcpy(buf, a, (size_t)n * sizeof(float));
+  float r = tree_pow2(buf, np);
+  free(buf);
+  return r;
+}
+
+/* q . k as one fmaf chain over the channels in ascending order. */
+static float dot_chain(const float* q, const uint16_t* k) {
+  float acc = 0.0f;
+  for (int ch = 0; ch < ORC_D; ++ch) acc = fmaf(q[ch], bf2f(k[ch]), acc);
+  return acc;
+}
+
+/* ------------------------------------------------------------------ */
+/* Public: element-wise exp2 and coefficient access (pins)             */
+/* ------------------------------------------------------------------ */
+void orc_exp2_f32(const float* y, float* out, long n) {
+  orc_init();
+  for (long i = 0; i < n; ++i) out[i] = orc_exp2(y[i]);
+}
+void orc_exp2_coeffs(float* c8, float* log2e) {
+  orc_init();
+  for (int k = 0; k < 8; ++k) c8[k] = EXPC[k];
+  *log2e = LOG2E_F;
+}
+
+/* ------------------------------------------------------------------ */
+/* Window scoring: accumulated attention of a window of queries        */
+/*  [K] "What carries the argument": keys are scored by the attention   */
+/*  all window queries give them; [K] Fig. 3: every query/key pair (no  */
+/*  causal mask).  Reading: softmax of each query over the whole domain */
+/*  of n_ctx keys, normalised globally; a token's score is the sum over */
+/*  the G q-heads of its group and the W window queries.               */
+/* ------------------------------------------------------------------ */
+/* Qw: [nq][128] bf16, query index qi = g*W + w.  K: [n_ctx][128].
+ * Outputs m[nq], invZ[nq] (global max and 1/Z of each query). */
+void orc_normalisers(int n_ctx, int nq, const uint16_t* K, const uint16_t* Qw,
+                     float scale, float* m_out, float* invZ_out, int n_threads) {
+  orc_init();
+  const int nblk = n_ctx / ORC_BLK;
+#pragma omp parallel for schedule(dynamic) num_threads(n_threads)
+  for (int qi = 0; qi < nq; ++qi) {
+    float q[ORC_D];
+    for (int ch = 0; ch < ORC_D; ++ch) q[ch] = bf2f(Qw[(size_t)qi * ORC_D + ch]);
+    float* mb = (float*)malloc(sizeof(float) * (size_t)nblk);
+    float* zb = (float*)malloc(sizeof(float) * (size_t)nblk);
+    float l[ORC_BLK], e[ORC_BLK];
+    for (int b = 0; b < nblk; ++b) {
+      /* partial of one 64-token block: its max and the pairwise sum of
+       * exp(l - max) */
+      float mx = -INFINITY;
+      for (int i = 0; i < ORC_BLK; ++i) {
+        const uint16_t* k = K + ((size_t)b * ORC_BLK + i) * ORC_D;
+        l[i] = dot_chain(q, k) * scale;
+        if (l[i] > mx) mx = l[i];
+      }
+      for (int i = 0; i < ORC_BLK; ++i) e[i] = orc_exp2((l[i] - mx) * LOG2E_F);
+      mb[b] = mx;
+      zb[b] = tree_pow2(e, ORC_BLK);
+    }
+    float m = -INFINITY;
+    for (int b = 0; b < nblk; ++b)
+      if (mb[b] > m) m = mb[b];
+    float* t = (float*)malloc(sizeof(float) * (size_t)nblk);
+    for (int b = 0; b < nblk; ++b) t[b] = zb[b] * orc_exp2((mb[b] - m) * LOG2E_F);
+    float Z = tree_any(t, nblk);
+    m_out[qi] = m;
+    invZ_out[qi] = 1.0f / Z;
+    free(t);
+    free(mb);
+    free(zb);
+  }
+}
+
+/* Scores of tokens [t0, t0+nt) of the domain: s = sum over qi ascending of
+ * exp(l - m_qi) * invZ_qi, accumulated one term at a time. */
+void orc_token_scores(int t0, int nt, int nq, const uint16_t* K, const uint16_t* Qw,
+                      float scale, const float* m, const float* invZ, float* s_out,
+                      int n_threads) {
+  orc_init();
+  float* qf = (float*)malloc(sizeof(float) * (size_t)nq * ORC_D);
+  for (size_t i = 0; i < (size_t)nq * ORC_D; ++i) qf[i] = bf2f(Qw[i]);
+#pragma omp parallel for schedule(static) num_threads(n_threads)
+  for (int i = 0; i < nt; ++i) {
+    const uint16_t* k = K + (size_t)(t0 + i) * ORC_D;
+    float s = 0.0f;
+    for (int qi = 0; qi < nq; ++qi) {
+      float l = dot_chain(qf + (size_t)qi * ORC_D, k) * scale;
+      float e = orc_exp2((l - m[qi]) * LOG2E_F);
+      s = s + e * invZ[qi];
+    }
+    s_out[i] = s;
+  }
+  free(qf);
+}
+
+/* ------------------------------------------------------------------ */
+/* Stage-1 per-vector channel selection ([M] Fig. 6 caption: the top-r  */
+/* important elements of each K or V vector).  Reading: importance is  */
+/* the magnitude of the stored bf16 value; order by magnitude (desc),   */
+/* ties by lower channel; keep the first c.                             */
+/* ------------------------------------------------------------------ */
+typedef struct {
+  uint16_t key;
+  uint16_t ch;
+} chkey;
+static int cmp_chkey(const void* a, const void* b) {
+  const chkey* x = (const chkey*)a;
+  const chkey* y = (const chkey*)b;
+  if (x->key != y->key) return x->key > y->key ? -1 : 1;
+  return (int)x->ch - (int)y->ch;
+}
+/* mask: 16 bytes, channel ch -> byte ch/8, bit ch%8.  rho = share of the
+ * vector's energy kept: pairwise sum of kept x^2 over pairwise sum of all
+ * x^2 (1 when the vector is zero). */
+void orc_channel_topc(const uint16_t* row, int c, uint8_t* mask, float* rho) {
+  chkey ks[ORC_D];
+  for (int ch = 0; ch < ORC_D; ++ch) {
+    ks[ch].key = row[ch] & 0x7FFF;
+    ks[ch].ch = (uint16_t)ch;
+  }
+  qsort(ks, ORC_D, sizeof(chkey), cmp_chkey);
+  memset(mask, 0, 16);
+  for (int i = 0; i < c && i < ORC_D; ++i) mask[ks[i].ch >> 3] |= (uint8_t)(1u << (ks[i].ch & 7));
+  float kept[ORC_D], all[ORC_D];
+  for (int ch = 0; ch < ORC_D; ++ch) {
+    float x = bf2f(row[ch]);
+    all[ch] = x * x;
+    kept[ch] = ((mask[ch >> 3] >> (ch & 7)) & 1) ? all[ch] : 0.0f;
+  }
+  float Ec = tree_pow2(kept, ORC_D);
+  float Ea = tree_pow2(all, ORC_D);
+  *rho = (Ea == 0.0f) ? 1.0f : Ec / Ea;
+}
+
+/* ------------------------------------------------------------------ */
+/* Token selection inside a segment                                     */
+/* ------------------------------------------------------------------ */
+typedef struct {
+  float s;
+  int idx;
+} tokkey;
+static int cmp_tokkey(const void* a, const void* b) {
+  const tokkey* x = (const tokkey*)a;
+  const tokkey* y = (const tokkey*)b;
+  if (x->s != y->s) return x->s > y->s ? -1 : 1;
+  return x->idx - y->idx;
+}
+/* Order of the segment's tokens by (score desc, index asc). */
+static void token_order(const float* s, int S, int* order) {
+  tokkey* t = (tokkey*)malloc(sizeof(tokkey) * (size_t)S);
+  for (int i = 0; i < S; ++i) {
+    t[i].s = s[i];
+    t[i].idx = i;
+  }
+  qsort(t, (size_t)S, sizeof(tokkey), cmp_tokkey);
+  for (int i = 0; i < S; ++i) order[i] = t[i].idx;
+  free(t);
+}
+/* keep[i] = 1 for the T best tokens. */
+void orc_top_t(const float* s, int S, int T, uint8_t* keep) {
+  int* order = (int*)malloc(sizeof(int) * (size_t)S);
+  token_order(s, S, order);
+  memset(keep, 0, (size_t)S);
+  for (int i = 0; i < T && i < S; ++i) keep[order[i]] = 1;
+  free(order);
+}
+
+/* Token2Chunk ([K] "What carries the argument": consecutive high-score
+ * tokens are endpoints of candidate chunks, the best kept under a length
+ * cap and a budget; ledger: budget alpha, max chunk length gamma).
+ * Reading: alpha tokens of the retention T are reserved for chunk interiors.
+ *  1. A = the T - alpha best tokens, in ascending position a_1 < ... < a_m.
+ *  2. Each neighbouring pair (a_k, a_k+1) with a gap (>= 1 token between)
+ *     and span a_k+1 - a_k + 1 <= gamma is a candidate, valued
+ *     s[a_k] + s[a_k+1] (fp32).
+ *  3. Candidates are visited by (value desc, gap asc, k asc); one is accepted
+ *     when its gap still fits the remaining budget (first fit), adding its
+ *     interior tokens.
+ *  4. Unused budget is filled with the best tokens not yet kept, so exactly
+ *     T tokens are kept. */
+void orc_token2chunk(const float* s, int S, int T, int alpha, int gamma, uint8_t* keep) {
+  int* order = (int*)malloc(sizeof(int) * (size_t)S);
+  token_order(s, S, order);
+  memset(keep, 0, (size_t)S);
+  int m = T - alpha;
+  for (int i = 0; i < m; ++i) keep[order[i]] = 1;
+  int* a = (int*)malloc(sizeof(int) * (size_t)(m > 0 ? m : 1));
+  int na = 0;
+  for (int i = 0; i < S; ++i)
+    if (keep[i]) a[na++] = i;
+  /* candidates */
+  int nc = 0;
+  int* ck = (int*)malloc(sizeof(int) * (size_t)(na > 0 ? na : 1));
+  uint8_t* done = (uint8_t*)calloc((size_t)(na > 0 ? na : 1), 1);
+  for (int k = 0; k + 1 < na; ++k) {
+    int gap = a[k + 1] - a[k] - 1;
+    int span = a[k + 1] - a[k] + 1;
+    if (gap >= 1 && span <= gamma) ck[nc++] = k;
+  }
+  int used = 0;
+  for (int it = 0; it < nc; ++it) {
+    /* best remaining candidate by (value desc, gap asc, k asc) */
+    int best = -1;
+    float bv = 0.0f;
+    int bg = 0;
+    for (int j = 0; j < nc; ++j) {
+      if (done[j]) continue;
+      int k = ck[j];
+      float v = s[a[k]] + s[a[k + 1]];
+      int g = a[k + 1] - a[k] - 1;
+      if (best < 0 || v > bv || (v == bv && (g < bg || (g == bg && k < ck[best])))) {
+        best = j;
+        bv = v;
+        bg = g;
+      }
+    }
+    done[best] = 1;
+    if (used + bg <= alpha) {
+      int k = ck[best];
+      for (int t = a[k] + 1; t < a[k + 1]; ++t) keep[t] = 1;
+      used += bg;
+    }
+  }
+  /* fill to exactly T */
+  int have = 0;
+  for (int i = 0; i < S; ++i) have += keep[i];
+  for (int i = 0; i < S && have < T; ++i) {
+    if (!keep[order[i]]) {
+      keep[order[i]] = 1;
+      ++have;
+    }
+  }
+  free(done);
+  free(ck);
+  free(a);
+  free(order);
+}
+
+/* ------------------------------------------------------------------ */
+/* Packed segment layout ([M] Fig. 6 caption: packed KV format; the     */
+/* spec layout is bf16 values + per-vector channel bitmask +      */
+/* token index list).  Parts, each starting 16-byte aligned:            */
+/*   K masks [T] x 16 B (only if c < 128), K values [T][c] bf16,        */
+/*   V masks (only if c < 128), V values, token indices [T] u16 (only   */
+/*   if T < S) zero-padded to 16 B.                                     */
+/* ------------------------------------------------------------------ */
+long orc_seg_bytes(int T, int c, int S) {
+  if (T <= 0) return 0;
+  long mk = (c < ORC_D) ? 16L * T : 0;
+  long vals = 2L * T * c;
+  long idx = (T < S) ? ((2L * T + 15) / 16) * 16 : 0;
+  return 2 * mk + 2 * vals + idx;
+}
+
+/* Descriptor, 16 bytes, same field order as the library's. */
+typedef struct {
+  uint64_t offset;
+  uint16_t n_tok;
+  uint16_t n_ch;
+  uint8_t strategy;
+  uint8_t flags;
+  uint16_t seg_tokens;
+} orc_desc;
+
+typedef struct {
+  int n_ctx;        /* tokens in the scoring domain */
+  int region_begin; /* first token compressed */
+  int region_len;   /* tokens compressed, a multiple of S */
+  int S;            /* segment tokens */
+  int G;            /* q heads per kv head */
+  int W;            /* window queries per q head */
+  int n_strat;
+  const int* strat_T;
+  const int* strat_c;
+  long budget_bytes; /* per segment */
+  int t2c_alpha;     /* 0: Token2Chunk off */
+  int t2c_gamma;
+  float scale;
+} orc_params;
+
+/* Compress one stream (one batch entry, one kv head).
+ * K, V: [n_ctx][128] bf16; Qw: [G][W][128] bf16; forced: [nseg] or NULL
+ * (value < n_strat forces a feasible strategy).  packed receives the stream's
+ * segments back to back from byte 0; desc offsets are base_offset + local.
+ * Optional outputs: scores [region_len], objective [nseg][n_strat],
+ * m/invZ [G*W].  Returns 0, or -3 when no strategy fits the budget. */
+int orc_compress_stream(const orc_params* p, const uint16_t* K, const uint16_t* V,
+                        const uint16_t* Qw, const uint8_t* forced, uint8_t* packed,
+                        uint64_t base_offset, orc_desc* desc, uint64_t* used_bytes,
+                        float* scores_out, float* objective_out, float* m_out,
+                        float* invZ_out, int n_threads) {
+  orc_init();
+  const int S = p->S, nseg = p->region_len / p->S, nq = p->G * p->W, ns = p->n_strat;
+  long* bytes = (long*)malloc(sizeof(long) * (size_t)ns);
+  int any_feasible = 0;
+  for (int i = 0; i < ns; ++i) {
+    bytes[i] = orc_seg_bytes(p->strat_T[i], p->strat_c[i], S);
+    if (bytes[i] <= p->budget_bytes) any_feasible = 1;
+  }
+  if (!any_feasible) {
+    free(bytes);
+    return -3;
+  }
+  /* 1. token scores over the region */
+  float* m = (float*)malloc(sizeof(float) * (size_t)nq);
+  float* invZ = (float*)malloc(sizeof(float) * (size_t)nq);
+  float* s = (float*)malloc(sizeof(float) * (size_t)p->region_len);
+  orc_normalisers(p->n_ctx, nq, K, Qw, p->scale, m, invZ, n_threads);
+  orc_token_scores(p->region_begin, p->region_len, nq, K, Qw, p->scale, m, invZ, s, n_threads);
+  if (scores_out) memcpy(scores_out, s, sizeof(float) * (size_t)p->region_len);
+  if (m_out) memcpy(m_out, m, sizeof(float) * (size_t)nq);
+  if (invZ_out) memcpy(invZ_out, invZ, sizeof(float) * (size_t)nq);
+
+  /* 2. per segment: selection, objective, choice */
+  int* chosen = (int*)malloc(sizeof(int) * (size_t)nseg);
+  uint8_t* flags = (uint8_t*)calloc((size_t)nseg, 1);
+#pragma omp parallel for schedule(dynamic) num_threads(n_threads)
+  for (int sg = 0; sg < nseg; ++sg) {
+    const int t0 = p->region_begin + sg * S;
+    const float* ss = s + (size_t)sg * S;
+    float J[64];
+    uint8_t* keep = (uint8_t*)malloc((size_t)S);
+    float* terms = (float*)malloc(sizeof(float) * (size_t)S);
+    /* energy shares of every K and V vector of the segment, per channel
+     * count c < 128 that the strategy table uses (c = 128 keeps all: 1) */
+    int cs[64], ncs = 0;
+    for (int i = 0; i < ns; ++i) {
+      int c = p->strat_c[i], seen = 0;
+      if (p->strat_T[i] == 0 || c >= ORC_D) continue;
+      for (int u = 0; u < ncs; ++u) seen |= (cs[u] == c);
+      if (!seen) cs[ncs++] = c;
+    }
+    float* rhoK = (float*)malloc(sizeof(float) * (size_t)S * (size_t)(ncs > 0 ? ncs : 1));
+    float* rhoV = (float*)malloc(sizeof(float) * (size_t)S * (size_t)(ncs > 0 ? ncs : 1));
+    for (int t = 0; t < S; ++t) {
+      for (int u = 0; u < ncs; ++u) {
+        uint8_t mk[16];
+        orc_channel_topc(K + (size_t)(t0 + t) * ORC_D, cs[u], mk, &rhoK[t * ncs + u]);
+        orc_channel_topc(V + (size_t)(t0 + t) * ORC_D, cs[u], mk, &rhoV[t * ncs + u]);
+      }
+    }
+    for (int i = 0; i < ns; ++i) {
+      const int T = p->strat_T[i], c = p->strat_c[i];
+      if (T == 0) {
+        J[i] = 0.0f;
+        continue;
+      }
+      if (T >= S)
+        memset(keep, 1, (size_t)S);
+      else if (p->t2c_alpha > 0)
+        orc_token2chunk(ss, S, T, p->t2c_alpha, p->t2c_gamma, keep);
+      else
+        orc_top_t(ss, S, T, keep);
+      int u = 0;
+      while (u < ncs && cs[u] != c) ++u;
+      /* objective: attention mass kept, weighted by the mean share of the
+       * K and V vector energy kept at c channels */
+      for (int t = 0; t < S; ++t) {
+        if (!keep[t]) {
+          terms[t] = 0.0f;
+          continue;
+        }
+        float rk = 1.0f, rv = 1.0f;
+        if (c < ORC_D) {
+          rk = rhoK[t * ncs + u];
+          rv = rhoV[t * ncs + u];
+        }
+        terms[t] = ss[t] * (0.5f * (rk + rv));
+      }
+      J[i] = tree_pow2(terms, S);
+    }
+    free(rhoK);
+    free(rhoV);
+    int best = -1;
+    if (forced && forced[sg] < ns && bytes[forced[sg]] <= p->budget_bytes) {
+      best = forced[sg];
+    } else {
+      if (forced && forced[sg] != 0xFF) flags[sg] |= 0x80;
+      for (int i = 0; i < ns; ++i) {
+        if (bytes[i] > p->budget_bytes) continue;
+        if (best < 0 || J[i] > J[best]) best = i;
+      }
+    }
+    chosen[sg] = best;
+    if (objective_out)
+      for (int i = 0; i < ns; ++i) objective_out[(size_t)sg * ns + i] = J[i];
+    free(keep);
+    free(terms);
+  }
+
+  /* 3. offsets (exclusive scan) and 4. pack */
+  uint64_t off = 0;
+  for (int sg = 0; sg < nseg; ++sg) {
+    const int i = chosen[sg], T = p->strat_T[i], c = p->strat_c[i];
+    const int t0 = p->region_begin + sg * S;
+    const long nb = bytes[i];
+    orc_desc d;
+    memset(&d, 0, sizeof d);
+    d.offset = base_offset + off;
+    d.n_tok = (uint16_t)T;
+    d.n_ch = (uint16_t)(T > 0 ? c : 0);
+    d.strategy = (uint8_t)i;
+    d.flags = (uint8_t)(flags[sg] | (T >= S ? 1 : 0) | (c >= ORC_D ? 2 : 0));
+    d.seg_tokens = (uint16_t)S;
+    desc[sg] = d;
+    uint8_t* out = packed + off;
+    memset(out, 0, (size_t)nb);
+    if (T > 0) {
+      uint8_t* keep = (uint8_t*)malloc((size_t)S);
+      if (T >= S)
+        memset(keep, 1, (size_t)S);
+      else if (p->t2c_alpha > 0)
+        orc_token2chunk(s + (size_t)sg * S, S, T, p->t2c_alpha, p->t2c_gamma, keep);
+      else
+        orc_top_t(s + (size_t)sg * S, S, T, keep);
+      size_t pos = 0;
+      for (int part = 0; part < 2; ++part) { /* 0: K, 1: V */
+        const uint16_t* X = part == 0 ? K : V;
+        if (c < ORC_D) {
+          for (int t = 0; t < S; ++t) {
+            if (!keep[t]) continue;
+            float r;
+            orc_channel_topc(X + (size_t)(t0 + t) * ORC_D, c, out + pos, &r);
+            pos += 16;
+          }
+        }
+        for (int t = 0; t < S; ++t) {
+          if (!keep[t]) continue;
+          const uint16_t* row = X + (size_t)(t0 + t) * ORC_D;
+          uint8_t mk[16];
+          float r;
+          if (c < ORC_D)
+            orc_channel_topc(row, c, mk, &r);
+          else
+            memset(mk, 0xFF, 16);
+          for (int ch = 0; ch < ORC_D; ++ch) {
+            if ((mk[ch >> 3] >> (ch & 7)) & 1) {
+              memcpy(out + pos, &row[ch], 2);
+              pos += 2;
+            }
+          }
+        }
+      }
+      if (T < S) {
+        for (int t = 0; t < S; ++t) {
+          if (!keep[t]) continue;
+          uint16_t u = (uint16_t)t;
+          memcpy(out + pos, &u, 2);
+          pos += 2;
+        }
+      }
+      free(keep);
+    }
+    off += (uint64_t)nb;
+  }
+  *used_bytes = off;
+  free(chosen);
+  free(flags);
+  free(m);
+  free(invZ);
+  free(s);
+  free(bytes);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Decode attention over a compressed stream ([M] Fig. 6/7 captions:    */
+/* PackedAttention computes attention over the packed KV).  Exact       */
+/* (fp64) softmax attention over every kept token; a dropped channel    */
+/* contributes 0 to q.k and to the output.                              */
+/* q: [G][128] bf16.  desc: n_desc descriptors whose offsets index      */
+/* packed.  out: [G][128] fp64, lse: [G] (log of the softmax            */
+/* denominator incl. the max; -inf and out = 0 if no token is kept).     */
+/* ------------------------------------------------------------------ */
+void orc_decode_stream(int G, const uint16_t* q, const uint8_t* packed, const orc_desc* desc,
+                       int n_desc, float scale, double* out, double* lse) {
+  long ntok = 0;
+  for (int i = 0; i < n_desc; ++i) ntok += desc[i].n_tok;
+  double* l = (double*)malloc(sizeof(double) * (size_t)(ntok > 0 ? ntok : 1) * (size_t)G);
+  /* pass 1: logits */
+  long j = 0;
+  for (int i = 0; i < n_desc; ++i) {
+    const int T = desc[i].n_tok, c = desc[i].n_ch;
+    const uint8_t* base = packed + desc[i].offset;
+    const uint8_t* kmask = base;
+    const uint8_t* kval = base + (c < ORC_D ? 16 * T : 0);
+    for (int t = 0; t < T; ++t, ++j) {
+      const uint8_t* mk = c < ORC_D ? kmask + 16 * t : NULL;
+      const uint8_t* vals = kval + (size_t)2 * c * t;
+      for (int g = 0; g < G; ++g) {
+        double acc = 0.0;
+        int r = 0;
+        for (int ch = 0; ch < ORC_D; ++ch) {
+          int on = mk ? ((mk[ch >> 3] >> (ch & 7)) & 1) : 1;
+          if (!on) continue;
+          uint16_t kv;
+          memcpy(&kv, vals + 2 * r, 2);
+          ++r;
+          acc += (double)bf2f(q[g * ORC_D + ch]) * (double)bf2f(kv);
+        }
+        l[j * G + g] = acc * (double)scale;
+      }
+    }
+  }
+  for (int g = 0; g < G; ++g) {
+    for (int ch = 0; ch < ORC_D; ++ch) out[g * ORC_D + ch] = 0.0;
+    if (ntok == 0) {
+      lse[g] = -INFINITY;
+      continue;
+    }
+    double mx = -INFINITY;
+    for (long t = 0; t < ntok; ++t)
+      if (l[t * G + g] > mx) mx = l[t * G + g];
+    double den = 0.0;
+    for (long t = 0; t < ntok; ++t) den += exp(l[t * G + g] - mx);
+    lse[g] = mx + log(den);
+    /* pass 2: weighted sum of the kept V elements */
+    long jj = 0;
+    for (int i = 0; i < n_desc; ++i) {
+      const int T = desc[i].n_tok, c = desc[i].n_ch;
+      const uint8_t* base = packed + desc[i].offset;
+      const size_t kpart = (size_t)(c < ORC_D ? 16 * T : 0) + (size_t)2 * T * c;
+      const uint8_t* vmask = base + kpart;
+      const uint8_t* vval = vmask + (c < ORC_D ? 16 * T : 0);
+      for (int t = 0; t < T; ++t, ++jj) {
+        const double pr = exp(l[jj * G + g] - mx) / den;
+        const uint8_t* mk = c < ORC_D ? vmask + 16 * t : NULL;
+        const uint8_t* vals = vval + (size_t)2 * c * t;
+        int r = 0;
+        for (int ch = 0; ch < ORC_D; ++ch) {
+          int on = mk ? ((mk[ch >> 3] >> (ch & 7)) & 1) : 1;
+          if (!on) continue;
+          uint16_t vv;
+          memcpy(&vv, vals + 2 * r, 2);
+          ++r;
+          out[g * ORC_D + ch] += pr * (double)bf2f(vv);
+        }
+      }
+    }
+  }
+  free(l);
+}
+
+int orc_max_threads(void) { return omp_get_max_threads(); }

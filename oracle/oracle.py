@@ -1,0 +1,191 @@
+"""ctypes wrapper of the CPU oracle ``liboracle.so`` (test infrastructure).
+
+Only the tests, the package's smoke check and the benchmark's CPU-baseline leg
+may import this module.  It never touches the GPU library.  Every function
+returns numpy arrays; bf16 data travels as uint16 bit patterns.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvc_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+DESC_DTYPE = np.dtype([("offset", "<u8"), ("n_tok", "<u2"), ("n_ch", "<u2"),
+                       ("strategy", "u1"), ("flags", "u1"), ("seg_tokens", "<u2")])
+assert DESC_DTYPE.itemsize == 16
+
+BUILD_CMD = ["gcc", "-O2", "-mfma", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+             "-fPIC", "-shared", "-std=c11", "-Wall", "-o", _LIB, _SRC, "-lm"]
+
+
+def build():
+    """Compile liboracle.so in place (plain gcc; no GPU code)."""
+    subprocess.check_call(BUILD_CMD)
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f32 = ctypes.c_int, ctypes.c_long, ctypes.c_float
+        L.orc_exp2_f32.argtypes = [P, P, i64]
+        L.orc_exp2_coeffs.argtypes = [P, P]
+        L.orc_normalisers.argtypes = [i32, i32, P, P, f32, P, P, i32]
+        L.orc_token_scores.argtypes = [i32, i32, i32, P, P, f32, P, P, P, i32]
+        L.orc_channel_topc.argtypes = [P, i32, P, P]
+        L.orc_top_t.argtypes = [P, i32, i32, P]
+        L.orc_token2chunk.argtypes = [P, i32, i32, i32, i32, P]
+        L.orc_seg_bytes.argtypes = [i32, i32, i32]
+        L.orc_seg_bytes.restype = i64
+        L.orc_compress_stream.argtypes = [P, P, P, P, P, P, ctypes.c_uint64, P, P, P, P, P, P, i32]
+        L.orc_compress_stream.restype = i32
+        L.orc_decode_stream.argtypes = [i32, P, P, P, i32, f32, P, P]
+        L.orc_max_threads.restype = i32
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, a.dtype
+    return a
+
+
+def max_threads():
+    return lib().orc_max_threads()
+
+
+def exp2(y):
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty_like(y)
+    lib().orc_exp2_f32(_p(y), _p(out), y.size)
+    return out
+
+
+def exp2_coeffs():
+    c = np.zeros(8, np.float32)
+    l2e = np.zeros(1, np.float32)
+    lib().orc_exp2_coeffs(_p(c), _p(l2e))
+    return c, l2e[0]
+
+
+def normalisers(K, Qw, scale, n_threads=0):
+    """K: [n_ctx,128] u16, Qw: [nq,128] u16 -> (m[nq], invZ[nq]) fp32."""
+    K, Qw = _u16(K), _u16(Qw)
+    nq = Qw.shape[0]
+    m = np.zeros(nq, np.float32)
+    iz = np.zeros(nq, np.float32)
+    lib().orc_normalisers(K.shape[0], nq, _p(K), _p(Qw), np.float32(scale), _p(m), _p(iz),
+                          n_threads or max_threads())
+    return m, iz
+
+
+def token_scores(K, Qw, scale, m, invZ, t0=0, nt=None, n_threads=0):
+    K, Qw = _u16(K), _u16(Qw)
+    nt = K.shape[0] - t0 if nt is None else nt
+    s = np.zeros(nt, np.float32)
+    m = np.ascontiguousarray(m, np.float32)
+    invZ = np.ascontiguousarray(invZ, np.float32)
+    lib().orc_token_scores(t0, nt, Qw.shape[0], _p(K), _p(Qw), np.float32(scale), _p(m),
+                           _p(invZ), _p(s), n_threads or max_threads())
+    return s
+
+
+def channel_topc(row, c):
+    """row: [128] u16 -> (mask bytes [16] u8, rho fp32)."""
+    row = _u16(row)
+    mask = np.zeros(16, np.uint8)
+    rho = np.zeros(1, np.float32)
+    lib().orc_channel_topc(_p(row), c, _p(mask), _p(rho))
+    return mask, rho[0]
+
+
+def top_t(s, T):
+    s = np.ascontiguousarray(s, np.float32)
+    keep = np.zeros(s.size, np.uint8)
+    lib().orc_top_t(_p(s), s.size, T, _p(keep))
+    return keep
+
+
+def token2chunk(s, T, alpha, gamma):
+    s = np.ascontiguousarray(s, np.float32)
+    keep = np.zeros(s.size, np.uint8)
+    lib().orc_token2chunk(_p(s), s.size, T, alpha, gamma, _p(keep))
+    return keep
+
+
+def seg_bytes(T, c, S):
+    return lib().orc_seg_bytes(T, c, S)
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("n_ctx", ctypes.c_int), ("region_begin", ctypes.c_int),
+                ("region_len", ctypes.c_int), ("S", ctypes.c_int), ("G", ctypes.c_int),
+                ("W", ctypes.c_int), ("n_strat", ctypes.c_int),
+                ("strat_T", ctypes.c_void_p), ("strat_c", ctypes.c_void_p),
+                ("budget_bytes", ctypes.c_long), ("t2c_alpha", ctypes.c_int),
+                ("t2c_gamma", ctypes.c_int), ("scale", ctypes.c_float)]
+
+
+def compress_stream(K, V, Qw, *, S, strategies, budget_bytes, scale, region_begin=0,
+                    region_len=None, t2c_alpha=0, t2c_gamma=0, forced=None, base_offset=0,
+                    n_threads=0):
+    """Compress one stream.
+
+    K, V: [n_ctx,128] u16; Qw: [G,W,128] u16; strategies: list of (T, c).
+    Returns dict(packed, desc, used, scores, objective, m, invZ).
+    """
+    K, V, Qw = _u16(K), _u16(V), _u16(Qw)
+    n_ctx = K.shape[0]
+    G, W = Qw.shape[0], Qw.shape[1]
+    region_len = n_ctx - region_begin if region_len is None else region_len
+    nseg = region_len // S
+    sT = np.array([t for t, _ in strategies], np.int32)
+    sc = np.array([c for _, c in strategies], np.int32)
+    prm = _Params(n_ctx, region_begin, region_len, S, G, W, len(strategies),
+                  sT.ctypes.data, sc.ctypes.data, int(budget_bytes), t2c_alpha, t2c_gamma,
+                  np.float32(scale))
+    cap = nseg * max(seg_bytes(t, c, S) for t, c in strategies) + 16
+    packed = np.zeros(cap, np.uint8)
+    desc = np.zeros(nseg, DESC_DTYPE)
+    used = np.zeros(1, np.uint64)
+    scores = np.zeros(region_len, np.float32)
+    obj = np.zeros((nseg, len(strategies)), np.float32)
+    m = np.zeros(G * W, np.float32)
+    iz = np.zeros(G * W, np.float32)
+    f = None if forced is None else np.ascontiguousarray(forced, np.uint8)
+    rc = lib().orc_compress_stream(ctypes.byref(prm), _p(K), _p(V), _p(Qw), _p(f), _p(packed),
+                                   base_offset, _p(desc), _p(used), _p(scores), _p(obj), _p(m),
+                                   _p(iz), n_threads or max_threads())
+    if rc != 0:
+        raise ValueError(f"oracle compress failed ({rc})")
+    return dict(packed=packed[: int(used[0])], desc=desc, used=int(used[0]), scores=scores,
+                objective=obj, m=m, invZ=iz)
+
+
+def decode_stream(q, packed, desc, scale):
+    """q: [G,128] u16; packed: u8 buffer the desc offsets index; -> (out fp64 [G,128], lse [G])."""
+    q = _u16(q)
+    packed = np.ascontiguousarray(packed, np.uint8)
+    desc = np.ascontiguousarray(desc, DESC_DTYPE)
+    G = q.shape[0]
+    out = np.zeros((G, 128), np.float64)
+    lse = np.zeros(G, np.float64)
+    buf = packed if packed.size else np.zeros(16, np.uint8)
+    lib().orc_decode_stream(G, _p(q), _p(buf), _p(desc), desc.size, np.float32(scale), _p(out),
+                            _p(lse))
+    return out, lse

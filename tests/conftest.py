@@ -1,0 +1,23 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+def pytest_report_header(config):
+    return "kvc tests: oracle = oracle/liboracle.so (CPU), library = libkvc.so (HIP)"
+
+
+@pytest.fixture(scope="session")
+def O():
+    from oracle import oracle as _O
+    _O.lib()
+    return _O

@@ -1,0 +1,473 @@
+"""Pins of the CPU oracle to facts outside itself (CPU only).
+
+Each test ties one oracle function to a closed form, a brute-force search, a
+textbook routine or a hand-worked example, chosen so that a plausible slip (a
+dropped term, a wrong sign or index, a transposed operand, per-segment instead
+of global normalisation) fails.  Passages cited are from the two review pages:
+MosaicKV (arXiv 2607.00760) and KARA (arXiv 2607.01237).
+"""
+import itertools
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_kv_cache_compress_amd import gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+SCALE = np.float32(1.0 / math.sqrt(128.0))
+
+
+def bf16_bits(x):
+    return gen.u16(torch.as_tensor(np.asarray(x, np.float32)).to(torch.bfloat16))
+
+
+def bits_to_f(u):
+    return (np.asarray(u, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def nearest_f32(fr):
+    """Exactly rounded fp32 of a Fraction (ties to even)."""
+    f = np.float32(float(fr))
+    best = None
+    for c in (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))):
+        d = abs(Fraction(float(c)) - fr)
+        if best is None or d < best[0] or (d == best[0] and (c.view(np.uint32) & 1) == 0):
+            best = (d, c)
+    return best[1]
+
+
+# --------------------------------------------------------------------- exp2
+def test_exp2_coefficients_are_exactly_rounded(O):
+    getcontext().prec = 60
+    ln2 = Fraction(Decimal(2).ln())
+    c, l2e = O.exp2_coeffs()
+    for k in range(8):
+        want = nearest_f32(ln2 ** k / math.factorial(k))
+        assert c[k] == want, (k, c[k], want)
+    assert l2e == nearest_f32(Fraction(Decimal(1).exp().ln() / Decimal(2).ln()))
+
+
+def test_exp2_within_two_ulp(O):
+    rng = np.random.default_rng(1)
+    y = np.concatenate([-rng.random(1_000_000, dtype=np.float32) * np.float32(125.0),
+                        np.array([0.0, -0.5, -1.0, -124.5, -125.0], np.float32)])
+    r = O.exp2(y).astype(np.float64)
+    exact = np.exp2(y.astype(np.float64))
+    ulp = np.spacing(exact.astype(np.float32)).astype(np.float64)
+    assert np.max(np.abs(r - exact) / ulp) <= 2.0
+
+
+def test_exp2_special_values(O):
+    ints = -np.arange(0, 126, dtype=np.float32)
+    assert np.array_equal(O.exp2(ints), np.ldexp(np.float32(1.0), ints.astype(np.int32)).astype(np.float32))
+    assert np.all(O.exp2(np.array([-125.01, -126, -1000, -np.inf], np.float32)) == 0.0)
+
+
+# ------------------------------------------------------------------ scoring
+def _stream(seed, N, G, W, uniform_k=False):
+    rng = np.random.default_rng(seed)
+    K = bf16_bits(np.zeros((N, 128)) if uniform_k else rng.standard_normal((N, 128)) * 1.5)
+    Qw = bf16_bits(rng.standard_normal((G * W, 128)))
+    return K, Qw
+
+
+def test_scores_uniform_keys_exact(O):
+    """K = 0: every logit is 0, every exp is 1, Z = N, so each token gets
+    exactly G*W/N (power-of-two N)."""
+    G, W, N = 2, 8, 512
+    K, Qw = _stream(3, N, G, W, uniform_k=True)
+    m, iz = O.normalisers(K, Qw, SCALE)
+    assert np.all(m == 0.0) and np.all(iz == np.float32(1.0 / N))
+    s = O.token_scores(K, Qw, SCALE, m, iz)
+    assert np.all(s == np.float32(G * W / N))
+
+
+def test_scores_sum_to_query_count(O):
+    """Each query's softmax sums to 1 over the domain, so the scores of all
+    tokens sum to G*W ([K] accumulated attention over the window)."""
+    G, W, N = 4, 16, 1024
+    K, Qw = _stream(4, N, G, W)
+    m, iz = O.normalisers(K, Qw, SCALE)
+    s = O.token_scores(K, Qw, SCALE, m, iz)
+    assert abs(np.sum(s.astype(np.float64)) - G * W) <= 1e-4 * G * W
+
+
+def test_scores_match_fp64_softmax(O):
+    """Brute force in fp64: per query a textbook softmax over all keys (no
+    causal mask, [K] Fig. 3), summed over the queries of the group."""
+    G, W, N = 2, 4, 256
+    K, Qw = _stream(5, N, G, W)
+    m, iz = O.normalisers(K, Qw, SCALE)
+    s = O.token_scores(K, Qw, SCALE, m, iz)
+    Kf = bits_to_f(K).astype(np.float64)
+    Qf = bits_to_f(Qw).astype(np.float64)
+    L = (Qf @ Kf.T) * float(SCALE)
+    P = np.exp(L - L.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    ref = P.sum(axis=0)
+    assert np.max(np.abs(s - ref)) <= 1e-5 * ref.max()
+    assert np.max(np.abs(m - L.max(axis=1))) <= 1e-5 * np.abs(L).max()
+    # a region sub-range returns the same scores
+    s2 = O.token_scores(K, Qw, SCALE, m, iz, t0=64, nt=128)
+    assert np.array_equal(s2, s[64:192])
+
+
+# -------------------------------------------------------- channel selection
+def test_channel_topc_vs_stable_sort(O):
+    """[M] Fig. 6 caption, Stage-1: top elements of each vector; reading:
+    magnitude order, ties to the lower channel."""
+    rng = np.random.default_rng(6)
+    for trial in range(200):
+        x = rng.standard_normal(128) * (10.0 ** rng.integers(-2, 3))
+        if trial % 3 == 0:  # many equal magnitudes, both signs, zeros
+            x = rng.integers(-3, 4, 128).astype(np.float64)
+        row = bf16_bits(x)
+        key = (row & 0x7FFF).astype(np.int64)
+        order = np.lexsort((np.arange(128), -key))
+        for c in (8, 32, 64, 120, 128):
+            mask, rho = O.channel_topc(row, c)
+            bits = np.unpackbits(mask, bitorder="little")
+            want = np.zeros(128, np.uint8)
+            want[order[:c]] = 1
+            assert np.array_equal(bits, want), (trial, c)
+            xf = bits_to_f(row).astype(np.float64)
+            e_all = np.sum(xf ** 2)
+            ref = 1.0 if e_all == 0 else np.sum(xf[want == 1] ** 2) / e_all
+            assert abs(rho - ref) <= 2e-6
+            if c == 128:
+                assert rho == 1.0
+
+
+def test_outlier_channels_in_every_topc():
+    """Generated keys: each of the 4 outlier channels (x10) is among the 32
+    largest of nearly every K vector."""
+    w = gen.make_workload("tiny", N=256)
+    from oracle import oracle as O
+    K = gen.u16(w["K"][0, 0])
+    mag = np.abs(bits_to_f(K))
+    outl = np.argsort(-mag.mean(axis=0))[:4]
+    hits = np.zeros(4)
+    n = 0
+    for t in range(256):
+        if w["heavy"][0, 0, t]:
+            continue
+        mask, _ = O.channel_topc(K[t], 32)
+        hits += np.unpackbits(mask, bitorder="little")[outl]
+        n += 1
+    assert np.all(hits / n >= 0.8)
+
+
+# ------------------------------------------------------- token selection
+def _brute_top_t(s, T):
+    best = None
+    for sub in itertools.combinations(range(len(s)), T):
+        tot = sum(Fraction(float(s[i])) for i in sub)
+        if best is None or tot > best[0]:
+            best = (tot, sub)
+    return set(best[1])  # combinations are lexicographic: first max wins ties
+
+
+def test_top_t_brute_force(O):
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        S = 12
+        s = rng.random(S).astype(np.float32)
+        if trial % 2:
+            s = np.round(s * 4).astype(np.float32) / 4  # ties
+        for T in (0, 1, 3, 6, 11, 12):
+            keep = O.top_t(s, T)
+            assert set(np.nonzero(keep)[0]) == _brute_top_t(s, T), (trial, T)
+
+
+def test_token2chunk_golden(O):
+    cases = json.load(open(os.path.join(GOLDEN, "token2chunk_examples.json")))["cases"]
+    for cs in cases:
+        keep = O.token2chunk(np.array(cs["scores"], np.float32), cs["T"], cs["alpha"], cs["gamma"])
+        assert list(np.nonzero(keep)[0]) == cs["keep"], cs["why"]
+
+
+def test_token2chunk_properties(O):
+    rng = np.random.default_rng(8)
+    for trial in range(300):
+        S = int(rng.choice([16, 32, 64]))
+        T = int(rng.integers(2, S))
+        alpha = int(rng.integers(0, T))
+        gamma = int(rng.integers(2, 17))
+        s = rng.random(S).astype(np.float32) ** 3
+        keep = O.token2chunk(s, T, alpha, gamma)
+        assert keep.sum() == T
+        A = O.top_t(s, T - alpha)
+        assert np.all(keep[A == 1] == 1)
+        if alpha == 0:
+            assert np.array_equal(keep, O.top_t(s, T))
+        # kept tokens outside A: whole gaps between neighbouring A tokens with
+        # span <= gamma (chunks, at most alpha tokens in all), plus the best
+        # remaining tokens (fill)
+        a = np.nonzero(A)[0]
+        chunk = set()
+        for k in range(len(a) - 1):
+            gap = list(range(a[k] + 1, a[k + 1]))
+            if gap and a[k + 1] - a[k] + 1 <= gamma and all(keep[t] for t in gap):
+                chunk.update(gap)
+        assert len(chunk) <= alpha
+        fill = [t for t in np.nonzero(keep)[0] if not A[t] and t not in chunk]
+        rest = [t for t in np.lexsort((np.arange(S), -s)) if not A[t] and t not in chunk]
+        assert sorted(fill) == sorted(rest[:len(fill)])
+
+
+# --------------------------------------------------- layout, pack, choice
+S128_PCT = [100.0, 56.25, 31.25, 50.2, 28.3, 15.8, 25.1, 14.2, 7.9]
+
+
+def test_segment_bytes_table(O):
+    S = 128
+    for (T, c), pct in zip(gen.table9(S), S128_PCT):
+        b = O.seg_bytes(T, c, S)
+        assert abs(100.0 * b / (4 * S * 128) - pct) < 0.06, (T, c, b)
+    assert O.seg_bytes(0, 0, S) == 0
+    assert O.seg_bytes(13, 128, 64) == 13 * 512 + 32
+
+
+def unpack_segment(buf, d, S):
+    """Independent parser of one packed segment -> (idx, Kd, Vd, mk, mv): dense
+    rows (zero where dropped) as uint16 bits and boolean masks."""
+    T, c, off = int(d["n_tok"]), int(d["n_ch"]), int(d["offset"])
+    pos = off
+
+    def masks():
+        nonlocal pos
+        if c < 128:
+            m = np.unpackbits(buf[pos:pos + 16 * T].reshape(T, 16), axis=1, bitorder="little")
+            pos += 16 * T
+            return m.astype(bool)
+        return np.ones((T, 128), bool)
+
+    def vals(m):
+        nonlocal pos
+        v = buf[pos:pos + 2 * T * c].view(np.uint16).reshape(T, c)
+        pos += 2 * T * c
+        out = np.zeros((T, 128), np.uint16)
+        for t in range(T):
+            out[t, m[t]] = v[t]
+        return out
+
+    mk = masks()
+    Kd = vals(mk)
+    mv = masks()
+    Vd = vals(mv)
+    if T < S:
+        idx = buf[pos:pos + 2 * T].view(np.uint16).astype(np.int64)
+        pad_end = off + int(O_seg_bytes(T, c, S))
+        assert np.all(buf[pos + 2 * T:pad_end] == 0)
+    else:
+        idx = np.arange(S)
+    return idx, Kd, Vd, mk, mv
+
+
+def O_seg_bytes(T, c, S):
+    from oracle import oracle as O
+    return O.seg_bytes(T, c, S)
+
+
+def _small_stream(seed, N=512, G=2, W=8):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((N, 128))
+    K[:, rng.choice(128, 4, replace=False)] *= 10
+    heavy = rng.choice(N, N // 32, replace=False)
+    K[heavy] = K[heavy] * 0.25 + 8.0 * np.sign(rng.standard_normal(128))
+    V = rng.standard_normal((N, 128))
+    Qw = rng.standard_normal((G, W, 128))
+    Qw += 0.7 * np.sign(K[heavy[0]])
+    return bf16_bits(K), bf16_bits(V), bf16_bits(Qw)
+
+
+def test_pack_round_trip(O):
+    K, V, Qw = _small_stream(9)
+    S = 64
+    r = O.compress_stream(K, V, Qw, S=S, strategies=gen.table9(S),
+                          budget_bytes=gen.budget_bytes(33, S), scale=SCALE)
+    buf = r["packed"]
+    off = 0
+    for sg, d in enumerate(r["desc"]):
+        assert int(d["offset"]) == off and d["seg_tokens"] == S
+        T, c = gen.table9(S)[d["strategy"]]
+        assert (d["n_tok"], d["n_ch"]) == (T, c)
+        idx, Kd, Vd, mk, mv = unpack_segment(buf, d, S)
+        assert len(idx) == T and np.all(np.diff(idx) > 0)
+        rows = sg * S + idx
+        assert np.all(mk.sum(axis=1) == c) and np.all(mv.sum(axis=1) == c)
+        assert np.array_equal(Kd, np.where(mk, K[rows], 0))
+        assert np.array_equal(Vd, np.where(mv, V[rows], 0))
+        off += O.seg_bytes(T, c, S)
+    assert r["used"] == off
+
+
+def test_keep_all_pack_is_the_dense_cache(O):
+    K, V, Qw = _small_stream(10, N=256)
+    S = 64
+    r = O.compress_stream(K, V, Qw, S=S, strategies=[(S, 128)], budget_bytes=4 * S * 128,
+                          scale=SCALE)
+    buf = r["packed"]
+    for sg in range(256 // S):
+        seg = buf[sg * 4 * S * 128:(sg + 1) * 4 * S * 128].view(np.uint16)
+        assert np.array_equal(seg[:S * 128], K[sg * S:(sg + 1) * S].ravel())
+        assert np.array_equal(seg[S * 128:], V[sg * S:(sg + 1) * S].ravel())
+
+
+def _j_from_segment(buf, d, S, s, K, V, sg):
+    """Objective recomputed from the materialised segment in fp64: kept score
+    mass weighted by the mean kept energy share of the K and V vectors."""
+    idx, Kd, Vd, mk, mv = unpack_segment(buf, d, S)
+    tot = 0.0
+    for j, t in enumerate(idx):
+        kr = bits_to_f(K[sg * S + t]).astype(np.float64)
+        vr = bits_to_f(V[sg * S + t]).astype(np.float64)
+        ek = np.sum(bits_to_f(Kd[j]).astype(np.float64) ** 2) / max(np.sum(kr ** 2), 1e-300)
+        ev = np.sum(bits_to_f(Vd[j]).astype(np.float64) ** 2) / max(np.sum(vr ** 2), 1e-300)
+        tot += float(s[sg * S + t]) * 0.5 * (ek + ev)
+    return tot
+
+
+def test_choice_brute_force_enumeration(O):
+    """[M] abstract / Fig. 5 caption: one strategy per segment; reading: the
+    objective is the kept attention mass times the kept energy share, under a
+    per-segment byte budget.  All 9^3 assignments of three segments are
+    materialised (forced), the objective recomputed from the packed bytes, and
+    the best feasible assignment (lowest on ties) must be the free choice."""
+    S = 32
+    strat = gen.table9(S)
+    for seed in (11, 12):
+        K, V, Qw = _small_stream(seed, N=96, G=2, W=4)
+        budget = gen.budget_bytes(33, S)
+        free = O.compress_stream(K, V, Qw, S=S, strategies=strat, budget_bytes=budget, scale=SCALE)
+        s = free["scores"]
+        feas = [i for i, (T, c) in enumerate(strat) if O.seg_bytes(T, c, S) <= budget]
+        # J of every (segment, strategy), each from its own materialised segment
+        Jm = {}
+        for i in feas:
+            f = O.compress_stream(K, V, Qw, S=S, strategies=strat, budget_bytes=budget,
+                                  scale=SCALE, forced=np.full(3, i, np.uint8))
+            for sg in range(3):
+                Jm[(sg, i)] = _j_from_segment(f["packed"], f["desc"][sg], S, s, K, V, sg)
+                assert abs(Jm[(sg, i)] - f["objective"][sg, i]) <= 1e-5 * max(1.0, Jm[(sg, i)])
+        best = None
+        for a in itertools.product(feas, repeat=3):  # lexicographic: first max wins ties
+            tot = sum(Fraction(Jm[(sg, a[sg])]) for sg in range(3))  # exact: J spans decades
+            if best is None or tot > best[0]:
+                best = (tot, a)
+        assert tuple(int(x) for x in free["desc"]["strategy"]) == best[1]
+
+
+def test_budget_feasible_sets(O):
+    for S, pct, want in ((64, 33, {2, 4, 5, 6, 7, 8}), (128, 33, {2, 4, 5, 6, 7, 8}),
+                         (128, 25, {5, 7, 8}), (256, 20, {5, 7, 8})):
+        b = gen.budget_bytes(pct, S)
+        got = {i for i, (T, c) in enumerate(gen.table9(S)) if O.seg_bytes(T, c, S) <= b}
+        assert got == want, (S, pct, got)
+
+
+# -------------------------------------------------------------- decode
+def dense_attention(q, K, V, scale):
+    """Textbook softmax attention in fp64 (q [G,128], K/V [n,128] floats)."""
+    L = (q @ K.T) * scale
+    if L.shape[1] == 0:
+        return np.zeros((q.shape[0], 128)), np.full(q.shape[0], -np.inf)
+    mx = L.max(axis=1, keepdims=True)
+    P = np.exp(L - mx)
+    den = P.sum(axis=1, keepdims=True)
+    return (P / den) @ V, (mx + np.log(den))[:, 0]
+
+
+def test_decode_keep_all_equals_dense_attention(O):
+    """Keep-all compression must equal dense softmax attention."""
+    K, V, Qw = _small_stream(13, N=256)
+    S = 64
+    r = O.compress_stream(K, V, Qw, S=S, strategies=[(S, 128)], budget_bytes=4 * S * 128,
+                          scale=SCALE)
+    q = bf16_bits(np.random.default_rng(1).standard_normal((2, 128)))
+    out, lse = O.decode_stream(q, r["packed"], r["desc"], SCALE)
+    ref, rlse = dense_attention(bits_to_f(q).astype(np.float64), bits_to_f(K).astype(np.float64),
+                                bits_to_f(V).astype(np.float64), float(SCALE))
+    assert np.max(np.abs(out - ref)) <= 1e-12 and np.max(np.abs(lse - rlse)) <= 1e-12
+
+
+def test_decode_zero_retention_segments_contribute_nothing(O):
+    """Segments forced to keep no token add nothing: they own no bytes, and the
+    output equals dense attention over the remaining tokens."""
+    K, V, Qw = _small_stream(14, N=256)
+    S = 64
+    strat = [(S, 128), (0, 0)]
+    r2 = O.compress_stream(K, V, Qw, S=S, strategies=strat, budget_bytes=4 * S * 128,
+                           scale=SCALE, forced=np.array([0, 1, 0, 1], np.uint8))
+    r = r2
+    q = bf16_bits(np.random.default_rng(2).standard_normal((2, 128)))
+    out, lse = O.decode_stream(q, r2["packed"], r2["desc"], SCALE)
+    keep = np.r_[0:64, 128:192]
+    ref, rlse = dense_attention(bits_to_f(q).astype(np.float64),
+                                bits_to_f(K[keep]).astype(np.float64),
+                                bits_to_f(V[keep]).astype(np.float64), float(SCALE))
+    assert np.all(np.isfinite(out))
+    assert np.max(np.abs(out - ref)) <= 1e-12 and np.max(np.abs(lse - rlse)) <= 1e-12
+    assert list(r["desc"]["n_tok"]) == [64, 0, 64, 0]
+
+
+def test_decode_sparse_matches_masked_dense_attention(O):
+    """Dropped channels count as 0 (reading): attention over the compressed
+    stream equals dense attention over kept tokens with dropped channels
+    zeroed, computed from an independent unpack."""
+    K, V, Qw = _small_stream(15)
+    S = 64
+    r = O.compress_stream(K, V, Qw, S=S, strategies=gen.table9(S),
+                          budget_bytes=gen.budget_bytes(33, S), scale=SCALE)
+    Ks, Vs = [], []
+    for d in r["desc"]:
+        idx, Kd, Vd, _, _ = unpack_segment(r["packed"], d, S)
+        Ks.append(Kd)
+        Vs.append(Vd)
+    Kc = bits_to_f(np.concatenate(Ks)).astype(np.float64)
+    Vc = bits_to_f(np.concatenate(Vs)).astype(np.float64)
+    q = bf16_bits(np.random.default_rng(3).standard_normal((2, 128)))
+    out, lse = O.decode_stream(q, r["packed"], r["desc"], SCALE)
+    ref, rlse = dense_attention(bits_to_f(q).astype(np.float64), Kc, Vc, float(SCALE))
+    assert np.max(np.abs(out - ref)) <= 1e-12 and np.max(np.abs(lse - rlse)) <= 1e-12
+
+
+def test_decode_empty_is_zero_minus_inf(O):
+    from oracle.oracle import DESC_DTYPE
+    q = bf16_bits(np.ones((3, 128)))
+    out, lse = O.decode_stream(q, np.zeros(0, np.uint8), np.zeros(0, DESC_DTYPE), SCALE)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+# ---------------------------------------------------------------- Kara
+def test_kara_window_scores(O):
+    """Kara event: window of 512 positions scored bidirectionally; scores of
+    all window tokens sum to G*512 queries ([K] Fig. 3: all pairs)."""
+    w = gen.make_kara(B=1, prompt=512, gen=512)
+    G = w["G"]
+    K = gen.u16(w["K"][0, 0, 512:1024])
+    Qw = gen.u16(w["Qall"][0, :G, 512:1024]).reshape(G * 512, 128)
+    m, iz = O.normalisers(K, Qw, SCALE)
+    s = O.token_scores(K, Qw, SCALE, m, iz)
+    assert abs(np.sum(s.astype(np.float64)) - G * 512) <= 1e-4 * G * 512
+    r = O.compress_stream(K, gen.u16(w["V"][0, 0, 512:1024]), Qw.reshape(G, 512, 128), S=64,
+                          strategies=[(13, 128)], budget_bytes=4 * 64 * 128, scale=SCALE,
+                          region_begin=384, region_len=64, t2c_alpha=3, t2c_gamma=16)
+    assert np.array_equal(r["scores"], s[384:448])
+    d = r["desc"][0]
+    assert (d["n_tok"], d["n_ch"], d["flags"]) == (13, 128, 2)
+    assert r["used"] == 13 * 512 + 32
+
+
+def test_kara_schedule():
+    ev, T = gen.kara_schedule(16384, 8192)
+    assert T == 13 and len(ev) == 127
+    L, w0, rb = ev[0]
+    assert L == 16384 + 128 and rb == 384 and w0 == L - 512
+    assert ev[-1][0] == 24576

@@ -1,0 +1,163 @@
+"""Python binding of libkvc (include/kvc.h): argument marshalling only.
+
+Every step of compression and decode runs in the HIP kernels of
+``libkvc.so``; this module only turns torch tensors into device pointers and
+the current HIP stream.  If the library is missing the import of the entry
+points fails loudly -- there is no CPU fallback.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvc.so")
+
+HEAD_DIM = 128
+MAX_STRATEGIES = 32
+DESC_CHOOSE = 0xFF
+
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported configuration",
+          -3: "no strategy fits the byte budget", -4: "workspace too small",
+          -5: "pointer not 16-byte aligned", -6: "HIP launch error"}
+
+DESC_DTYPE = np.dtype([("offset", "<u8"), ("n_tok", "<u2"), ("n_ch", "<u2"),
+                       ("strategy", "u1"), ("flags", "u1"), ("seg_tokens", "<u2")])
+
+
+class KvcError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+class Strategy(ctypes.Structure):
+    _fields_ = [("n_tok", ctypes.c_uint16), ("n_ch", ctypes.c_uint16)]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("batch", ctypes.c_uint32),
+                ("n_q_heads", ctypes.c_uint32), ("n_kv_heads", ctypes.c_uint32),
+                ("head_dim", ctypes.c_uint32), ("n_ctx", ctypes.c_uint32),
+                ("region_begin", ctypes.c_uint32), ("region_len", ctypes.c_uint32),
+                ("seg_tokens", ctypes.c_uint32), ("n_win", ctypes.c_uint32),
+                ("strategies", ctypes.POINTER(Strategy)), ("n_strategies", ctypes.c_uint32),
+                ("budget_bytes", ctypes.c_uint32), ("t2c_alpha", ctypes.c_uint32),
+                ("t2c_gamma", ctypes.c_uint32), ("scale", ctypes.c_float),
+                ("kv_stream_stride", ctypes.c_uint64), ("qw_head_stride", ctypes.c_uint64),
+                ("packed_stream_stride", ctypes.c_uint64), ("packed_base_offset", ctypes.c_uint64),
+                ("desc_stream_stride", ctypes.c_uint32), ("max_desc_per_stream", ctypes.c_uint32),
+                ("decode_splits", ctypes.c_uint32), ("reserved", ctypes.c_uint32 * 4)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("seg_bytes", ctypes.c_uint32 * MAX_STRATEGIES), ("feasible_mask", ctypes.c_uint32),
+                ("n_seg", ctypes.c_uint32), ("max_seg_bytes", ctypes.c_uint64),
+                ("stream_capacity", ctypes.c_uint64), ("packed_bytes_max", ctypes.c_uint64),
+                ("n_desc", ctypes.c_uint64), ("compress_ws_bytes", ctypes.c_uint64),
+                ("decode_ws_bytes", ctypes.c_uint64), ("decode_splits", ctypes.c_uint32),
+                ("needs_scoring", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libkvc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libkvc.so not built ({LIB_PATH}); run "
+                              "python -m compressed_kv_cache_compress_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        L.kv_layout_query.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Layout)]
+        L.kv_layout_query.restype = ctypes.c_int
+        L.kv_compress.argtypes = [ctypes.POINTER(Params), P, P, P, P, P, P, P, P, P, P,
+                                  ctypes.c_size_t, P]
+        L.kv_compress.restype = ctypes.c_int
+        L.kv_attend_decode.argtypes = [ctypes.POINTER(Params), P, P, P, P, P, P, P,
+                                       ctypes.c_size_t, P]
+        L.kv_attend_decode.restype = ctypes.c_int
+        L.kvc_status_str.argtypes = [ctypes.c_int]
+        L.kvc_status_str.restype = ctypes.c_char_p
+        L.kvc_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+class KvParams:
+    """Owner of a kvc_params struct and of the host strategy array it points to."""
+
+    def __init__(self, *, batch, n_q_heads, n_kv_heads, head_dim=HEAD_DIM, n_ctx=0,
+                 region_begin=0, region_len=None, seg_tokens=0, n_win=0, strategies=(),
+                 budget_bytes=0, t2c_alpha=0, t2c_gamma=0, scale=0.0, kv_stream_stride=0,
+                 qw_head_stride=0, packed_stream_stride=0, packed_base_offset=0,
+                 desc_stream_stride=0, max_desc_per_stream=0, decode_splits=0):
+        strategies = list(strategies)
+        self._strat = (Strategy * max(1, len(strategies)))(*[Strategy(t, c) for t, c in strategies])
+        if region_len is None:
+            region_len = n_ctx - region_begin
+        self.p = Params()
+        p = self.p
+        p.struct_size = ctypes.sizeof(Params)
+        p.batch, p.n_q_heads, p.n_kv_heads, p.head_dim = batch, n_q_heads, n_kv_heads, head_dim
+        p.n_ctx, p.region_begin, p.region_len = n_ctx, region_begin, region_len
+        p.seg_tokens, p.n_win = seg_tokens, n_win
+        p.strategies = ctypes.cast(self._strat, ctypes.POINTER(Strategy)) if strategies else None
+        p.n_strategies = len(strategies)
+        p.budget_bytes, p.t2c_alpha, p.t2c_gamma = budget_bytes, t2c_alpha, t2c_gamma
+        p.scale = scale
+        p.kv_stream_stride, p.qw_head_stride = kv_stream_stride, qw_head_stride
+        p.packed_stream_stride, p.packed_base_offset = packed_stream_stride, packed_base_offset
+        p.desc_stream_stride, p.max_desc_per_stream = desc_stream_stride, max_desc_per_stream
+        p.decode_splits = decode_splits
+        self.strategies = strategies
+
+    @property
+    def streams(self):
+        return self.p.batch * self.p.n_kv_heads
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def kv_layout_query(params, check=True):
+    """Host-only layout query -> (status, Layout)."""
+    L = Layout()
+    st = lib().kv_layout_query(ctypes.byref(params.p), ctypes.byref(L))
+    if check and st not in (0,):
+        raise KvcError("kv_layout_query", st)
+    return st, L
+
+
+def kv_compress(params, K, V, Qwin, forced, packed, desc, used_bytes, scores, objective, ws):
+    """Enqueue compression on the current stream (tensors on the GPU)."""
+    st = lib().kv_compress(ctypes.byref(params.p), _ptr(K), _ptr(V), _ptr(Qwin), _ptr(forced),
+                           _ptr(packed), _ptr(desc), _ptr(used_bytes), _ptr(scores),
+                           _ptr(objective), _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+                           _stream())
+    if st != 0:
+        raise KvcError("kv_compress", st)
+
+
+def kv_attend_decode(params, q, packed, desc, n_desc, out, lse, ws):
+    """Enqueue decode attention on the current stream (tensors on the GPU)."""
+    st = lib().kv_attend_decode(ctypes.byref(params.p), _ptr(q), _ptr(packed), _ptr(desc),
+                                _ptr(n_desc), _ptr(out), _ptr(lse), _ptr(ws),
+                                ws.numel() * ws.element_size() if ws is not None else 0, _stream())
+    if st != 0:
+        raise KvcError("kv_attend_decode", st)
+
+
+def desc_view(t):
+    """uint8 tensor of descriptors (host copy) -> numpy structured array."""
+    return t.detach().cpu().numpy().view(DESC_DTYPE)

@@ -1,0 +1,613 @@
+// kvc_compress.hip -- gfx950 kernels of segment-wise two-dimensional KV-cache
+// compression (MosaicKV review page: abstract, Fig. 5 and Fig. 6 captions;
+// KARA review page: "What carries the argument", Fig. 3 caption).
+//
+// Pipeline per call (every kernel on the caller's stream):
+//   score_partials  per 64-token block of the domain and per window query:
+//                   block max m_b and pairwise sum z_b of exp(l - m_b)
+//   score_normalise per window query: global max m and 1/Z
+//   token_scores    per region token: sum over the group's window queries of
+//                   exp(l - m) / Z, accumulated one query at a time
+//   channel_select  per region K and V vector and per channel count c < 128:
+//                   top-c magnitude mask and kept energy share
+//   segment_choose  per segment: top-T (or Token2Chunk) per strategy,
+//                   objective, choice under the byte budget, descriptor
+//   offsets_scan    per stream: exclusive scan of segment bytes
+//   pack            per segment: masks, values, index list
+//
+// Selection outputs are bit-exact functions of the inputs: every float that
+// feeds a comparison is produced by correctly rounded fp32 operations in a
+// fixed order (fma chains over ascending channels, pairwise trees with
+// adjacent pairs first, sequential sums over queries), built with
+// -ffp-contract=off and without packed fp32 math.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "kvc_device.h"
+#include "kvc_internal.h"
+
+namespace kvc {
+
+// ---------------------------------------------------------------------------
+// Window scoring.
+// ---------------------------------------------------------------------------
+
+// Loads one key row (128 bf16) of this lane into fp32 registers.
+__device__ __forceinline__ void load_row_f32(const uint16_t* __restrict__ row, float* kf) {
+  const uint4* r4 = reinterpret_cast<const uint4*>(row);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint4 v = r4[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      kf[8 * i + 2 * k] = __uint_as_float(w[k] << 16);
+      kf[8 * i + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  }
+}
+
+// q . k as one fma chain over ascending channels; q is wave-uniform.
+__device__ __forceinline__ float dot_chain(const uint16_t* __restrict__ qrow, const float* kf) {
+  const uint32_t* q32 = reinterpret_cast<const uint32_t*>(qrow);
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const uint32_t w = q32[i];
+    acc = __builtin_fmaf(__uint_as_float(w << 16), kf[2 * i], acc);
+    acc = __builtin_fmaf(__uint_as_float(w & 0xFFFF0000u), kf[2 * i + 1], acc);
+  }
+  return acc;
+}
+
+struct ScoreArgs {
+  const uint16_t* K;
+  const uint16_t* Qw;
+  float* part_m;
+  float* part_z;
+  float* norm_m;
+  float* norm_iz;
+  float* scores;
+  float* scores_out;
+  uint64_t kv_stride, qw_stride;
+  int hkv, hq, G, W, nq, nblk, region_begin, region_len;
+  float scale;
+};
+
+__device__ __forceinline__ const uint16_t* qrow_of(const ScoreArgs& a, int s, int qi) {
+  const int b = s / a.hkv, h = s - b * a.hkv;
+  const int g = qi / a.W, w = qi - g * a.W;
+  return a.Qw + (uint64_t)(b * a.hq + h * a.G + g) * a.qw_stride + (uint64_t)w * D;
+}
+
+// grid (nblk, streams), 64 threads: lane = token of the 64-token block.
+__global__ __launch_bounds__(64) void k_score_partials(ScoreArgs a) {
+  const int blk = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+  const int t = blk * BLK + lane;
+  float kf[D];
+  load_row_f32(a.K + (uint64_t)s * a.kv_stride + (uint64_t)t * D, kf);
+  for (int qi = 0; qi < a.nq; ++qi) {
+    const float l = dot_chain(qrow_of(a, s, qi), kf) * a.scale;
+    const float mb = wave_max(l);
+    const float e = spec_exp2((l - mb) * KVC_LOG2E);
+    const float z = tree_sum_lanes(e);
+    if (lane == 0) {
+      const uint64_t o = ((uint64_t)s * a.nq + qi) * a.nblk + blk;
+      a.part_m[o] = mb;
+      a.part_z[o] = z;
+    }
+  }
+}
+
+// grid (nq, streams), 64 threads: lane l owns the contiguous blocks
+// [l*ch, (l+1)*ch) of the zero-padded power-of-two block range; its pairwise
+// sum is built bottom-up with a binary-counter stack, then combined across
+// lanes in the same tree order.
+__global__ __launch_bounds__(64) void k_score_normalise(ScoreArgs a) {
+  const int qi = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+  const float* pm = a.part_m + ((uint64_t)s * a.nq + qi) * a.nblk;
+  const float* pz = a.part_z + ((uint64_t)s * a.nq + qi) * a.nblk;
+  int np = 1;
+  while (np < a.nblk) np <<= 1;
+  const int ch = np >= 64 ? np / 64 : 1;
+  const int b0 = lane * ch;
+  float mx = -INFINITY;
+  for (int i = 0; i < ch; ++i)
+    if (b0 + i < a.nblk) mx = fmaxf(mx, pm[b0 + i]);
+  const float m = wave_max(mx);
+  float stk[16];
+  for (int i = 0; i < ch; ++i) {
+    const int bb = b0 + i;
+    float v = (bb < a.nblk) ? pz[bb] * spec_exp2((pm[bb] - m) * KVC_LOG2E) : 0.0f;
+    int lvl = 0;
+    for (int j = i; j & 1; j >>= 1) {
+      v = stk[lvl] + v;
+      ++lvl;
+    }
+    stk[lvl] = v;
+  }
+  int top = 0;
+  while ((1 << top) < ch) ++top;
+  const float part = stk[top];
+  const float Z = tree_sum_lanes(part);
+  if (lane == 0) {
+    a.norm_m[(uint64_t)s * a.nq + qi] = m;
+    a.norm_iz[(uint64_t)s * a.nq + qi] = 1.0f / Z;
+  }
+}
+
+// grid (ceil(region_len/64), streams), 64 threads: lane = region token.
+__global__ __launch_bounds__(64) void k_token_scores(ScoreArgs a) {
+  const int s = blockIdx.y, lane = threadIdx.x;
+  const int tr = blockIdx.x * 64 + lane;
+  const bool valid = tr < a.region_len;
+  const int t = a.region_begin + (valid ? tr : 0);
+  float kf[D];
+  load_row_f32(a.K + (uint64_t)s * a.kv_stride + (uint64_t)t * D, kf);
+  const float* nm = a.norm_m + (uint64_t)s * a.nq;
+  const float* ni = a.norm_iz + (uint64_t)s * a.nq;
+  float sc = 0.0f;
+  for (int qi = 0; qi < a.nq; ++qi) {
+    const float l = dot_chain(qrow_of(a, s, qi), kf) * a.scale;
+    const float e = spec_exp2((l - nm[qi]) * KVC_LOG2E);
+    sc = sc + e * ni[qi];
+  }
+  if (valid) {
+    a.scores[(uint64_t)s * a.region_len + tr] = sc;
+    if (a.scores_out) a.scores_out[(uint64_t)s * a.region_len + tr] = sc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-vector channel selection (Stage-1): one wave per K or V vector, lane l
+// holding channels l and l+64.
+// ---------------------------------------------------------------------------
+struct SelectArgs {
+  const uint16_t* K;
+  const uint16_t* V;
+  uint32_t* masks;
+  float* rho;
+  uint64_t kv_stride;
+  int region_begin, region_len, nc;
+  int cvals[MAX_NC];
+};
+
+constexpr int SEL_TOKENS = 16;  // tokens per block (x2 vectors, 8 per wave)
+
+__global__ __launch_bounds__(256) void k_channel_select(SelectArgs a) {
+  const int s = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int r = wv; r < 2 * SEL_TOKENS; r += 4) {
+    const int tr = blockIdx.x * SEL_TOKENS + (r >> 1);
+    const int kv = r & 1;
+    if (tr >= a.region_len) break;
+    const uint16_t* row = (kv ? a.V : a.K) + (uint64_t)s * a.kv_stride +
+                          (uint64_t)(a.region_begin + tr) * D;
+    const uint32_t b0 = row[lane], b1 = row[lane + 64];
+    const uint32_t k0 = b0 & 0x7FFFu, k1 = b1 & 0x7FFFu;
+    const float x0 = bf2f(b0), x1 = bf2f(b1);
+    const float q0 = x0 * x0, q1 = x1 * x1;
+    const float Eall = tree_sum_lanes(q0) + tree_sum_lanes(q1);
+    for (int u = 0; u < a.nc; ++u) {
+      const uint32_t c = (uint32_t)a.cvals[u];
+      // the c-th largest key, bit by bit from the top
+      uint32_t tau = 0;
+      for (int bit = 14; bit >= 0; --bit) {
+        const uint32_t cand = tau | (1u << bit);
+        const uint32_t cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand));
+        if (cnt >= c) tau = cand;
+      }
+      const uint32_t ngt = __popcll(__ballot(k0 > tau)) + __popcll(__ballot(k1 > tau));
+      const uint32_t need = c - ngt;
+      const uint64_t e0 = __ballot(k0 == tau), e1 = __ballot(k1 == tau);
+      const uint32_t rk0 = lanes_below(e0);
+      const uint32_t rk1 = (uint32_t)__popcll(e0) + lanes_below(e1);
+      const bool s0 = k0 > tau || (k0 == tau && rk0 < need);
+      const bool s1 = k1 > tau || (k1 == tau && rk1 < need);
+      const uint64_t m0 = __ballot(s0), m1 = __ballot(s1);
+      const float Ec = tree_sum_lanes(s0 ? q0 : 0.0f) + tree_sum_lanes(s1 ? q1 : 0.0f);
+      if (lane == 0) {
+        const uint64_t o = (((uint64_t)s * a.region_len + tr) * a.nc + u) * 2 + kv;
+        uint4 w;
+        w.x = (uint32_t)m0;
+        w.y = (uint32_t)(m0 >> 32);
+        w.z = (uint32_t)m1;
+        w.w = (uint32_t)(m1 >> 32);
+        reinterpret_cast<uint4*>(a.masks)[o] = w;
+        a.rho[o] = (Eall == 0.0f) ? 1.0f : Ec / Eall;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-segment strategy choice.
+// ---------------------------------------------------------------------------
+struct ChooseArgs {
+  const float* scores;
+  const float* rho;
+  const uint8_t* forced;
+  kvc_seg_desc* desc;
+  uint32_t* keep;
+  float* objective;
+  int region_len, S, n_seg, nc, n_strat, t2c_alpha, t2c_gamma;
+  uint32_t dstride, feasible_mask;
+  bool have_scores;
+  int sT[KVC_MAX_STRATEGIES], sc[KVC_MAX_STRATEGIES], su[KVC_MAX_STRATEGIES];
+};
+
+// Keys of the segment's tokens: slot j of lane l is token 64*j + l.  Returns
+// per slot whether the token is among the T best by (score desc, position asc).
+__device__ __forceinline__ void top_t_flags(const uint32_t* key, const bool* valid, int NJ, int T,
+                                            bool* out) {
+  uint32_t tau = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    uint32_t cnt = 0;
+    for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(valid[j] && key[j] >= cand));
+    if (cnt >= (uint32_t)T) tau = cand;
+  }
+  uint32_t ngt = 0;
+  for (int j = 0; j < NJ; ++j) ngt += __popcll(__ballot(valid[j] && key[j] > tau));
+  const uint32_t need = (uint32_t)T - ngt;
+  uint32_t before = 0;
+  for (int j = 0; j < NJ; ++j) {
+    const uint64_t e = __ballot(valid[j] && key[j] == tau);
+    const uint32_t rk = before + lanes_below(e);
+    out[j] = valid[j] && (key[j] > tau || (key[j] == tau && rk < need));
+    before += (uint32_t)__popcll(e);
+  }
+}
+
+// Token2Chunk on one lane, from the top-(T-alpha) flags in `fl` (bytes, one
+// per token); leaves exactly T flags set.
+// a, ck: LDS scratch of >= S ints; done: >= S bytes.
+__device__ void token2chunk_lane(const float* s, uint8_t* fl, int S, int T, int alpha, int gamma,
+                                 int* a, int* ck, uint8_t* done) {
+  int m = 0;
+  for (int i = 0; i < S; ++i)
+    if (fl[i]) a[m++] = i;
+  int nc = 0;
+  for (int k = 0; k + 1 < m; ++k) {
+    const int gap = a[k + 1] - a[k] - 1;
+    if (gap >= 1 && a[k + 1] - a[k] + 1 <= gamma) ck[nc++] = k;
+  }
+  for (int j = 0; j < nc; ++j) done[j] = 0;
+  int used = 0;
+  for (int it = 0; it < nc; ++it) {
+    int best = -1, bg = 0;
+    float bv = 0.0f;
+    for (int j = 0; j < nc; ++j) {
+      if (done[j]) continue;
+      const int k = ck[j];
+      const float v = s[a[k]] + s[a[k + 1]];
+      const int g = a[k + 1] - a[k] - 1;
+      if (best < 0 || v > bv || (v == bv && (g < bg || (g == bg && k < ck[best])))) {
+        best = j;
+        bv = v;
+        bg = g;
+      }
+    }
+    done[best] = 1;
+    if (used + bg <= alpha) {
+      const int k = ck[best];
+      for (int t = a[k] + 1; t < a[k + 1]; ++t) fl[t] = 1;
+      used += bg;
+    }
+  }
+  int have = 0;
+  for (int i = 0; i < S; ++i) have += fl[i];
+  while (have < T) {
+    int best = -1;
+    for (int i = 0; i < S; ++i) {
+      if (fl[i]) continue;
+      if (best < 0 || s[i] > s[best]) best = i;  // first index wins ties
+    }
+    fl[best] = 1;
+    ++have;
+  }
+}
+
+// grid (n_seg, streams), 64 threads.
+__global__ __launch_bounds__(64) void k_segment_choose(ChooseArgs a) {
+  const int sg = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+  const int S = a.S;
+  const int NJ = S >= 64 ? S / 64 : 1;
+  const int width = S >= 64 ? 64 : S;
+  __shared__ float s_sc[256];
+  __shared__ uint8_t s_fl[256];
+  __shared__ int s_a[256], s_ck[256];
+  __shared__ uint8_t s_done[256];
+  __shared__ float s_J[KVC_MAX_STRATEGIES];
+  __shared__ uint32_t s_keep[KVC_MAX_STRATEGIES][8];
+  float sc[4];
+  uint32_t key[4];
+  bool valid[4];
+  for (int j = 0; j < NJ; ++j) {
+    const int t = 64 * j + lane;
+    valid[j] = t < S;
+    sc[j] = (valid[j] && a.have_scores) ? a.scores[(uint64_t)s * a.region_len + sg * S + t] : 0.0f;
+    key[j] = __float_as_uint(sc[j]);
+    if (valid[j]) s_sc[t] = sc[j];
+  }
+  __syncthreads();
+  for (int i = 0; i < a.n_strat; ++i) {
+    const int T = a.sT[i], c = a.sc[i];
+    bool kp[4];
+    if (T == 0) {
+      for (int j = 0; j < NJ; ++j) kp[j] = false;
+    } else if (T >= S) {
+      for (int j = 0; j < NJ; ++j) kp[j] = valid[j];
+    } else if (a.t2c_alpha > 0) {
+      top_t_flags(key, valid, NJ, T - a.t2c_alpha, kp);
+      for (int j = 0; j < NJ; ++j)
+        if (valid[j]) s_fl[64 * j + lane] = kp[j] ? 1 : 0;
+      __syncthreads();
+      if (lane == 0) token2chunk_lane(s_sc, s_fl, S, T, a.t2c_alpha, a.t2c_gamma, s_a, s_ck, s_done);
+      __syncthreads();
+      for (int j = 0; j < NJ; ++j) kp[j] = valid[j] && s_fl[64 * j + lane];
+      __syncthreads();
+    } else {
+      top_t_flags(key, valid, NJ, T, kp);
+    }
+    // objective: pairwise tree over the segment's slots
+    float tj[4];
+    for (int j = 0; j < NJ; ++j) {
+      float term = 0.0f;
+      if (kp[j] && a.have_scores) {
+        float rk = 1.0f, rv = 1.0f;
+        if (c < D) {
+          const uint64_t o = (((uint64_t)s * a.region_len + sg * S + 64 * j + lane) * a.nc + a.su[i]) * 2;
+          rk = a.rho[o];
+          rv = a.rho[o + 1];
+        }
+        term = sc[j] * (0.5f * (rk + rv));
+      }
+      tj[j] = tree_sum_lanes(term, width);
+    }
+    float J;
+    if (NJ == 1)
+      J = tj[0];
+    else if (NJ == 2)
+      J = tj[0] + tj[1];
+    else
+      J = (tj[0] + tj[1]) + (tj[2] + tj[3]);
+    for (int j = 0; j < NJ; ++j) {
+      const uint64_t bal = __ballot(kp[j]);
+      if (lane == 0) {
+        s_keep[i][2 * j] = (uint32_t)bal;
+        s_keep[i][2 * j + 1] = (uint32_t)(bal >> 32);
+      }
+    }
+    if (lane == 0) s_J[i] = J;
+  }
+  __syncthreads();
+  if (lane == 0) {
+    const uint64_t si = (uint64_t)s * a.n_seg + sg;
+    int best = -1;
+    uint8_t rej = 0;
+    const uint8_t f = a.forced ? a.forced[si] : (uint8_t)KVC_DESC_CHOOSE;
+    if (f < a.n_strat && ((a.feasible_mask >> f) & 1u)) {
+      best = f;
+    } else {
+      if (a.forced && f != KVC_DESC_CHOOSE) rej = 0x80;
+      for (int i = 0; i < a.n_strat; ++i) {
+        if (!((a.feasible_mask >> i) & 1u)) continue;
+        if (best < 0 || s_J[i] > s_J[best]) best = i;
+      }
+    }
+    const int T = a.sT[best], c = a.sc[best];
+    kvc_seg_desc d;
+    d.offset = 0;
+    d.n_tok = (uint16_t)T;
+    d.n_ch = (uint16_t)(T > 0 ? c : 0);
+    d.strategy = (uint8_t)best;
+    d.flags = (uint8_t)(rej | (T >= S ? 1 : 0) | (c >= D ? 2 : 0));
+    d.seg_tokens = (uint16_t)S;
+    a.desc[(uint64_t)s * a.dstride + sg] = d;
+    const int nw = (S + 31) / 32;
+    for (int w = 0; w < nw; ++w) a.keep[si * nw + w] = s_keep[best][w];
+    if (a.objective)
+      for (int i = 0; i < a.n_strat; ++i) a.objective[si * a.n_strat + i] = s_J[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Offsets: per-stream exclusive scan of the chosen segments' bytes.
+// ---------------------------------------------------------------------------
+struct ScanArgs {
+  kvc_seg_desc* desc;
+  uint64_t* used;
+  uint64_t pstride, pbase;
+  uint32_t dstride;
+  int n_seg, S;
+};
+
+__global__ __launch_bounds__(64) void k_offsets_scan(ScanArgs a) {
+  const int s = blockIdx.x, lane = threadIdx.x;
+  uint64_t run = 0;
+  for (int b0 = 0; b0 < a.n_seg; b0 += 64) {
+    const int i = b0 + lane;
+    kvc_seg_desc* d = a.desc + (uint64_t)s * a.dstride + i;
+    const uint32_t by = (i < a.n_seg) ? seg_bytes(d->n_tok, d->n_ch, a.S) : 0u;
+    uint32_t inc = by;
+    for (int m = 1; m < 64; m <<= 1) {
+      const uint32_t o = __shfl_up(inc, m, 64);
+      if (lane >= m) inc += o;
+    }
+    if (i < a.n_seg) d->offset = a.pbase + (uint64_t)s * a.pstride + run + (inc - by);
+    run += __shfl(inc, 63, 64);
+  }
+  if (lane == 0 && a.used) a.used[s] = run;
+}
+
+// ---------------------------------------------------------------------------
+// Pack: one block per segment.
+// ---------------------------------------------------------------------------
+struct PackArgs {
+  const uint16_t* K;
+  const uint16_t* V;
+  const uint32_t* masks;
+  const uint32_t* keep;
+  const kvc_seg_desc* desc;
+  uint8_t* packed;
+  uint64_t kv_stride, pstride, pbase;
+  uint32_t dstride;
+  int region_begin, region_len, S, n_seg, nc;
+  int su[KVC_MAX_STRATEGIES];
+};
+
+__global__ __launch_bounds__(256) void k_pack(PackArgs a) {
+  const int sg = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const kvc_seg_desc d = a.desc[(uint64_t)s * a.dstride + sg];
+  const int T = d.n_tok, c = d.n_ch, S = a.S;
+  if (T == 0) return;
+  const uint64_t local = d.offset - a.pbase - (uint64_t)s * a.pstride;
+  uint8_t* out = a.packed + (uint64_t)s * a.pstride + local;
+  __shared__ uint16_t s_idx[256];
+  if (wv == 0) {
+    const int nw = (S + 31) / 32;
+    const uint32_t* kw = a.keep + ((uint64_t)s * a.n_seg + sg) * nw;
+    uint32_t before = 0;
+    for (int j = 0; j * 64 < S; ++j) {
+      const int t = 64 * j + lane;
+      const bool on = t < S && ((kw[t >> 5] >> (t & 31)) & 1u);
+      const uint64_t bal = __ballot(on);
+      if (on) s_idx[before + lanes_below(bal)] = (uint16_t)t;
+      before += (uint32_t)__popcll(bal);
+    }
+  }
+  __syncthreads();
+  const bool hasmask = c < D;
+  const int u = a.su[d.strategy];
+  const uint32_t kmask = 0, kval = hasmask ? 16u * T : 0u;
+  const uint32_t vmask = kval + 2u * T * c, vval = vmask + (hasmask ? 16u * T : 0u);
+  const uint32_t idxo = vval + 2u * T * c;
+  for (int part = 0; part < 2; ++part) {
+    const uint16_t* X = part ? a.V : a.K;
+    const uint32_t mo = part ? vmask : kmask, vo = part ? vval : kval;
+    if (hasmask) {
+      for (int j = tid; j < T; j += 256) {
+        const uint64_t o = (((uint64_t)s * a.region_len + sg * S + s_idx[j]) * a.nc + u) * 2 + part;
+        reinterpret_cast<uint4*>(out + mo)[j] = reinterpret_cast<const uint4*>(a.masks)[o];
+      }
+    }
+    for (int j = wv; j < T; j += 4) {
+      const int tr = sg * S + s_idx[j];
+      const uint16_t* row = X + (uint64_t)s * a.kv_stride + (uint64_t)(a.region_begin + tr) * D;
+      uint16_t* ov = reinterpret_cast<uint16_t*>(out + vo) + (uint64_t)j * c;
+      if (!hasmask) {
+        ov[lane] = row[lane];
+        ov[lane + 64] = row[lane + 64];
+      } else {
+        const uint64_t o = (((uint64_t)s * a.region_len + tr) * a.nc + u) * 2 + part;
+        const uint4 w = reinterpret_cast<const uint4*>(a.masks)[o];
+        const uint64_t lo = (uint64_t)w.x | ((uint64_t)w.y << 32);
+        const uint64_t hi = (uint64_t)w.z | ((uint64_t)w.w << 32);
+        if ((lo >> lane) & 1u) ov[lanes_below(lo)] = row[lane];
+        if ((hi >> lane) & 1u) ov[(uint32_t)__popcll(lo) + lanes_below(hi)] = row[lane + 64];
+      }
+    }
+  }
+  if (T < S) {
+    const uint32_t nidx = ((2u * T + 15u) / 16u) * 8u;  // u16 slots incl. padding
+    uint16_t* oi = reinterpret_cast<uint16_t*>(out + idxo);
+    for (uint32_t j = tid; j < nidx; j += 256) oi[j] = j < (uint32_t)T ? s_idx[j] : (uint16_t)0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
+  if (p.scoring) {
+    ScoreArgs sa;
+    sa.K = p.K;
+    sa.Qw = p.Qw;
+    sa.part_m = p.part_m;
+    sa.part_z = p.part_z;
+    sa.norm_m = p.norm_m;
+    sa.norm_iz = p.norm_iz;
+    sa.scores = p.scores;
+    sa.scores_out = p.scores_out;
+    sa.kv_stride = p.kv_stride;
+    sa.qw_stride = p.qw_stride;
+    sa.hkv = p.hkv;
+    sa.hq = p.hq;
+    sa.G = p.G;
+    sa.W = p.W;
+    sa.nq = p.nq;
+    sa.nblk = p.nblk;
+    sa.region_begin = p.region_begin;
+    sa.region_len = p.region_len;
+    sa.scale = p.scale;
+    hipLaunchKernelGGL(k_score_partials, dim3(p.nblk, p.streams), dim3(64), 0, st, sa);
+    hipLaunchKernelGGL(k_score_normalise, dim3(p.nq, p.streams), dim3(64), 0, st, sa);
+    hipLaunchKernelGGL(k_token_scores, dim3((p.region_len + 63) / 64, p.streams), dim3(64), 0, st, sa);
+  }
+  if (p.nc > 0) {
+    SelectArgs se;
+    se.K = p.K;
+    se.V = p.V;
+    se.masks = p.masks;
+    se.rho = p.rho;
+    se.kv_stride = p.kv_stride;
+    se.region_begin = p.region_begin;
+    se.region_len = p.region_len;
+    se.nc = p.nc;
+    for (int i = 0; i < MAX_NC; ++i) se.cvals[i] = p.cvals[i];
+    hipLaunchKernelGGL(k_channel_select, dim3((p.region_len + SEL_TOKENS - 1) / SEL_TOKENS, p.streams),
+                       dim3(256), 0, st, se);
+  }
+  ChooseArgs ca;
+  ca.scores = p.scores;
+  ca.rho = p.rho;
+  ca.forced = p.forced;
+  ca.desc = p.desc;
+  ca.keep = p.keep;
+  ca.objective = p.objective;
+  ca.region_len = p.region_len;
+  ca.S = p.S;
+  ca.n_seg = p.n_seg;
+  ca.nc = p.nc;
+  ca.n_strat = p.n_strat;
+  ca.t2c_alpha = p.t2c_alpha;
+  ca.t2c_gamma = p.t2c_gamma;
+  ca.dstride = p.dstride;
+  ca.feasible_mask = p.feasible_mask;
+  ca.have_scores = p.scoring;
+  for (int i = 0; i < KVC_MAX_STRATEGIES; ++i) {
+    ca.sT[i] = p.sT[i];
+    ca.sc[i] = p.sc[i];
+    ca.su[i] = p.su[i];
+  }
+  hipLaunchKernelGGL(k_segment_choose, dim3(p.n_seg, p.streams), dim3(64), 0, st, ca);
+  ScanArgs sc;
+  sc.desc = p.desc;
+  sc.used = p.used;
+  sc.pstride = p.pstride;
+  sc.pbase = p.pbase;
+  sc.dstride = p.dstride;
+  sc.n_seg = p.n_seg;
+  sc.S = p.S;
+  hipLaunchKernelGGL(k_offsets_scan, dim3(p.streams), dim3(64), 0, st, sc);
+  PackArgs pa;
+  pa.K = p.K;
+  pa.V = p.V;
+  pa.masks = p.masks;
+  pa.keep = p.keep;
+  pa.desc = p.desc;
+  pa.packed = p.packed;
+  pa.kv_stride = p.kv_stride;
+  pa.pstride = p.pstride;
+  pa.pbase = p.pbase;
+  pa.dstride = p.dstride;
+  pa.region_begin = p.region_begin;
+  pa.region_len = p.region_len;
+  pa.S = p.S;
+  pa.n_seg = p.n_seg;
+  pa.nc = p.nc;
+  for (int i = 0; i < KVC_MAX_STRATEGIES; ++i) pa.su[i] = p.su[i];
+  hipLaunchKernelGGL(k_pack, dim3(p.n_seg, p.streams), dim3(256), 0, st, pa);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

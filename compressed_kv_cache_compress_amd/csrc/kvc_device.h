@@ -1,0 +1,72 @@
+// kvc_device.h -- device helpers for the gfx950 kernels: bf16 bit handling,
+// the specified fp32 exp2, and wave64 reductions whose summation order is the
+// pairwise tree (adjacent pairs first) used throughout the selection path.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace kvc {
+
+__device__ __forceinline__ float bf2f(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// log2(e) rounded to fp32.
+#define KVC_LOG2E 0x1.715476p+0f
+
+// 2^y for y <= 0 from the Taylor series of e^(f ln 2) truncated after the
+// degree-7 term (coefficients ln2^k / k! rounded to fp32), evaluated by Horner
+// with fused multiply-adds after the split y = n + f, n = rint(y), |f| <= 1/2.
+// Below -125 the result is +0, so no result is subnormal.  Every operation is
+// a correctly rounded IEEE fp32 operation, so the value is reproducible on any
+// IEEE machine that evaluates the same sequence.
+__device__ __forceinline__ float spec_exp2(float y) {
+  if (!(y >= -125.0f)) return 0.0f;
+  const float n = __builtin_rintf(y);
+  const float f = y - n;
+  float p = 0x1.ffcbfcp-17f;
+  p = __builtin_fmaf(p, f, 0x1.430912p-13f);
+  p = __builtin_fmaf(p, f, 0x1.5d87fep-10f);
+  p = __builtin_fmaf(p, f, 0x1.3b2ab6p-7f);
+  p = __builtin_fmaf(p, f, 0x1.c6b08ep-5f);
+  p = __builtin_fmaf(p, f, 0x1.ebfbe0p-3f);
+  p = __builtin_fmaf(p, f, 0x1.62e430p-1f);
+  p = __builtin_fmaf(p, f, 1.0f);
+  return __builtin_ldexpf(p, (int)n);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Sum over `width` consecutive lanes (a power of two <= 64) in pairwise-tree
+// order: lanes 2i and 2i+1 first, then pairs of pairs, ...  IEEE addition is
+// commutative, so every lane of the group ends with the same bits.
+__device__ __forceinline__ float tree_sum_lanes(float v, int width = 64) {
+  for (int m = 1; m < width; m <<= 1) v = v + shfl_xor_f(v, m);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  return v;
+}
+
+// Count of set bits of a 64-bit lane mask below the calling lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Packed bytes of one segment (layout in kvc.h).
+__host__ __device__ __forceinline__ uint32_t seg_bytes(uint32_t T, uint32_t c, uint32_t S) {
+  if (T == 0) return 0;
+  const uint32_t mk = (c < 128) ? 16u * T : 0u;
+  const uint32_t vals = 2u * T * c;
+  const uint32_t idx = (T < S) ? ((2u * T + 15u) / 16u) * 16u : 0u;
+  return 2u * mk + 2u * vals + idx;
+}
+
+}  // namespace kvc

@@ -1,0 +1,297 @@
+// kvc_host.cpp -- host side of libkvc: argument validation, byte costs and
+// feasible strategies, workspace carve-up, split-K sizing, kernel launches.
+// No device memory is allocated and no call synchronises.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "kvc_device.h"
+#include "kvc_internal.h"
+
+namespace {
+
+using namespace kvc;
+
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+bool pow2(uint32_t x) { return x && !(x & (x - 1)); }
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Shape {
+  int batch, hq, hkv, G, streams;
+};
+
+kvc_status check_shape(const kvc_params* p, Shape* s) {
+  if (!p || p->struct_size != sizeof(kvc_params)) return KVC_E_INVALID;
+  if (p->head_dim != KVC_HEAD_DIM) return KVC_E_UNSUPPORTED;
+  if (p->batch == 0 || p->n_q_heads == 0 || p->n_kv_heads == 0) return KVC_E_INVALID;
+  if (p->n_q_heads % p->n_kv_heads) return KVC_E_INVALID;
+  const uint32_t G = p->n_q_heads / p->n_kv_heads;
+  if (G > 16) return KVC_E_UNSUPPORTED;
+  if ((uint64_t)p->batch * p->n_q_heads > (1u << 24)) return KVC_E_UNSUPPORTED;
+  if ((uint64_t)p->batch * p->n_kv_heads > 65535u) return KVC_E_UNSUPPORTED;  // grid.y
+  s->batch = (int)p->batch;
+  s->hq = (int)p->n_q_heads;
+  s->hkv = (int)p->n_kv_heads;
+  s->G = (int)G;
+  s->streams = (int)(p->batch * p->n_kv_heads);
+  return KVC_OK;
+}
+
+float eff_scale(const kvc_params* p) {
+  return p->scale != 0.0f ? p->scale : (float)(1.0 / std::sqrt((double)p->head_dim));
+}
+
+// Fills the compression part of the layout.  Returns KVC_E_BUDGET when no
+// strategy fits (layout still filled).
+kvc_status compress_layout(const kvc_params* p, const Shape& sh, kvc_layout* L, int* nc_out,
+                           int* cvals, int* su) {
+  if (p->n_strategies == 0 || p->n_strategies > KVC_MAX_STRATEGIES || !p->strategies)
+    return KVC_E_INVALID;
+  const uint32_t S = p->seg_tokens;
+  if (!pow2(S) || S < 16 || S > 256) return KVC_E_INVALID;
+  if (p->n_ctx == 0 || p->n_ctx % BLK || p->n_ctx > (1u << 22)) return KVC_E_INVALID;
+  if (p->region_len == 0 || p->region_len % S) return KVC_E_INVALID;
+  if ((uint64_t)p->region_begin + p->region_len > p->n_ctx) return KVC_E_INVALID;
+  int nc = 0;
+  bool t2c_used = false;
+  uint32_t feas = 0, nfeas = 0;
+  uint64_t maxb = 0;
+  bool partial = false;
+  for (uint32_t i = 0; i < p->n_strategies; ++i) {
+    const kvc_strategy& st = p->strategies[i];
+    if (st.n_tok > S) return KVC_E_INVALID;
+    if (st.n_tok > 0) {
+      if (st.n_ch < 8 || st.n_ch > KVC_HEAD_DIM || st.n_ch % 8) return KVC_E_INVALID;
+      if (st.n_tok < S) {
+        t2c_used = true;
+        if (p->t2c_alpha > 0 && p->t2c_alpha >= st.n_tok) return KVC_E_INVALID;
+      }
+    }
+    su[i] = 0;
+    if (st.n_tok > 0 && st.n_ch < KVC_HEAD_DIM) {
+      int u = 0;
+      while (u < nc && cvals[u] != st.n_ch) ++u;
+      if (u == nc) {
+        if (nc == MAX_NC) return KVC_E_UNSUPPORTED;
+        cvals[nc++] = st.n_ch;
+      }
+      su[i] = u;
+    }
+    const uint32_t by = seg_bytes(st.n_tok, st.n_tok ? st.n_ch : 0, S);
+    L->seg_bytes[i] = by;
+    if (by <= p->budget_bytes) {
+      feas |= 1u << i;
+      ++nfeas;
+      if (by > maxb) maxb = by;
+      if (st.n_tok > 0 && st.n_tok < S) partial = true;
+    }
+  }
+  if (p->t2c_alpha > 0 && t2c_used && p->t2c_gamma < 2) return KVC_E_INVALID;
+  *nc_out = nc;
+  const uint64_t n_seg = p->region_len / S;
+  L->feasible_mask = feas;
+  L->n_seg = (uint32_t)n_seg;
+  L->max_seg_bytes = maxb;
+  L->stream_capacity = align_up(n_seg * maxb, kAlign);
+  L->packed_bytes_max = (uint64_t)sh.streams * L->stream_capacity;
+  L->n_desc = (uint64_t)sh.streams * n_seg;
+  L->needs_scoring = (partial || nfeas > 1) ? 1u : 0u;
+  if (L->needs_scoring && p->n_win == 0) return KVC_E_INVALID;
+  // workspace: partials, normalisers, scores, masks, energy shares, keep bits
+  const uint64_t nq = (uint64_t)sh.G * (p->n_win ? p->n_win : 1);
+  const uint64_t nblk = p->n_ctx / BLK;
+  uint64_t ws = 0;
+  ws += 2 * align_up((uint64_t)sh.streams * nq * nblk * 4, kAlign);
+  ws += 2 * align_up((uint64_t)sh.streams * nq * 4, kAlign);
+  ws += align_up((uint64_t)sh.streams * p->region_len * 4, kAlign);
+  ws += align_up((uint64_t)sh.streams * p->region_len * (uint64_t)nc * 2 * 16, kAlign);
+  ws += align_up((uint64_t)sh.streams * p->region_len * (uint64_t)nc * 2 * 4, kAlign);
+  ws += align_up((uint64_t)sh.streams * n_seg * ((S + 31) / 32) * 4, kAlign);
+  L->compress_ws_bytes = ws;
+  return nfeas ? KVC_OK : KVC_E_BUDGET;
+}
+
+uint32_t choose_splits(const kvc_params* p, const Shape& sh, uint32_t maxd) {
+  if (p->decode_splits) return p->decode_splits;
+  // about 8 waves per CU on 256 CUs, at least one descriptor per split
+  uint32_t want = (2048u + (uint32_t)sh.streams - 1) / (uint32_t)sh.streams;
+  if (want > maxd) want = maxd;
+  if (want < 1) want = 1;
+  if (want > 1024) want = 1024;
+  return want;
+}
+
+void decode_layout(const kvc_params* p, const Shape& sh, uint32_t maxd, kvc_layout* L) {
+  const uint32_t splits = choose_splits(p, sh, maxd ? maxd : 1);
+  L->decode_splits = splits;
+  const uint64_t rows = (uint64_t)sh.batch * sh.hq * splits;
+  L->decode_ws_bytes = align_up(rows * 2 * 4, kAlign) + align_up(rows * KVC_HEAD_DIM * 4, kAlign);
+}
+
+uint32_t decode_maxd(const kvc_params* p) {
+  if (p->max_desc_per_stream) return p->max_desc_per_stream;
+  if (p->seg_tokens && p->region_len) return p->region_len / p->seg_tokens;
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+const char* kvc_status_str(kvc_status s) {
+  switch (s) {
+    case KVC_OK: return "ok";
+    case KVC_E_INVALID: return "invalid argument";
+    case KVC_E_UNSUPPORTED: return "unsupported configuration";
+    case KVC_E_BUDGET: return "no strategy fits the byte budget";
+    case KVC_E_WORKSPACE: return "workspace too small";
+    case KVC_E_ALIGN: return "pointer not 16-byte aligned";
+    case KVC_E_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+kvc_status kv_layout_query(const kvc_params* p, kvc_layout* out) {
+  if (!out) return KVC_E_INVALID;
+  std::memset(out, 0, sizeof(*out));
+  Shape sh;
+  kvc_status st = check_shape(p, &sh);
+  if (st != KVC_OK) return st;
+  kvc_status cs = KVC_OK;
+  if (p->n_strategies > 0) {
+    int nc, cvals[MAX_NC], su[KVC_MAX_STRATEGIES];
+    cs = compress_layout(p, sh, out, &nc, cvals, su);
+    if (cs != KVC_OK && cs != KVC_E_BUDGET) return cs;
+  }
+  const uint32_t maxd = decode_maxd(p);
+  if (maxd) decode_layout(p, sh, maxd, out);
+  else if (p->n_strategies == 0) return KVC_E_INVALID;
+  return cs;
+}
+
+kvc_status kv_compress(const kvc_params* p, const uint16_t* K, const uint16_t* V,
+                       const uint16_t* Qwin, const uint8_t* forced_strategy, void* packed,
+                       kvc_seg_desc* desc, uint64_t* used_bytes, float* scores, float* objective,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  Shape sh;
+  kvc_status st = check_shape(p, &sh);
+  if (st != KVC_OK) return st;
+  kvc_layout L;
+  std::memset(&L, 0, sizeof L);
+  CompressPlan c;
+  std::memset(&c, 0, sizeof c);
+  st = compress_layout(p, sh, &L, &c.nc, c.cvals, c.su);
+  if (st != KVC_OK) return st;
+  const bool scoring = L.needs_scoring || scores || objective;
+  if (!K || !V || !packed || !desc || (scoring && !Qwin)) return KVC_E_INVALID;
+  if (!aligned16(K) || !aligned16(V) || !aligned16(Qwin) || !aligned16(packed) ||
+      !aligned16(desc) || !aligned16(ws))
+    return KVC_E_ALIGN;
+  if (p->packed_base_offset % 16 || (p->packed_stream_stride && p->packed_stream_stride % 16))
+    return KVC_E_ALIGN;
+  if (p->kv_stream_stride % 8 || p->qw_head_stride % 8) return KVC_E_ALIGN;
+  if (ws_bytes < L.compress_ws_bytes || (L.compress_ws_bytes && !ws)) return KVC_E_WORKSPACE;
+  const uint64_t pstride = p->packed_stream_stride ? p->packed_stream_stride : L.stream_capacity;
+  if (pstride < L.n_seg * L.max_seg_bytes) return KVC_E_INVALID;
+  const uint32_t dstride = p->desc_stream_stride ? p->desc_stream_stride : L.n_seg;
+  if (dstride < L.n_seg) return KVC_E_INVALID;
+
+  c.batch = sh.batch;
+  c.hq = sh.hq;
+  c.hkv = sh.hkv;
+  c.G = sh.G;
+  c.streams = sh.streams;
+  c.n_ctx = (int)p->n_ctx;
+  c.region_begin = (int)p->region_begin;
+  c.region_len = (int)p->region_len;
+  c.S = (int)p->seg_tokens;
+  c.W = (int)(p->n_win ? p->n_win : 1);
+  c.nq = c.G * c.W;
+  c.nblk = (int)(p->n_ctx / BLK);
+  c.n_seg = (int)L.n_seg;
+  c.scale = eff_scale(p);
+  c.kv_stride = p->kv_stream_stride ? p->kv_stream_stride : (uint64_t)p->n_ctx * KVC_HEAD_DIM;
+  c.qw_stride = p->qw_head_stride ? p->qw_head_stride : (uint64_t)c.W * KVC_HEAD_DIM;
+  c.pstride = pstride;
+  c.pbase = p->packed_base_offset;
+  c.dstride = dstride;
+  c.n_strat = (int)p->n_strategies;
+  for (uint32_t i = 0; i < p->n_strategies; ++i) {
+    c.sT[i] = p->strategies[i].n_tok;
+    c.sc[i] = p->strategies[i].n_tok ? p->strategies[i].n_ch : 0;
+  }
+  c.feasible_mask = L.feasible_mask;
+  c.t2c_alpha = (int)p->t2c_alpha;
+  c.t2c_gamma = (int)p->t2c_gamma;
+  c.scoring = scoring;
+  c.K = K;
+  c.V = V;
+  c.Qw = Qwin;
+  c.forced = forced_strategy;
+  c.packed = static_cast<uint8_t*>(packed);
+  c.desc = desc;
+  c.used = used_bytes;
+  c.scores_out = scores;
+  c.objective = objective;
+  // workspace carve-up (same order and sizes as compress_layout)
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  auto take = [&](uint64_t bytes) {
+    uint8_t* r = w;
+    w += align_up(bytes, kAlign);
+    return r;
+  };
+  const uint64_t S64 = (uint64_t)c.streams;
+  c.part_m = reinterpret_cast<float*>(take(S64 * c.nq * c.nblk * 4));
+  c.part_z = reinterpret_cast<float*>(take(S64 * c.nq * c.nblk * 4));
+  c.norm_m = reinterpret_cast<float*>(take(S64 * c.nq * 4));
+  c.norm_iz = reinterpret_cast<float*>(take(S64 * c.nq * 4));
+  c.scores = reinterpret_cast<float*>(take(S64 * c.region_len * 4));
+  c.masks = reinterpret_cast<uint32_t*>(take(S64 * c.region_len * (uint64_t)c.nc * 2 * 16));
+  c.rho = reinterpret_cast<float*>(take(S64 * c.region_len * (uint64_t)c.nc * 2 * 4));
+  c.keep = reinterpret_cast<uint32_t*>(take(S64 * c.n_seg * ((c.S + 31) / 32) * 4));
+  if (launch_compress(c, stream) != hipSuccess) return KVC_E_HIP;
+  return KVC_OK;
+}
+
+kvc_status kv_attend_decode(const kvc_params* p, const uint16_t* q, const void* packed,
+                            const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
+                            uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  Shape sh;
+  kvc_status st = check_shape(p, &sh);
+  if (st != KVC_OK) return st;
+  const uint32_t maxd = decode_maxd(p);
+  if (maxd == 0 || !q || !out || !desc || !packed) return KVC_E_INVALID;
+  if (!aligned16(q) || !aligned16(packed) || !aligned16(desc) || !aligned16(out) || !aligned16(ws))
+    return KVC_E_ALIGN;
+  kvc_layout L;
+  std::memset(&L, 0, sizeof L);
+  decode_layout(p, sh, maxd, &L);
+  if (ws_bytes < L.decode_ws_bytes || !ws) return KVC_E_WORKSPACE;
+  DecodePlan d;
+  d.batch = sh.batch;
+  d.hq = sh.hq;
+  d.hkv = sh.hkv;
+  d.G = sh.G;
+  d.streams = sh.streams;
+  d.maxd = (int)maxd;
+  d.splits = (int)L.decode_splits;
+  d.scale = eff_scale(p);
+  d.q = q;
+  d.packed = static_cast<const uint8_t*>(packed);
+  d.desc = desc;
+  d.n_desc = n_desc_per_stream;
+  d.out = out;
+  d.lse = lse;
+  const uint64_t rows = (uint64_t)sh.batch * sh.hq * d.splits;
+  d.part_ml = static_cast<float*>(ws);
+  d.part_acc = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up(rows * 2 * 4, kAlign));
+  if (launch_decode(d, stream) != hipSuccess) return KVC_E_HIP;
+  return KVC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// kvc_internal.h -- launch interface between the host planner (kvc_host.cpp)
+// and the gfx950 kernels (kvc_compress.hip, kvc_decode.hip).  Not installed.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+#include <hip/hip_runtime.h>
+
+#include "../../include/kvc.h"
+
+namespace kvc {
+
+constexpr int D = KVC_HEAD_DIM;
+constexpr int BLK = 64;        // tokens per normalisation partial block
+constexpr int MAX_NC = 8;      // distinct channel counts below 128 per table
+
+// Everything the compress kernels need, resolved on the host.
+struct CompressPlan {
+  // shapes
+  int batch, hq, hkv, G, n_ctx, region_begin, region_len, S, W, nq, nblk, n_seg, streams;
+  float scale;
+  uint64_t kv_stride, qw_stride, pstride, pbase;
+  uint32_t dstride;
+  // strategy table
+  int n_strat;
+  int sT[KVC_MAX_STRATEGIES], sc[KVC_MAX_STRATEGIES], su[KVC_MAX_STRATEGIES];
+  uint32_t feasible_mask;
+  int nc;                 // distinct channel counts < 128
+  int cvals[MAX_NC];
+  int t2c_alpha, t2c_gamma;
+  bool scoring;           // run the window-scoring kernels
+  // inputs / outputs
+  const uint16_t *K, *V, *Qw;
+  const uint8_t* forced;
+  uint8_t* packed;
+  kvc_seg_desc* desc;
+  uint64_t* used;
+  float* scores_out;
+  float* objective;
+  // workspace carve-up (device pointers)
+  float *part_m, *part_z, *norm_m, *norm_iz, *scores, *rho;
+  uint32_t* masks;        // [streams][region_len][nc][2][4]
+  uint32_t* keep;         // [streams][n_seg][S/32]
+};
+
+struct DecodePlan {
+  int batch, hq, hkv, G, streams, maxd, splits;
+  float scale;
+  const uint16_t* q;
+  const uint8_t* packed;
+  const kvc_seg_desc* desc;
+  const uint32_t* n_desc;
+  uint16_t* out;
+  float* lse;
+  float *part_ml, *part_acc;
+};
+
+hipError_t launch_compress(const CompressPlan& p, hipStream_t st);
+hipError_t launch_decode(const DecodePlan& p, hipStream_t st);
+
+}  // namespace kvc

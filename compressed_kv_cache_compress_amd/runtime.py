@@ -1,0 +1,101 @@
+"""Convenience layer over the C ABI: allocates outputs and workspaces with
+torch on the current device and calls kv_compress / kv_attend_decode.
+
+All computation happens in libkvc's HIP kernels; nothing here touches the
+data except to allocate it.
+"""
+import torch
+
+from . import (DESC_DTYPE, KvParams, kv_attend_decode, kv_compress, kv_layout_query)
+
+
+def _u8(n, device):
+    return torch.empty(max(int(n), 16), dtype=torch.uint8, device=device)
+
+
+def _as_u16(t):
+    assert t.dtype == torch.bfloat16 and t.is_cuda, (t.dtype, t.device)
+    return t
+
+
+class Compressed:
+    """Result of compress(): packed bytes, descriptors and optional outputs."""
+
+    def __init__(self, params, layout, packed, desc, used, scores, objective):
+        self.params, self.layout = params, layout
+        self.packed, self.desc, self.used = packed, desc, used
+        self.scores, self.objective = scores, objective
+
+    @property
+    def n_seg(self):
+        return self.layout.n_seg
+
+    def desc_host(self):
+        return self.desc.cpu().numpy().view(DESC_DTYPE).reshape(self.params.streams, -1)
+
+
+def compress_params(*, batch, n_q_heads, n_kv_heads, n_ctx, seg_tokens, n_win, strategies,
+                    budget_bytes, **kw):
+    return KvParams(batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, n_ctx=n_ctx,
+                    seg_tokens=seg_tokens, n_win=n_win, strategies=strategies,
+                    budget_bytes=budget_bytes, **kw)
+
+
+def compress(K, V, Qw, *, seg_tokens, strategies, budget_bytes, region_begin=0, region_len=None,
+             t2c_alpha=0, t2c_gamma=0, scale=0.0, forced=None, want_scores=False,
+             want_objective=False, ws=None, packed=None, desc=None, n_ctx=None,
+             kv_stream_stride=0, qw_head_stride=0, packed_stream_stride=0, packed_base_offset=0,
+             desc_stream_stride=0, n_q_heads=None):
+    """K, V: [B, Hkv, N, 128] bf16 (or strided views described by the stride
+    arguments); Qw: [B, Hq, W, 128] bf16 or None."""
+    B, Hkv = K.shape[0], K.shape[1]
+    N = K.shape[2] if n_ctx is None else n_ctx
+    Hq = Qw.shape[1] if Qw is not None else (n_q_heads or Hkv)
+    W = Qw.shape[2] if Qw is not None else 0
+    p = KvParams(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, n_ctx=N, region_begin=region_begin,
+                 region_len=region_len, seg_tokens=seg_tokens, n_win=W, strategies=strategies,
+                 budget_bytes=budget_bytes, t2c_alpha=t2c_alpha, t2c_gamma=t2c_gamma, scale=scale,
+                 kv_stream_stride=kv_stream_stride, qw_head_stride=qw_head_stride,
+                 packed_stream_stride=packed_stream_stride,
+                 packed_base_offset=packed_base_offset, desc_stream_stride=desc_stream_stride)
+    _, L = kv_layout_query(p)
+    dev = K.device
+    streams = B * Hkv
+    dstride = desc_stream_stride or L.n_seg
+    if packed is None:
+        packed = _u8(L.packed_bytes_max, dev)
+    if desc is None:
+        desc = torch.zeros(streams * dstride * 16, dtype=torch.uint8, device=dev)
+    used = torch.zeros(streams, dtype=torch.int64, device=dev)
+    scores = torch.empty((streams, p.p.region_len), dtype=torch.float32, device=dev) if want_scores else None
+    objective = (torch.empty((streams, L.n_seg, len(strategies)), dtype=torch.float32, device=dev)
+                 if want_objective else None)
+    if ws is None or ws.numel() < L.compress_ws_bytes:
+        ws = _u8(L.compress_ws_bytes, dev)
+    kv_compress(p, _as_u16(K), _as_u16(V), Qw, forced, packed, desc, used, scores, objective, ws)
+    return Compressed(p, L, packed, desc, used, scores, objective)
+
+
+def decode_params(*, batch, n_q_heads, n_kv_heads, max_desc_per_stream, decode_splits=0,
+                  scale=0.0):
+    return KvParams(batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
+                    max_desc_per_stream=max_desc_per_stream, decode_splits=decode_splits,
+                    scale=scale)
+
+
+def decode(q, packed, desc, *, n_kv_heads, max_desc_per_stream, n_desc=None, decode_splits=0,
+           scale=0.0, want_lse=True, out=None, lse=None, ws=None, params=None):
+    """q: [B, Hq, 128] bf16 -> (out [B, Hq, 128] bf16, lse [B, Hq] fp32 or None)."""
+    B, Hq = q.shape[0], q.shape[1]
+    p = params or decode_params(batch=B, n_q_heads=Hq, n_kv_heads=n_kv_heads,
+                                max_desc_per_stream=max_desc_per_stream,
+                                decode_splits=decode_splits, scale=scale)
+    if ws is None:
+        _, L = kv_layout_query(p)
+        ws = _u8(L.decode_ws_bytes, q.device)
+    if out is None:
+        out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    kv_attend_decode(p, q, packed, desc, n_desc, out, lse, ws)
+    return out, lse

@@ -1,0 +1,213 @@
+/*
+ * kvc.h -- C ABI of libkvc: segment-wise two-dimensional KV-cache compression
+ * and decode attention over the compressed cache, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Method sources (review pages):
+ *  - "MosaicKV: Serving Long-Context LLM with Dynamic Two-D KV Cache
+ *    Compression" (arXiv 2607.00760): abstract (important elements of each KV
+ *    vector; a compression strategy chosen per KV segment), Fig. 5 caption
+ *    (segments and strategy generation), Fig. 6 caption (Stage-1 per-vector
+ *    top-r elements, packed KV format, flexible KV encoding, PackedAttention).
+ *  - "KARA: Efficient Reasoning LLM Serving via Sliding-Window KV Cache
+ *    Compression" (arXiv 2607.01237): "What carries the argument" (keys of a
+ *    recent window scored by the attention all window queries give them;
+ *    Token2Chunk), Fig. 3 caption (bidirectional: every query/key pair),
+ *    free-parameter ledger (retention, window, chunk budget alpha, max chunk
+ *    length gamma).
+ *
+ * Conventions for every entry point:
+ *  - Tensor arguments are DEVICE pointers (HIP global memory), 16-byte
+ *    aligned, owned by the caller.  bf16 tensors are uint16_t bit patterns.
+ *  - Work is enqueued on the caller's `stream`; nothing is synchronised and
+ *    the library never allocates or frees device memory.  All scratch space
+ *    comes from the caller's workspace `ws` (size from kv_layout_query).
+ *  - Arguments are validated on the host first; on any error nothing is
+ *    enqueued and the call returns a negative kvc_status.  Device faults
+ *    surface at the caller's next synchronisation.
+ *  - Inputs must be finite; results for NaN/Inf inputs are undefined (a
+ *    segment whose tokens are all dropped is never read, so its bytes may
+ *    hold anything).
+ *  - Calls on distinct streams with distinct buffers may run concurrently.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1
+#define KVC_HEAD_DIM 128
+#define KVC_MAX_STRATEGIES 32
+#define KVC_DESC_CHOOSE 0xFF      /* forced_strategy entry: let the library choose */
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_E_INVALID = -1,     /* malformed parameters */
+  KVC_E_UNSUPPORTED = -2, /* valid but not supported (head_dim != 128, ...) */
+  KVC_E_BUDGET = -3,      /* no strategy fits the per-segment byte budget */
+  KVC_E_WORKSPACE = -4,   /* workspace too small */
+  KVC_E_ALIGN = -5,       /* a pointer is not 16-byte aligned */
+  KVC_E_HIP = -6          /* a HIP launch failed */
+} kvc_status;
+
+/* One compression strategy: keep n_tok of the segment's S tokens and, of each
+ * kept K and V vector, its n_ch largest-magnitude channels.  n_tok in [0, S];
+ * n_ch in {8, 16, ..., 128} when n_tok > 0 (ignored when n_tok == 0). */
+typedef struct {
+  uint16_t n_tok;
+  uint16_t n_ch;
+} kvc_strategy;
+
+/* Shapes and knobs shared by every entry point.  Zero-initialise, set
+ * struct_size = sizeof(kvc_params), then fill what the call uses.
+ *
+ * Streams: one stream = one (batch entry b, kv head h), index b*n_kv_heads+h.
+ * K, V:  [batch][n_kv_heads][n_ctx][128] bf16 (stream stride kv_stream_stride
+ *        elements).  Qwin: [batch][n_q_heads][n_win][128] bf16 (row stride
+ *        qw_head_stride elements).  q heads h*G .. h*G+G-1 (G = n_q_heads /
+ *        n_kv_heads) belong to kv head h.
+ */
+typedef struct {
+  uint32_t struct_size;      /* == sizeof(kvc_params) (ABI guard) */
+  uint32_t batch;
+  uint32_t n_q_heads;
+  uint32_t n_kv_heads;       /* divides n_q_heads; G <= 16 */
+  uint32_t head_dim;         /* must be 128 */
+  /* --- compression (kv_compress) --- */
+  uint32_t n_ctx;            /* tokens per stream in the scoring domain; multiple of 64 */
+  uint32_t region_begin;     /* first token to compress (domain position) */
+  uint32_t region_len;       /* tokens to compress; multiple of seg_tokens */
+  uint32_t seg_tokens;       /* S: power of two in [16, 256] */
+  uint32_t n_win;            /* W: window queries per q head (>= 1) */
+  const kvc_strategy* strategies; /* HOST array; index order is the tie-break order */
+  uint32_t n_strategies;     /* 1 .. KVC_MAX_STRATEGIES */
+  uint32_t budget_bytes;     /* per-segment cap on packed bytes */
+  uint32_t t2c_alpha;        /* Token2Chunk budget (0 = plain top-T) */
+  uint32_t t2c_gamma;        /* Token2Chunk max chunk length (>= 2 when alpha > 0) */
+  float scale;               /* logit scale; 0 => (float)(1/sqrt(head_dim)) */
+  uint64_t kv_stream_stride; /* elements between streams of K and V; 0 => n_ctx*128 */
+  uint64_t qw_head_stride;   /* elements between q-head rows of Qwin; 0 => n_win*128 */
+  uint64_t packed_stream_stride; /* bytes between streams' packed slots; 0 => layout.stream_capacity */
+  uint64_t packed_base_offset;   /* added to every descriptor offset written */
+  uint32_t desc_stream_stride;   /* descriptors between streams; 0 => region_len/seg_tokens */
+  /* --- decode (kv_attend_decode) --- */
+  uint32_t max_desc_per_stream;  /* descriptor stride per stream for decode; 0 => region_len/seg_tokens */
+  uint32_t decode_splits;        /* split-K factor; 0 => library choice */
+  uint32_t reserved[4];
+} kvc_params;
+
+/* Segment descriptor (16 bytes), one per compressed segment.
+ * offset: byte offset of the segment's data from the packed base pointer.
+ * flags: bit0 = all S tokens kept (no index list), bit1 = all 128 channels
+ * kept (no masks), bit7 = a forced strategy was rejected (out of range or
+ * over budget) and the library chose instead. */
+typedef struct {
+  uint64_t offset;
+  uint16_t n_tok;
+  uint16_t n_ch;
+  uint8_t strategy;
+  uint8_t flags;
+  uint16_t seg_tokens;
+} kvc_seg_desc;
+
+/* Packed segment layout (MosaicKV Fig. 6 caption: packed KV format), parts
+ * in this order, each starting 16-byte aligned:
+ *   K masks  [n_tok] x 16 B   (only if n_ch < 128; channel c = byte c/8, bit c%8)
+ *   K values [n_tok][n_ch] bf16, kept channels in ascending order
+ *   V masks  [n_tok] x 16 B   (only if n_ch < 128)
+ *   V values [n_tok][n_ch] bf16
+ *   indices  [n_tok] u16 ascending, position in the segment (only if n_tok < S),
+ *            zero-padded to a multiple of 16 bytes.
+ * Decode never reads the index list. */
+
+typedef struct {
+  uint32_t seg_bytes[KVC_MAX_STRATEGIES]; /* packed bytes of one segment per strategy */
+  uint32_t feasible_mask;     /* bit i: strategy i fits budget_bytes */
+  uint32_t n_seg;             /* segments per stream in the region */
+  uint64_t max_seg_bytes;     /* largest feasible seg_bytes */
+  uint64_t stream_capacity;   /* n_seg * max_seg_bytes, rounded up to 256 */
+  uint64_t packed_bytes_max;  /* streams * stream_capacity */
+  uint64_t n_desc;            /* streams * n_seg */
+  uint64_t compress_ws_bytes; /* workspace for kv_compress */
+  uint64_t decode_ws_bytes;   /* workspace for kv_attend_decode */
+  uint32_t decode_splits;     /* split-K factor kv_attend_decode will use */
+  uint32_t needs_scoring;     /* 1 if kv_compress runs the window-scoring kernels */
+} kvc_layout;
+
+/* Host only (no device call).  Validates p and reports byte costs, feasible
+ * strategies, buffer and workspace sizes.  Returns KVC_E_BUDGET when no
+ * strategy fits budget_bytes (the layout is still filled). */
+kvc_status kv_layout_query(const kvc_params* p, kvc_layout* out);
+
+/* Compress the region of every stream (MosaicKV: dynamic two-D compression;
+ * Kara: a sliding window with Token2Chunk when t2c_alpha > 0).
+ *  1. Window scores: each of the G*n_win window queries of a stream attends
+ *     to all n_ctx keys (no mask); a region token's score is the sum of the
+ *     probabilities it receives.  (KARA, "What carries the argument";
+ *     Fig. 3 caption.)
+ *  2. Per K and V vector and per channel count used by the table: the top
+ *     n_ch channels by bf16 magnitude (ties to the lower channel) and the
+ *     share of the vector's energy they hold.  (MosaicKV Fig. 6, Stage-1.)
+ *  3. Per segment and strategy: top n_tok tokens by score (ties to the lower
+ *     position) or Token2Chunk; objective = kept score mass weighted by the
+ *     mean kept energy share; the best strategy within budget_bytes (ties to
+ *     the lower index), unless forced.  (MosaicKV abstract, Fig. 5 caption.)
+ *  4. Offsets (per-stream scan) and packing into the layout above.
+ * Arguments:
+ *  K, V              device, layout above.
+ *  Qwin              device [batch][n_q_heads][n_win][128]; may be NULL when
+ *                    layout.needs_scoring == 0.
+ *  forced_strategy   device [streams][n_seg] u8 or NULL; entry < n_strategies
+ *                    forces that strategy if it fits the budget (else flag
+ *                    bit7 and choose); KVC_DESC_CHOOSE lets the library choose.
+ *  packed            device, stream s writes at packed + s*packed_stream_stride.
+ *  desc              device [streams][desc_stream_stride] descriptors.
+ *  used_bytes        device [streams] u64: packed bytes written per stream; may be NULL.
+ *  scores            device [streams][region_len] fp32 or NULL.
+ *  objective         device [streams][n_seg][n_strategies] fp32 or NULL.
+ *  ws, ws_bytes      device workspace, >= layout.compress_ws_bytes.
+ * Every selection output (desc, masks, index lists, packed bytes) is a
+ * deterministic function of the inputs. */
+kvc_status kv_compress(const kvc_params* p, const uint16_t* K, const uint16_t* V,
+                       const uint16_t* Qwin, const uint8_t* forced_strategy, void* packed,
+                       kvc_seg_desc* desc, uint64_t* used_bytes, float* scores, float* objective,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Decode attention of one query per q head over every stream's compressed
+ * segments (MosaicKV Fig. 6 caption, PackedAttention): softmax over all kept
+ * tokens of the stream's descriptors; a dropped channel contributes 0 to
+ * q.k and to the output; fp32 accumulation.  Split-K over descriptors, then a
+ * log-sum-exp merge.
+ *  q                 device [batch][n_q_heads][128] bf16.
+ *  packed            device base that descriptor offsets index.
+ *  desc              device [streams][max_desc_per_stream].
+ *  n_desc_per_stream device [streams] u32 or NULL (= max_desc_per_stream each).
+ *  out               device [batch][n_q_heads][128] bf16 (RNE), overwritten;
+ *                    zero for a stream with no kept token.
+ *  lse               device [batch][n_q_heads] fp32 or NULL: natural-log
+ *                    softmax denominator including the max (-inf if empty).
+ *  ws, ws_bytes      device workspace, >= layout.decode_ws_bytes.
+ * Uses batch, n_q_heads, n_kv_heads, head_dim, scale, max_desc_per_stream
+ * and decode_splits of p. */
+kvc_status kv_attend_decode(const kvc_params* p, const uint16_t* q, const void* packed,
+                            const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
+                            uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Static description of a status code. */
+const char* kvc_status_str(kvc_status s);
+
+/* KVC_ABI_VERSION of the loaded library. */
+int kvc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

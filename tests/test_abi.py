@@ -1,0 +1,176 @@
+"""C-ABI library: loads, exports every declared entry point, host-side layout
+and validation (CPU only: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import compressed_kv_cache_compress_amd as kvc
+from compressed_kv_cache_compress_amd import gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(kvc?_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("kv_layout_query", "kv_compress", "kv_attend_decode", "kvc_status_str",
+              "kvc_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = kvc.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", kvc.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    for n in declared_functions():
+        assert n in exported, n
+        assert getattr(L, n) is not None
+    assert L.kvc_abi_version() == 1
+    assert L.kvc_status_str(-3) == b"no strategy fits the byte budget"
+
+
+def test_struct_sizes_match_header():
+    # kvc_params: 14 u32 + ptr + 5 u32 + f32 -> then u64 fields; layout of the
+    # Python mirror must equal the C struct (checked through offsets the C
+    # side relies on: 16-byte descriptor, pointer-aligned strategies).
+    assert ctypes.sizeof(kvc.Strategy) == 4
+    assert kvc.DESC_DTYPE.itemsize == 16
+    assert kvc.Params.strategies.offset % 8 == 0
+    assert kvc.Params.kv_stream_stride.offset % 8 == 0
+    p = kvc.KvParams(batch=1, n_q_heads=1, n_kv_heads=1, n_ctx=64, seg_tokens=64, n_win=1,
+                     strategies=[(64, 128)], budget_bytes=1 << 20)
+    st, L = kvc.kv_layout_query(p)
+    assert st == 0 and L.seg_bytes[0] == 64 * 512
+
+
+def _params(cfg, **kw):
+    c = gen.CONFIGS[cfg]
+    S = c["S"]
+    d = dict(batch=c["B"], n_q_heads=c["Hq"], n_kv_heads=c["Hkv"], n_ctx=c["N"], seg_tokens=S,
+             n_win=c["W"], strategies=gen.table9(S), budget_bytes=gen.budget_bytes(c["budget_pct"], S))
+    d.update(kw)
+    return kvc.KvParams(**d)
+
+
+@pytest.mark.parametrize("cfg", list(gen.CONFIGS))
+def test_layout_matches_oracle_byte_costs(cfg, O):
+    c = gen.CONFIGS[cfg]
+    p = _params(cfg)
+    st, L = kvc.kv_layout_query(p)
+    assert st == 0
+    S = c["S"]
+    budget = gen.budget_bytes(c["budget_pct"], S)
+    feas = 0
+    mx = 0
+    for i, (T, ch) in enumerate(gen.table9(S)):
+        b = O.seg_bytes(T, ch, S)
+        assert L.seg_bytes[i] == b
+        if b <= budget:
+            feas |= 1 << i
+            mx = max(mx, b)
+    assert L.feasible_mask == feas and L.max_seg_bytes == mx
+    assert L.n_seg == c["N"] // S and L.needs_scoring == 1
+    streams = c["B"] * c["Hkv"]
+    assert L.packed_bytes_max == streams * L.stream_capacity >= streams * L.n_seg * mx
+    assert L.packed_bytes_max <= 0.34 * streams * c["N"] * 512
+    assert L.decode_splits >= 1 and L.decode_ws_bytes > 0 and L.compress_ws_bytes > 0
+
+
+def test_layout_errors():
+    st, _ = kvc.kv_layout_query(_params("tiny", head_dim=64), check=False)
+    assert st == -2
+    st, _ = kvc.kv_layout_query(_params("tiny", seg_tokens=48), check=False)
+    assert st == -1
+    st, _ = kvc.kv_layout_query(_params("tiny", region_len=100), check=False)
+    assert st == -1
+    st, _ = kvc.kv_layout_query(_params("tiny", budget_bytes=100), check=False)
+    assert st == -3
+    st, _ = kvc.kv_layout_query(_params("tiny", strategies=[(64, 12)]), check=False)
+    assert st == -1
+    st, _ = kvc.kv_layout_query(_params("tiny", n_kv_heads=3), check=False)
+    assert st == -1
+    st, _ = kvc.kv_layout_query(_params("llama8b", t2c_alpha=40, t2c_gamma=8), check=False)
+    assert st == -1  # alpha must stay below every partial token count (32)
+    p = _params("tiny")
+    p.p.struct_size -= 4
+    st, _ = kvc.kv_layout_query(p, check=False)
+    assert st == -1
+
+
+def test_keep_all_needs_no_scoring():
+    p = kvc.KvParams(batch=2, n_q_heads=8, n_kv_heads=2, n_ctx=1024, seg_tokens=256,
+                     strategies=[(256, 128)], budget_bytes=4 * 256 * 128)
+    st, L = kvc.kv_layout_query(p)
+    assert st == 0 and L.needs_scoring == 0 and L.stream_capacity == 1024 * 512
+
+
+def test_decode_only_layout():
+    p = kvc.KvParams(batch=4, n_q_heads=32, n_kv_heads=8, max_desc_per_stream=100)
+    st, L = kvc.kv_layout_query(p)
+    assert st == 0 and L.decode_splits >= 1
+    assert L.decode_ws_bytes >= 4 * 32 * L.decode_splits * 130 * 4
+
+
+class _Fake:
+    """Stand-in tensor exposing only a device address; validation rejects the
+    call before any kernel could touch it."""
+
+    def __init__(self, addr, n=1 << 30):
+        self.addr, self.n = addr, n
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return 1
+
+
+def test_compress_validates_before_launch(monkeypatch):
+    monkeypatch.setattr(kvc, "_stream", lambda: ctypes.c_void_p(0))
+    p = _params("tiny")
+    a = _Fake(0x10000)
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_compress(p, None, a, a, None, a, a, None, None, None, a)
+    assert e.value.status == -1
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_compress(p, _Fake(0x10008), a, a, None, a, a, None, None, None, a)
+    assert e.value.status == -5
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_compress(p, a, a, a, None, a, a, None, None, None, _Fake(0x10000, 16))
+    assert e.value.status == -4
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_compress(_params("tiny", budget_bytes=10), a, a, a, None, a, a, None, None, None, a)
+    assert e.value.status == -3
+
+
+def test_decode_validates_before_launch(monkeypatch):
+    monkeypatch.setattr(kvc, "_stream", lambda: ctypes.c_void_p(0))
+    p = kvc.KvParams(batch=1, n_q_heads=4, n_kv_heads=1, max_desc_per_stream=8)
+    a = _Fake(0x20000)
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_attend_decode(p, a, a, a, None, a, None, _Fake(0x20000, 8))
+    assert e.value.status == -4
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_attend_decode(p, _Fake(0x20004), a, a, None, a, None, a)
+    assert e.value.status == -5
+    p0 = kvc.KvParams(batch=1, n_q_heads=4, n_kv_heads=1)
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_attend_decode(p0, a, a, a, None, a, None, a)
+    assert e.value.status == -1
+    p17 = kvc.KvParams(batch=1, n_q_heads=17, n_kv_heads=1, max_desc_per_stream=8)
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_attend_decode(p17, a, a, a, None, a, None, a)
+    assert e.value.status == -2

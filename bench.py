@@ -1,0 +1,205 @@
+"""Benchmark: compressed decode attention on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input already
+resident in HBM: kv_compress (window scoring, per-vector channel top-c,
+per-segment strategy choice, offsets, pack) followed by kv_attend_decode
+(split-K decode over the packed segments + log-sum-exp merge).
+
+Workload (default): batched long context -- B 16, GQA 32/8, head_dim 128,
+context 131072, segment 128, window 64 queries per q head, budget 25 % of the
+dense K+V bytes per segment, per-segment heavy-token density U(0, 2 %),
+seeded synthetic bf16 data (gen.py).
+
+Printed JSON (one line):
+  value        KV tokens/s of decode attention = batch * context / mean decode
+               time (HIP events around kv_attend_decode on its stream)
+  ms_per_step  wall time of one whole step (compress + decode)
+  roofline     decode (k_decode_split + k_decode_reduce) against 8 TB/s HBM;
+               algorithmic bytes = descriptors + masks + values of every kept
+               segment + q + out + partials written and read back
+  cpu_baseline the CPU oracle (C, OpenMP) on a bounded sample: compress of
+               one stream and fp64 decode of that stream
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="batched128k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-splits", type=int, default=0, help="0 = library choice")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured decode HBM bytes per launch (from rocprofv3 pmc)")
+    return ap.parse_args()
+
+
+def algorithmic_decode_bytes(desc, S, B, Hq, splits):
+    n = desc["n_tok"].astype(np.int64)
+    c = desc["n_ch"].astype(np.int64)
+    masks = np.where(c < 128, 2 * 16 * n, 0)
+    vals = 2 * 2 * n * c
+    seg = (16 + masks + vals).sum()  # descriptor + masks + values (index lists unread)
+    q = out = B * Hq * 128 * 2
+    partials = 2 * B * Hq * splits * (2 + 128) * 4
+    return int(seg + q + out + partials)
+
+
+def cpu_baseline(w, S, strategies, budget, scale):
+    """Oracle as it stands on a bounded sample: one stream compressed, then its
+    decode timed (fp64)."""
+    from compressed_kv_cache_compress_amd import gen
+    from oracle import oracle as O
+    G = w["G"]
+    Ks = gen.u16(w["K"][0, 0])
+    Vs = gen.u16(w["V"][0, 0])
+    Qs = gen.u16(w["Qw"][0, :G])
+    t0 = time.perf_counter()
+    r = O.compress_stream(Ks, Vs, Qs, S=S, strategies=strategies, budget_bytes=budget, scale=scale)
+    tc = time.perf_counter() - t0
+    q = gen.u16(w["q"][0, :G])
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.decode_stream(q, r["packed"], r["desc"], scale)
+        reps += 1
+        td = time.perf_counter() - t0
+        if td > 2.0 or reps >= 50:
+            break
+    n_ctx = Ks.shape[0]
+    return dict(value=n_ctx * reps / td, unit="KV tokens/s", cores=1, kind="oracle",
+                sample=f"stream (b=0, kv head 0) of the workload: oracle decode (fp64, 1 thread) "
+                       f"of its {n_ctx} tokens x {G} q heads, {reps} reps in {td:.2f} s; oracle "
+                       f"compress of that stream took {tc:.2f} s on {O.max_threads()} threads",
+                compress_s_per_stream=tc, compress_threads=O.max_threads())
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for {a.gpus}); the "
+              "multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        sys.exit(2)
+    import compressed_kv_cache_compress_amd as kvc
+    from compressed_kv_cache_compress_amd import gen, runtime
+
+    kvc.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = gen.CONFIGS[a.config]
+    S, W, B, N = cfg["S"], cfg["W"], cfg["B"], cfg["N"]
+    Hq, Hkv = cfg["Hq"], cfg["Hkv"]
+    strategies = gen.table9(S)
+    budget = gen.budget_bytes(cfg["budget_pct"], S)
+    scale = np.float32(1.0 / math.sqrt(128.0))
+    print(f"[bench] generating {a.config} on {dev} ...", file=sys.stderr, flush=True)
+    w = gen.make_workload(a.config, seed=a.seed, device=dev)
+    K, V, Qw, q = w["K"], w["V"], w["Qw"], w["q"]
+
+    p = kvc.KvParams(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, n_ctx=N, seg_tokens=S, n_win=W,
+                     strategies=strategies, budget_bytes=budget, scale=float(scale),
+                     decode_splits=a.decode_splits)
+    _, L = kvc.kv_layout_query(p)
+    streams = B * Hkv
+    packed = torch.empty(L.packed_bytes_max, dtype=torch.uint8, device=dev)
+    desc = torch.zeros(streams * L.n_seg * 16, dtype=torch.uint8, device=dev)
+    used = torch.zeros(streams, dtype=torch.int64, device=dev)
+    cws = torch.empty(L.compress_ws_bytes, dtype=torch.uint8, device=dev)
+    dws = torch.empty(L.decode_ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+
+    def step(e=None):
+        if e:
+            e[0].record(stream)
+        kvc.kv_compress(p, K, V, Qw, None, packed, desc, used, None, None, cws)
+        if e:
+            e[1].record(stream)
+        kvc.kv_attend_decode(p, q, packed, desc, None, out, lse, dws)
+        if e:
+            e[2].record(stream)
+
+    print(f"[bench] warmup {a.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    comp_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+
+    dh = desc.cpu().numpy().view(kvc.DESC_DTYPE)
+    hist = np.bincount(dh["strategy"], minlength=len(strategies)).tolist()
+    alg = algorithmic_decode_bytes(dh, S, B, Hq, L.decode_splits)
+    t_dec = float(dec_ms.mean()) * 1e-3
+    achieved = alg / t_dec / 1e9
+    traffic = None
+    if a.traffic and os.path.exists(a.traffic):
+        traffic = json.load(open(a.traffic)).get("bytes_per_launch")
+    packed_total = int(used.sum().item())
+    res = {
+        "metric": "compressed decode attention: KV tokens/s and achieved HBM GB/s (% of peak)",
+        "value": B * N / t_dec,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": wall * 1e3 / a.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 storage, fp32 accumulate (decode: bf16 MFMA inputs); fp32 selection",
+        "data": "synthetic (seeded torch generator; gen.py recipe), inputs resident in HBM",
+        "config": {"workload": a.config, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": 128, "context": N, "segment": S, "window": W,
+                   "budget_pct": cfg["budget_pct"], "strategies": strategies,
+                   "decode_splits": L.decode_splits, "parallelism": "single GPU"},
+        "decode_us": t_dec * 1e6,
+        "decode_us_p10_p90": [float(np.percentile(dec_ms, 10) * 1e3), float(np.percentile(dec_ms, 90) * 1e3)],
+        "compress_ms": float(comp_ms.mean()),
+        "achieved_GBs": achieved,
+        "pct_of_peak_hbm": 100.0 * achieved / PEAK_HBM_GBS,
+        "stored_tokens_per_s": float(dh["n_tok"].astype(np.int64).sum()) / t_dec,
+        "packed_bytes": packed_total,
+        "dense_kv_bytes": B * Hkv * N * 512,
+        "strategy_histogram": hist,
+        "roofline": {"kernel": "kv_attend_decode (k_decode_split + k_decode_reduce)",
+                     "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg},
+        "value_basis": "B*context / mean decode time over the timed steps; each timed step also "
+                       "runs kv_compress (compress_ms)",
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        wc = {k: (v[:1].cpu() if torch.is_tensor(v) else v) for k, v in w.items()}
+        res["cpu_baseline"] = cpu_baseline(wc, S, strategies, budget, scale)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

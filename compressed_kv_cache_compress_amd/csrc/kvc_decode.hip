@@ -1,17 +1,31 @@
 // kvc_decode.hip -- gfx950 decode attention over compressed KV segments
 // (MosaicKV review page, Fig. 6 caption: PackedAttention over the packed KV
-// format).  One wave per (stream, split): the split's descriptors are
-// streamed through LDS in chunks of 16 kept tokens; each kept vector is
-// expanded from (bitmask, compact bf16 values) to a dense 128-channel row,
-// q.k and p.v run on MFMA (bf16 inputs, fp32 accumulation), and the softmax
-// is online in base 2.  A second kernel merges the splits (log-sum-exp) and
-// rounds the output to bf16.
+// format).
 //
-// MFMA row mapping: the q head h of the group occupies A-row
-// 4*(h & 3) + (h >> 2), so in the 16x16 accumulator layout (lane l, item j
-// <-> row 4*(l>>4)+j, column l&15) lane l's item j belongs to head 4*j+(l>>4)
-// and to token/channel l&15 -- for G <= 4 every head's scores and outputs sit
-// in item 0 of its own 16-lane row.
+// Work split: one wave per (stream, split); a split is a contiguous range of
+// the stream's descriptors.  Four independent waves share a workgroup only to
+// share one LDS table.  Each wave walks its descriptors in chunks of 16 kept
+// tokens:
+//   * the next chunk's K and V bytes (masks + compact values) are loaded into
+//     registers while the current chunk is computed, then written to LDS;
+//   * every kept vector is expanded from (bitmask, compact bf16 values) to a
+//     dense 128-channel row, one mask byte (8 channels) per lane and step,
+//     one nibble (4 channels) at a time: the nibble's candidate values are
+//     the 4 compact elements starting at its rank (an 8-byte window, shifted
+//     by one element when the rank is odd), and one v_perm_b32 per output
+//     dword places them (or zero) using a 16-entry selector table indexed by
+//     the nibble;
+//   * staged rows are padded by 16 bytes so that the 16 tokens of a chunk
+//     start on different LDS banks;
+//   * q.k of the 16 tokens and p.v run on MFMA (bf16 inputs, fp32
+//     accumulation); the softmax is online, in base 2, with DPP row
+//     reductions.
+// A second kernel merges the splits (log-sum-exp) and rounds to bf16.
+//
+// MFMA row mapping: q head h of the group is A-row 4*(h & 3) + (h >> 2), so
+// in the 16x16 accumulator layout (lane l, item j <-> row 4*(l>>4)+j, column
+// l&15) lane l's item j belongs to head 4*j+(l>>4) and to token/channel l&15;
+// for G <= 4 every head lives in item 0 of its own 16-lane row.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -21,12 +35,19 @@
 namespace kvc {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(8))) unsigned short u16x8_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
-constexpr int CT = 16;                       // kept tokens per chunk
-constexpr int STAGE_BYTES = CT * 16 + CT * 256;  // masks + values of one chunk
+constexpr int CT = 16;                            // kept tokens per chunk
+constexpr int STAGE = CT * 16 + CT * (256 + 16) + 32;  // masks + padded rows + window pad
+constexpr int NPF = (CT * 16 + CT * 256) / 16 / 64 + 1;  // uint4 prefetch slots per lane (5)
+constexpr float RESCALE_SLACK = 8.0f;             // log2 units the running max may lag
+constexpr int VT_STRIDE = 20;                     // u16 per channel row of the dense V tile
+constexpr int WAVES = 4;
+#ifndef KVC_DECODE_DEPTH
+#define KVC_DECODE_DEPTH 1  // chunks prefetched ahead into registers
+#endif
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -35,53 +56,279 @@ struct DecodeArgs {
   const uint32_t* n_desc;
   float* part_ml;
   float* part_acc;
-  int hkv, hq, G, maxd, splits;
+  int hkv, hq, G, maxd, splits, items;
   float sl2;  // scale * log2(e)
 };
 
-// Copies `bytes` (multiple of 16) from global to LDS with the wave's lanes.
-__device__ __forceinline__ void stage16(uint4* dst, const uint8_t* src, uint32_t bytes, int lane) {
-  const uint4* s4 = reinterpret_cast<const uint4*>(src);
-  for (uint32_t i = lane; i < bytes / 16; i += 64) dst[i] = s4[i];
+struct WaveLds {
+  u32x4_t k[STAGE / 16];
+  u32x4_t v[STAGE / 16];
+  uint16_t vt[D * VT_STRIDE];  // dense V of the chunk, [channel][token]
+  uint16_t pl[16 * CT];        // probabilities, [head][token]
+};
+
+__device__ __forceinline__ float dpp_f(float v, int ctrl) {
+  switch (ctrl) {  // the control must be a constant
+    case 0xB1: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    case 0x4E: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+    case 0x141: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  }
+}
+// Max / sum over the 16 lanes of a DPP row (every lane gets the result).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f(v, 0xB1));
+  v = fmaxf(v, dpp_f(v, 0x4E));
+  v = fmaxf(v, dpp_f(v, 0x141));
+  v = fmaxf(v, dpp_f(v, 0x140));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f(v, 0xB1);
+  v += dpp_f(v, 0x4E);
+  v += dpp_f(v, 0x141);
+  v += dpp_f(v, 0x140);
+  return v;
 }
 
-// Dense channels 32*kk + 8*grp .. +7 of token `tok` of the staged chunk.
-// Staged chunk: masks [nt][16 B] (if hasmask) then values [nt][c] bf16.
-__device__ __forceinline__ u16x8_t expand8(const uint8_t* st, int tok, int kk, int grp, int nt,
-                                           int c, bool hasmask) {
-  u16x8_t r = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (tok >= nt) return r;
-  if (!hasmask) {
-    return *reinterpret_cast<const u16x8_t*>(st + tok * 256 + 2 * (32 * kk + 8 * grp));
-  }
-  const uint32_t* m = reinterpret_cast<const uint32_t*>(st + 16 * tok);
-  const uint16_t* vals = reinterpret_cast<const uint16_t*>(st + 16 * nt + 2 * c * tok);
-  uint32_t rk = 0;
-  for (int w = 0; w < kk; ++w) rk += __popc(m[w]);
-  const uint32_t mw = m[kk];
-  rk += __popc(mw & ((1u << (8 * grp)) - 1u));
-  const uint32_t byte = (mw >> (8 * grp)) & 0xFFu;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if ((byte >> i) & 1u) {
-      r[i] = vals[rk];
-      ++rk;
+__device__ __forceinline__ void lds_order() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Selector table entry for a mask nibble n (channels 0..3 of the nibble):
+// dword d holds the v_perm_b32 selectors of channels 2d and 2d+1, i.e. bytes
+// (2e, 2e+1) of an 8-byte window of compact elements where e = kept channels
+// of the nibble before this one, or 0x0C (zero byte) when the channel is
+// dropped.
+__device__ void build_lut_entry(uint32_t n, uint32_t* e) {
+  for (int d = 0; d < 2; ++d) {
+    uint32_t sel = 0;
+    for (int h = 0; h < 2; ++h) {
+      const int ch = 2 * d + h;
+      uint32_t pair = 0x0C0Cu;
+      if ((n >> ch) & 1u) {
+        const uint32_t el = __popc(n & ((1u << ch) - 1u));
+        pair = (2 * el) | ((2 * el + 1) << 8);
+      }
+      sel |= pair << (16 * h);
     }
+    e[d] = sel;
   }
-  return r;
 }
 
-template <int JG>
-__global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
-  const int sp = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+// Expansion of one staged token (this lane's `col`) to the dense channels
+// 8*(4*kk + grp) .. +7 for kk = 0..3 (mask byte 4*kk + grp; the MFMA
+// contraction order over channels is the same permutation for q, so any
+// assignment of channels to k-slots works).  Two phases so that every LDS
+// read of a token side is in flight at once: issue() reads the mask, the
+// two 12-byte windows (low and high nibble) per byte and the two selector
+// entries; finish() aligns each window to its first element and places the
+// values with one v_perm_b32 per output dword.  Reads stay inside the staging
+// buffer for any mask, so lanes past the chunk run the same code and are
+// zeroed at the end.
+struct Expand {
+  uint32_t a[4][3], b[4][3];  // windows of the low / high nibble
+  uint32_t sa[4], sb[4];      // 0 or 16 (odd start)
+  uint2 tl[4], th[4];         // selectors of the low / high nibble
+};
+
+__device__ __forceinline__ void expand_issue(const uint8_t* st, int col, int grp, int nt, int c,
+                                             const uint2* lut, Expand& e) {
+  const u32x4_t m = *reinterpret_cast<const u32x4_t*>(st + 16 * col);
+  const uint32_t* row = reinterpret_cast<const uint32_t*>(st + 16 * nt + (2 * c + 16) * col);
+  uint32_t pre = 0;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const uint32_t mw = m[kk];
+    const uint32_t mb = (mw >> (8 * grp)) & 0xFFu;
+    const uint32_t ra = pre + __popc(mw & ((1u << (8 * grp)) - 1u));
+    const uint32_t rb = ra + __popc(mb & 0xFu);
+    pre += __popc(mw);
+    const uint32_t* wa = row + (ra >> 1);
+    const uint32_t* wb = row + (rb >> 1);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      e.a[kk][i] = wa[i];
+      e.b[kk][i] = wb[i];
+    }
+    e.sa[kk] = (ra & 1u) << 4;
+    e.sb[kk] = (rb & 1u) << 4;
+    e.tl[kk] = lut[mb & 0xFu];
+    e.th[kk] = lut[mb >> 4];
+  }
+}
+
+__device__ __forceinline__ u32x4_t expand_finish(const Expand& e, int kk) {
+  const uint32_t xa0 = __builtin_amdgcn_alignbit(e.a[kk][1], e.a[kk][0], e.sa[kk]);
+  const uint32_t xa1 = __builtin_amdgcn_alignbit(e.a[kk][2], e.a[kk][1], e.sa[kk]);
+  const uint32_t xb0 = __builtin_amdgcn_alignbit(e.b[kk][1], e.b[kk][0], e.sb[kk]);
+  const uint32_t xb1 = __builtin_amdgcn_alignbit(e.b[kk][2], e.b[kk][1], e.sb[kk]);
+  u32x4_t o;
+  o[0] = __builtin_amdgcn_perm(xa1, xa0, e.tl[kk].x);
+  o[1] = __builtin_amdgcn_perm(xa1, xa0, e.tl[kk].y);
+  o[2] = __builtin_amdgcn_perm(xb1, xb0, e.th[kk].x);
+  o[3] = __builtin_amdgcn_perm(xb1, xb0, e.th[kk].y);
+  return o;
+}
+
+// Dense rows (all 128 channels kept): the 4 x 16 bytes of this lane.
+__device__ __forceinline__ void dense_issue(const uint8_t* st, int col, int grp, u32x4_t* o) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    o[kk] = *reinterpret_cast<const u32x4_t*>(st + col * (256 + 16) + 16 * (4 * kk + grp));
+}
+
+// The 4 x 8 dense channels of this lane's token, zero past the chunk.
+__device__ __forceinline__ void expand_side(const uint8_t* st, int col, int grp, int nt, int c,
+                                            const uint2* lut, u32x4_t* o) {
+  if (c < D) {
+    Expand e;
+    expand_issue(st, col, grp, nt, c, lut, e);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) o[kk] = expand_finish(e, kk);
+  } else {
+    dense_issue(st, col, grp, o);
+  }
+  if (col >= nt) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) o[kk] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+// One chunk to stream: K part and V part each = [masks 16*nt][values 2*c*nt].
+struct Chunk {
+  const uint8_t* kmask;
+  const uint8_t* kval;
+  const uint8_t* vmask;
+  const uint8_t* vval;
+  int nt, c;
+  uint32_t magic;  // ceil(2^20 / (c/8)): value slot -> row by multiply-shift
+  bool valid;
+};
+
+// The next chunk's bytes, one uint4 of K and one of V per slot and lane.
+struct Regs {
+  u32x4_t k[NPF], v[NPF];
+};
+
+template <int I>
+__device__ __forceinline__ void prefetch_slot(const Chunk& ch, int lane, int nm, int n16, Regs& r) {
+  // lanes past the chunk re-read its last 16 bytes (slot unused by commit)
+  const int j = min(lane + 64 * I, n16 - 1);
+  const u32x4_t* ks = j < nm ? reinterpret_cast<const u32x4_t*>(ch.kmask) + j
+                            : reinterpret_cast<const u32x4_t*>(ch.kval) + (j - nm);
+  const u32x4_t* vs = j < nm ? reinterpret_cast<const u32x4_t*>(ch.vmask) + j
+                            : reinterpret_cast<const u32x4_t*>(ch.vval) + (j - nm);
+  r.k[I] = *ks;
+  r.v[I] = *vs;
+}
+
+__device__ __forceinline__ void prefetch(const Chunk& ch, int lane, Regs& r) {
+  if (!ch.valid) return;
+  const int nm = ch.c < D ? ch.nt : 0;
+  const int n16 = nm + (2 * ch.c * ch.nt) / 16;
+  prefetch_slot<0>(ch, lane, nm, n16, r);
+  prefetch_slot<1>(ch, lane, nm, n16, r);
+  prefetch_slot<2>(ch, lane, nm, n16, r);
+  prefetch_slot<3>(ch, lane, nm, n16, r);
+  prefetch_slot<4>(ch, lane, nm, n16, r);
+}
+
+// Slot j of the [masks | values] stream goes to LDS slot j (masks) or, for
+// value slot v = j - nm, to nm + v + v / (c/8): one 16-byte pad per row.
+template <int I>
+__device__ __forceinline__ void commit_slot(int lane, int nm, int n16, uint32_t magic, const Regs& r,
+                                            u32x4_t* sk, u32x4_t* sv) {
+  const int j = lane + 64 * I;
+  if (j < n16) {
+    const uint32_t v = (uint32_t)(j - nm);
+    const int dst = j < nm ? j : j + (int)(__umul24(v, magic) >> 20);
+    sk[dst] = r.k[I];
+    sv[dst] = r.v[I];
+  }
+}
+
+__device__ __forceinline__ void commit(const Chunk& ch, int lane, const Regs& r, u32x4_t* sk, u32x4_t* sv) {
+  const int nm = ch.c < D ? ch.nt : 0;
+  const int n16 = nm + (2 * ch.c * ch.nt) / 16;
+  commit_slot<0>(lane, nm, n16, ch.magic, r, sk, sv);
+  commit_slot<1>(lane, nm, n16, ch.magic, r, sk, sv);
+  commit_slot<2>(lane, nm, n16, ch.magic, r, sk, sv);
+  commit_slot<3>(lane, nm, n16, ch.magic, r, sk, sv);
+  commit_slot<4>(lane, nm, n16, ch.magic, r, sk, sv);
+}
+
+// Descriptor cursor of one wave.  Descriptors are fetched 64 at a time, one
+// per lane, and read back wave-uniformly with readlane, so walking them costs
+// no memory round trip per segment.
+struct Cursor {
+  const kvc_seg_desc* dl;
+  const uint8_t* packed;
+  int di, d1, t0, base;  // base: first descriptor held in the lanes
+  uint32_t w0, w1, w2, w3;  // this lane's descriptor (base + lane)
+};
+
+__device__ __forceinline__ void fetch_descs(Cursor& cu, int lane) {
+  cu.base = cu.di;
+  const int i = min(cu.di + lane, cu.d1 - 1);
+  const u32x4_t d = *reinterpret_cast<const u32x4_t*>(cu.dl + i);
+  cu.w0 = d[0];
+  cu.w1 = d[1];
+  cu.w2 = d[2];
+  cu.w3 = d[3];
+}
+
+// Advances to the next non-empty chunk; returns its description.
+__device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
+  Chunk ch;
+  ch.valid = false;
+  while (cu.di < cu.d1) {
+    if (cu.di - cu.base >= 64) fetch_descs(cu, lane);
+    const int sl = cu.di - cu.base;
+    const uint32_t lo = __builtin_amdgcn_readlane(cu.w0, sl);
+    const uint32_t hi = __builtin_amdgcn_readlane(cu.w1, sl);
+    const uint32_t tc = __builtin_amdgcn_readlane(cu.w2, sl);
+    const int T = (int)(tc & 0xFFFFu);
+    if (cu.t0 < T) {
+      const int c = (int)(tc >> 16);
+      const bool hm = c < D;
+      const uint8_t* base = cu.packed + (((uint64_t)hi << 32) | lo);
+      const uint32_t mb = hm ? 16u * T : 0u;
+      ch.kmask = base + 16 * cu.t0;
+      ch.kval = base + mb + 2 * c * cu.t0;
+      ch.vmask = base + mb + 2u * T * c + 16 * cu.t0;
+      ch.vval = base + 2 * mb + 2u * T * c + 2 * c * cu.t0;
+      ch.nt = min(CT, T - cu.t0);
+      ch.c = c;
+      ch.magic = ((1u << 20) + (uint32_t)(c >> 3) - 1u) / (uint32_t)(c >> 3);
+      ch.valid = true;
+      cu.t0 += CT;
+      return ch;
+    }
+    ++cu.di;
+    cu.t0 = 0;
+  }
+  return ch;
+}
+
+template <int JG, int DEPTH>
+__global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
+  __shared__ uint2 lut[16];
+  __shared__ WaveLds wl[WAVES];
+  const int tid = threadIdx.x;
+  if (tid < 16) {
+    uint32_t e[2];
+    build_lut_entry((uint32_t)tid, e);
+    lut[tid] = make_uint2(e[0], e[1]);
+  }
+  __syncthreads();
+
+  const int lane = tid & 63, wv = tid >> 6;
+  const int item = blockIdx.x * WAVES + wv;
+  if (item >= a.items) return;
+  const int s = item / a.splits, sp = item - s * a.splits;
   const int grp = lane >> 4, col = lane & 15;
   const int b = s / a.hkv, h = s - b * a.hkv;
-  __shared__ uint4 kst[STAGE_BYTES / 16];
-  __shared__ uint4 vst[STAGE_BYTES / 16];
-  __shared__ uint16_t vt[D * CT];   // dense V of the chunk, [channel][token]
-  __shared__ uint16_t pl[16 * CT];  // probabilities, [head][token]
-
-  for (int i = lane; i < 16 * CT; i += 64) pl[i] = 0;
+  WaveLds& L = wl[wv];
+  for (int i = lane; i < 16 * CT; i += 64) L.pl[i] = 0;
 
   // A operand of the score MFMA: row col holds head hh (zero if none)
   const int hh = 4 * (col & 3) + (col >> 2);
@@ -90,8 +337,8 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
   bf16x8_t qa[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    u16x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (hh_ok) v = *reinterpret_cast<const u16x8_t*>(qh + 32 * kk + 8 * grp);
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (hh_ok) v = *reinterpret_cast<const u32x4_t*>(qh + 8 * (4 * kk + grp));
     qa[kk] = __builtin_bit_cast(bf16x8_t, v);
   }
 
@@ -106,86 +353,118 @@ __global__ __launch_bounds__(64) void k_decode_split(DecodeArgs a) {
   }
 
   const int nd = a.n_desc ? min((int)a.n_desc[s], a.maxd) : a.maxd;
-  const int d0 = (int)(((int64_t)sp * nd) / a.splits);
-  const int d1 = (int)(((int64_t)(sp + 1) * nd) / a.splits);
-  const kvc_seg_desc* dl = a.desc + (uint64_t)s * a.maxd;
-  const uint8_t* kst8 = reinterpret_cast<const uint8_t*>(kst);
-  const uint8_t* vst8 = reinterpret_cast<const uint8_t*>(vst);
+  Cursor cu;
+  cu.dl = a.desc + (uint64_t)s * a.maxd;
+  cu.packed = a.packed;
+  cu.di = (int)(((int64_t)sp * nd) / a.splits);
+  cu.d1 = (int)(((int64_t)(sp + 1) * nd) / a.splits);
+  cu.t0 = 0;
+  if (cu.di < cu.d1) fetch_descs(cu, lane);
 
-  for (int di = d0; di < d1; ++di) {
-    const kvc_seg_desc d = dl[di];
-    const int T = d.n_tok, c = d.n_ch;
-    if (T == 0) continue;
-    const bool hasmask = c < D;
-    const uint8_t* base = a.packed + d.offset;
-    const uint32_t mb = hasmask ? 16u * T : 0u;
-    const uint8_t* kval = base + mb;
-    const uint8_t* vmask = kval + 2u * T * c;
-    const uint8_t* vval = vmask + mb;
-    for (int t0 = 0; t0 < T; t0 += CT) {
-      const int nt = min(CT, T - t0);
-      __syncthreads();
-      if (hasmask) {
-        stage16(kst, base + 16 * t0, 16 * nt, lane);
-        stage16(vst, vmask + 16 * t0, 16 * nt, lane);
-      }
-      stage16(kst + (hasmask ? nt : 0), kval + 2 * c * t0, 2 * c * nt, lane);
-      stage16(vst + (hasmask ? nt : 0), vval + 2 * c * t0, 2 * c * nt, lane);
-      __syncthreads();
+  const uint8_t* sk8 = reinterpret_cast<const uint8_t*>(L.k);
+  const uint8_t* sv8 = reinterpret_cast<const uint8_t*>(L.v);
 
-      // scores of the chunk: S^T = Q Kd^T
-      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+  // computes one staged chunk
+  auto compute = [&](const Chunk& cur) {
+    const int nt = cur.nt, c = cur.c;
+
+    // scores of the chunk: S^T = Q Kd^T
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+    {
+      u32x4_t kb[4];
+      expand_side(sk8, col, grp, nt, c, lut, kb);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const u16x8_t kb = expand8(kst8, col, kk, grp, nt, c, hasmask);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], __builtin_bit_cast(bf16x8_t, kb),
+      for (int kk = 0; kk < 4; ++kk)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], __builtin_bit_cast(bf16x8_t, kb[kk]),
                                                        sacc, 0, 0, 0);
-      }
-      // online softmax, one head per (16-lane row, item j)
+    }
+    // online softmax, one head per (16-lane row, item j); the running max
+    // moves only when the chunk max exceeds it by RESCALE_SLACK (so p <=
+    // 2^RESCALE_SLACK), and the accumulators are rescaled only when some
+    // head's max moved
 #pragma unroll
-      for (int j = 0; j < JG; ++j) {
-        const int hd = 4 * j + grp;
-        const bool ok = col < nt && hd < a.G;
-        const float x = ok ? sacc[j] * a.sl2 : -INFINITY;
-        float cm = x;
-        cm = fmaxf(cm, __shfl_xor(cm, 1, 64));
-        cm = fmaxf(cm, __shfl_xor(cm, 2, 64));
-        cm = fmaxf(cm, __shfl_xor(cm, 4, 64));
-        cm = fmaxf(cm, __shfl_xor(cm, 8, 64));
-        const float mn = fmaxf(m_run[j], cm);
-        float alpha = 1.0f, p = 0.0f;
-        if (mn != -INFINITY) {
-          alpha = exp2f(m_run[j] - mn);
-          p = exp2f(x - mn);
-        }
-        float rs = p;
-        rs += __shfl_xor(rs, 1, 64);
-        rs += __shfl_xor(rs, 2, 64);
-        rs += __shfl_xor(rs, 4, 64);
-        rs += __shfl_xor(rs, 8, 64);
-        l_run[j] = l_run[j] * alpha + rs;
-        m_run[j] = mn;
+    for (int j = 0; j < JG; ++j) {
+      const int hd = 4 * j + grp;
+      const bool ok = col < nt && hd < a.G;
+      const float x = ok ? sacc[j] * a.sl2 : -INFINITY;
+      const float cm = row16_max(x);
+      const float mo = m_run[j];
+      const float mn = (cm > mo + RESCALE_SLACK) ? cm : mo;
+      const float alpha = (mn == mo) ? 1.0f : __builtin_amdgcn_exp2f(mo - mn);
+      const float p = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x - mn);
+      l_run[j] = l_run[j] * alpha + row16_sum(p);
+      m_run[j] = mn;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
         for (int nn = 0; nn < 8; ++nn) O[nn][j] *= alpha;
-        if (hd < a.G) pl[hd * CT + col] = (uint16_t)f2bf(p);
       }
-      // dense V of the chunk, transposed into LDS
+      if (hd < a.G) L.pl[hd * CT + col] = (uint16_t)f2bf(p);
+    }
+    // dense V of the chunk, transposed into LDS
+    {
+      u32x4_t vb[4];
+      expand_side(sv8, col, grp, nt, c, lut, vb);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const u16x8_t vb = expand8(vst8, col, kk, grp, nt, c, hasmask);
+        uint16_t* dst = L.vt + (8 * (4 * kk + grp)) * VT_STRIDE + col;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) vt[(32 * kk + 8 * grp + i) * CT + col] = vb[i];
-      }
-      __syncthreads();
-      // O += P Vd
-      s16x4_t pa = {0, 0, 0, 0};
-      if (hh_ok) pa = *reinterpret_cast<const s16x4_t*>(pl + hh * CT + 4 * grp);
-#pragma unroll
-      for (int nn = 0; nn < 8; ++nn) {
-        const s16x4_t vb = *reinterpret_cast<const s16x4_t*>(vt + (16 * nn + col) * CT + 4 * grp);
-        O[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[nn], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          dst[(2 * i) * VT_STRIDE] = (uint16_t)(vb[kk][i] & 0xFFFFu);
+          dst[(2 * i + 1) * VT_STRIDE] = (uint16_t)(vb[kk][i] >> 16);
+        }
       }
     }
+    lds_order();
+    // O += P Vd
+    s16x4_t pa = {0, 0, 0, 0};
+    if (hh_ok) pa = *reinterpret_cast<const s16x4_t*>(L.pl + hh * CT + 4 * grp);
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) {
+      const s16x4_t vb = *reinterpret_cast<const s16x4_t*>(L.vt + (16 * nn + col) * VT_STRIDE + 4 * grp);
+      O[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[nn], 0, 0, 0);
+    }
+  };
+  // one chunk: stage it (its bytes are in rc), refill rc DEPTH chunks ahead,
+  // then compute it from LDS
+  auto body = [&](Chunk& cur, Chunk& nxt, Regs& rc) {
+    lds_order();
+    commit(cur, lane, rc, L.k, L.v);
+    const Chunk far = next_chunk(cu, lane);
+    prefetch(far, lane, rc);
+    lds_order();
+    compute(cur);
+    cur = nxt;
+    nxt = far;
+  };
+  auto body1 = [&](Chunk& cur, Regs& rc) {
+    lds_order();
+    commit(cur, lane, rc, L.k, L.v);
+    const Chunk nxt = next_chunk(cu, lane);
+    prefetch(nxt, lane, rc);
+    lds_order();
+    compute(cur);
+    cur = nxt;
+  };
+
+  static_assert(NPF == 5, "prefetch slots are unrolled by hand");
+  if (DEPTH == 2) {
+    Regs ra, rb;
+    Chunk cur = next_chunk(cu, lane);
+    prefetch(cur, lane, ra);
+    Chunk nxt = next_chunk(cu, lane);
+    prefetch(nxt, lane, rb);
+    while (cur.valid) {
+      body(cur, nxt, ra);
+      if (!cur.valid) break;
+      body(cur, nxt, rb);
+    }
+  } else {
+    Regs ra;
+    Chunk cur = next_chunk(cu, lane);
+    prefetch(cur, lane, ra);
+    Chunk none;
+    none.valid = false;
+    while (cur.valid) body1(cur, ra);
   }
 
   // partial state of this split
@@ -241,14 +520,15 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
   a.G = p.G;
   a.maxd = p.maxd;
   a.splits = p.splits;
+  a.items = p.streams * p.splits;
   a.sl2 = p.scale * KVC_LOG2E;
-  const dim3 grid(p.splits, p.streams);
+  const dim3 grid((a.items + WAVES - 1) / WAVES);
   if (p.G <= 4)
-    hipLaunchKernelGGL(k_decode_split<1>, grid, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((k_decode_split<1, KVC_DECODE_DEPTH>), grid, dim3(64 * WAVES), 0, st, a);
   else if (p.G <= 8)
-    hipLaunchKernelGGL(k_decode_split<2>, grid, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((k_decode_split<2, 1>), grid, dim3(64 * WAVES), 0, st, a);
   else
-    hipLaunchKernelGGL(k_decode_split<4>, grid, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((k_decode_split<4, 1>), grid, dim3(64 * WAVES), 0, st, a);
   hipLaunchKernelGGL(k_decode_reduce, dim3(p.batch * p.hq), dim3(128), 0, st, p.part_ml, p.part_acc,
                      p.out, p.lse, p.splits);
   return hipGetLastError();

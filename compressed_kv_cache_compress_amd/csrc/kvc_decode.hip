@@ -25,7 +25,11 @@
 // MFMA row mapping: q head h of the group is A-row 4*(h & 3) + (h >> 2), so
 // in the 16x16 accumulator layout (lane l, item j <-> row 4*(l>>4)+j, column
 // l&15) lane l's item j belongs to head 4*j+(l>>4) and to token/channel l&15;
-// for G <= 4 every head lives in item 0 of its own 16-lane row.
+// for G <= 4 every head lives in item 0 of its own 16-lane row.  For G <= 4
+// the p.v product uses the 16-block 4x4x4 MFMA instead (block b = lanes
+// 4b..4b+3; A[i][k] at lane 4b+i item k, B[k][j] at lane 4b+j item k, D[i][j]
+// at lane 4b+j item i): head i x channel (64*half + lane) accumulates over 4
+// tokens per instruction, so the output needs 8 instead of 32 registers.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -41,10 +45,15 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int CT = 16;                            // kept tokens per chunk
 constexpr int STAGE = CT * 16 + CT * (256 + 16) + 32;  // masks + padded rows + window pad
-constexpr int NPF = (CT * 16 + CT * 256) / 16 / 64 + 1;  // uint4 prefetch slots per lane (5)
+// uint4 prefetch slots per lane: a chunk is at most 16*16 + 16*2*120 bytes
+// (masked) or 16*256 bytes (dense) = 256 slots.
+constexpr int NPF = 4;
 constexpr float RESCALE_SLACK = 8.0f;             // log2 units the running max may lag
 constexpr int VT_STRIDE = 20;                     // u16 per channel row of the dense V tile
 constexpr int WAVES = 4;
+#ifndef KVC_DECODE_MIN_BLOCKS
+#define KVC_DECODE_MIN_BLOCKS 2  // workgroups per CU the register budget is sized for
+#endif
 #ifndef KVC_DECODE_DEPTH
 #define KVC_DECODE_DEPTH 1  // chunks prefetched ahead into registers
 #endif
@@ -60,11 +69,18 @@ struct DecodeArgs {
   float sl2;  // scale * log2(e)
 };
 
+// Per-wave LDS.  The dense V tile is written from the registers that the V
+// stage's reads produced, so it can share the V stage's storage without
+// ordering anything that is not already ordered; the K stage stays separate
+// so that K- and V-side LDS traffic overlap.
+constexpr int VBYTES = (STAGE > D * VT_STRIDE * 2) ? STAGE : D * VT_STRIDE * 2;
 struct WaveLds {
   u32x4_t k[STAGE / 16];
-  u32x4_t v[STAGE / 16];
-  uint16_t vt[D * VT_STRIDE];  // dense V of the chunk, [channel][token]
-  uint16_t pl[16 * CT];        // probabilities, [head][token]
+  union {
+    u32x4_t v[VBYTES / 16];
+    uint16_t vt[VBYTES / 2];  // dense V of the chunk, [channel][token]
+  };
+  uint16_t pl[16 * CT];       // probabilities, [head][token]
 };
 
 __device__ __forceinline__ float dpp_f(float v, int ctrl) {
@@ -193,16 +209,23 @@ __device__ __forceinline__ void expand_side(const uint8_t* st, int col, int grp,
   }
 }
 
-// One chunk to stream: K part and V part each = [masks 16*nt][values 2*c*nt].
+// One chunk to stream: K part and V part each = [masks 16*nt][values 2*c*nt]
+// in global memory.  Uniform bases: the value stream of a side is addressed
+// as val + 16*j for stream slot j >= nm (val already offset by -16*nm).
 struct Chunk {
   const uint8_t* kmask;
   const uint8_t* kval;
   const uint8_t* vmask;
   const uint8_t* vval;
-  int nt, c;
+  int nt, c, nm, n16;
   uint32_t magic;  // ceil(2^20 / (c/8)): value slot -> row by multiply-shift
   bool valid;
 };
+
+// ceil(2^20 / k) for k = c/8 in 1..16.
+__constant__ uint32_t c_row_magic[17] = {
+    0u,      1048576u, 524288u, 349526u, 262144u, 209716u, 174763u, 149797u, 131072u,
+    116509u, 104858u,  95326u,  87382u,  80660u,  74899u,  69906u,  65536u};
 
 // The next chunk's bytes, one uint4 of K and one of V per slot and lane.
 struct Regs {
@@ -210,60 +233,62 @@ struct Regs {
 };
 
 template <int I>
-__device__ __forceinline__ void prefetch_slot(const Chunk& ch, int lane, int nm, int n16, Regs& r) {
-  // lanes past the chunk re-read its last 16 bytes (slot unused by commit)
-  const int j = min(lane + 64 * I, n16 - 1);
-  const u32x4_t* ks = j < nm ? reinterpret_cast<const u32x4_t*>(ch.kmask) + j
-                            : reinterpret_cast<const u32x4_t*>(ch.kval) + (j - nm);
-  const u32x4_t* vs = j < nm ? reinterpret_cast<const u32x4_t*>(ch.vmask) + j
-                            : reinterpret_cast<const u32x4_t*>(ch.vval) + (j - nm);
-  r.k[I] = *ks;
-  r.v[I] = *vs;
+__device__ __forceinline__ void prefetch_slot(const Chunk& ch, int lane, Regs& r) {
+  const int j = lane + 64 * I;
+  if (j < ch.n16) {
+    if (I == 0 && j < ch.nm) {
+      r.k[I] = *reinterpret_cast<const u32x4_t*>(ch.kmask + 16 * j);
+      r.v[I] = *reinterpret_cast<const u32x4_t*>(ch.vmask + 16 * j);
+    } else {
+      r.k[I] = *reinterpret_cast<const u32x4_t*>(ch.kval + 16 * j);
+      r.v[I] = *reinterpret_cast<const u32x4_t*>(ch.vval + 16 * j);
+    }
+  }
 }
 
 __device__ __forceinline__ void prefetch(const Chunk& ch, int lane, Regs& r) {
   if (!ch.valid) return;
-  const int nm = ch.c < D ? ch.nt : 0;
-  const int n16 = nm + (2 * ch.c * ch.nt) / 16;
-  prefetch_slot<0>(ch, lane, nm, n16, r);
-  prefetch_slot<1>(ch, lane, nm, n16, r);
-  prefetch_slot<2>(ch, lane, nm, n16, r);
-  prefetch_slot<3>(ch, lane, nm, n16, r);
-  prefetch_slot<4>(ch, lane, nm, n16, r);
+  prefetch_slot<0>(ch, lane, r);
+  prefetch_slot<1>(ch, lane, r);
+  prefetch_slot<2>(ch, lane, r);
+  prefetch_slot<3>(ch, lane, r);
 }
 
 // Slot j of the [masks | values] stream goes to LDS slot j (masks) or, for
 // value slot v = j - nm, to nm + v + v / (c/8): one 16-byte pad per row.
 template <int I>
-__device__ __forceinline__ void commit_slot(int lane, int nm, int n16, uint32_t magic, const Regs& r,
-                                            u32x4_t* sk, u32x4_t* sv) {
+__device__ __forceinline__ void commit_slot(const Chunk& ch, int lane, const Regs& r, u32x4_t* sk,
+                                            u32x4_t* sv) {
   const int j = lane + 64 * I;
-  if (j < n16) {
-    const uint32_t v = (uint32_t)(j - nm);
-    const int dst = j < nm ? j : j + (int)(__umul24(v, magic) >> 20);
+  if (j < ch.n16) {
+    const uint32_t v = (uint32_t)(j - ch.nm);
+    const int dst = (I == 0 && j < ch.nm) ? j : j + (int)(__umul24(v, ch.magic) >> 20);
     sk[dst] = r.k[I];
     sv[dst] = r.v[I];
   }
 }
 
-__device__ __forceinline__ void commit(const Chunk& ch, int lane, const Regs& r, u32x4_t* sk, u32x4_t* sv) {
-  const int nm = ch.c < D ? ch.nt : 0;
-  const int n16 = nm + (2 * ch.c * ch.nt) / 16;
-  commit_slot<0>(lane, nm, n16, ch.magic, r, sk, sv);
-  commit_slot<1>(lane, nm, n16, ch.magic, r, sk, sv);
-  commit_slot<2>(lane, nm, n16, ch.magic, r, sk, sv);
-  commit_slot<3>(lane, nm, n16, ch.magic, r, sk, sv);
-  commit_slot<4>(lane, nm, n16, ch.magic, r, sk, sv);
+__device__ __forceinline__ void commit(const Chunk& ch, int lane, const Regs& r, u32x4_t* sk,
+                                       u32x4_t* sv) {
+  commit_slot<0>(ch, lane, r, sk, sv);
+  commit_slot<1>(ch, lane, r, sk, sv);
+  commit_slot<2>(ch, lane, r, sk, sv);
+  commit_slot<3>(ch, lane, r, sk, sv);
 }
 
 // Descriptor cursor of one wave.  Descriptors are fetched 64 at a time, one
 // per lane, and read back wave-uniformly with readlane, so walking them costs
-// no memory round trip per segment.
+// no memory round trip per segment.  The current segment's geometry is kept
+// in (scalar) registers so that chunks after the first of a segment only
+// advance offsets.
 struct Cursor {
   const kvc_seg_desc* dl;
   const uint8_t* packed;
-  int di, d1, t0, base;  // base: first descriptor held in the lanes
-  uint32_t w0, w1, w2, w3;  // this lane's descriptor (base + lane)
+  int di, d1, base;         // next descriptor, end, first descriptor held in the lanes
+  uint32_t w0, w1, w2;      // this lane's descriptor (base + lane): offset lo/hi, n_tok|n_ch<<16
+  // current segment
+  const uint8_t *kmask, *kval, *vmask, *vval;  // at token 0
+  int T, c, t0;
 };
 
 __device__ __forceinline__ void fetch_descs(Cursor& cu, int lane) {
@@ -273,44 +298,58 @@ __device__ __forceinline__ void fetch_descs(Cursor& cu, int lane) {
   cu.w0 = d[0];
   cu.w1 = d[1];
   cu.w2 = d[2];
-  cu.w3 = d[3];
 }
 
 // Advances to the next non-empty chunk; returns its description.
 __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
   Chunk ch;
   ch.valid = false;
-  while (cu.di < cu.d1) {
-    if (cu.di - cu.base >= 64) fetch_descs(cu, lane);
-    const int sl = cu.di - cu.base;
-    const uint32_t lo = __builtin_amdgcn_readlane(cu.w0, sl);
-    const uint32_t hi = __builtin_amdgcn_readlane(cu.w1, sl);
-    const uint32_t tc = __builtin_amdgcn_readlane(cu.w2, sl);
-    const int T = (int)(tc & 0xFFFFu);
-    if (cu.t0 < T) {
-      const int c = (int)(tc >> 16);
-      const bool hm = c < D;
-      const uint8_t* base = cu.packed + (((uint64_t)hi << 32) | lo);
-      const uint32_t mb = hm ? 16u * T : 0u;
-      ch.kmask = base + 16 * cu.t0;
-      ch.kval = base + mb + 2 * c * cu.t0;
-      ch.vmask = base + mb + 2u * T * c + 16 * cu.t0;
-      ch.vval = base + 2 * mb + 2u * T * c + 2 * c * cu.t0;
-      ch.nt = min(CT, T - cu.t0);
-      ch.c = c;
-      ch.magic = ((1u << 20) + (uint32_t)(c >> 3) - 1u) / (uint32_t)(c >> 3);
-      ch.valid = true;
-      cu.t0 += CT;
-      return ch;
+  if (cu.t0 >= cu.T) {
+    // next non-empty descriptor
+    cu.T = 0;
+    while (cu.di < cu.d1) {
+      if (cu.di - cu.base >= 64) fetch_descs(cu, lane);
+      const int sl = cu.di - cu.base;
+      const uint32_t tc = __builtin_amdgcn_readlane(cu.w2, sl);
+      const int T = (int)(tc & 0xFFFFu);
+      ++cu.di;
+      if (T > 0) {
+        const uint32_t lo = __builtin_amdgcn_readlane(cu.w0, sl);
+        const uint32_t hi = __builtin_amdgcn_readlane(cu.w1, sl);
+        const int c = (int)(tc >> 16);
+        const uint32_t mb = c < D ? 16u * T : 0u;
+        const uint8_t* base = cu.packed + (((uint64_t)hi << 32) | lo);
+        cu.kmask = base;
+        cu.kval = base + mb;
+        cu.vmask = base + mb + 2u * T * c;
+        cu.vval = base + 2 * mb + 2u * T * c;
+        cu.T = T;
+        cu.c = c;
+        cu.t0 = 0;
+        break;
+      }
     }
-    ++cu.di;
-    cu.t0 = 0;
+    if (cu.T == 0) return ch;
   }
+  const int c = cu.c, t0 = cu.t0;
+  const int nt = min(CT, cu.T - t0);
+  const int nm = c < D ? nt : 0;
+  ch.kmask = cu.kmask + 16 * t0;
+  ch.vmask = cu.vmask + 16 * t0;
+  ch.kval = cu.kval + 2 * c * t0 - 16 * nm;
+  ch.vval = cu.vval + 2 * c * t0 - 16 * nm;
+  ch.nt = nt;
+  ch.c = c;
+  ch.nm = nm;
+  ch.n16 = nm + (2 * c * nt) / 16;
+  ch.magic = c_row_magic[c >> 3];
+  ch.valid = true;
+  cu.t0 = t0 + CT;
   return ch;
 }
 
 template <int JG, int DEPTH>
-__global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
+__global__ __launch_bounds__(256, KVC_DECODE_MIN_BLOCKS) void k_decode_split(DecodeArgs a) {
   __shared__ uint2 lut[16];
   __shared__ WaveLds wl[WAVES];
   const int tid = threadIdx.x;
@@ -342,9 +381,12 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
     qa[kk] = __builtin_bit_cast(bf16x8_t, v);
   }
 
-  f32x4_t O[8];
+  // JG == 1: O4[half][item i] = head i, channel 64*half + lane (4x4x4 MFMA);
+  // otherwise O[nn] is the 16x16 tile of channels 16*nn .. +15
+  constexpr int NO = JG == 1 ? 2 : 8;
+  f32x4_t O[NO];
 #pragma unroll
-  for (int nn = 0; nn < 8; ++nn) O[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int nn = 0; nn < NO; ++nn) O[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run[JG], l_run[JG];
 #pragma unroll
   for (int j = 0; j < JG; ++j) {
@@ -358,6 +400,8 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
   cu.packed = a.packed;
   cu.di = (int)(((int64_t)sp * nd) / a.splits);
   cu.d1 = (int)(((int64_t)(sp + 1) * nd) / a.splits);
+  cu.T = 0;
+  cu.c = 0;
   cu.t0 = 0;
   if (cu.di < cu.d1) fetch_descs(cu, lane);
 
@@ -395,8 +439,18 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
       l_run[j] = l_run[j] * alpha + row16_sum(p);
       m_run[j] = mn;
       if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+        if (JG == 1) {
+          // every lane holds all four heads: alpha of head i sits in row i
 #pragma unroll
-        for (int nn = 0; nn < 8; ++nn) O[nn][j] *= alpha;
+          for (int i = 0; i < 4; ++i) {
+            const float ai = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 16 * i));
+            O[0][i] *= ai;
+            O[1][i] *= ai;
+          }
+        } else {
+#pragma unroll
+          for (int nn = 0; nn < NO; ++nn) O[nn][j] *= alpha;
+        }
       }
       if (hd < a.G) L.pl[hd * CT + col] = (uint16_t)f2bf(p);
     }
@@ -416,12 +470,25 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
     }
     lds_order();
     // O += P Vd
-    s16x4_t pa = {0, 0, 0, 0};
-    if (hh_ok) pa = *reinterpret_cast<const s16x4_t*>(L.pl + hh * CT + 4 * grp);
+    if (JG == 1) {
 #pragma unroll
-    for (int nn = 0; nn < 8; ++nn) {
-      const s16x4_t vb = *reinterpret_cast<const s16x4_t*>(L.vt + (16 * nn + col) * VT_STRIDE + 4 * grp);
-      O[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[nn], 0, 0, 0);
+      for (int sg = 0; sg < CT / 4; ++sg) {
+        // A: head (lane & 3) x tokens 4sg..4sg+3; B: tokens x channel 64*hf + lane
+        const s16x4_t pa = *reinterpret_cast<const s16x4_t*>(L.pl + (lane & 3) * CT + 4 * sg);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const s16x4_t vb = *reinterpret_cast<const s16x4_t*>(L.vt + (64 * hf + lane) * VT_STRIDE + 4 * sg);
+          O[hf] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(pa, vb, O[hf], 0, 0, 0);
+        }
+      }
+    } else {
+      s16x4_t pa = {0, 0, 0, 0};
+      if (hh_ok) pa = *reinterpret_cast<const s16x4_t*>(L.pl + hh * CT + 4 * grp);
+#pragma unroll
+      for (int nn = 0; nn < NO; ++nn) {
+        const s16x4_t vb = *reinterpret_cast<const s16x4_t*>(L.vt + (16 * nn + col) * VT_STRIDE + 4 * grp);
+        O[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[nn], 0, 0, 0);
+      }
     }
   };
   // one chunk: stage it (its bytes are in rc), refill rc DEPTH chunks ahead,
@@ -446,7 +513,7 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
     cur = nxt;
   };
 
-  static_assert(NPF == 5, "prefetch slots are unrolled by hand");
+  static_assert(NPF == 4 && CT == 16, "prefetch slots are unrolled by hand; masks fit slot 0");
   if (DEPTH == 2) {
     Regs ra, rb;
     Chunk cur = next_chunk(cu, lane);
@@ -471,14 +538,30 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeArgs a) {
 #pragma unroll
   for (int j = 0; j < JG; ++j) {
     const int hd = 4 * j + grp;
-    if (hd < a.G) {
+    if (hd < a.G && col == 0) {
       const uint64_t pi = (uint64_t)(b * a.hq + h * a.G + hd) * a.splits + sp;
-      if (col == 0) {
-        a.part_ml[2 * pi] = m_run[j];
-        a.part_ml[2 * pi + 1] = l_run[j];
-      }
+      a.part_ml[2 * pi] = m_run[j];
+      a.part_ml[2 * pi + 1] = l_run[j];
+    }
+  }
+  if (JG == 1) {
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn) a.part_acc[pi * D + 16 * nn + col] = O[nn][j];
+    for (int i = 0; i < 4; ++i) {
+      if (i < a.G) {
+        const uint64_t pi = (uint64_t)(b * a.hq + h * a.G + i) * a.splits + sp;
+        a.part_acc[pi * D + lane] = O[0][i];
+        a.part_acc[pi * D + 64 + lane] = O[1][i];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < JG; ++j) {
+      const int hd = 4 * j + grp;
+      if (hd < a.G) {
+        const uint64_t pi = (uint64_t)(b * a.hq + h * a.G + hd) * a.splits + sp;
+#pragma unroll
+        for (int nn = 0; nn < NO; ++nn) a.part_acc[pi * D + 16 * nn + col] = O[nn][j];
+      }
     }
   }
 }

@@ -10,6 +10,8 @@ correctness:
                                          specified operation by operation)
   -fno-gpu-flush-denormals-to-zero       IEEE fp32 denormals
   -target-feature -packed-fp32-ops       no packed fp32 instructions
+  -fno-strict-aliasing                   LDS staging buffers are written and
+                                         read through different types
 """
 import os
 import subprocess
@@ -26,7 +28,8 @@ ARCH = "gfx950"
 
 def command(out=LIB, extra=()):
     return [HIPCC, "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero", "-Xclang", "-target-feature",
+            "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero", "-fno-strict-aliasing",
+            "-Xclang", "-target-feature",
             "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-result",
             "-I", os.path.join(ROOT, "include"), *extra, *SOURCES, "-o", out]
 

@@ -29,7 +29,11 @@
 // the p.v product uses the 16-block 4x4x4 MFMA instead (block b = lanes
 // 4b..4b+3; A[i][k] at lane 4b+i item k, B[k][j] at lane 4b+j item k, D[i][j]
 // at lane 4b+j item i): head i x channel (64*half + lane) accumulates over 4
-// tokens per instruction, so the output needs 8 instead of 32 registers.
+// tokens per instruction, so the output needs 8 instead of 32 registers.  Its
+// B operand (4 tokens x 1 channel per lane) comes from the row-major dense V
+// tile through ds_read_b64_tr_b16: within each 16-lane group, element r of
+// lane i is element (i & 3) of the 8 bytes read by lane 4r + (i >> 2), so lane
+// l reads row 4*sg + ((l & 15) >> 2), channels 64*half + 16*(l >> 4) + 4*(l & 3).
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -42,6 +46,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int CT = 16;                            // kept tokens per chunk
 constexpr int STAGE = CT * 16 + CT * (256 + 16) + 32;  // masks + padded rows + window pad
@@ -49,7 +54,8 @@ constexpr int STAGE = CT * 16 + CT * (256 + 16) + 32;  // masks + padded rows + 
 // (masked) or 16*256 bytes (dense) = 256 slots.
 constexpr int NPF = 4;
 constexpr float RESCALE_SLACK = 8.0f;             // log2 units the running max may lag
-constexpr int VT_STRIDE = 20;                     // u16 per channel row of the dense V tile
+constexpr int VT_STRIDE = 20;                     // u16 per channel row of the transposed V tile (G > 4)
+constexpr int VR_STRIDE = 136;                    // u16 per token row of the row-major V tile (G <= 4)
 constexpr int WAVES = 4;
 #ifndef KVC_DECODE_MIN_BLOCKS
 #define KVC_DECODE_MIN_BLOCKS 2  // workgroups per CU the register budget is sized for
@@ -69,18 +75,20 @@ struct DecodeArgs {
   float sl2;  // scale * log2(e)
 };
 
-// Per-wave LDS.  The dense V tile is written from the registers that the V
-// stage's reads produced, so it can share the V stage's storage without
-// ordering anything that is not already ordered; the K stage stays separate
-// so that K- and V-side LDS traffic overlap.
+// Per-wave LDS.  The loop is software-pipelined: while the K side of chunk
+// i+1 is computed, the V side of chunk i is, so V stages and probabilities
+// are double-buffered.  A V stage's dense tile is written from the registers
+// its own reads produced, so the two share storage.
 constexpr int VBYTES = (STAGE > D * VT_STRIDE * 2) ? STAGE : D * VT_STRIDE * 2;
+static_assert(CT * VR_STRIDE * 2 <= VBYTES, "row-major V tile fits the V stage");
+union VStage {
+  u32x4_t v[VBYTES / 16];
+  uint16_t vt[VBYTES / 2];  // dense V of the chunk, [channel][token]
+};
 struct WaveLds {
   u32x4_t k[STAGE / 16];
-  union {
-    u32x4_t v[VBYTES / 16];
-    uint16_t vt[VBYTES / 2];  // dense V of the chunk, [channel][token]
-  };
-  uint16_t pl[16 * CT];       // probabilities, [head][token]
+  VStage vs[2];             // chunk i's V side and chunk i+1's, alternating
+  uint16_t pl[2][16 * CT];  // probabilities, [head][token], alternating
 };
 
 __device__ __forceinline__ float dpp_f(float v, int ctrl) {
@@ -107,7 +115,13 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ void lds_order() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Ordering of this wave's LDS accesses.  LDS executes a wave's DS
+// instructions in issue order, so a later read sees an earlier write (also
+// from another lane) and a later write cannot overtake an earlier read; the
+// compiler keeps accesses that may overlap in program order (the library is
+// built with -fno-strict-aliasing because the staging buffers are read and
+// written through different types).  No fence is needed.
+__device__ __forceinline__ void lds_order() {}
 
 // Selector table entry for a mask nibble n (channels 0..3 of the nibble):
 // dword d holds the v_perm_b32 selectors of channels 2d and 2d+1, i.e. bytes
@@ -142,19 +156,23 @@ __device__ void build_lut_entry(uint32_t n, uint32_t* e) {
 // zeroed at the end.
 struct Expand {
   uint32_t a[4][3], b[4][3];  // windows of the low / high nibble
-  uint32_t sa[4], sb[4];      // 0 or 16 (odd start)
+  uint32_t sa[4], sb[4];      // shift: 16 * (start & 1) in bits 4:0
   uint2 tl[4], th[4];         // selectors of the low / high nibble
 };
 
 __device__ __forceinline__ void expand_issue(const uint8_t* st, int col, int grp, int nt, int c,
                                              const uint2* lut, Expand& e) {
-  const u32x4_t m = *reinterpret_cast<const u32x4_t*>(st + 16 * col);
-  const uint32_t* row = reinterpret_cast<const uint32_t*>(st + 16 * nt + (2 * c + 16) * col);
+  // masked rows read their mask; dense rows (c == 128) behave as all-ones
+  // masks; tokens past the chunk behave as empty masks (all outputs zero)
+  const bool hm = c < D;
+  const u32x4_t ml = *reinterpret_cast<const u32x4_t*>(st + 16 * (hm ? col : 0));
+  const uint32_t* row = reinterpret_cast<const uint32_t*>(st + (hm ? 16 * nt : 0) + (2 * c + 16) * col);
+  const bool live = col < nt;
   uint32_t pre = 0;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    const uint32_t mw = m[kk];
-    const uint32_t mb = (mw >> (8 * grp)) & 0xFFu;
+    const uint32_t mw = hm ? ml[kk] : 0xFFFFFFFFu;
+    const uint32_t mb = live ? (mw >> (8 * grp)) & 0xFFu : 0u;
     const uint32_t ra = pre + __popc(mw & ((1u << (8 * grp)) - 1u));
     const uint32_t rb = ra + __popc(mb & 0xFu);
     pre += __popc(mw);
@@ -165,8 +183,8 @@ __device__ __forceinline__ void expand_issue(const uint8_t* st, int col, int grp
       e.a[kk][i] = wa[i];
       e.b[kk][i] = wb[i];
     }
-    e.sa[kk] = (ra & 1u) << 4;
-    e.sb[kk] = (rb & 1u) << 4;
+    e.sa[kk] = ra << 4;  // alignbit uses bits 4:0, i.e. 16 * (ra & 1)
+    e.sb[kk] = rb << 4;
     e.tl[kk] = lut[mb & 0xFu];
     e.th[kk] = lut[mb >> 4];
   }
@@ -185,28 +203,13 @@ __device__ __forceinline__ u32x4_t expand_finish(const Expand& e, int kk) {
   return o;
 }
 
-// Dense rows (all 128 channels kept): the 4 x 16 bytes of this lane.
-__device__ __forceinline__ void dense_issue(const uint8_t* st, int col, int grp, u32x4_t* o) {
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    o[kk] = *reinterpret_cast<const u32x4_t*>(st + col * (256 + 16) + 16 * (4 * kk + grp));
-}
-
-// The 4 x 8 dense channels of this lane's token, zero past the chunk.
+// The 4 x 8 dense channels of this lane's token (zero past the chunk).
 __device__ __forceinline__ void expand_side(const uint8_t* st, int col, int grp, int nt, int c,
                                             const uint2* lut, u32x4_t* o) {
-  if (c < D) {
-    Expand e;
-    expand_issue(st, col, grp, nt, c, lut, e);
+  Expand e;
+  expand_issue(st, col, grp, nt, c, lut, e);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) o[kk] = expand_finish(e, kk);
-  } else {
-    dense_issue(st, col, grp, o);
-  }
-  if (col >= nt) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) o[kk] = u32x4_t{0u, 0u, 0u, 0u};
-  }
+  for (int kk = 0; kk < 4; ++kk) o[kk] = expand_finish(e, kk);
 }
 
 // One chunk to stream: K part and V part each = [masks 16*nt][values 2*c*nt]
@@ -367,7 +370,7 @@ __global__ __launch_bounds__(256, KVC_DECODE_MIN_BLOCKS) void k_decode_split(Dec
   const int grp = lane >> 4, col = lane & 15;
   const int b = s / a.hkv, h = s - b * a.hkv;
   WaveLds& L = wl[wv];
-  for (int i = lane; i < 16 * CT; i += 64) L.pl[i] = 0;
+  for (int i = lane; i < 2 * 16 * CT; i += 64) (&L.pl[0][0])[i] = 0;
 
   // A operand of the score MFMA: row col holds head hh (zero if none)
   const int hh = 4 * (col & 3) + (col >> 2);
@@ -406,135 +409,138 @@ __global__ __launch_bounds__(256, KVC_DECODE_MIN_BLOCKS) void k_decode_split(Dec
   if (cu.di < cu.d1) fetch_descs(cu, lane);
 
   const uint8_t* sk8 = reinterpret_cast<const uint8_t*>(L.k);
-  const uint8_t* sv8 = reinterpret_cast<const uint8_t*>(L.v);
 
-  // computes one staged chunk
-  auto compute = [&](const Chunk& cur) {
-    const int nt = cur.nt, c = cur.c;
-
-    // scores of the chunk: S^T = Q Kd^T
+  // K side of a chunk staged in L.k: scores, online-softmax state, and the
+  // probabilities into L.pl[pb].  The running max of a head moves only when
+  // some score exceeds it by RESCALE_SLACK (so p <= 2^RESCALE_SLACK); the
+  // accumulator rescale factor of each head is returned in alpha (1 = none)
+  // and applied by the caller once the previous chunk's p.v is in.  Each lane
+  // keeps its own part of the denominator; the parts are summed at the end.
+  auto k_side = [&](const Chunk& ch, int pb, float* alpha) -> bool {
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
     {
       u32x4_t kb[4];
-      expand_side(sk8, col, grp, nt, c, lut, kb);
+      expand_side(sk8, col, grp, ch.nt, ch.c, lut, kb);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], __builtin_bit_cast(bf16x8_t, kb[kk]),
                                                        sacc, 0, 0, 0);
     }
-    // online softmax, one head per (16-lane row, item j); the running max
-    // moves only when the chunk max exceeds it by RESCALE_SLACK (so p <=
-    // 2^RESCALE_SLACK), and the accumulators are rescaled only when some
-    // head's max moved
+    bool resc = false;
 #pragma unroll
     for (int j = 0; j < JG; ++j) {
       const int hd = 4 * j + grp;
-      const bool ok = col < nt && hd < a.G;
+      const bool ok = col < ch.nt && hd < a.G;
       const float x = ok ? sacc[j] * a.sl2 : -INFINITY;
-      const float cm = row16_max(x);
-      const float mo = m_run[j];
-      const float mn = (cm > mo + RESCALE_SLACK) ? cm : mo;
-      const float alpha = (mn == mo) ? 1.0f : __builtin_amdgcn_exp2f(mo - mn);
-      const float p = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x - mn);
-      l_run[j] = l_run[j] * alpha + row16_sum(p);
-      m_run[j] = mn;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-        if (JG == 1) {
-          // every lane holds all four heads: alpha of head i sits in row i
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float ai = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 16 * i));
-            O[0][i] *= ai;
-            O[1][i] *= ai;
-          }
-        } else {
-#pragma unroll
-          for (int nn = 0; nn < NO; ++nn) O[nn][j] *= alpha;
-        }
+      alpha[j] = 1.0f;
+      if (__builtin_amdgcn_ballot_w64(x > m_run[j] + RESCALE_SLACK)) {
+        const float cm = row16_max(x);
+        const float mo = m_run[j];
+        const float mn = (cm > mo + RESCALE_SLACK) ? cm : mo;
+        alpha[j] = (mn == mo) ? 1.0f : __builtin_amdgcn_exp2f(mo - mn);
+        l_run[j] *= alpha[j];
+        m_run[j] = mn;
+        resc = true;
       }
-      if (hd < a.G) L.pl[hd * CT + col] = (uint16_t)f2bf(p);
+      const float p = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x - m_run[j]);
+      l_run[j] += p;
+      if (hd < a.G) L.pl[pb][hd * CT + col] = (uint16_t)f2bf(p);
     }
-    // dense V of the chunk, transposed into LDS
-    {
-      u32x4_t vb[4];
-      expand_side(sv8, col, grp, nt, c, lut, vb);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        uint16_t* dst = L.vt + (8 * (4 * kk + grp)) * VT_STRIDE + col;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dst[(2 * i) * VT_STRIDE] = (uint16_t)(vb[kk][i] & 0xFFFFu);
-          dst[(2 * i + 1) * VT_STRIDE] = (uint16_t)(vb[kk][i] >> 16);
-        }
-      }
-    }
-    lds_order();
-    // O += P Vd
+    return resc;
+  };
+  // V side of a chunk staged in L.vs[vb]: dense V tile (over the stage),
+  // then O += P V with the probabilities in L.pl[vb].
+  auto v_side = [&](const Chunk& ch, int vb) {
+    VStage& S = L.vs[vb];
+    u32x4_t vv[4];
+    expand_side(reinterpret_cast<const uint8_t*>(S.v), col, grp, ch.nt, ch.c, lut, vv);
     if (JG == 1) {
+      // row-major dense tile [token][channel]
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        *reinterpret_cast<u32x4_t*>(S.vt + col * VR_STRIDE + 8 * (4 * kk + grp)) = vv[kk];
+      const int trow = (lane & 15) >> 2, tcol = 16 * (lane >> 4) + 4 * (lane & 3);
 #pragma unroll
       for (int sg = 0; sg < CT / 4; ++sg) {
         // A: head (lane & 3) x tokens 4sg..4sg+3; B: tokens x channel 64*hf + lane
-        const s16x4_t pa = *reinterpret_cast<const s16x4_t*>(L.pl + (lane & 3) * CT + 4 * sg);
+        const s16x4_t pa = *reinterpret_cast<const s16x4_t*>(L.pl[vb] + (lane & 3) * CT + 4 * sg);
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const s16x4_t vb = *reinterpret_cast<const s16x4_t*>(L.vt + (64 * hf + lane) * VT_STRIDE + 4 * sg);
-          O[hf] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(pa, vb, O[hf], 0, 0, 0);
+          const uint16_t* src = S.vt + (4 * sg + trow) * VR_STRIDE + 64 * hf + tcol;
+          const s16x4_t w = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)src);
+          O[hf] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(pa, w, O[hf], 0, 0, 0);
         }
       }
     } else {
+      // transposed dense tile [channel][token]
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        uint16_t* dst = S.vt + (8 * (4 * kk + grp)) * VT_STRIDE + col;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dst[(2 * i) * VT_STRIDE] = (uint16_t)(vv[kk][i] & 0xFFFFu);
+          dst[(2 * i + 1) * VT_STRIDE] = (uint16_t)(vv[kk][i] >> 16);
+        }
+      }
       s16x4_t pa = {0, 0, 0, 0};
-      if (hh_ok) pa = *reinterpret_cast<const s16x4_t*>(L.pl + hh * CT + 4 * grp);
+      if (hh_ok) pa = *reinterpret_cast<const s16x4_t*>(L.pl[vb] + hh * CT + 4 * grp);
 #pragma unroll
       for (int nn = 0; nn < NO; ++nn) {
-        const s16x4_t vb = *reinterpret_cast<const s16x4_t*>(L.vt + (16 * nn + col) * VT_STRIDE + 4 * grp);
-        O[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[nn], 0, 0, 0);
+        const s16x4_t w = *reinterpret_cast<const s16x4_t*>(S.vt + (16 * nn + col) * VT_STRIDE + 4 * grp);
+        O[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, w, O[nn], 0, 0, 0);
       }
     }
   };
-  // one chunk: stage it (its bytes are in rc), refill rc DEPTH chunks ahead,
-  // then compute it from LDS
-  auto body = [&](Chunk& cur, Chunk& nxt, Regs& rc) {
-    lds_order();
-    commit(cur, lane, rc, L.k, L.v);
-    const Chunk far = next_chunk(cu, lane);
-    prefetch(far, lane, rc);
-    lds_order();
-    compute(cur);
-    cur = nxt;
-    nxt = far;
-  };
-  auto body1 = [&](Chunk& cur, Regs& rc) {
-    lds_order();
-    commit(cur, lane, rc, L.k, L.v);
-    const Chunk nxt = next_chunk(cu, lane);
-    prefetch(nxt, lane, rc);
-    lds_order();
-    compute(cur);
-    cur = nxt;
+  auto rescale = [&](const float* alpha) {
+    if (JG == 1) {
+      // every lane holds all four heads: alpha of head i sits in row i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[0]), 16 * i));
+        O[0][i] *= ai;
+        O[1][i] *= ai;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < JG; ++j)
+#pragma unroll
+        for (int nn = 0; nn < NO; ++nn) O[nn][j] *= alpha[j];
+    }
   };
 
   static_assert(NPF == 4 && CT == 16, "prefetch slots are unrolled by hand; masks fit slot 0");
-  if (DEPTH == 2) {
-    Regs ra, rb;
-    Chunk cur = next_chunk(cu, lane);
-    prefetch(cur, lane, ra);
+  Regs rg;
+  Chunk cur = next_chunk(cu, lane);
+  if (cur.valid) {
+    prefetch(cur, lane, rg);
+    commit(cur, lane, rg, L.k, L.vs[0].v);
     Chunk nxt = next_chunk(cu, lane);
-    prefetch(nxt, lane, rb);
-    while (cur.valid) {
-      body(cur, nxt, ra);
-      if (!cur.valid) break;
-      body(cur, nxt, rb);
+    prefetch(nxt, lane, rg);
+    lds_order();
+    float alpha[JG];
+    if (k_side(cur, 0, alpha)) rescale(alpha);
+    int vb = 0;
+    // iteration: stage chunk i+1, load chunk i+2, K side of i+1, V side of i
+    while (nxt.valid) {
+      lds_order();
+      commit(nxt, lane, rg, L.k, L.vs[vb ^ 1].v);
+      const Chunk far = next_chunk(cu, lane);
+      prefetch(far, lane, rg);
+      lds_order();
+      const bool resc = k_side(nxt, vb ^ 1, alpha);
+      v_side(cur, vb);
+      if (resc) rescale(alpha);
+      cur = nxt;
+      nxt = far;
+      vb ^= 1;
     }
-  } else {
-    Regs ra;
-    Chunk cur = next_chunk(cu, lane);
-    prefetch(cur, lane, ra);
-    Chunk none;
-    none.valid = false;
-    while (cur.valid) body1(cur, ra);
+    lds_order();
+    v_side(cur, vb);
   }
 
   // partial state of this split
+#pragma unroll
+  for (int j = 0; j < JG; ++j) l_run[j] = row16_sum(l_run[j]);
 #pragma unroll
   for (int j = 0; j < JG; ++j) {
     const int hd = 4 * j + grp;

@@ -1,0 +1,140 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py
+times (library-chosen split count), on sampled streams the oracle computes
+one by one: every selection output of a sampled stream is compared bit for
+bit (scores, descriptors, the stream's whole packed byte range) and its
+decode output within the attention tolerance.  Properties that hold at any
+size are checked on all streams (descriptor sanity, used bytes within the
+budget, score mass = G * W per stream)."""
+import numpy as np
+import pytest
+import torch
+
+import compressed_kv_cache_compress_amd as kvc
+from compressed_kv_cache_compress_amd import DESC_DTYPE, gen, kara, runtime
+from helpers import SCALE, check_attention, say
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _sampled(cfg, streams_to_check):
+    c = gen.CONFIGS[cfg]
+    S = c["S"]
+    strat = gen.table9(S)
+    budget = gen.budget_bytes(c["budget_pct"], S)
+    say(f"[fullsize] {cfg}: generating B={c['B']} N={c['N']}")
+    w = gen.make_workload(cfg, device="cuda")
+    say(f"[fullsize] {cfg}: kv_compress + kv_attend_decode")
+    r = runtime.compress(w["K"], w["V"], w["Qw"], seg_tokens=S, strategies=strat,
+                         budget_bytes=budget, scale=float(SCALE), want_scores=True)
+    out, lse = runtime.decode(w["q"], r.packed, r.desc, n_kv_heads=c["Hkv"],
+                              max_desc_per_stream=r.n_seg, scale=float(SCALE))
+    torch.cuda.synchronize()
+    desc = r.desc_host()
+    used = r.used.cpu().numpy()
+    cap = r.layout.stream_capacity
+    G, W = w["G"], w["W"]
+    # properties on every stream
+    assert np.all(used <= r.layout.n_seg * r.layout.max_seg_bytes)
+    feas = [i for i in range(len(strat)) if (r.layout.feasible_mask >> i) & 1]
+    assert np.isin(desc["strategy"], feas).all()
+    assert np.all(desc["seg_tokens"] == S) and np.all(desc["offset"] % 16 == 0)
+    mass = r.scores.double().sum(dim=1).cpu().numpy()
+    assert np.all(np.abs(mass - G * W) <= 1e-3 * G * W), mass
+    say(f"  strategies {np.bincount(desc['strategy'].ravel(), minlength=9).tolist()}")
+    packed = r.packed
+    Hkv = c["Hkv"]
+    for s in streams_to_check:
+        b, h = divmod(s, Hkv)
+        say(f"  oracle stream {s} (b={b}, kv head {h})")
+        Ks, Vs = gen.u16(w["K"][b, h]), gen.u16(w["V"][b, h])
+        Qs = gen.u16(w["Qw"][b, h * G:(h + 1) * G])
+        o = O.compress_stream(Ks, Vs, Qs, S=S, strategies=strat, budget_bytes=budget, scale=SCALE,
+                              base_offset=s * cap)
+        assert np.array_equal(r.scores[s].cpu().numpy().view(np.uint32), o["scores"].view(np.uint32))
+        assert np.array_equal(desc[s].view(np.uint8), o["desc"].view(np.uint8))
+        assert used[s] == o["used"]
+        got = packed[s * cap:s * cap + o["used"]].cpu().numpy()
+        assert np.array_equal(got, o["packed"])
+        q = gen.u16(w["q"][b, h * G:(h + 1) * G])
+        local = o["desc"].copy()
+        local["offset"] -= s * cap
+        ref, rlse = O.decode_stream(q, o["packed"], local, SCALE)
+        check_attention(out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G], ref, rlse,
+                        f"{cfg} stream {s}")
+    del w, r, packed
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_llama8b():
+    _sampled("llama8b", [0, 5])
+
+
+def test_fullsize_batched128k():
+    _sampled("batched128k", [0, 77])
+
+
+def test_fullsize_million():
+    _sampled("million", [3])
+
+
+def test_fullsize_kara():
+    """Kara workload: B 64, GQA 32/8, prompt 16384 + 8192 generated, window 512,
+    retention 20 % (13 of each 64-token region), Token2Chunk alpha 3 gamma 16,
+    an event every 64 steps (127 events compress generated tokens); decode over
+    dense prompt + compressed segments + dense tail."""
+    k = gen.KARA
+    say("[fullsize] kara: generating")
+    w = gen.make_kara(device="cuda")
+    say("[fullsize] kara: 127 events + decode")
+    cache = kara.build_cache(w["K"], w["V"], w["Qall"], prompt=w["prompt"], gen=w["gen"],
+                             window=k["window"], delta=k["delta"], protect=k["protect"], seg=64,
+                             retention_pct=k["retention_pct"], alpha=k["alpha"], gamma=k["gamma"],
+                             scale=float(SCALE))
+    out, lse = runtime.decode(w["q"], cache.packed, cache.desc, n_kv_heads=w["Hkv"],
+                              max_desc_per_stream=cache.max_desc, scale=float(SCALE))
+    torch.cuda.synchronize()
+    assert cache.n_events == 127 and cache.T == 13
+    desc = cache.desc.cpu().numpy().view(DESC_DTYPE).reshape(w["B"] * w["Hkv"], cache.max_desc)
+    lay = cache.layout
+    assert np.all(desc[:, lay["n_prompt_desc"]:lay["n_prompt_desc"] + 127]["n_tok"] == 13)
+    assert desc["n_tok"].astype(np.int64).sum(axis=1).tolist() == [16384 + 127 * 13 + 64] * desc.shape[0]
+    G, Hkv = w["G"], w["Hkv"]
+    prompt, L = w["prompt"], w["L"]
+    for s in (0, 301):
+        b, h = divmod(s, Hkv)
+        say(f"  oracle stream {s}: prompt, 127 events, tail")
+        Kf, Vf = gen.u16(w["K"][b, h]), gen.u16(w["V"][b, h])
+        Qf = gen.u16(w["Qall"][b, h * G:(h + 1) * G])
+        zq = np.zeros((G, 1, 128), np.uint16)
+        parts, descs = [], []
+        off = 0
+        pr = O.compress_stream(Kf[:prompt], Vf[:prompt], zq, S=256, strategies=[(256, 128)],
+                               budget_bytes=4 * 256 * 128, scale=SCALE)
+        parts.append(pr["packed"])
+        d = pr["desc"].copy()
+        descs.append(d)
+        off += pr["used"]
+        for (Le, w0, rb) in lay["schedule"]:
+            e = O.compress_stream(Kf[w0:w0 + 512], Vf[w0:w0 + 512], Qf[:, w0:w0 + 512], S=64,
+                                  strategies=[(13, 128)], budget_bytes=4 * 64 * 128, scale=SCALE,
+                                  region_begin=rb, region_len=64, t2c_alpha=3, t2c_gamma=16,
+                                  base_offset=off)
+            parts.append(e["packed"])
+            descs.append(e["desc"])
+            off += e["used"]
+        tl = O.compress_stream(Kf[L - 64:], Vf[L - 64:], zq, S=64, strategies=[(64, 128)],
+                               budget_bytes=4 * 64 * 128, scale=SCALE, base_offset=off)
+        parts.append(tl["packed"])
+        descs.append(tl["desc"])
+        ref_buf = np.concatenate(parts)
+        ref_desc = np.concatenate(descs)
+        got = cache.packed[s * cache.stream_bytes:s * cache.stream_bytes + ref_buf.size].cpu().numpy()
+        assert np.array_equal(got, ref_buf)
+        gd = desc[s].copy()
+        gd["offset"] -= s * cache.stream_bytes
+        assert np.array_equal(gd.view(np.uint8), ref_desc.view(np.uint8))
+        q = gen.u16(w["q"][b, h * G:(h + 1) * G])
+        ref, rlse = O.decode_stream(q, ref_buf, ref_desc, SCALE)
+        check_attention(out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G], ref, rlse,
+                        f"kara stream {s}")

@@ -45,8 +45,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-splits", type=int, default=0, help="0 = library choice")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured decode HBM bytes per launch (from rocprofv3 pmc)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "decode_batched128k_traffic.md"),
+                    help="summary with the measured decode HBM bytes per launch (rocprofv3 pmc)")
     return ap.parse_args()
 
 
@@ -59,6 +59,30 @@ def algorithmic_decode_bytes(desc, S, B, Hq, splits):
     q = out = B * Hq * 128 * 2
     partials = 2 * B * Hq * splits * (2 + 128) * 4
     return int(seg + q + out + partials)
+
+
+def decode_source_hash():
+    import hashlib
+    src = os.path.join(ROOT, "compressed_kv_cache_compress_amd", "csrc", "kvc_decode.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()
+
+
+def measured_traffic(path):
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when there is none or the decode source changed since it was taken."""
+    if not path or not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kvc_decode.hip sha256") != decode_source_hash():
+        return None
+    try:
+        return int(vals["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, S, strategies, budget, scale):
@@ -157,9 +181,7 @@ def main():
     alg = algorithmic_decode_bytes(dh, S, B, Hq, L.decode_splits)
     t_dec = float(dec_ms.mean()) * 1e-3
     achieved = alg / t_dec / 1e9
-    traffic = None
-    if a.traffic and os.path.exists(a.traffic):
-        traffic = json.load(open(a.traffic)).get("bytes_per_launch")
+    traffic = measured_traffic(a.traffic) if a.config == "batched128k" and not a.decode_splits else None
     packed_total = int(used.sum().item())
     res = {
         "metric": "compressed decode attention: KV tokens/s and achieved HBM GB/s (% of peak)",

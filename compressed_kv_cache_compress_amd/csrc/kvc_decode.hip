@@ -4,8 +4,8 @@
 //
 // Work split: one wave per (stream, split); a split is a contiguous range of
 // the stream's descriptors.  Four independent waves share a workgroup only to
-// share one LDS table.  Each wave walks its descriptors in chunks of 16 kept
-// tokens:
+// share one LDS table.  Each wave walks its descriptors in chunks of up to 16
+// kept tokens (fewer for rows wider than 96 channels):
 //   * the next chunk's K and V bytes (masks + compact values) are loaded into
 //     registers while the current chunk is computed, then written to LDS;
 //   * every kept vector is expanded from (bitmask, compact bf16 values) to a
@@ -48,11 +48,31 @@ typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-constexpr int CT = 16;                            // kept tokens per chunk
-constexpr int STAGE = CT * 16 + CT * (256 + 16) + 32;  // masks + padded rows + window pad
-// uint4 prefetch slots per lane: a chunk is at most 16*16 + 16*2*120 bytes
-// (masked) or 16*256 bytes (dense) = 256 slots.
-constexpr int NPF = 4;
+constexpr int CT = 16;  // MFMA columns: at most this many kept tokens per chunk
+#ifndef KVC_DECODE_SLOTS
+#define KVC_DECODE_SLOTS 3
+#endif
+// uint4 prefetch slots per lane and side: a chunk side (masks + values) is at
+// most 64 * NPF slots of 16 bytes.
+constexpr int NPF = KVC_DECODE_SLOTS;
+// Tokens per chunk for c kept channels: at most CT, at most what the prefetch
+// slots hold, and at most 3584 staged bytes (16 tokens up to c = 96), so that
+// wide rows do not set the staging size.  Narrow rows get 16 tokens; dense
+// rows 12.
+constexpr int slots_per_token(int c) { return (c < D ? 1 : 0) + c / 8; }
+constexpr int staged_per_token(int c) { return (c < D ? 16 : 0) + 2 * c + 16; }
+constexpr int cmin(int x, int y) { return x < y ? x : y; }
+constexpr int cmax(int x, int y) { return x > y ? x : y; }
+constexpr int chunk_tokens(int c) {
+  return cmin(CT, cmin(64 * NPF / slots_per_token(c), 3584 / staged_per_token(c)));
+}
+constexpr int stage_bytes() {
+  int m = 0;
+  for (int c = 8; c <= D; c += 8) m = cmax(m, chunk_tokens(c) * staged_per_token(c));
+  return m + 32;  // + pad: a window may read 12 bytes past a row's last element
+}
+// Staging bytes of one side of a chunk: [masks 16 * nt][rows (2c + 16) * nt].
+constexpr int STAGE = (stage_bytes() + 15) / 16 * 16;
 constexpr float RESCALE_SLACK = 8.0f;             // log2 units the running max may lag
 constexpr int VT_STRIDE = 20;                     // u16 per channel row of the transposed V tile (G > 4)
 constexpr int VR_STRIDE = 136;                    // u16 per token row of the row-major V tile (G <= 4)
@@ -79,17 +99,30 @@ struct DecodeArgs {
 // i+1 is computed, the V side of chunk i is, so V stages and probabilities
 // are double-buffered.  A V stage's dense tile is written from the registers
 // its own reads produced, so the two share storage.
-constexpr int VBYTES = (STAGE > D * VT_STRIDE * 2) ? STAGE : D * VT_STRIDE * 2;
-static_assert(CT * VR_STRIDE * 2 <= VBYTES, "row-major V tile fits the V stage");
-union VStage {
-  u32x4_t v[VBYTES / 16];
-  uint16_t vt[VBYTES / 2];  // dense V of the chunk, [channel][token]
+// JG == 1: row-major dense V tile [token][VR_STRIDE]; otherwise transposed
+// [channel][VT_STRIDE].  Either is written over the V stage it is expanded from.
+template <int JG>
+struct VStage {
+  static constexpr int BYTES = cmax(STAGE, JG == 1 ? CT * VR_STRIDE * 2 : D * VT_STRIDE * 2);
+  union {
+    u32x4_t v[BYTES / 16];
+    uint16_t vt[BYTES / 2];
+  };
 };
+template <int JG>
 struct WaveLds {
   u32x4_t k[STAGE / 16];
-  VStage vs[2];             // chunk i's V side and chunk i+1's, alternating
-  uint16_t pl[2][16 * CT];  // probabilities, [head][token], alternating
+  VStage<JG> vs[2];               // chunk i's V side and chunk i+1's, alternating
+  uint16_t pl[2][4 * JG * CT];    // probabilities, [head][token], alternating
 };
+
+// Tokens per chunk for c = 8 * index.
+__constant__ uint8_t c_chunk_tok[17] = {
+    CT,               chunk_tokens(8),   chunk_tokens(16),  chunk_tokens(24),  chunk_tokens(32),
+    chunk_tokens(40), chunk_tokens(48),  chunk_tokens(56),  chunk_tokens(64),  chunk_tokens(72),
+    chunk_tokens(80), chunk_tokens(88),  chunk_tokens(96),  chunk_tokens(104), chunk_tokens(112),
+    chunk_tokens(120), chunk_tokens(128)};
+static_assert(chunk_tokens(64) == CT && chunk_tokens(D) >= 12, "stage sizing");
 
 __device__ __forceinline__ float dpp_f(float v, int ctrl) {
   switch (ctrl) {  // the control must be a constant
@@ -165,9 +198,10 @@ __device__ __forceinline__ void expand_issue(const uint8_t* st, int col, int grp
   // masked rows read their mask; dense rows (c == 128) behave as all-ones
   // masks; tokens past the chunk behave as empty masks (all outputs zero)
   const bool hm = c < D;
-  const u32x4_t ml = *reinterpret_cast<const u32x4_t*>(st + 16 * (hm ? col : 0));
-  const uint32_t* row = reinterpret_cast<const uint32_t*>(st + (hm ? 16 * nt : 0) + (2 * c + 16) * col);
   const bool live = col < nt;
+  const int rc = live ? col : 0;  // rows past the chunk read row 0 (their mask is empty)
+  const u32x4_t ml = *reinterpret_cast<const u32x4_t*>(st + 16 * (hm ? rc : 0));
+  const uint32_t* row = reinterpret_cast<const uint32_t*>(st + (hm ? 16 * nt : 0) + (2 * c + 16) * rc);
   uint32_t pre = 0;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -254,7 +288,7 @@ __device__ __forceinline__ void prefetch(const Chunk& ch, int lane, Regs& r) {
   prefetch_slot<0>(ch, lane, r);
   prefetch_slot<1>(ch, lane, r);
   prefetch_slot<2>(ch, lane, r);
-  prefetch_slot<3>(ch, lane, r);
+  if constexpr (NPF > 3) prefetch_slot<3>(ch, lane, r);
 }
 
 // Slot j of the [masks | values] stream goes to LDS slot j (masks) or, for
@@ -276,7 +310,7 @@ __device__ __forceinline__ void commit(const Chunk& ch, int lane, const Regs& r,
   commit_slot<0>(ch, lane, r, sk, sv);
   commit_slot<1>(ch, lane, r, sk, sv);
   commit_slot<2>(ch, lane, r, sk, sv);
-  commit_slot<3>(ch, lane, r, sk, sv);
+  if constexpr (NPF > 3) commit_slot<3>(ch, lane, r, sk, sv);
 }
 
 // Descriptor cursor of one wave.  Descriptors are fetched 64 at a time, one
@@ -335,7 +369,8 @@ __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
     if (cu.T == 0) return ch;
   }
   const int c = cu.c, t0 = cu.t0;
-  const int nt = min(CT, cu.T - t0);
+  const int ct = c_chunk_tok[c >> 3];
+  const int nt = min(ct, cu.T - t0);
   const int nm = c < D ? nt : 0;
   ch.kmask = cu.kmask + 16 * t0;
   ch.vmask = cu.vmask + 16 * t0;
@@ -347,14 +382,14 @@ __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
   ch.n16 = nm + (2 * c * nt) / 16;
   ch.magic = c_row_magic[c >> 3];
   ch.valid = true;
-  cu.t0 = t0 + CT;
+  cu.t0 = t0 + ct;
   return ch;
 }
 
 template <int JG, int DEPTH>
-__global__ __launch_bounds__(256, KVC_DECODE_MIN_BLOCKS) void k_decode_split(DecodeArgs a) {
+__global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_decode_split(DecodeArgs a) {
   __shared__ uint2 lut[16];
-  __shared__ WaveLds wl[WAVES];
+  __shared__ WaveLds<JG> wl[WAVES];
   const int tid = threadIdx.x;
   if (tid < 16) {
     uint32_t e[2];
@@ -369,8 +404,8 @@ __global__ __launch_bounds__(256, KVC_DECODE_MIN_BLOCKS) void k_decode_split(Dec
   const int s = item / a.splits, sp = item - s * a.splits;
   const int grp = lane >> 4, col = lane & 15;
   const int b = s / a.hkv, h = s - b * a.hkv;
-  WaveLds& L = wl[wv];
-  for (int i = lane; i < 2 * 16 * CT; i += 64) (&L.pl[0][0])[i] = 0;
+  WaveLds<JG>& L = wl[wv];
+  for (int i = lane; i < 2 * 4 * JG * CT; i += 64) (&L.pl[0][0])[i] = 0;
 
   // A operand of the score MFMA: row col holds head hh (zero if none)
   const int hh = 4 * (col & 3) + (col >> 2);
@@ -451,7 +486,7 @@ __global__ __launch_bounds__(256, KVC_DECODE_MIN_BLOCKS) void k_decode_split(Dec
   // V side of a chunk staged in L.vs[vb]: dense V tile (over the stage),
   // then O += P V with the probabilities in L.pl[vb].
   auto v_side = [&](const Chunk& ch, int vb) {
-    VStage& S = L.vs[vb];
+    VStage<JG>& S = L.vs[vb];
     u32x4_t vv[4];
     expand_side(reinterpret_cast<const uint8_t*>(S.v), col, grp, ch.nt, ch.c, lut, vv);
     if (JG == 1) {
@@ -508,7 +543,7 @@ __global__ __launch_bounds__(256, KVC_DECODE_MIN_BLOCKS) void k_decode_split(Dec
     }
   };
 
-  static_assert(NPF == 4 && CT == 16, "prefetch slots are unrolled by hand; masks fit slot 0");
+  static_assert((NPF == 3 || NPF == 4) && CT == 16, "prefetch slots are unrolled by hand; masks fit slot 0");
   Regs rg;
   Chunk cur = next_chunk(cu, lane);
   if (cur.valid) {

@@ -115,8 +115,11 @@ kvc_status compress_layout(const kvc_params* p, const Shape& sh, kvc_layout* L, 
 
 uint32_t choose_splits(const kvc_params* p, const Shape& sh, uint32_t maxd) {
   if (p->decode_splits) return p->decode_splits;
-  // about 8 waves per CU on 256 CUs, at least one descriptor per split
-  uint32_t want = (2048u + (uint32_t)sh.streams - 1) / (uint32_t)sh.streams;
+  // one wave per (stream, split); a CU holds 12 decode waves for groups of up
+  // to 4 q heads and 8 for larger groups (LDS and registers): fill 256 CUs
+  // once, with at least one descriptor per split
+  const uint32_t waves = sh.G <= 4 ? 3072u : 2048u;
+  uint32_t want = (waves + (uint32_t)sh.streams - 1) / (uint32_t)sh.streams;
   if (want > maxd) want = maxd;
   if (want < 1) want = 1;
   if (want > 1024) want = 1024;

@@ -47,114 +47,160 @@ __device__ __forceinline__ void load_row_f32(const uint16_t* __restrict__ row, f
   }
 }
 
-// q . k as one fma chain over ascending channels; q is wave-uniform.
-__device__ __forceinline__ float dot_chain(const uint16_t* __restrict__ qrow, const float* kf) {
-  const uint32_t* q32 = reinterpret_cast<const uint32_t*>(qrow);
-  float acc = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    const uint32_t w = q32[i];
-    acc = __builtin_fmaf(__uint_as_float(w << 16), kf[2 * i], acc);
-    acc = __builtin_fmaf(__uint_as_float(w & 0xFFFF0000u), kf[2 * i + 1], acc);
-  }
-  return acc;
-}
-
+// Shapes and inputs of the scoring kernels; outputs and workspace arrays are
+// separate restrict-qualified arguments (so uniform loads become scalar).
 struct ScoreArgs {
   const uint16_t* K;
   const uint16_t* Qw;
-  float* part_m;
-  float* part_z;
-  float* norm_m;
-  float* norm_iz;
-  float* scores;
-  float* scores_out;
   uint64_t kv_stride, qw_stride;
   int hkv, hq, G, W, nq, nblk, region_begin, region_len;
   float scale;
 };
 
-__device__ __forceinline__ const uint16_t* qrow_of(const ScoreArgs& a, int s, int qi) {
+// Window queries to fp32, [stream][g * W + w][128], so that the scoring
+// kernels read them with scalar loads and no per-use conversion.
+// grid (G * W, streams), 64 threads: lane = channel pair.
+__global__ __launch_bounds__(64) void k_q_convert(ScoreArgs a, float* __restrict__ qf) {
+  const int qi = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
   const int b = s / a.hkv, h = s - b * a.hkv;
   const int g = qi / a.W, w = qi - g * a.W;
-  return a.Qw + (uint64_t)(b * a.hq + h * a.G + g) * a.qw_stride + (uint64_t)w * D;
+  const uint16_t* src = a.Qw + (uint64_t)(b * a.hq + h * a.G + g) * a.qw_stride + (uint64_t)w * D;
+  const uint32_t v = reinterpret_cast<const uint32_t*>(src)[lane];
+  float2 o;
+  o.x = __uint_as_float(v << 16);
+  o.y = __uint_as_float(v & 0xFFFF0000u);
+  reinterpret_cast<float2*>(qf + ((uint64_t)s * a.nq + qi) * D)[lane] = o;
+}
+
+constexpr int QB = 4;  // window queries scored together (independent fma chains)
+
+// Logits of NQ consecutive window queries (rows qr, qr + 128, ...) against
+// this lane's key: one fma chain per query over ascending channels, times
+// scale.
+template <int NQ>
+__device__ __forceinline__ void logits(const float* __restrict__ qr, const float* kf, float scale,
+                                       float* l) {
+  float acc[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) acc[j] = 0.0f;
+#pragma unroll
+  for (int ch = 0; ch < D; ++ch)
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) acc[j] = __builtin_fmaf(qr[j * D + ch], kf[ch], acc[j]);
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) l[j] = acc[j] * scale;
+}
+
+// Block maximum and pairwise exp-sum of NQ window queries q0.. over the 64
+// tokens of a block (lane = token).
+template <int NQ>
+__device__ __forceinline__ void block_partials(const float* __restrict__ qs, int q0, const float* kf,
+                                               const ScoreArgs& a, int s, int blk, int lane,
+                                               float* __restrict__ part_m,
+                                               float* __restrict__ part_z) {
+  float l[NQ], mb[NQ], z[NQ];
+  logits<NQ>(qs + (uint64_t)q0 * D, kf, a.scale, l);
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) mb[j] = max64(l[j]);
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) z[j] = tree_sum64(spec_exp2((l[j] - mb[j]) * KVC_LOG2E));
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    if (lane == j) {
+      const uint64_t o = ((uint64_t)s * a.nq + q0 + j) * a.nblk + blk;
+      part_m[o] = mb[j];
+      part_z[o] = z[j];
+    }
+  }
 }
 
 // grid (nblk, streams), 64 threads: lane = token of the 64-token block.
-__global__ __launch_bounds__(64) void k_score_partials(ScoreArgs a) {
+__global__ __launch_bounds__(64) void k_score_partials(ScoreArgs a, const float* __restrict__ qf,
+                                                       float* __restrict__ part_m,
+                                                       float* __restrict__ part_z) {
   const int blk = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
   const int t = blk * BLK + lane;
   float kf[D];
   load_row_f32(a.K + (uint64_t)s * a.kv_stride + (uint64_t)t * D, kf);
-  for (int qi = 0; qi < a.nq; ++qi) {
-    const float l = dot_chain(qrow_of(a, s, qi), kf) * a.scale;
-    const float mb = wave_max(l);
-    const float e = spec_exp2((l - mb) * KVC_LOG2E);
-    const float z = tree_sum_lanes(e);
-    if (lane == 0) {
-      const uint64_t o = ((uint64_t)s * a.nq + qi) * a.nblk + blk;
-      a.part_m[o] = mb;
-      a.part_z[o] = z;
-    }
-  }
+  const float* qs = qf + (uint64_t)s * a.nq * D;
+  int q0 = 0;
+  for (; q0 + QB <= a.nq; q0 += QB) block_partials<QB>(qs, q0, kf, a, s, blk, lane, part_m, part_z);
+  for (; q0 < a.nq; ++q0) block_partials<1>(qs, q0, kf, a, s, blk, lane, part_m, part_z);
 }
 
-// grid (nq, streams), 64 threads: lane l owns the contiguous blocks
-// [l*ch, (l+1)*ch) of the zero-padded power-of-two block range; its pairwise
-// sum is built bottom-up with a binary-counter stack, then combined across
-// lanes in the same tree order.
-__global__ __launch_bounds__(64) void k_score_normalise(ScoreArgs a) {
+// grid (nq, streams), 64 threads.  m = max of the block maxima; Z = pairwise
+// tree over the blocks (zero-padded to a power of two) of z_b exp(m_b - m):
+// groups of 64 consecutive blocks are summed across lanes, then the group
+// sums are combined pairwise in LDS.
+constexpr int NORM_GROUPS = (1 << 22) / BLK / 64;  // n_ctx <= 2^22
+__global__ __launch_bounds__(64) void k_score_normalise(ScoreArgs a, const float* __restrict__ part_m,
+                                                        const float* __restrict__ part_z,
+                                                        float* __restrict__ norm_m,
+                                                        float* __restrict__ norm_iz) {
+  __shared__ float grp[NORM_GROUPS];
   const int qi = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
-  const float* pm = a.part_m + ((uint64_t)s * a.nq + qi) * a.nblk;
-  const float* pz = a.part_z + ((uint64_t)s * a.nq + qi) * a.nblk;
-  int np = 1;
-  while (np < a.nblk) np <<= 1;
-  const int ch = np >= 64 ? np / 64 : 1;
-  const int b0 = lane * ch;
+  const float* pm = part_m + ((uint64_t)s * a.nq + qi) * a.nblk;
+  const float* pz = part_z + ((uint64_t)s * a.nq + qi) * a.nblk;
   float mx = -INFINITY;
-  for (int i = 0; i < ch; ++i)
-    if (b0 + i < a.nblk) mx = fmaxf(mx, pm[b0 + i]);
-  const float m = wave_max(mx);
-  float stk[16];
-  for (int i = 0; i < ch; ++i) {
-    const int bb = b0 + i;
-    float v = (bb < a.nblk) ? pz[bb] * spec_exp2((pm[bb] - m) * KVC_LOG2E) : 0.0f;
-    int lvl = 0;
-    for (int j = i; j & 1; j >>= 1) {
-      v = stk[lvl] + v;
-      ++lvl;
-    }
-    stk[lvl] = v;
+  for (int b = lane; b < a.nblk; b += 64) mx = fmaxf(mx, pm[b]);
+  const float m = max64(mx);
+  const int ng = (a.nblk + 63) / 64;
+  int np = 1;
+  while (np < ng) np <<= 1;
+  for (int i = 0; i < ng; ++i) {
+    const int b = 64 * i + lane;
+    const float v = b < a.nblk ? pz[b] * spec_exp2((pm[b] - m) * KVC_LOG2E) : 0.0f;
+    const float t = tree_sum64(v);
+    if (lane == 0) grp[i] = t;
   }
-  int top = 0;
-  while ((1 << top) < ch) ++top;
-  const float part = stk[top];
-  const float Z = tree_sum_lanes(part);
+  for (int i = ng + lane; i < np; i += 64) grp[i] = 0.0f;
+  // in-order LDS within the wave: level w reads [0, 2w) before writing [0, w)
+  for (int w = np >> 1; w >= 1; w >>= 1)
+    for (int j = lane; j < w; j += 64) grp[j] = grp[2 * j] + grp[2 * j + 1];
   if (lane == 0) {
-    a.norm_m[(uint64_t)s * a.nq + qi] = m;
-    a.norm_iz[(uint64_t)s * a.nq + qi] = 1.0f / Z;
+    norm_m[(uint64_t)s * a.nq + qi] = m;
+    norm_iz[(uint64_t)s * a.nq + qi] = 1.0f / grp[0];
   }
 }
 
-// grid (ceil(region_len/64), streams), 64 threads: lane = region token.
-__global__ __launch_bounds__(64) void k_token_scores(ScoreArgs a) {
+// Adds the probabilities NQ window queries q0.. give this lane's key to sc,
+// in query order.
+template <int NQ>
+__device__ __forceinline__ void add_scores(const float* __restrict__ qs, int q0, const float* kf,
+                                           float scale, const float* __restrict__ nm,
+                                           const float* __restrict__ ni, float& sc) {
+  float l[NQ];
+  logits<NQ>(qs + (uint64_t)q0 * D, kf, scale, l);
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const float e = spec_exp2((l[j] - nm[q0 + j]) * KVC_LOG2E);
+    sc = sc + e * ni[q0 + j];
+  }
+}
+
+// grid (ceil(region_len/64), streams), 64 threads: lane = region token.  The
+// score is accumulated one window query at a time, in query order.
+__global__ __launch_bounds__(64) void k_token_scores(ScoreArgs a, const float* __restrict__ qf,
+                                                     const float* __restrict__ norm_m,
+                                                     const float* __restrict__ norm_iz,
+                                                     float* __restrict__ scores,
+                                                     float* __restrict__ scores_out) {
   const int s = blockIdx.y, lane = threadIdx.x;
   const int tr = blockIdx.x * 64 + lane;
   const bool valid = tr < a.region_len;
   const int t = a.region_begin + (valid ? tr : 0);
   float kf[D];
   load_row_f32(a.K + (uint64_t)s * a.kv_stride + (uint64_t)t * D, kf);
-  const float* nm = a.norm_m + (uint64_t)s * a.nq;
-  const float* ni = a.norm_iz + (uint64_t)s * a.nq;
+  const float* qs = qf + (uint64_t)s * a.nq * D;
+  const float* nm = norm_m + (uint64_t)s * a.nq;
+  const float* ni = norm_iz + (uint64_t)s * a.nq;
   float sc = 0.0f;
-  for (int qi = 0; qi < a.nq; ++qi) {
-    const float l = dot_chain(qrow_of(a, s, qi), kf) * a.scale;
-    const float e = spec_exp2((l - nm[qi]) * KVC_LOG2E);
-    sc = sc + e * ni[qi];
-  }
+  int q0 = 0;
+  for (; q0 + QB <= a.nq; q0 += QB) add_scores<QB>(qs, q0, kf, a.scale, nm, ni, sc);
+  for (; q0 < a.nq; ++q0) add_scores<1>(qs, q0, kf, a.scale, nm, ni, sc);
   if (valid) {
-    a.scores[(uint64_t)s * a.region_len + tr] = sc;
-    if (a.scores_out) a.scores_out[(uint64_t)s * a.region_len + tr] = sc;
+    scores[(uint64_t)s * a.region_len + tr] = sc;
+    if (scores_out) scores_out[(uint64_t)s * a.region_len + tr] = sc;
   }
 }
 
@@ -174,37 +220,47 @@ struct SelectArgs {
 
 constexpr int SEL_TOKENS = 16;  // tokens per block (x2 vectors, 8 per wave)
 
+// NC = number of distinct channel counts; the NC threshold searches of a
+// vector run interleaved (independent ballot chains).
+template <int NC>
 __global__ __launch_bounds__(256) void k_channel_select(SelectArgs a) {
   const int s = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   for (int r = wv; r < 2 * SEL_TOKENS; r += 4) {
     const int tr = blockIdx.x * SEL_TOKENS + (r >> 1);
     const int kv = r & 1;
-    if (tr >= a.region_len) break;
+    if (tr >= a.region_len) break;  // wave-uniform
     const uint16_t* row = (kv ? a.V : a.K) + (uint64_t)s * a.kv_stride +
                           (uint64_t)(a.region_begin + tr) * D;
     const uint32_t b0 = row[lane], b1 = row[lane + 64];
     const uint32_t k0 = b0 & 0x7FFFu, k1 = b1 & 0x7FFFu;
     const float x0 = bf2f(b0), x1 = bf2f(b1);
     const float q0 = x0 * x0, q1 = x1 * x1;
-    const float Eall = tree_sum_lanes(q0) + tree_sum_lanes(q1);
-    for (int u = 0; u < a.nc; ++u) {
-      const uint32_t c = (uint32_t)a.cvals[u];
-      // the c-th largest key, bit by bit from the top
-      uint32_t tau = 0;
-      for (int bit = 14; bit >= 0; --bit) {
-        const uint32_t cand = tau | (1u << bit);
+    // tree over channels 0..127 = tree(0..63) + tree(64..127)
+    const float Eall = tree_sum64(q0) + tree_sum64(q1);
+    // the c-th largest key, bit by bit from the top
+    uint32_t tau[NC];
+#pragma unroll
+    for (int u = 0; u < NC; ++u) tau[u] = 0;
+    for (int bit = 14; bit >= 0; --bit) {
+#pragma unroll
+      for (int u = 0; u < NC; ++u) {
+        const uint32_t cand = tau[u] | (1u << bit);
         const uint32_t cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand));
-        if (cnt >= c) tau = cand;
+        tau[u] = (cnt >= (uint32_t)a.cvals[u]) ? cand : tau[u];
       }
-      const uint32_t ngt = __popcll(__ballot(k0 > tau)) + __popcll(__ballot(k1 > tau));
+    }
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const uint32_t c = (uint32_t)a.cvals[u];
+      const uint32_t ngt = __popcll(__ballot(k0 > tau[u])) + __popcll(__ballot(k1 > tau[u]));
       const uint32_t need = c - ngt;
-      const uint64_t e0 = __ballot(k0 == tau), e1 = __ballot(k1 == tau);
+      const uint64_t e0 = __ballot(k0 == tau[u]), e1 = __ballot(k1 == tau[u]);
       const uint32_t rk0 = lanes_below(e0);
       const uint32_t rk1 = (uint32_t)__popcll(e0) + lanes_below(e1);
-      const bool s0 = k0 > tau || (k0 == tau && rk0 < need);
-      const bool s1 = k1 > tau || (k1 == tau && rk1 < need);
+      const bool s0 = k0 > tau[u] || (k0 == tau[u] && rk0 < need);
+      const bool s1 = k1 > tau[u] || (k1 == tau[u] && rk1 < need);
       const uint64_t m0 = __ballot(s0), m1 = __ballot(s1);
-      const float Ec = tree_sum_lanes(s0 ? q0 : 0.0f) + tree_sum_lanes(s1 ? q1 : 0.0f);
+      const float Ec = tree_sum64(s0 ? q0 : 0.0f) + tree_sum64(s1 ? q1 : 0.0f);
       if (lane == 0) {
         const uint64_t o = (((uint64_t)s * a.region_len + tr) * a.nc + u) * 2 + kv;
         uint4 w;
@@ -330,10 +386,18 @@ __global__ __launch_bounds__(64) void k_segment_choose(ChooseArgs a) {
     if (valid[j]) s_sc[t] = sc[j];
   }
   __syncthreads();
+  // Without the objective output only feasible strategies matter (and a
+  // forced one, which is feasible or else replaced by the choice).  Keep
+  // sets depend on T only, so consecutive strategies with the same T share
+  // them.
+  int last_T = -1;
+  bool kp[4] = {false, false, false, false};
   for (int i = 0; i < a.n_strat; ++i) {
+    if (!a.objective && !((a.feasible_mask >> i) & 1u)) continue;
     const int T = a.sT[i], c = a.sc[i];
-    bool kp[4];
-    if (T == 0) {
+    if (T == last_T) {
+      // same keep set as the previous strategy computed
+    } else if (T == 0) {
       for (int j = 0; j < NJ; ++j) kp[j] = false;
     } else if (T >= S) {
       for (int j = 0; j < NJ; ++j) kp[j] = valid[j];
@@ -349,6 +413,7 @@ __global__ __launch_bounds__(64) void k_segment_choose(ChooseArgs a) {
     } else {
       top_t_flags(key, valid, NJ, T, kp);
     }
+    last_T = T;
     // objective: pairwise tree over the segment's slots
     float tj[4];
     for (int j = 0; j < NJ; ++j) {
@@ -362,7 +427,7 @@ __global__ __launch_bounds__(64) void k_segment_choose(ChooseArgs a) {
         }
         term = sc[j] * (0.5f * (rk + rv));
       }
-      tj[j] = tree_sum_lanes(term, width);
+      tj[j] = width == 64 ? tree_sum64(term) : tree_sum_lanes(term, width);
     }
     float J;
     if (NJ == 1)
@@ -522,12 +587,6 @@ hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
     ScoreArgs sa;
     sa.K = p.K;
     sa.Qw = p.Qw;
-    sa.part_m = p.part_m;
-    sa.part_z = p.part_z;
-    sa.norm_m = p.norm_m;
-    sa.norm_iz = p.norm_iz;
-    sa.scores = p.scores;
-    sa.scores_out = p.scores_out;
     sa.kv_stride = p.kv_stride;
     sa.qw_stride = p.qw_stride;
     sa.hkv = p.hkv;
@@ -539,9 +598,14 @@ hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
     sa.region_begin = p.region_begin;
     sa.region_len = p.region_len;
     sa.scale = p.scale;
-    hipLaunchKernelGGL(k_score_partials, dim3(p.nblk, p.streams), dim3(64), 0, st, sa);
-    hipLaunchKernelGGL(k_score_normalise, dim3(p.nq, p.streams), dim3(64), 0, st, sa);
-    hipLaunchKernelGGL(k_token_scores, dim3((p.region_len + 63) / 64, p.streams), dim3(64), 0, st, sa);
+    hipLaunchKernelGGL(k_q_convert, dim3(p.nq, p.streams), dim3(64), 0, st, sa, p.qf);
+    hipLaunchKernelGGL(k_score_partials, dim3(p.nblk, p.streams), dim3(64), 0, st, sa,
+                       (const float*)p.qf, p.part_m, p.part_z);
+    hipLaunchKernelGGL(k_score_normalise, dim3(p.nq, p.streams), dim3(64), 0, st, sa,
+                       (const float*)p.part_m, (const float*)p.part_z, p.norm_m, p.norm_iz);
+    hipLaunchKernelGGL(k_token_scores, dim3((p.region_len + 63) / 64, p.streams), dim3(64), 0, st,
+                       sa, (const float*)p.qf, (const float*)p.norm_m, (const float*)p.norm_iz,
+                       p.scores, p.scores_out);
   }
   if (p.nc > 0) {
     SelectArgs se;
@@ -554,8 +618,17 @@ hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
     se.region_len = p.region_len;
     se.nc = p.nc;
     for (int i = 0; i < MAX_NC; ++i) se.cvals[i] = p.cvals[i];
-    hipLaunchKernelGGL(k_channel_select, dim3((p.region_len + SEL_TOKENS - 1) / SEL_TOKENS, p.streams),
-                       dim3(256), 0, st, se);
+    const dim3 grid((p.region_len + SEL_TOKENS - 1) / SEL_TOKENS, p.streams);
+    switch (p.nc) {
+      case 1: hipLaunchKernelGGL(k_channel_select<1>, grid, dim3(256), 0, st, se); break;
+      case 2: hipLaunchKernelGGL(k_channel_select<2>, grid, dim3(256), 0, st, se); break;
+      case 3: hipLaunchKernelGGL(k_channel_select<3>, grid, dim3(256), 0, st, se); break;
+      case 4: hipLaunchKernelGGL(k_channel_select<4>, grid, dim3(256), 0, st, se); break;
+      case 5: hipLaunchKernelGGL(k_channel_select<5>, grid, dim3(256), 0, st, se); break;
+      case 6: hipLaunchKernelGGL(k_channel_select<6>, grid, dim3(256), 0, st, se); break;
+      case 7: hipLaunchKernelGGL(k_channel_select<7>, grid, dim3(256), 0, st, se); break;
+      default: hipLaunchKernelGGL(k_channel_select<8>, grid, dim3(256), 0, st, se); break;
+    }
   }
   ChooseArgs ca;
   ca.scores = p.scores;

@@ -26,9 +26,10 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 // a correctly rounded IEEE fp32 operation, so the value is reproducible on any
 // IEEE machine that evaluates the same sequence.
 __device__ __forceinline__ float spec_exp2(float y) {
-  if (!(y >= -125.0f)) return 0.0f;
-  const float n = __builtin_rintf(y);
-  const float f = y - n;
+  // branch-free: evaluate at max(y, -125) and select
+  const float yc = fmaxf(y, -125.0f);
+  const float n = __builtin_rintf(yc);
+  const float f = yc - n;
   float p = 0x1.ffcbfcp-17f;
   p = __builtin_fmaf(p, f, 0x1.430912p-13f);
   p = __builtin_fmaf(p, f, 0x1.5d87fep-10f);
@@ -37,7 +38,8 @@ __device__ __forceinline__ float spec_exp2(float y) {
   p = __builtin_fmaf(p, f, 0x1.ebfbe0p-3f);
   p = __builtin_fmaf(p, f, 0x1.62e430p-1f);
   p = __builtin_fmaf(p, f, 1.0f);
-  return __builtin_ldexpf(p, (int)n);
+  const float r = __builtin_ldexpf(p, (int)n);
+  return (y >= -125.0f) ? r : 0.0f;
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
@@ -53,6 +55,43 @@ __device__ __forceinline__ float tree_sum_lanes(float v, int width = 64) {
 __device__ __forceinline__ float wave_max(float v) {
   for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
   return v;
+}
+
+// Cross-lane moves inside DPP rows of 16 lanes (controls: quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row_half_mirror, row_mirror).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Pairwise-tree sum over the 64 lanes of a full wave (every lane active),
+// returned wave-uniform.  Same order as tree_sum_lanes: lane pairs, quads,
+// 8-lane halves and 16-lane rows by DPP (after each step the lanes of a group
+// agree, so a mirror reaches the partner group), then (r0 + r1) + (r2 + r3)
+// over the four rows.
+__device__ __forceinline__ float tree_sum64(float v) {
+  v = v + dpp_mov<0xB1>(v);
+  v = v + dpp_mov<0x4E>(v);
+  v = v + dpp_mov<0x141>(v);
+  v = v + dpp_mov<0x140>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Maximum over the 64 lanes of a full wave, returned wave-uniform.
+__device__ __forceinline__ float max64(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, dpp_mov<0x140>(v));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // Count of set bits of a 64-bit lane mask below the calling lane.

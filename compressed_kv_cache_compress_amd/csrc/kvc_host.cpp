@@ -109,6 +109,8 @@ kvc_status compress_layout(const kvc_params* p, const Shape& sh, kvc_layout* L, 
   ws += align_up((uint64_t)sh.streams * p->region_len * (uint64_t)nc * 2 * 16, kAlign);
   ws += align_up((uint64_t)sh.streams * p->region_len * (uint64_t)nc * 2 * 4, kAlign);
   ws += align_up((uint64_t)sh.streams * n_seg * ((S + 31) / 32) * 4, kAlign);
+  // window queries converted to fp32 once per call
+  if (p->n_win) ws += align_up((uint64_t)sh.streams * nq * KVC_HEAD_DIM * 4, kAlign);
   L->compress_ws_bytes = ws;
   return nfeas ? KVC_OK : KVC_E_BUDGET;
 }
@@ -190,7 +192,7 @@ kvc_status kv_compress(const kvc_params* p, const uint16_t* K, const uint16_t* V
   st = compress_layout(p, sh, &L, &c.nc, c.cvals, c.su);
   if (st != KVC_OK) return st;
   const bool scoring = L.needs_scoring || scores || objective;
-  if (!K || !V || !packed || !desc || (scoring && !Qwin)) return KVC_E_INVALID;
+  if (!K || !V || !packed || !desc || (scoring && (!Qwin || !p->n_win))) return KVC_E_INVALID;
   if (!aligned16(K) || !aligned16(V) || !aligned16(Qwin) || !aligned16(packed) ||
       !aligned16(desc) || !aligned16(ws))
     return KVC_E_ALIGN;
@@ -256,6 +258,7 @@ kvc_status kv_compress(const kvc_params* p, const uint16_t* K, const uint16_t* V
   c.masks = reinterpret_cast<uint32_t*>(take(S64 * c.region_len * (uint64_t)c.nc * 2 * 16));
   c.rho = reinterpret_cast<float*>(take(S64 * c.region_len * (uint64_t)c.nc * 2 * 4));
   c.keep = reinterpret_cast<uint32_t*>(take(S64 * c.n_seg * ((c.S + 31) / 32) * 4));
+  c.qf = p->n_win ? reinterpret_cast<float*>(take(S64 * c.nq * D * 4)) : nullptr;
   if (launch_compress(c, stream) != hipSuccess) return KVC_E_HIP;
   return KVC_OK;
 }

@@ -38,6 +38,7 @@ struct CompressPlan {
   float* objective;
   // workspace carve-up (device pointers)
   float *part_m, *part_z, *norm_m, *norm_iz, *scores, *rho;
+  float* qf;              // window queries in fp32, [streams][G * W][128]
   uint32_t* masks;        // [streams][region_len][nc][2][4]
   uint32_t* keep;         // [streams][n_seg][S/32]
 };

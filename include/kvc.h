@@ -162,7 +162,8 @@ kvc_status kv_layout_query(const kvc_params* p, kvc_layout* out);
  * Arguments:
  *  K, V              device, layout above.
  *  Qwin              device [batch][n_q_heads][n_win][128]; may be NULL when
- *                    layout.needs_scoring == 0.
+ *                    layout.needs_scoring == 0 and neither scores nor
+ *                    objective is requested (scoring needs n_win >= 1).
  *  forced_strategy   device [streams][n_seg] u8 or NULL; entry < n_strategies
  *                    forces that strategy if it fits the budget (else flag
  *                    bit7 and choose); KVC_DESC_CHOOSE lets the library choose.

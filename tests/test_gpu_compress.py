@@ -110,6 +110,21 @@ def test_compress_forced_and_rejected():
     assert d["flags"][2] & 0x80 and d["flags"][3] & 0x80 and not d["flags"][6] & 0x80
 
 
+def test_compress_many_channel_counts():
+    """Six distinct channel counts below 128 (six interleaved threshold
+    searches per vector), odd token counts, choice under a mid budget and a
+    forced pattern."""
+    w = gen.make_workload("llama8b", B=1, N=2048)
+    S = 128
+    strat = [(37, 8), (100, 56), (17, 96), (128, 104), (45, 112), (99, 120), (77, 128), (128, 128)]
+    _compare(w, S=S, strategies=strat, budget=gen.budget_bytes(40, S), label="six c, choice")
+    nseg = 2048 // S
+    streams = w["B"] * w["Hkv"]
+    forced = np.array([[(s + 3 * j) % len(strat) for j in range(nseg)] for s in range(streams)],
+                      np.uint8)
+    _compare(w, S=S, strategies=strat, budget=4 * S * 128, forced=forced, label="six c, forced")
+
+
 def test_compress_kara_event_strided_window():
     """One Kara event: window = last 512 positions of a longer buffer (strided
     views), region [384, 448), T = 13 of 64, Token2Chunk alpha 3, gamma 16."""

@@ -124,3 +124,20 @@ def test_decode_ragged_descriptor_lists_and_empty_streams():
     check_attention(out, lse, ref, rlse, "ragged")
     G = w["G"]
     assert np.all(np.isneginf(lse.cpu().numpy().reshape(-1)[5 * G:6 * G]))
+
+
+def test_decode_wide_rows_and_chunk_tails():
+    """Rows wider than 96 channels take 12-14 tokens per chunk: every channel
+    count class (8, 56, 96, 104, 112, 120, dense) with token counts that leave
+    ragged chunk tails, forced per segment, at several split counts."""
+    w = gen.make_workload("llama8b", B=1, N=2048)
+    S = 128
+    strategies = [(37, 8), (100, 56), (17, 96), (128, 104), (45, 112), (99, 120), (77, 128),
+                  (128, 128), (1, 120), (29, 104)]
+    streams = w["B"] * w["Hkv"]
+    n_seg = w["N"] // S
+    forced = np.array([[(s + 3 * j) % len(strategies) for j in range(n_seg)] for s in range(streams)],
+                      np.uint8)
+    for splits in (0, 3):
+        worst, _, _ = _run(w, S, strategies, 4 * S * 128, splits=splits, forced=forced)
+        say(f"  splits={splits} worst rel err {worst:.2e}")

@@ -116,12 +116,6 @@ struct WaveLds {
   uint16_t pl[2][4 * JG * CT];    // probabilities, [head][token], alternating
 };
 
-// Tokens per chunk for c = 8 * index.
-__constant__ uint8_t c_chunk_tok[17] = {
-    CT,               chunk_tokens(8),   chunk_tokens(16),  chunk_tokens(24),  chunk_tokens(32),
-    chunk_tokens(40), chunk_tokens(48),  chunk_tokens(56),  chunk_tokens(64),  chunk_tokens(72),
-    chunk_tokens(80), chunk_tokens(88),  chunk_tokens(96),  chunk_tokens(104), chunk_tokens(112),
-    chunk_tokens(120), chunk_tokens(128)};
 static_assert(chunk_tokens(64) == CT && chunk_tokens(D) >= 12, "stage sizing");
 
 __device__ __forceinline__ float dpp_f(float v, int ctrl) {
@@ -259,11 +253,6 @@ struct Chunk {
   bool valid;
 };
 
-// ceil(2^20 / k) for k = c/8 in 1..16.
-__constant__ uint32_t c_row_magic[17] = {
-    0u,      1048576u, 524288u, 349526u, 262144u, 209716u, 174763u, 149797u, 131072u,
-    116509u, 104858u,  95326u,  87382u,  80660u,  74899u,  69906u,  65536u};
-
 // The next chunk's bytes, one uint4 of K and one of V per slot and lane.
 struct Regs {
   u32x4_t k[NPF], v[NPF];
@@ -323,10 +312,16 @@ struct Cursor {
   const uint8_t* packed;
   int di, d1, base;         // next descriptor, end, first descriptor held in the lanes
   uint32_t w0, w1, w2;      // this lane's descriptor (base + lane): offset lo/hi, n_tok|n_ch<<16
+  uint32_t w3;              // its chunk geometry: tokens per chunk | row magic << 5
   // current segment
   const uint8_t *kmask, *kval, *vmask, *vval;  // at token 0
-  int T, c, t0;
+  int T, c, t0, ct;
+  uint32_t magic;
 };
+
+// ceil(2^20 / k): value slot v of a stage with k slots per row is in row
+// (v * magic) >> 20 for v < 16 * k.
+constexpr uint32_t row_magic(int k) { return (1048576u + (uint32_t)k - 1u) / (uint32_t)k; }
 
 __device__ __forceinline__ void fetch_descs(Cursor& cu, int lane) {
   cu.base = cu.di;
@@ -335,6 +330,11 @@ __device__ __forceinline__ void fetch_descs(Cursor& cu, int lane) {
   cu.w0 = d[0];
   cu.w1 = d[1];
   cu.w2 = d[2];
+  // per-descriptor chunk geometry, computed once per 64 descriptors so that
+  // the chunk loop reads it with readlane instead of a memory lookup
+  const int c = (int)(d[2] >> 16) & ~7;
+  const int cc = c < 8 ? 8 : (c > D ? D : c);
+  cu.w3 = (uint32_t)chunk_tokens(cc) | (row_magic(cc >> 3) << 5);
 }
 
 // Advances to the next non-empty chunk; returns its description.
@@ -353,7 +353,10 @@ __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
       if (T > 0) {
         const uint32_t lo = __builtin_amdgcn_readlane(cu.w0, sl);
         const uint32_t hi = __builtin_amdgcn_readlane(cu.w1, sl);
+        const uint32_t geo = __builtin_amdgcn_readlane(cu.w3, sl);
         const int c = (int)(tc >> 16);
+        cu.ct = (int)(geo & 31u);
+        cu.magic = geo >> 5;
         const uint32_t mb = c < D ? 16u * T : 0u;
         const uint8_t* base = cu.packed + (((uint64_t)hi << 32) | lo);
         cu.kmask = base;
@@ -368,9 +371,9 @@ __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
     }
     if (cu.T == 0) return ch;
   }
-  const int c = cu.c, t0 = cu.t0;
-  const int ct = c_chunk_tok[c >> 3];
-  const int nt = min(ct, cu.T - t0);
+  const int c = cu.c, t0 = cu.t0, T = cu.T;
+  const int ct = cu.ct;
+  const int nt = min(ct, T - t0);
   const int nm = c < D ? nt : 0;
   ch.kmask = cu.kmask + 16 * t0;
   ch.vmask = cu.vmask + 16 * t0;
@@ -380,7 +383,7 @@ __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
   ch.c = c;
   ch.nm = nm;
   ch.n16 = nm + (2 * c * nt) / 16;
-  ch.magic = c_row_magic[c >> 3];
+  ch.magic = cu.magic;
   ch.valid = true;
   cu.t0 = t0 + ct;
   return ch;

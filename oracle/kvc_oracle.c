@@ -640,4 +640,116 @@ void orc_decode_stream(int G, const uint16_t* q, const uint8_t* packed, const or
   free(l);
 }
 
+/* ------------------------------------------------------------------ */
+/* Query-aware segment selection at decode time ([M] Fig. 6 caption:    */
+/* stage 2 runs during decode before each attention layer; Sec. 5.3:    */
+/* PackedAttention performs sequence compression in each attention      */
+/* layer of the decode stage; Fig. 8: token selection rates 6.25 % and  */
+/* 12.5 %; Quest, the query-aware page selection the page compares      */
+/* against).  Reading: per segment, the per-channel maximum and minimum */
+/* of its decoded keys (a dropped channel counts as 0); per q head an   */
+/* upper bound of q.k over the segment, sum over channels of            */
+/* max(q kmax, q kmin); a segment's score is the largest bound over     */
+/* the group's heads; the k best segments by (score desc, index asc)    */
+/* are kept, in index order.                                            */
+/* ------------------------------------------------------------------ */
+
+/* summary: [n_desc][2][128] bf16 bits: kmax, kmin of each descriptor's
+ * kept K vectors (zeros for an empty descriptor). */
+void orc_summarize_stream(const uint8_t* packed, const orc_desc* desc, int n_desc,
+                          uint16_t* summary) {
+  for (int i = 0; i < n_desc; ++i) {
+    const int T = desc[i].n_tok, c = desc[i].n_ch;
+    uint16_t* smax = summary + (size_t)i * 2 * ORC_D;
+    uint16_t* smin = smax + ORC_D;
+    const uint8_t* base = packed + desc[i].offset;
+    const uint8_t* kval = base + (c < ORC_D ? 16 * T : 0);
+    float mx[ORC_D], mn[ORC_D];
+    for (int ch = 0; ch < ORC_D; ++ch) {
+      mx[ch] = -INFINITY;
+      mn[ch] = INFINITY;
+    }
+    for (int t = 0; t < T; ++t) {
+      const uint8_t* mk = c < ORC_D ? base + 16 * t : NULL;
+      const uint8_t* vals = kval + (size_t)2 * c * t;
+      int r = 0;
+      for (int ch = 0; ch < ORC_D; ++ch) {
+        float x = 0.0f;
+        int on = mk ? ((mk[ch >> 3] >> (ch & 7)) & 1) : 1;
+        if (on) {
+          uint16_t kv;
+          memcpy(&kv, vals + 2 * r, 2);
+          ++r;
+          x = bf2f(kv);
+        }
+        if (x > mx[ch]) mx[ch] = x;
+        if (x < mn[ch]) mn[ch] = x;
+      }
+    }
+    for (int ch = 0; ch < ORC_D; ++ch) {
+      float a = T > 0 ? mx[ch] : 0.0f, b = T > 0 ? mn[ch] : 0.0f;
+      uint32_t ua, ub;
+      memcpy(&ua, &a, 4);
+      memcpy(&ub, &b, 4);
+      smax[ch] = (uint16_t)(ua >> 16); /* exact: every candidate is a bf16 value */
+      smin[ch] = (uint16_t)(ub >> 16);
+    }
+  }
+}
+
+/* Score of one segment: max over the G heads of the fp32 sum, over
+ * channels in ascending order, of max(q kmax, q kmin) (each product of two
+ * bf16 values is exact in fp32). */
+static float segment_score(int G, const uint16_t* q, const uint16_t* sm) {
+  float best = -INFINITY;
+  for (int g = 0; g < G; ++g) {
+    float acc = 0.0f;
+    for (int ch = 0; ch < ORC_D; ++ch) {
+      const float qv = bf2f(q[g * ORC_D + ch]);
+      const float a = qv * bf2f(sm[ch]), b = qv * bf2f(sm[ORC_D + ch]);
+      acc = acc + (a > b ? a : b);
+    }
+    if (acc > best) best = acc;
+  }
+  return best;
+}
+
+typedef struct {
+  float s;
+  int i;
+} seg_key;
+static int cmp_segkey(const void* a, const void* b) {
+  const seg_key* x = (const seg_key*)a;
+  const seg_key* y = (const seg_key*)b;
+  if (x->s != y->s) return x->s > y->s ? -1 : 1;
+  return x->i - y->i;
+}
+
+/* q: [G][128] bf16; summary from orc_summarize_stream.  Writes the score of
+ * every descriptor (-inf for an empty one) and the indices of the kept
+ * descriptors in ascending order; returns their number, min(k, non-empty). */
+int orc_select_stream(int G, const uint16_t* q, const uint16_t* summary, const orc_desc* desc,
+                      int n_desc, int k, float* score, int* sel) {
+  seg_key* keys = (seg_key*)malloc(sizeof(seg_key) * (size_t)(n_desc > 0 ? n_desc : 1));
+  int m = 0;
+  for (int i = 0; i < n_desc; ++i) {
+    score[i] = desc[i].n_tok > 0 ? segment_score(G, q, summary + (size_t)i * 2 * ORC_D) : -INFINITY;
+    if (desc[i].n_tok > 0) {
+      keys[m].s = score[i];
+      keys[m].i = i;
+      ++m;
+    }
+  }
+  qsort(keys, (size_t)m, sizeof(seg_key), cmp_segkey);
+  const int n = k < m ? k : m;
+  uint8_t* on = (uint8_t*)calloc((size_t)(n_desc > 0 ? n_desc : 1), 1);
+  for (int j = 0; j < n; ++j) on[keys[j].i] = 1;
+  int w = 0;
+  for (int i = 0; i < n_desc; ++i)
+    if (on[i]) sel[w++] = i;
+  free(on);
+  free(keys);
+  return n;
+}
+
 int orc_max_threads(void) { return omp_get_max_threads(); }

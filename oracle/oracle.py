@@ -51,6 +51,9 @@ def lib():
         L.orc_compress_stream.restype = i32
         L.orc_decode_stream.argtypes = [i32, P, P, P, i32, f32, P, P]
         L.orc_max_threads.restype = i32
+        L.orc_summarize_stream.argtypes = [P, P, i32, P]
+        L.orc_select_stream.argtypes = [i32, P, P, P, i32, i32, P, P]
+        L.orc_select_stream.restype = i32
         _lib = L
     return _lib
 
@@ -189,3 +192,27 @@ def decode_stream(q, packed, desc, scale):
     lib().orc_decode_stream(G, _p(q), _p(buf), _p(desc), desc.size, np.float32(scale), _p(out),
                             _p(lse))
     return out, lse
+
+
+def summarize_stream(packed, desc):
+    """Per-descriptor key summary: [n_desc, 2, 128] u16 (bf16 max, min per channel)."""
+    packed = np.ascontiguousarray(packed, np.uint8)
+    desc = np.ascontiguousarray(desc, DESC_DTYPE)
+    out = np.zeros((desc.size, 2, 128), np.uint16)
+    buf = packed if packed.size else np.zeros(16, np.uint8)
+    lib().orc_summarize_stream(_p(buf), _p(desc), desc.size, _p(out))
+    return out
+
+
+def select_stream(q, summary, desc, k):
+    """Query-aware segment selection: (selected descriptor indices ascending,
+    scores [n_desc] fp32 with -inf for empty descriptors)."""
+    q = _u16(q)
+    summary = np.ascontiguousarray(summary, np.uint16)
+    desc = np.ascontiguousarray(desc, DESC_DTYPE)
+    n = desc.size
+    score = np.zeros(max(n, 1), np.float32)
+    sel = np.zeros(max(n, 1), np.int32)
+    m = lib().orc_select_stream(q.shape[0], _p(q), _p(summary), _p(desc), n, int(k), _p(score),
+                                _p(sel))
+    return sel[:m].copy(), score[:n].copy()

@@ -471,3 +471,129 @@ def test_kara_schedule():
     L, w0, rb = ev[0]
     assert L == 16384 + 128 and rb == 384 and w0 == L - 512
     assert ev[-1][0] == 24576
+
+
+# ---------------------------------------------------------------------------
+# Query-aware segment selection (MosaicKV page, Fig. 6 caption: stage 2 runs
+# during decode before each attention layer; Sec. 5.3: sequence compression in
+# each decode attention layer; Fig. 8: token selection rates 6.25 % / 12.5 %).
+# ---------------------------------------------------------------------------
+
+def _selection_stream(O, seed, S=64):
+    K, V, Qw = _small_stream(seed)
+    r = O.compress_stream(K, V, Qw, S=S, strategies=gen.table9(S),
+                          budget_bytes=gen.budget_bytes(33, S), scale=SCALE)
+    return K, V, Qw, r
+
+
+def test_summary_is_the_exact_channel_range(O):
+    """kmin <= k <= kmax per channel over the decoded kept keys (dropped = 0),
+    and both bounds are attained (independent unpacking of the segment)."""
+    S = 64
+    K, V, Qw, r = _selection_stream(O, 21, S)
+    sm = O.summarize_stream(r["packed"], r["desc"])
+    for i, d in enumerate(r["desc"]):
+        _, Kd, _, _, _ = unpack_segment(r["packed"], d, S)
+        kf = bits_to_f(Kd)
+        assert np.array_equal(bits_to_f(sm[i, 0]), kf.max(axis=0))
+        assert np.array_equal(bits_to_f(sm[i, 1]), kf.min(axis=0))
+
+
+def test_select_score_closed_form(O):
+    """Two non-zero channels: q = (1, -2), kmax = (3, 1), kmin = (-1, -4) gives
+    max(3, -1) + max(-2, 8) = 11 for head 0; head 1 = -q gives
+    max(-3, 1) + max(2, -8) = 3; the segment's score is the larger, 11."""
+    q = np.zeros((2, 128), np.float32)
+    q[0, :2] = [1, -2]
+    q[1, :2] = [-1, 2]
+    sm = np.zeros((1, 2, 128), np.float32)
+    sm[0, 0, :2] = [3, 1]
+    sm[0, 1, :2] = [-1, -4]
+    desc = np.zeros(1, O.DESC_DTYPE)
+    desc["n_tok"] = 1
+    sel, score = O.select_stream(bf16_bits(q), bf16_bits(sm), desc, 1)
+    assert score[0] == 11.0 and list(sel) == [0]
+
+
+def test_select_score_bounds_every_kept_logit(O):
+    """For every kept token and head, q.k (fp64, dropped channels 0) is at most
+    the segment's score, up to the fp32 rounding of the score's sum."""
+    S = 64
+    K, V, Qw, r = _selection_stream(O, 22, S)
+    q = bf16_bits(np.random.default_rng(3).standard_normal((2, 128)))
+    sm = O.summarize_stream(r["packed"], r["desc"])
+    _, score = O.select_stream(q, sm, r["desc"], 1)
+    qf = bits_to_f(q).astype(np.float64)
+    smf = bits_to_f(sm).astype(np.float64)
+    for i, d in enumerate(r["desc"]):
+        if d["n_tok"] == 0:
+            assert np.isneginf(score[i])
+            continue
+        _, Kd, _, _, _ = unpack_segment(r["packed"], d, S)
+        logits = bits_to_f(Kd).astype(np.float64) @ qf.T
+        terms = np.maximum(qf[:, None, :] * smf[i, 0][None], qf[:, None, :] * smf[i, 1][None])
+        slack = 128 * 2.0 ** -23 * np.abs(terms).sum(axis=-1).max()
+        assert logits.max() <= float(score[i]) + slack
+
+
+def test_select_top_k_brute_force(O):
+    """On 8 segments with crafted summaries (ties included), the kept set is
+    the k-subset of largest total score, ties to the lexicographically
+    smallest indices, for every k."""
+    rng = np.random.default_rng(4)
+    n = 8
+    q = np.zeros((1, 128), np.float32)
+    q[0, 0] = 1.0
+    sm = np.zeros((n, 2, 128), np.float32)
+    vals = rng.integers(-3, 4, n).astype(np.float32)
+    vals[5] = vals[2]  # a tie
+    sm[:, 0, 0] = vals
+    sm[:, 1, 0] = vals - 1
+    desc = np.zeros(n, O.DESC_DTYPE)
+    desc["n_tok"] = 1
+    desc["n_tok"][6] = 0  # empty: never kept
+    for k in range(0, n + 2):
+        sel, score = O.select_stream(bf16_bits(q), bf16_bits(sm), desc, k)
+        cand = [i for i in range(n) if desc["n_tok"][i] > 0]
+        kk = min(k, len(cand))
+        best = None
+        for sub in itertools.combinations(cand, kk):
+            key = (-sum(vals[list(sub)]), sub)
+            if best is None or key < best:
+                best = key
+        assert tuple(sel) == best[1], (k, sel, best)
+
+
+def test_select_all_equals_full_decode(O):
+    """Keeping every segment reproduces decode over the whole stream; keeping
+    the best quarter is decode over exactly those descriptors."""
+    S = 64
+    K, V, Qw, r = _selection_stream(O, 23, S)
+    q = bf16_bits(np.random.default_rng(5).standard_normal((2, 128)))
+    sm = O.summarize_stream(r["packed"], r["desc"])
+    sel, _ = O.select_stream(q, sm, r["desc"], len(r["desc"]))
+    nonempty = [i for i, d in enumerate(r["desc"]) if d["n_tok"] > 0]
+    assert list(sel) == nonempty
+    o_all, l_all = O.decode_stream(q, r["packed"], r["desc"], SCALE)
+    o_sel, l_sel = O.decode_stream(q, r["packed"], r["desc"][sel], SCALE)
+    assert np.array_equal(o_all, o_sel) and np.array_equal(l_all, l_sel)
+
+
+def test_select_keeps_the_heavy_segment(O):
+    """A segment whose keys align with q has the largest bound and is kept at
+    the smallest k."""
+    S = 64
+    N = 512
+    rng = np.random.default_rng(6)
+    K = rng.standard_normal((N, 128)) * 0.5
+    u = np.sign(rng.standard_normal(128))
+    K[300] = 4.0 * u
+    V = rng.standard_normal((N, 128))
+    Qw = rng.standard_normal((1, 8, 128))
+    K, V, Qw = bf16_bits(K), bf16_bits(V), bf16_bits(Qw)
+    r = O.compress_stream(K, V, Qw, S=S, strategies=[(S, 128)], budget_bytes=4 * S * 128,
+                          scale=SCALE)
+    q = bf16_bits(u[None, :])
+    sm = O.summarize_stream(r["packed"], r["desc"])
+    sel, score = O.select_stream(q, sm, r["desc"], 1)
+    assert list(sel) == [300 // S] and int(np.argmax(score)) == 300 // S

@@ -655,7 +655,8 @@ void orc_decode_stream(int G, const uint16_t* q, const uint8_t* packed, const or
 /* ------------------------------------------------------------------ */
 
 /* summary: [n_desc][2][128] bf16 bits: kmax, kmin of each descriptor's
- * kept K vectors (zeros for an empty descriptor). */
+ * kept K vectors (zeros for an empty descriptor).  Zeros are taken as +0,
+ * so that the maximum and minimum do not depend on the token order. */
 void orc_summarize_stream(const uint8_t* packed, const orc_desc* desc, int n_desc,
                           uint16_t* summary) {
   for (int i = 0; i < n_desc; ++i) {
@@ -680,7 +681,7 @@ void orc_summarize_stream(const uint8_t* packed, const orc_desc* desc, int n_des
           uint16_t kv;
           memcpy(&kv, vals + 2 * r, 2);
           ++r;
-          x = bf2f(kv);
+          x = bf2f(kv) + 0.0f; /* -0 counts as +0, so the range has one bit pattern */
         }
         if (x > mx[ch]) mx[ch] = x;
         if (x < mn[ch]) mn[ch] = x;

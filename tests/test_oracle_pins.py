@@ -597,3 +597,20 @@ def test_select_keeps_the_heavy_segment(O):
     sm = O.summarize_stream(r["packed"], r["desc"])
     sel, score = O.select_stream(q, sm, r["desc"], 1)
     assert list(sel) == [300 // S] and int(np.argmax(score)) == 300 // S
+
+
+def test_summary_zero_sign_does_not_depend_on_order(O):
+    """A channel holding -0 in one token and a dropped (+0) channel in another
+    has range [+0, +0] in either token order."""
+    S = 16
+    K = np.zeros((S, 128), np.float32)
+    K[:, 1:] = 1.0
+    K[0, 0] = -0.0
+    Kb = bf16_bits(K)
+    V = bf16_bits(np.ones((S, 128), np.float32))
+    Qw = bf16_bits(np.ones((1, 1, 128), np.float32))
+    for order in (np.arange(S), np.arange(S)[::-1]):
+        r = O.compress_stream(Kb[order], V, Qw, S=S, strategies=[(S, 128)],
+                              budget_bytes=4 * S * 128, scale=SCALE)
+        sm = O.summarize_stream(r["packed"], r["desc"])
+        assert sm[0, 0, 0] == 0 and sm[0, 1, 0] == 0

@@ -698,18 +698,19 @@ void orc_summarize_stream(const uint8_t* packed, const orc_desc* desc, int n_des
   }
 }
 
-/* Score of one segment: max over the G heads of the fp32 sum, over
- * channels in ascending order, of max(q kmax, q kmin) (each product of two
- * bf16 values is exact in fp32). */
+/* Score of one segment: max over the G heads of the pairwise-tree fp32
+ * sum over channels 0..127 (the selection path's summation order) of
+ * max(q kmax, q kmin); each product of two bf16 values is exact in fp32. */
 static float segment_score(int G, const uint16_t* q, const uint16_t* sm) {
   float best = -INFINITY;
+  float term[ORC_D];
   for (int g = 0; g < G; ++g) {
-    float acc = 0.0f;
     for (int ch = 0; ch < ORC_D; ++ch) {
       const float qv = bf2f(q[g * ORC_D + ch]);
       const float a = qv * bf2f(sm[ch]), b = qv * bf2f(sm[ORC_D + ch]);
-      acc = acc + (a > b ? a : b);
+      term[ch] = a > b ? a : b;
     }
+    const float acc = tree_pow2(term, ORC_D);
     if (acc > best) best = acc;
   }
   return best;

@@ -708,7 +708,7 @@ static float segment_score(int G, const uint16_t* q, const uint16_t* sm) {
     for (int ch = 0; ch < ORC_D; ++ch) {
       const float qv = bf2f(q[g * ORC_D + ch]);
       const float a = qv * bf2f(sm[ch]), b = qv * bf2f(sm[ORC_D + ch]);
-      term[ch] = a > b ? a : b;
+      term[ch] = (a > b ? a : b) + 0.0f; /* -0 counts as +0 (a q element may be -0) */
     }
     const float acc = tree_pow2(term, ORC_D);
     if (acc > best) best = acc;

@@ -19,6 +19,10 @@ Printed JSON (one line):
                segment + q + out + partials written and read back
   cpu_baseline the CPU oracle (C, OpenMP) on a bounded sample: compress of
                one stream and fp64 decode of that stream
+  stage2       beside the headline (not part of `value`): query-aware
+               selection of --select-pct percent of the segments
+               (kv_summarize once, kv_select_segments + kv_attend_decode over
+               the kept descriptors per step)
 """
 import argparse
 import json
@@ -45,6 +49,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-splits", type=int, default=0, help="0 = library choice")
+    ap.add_argument("--select-pct", type=float, default=12.5,
+                    help="query-aware selection measured beside the headline: percent of the "
+                         "segments kept (0 = off)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "decode_batched128k_traffic.md"),
                     help="summary with the measured decode HBM bytes per launch (rocprofv3 pmc)")
     return ap.parse_args()
@@ -83,6 +90,55 @@ def measured_traffic(path):
         return int(vals["bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def bench_stage2(a, kvc, p, L, q, packed, desc, B, Hq, Hkv, N, stream):
+    """Query-aware segment selection (decode-time stage 2) on the same cache:
+    kv_summarize once, then per step kv_select_segments + kv_attend_decode
+    over the kept descriptors; HIP events on the launch stream."""
+    streams = B * Hkv
+    n_seg = L.n_seg
+    keep = max(1, int(round(n_seg * a.select_pct / 100.0)))
+    dev = q.device
+    summary = torch.empty((streams, n_seg, 2, 128), dtype=torch.int16, device=dev)
+    out_desc = torch.zeros(streams * keep * 16, dtype=torch.uint8, device=dev)
+    out_n = torch.empty(streams, dtype=torch.int32, device=dev)
+    score = torch.empty((streams, n_seg), dtype=torch.float32, device=dev)
+    ps = kvc.KvParams(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, max_desc_per_stream=n_seg,
+                      scale=p.p.scale)
+    pd = kvc.KvParams(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, max_desc_per_stream=keep,
+                      scale=p.p.scale)
+    _, Ld = kvc.kv_layout_query(pd)
+    dws = torch.empty(max(Ld.decode_ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record(stream)
+    kvc.kv_summarize(ps, packed, desc, None, summary)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_sum = e0.elapsed_time(e1) * 1e3
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(a.steps)]
+    for i in range(a.warmup + a.steps):
+        e = ev[i - a.warmup] if i >= a.warmup else None
+        if e:
+            e[0].record(stream)
+        kvc.kv_select_segments(ps, q, summary, desc, None, keep, out_desc, out_n, score)
+        if e:
+            e[1].record(stream)
+        kvc.kv_attend_decode(pd, q, packed, out_desc, out_n, out, None, dws)
+        if e:
+            e[2].record(stream)
+    torch.cuda.synchronize()
+    sel_us = float(np.mean([x[0].elapsed_time(x[1]) for x in ev])) * 1e3
+    dec_us = float(np.mean([x[1].elapsed_time(x[2]) for x in ev])) * 1e3
+    kept = np.asarray(out_desc.cpu().numpy().view(kvc.DESC_DTYPE)["n_tok"], np.int64)
+    n = out_n.cpu().numpy()
+    kept_tok = int(sum(kept.reshape(streams, keep)[s, :n[s]].sum() for s in range(streams)))
+    return {"keep_segments_per_stream": keep, "keep_pct": a.select_pct,
+            "summarize_us_once": t_sum, "select_us": sel_us, "decode_us": dec_us,
+            "select_plus_decode_us": sel_us + dec_us,
+            "kept_tokens": kept_tok,
+            "kv_tokens_per_s": B * N / ((sel_us + dec_us) * 1e-6)}
 
 
 def cpu_baseline(w, S, strategies, budget, scale):
@@ -176,6 +232,10 @@ def main():
     comp_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
 
+    stage2 = None
+    if a.select_pct > 0:
+        stage2 = bench_stage2(a, kvc, p, L, q, packed, desc, B, Hq, Hkv, N, stream)
+
     dh = desc.cpu().numpy().view(kvc.DESC_DTYPE)
     hist = np.bincount(dh["strategy"], minlength=len(strategies)).tolist()
     alg = algorithmic_decode_bytes(dh, S, B, Hq, L.decode_splits)
@@ -216,6 +276,8 @@ def main():
         "value_basis": "B*context / mean decode time over the timed steps; each timed step also "
                        "runs kv_compress (compress_ms)",
     }
+    if stage2 is not None:
+        res["stage2"] = stage2
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         wc = {k: (v[:1].cpu() if torch.is_tensor(v) else v) for k, v in w.items()}

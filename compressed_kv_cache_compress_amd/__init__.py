@@ -79,6 +79,11 @@ def lib():
         L.kv_attend_decode.argtypes = [ctypes.POINTER(Params), P, P, P, P, P, P, P,
                                        ctypes.c_size_t, P]
         L.kv_attend_decode.restype = ctypes.c_int
+        L.kv_summarize.argtypes = [ctypes.POINTER(Params), P, P, P, P, P]
+        L.kv_summarize.restype = ctypes.c_int
+        L.kv_select_segments.argtypes = [ctypes.POINTER(Params), P, P, P, P, ctypes.c_uint32, P,
+                                         P, P, P]
+        L.kv_select_segments.restype = ctypes.c_int
         L.kvc_status_str.argtypes = [ctypes.c_int]
         L.kvc_status_str.restype = ctypes.c_char_p
         L.kvc_abi_version.restype = ctypes.c_int
@@ -156,6 +161,23 @@ def kv_attend_decode(params, q, packed, desc, n_desc, out, lse, ws):
                                 ws.numel() * ws.element_size() if ws is not None else 0, _stream())
     if st != 0:
         raise KvcError("kv_attend_decode", st)
+
+
+def kv_summarize(params, packed, desc, n_desc, summary):
+    """Enqueue the per-descriptor key summaries on the current stream."""
+    st = lib().kv_summarize(ctypes.byref(params.p), _ptr(packed), _ptr(desc), _ptr(n_desc),
+                            _ptr(summary), _stream())
+    if st != 0:
+        raise KvcError("kv_summarize", st)
+
+
+def kv_select_segments(params, q, summary, desc, n_desc, keep, out_desc, out_n, score):
+    """Enqueue query-aware segment selection on the current stream."""
+    st = lib().kv_select_segments(ctypes.byref(params.p), _ptr(q), _ptr(summary), _ptr(desc),
+                                  _ptr(n_desc), int(keep), _ptr(out_desc), _ptr(out_n),
+                                  _ptr(score), _stream())
+    if st != 0:
+        raise KvcError("kv_select_segments", st)
 
 
 def desc_view(t):

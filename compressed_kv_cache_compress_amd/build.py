@@ -21,7 +21,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvc.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("kvc_host.cpp", "kvc_compress.hip", "kvc_decode.hip")]
+SOURCES = [os.path.join(CSRC, f)
+           for f in ("kvc_host.cpp", "kvc_compress.hip", "kvc_decode.hip", "kvc_select.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

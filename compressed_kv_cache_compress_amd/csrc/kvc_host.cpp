@@ -300,4 +300,55 @@ kvc_status kv_attend_decode(const kvc_params* p, const uint16_t* q, const void* 
   return KVC_OK;
 }
 
+kvc_status kv_summarize(const kvc_params* p, const void* packed, const kvc_seg_desc* desc,
+                        const uint32_t* n_desc_per_stream, uint16_t* summary, hipStream_t stream) {
+  Shape sh;
+  kvc_status st = check_shape(p, &sh);
+  if (st != KVC_OK) return st;
+  const uint32_t maxd = decode_maxd(p);
+  if (maxd == 0 || maxd > 65535u || !packed || !desc || !summary) return KVC_E_INVALID;
+  if (!aligned16(packed) || !aligned16(desc) || !aligned16(summary)) return KVC_E_ALIGN;
+  SummaryPlan sp;
+  sp.streams = sh.streams;
+  sp.maxd = (int)maxd;
+  sp.packed = static_cast<const uint8_t*>(packed);
+  sp.desc = desc;
+  sp.n_desc = n_desc_per_stream;
+  sp.summary = summary;
+  if (launch_summarize(sp, stream) != hipSuccess) return KVC_E_HIP;
+  return KVC_OK;
+}
+
+kvc_status kv_select_segments(const kvc_params* p, const uint16_t* q, const uint16_t* summary,
+                              const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
+                              uint32_t keep, kvc_seg_desc* out_desc, uint32_t* out_n, float* score,
+                              hipStream_t stream) {
+  Shape sh;
+  kvc_status st = check_shape(p, &sh);
+  if (st != KVC_OK) return st;
+  const uint32_t maxd = decode_maxd(p);
+  if (maxd == 0 || keep == 0 || !q || !summary || !desc || !out_desc || !out_n || !score)
+    return KVC_E_INVALID;
+  if (maxd > (uint32_t)SEL_MAXD) return KVC_E_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(summary) || !aligned16(desc) || !aligned16(out_desc) ||
+      !aligned16(score))
+    return KVC_E_ALIGN;
+  SelectPlan sp;
+  sp.streams = sh.streams;
+  sp.hkv = sh.hkv;
+  sp.hq = sh.hq;
+  sp.G = sh.G;
+  sp.maxd = (int)maxd;
+  sp.keep = (int)(keep < maxd ? keep : maxd);
+  sp.q = q;
+  sp.summary = summary;
+  sp.desc = desc;
+  sp.n_desc = n_desc_per_stream;
+  sp.out_desc = out_desc;
+  sp.out_n = out_n;
+  sp.score = score;
+  if (launch_select(sp, stream) != hipSuccess) return KVC_E_HIP;
+  return KVC_OK;
+}
+
 }  // extern "C"

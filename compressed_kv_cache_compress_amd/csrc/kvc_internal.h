@@ -55,7 +55,30 @@ struct DecodePlan {
   float *part_ml, *part_acc;
 };
 
+// Query-aware segment selection (kvc_select.hip).
+constexpr int SEL_MAXD = 8192;  // descriptors per stream the selection holds in LDS
+struct SummaryPlan {
+  int streams, maxd;
+  const uint8_t* packed;
+  const kvc_seg_desc* desc;
+  const uint32_t* n_desc;
+  uint16_t* summary;      // [streams][maxd][2][128]
+};
+
+struct SelectPlan {
+  int streams, hkv, hq, G, maxd, keep;
+  const uint16_t* q;
+  const uint16_t* summary;
+  const kvc_seg_desc* desc;
+  const uint32_t* n_desc;
+  kvc_seg_desc* out_desc;  // [streams][keep]
+  uint32_t* out_n;         // [streams]
+  float* score;            // [streams][maxd]
+};
+
 hipError_t launch_compress(const CompressPlan& p, hipStream_t st);
+hipError_t launch_summarize(const SummaryPlan& p, hipStream_t st);
+hipError_t launch_select(const SelectPlan& p, hipStream_t st);
 hipError_t launch_decode(const DecodePlan& p, hipStream_t st);
 
 }  // namespace kvc

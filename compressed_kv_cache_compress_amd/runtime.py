@@ -1,12 +1,14 @@
 """Convenience layer over the C ABI: allocates outputs and workspaces with
-torch on the current device and calls kv_compress / kv_attend_decode.
+torch on the current device and calls kv_compress / kv_attend_decode /
+kv_summarize / kv_select_segments.
 
 All computation happens in libkvc's HIP kernels; nothing here touches the
 data except to allocate it.
 """
 import torch
 
-from . import (DESC_DTYPE, KvParams, kv_attend_decode, kv_compress, kv_layout_query)
+from . import (DESC_DTYPE, KvParams, kv_attend_decode, kv_compress, kv_layout_query,
+               kv_select_segments, kv_summarize)
 
 
 def _u8(n, device):
@@ -99,3 +101,38 @@ def decode(q, packed, desc, *, n_kv_heads, max_desc_per_stream, n_desc=None, dec
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     kv_attend_decode(p, q, packed, desc, n_desc, out, lse, ws)
     return out, lse
+
+
+def summarize(packed, desc, *, batch, n_q_heads, n_kv_heads, max_desc_per_stream, n_desc=None,
+              summary=None):
+    """Per-descriptor key summaries: uint16 [streams, max_desc, 2, 128] (bf16
+    channel maximum, minimum)."""
+    streams = batch * n_kv_heads
+    p = decode_params(batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
+                      max_desc_per_stream=max_desc_per_stream)
+    if summary is None:
+        summary = torch.empty((streams, max_desc_per_stream, 2, 128), dtype=torch.int16,
+                              device=packed.device)
+    kv_summarize(p, packed, desc, n_desc, summary)
+    return summary
+
+
+def select(q, summary, desc, keep, *, n_kv_heads, max_desc_per_stream, n_desc=None,
+           out_desc=None, out_n=None, score=None):
+    """Query-aware selection: (out_desc uint8 [streams * keep * 16], out_n int32
+    [streams], score fp32 [streams, max_desc]).  Decode over it with
+    max_desc_per_stream = keep and n_desc = out_n."""
+    B, Hq = q.shape[0], q.shape[1]
+    streams = B * n_kv_heads
+    keep = min(int(keep), int(max_desc_per_stream))
+    p = decode_params(batch=B, n_q_heads=Hq, n_kv_heads=n_kv_heads,
+                      max_desc_per_stream=max_desc_per_stream)
+    dev = q.device
+    if out_desc is None:
+        out_desc = torch.zeros(streams * keep * 16, dtype=torch.uint8, device=dev)
+    if out_n is None:
+        out_n = torch.empty(streams, dtype=torch.int32, device=dev)
+    if score is None:
+        score = torch.empty((streams, max_desc_per_stream), dtype=torch.float32, device=dev)
+    kv_select_segments(p, q, summary, desc, n_desc, keep, out_desc, out_n, score)
+    return out_desc, out_n, score

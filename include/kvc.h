@@ -201,6 +201,43 @@ kvc_status kv_attend_decode(const kvc_params* p, const uint16_t* q, const void* 
                             uint16_t* out, float* lse, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
+/* Query-aware segment selection before decode attention (MosaicKV review
+ * page: Fig. 6 caption, stage 2 runs during the decode stage before each
+ * attention layer; Sec. 5.3, PackedAttention performs sequence compression in
+ * each decode attention layer; Fig. 8, token selection rates 6.25 % and
+ * 12.5 %).  Two calls: kv_summarize once per compressed cache, then
+ * kv_select_segments per decode step, whose output descriptor list feeds
+ * kv_attend_decode (max_desc_per_stream = keep, n_desc_per_stream = out_n).
+ *
+ * kv_summarize: for every descriptor, the channel-wise maximum and minimum of
+ * its decoded K vectors (a dropped channel counts as 0, -0 as +0).
+ *  packed, desc, n_desc_per_stream   as for kv_attend_decode.
+ *  summary   device [streams][max_desc_per_stream][2][128] bf16: kmax then
+ *            kmin; zeros for an empty descriptor or one past n_desc.
+ * Uses batch, n_q_heads, n_kv_heads, head_dim and max_desc_per_stream of p
+ * (max_desc_per_stream <= 65535).  Errors as for every entry point. */
+kvc_status kv_summarize(const kvc_params* p, const void* packed, const kvc_seg_desc* desc,
+                        const uint32_t* n_desc_per_stream, uint16_t* summary, hipStream_t stream);
+
+/* kv_select_segments: for each stream, every non-empty descriptor d below
+ * n_desc gets score(d) = max over the group's q heads g of the fp32 sum over
+ * channels 0..127 in order of max(q_g kmax, q_g kmin) (exact bf16 products),
+ * an upper bound of q_g . k over the descriptor's kept keys (scale omitted:
+ * it does not change the order).  The keep best by (score desc, index asc)
+ * are written to out_desc in index order.
+ *  q         device [batch][n_q_heads][128] bf16 (the decode query).
+ *  summary   from kv_summarize.
+ *  keep      descriptors to keep per stream, >= 1 (capped at max_desc).
+ *  out_desc  device [streams][keep]; entries past out_n are left untouched.
+ *  out_n     device [streams] u32: min(keep, non-empty descriptors).
+ *  score     device [streams][max_desc_per_stream] fp32: each descriptor's
+ *            score, -inf for an empty one or one past n_desc.
+ * max_desc_per_stream <= 8192 (else KVC_E_UNSUPPORTED).  No workspace. */
+kvc_status kv_select_segments(const kvc_params* p, const uint16_t* q, const uint16_t* summary,
+                              const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
+                              uint32_t keep, kvc_seg_desc* out_desc, uint32_t* out_n, float* score,
+                              hipStream_t stream);
+
 /* Static description of a status code. */
 const char* kvc_status_str(kvc_status s);
 

@@ -22,8 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("kv_layout_query", "kv_compress", "kv_attend_decode", "kvc_status_str",
-              "kvc_abi_version"):
+    for n in ("kv_layout_query", "kv_compress", "kv_attend_decode", "kv_summarize",
+              "kv_select_segments", "kvc_status_str", "kvc_abi_version"):
         assert n in names
 
 
@@ -173,4 +173,35 @@ def test_decode_validates_before_launch(monkeypatch):
     p17 = kvc.KvParams(batch=1, n_q_heads=17, n_kv_heads=1, max_desc_per_stream=8)
     with pytest.raises(kvc.KvcError) as e:
         kvc.kv_attend_decode(p17, a, a, a, None, a, None, a)
+    assert e.value.status == -2
+
+
+def test_selection_validates_before_launch(monkeypatch):
+    """Invalid arguments are rejected on the host with nothing enqueued (the
+    fake pointers would fault if anything ran)."""
+    monkeypatch.setattr(kvc, "_stream", lambda: ctypes.c_void_p(0))
+    p = kvc.KvParams(batch=1, n_q_heads=4, n_kv_heads=1, max_desc_per_stream=8)
+    a = _Fake(0x30000)
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_summarize(p, a, a, None, None)
+    assert e.value.status == -1
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_summarize(p, a, _Fake(0x30008), None, a)
+    assert e.value.status == -5
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_select_segments(p, a, a, a, None, 0, a, a, a)
+    assert e.value.status == -1
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_select_segments(p, a, a, a, None, 4, a, a, None)
+    assert e.value.status == -1
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_select_segments(p, a, _Fake(0x30002), a, None, 4, a, a, a)
+    assert e.value.status == -5
+    p0 = kvc.KvParams(batch=1, n_q_heads=4, n_kv_heads=1)
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_select_segments(p0, a, a, a, None, 4, a, a, a)
+    assert e.value.status == -1
+    p17 = kvc.KvParams(batch=1, n_q_heads=17, n_kv_heads=1, max_desc_per_stream=8)
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_select_segments(p17, a, a, a, None, 4, a, a, a)
     assert e.value.status == -2

@@ -375,7 +375,67 @@ typedef struct {
   int t2c_alpha;     /* 0: Token2Chunk off */
   int t2c_gamma;
   float scale;
+  int budget_scope;  /* 0: each segment <= budget_bytes; 1: the stream's
+                        segments together <= nseg * budget_bytes */
 } orc_params;
+
+/* ------------------------------------------------------------------ */
+/* Per-stream byte budget ([M] abstract: compression strategies chosen   */
+/* per KV segment under a memory target; Fig. 5 caption: strategy        */
+/* generation).  Reading: a multiple-choice knapsack over the stream's   */
+/* segments, maximise the sum of objectives J[sg][i] with the total      */
+/* packed bytes <= B, solved by Lagrangian relaxation: for a multiplier  */
+/* lambda >= 0 every segment takes argmax_i fl(J - fl(lambda * bytes_i)) */
+/* (ties to the lower index); lambda is the smallest fp32 value, found   */
+/* by binary search over the bit patterns 0 .. 2^97, whose total fits B  */
+/* (2^97 x bytes stays finite and exceeds any objective difference, so   */
+/* there every segment takes its smallest strategy, ties to the lower    */
+/* index; if even that does not fit, that assignment is returned).  A    */
+/* Lagrangian solution is optimal among all assignments that use at most */
+/* its own bytes.                                                         */
+/* ------------------------------------------------------------------ */
+static uint64_t lagrange_pick(const float* J, const long* bytes, int nseg, int ns, float lambda,
+                              int* chosen) {
+  uint64_t tot = 0;
+  for (int sg = 0; sg < nseg; ++sg) {
+    int best = 0;
+    float bv = J[(size_t)sg * ns] - lambda * (float)bytes[0];
+    for (int i = 1; i < ns; ++i) {
+      const float v = J[(size_t)sg * ns + i] - lambda * (float)bytes[i];
+      if (v > bv) {
+        bv = v;
+        best = i;
+      }
+    }
+    chosen[sg] = best;
+    tot += (uint64_t)bytes[best];
+  }
+  return tot;
+}
+
+static float bits_f(uint32_t u) {
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* Returns the multiplier's bit pattern. */
+uint32_t orc_stream_choose(const float* J, const long* bytes, int nseg, int ns, uint64_t B,
+                           int* chosen) {
+  if (lagrange_pick(J, bytes, nseg, ns, 0.0f, chosen) <= B) return 0u;
+  const uint32_t top = 0x70000000u; /* 2^97 */
+  if (lagrange_pick(J, bytes, nseg, ns, bits_f(top), chosen) > B) return top;
+  uint32_t lo = 0u, hi = top; /* total(lo) > B, total(hi) <= B */
+  while (hi - lo > 1u) {
+    const uint32_t mid = lo + (hi - lo) / 2u;
+    if (lagrange_pick(J, bytes, nseg, ns, bits_f(mid), chosen) <= B)
+      hi = mid;
+    else
+      lo = mid;
+  }
+  lagrange_pick(J, bytes, nseg, ns, bits_f(hi), chosen);
+  return hi;
+}
 
 /* Compress one stream (one batch entry, one kv head).
  * K, V: [n_ctx][128] bf16; Qw: [G][W][128] bf16; forced: [nseg] or NULL
@@ -390,6 +450,7 @@ int orc_compress_stream(const orc_params* p, const uint16_t* K, const uint16_t* 
                         float* invZ_out, int n_threads) {
   orc_init();
   const int S = p->S, nseg = p->region_len / p->S, nq = p->G * p->W, ns = p->n_strat;
+  if (p->budget_scope && forced) return -1;
   long* bytes = (long*)malloc(sizeof(long) * (size_t)ns);
   int any_feasible = 0;
   for (int i = 0; i < ns; ++i) {
@@ -413,6 +474,7 @@ int orc_compress_stream(const orc_params* p, const uint16_t* K, const uint16_t* 
   /* 2. per segment: selection, objective, choice */
   int* chosen = (int*)malloc(sizeof(int) * (size_t)nseg);
   uint8_t* flags = (uint8_t*)calloc((size_t)nseg, 1);
+  float* Jall = (float*)malloc(sizeof(float) * (size_t)nseg * (size_t)ns);
 #pragma omp parallel for schedule(dynamic) num_threads(n_threads)
   for (int sg = 0; sg < nseg; ++sg) {
     const int t0 = p->region_begin + sg * S;
@@ -481,11 +543,16 @@ int orc_compress_stream(const orc_params* p, const uint16_t* K, const uint16_t* 
       }
     }
     chosen[sg] = best;
+    for (int i = 0; i < ns; ++i) Jall[(size_t)sg * ns + i] = J[i];
     if (objective_out)
       for (int i = 0; i < ns; ++i) objective_out[(size_t)sg * ns + i] = J[i];
     free(keep);
     free(terms);
   }
+
+  if (p->budget_scope)
+    orc_stream_choose(Jall, bytes, nseg, ns, (uint64_t)p->budget_bytes * (uint64_t)nseg, chosen);
+  free(Jall);
 
   /* 3. offsets (exclusive scan) and 4. pack */
   uint64_t off = 0;

@@ -54,6 +54,8 @@ def lib():
         L.orc_summarize_stream.argtypes = [P, P, i32, P]
         L.orc_select_stream.argtypes = [i32, P, P, P, i32, i32, P, P]
         L.orc_select_stream.restype = i32
+        L.orc_stream_choose.argtypes = [P, P, i32, i32, ctypes.c_uint64, P]
+        L.orc_stream_choose.restype = ctypes.c_uint32
         _lib = L
     return _lib
 
@@ -141,15 +143,18 @@ class _Params(ctypes.Structure):
                 ("W", ctypes.c_int), ("n_strat", ctypes.c_int),
                 ("strat_T", ctypes.c_void_p), ("strat_c", ctypes.c_void_p),
                 ("budget_bytes", ctypes.c_long), ("t2c_alpha", ctypes.c_int),
-                ("t2c_gamma", ctypes.c_int), ("scale", ctypes.c_float)]
+                ("t2c_gamma", ctypes.c_int), ("scale", ctypes.c_float),
+                ("budget_scope", ctypes.c_int)]
 
 
 def compress_stream(K, V, Qw, *, S, strategies, budget_bytes, scale, region_begin=0,
                     region_len=None, t2c_alpha=0, t2c_gamma=0, forced=None, base_offset=0,
-                    n_threads=0):
+                    n_threads=0, budget_scope=0):
     """Compress one stream.
 
     K, V: [n_ctx,128] u16; Qw: [G,W,128] u16; strategies: list of (T, c).
+    budget_scope 0: every segment within budget_bytes; 1: the stream's
+    segments together within n_seg * budget_bytes (Lagrangian choice).
     Returns dict(packed, desc, used, scores, objective, m, invZ).
     """
     K, V, Qw = _u16(K), _u16(V), _u16(Qw)
@@ -161,7 +166,7 @@ def compress_stream(K, V, Qw, *, S, strategies, budget_bytes, scale, region_begi
     sc = np.array([c for _, c in strategies], np.int32)
     prm = _Params(n_ctx, region_begin, region_len, S, G, W, len(strategies),
                   sT.ctypes.data, sc.ctypes.data, int(budget_bytes), t2c_alpha, t2c_gamma,
-                  np.float32(scale))
+                  np.float32(scale), int(budget_scope))
     cap = nseg * max(seg_bytes(t, c, S) for t, c in strategies) + 16
     packed = np.zeros(cap, np.uint8)
     desc = np.zeros(nseg, DESC_DTYPE)
@@ -216,3 +221,14 @@ def select_stream(q, summary, desc, k):
     m = lib().orc_select_stream(q.shape[0], _p(q), _p(summary), _p(desc), n, int(k), _p(score),
                                 _p(sel))
     return sel[:m].copy(), score[:n].copy()
+
+
+def stream_choose(J, nbytes, B):
+    """Per-stream budget choice from objectives J [nseg, n_strat] fp32 and
+    strategy bytes [n_strat]: (chosen [nseg], multiplier bit pattern)."""
+    J = np.ascontiguousarray(J, np.float32)
+    nb = np.ascontiguousarray(nbytes, np.int64)
+    nseg, ns = J.shape
+    chosen = np.zeros(max(nseg, 1), np.int32)
+    u = lib().orc_stream_choose(_p(J), _p(nb), nseg, ns, int(B), _p(chosen))
+    return chosen[:nseg].copy(), int(u)

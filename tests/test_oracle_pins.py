@@ -614,3 +614,104 @@ def test_summary_zero_sign_does_not_depend_on_order(O):
                               budget_bytes=4 * S * 128, scale=SCALE)
         sm = O.summarize_stream(r["packed"], r["desc"])
         assert sm[0, 0, 0] == 0 and sm[0, 1, 0] == 0
+
+
+# ---------------------------------------------------------------------------
+# Per-stream byte budget (MosaicKV page, abstract: strategies chosen per KV
+# segment under the memory target; Fig. 5 caption: strategy generation):
+# multiple-choice knapsack over a stream's segments by Lagrangian relaxation.
+# ---------------------------------------------------------------------------
+
+def _table9_bytes(O, S):
+    return [O.seg_bytes(t, c, S) for t, c in gen.table9(S)]
+
+
+def _exact_sum(vals):
+    return sum((Fraction(float(v)) for v in vals), Fraction(0))
+
+
+def test_stream_budget_brute_force_optimality(O):
+    """n_seg = 4, nine strategies: the choice fits B and no assignment using at
+    most the chosen bytes has a larger objective sum (the defining property
+    of a Lagrangian solution), checked over all 9^4 assignments."""
+    S = 64
+    nb = _table9_bytes(O, S)
+    rng = np.random.default_rng(11)
+    J = rng.random((4, 9)).astype(np.float32) * np.array([1, .9, .8, .7, .6, .5, .4, .3, .2],
+                                                         np.float32)
+    allsum = {}
+    for a in itertools.product(range(9), repeat=4):
+        allsum[a] = (sum(nb[i] for i in a), _exact_sum(J[k, i] for k, i in enumerate(a)))
+    for B in (4 * min(nb), 12000, 20000, 30000, 45000, 4 * max(nb)):
+        ch, _ = O.stream_choose(J, nb, B)
+        used = sum(nb[i] for i in ch)
+        assert used <= B
+        val = _exact_sum(J[k, i] for k, i in enumerate(ch))
+        best = max(v for (b, v) in allsum.values() if b <= used)
+        assert val >= best * (1 - Fraction(1, 10**6)), (B, ch)
+
+
+def test_stream_budget_dp_optimality(O):
+    """n_seg = 24: exact dynamic programme over bytes (in 16-byte units) at the
+    chosen total agrees with the choice's objective sum."""
+    S = 64
+    nb = _table9_bytes(O, S)
+    units = [b // 16 for b in nb]
+    rng = np.random.default_rng(12)
+    n = 24
+    J = (rng.random((n, 9)) ** 2).astype(np.float32)
+    for frac in (0.2, 0.35, 0.6):
+        B = int(frac * n * max(nb))
+        ch, _ = O.stream_choose(J, nb, B)
+        used = sum(nb[i] for i in ch)
+        assert used <= B
+        cap = used // 16
+        dp = np.full(cap + 1, -np.inf)
+        dp[0] = 0.0
+        for k in range(n):
+            nxt = np.full(cap + 1, -np.inf)
+            for i in range(9):
+                u = units[i]
+                if u <= cap:
+                    nxt[u:] = np.maximum(nxt[u:], dp[:cap + 1 - u] + float(J[k, i]))
+            dp = nxt
+        val = float(sum(float(J[k, i]) for k, i in enumerate(ch)))
+        assert val >= dp.max() - 1e-6 * abs(dp.max()), (frac, val, dp.max())
+
+
+def test_stream_budget_limits_and_monotone(O):
+    """A budget covering every segment's best strategy keeps the per-segment
+    argmax (multiplier 0); the smallest budget forces the smallest strategy;
+    the objective sum never decreases as the budget grows."""
+    S = 64
+    nb = _table9_bytes(O, S)
+    rng = np.random.default_rng(13)
+    J = rng.random((10, 9)).astype(np.float32)
+    best = J.argmax(axis=1)
+    ch, u = O.stream_choose(J, nb, sum(nb[i] for i in best))
+    assert u == 0 and list(ch) == list(best)
+    small = int(np.argmin(nb))
+    ch, _ = O.stream_choose(J, nb, 10 * nb[small])
+    assert np.all(ch == small)
+    prev = -1.0
+    for B in range(10 * nb[small], 10 * max(nb) + 1, 4096):
+        ch, _ = O.stream_choose(J, nb, B)
+        v = float(sum(float(J[k, i]) for k, i in enumerate(ch)))
+        assert v >= prev - 1e-6
+        prev = v
+
+
+def test_stream_budget_compress_end_to_end(O):
+    """Stream scope in the compress path: bytes within n_seg * budget, the
+    strategies are the Lagrangian choice over the reported objectives, and at
+    least one segment exceeds the per-segment cap (the point of the mode)."""
+    K, V, Qw = _small_stream(14, N=1024)
+    S = 64
+    budget = gen.budget_bytes(25, S)
+    r = O.compress_stream(K, V, Qw, S=S, strategies=gen.table9(S), budget_bytes=budget,
+                          scale=SCALE, budget_scope=1)
+    nseg = 1024 // S
+    assert r["used"] <= nseg * budget
+    ch, _ = O.stream_choose(r["objective"], _table9_bytes(O, S), nseg * budget)
+    assert list(r["desc"]["strategy"]) == list(ch)
+    assert max(_table9_bytes(O, S)[i] for i in ch) > budget

@@ -19,6 +19,8 @@ Printed JSON (one line):
                segment + q + out + partials written and read back
   cpu_baseline the CPU oracle (C, OpenMP) on a bounded sample: compress of
                one stream and fp64 decode of that stream
+  stream_budget beside the headline (not part of `value`): the same workload
+               with the byte budget shared by each stream's segments
   stage2       beside the headline (not part of `value`): query-aware
                selection of --select-pct percent of the segments
                (kv_summarize once, kv_select_segments + kv_attend_decode over
@@ -52,6 +54,8 @@ def parse():
     ap.add_argument("--select-pct", type=float, default=12.5,
                     help="query-aware selection measured beside the headline: percent of the "
                          "segments kept (0 = off)")
+    ap.add_argument("--no-stream-budget", action="store_true",
+                    help="skip the per-stream budget measurement beside the headline")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "decode_batched128k_traffic.md"),
                     help="summary with the measured decode HBM bytes per launch (rocprofv3 pmc)")
     return ap.parse_args()
@@ -90,6 +94,43 @@ def measured_traffic(path):
         return int(vals["bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def bench_stream_budget(a, kvc, K, V, Qw, q, B, Hq, Hkv, N, S, W, strategies, budget, scale,
+                        stream, steps=3):
+    """The same workload with the byte budget shared by each stream's segments
+    (budget_scope = stream): compress and decode times, bytes and the chosen
+    strategies; HIP events on the launch stream."""
+    p = kvc.KvParams(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, n_ctx=N, seg_tokens=S, n_win=W,
+                     strategies=strategies, budget_bytes=budget, scale=float(scale),
+                     budget_scope=1)
+    _, L = kvc.kv_layout_query(p)
+    dev = q.device
+    streams = B * Hkv
+    packed = torch.empty(L.packed_bytes_max, dtype=torch.uint8, device=dev)
+    desc = torch.zeros(streams * L.n_seg * 16, dtype=torch.uint8, device=dev)
+    used = torch.zeros(streams, dtype=torch.int64, device=dev)
+    cws = torch.empty(L.compress_ws_bytes, dtype=torch.uint8, device=dev)
+    dws = torch.empty(L.decode_ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    for i in range(steps + 1):
+        e = ev[i - 1] if i >= 1 else None
+        if e:
+            e[0].record(stream)
+        kvc.kv_compress(p, K, V, Qw, None, packed, desc, used, None, None, cws)
+        if e:
+            e[1].record(stream)
+        kvc.kv_attend_decode(p, q, packed, desc, None, out, None, dws)
+        if e:
+            e[2].record(stream)
+    torch.cuda.synchronize()
+    dh = desc.cpu().numpy().view(kvc.DESC_DTYPE)
+    return {"budget_bytes_per_stream": int(L.n_seg) * int(budget),
+            "compress_ms": float(np.mean([x[0].elapsed_time(x[1]) for x in ev])),
+            "decode_us": float(np.mean([x[1].elapsed_time(x[2]) for x in ev])) * 1e3,
+            "packed_bytes": int(used.sum().item()),
+            "strategy_histogram": np.bincount(dh["strategy"], minlength=len(strategies)).tolist()}
 
 
 def bench_stage2(a, kvc, p, L, q, packed, desc, B, Hq, Hkv, N, stream):
@@ -232,6 +273,10 @@ def main():
     comp_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
 
+    sbud = None
+    if not a.no_stream_budget:
+        sbud = bench_stream_budget(a, kvc, K, V, Qw, q, B, Hq, Hkv, N, S, W, strategies, budget,
+                                   scale, stream)
     stage2 = None
     if a.select_pct > 0:
         stage2 = bench_stage2(a, kvc, p, L, q, packed, desc, B, Hq, Hkv, N, stream)
@@ -278,6 +323,8 @@ def main():
     }
     if stage2 is not None:
         res["stage2"] = stage2
+    if sbud is not None:
+        res["stream_budget"] = sbud
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         wc = {k: (v[:1].cpu() if torch.is_tensor(v) else v) for k, v in w.items()}

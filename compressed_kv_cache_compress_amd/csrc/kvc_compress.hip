@@ -288,6 +288,8 @@ struct ChooseArgs {
   int region_len, S, n_seg, nc, n_strat, t2c_alpha, t2c_gamma;
   uint32_t dstride, feasible_mask;
   bool have_scores;
+  uint32_t* keep_all;  // stream scope: keep sets of every strategy, else null
+  float* J_all;        // stream scope: objectives of every strategy, else null
   int sT[KVC_MAX_STRATEGIES], sc[KVC_MAX_STRATEGIES], su[KVC_MAX_STRATEGIES];
 };
 
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(64) void k_segment_choose(ChooseArgs a) {
   int last_T = -1;
   bool kp[4] = {false, false, false, false};
   for (int i = 0; i < a.n_strat; ++i) {
-    if (!a.objective && !((a.feasible_mask >> i) & 1u)) continue;
+    if (!a.objective && !a.J_all && !((a.feasible_mask >> i) & 1u)) continue;
     const int T = a.sT[i], c = a.sc[i];
     if (T == last_T) {
       // same keep set as the previous strategy computed
@@ -446,6 +448,18 @@ __global__ __launch_bounds__(64) void k_segment_choose(ChooseArgs a) {
     if (lane == 0) s_J[i] = J;
   }
   __syncthreads();
+  if (a.J_all) {
+    // stream scope: every strategy's keep set and objective; k_stream_choose
+    // chooses and writes the descriptor
+    const uint64_t si = (uint64_t)s * a.n_seg + sg;
+    const int nw = (S + 31) / 32;
+    for (int i = lane; i < a.n_strat; i += 64) a.J_all[si * a.n_strat + i] = s_J[i];
+    for (int e = lane; e < a.n_strat * nw; e += 64)
+      a.keep_all[si * a.n_strat * nw + e] = s_keep[e / nw][e % nw];
+    if (a.objective)
+      for (int i = lane; i < a.n_strat; i += 64) a.objective[si * a.n_strat + i] = s_J[i];
+    return;
+  }
   if (lane == 0) {
     const uint64_t si = (uint64_t)s * a.n_seg + sg;
     int best = -1;
@@ -473,6 +487,96 @@ __global__ __launch_bounds__(64) void k_segment_choose(ChooseArgs a) {
     for (int w = 0; w < nw; ++w) a.keep[si * nw + w] = s_keep[best][w];
     if (a.objective)
       for (int i = 0; i < a.n_strat; ++i) a.objective[si * a.n_strat + i] = s_J[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-stream budget: multiple-choice knapsack over the stream's segments by
+// Lagrangian relaxation (MosaicKV abstract and Fig. 5 caption: strategies per
+// segment under the memory target).  Every segment takes
+// argmax_i fl(J_i - fl(lambda * bytes_i)) (ties to the lower index); lambda
+// is the smallest fp32 value, by binary search over its bit patterns
+// 0 .. 2^97, whose total fits the stream's bytes.
+// ---------------------------------------------------------------------------
+struct StreamChooseArgs {
+  const float* J_all;
+  const uint32_t* keep_all;
+  kvc_seg_desc* desc;
+  uint32_t* keep;
+  uint64_t stream_bytes;
+  uint32_t dstride;
+  int n_seg, n_strat, S;
+  int sT[KVC_MAX_STRATEGIES], sc[KVC_MAX_STRATEGIES];
+  uint32_t seg_bytes[KVC_MAX_STRATEGIES];
+};
+
+constexpr int SC_THREADS = 256;
+
+__device__ __forceinline__ int lagrange_best(const float* J, const StreamChooseArgs& a, float lambda) {
+  int best = 0;
+  float bv = J[0] - lambda * (float)a.seg_bytes[0];
+  for (int i = 1; i < a.n_strat; ++i) {
+    const float v = J[i] - lambda * (float)a.seg_bytes[i];
+    if (v > bv) {
+      bv = v;
+      best = i;
+    }
+  }
+  return best;
+}
+
+// Total bytes of the Lagrangian choice at lambda (block-wide, every thread
+// gets it).
+__device__ __forceinline__ uint64_t lagrange_total(const StreamChooseArgs& a, const float* Js,
+                                                   float lambda, unsigned long long* tot) {
+  uint64_t mine = 0;
+  for (int sg = threadIdx.x; sg < a.n_seg; sg += SC_THREADS)
+    mine += a.seg_bytes[lagrange_best(Js + (uint64_t)sg * a.n_strat, a, lambda)];
+  if (threadIdx.x == 0) *tot = 0ull;
+  __syncthreads();
+  atomicAdd(tot, (unsigned long long)mine);
+  __syncthreads();
+  const uint64_t r = *tot;
+  __syncthreads();
+  return r;
+}
+
+// grid (streams), 256 threads.
+__global__ __launch_bounds__(SC_THREADS) void k_stream_choose(StreamChooseArgs a) {
+  __shared__ unsigned long long tot;
+  const int s = blockIdx.x;
+  const float* Js = a.J_all + (uint64_t)s * a.n_seg * a.n_strat;
+  uint32_t u = 0u;
+  if (lagrange_total(a, Js, 0.0f, &tot) > a.stream_bytes) {
+    const uint32_t top = 0x70000000u;  // 2^97: every segment takes its smallest strategy
+    u = top;
+    if (lagrange_total(a, Js, __uint_as_float(top), &tot) <= a.stream_bytes) {
+      uint32_t lo = 0u, hi = top;  // total(lo) > budget, total(hi) <= budget
+      while (hi - lo > 1u) {
+        const uint32_t mid = lo + (hi - lo) / 2u;
+        if (lagrange_total(a, Js, __uint_as_float(mid), &tot) <= a.stream_bytes)
+          hi = mid;
+        else
+          lo = mid;
+      }
+      u = hi;
+    }
+  }
+  const float lambda = __uint_as_float(u);
+  const int nw = (a.S + 31) / 32;
+  for (int sg = threadIdx.x; sg < a.n_seg; sg += SC_THREADS) {
+    const uint64_t si = (uint64_t)s * a.n_seg + sg;
+    const int best = lagrange_best(Js + (uint64_t)sg * a.n_strat, a, lambda);
+    const int T = a.sT[best], c = a.sc[best];
+    kvc_seg_desc d;
+    d.offset = 0;
+    d.n_tok = (uint16_t)T;
+    d.n_ch = (uint16_t)(T > 0 ? c : 0);
+    d.strategy = (uint8_t)best;
+    d.flags = (uint8_t)((T >= a.S ? 1 : 0) | (c >= D ? 2 : 0));
+    d.seg_tokens = (uint16_t)a.S;
+    a.desc[(uint64_t)s * a.dstride + sg] = d;
+    for (int w = 0; w < nw; ++w) a.keep[si * nw + w] = a.keep_all[(si * a.n_strat + best) * nw + w];
   }
 }
 
@@ -652,7 +756,27 @@ hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
     ca.sc[i] = p.sc[i];
     ca.su[i] = p.su[i];
   }
+  ca.keep_all = p.stream_budget ? p.keep_all : nullptr;
+  ca.J_all = p.stream_budget ? p.J_all : nullptr;
   hipLaunchKernelGGL(k_segment_choose, dim3(p.n_seg, p.streams), dim3(64), 0, st, ca);
+  if (p.stream_budget) {
+    StreamChooseArgs sa;
+    sa.J_all = p.J_all;
+    sa.keep_all = p.keep_all;
+    sa.desc = p.desc;
+    sa.keep = p.keep;
+    sa.stream_bytes = p.stream_bytes;
+    sa.dstride = p.dstride;
+    sa.n_seg = p.n_seg;
+    sa.n_strat = p.n_strat;
+    sa.S = p.S;
+    for (int i = 0; i < KVC_MAX_STRATEGIES; ++i) {
+      sa.sT[i] = p.sT[i];
+      sa.sc[i] = p.sc[i];
+      sa.seg_bytes[i] = p.seg_bytes[i];
+    }
+    hipLaunchKernelGGL(k_stream_choose, dim3(p.streams), dim3(SC_THREADS), 0, st, sa);
+  }
   ScanArgs sc;
   sc.desc = p.desc;
   sc.used = p.used;

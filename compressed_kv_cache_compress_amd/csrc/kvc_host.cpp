@@ -49,6 +49,8 @@ kvc_status compress_layout(const kvc_params* p, const Shape& sh, kvc_layout* L, 
                            int* cvals, int* su) {
   if (p->n_strategies == 0 || p->n_strategies > KVC_MAX_STRATEGIES || !p->strategies)
     return KVC_E_INVALID;
+  if (p->budget_scope > KVC_BUDGET_STREAM) return KVC_E_INVALID;
+  const bool stream_scope = p->budget_scope == KVC_BUDGET_STREAM;
   const uint32_t S = p->seg_tokens;
   if (!pow2(S) || S < 16 || S > 256) return KVC_E_INVALID;
   if (p->n_ctx == 0 || p->n_ctx % BLK || p->n_ctx > (1u << 22)) return KVC_E_INVALID;
@@ -81,7 +83,9 @@ kvc_status compress_layout(const kvc_params* p, const Shape& sh, kvc_layout* L, 
     }
     const uint32_t by = seg_bytes(st.n_tok, st.n_tok ? st.n_ch : 0, S);
     L->seg_bytes[i] = by;
-    if (by <= p->budget_bytes) {
+    const uint64_t cap = stream_scope ? (uint64_t)p->budget_bytes * (p->region_len / S)
+                                      : (uint64_t)p->budget_bytes;
+    if (by <= cap) {
       feas |= 1u << i;
       ++nfeas;
       if (by > maxb) maxb = by;
@@ -94,7 +98,16 @@ kvc_status compress_layout(const kvc_params* p, const Shape& sh, kvc_layout* L, 
   L->feasible_mask = feas;
   L->n_seg = (uint32_t)n_seg;
   L->max_seg_bytes = maxb;
-  L->stream_capacity = align_up(n_seg * maxb, kAlign);
+  uint64_t stream_max = n_seg * maxb;
+  if (stream_scope) {
+    // the smallest strategy must fit every segment; the stream never writes
+    // more than n_seg * budget_bytes
+    uint32_t mn = 0xFFFFFFFFu;
+    for (uint32_t i = 0; i < p->n_strategies; ++i) mn = L->seg_bytes[i] < mn ? L->seg_bytes[i] : mn;
+    if (mn > p->budget_bytes) nfeas = 0;
+    if (n_seg * p->budget_bytes < stream_max) stream_max = n_seg * p->budget_bytes;
+  }
+  L->stream_capacity = align_up(stream_max, kAlign);
   L->packed_bytes_max = (uint64_t)sh.streams * L->stream_capacity;
   L->n_desc = (uint64_t)sh.streams * n_seg;
   L->needs_scoring = (partial || nfeas > 1) ? 1u : 0u;
@@ -111,6 +124,11 @@ kvc_status compress_layout(const kvc_params* p, const Shape& sh, kvc_layout* L, 
   ws += align_up((uint64_t)sh.streams * n_seg * ((S + 31) / 32) * 4, kAlign);
   // window queries converted to fp32 once per call
   if (p->n_win) ws += align_up((uint64_t)sh.streams * nq * KVC_HEAD_DIM * 4, kAlign);
+  // stream scope: keep sets and objectives of every strategy
+  if (stream_scope) {
+    ws += align_up((uint64_t)sh.streams * n_seg * p->n_strategies * ((S + 31) / 32) * 4, kAlign);
+    ws += align_up((uint64_t)sh.streams * n_seg * p->n_strategies * 4, kAlign);
+  }
   L->compress_ws_bytes = ws;
   return nfeas ? KVC_OK : KVC_E_BUDGET;
 }
@@ -200,8 +218,12 @@ kvc_status kv_compress(const kvc_params* p, const uint16_t* K, const uint16_t* V
     return KVC_E_ALIGN;
   if (p->kv_stream_stride % 8 || p->qw_head_stride % 8) return KVC_E_ALIGN;
   if (ws_bytes < L.compress_ws_bytes || (L.compress_ws_bytes && !ws)) return KVC_E_WORKSPACE;
+  const bool stream_scope = p->budget_scope == KVC_BUDGET_STREAM;
+  if (stream_scope && forced_strategy) return KVC_E_INVALID;
   const uint64_t pstride = p->packed_stream_stride ? p->packed_stream_stride : L.stream_capacity;
-  if (pstride < L.n_seg * L.max_seg_bytes) return KVC_E_INVALID;
+  const uint64_t stream_max =
+      stream_scope ? (uint64_t)L.n_seg * p->budget_bytes : L.n_seg * L.max_seg_bytes;
+  if (pstride < stream_max) return KVC_E_INVALID;
   const uint32_t dstride = p->desc_stream_stride ? p->desc_stream_stride : L.n_seg;
   if (dstride < L.n_seg) return KVC_E_INVALID;
 
@@ -259,6 +281,16 @@ kvc_status kv_compress(const kvc_params* p, const uint16_t* K, const uint16_t* V
   c.rho = reinterpret_cast<float*>(take(S64 * c.region_len * (uint64_t)c.nc * 2 * 4));
   c.keep = reinterpret_cast<uint32_t*>(take(S64 * c.n_seg * ((c.S + 31) / 32) * 4));
   c.qf = p->n_win ? reinterpret_cast<float*>(take(S64 * c.nq * D * 4)) : nullptr;
+  c.stream_budget = stream_scope;
+  c.stream_bytes = (uint64_t)L.n_seg * p->budget_bytes;
+  for (int i = 0; i < KVC_MAX_STRATEGIES; ++i) c.seg_bytes[i] = L.seg_bytes[i];
+  c.keep_all = nullptr;
+  c.J_all = nullptr;
+  if (stream_scope) {
+    c.keep_all = reinterpret_cast<uint32_t*>(
+        take(S64 * c.n_seg * (uint64_t)c.n_strat * ((c.S + 31) / 32) * 4));
+    c.J_all = reinterpret_cast<float*>(take(S64 * c.n_seg * (uint64_t)c.n_strat * 4));
+  }
   if (launch_compress(c, stream) != hipSuccess) return KVC_E_HIP;
   return KVC_OK;
 }

@@ -41,6 +41,12 @@ struct CompressPlan {
   float* qf;              // window queries in fp32, [streams][G * W][128]
   uint32_t* masks;        // [streams][region_len][nc][2][4]
   uint32_t* keep;         // [streams][n_seg][S/32]
+  // per-stream budget (budget_scope == KVC_BUDGET_STREAM)
+  bool stream_budget;
+  uint64_t stream_bytes;  // n_seg * budget_bytes
+  uint32_t seg_bytes[KVC_MAX_STRATEGIES];
+  uint32_t* keep_all;     // [streams][n_seg][n_strat][S/32]
+  float* J_all;           // [streams][n_seg][n_strat]
 };
 
 struct DecodePlan {

@@ -47,9 +47,10 @@ def compress(K, V, Qw, *, seg_tokens, strategies, budget_bytes, region_begin=0, 
              t2c_alpha=0, t2c_gamma=0, scale=0.0, forced=None, want_scores=False,
              want_objective=False, ws=None, packed=None, desc=None, n_ctx=None,
              kv_stream_stride=0, qw_head_stride=0, packed_stream_stride=0, packed_base_offset=0,
-             desc_stream_stride=0, n_q_heads=None):
+             desc_stream_stride=0, n_q_heads=None, budget_scope=0):
     """K, V: [B, Hkv, N, 128] bf16 (or strided views described by the stride
-    arguments); Qw: [B, Hq, W, 128] bf16 or None."""
+    arguments); Qw: [B, Hq, W, 128] bf16 or None.  budget_scope 1 shares
+    n_seg * budget_bytes among a stream's segments."""
     B, Hkv = K.shape[0], K.shape[1]
     N = K.shape[2] if n_ctx is None else n_ctx
     Hq = Qw.shape[1] if Qw is not None else (n_q_heads or Hkv)
@@ -59,7 +60,8 @@ def compress(K, V, Qw, *, seg_tokens, strategies, budget_bytes, region_begin=0, 
                  budget_bytes=budget_bytes, t2c_alpha=t2c_alpha, t2c_gamma=t2c_gamma, scale=scale,
                  kv_stream_stride=kv_stream_stride, qw_head_stride=qw_head_stride,
                  packed_stream_stride=packed_stream_stride,
-                 packed_base_offset=packed_base_offset, desc_stream_stride=desc_stream_stride)
+                 packed_base_offset=packed_base_offset, desc_stream_stride=desc_stream_stride,
+                 budget_scope=budget_scope)
     _, L = kv_layout_query(p)
     dev = K.device
     streams = B * Hkv

@@ -99,8 +99,24 @@ typedef struct {
   /* --- decode (kv_attend_decode) --- */
   uint32_t max_desc_per_stream;  /* descriptor stride per stream for decode; 0 => region_len/seg_tokens */
   uint32_t decode_splits;        /* split-K factor; 0 => library choice */
-  uint32_t reserved[4];
+  /* --- compression, continued --- */
+  uint32_t budget_scope;         /* KVC_BUDGET_SEGMENT (0) or KVC_BUDGET_STREAM (1) */
+  uint32_t reserved[3];
 } kvc_params;
+
+/* budget_scope values.
+ * KVC_BUDGET_SEGMENT: every segment's packed bytes <= budget_bytes; each
+ *   segment takes its best feasible strategy.
+ * KVC_BUDGET_STREAM: a stream's segments together <= n_seg * budget_bytes
+ *   (MosaicKV abstract: strategies chosen per segment under the memory
+ *   target; Fig. 5 caption: strategy generation).  Multiple-choice knapsack
+ *   by Lagrangian relaxation: every segment takes argmax_i fl(J_i -
+ *   fl(lambda * seg_bytes_i)) (ties to the lower index) for the smallest fp32
+ *   lambda, by binary search over its bit patterns 0 .. 2^97, whose total
+ *   fits; optimal among all assignments that use at most the bytes it uses.
+ *   forced_strategy must be NULL. */
+#define KVC_BUDGET_SEGMENT 0u
+#define KVC_BUDGET_STREAM 1u
 
 /* Segment descriptor (16 bytes), one per compressed segment.
  * offset: byte offset of the segment's data from the packed base pointer.
@@ -128,10 +144,13 @@ typedef struct {
 
 typedef struct {
   uint32_t seg_bytes[KVC_MAX_STRATEGIES]; /* packed bytes of one segment per strategy */
-  uint32_t feasible_mask;     /* bit i: strategy i fits budget_bytes */
+  uint32_t feasible_mask;     /* bit i: strategy i can be chosen (fits budget_bytes;
+                                 stream scope: fits n_seg * budget_bytes) */
   uint32_t n_seg;             /* segments per stream in the region */
   uint64_t max_seg_bytes;     /* largest feasible seg_bytes */
-  uint64_t stream_capacity;   /* n_seg * max_seg_bytes, rounded up to 256 */
+  uint64_t stream_capacity;   /* bytes one stream may write, rounded up to 256:
+                                 n_seg * max_seg_bytes (stream scope: at most
+                                 n_seg * budget_bytes) */
   uint64_t packed_bytes_max;  /* streams * stream_capacity */
   uint64_t n_desc;            /* streams * n_seg */
   uint64_t compress_ws_bytes; /* workspace for kv_compress */

@@ -205,3 +205,28 @@ def test_selection_validates_before_launch(monkeypatch):
     with pytest.raises(kvc.KvcError) as e:
         kvc.kv_select_segments(p17, a, a, a, None, 4, a, a, a)
     assert e.value.status == -2
+
+
+def test_stream_budget_layout_and_validation(monkeypatch):
+    """Stream scope: every strategy within n_seg * budget can be chosen, the
+    stream writes at most n_seg * budget bytes, forced strategies and an
+    unknown scope are rejected, and a budget below the smallest strategy is
+    KVC_E_BUDGET."""
+    c = gen.CONFIGS["batched128k"]
+    S = c["S"]
+    budget = gen.budget_bytes(25, S)
+    st, L = kvc.kv_layout_query(_params("batched128k", budget_scope=1))
+    n_seg = c["N"] // S
+    assert st == 0 and L.feasible_mask == (1 << 9) - 1 and L.needs_scoring == 1
+    assert L.stream_capacity == (n_seg * budget + 255) // 256 * 256
+    st, Ls = kvc.kv_layout_query(_params("batched128k"))
+    assert L.compress_ws_bytes > Ls.compress_ws_bytes  # keep sets and objectives of all strategies
+    st, _ = kvc.kv_layout_query(_params("tiny", budget_scope=2), check=False)
+    assert st == -1
+    st, _ = kvc.kv_layout_query(_params("tiny", budget_scope=1, budget_bytes=100), check=False)
+    assert st == -3
+    monkeypatch.setattr(kvc, "_stream", lambda: ctypes.c_void_p(0))
+    a = _Fake(0x40000)
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_compress(_params("tiny", budget_scope=1), a, a, a, a, a, a, None, None, None, a)
+    assert e.value.status == -1

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _compare(w, *, S, strategies, budget, region_begin=0, region_len=None, t2c_alpha=0,
-             t2c_gamma=0, forced=None, streams=None, label=""):
+             t2c_gamma=0, forced=None, streams=None, label="", budget_scope=0):
     say(f"[compress] {label} B={w['B']} Hq={w['Hq']} Hkv={w['Hkv']} N={w['N']} S={S} "
         f"W={w['W']} region=({region_begin},{region_len})")
     K, V, Qw = w["K"].cuda(), w["V"].cuda(), w["Qw"].cuda()
@@ -21,13 +21,13 @@ def _compare(w, *, S, strategies, budget, region_begin=0, region_len=None, t2c_a
     r = runtime.compress(K, V, Qw, seg_tokens=S, strategies=strategies, budget_bytes=budget,
                          region_begin=region_begin, region_len=region_len, t2c_alpha=t2c_alpha,
                          t2c_gamma=t2c_gamma, scale=float(SCALE), forced=fdev, want_scores=True,
-                         want_objective=True)
+                         want_objective=True, budget_scope=budget_scope)
     torch.cuda.synchronize()
     cap = r.layout.stream_capacity
     ref = oracle_compress_all(w, S=S, strategies=strategies, budget=budget,
                               region_begin=region_begin, region_len=region_len,
                               t2c_alpha=t2c_alpha, t2c_gamma=t2c_gamma, forced=forced,
-                              streams=streams, capacity=cap)
+                              streams=streams, capacity=cap, budget_scope=budget_scope)
     packed = r.packed.cpu().numpy()
     desc = r.desc_host()
     used = r.used.cpu().numpy()
@@ -123,6 +123,25 @@ def test_compress_many_channel_counts():
     forced = np.array([[(s + 3 * j) % len(strat) for j in range(nseg)] for s in range(streams)],
                       np.uint8)
     _compare(w, S=S, strategies=strat, budget=4 * S * 128, forced=forced, label="six c, forced")
+
+
+@pytest.mark.parametrize("cfg,pct", [("tiny", 25), ("llama8b", 33), ("batched128k", 25)])
+def test_compress_stream_budget(cfg, pct):
+    """Per-stream budget (Lagrangian choice over all strategies): descriptors,
+    packed bytes and objectives bit-exact; the stream stays within
+    n_seg * budget and some segment exceeds the per-segment cap."""
+    c = gen.CONFIGS[cfg]
+    w = gen.make_workload(cfg, N=2048 if cfg != "tiny" else None, B=min(c["B"], 2))
+    S = c["S"]
+    budget = gen.budget_bytes(pct, S)
+    r, ref = _compare(w, S=S, strategies=gen.table9(S), budget=budget, budget_scope=1,
+                      label=f"{cfg} stream budget")
+    n_seg = w["N"] // S
+    used = r.used.cpu().numpy()
+    assert np.all(used <= n_seg * budget)
+    sb = [r.layout.seg_bytes[i] for i in range(9)]
+    d = r.desc_host()
+    assert max(sb[i] for i in d["strategy"].ravel()) > budget
 
 
 def test_compress_kara_event_strided_window():

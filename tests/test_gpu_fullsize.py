@@ -17,7 +17,7 @@ from oracle import oracle as O
 pytestmark = pytest.mark.gpu
 
 
-def _sampled(cfg, streams_to_check):
+def _sampled(cfg, streams_to_check, budget_scope=0):
     c = gen.CONFIGS[cfg]
     S = c["S"]
     strat = gen.table9(S)
@@ -26,7 +26,8 @@ def _sampled(cfg, streams_to_check):
     w = gen.make_workload(cfg, device="cuda")
     say(f"[fullsize] {cfg}: kv_compress + kv_attend_decode")
     r = runtime.compress(w["K"], w["V"], w["Qw"], seg_tokens=S, strategies=strat,
-                         budget_bytes=budget, scale=float(SCALE), want_scores=True)
+                         budget_bytes=budget, scale=float(SCALE), want_scores=True,
+                         budget_scope=budget_scope)
     out, lse = runtime.decode(w["q"], r.packed, r.desc, n_kv_heads=c["Hkv"],
                               max_desc_per_stream=r.n_seg, scale=float(SCALE))
     torch.cuda.synchronize()
@@ -35,7 +36,7 @@ def _sampled(cfg, streams_to_check):
     cap = r.layout.stream_capacity
     G, W = w["G"], w["W"]
     # properties on every stream
-    assert np.all(used <= r.layout.n_seg * r.layout.max_seg_bytes)
+    assert np.all(used <= r.layout.n_seg * (budget if budget_scope else r.layout.max_seg_bytes))
     feas = [i for i in range(len(strat)) if (r.layout.feasible_mask >> i) & 1]
     assert np.isin(desc["strategy"], feas).all()
     assert np.all(desc["seg_tokens"] == S) and np.all(desc["offset"] % 16 == 0)
@@ -50,7 +51,7 @@ def _sampled(cfg, streams_to_check):
         Ks, Vs = gen.u16(w["K"][b, h]), gen.u16(w["V"][b, h])
         Qs = gen.u16(w["Qw"][b, h * G:(h + 1) * G])
         o = O.compress_stream(Ks, Vs, Qs, S=S, strategies=strat, budget_bytes=budget, scale=SCALE,
-                              base_offset=s * cap)
+                              base_offset=s * cap, budget_scope=budget_scope)
         assert np.array_equal(r.scores[s].cpu().numpy().view(np.uint32), o["scores"].view(np.uint32))
         assert np.array_equal(desc[s].view(np.uint8), o["desc"].view(np.uint8))
         assert used[s] == o["used"]
@@ -72,6 +73,11 @@ def test_fullsize_llama8b():
 
 def test_fullsize_batched128k():
     _sampled("batched128k", [0, 77])
+
+
+def test_fullsize_batched128k_stream_budget():
+    """The same workload with the budget shared by each stream's segments."""
+    _sampled("batched128k", [3, 120], budget_scope=1)
 
 
 def test_fullsize_million():

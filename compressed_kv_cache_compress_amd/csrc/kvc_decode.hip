@@ -458,7 +458,19 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
     {
       u32x4_t kb[4];
-      expand_side(sk8, col, grp, ch.nt, ch.c, lut, kb);
+      if (ch.c == D) {
+        // dense rows need no expansion: 16 aligned bytes of the staged row
+        // (stride 2*128 + 16 bytes) per MFMA step; tokens past the chunk are 0
+        const bool live = col < ch.nt;
+        const u32x4_t* r = reinterpret_cast<const u32x4_t*>(sk8 + (2 * D + 16) * (live ? col : 0));
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const u32x4_t z = {0u, 0u, 0u, 0u};
+          kb[kk] = live ? r[4 * kk + grp] : z;
+        }
+      } else {
+        expand_side(sk8, col, grp, ch.nt, ch.c, lut, kb);
+      }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], __builtin_bit_cast(bf16x8_t, kb[kk]),
@@ -490,13 +502,24 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   // then O += P V with the probabilities in L.pl[vb].
   auto v_side = [&](const Chunk& ch, int vb) {
     VStage<JG>& S = L.vs[vb];
-    u32x4_t vv[4];
-    expand_side(reinterpret_cast<const uint8_t*>(S.v), col, grp, ch.nt, ch.c, lut, vv);
     if (JG == 1) {
-      // row-major dense tile [token][channel]
+      // row-major dense tile [token][channel], row stride VR_STRIDE
+      static_assert(2 * VR_STRIDE == 2 * D + 16, "dense staged rows are the tile rows");
+      if (ch.c == D) {
+        // dense rows are staged exactly as the tile; rows past the chunk may
+        // hold older data (their probabilities are 0, but 0 * NaN is NaN)
+        const int nz = (CT - ch.nt) * (VR_STRIDE / 8);
+        for (int i = lane; i < nz; i += 64) {
+          const u32x4_t z = {0u, 0u, 0u, 0u};
+          S.v[ch.nt * (VR_STRIDE / 8) + i] = z;
+        }
+      } else {
+        u32x4_t vv[4];
+        expand_side(reinterpret_cast<const uint8_t*>(S.v), col, grp, ch.nt, ch.c, lut, vv);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        *reinterpret_cast<u32x4_t*>(S.vt + col * VR_STRIDE + 8 * (4 * kk + grp)) = vv[kk];
+        for (int kk = 0; kk < 4; ++kk)
+          *reinterpret_cast<u32x4_t*>(S.vt + col * VR_STRIDE + 8 * (4 * kk + grp)) = vv[kk];
+      }
       const int trow = (lane & 15) >> 2, tcol = 16 * (lane >> 4) + 4 * (lane & 3);
 #pragma unroll
       for (int sg = 0; sg < CT / 4; ++sg) {
@@ -511,6 +534,8 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
       }
     } else {
       // transposed dense tile [channel][token]
+      u32x4_t vv[4];
+      expand_side(reinterpret_cast<const uint8_t*>(S.v), col, grp, ch.nt, ch.c, lut, vv);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         uint16_t* dst = S.vt + (8 * (4 * kk + grp)) * VT_STRIDE + col;

@@ -19,6 +19,8 @@ Printed JSON (one line):
                segment + q + out + partials written and read back
   cpu_baseline the CPU oracle (C, OpenMP) on a bounded sample: compress of
                one stream and fp64 decode of that stream
+  kara         beside the headline (not part of `value`): decode over the
+               Kara sliding-window cache (mostly dense prompt)
   stream_budget beside the headline (not part of `value`): the same workload
                with the byte budget shared by each stream's segments
   stage2       beside the headline (not part of `value`): query-aware
@@ -54,6 +56,8 @@ def parse():
     ap.add_argument("--select-pct", type=float, default=12.5,
                     help="query-aware selection measured beside the headline: percent of the "
                          "segments kept (0 = off)")
+    ap.add_argument("--no-kara", action="store_true",
+                    help="skip the Kara sliding-window decode measurement beside the headline")
     ap.add_argument("--no-stream-budget", action="store_true",
                     help="skip the per-stream budget measurement beside the headline")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "decode_batched128k_traffic.md"),
@@ -94,6 +98,58 @@ def measured_traffic(path):
         return int(vals["bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def bench_kara(a, kvc, stream):
+    """Kara sliding-window workload (B 64, GQA 32/8, prompt 16384 dense + 127
+    compressed events of 13 tokens + 64-token dense tail per stream): the
+    cache is built once with kv_compress events, then decode attention over it
+    is timed with HIP events on the launch stream."""
+    from compressed_kv_cache_compress_amd import gen, kara
+    k = gen.KARA
+    dev = torch.device("cuda:0")
+    w = gen.make_kara(seed=a.seed, device=dev)
+    scale = float(np.float32(1.0 / math.sqrt(128.0)))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    cache = kara.build_cache(w["K"], w["V"], w["Qall"], prompt=w["prompt"], gen=w["gen"],
+                             window=k["window"], delta=k["delta"], protect=k["protect"], seg=64,
+                             retention_pct=k["retention_pct"], alpha=k["alpha"], gamma=k["gamma"],
+                             scale=scale)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    build_ms = e0.elapsed_time(e1)
+    del w["K"], w["V"], w["Qall"]
+    torch.cuda.empty_cache()
+    B, Hq, Hkv = w["B"], w["Hq"], w["Hkv"]
+    p = kvc.KvParams(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, max_desc_per_stream=cache.max_desc,
+                     scale=scale)
+    _, L = kvc.kv_layout_query(p)
+    dws = torch.empty(L.decode_ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(a.steps)]
+    for i in range(a.warmup + a.steps):
+        e = ev[i - a.warmup] if i >= a.warmup else None
+        if e:
+            e[0].record(stream)
+        kvc.kv_attend_decode(p, w["q"], cache.packed, cache.desc, None, out, None, dws)
+        if e:
+            e[1].record(stream)
+    torch.cuda.synchronize()
+    t = float(np.mean([x[0].elapsed_time(x[1]) for x in ev])) * 1e-3
+    dh = cache.desc.cpu().numpy().view(kvc.DESC_DTYPE)
+    n = dh["n_tok"].astype(np.int64)
+    c = dh["n_ch"].astype(np.int64)
+    alg = int((16 + np.where(c < 128, 32 * n, 0) + 4 * n * c).sum()) + 2 * B * Hq * 256 + \
+        2 * B * Hq * L.decode_splits * 520
+    L_ctx = w["prompt"] + w["gen"]
+    return {"workload": "kara: B 64, GQA 32/8, prompt 16384 + 8192 generated, window 512, "
+                        "retention 20 %, Token2Chunk alpha 3 gamma 16, an event every 64 steps",
+            "cache_build_ms": build_ms, "events": cache.n_events, "decode_us": t * 1e6,
+            "kv_tokens_per_s": B * L_ctx / t, "stored_tokens": int(n.sum()),
+            "achieved_GBs": alg / t / 1e9, "pct_of_peak_hbm": 100.0 * alg / t / 1e9 / PEAK_HBM_GBS,
+            "algorithmic_bytes_per_launch": alg}
 
 
 def bench_stream_budget(a, kvc, K, V, Qw, q, B, Hq, Hkv, N, S, W, strategies, budget, scale,
@@ -325,9 +381,14 @@ def main():
         res["stage2"] = stage2
     if sbud is not None:
         res["stream_budget"] = sbud
+    wc = {k: (v[:1].cpu() if torch.is_tensor(v) else v) for k, v in w.items()}
+    if not a.no_kara:
+        print("[bench] kara cache and decode ...", file=sys.stderr, flush=True)
+        del w, K, V, Qw, packed, cws, dws
+        torch.cuda.empty_cache()
+        res["kara"] = bench_kara(a, kvc, stream)
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        wc = {k: (v[:1].cpu() if torch.is_tensor(v) else v) for k, v in w.items()}
         res["cpu_baseline"] = cpu_baseline(wc, S, strategies, budget, scale)
     print(json.dumps(res))
 

@@ -80,9 +80,6 @@ constexpr int WAVES = 4;
 #ifndef KVC_DECODE_MIN_BLOCKS
 #define KVC_DECODE_MIN_BLOCKS 2  // workgroups per CU the register budget is sized for
 #endif
-#ifndef KVC_DECODE_DEPTH
-#define KVC_DECODE_DEPTH 1  // chunks prefetched ahead into registers
-#endif
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -118,37 +115,13 @@ struct WaveLds {
 
 static_assert(chunk_tokens(64) == CT && chunk_tokens(D) >= 12, "stage sizing");
 
-__device__ __forceinline__ float dpp_f(float v, int ctrl) {
-  switch (ctrl) {  // the control must be a constant
-    case 0xB1: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-    case 0x4E: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-    case 0x141: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
-    default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
-  }
-}
-// Max / sum over the 16 lanes of a DPP row (every lane gets the result).
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_f(v, 0xB1));
-  v = fmaxf(v, dpp_f(v, 0x4E));
-  v = fmaxf(v, dpp_f(v, 0x141));
-  v = fmaxf(v, dpp_f(v, 0x140));
-  return v;
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f(v, 0xB1);
-  v += dpp_f(v, 0x4E);
-  v += dpp_f(v, 0x141);
-  v += dpp_f(v, 0x140);
-  return v;
-}
 
-// Ordering of this wave's LDS accesses.  LDS executes a wave's DS
-// instructions in issue order, so a later read sees an earlier write (also
-// from another lane) and a later write cannot overtake an earlier read; the
-// compiler keeps accesses that may overlap in program order (the library is
-// built with -fno-strict-aliasing because the staging buffers are read and
-// written through different types).  No fence is needed.
-__device__ __forceinline__ void lds_order() {}
+// Ordering of a wave's LDS accesses, and why the chunk loop needs no fence:
+// LDS executes a wave's DS instructions in issue order, so a later read sees
+// an earlier write (also from another lane) and a later write cannot overtake
+// an earlier read; the compiler keeps accesses that may overlap in program
+// order (the library is built with -fno-strict-aliasing because the staging
+// buffers are read and written through different types).
 
 // Selector table entry for a mask nibble n (channels 0..3 of the nibble):
 // dword d holds the v_perm_b32 selectors of channels 2d and 2d+1, i.e. bytes
@@ -389,7 +362,7 @@ __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
   return ch;
 }
 
-template <int JG, int DEPTH>
+template <int JG>
 __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_decode_split(DecodeArgs a) {
   __shared__ uint2 lut[16];
   __shared__ WaveLds<JG> wl[WAVES];
@@ -579,25 +552,21 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
     commit(cur, lane, rg, L.k, L.vs[0].v);
     Chunk nxt = next_chunk(cu, lane);
     prefetch(nxt, lane, rg);
-    lds_order();
     float alpha[JG];
     if (k_side(cur, 0, alpha)) rescale(alpha);
     int vb = 0;
     // iteration: stage chunk i+1, load chunk i+2, K side of i+1, V side of i
     while (nxt.valid) {
-      lds_order();
-      commit(nxt, lane, rg, L.k, L.vs[vb ^ 1].v);
+        commit(nxt, lane, rg, L.k, L.vs[vb ^ 1].v);
       const Chunk far = next_chunk(cu, lane);
       prefetch(far, lane, rg);
-      lds_order();
-      const bool resc = k_side(nxt, vb ^ 1, alpha);
+        const bool resc = k_side(nxt, vb ^ 1, alpha);
       v_side(cur, vb);
       if (resc) rescale(alpha);
       cur = nxt;
       nxt = far;
       vb ^= 1;
     }
-    lds_order();
     v_side(cur, vb);
   }
 
@@ -676,11 +645,11 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
   a.sl2 = p.scale * KVC_LOG2E;
   const dim3 grid((a.items + WAVES - 1) / WAVES);
   if (p.G <= 4)
-    hipLaunchKernelGGL((k_decode_split<1, KVC_DECODE_DEPTH>), grid, dim3(64 * WAVES), 0, st, a);
+    hipLaunchKernelGGL((k_decode_split<1>), grid, dim3(64 * WAVES), 0, st, a);
   else if (p.G <= 8)
-    hipLaunchKernelGGL((k_decode_split<2, 1>), grid, dim3(64 * WAVES), 0, st, a);
+    hipLaunchKernelGGL((k_decode_split<2>), grid, dim3(64 * WAVES), 0, st, a);
   else
-    hipLaunchKernelGGL((k_decode_split<4, 1>), grid, dim3(64 * WAVES), 0, st, a);
+    hipLaunchKernelGGL((k_decode_split<4>), grid, dim3(64 * WAVES), 0, st, a);
   hipLaunchKernelGGL(k_decode_reduce, dim3(p.batch * p.hq), dim3(128), 0, st, p.part_ml, p.part_acc,
                      p.out, p.lse, p.splits);
   return hipGetLastError();

@@ -64,16 +64,30 @@ __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// Maximum and pairwise-tree sum over the 16 lanes of a DPP row (every lane
+// gets the result): lane pairs, quads, 8-lane halves, then the two halves.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, dpp_mov<0x140>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v = v + dpp_mov<0xB1>(v);
+  v = v + dpp_mov<0x4E>(v);
+  v = v + dpp_mov<0x141>(v);
+  v = v + dpp_mov<0x140>(v);
+  return v;
+}
+
 // Pairwise-tree sum over the 64 lanes of a full wave (every lane active),
 // returned wave-uniform.  Same order as tree_sum_lanes: lane pairs, quads,
 // 8-lane halves and 16-lane rows by DPP (after each step the lanes of a group
 // agree, so a mirror reaches the partner group), then (r0 + r1) + (r2 + r3)
 // over the four rows.
 __device__ __forceinline__ float tree_sum64(float v) {
-  v = v + dpp_mov<0xB1>(v);
-  v = v + dpp_mov<0x4E>(v);
-  v = v + dpp_mov<0x141>(v);
-  v = v + dpp_mov<0x140>(v);
+  v = row16_sum(v);
   const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
   const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
   const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
@@ -83,10 +97,7 @@ __device__ __forceinline__ float tree_sum64(float v) {
 
 // Maximum over the 64 lanes of a full wave, returned wave-uniform.
 __device__ __forceinline__ float max64(float v) {
-  v = fmaxf(v, dpp_mov<0xB1>(v));
-  v = fmaxf(v, dpp_mov<0x4E>(v));
-  v = fmaxf(v, dpp_mov<0x141>(v));
-  v = fmaxf(v, dpp_mov<0x140>(v));
+  v = row16_max(v);
   const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
   const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
   const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));

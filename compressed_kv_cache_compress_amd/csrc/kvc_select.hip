@@ -79,15 +79,6 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 
 constexpr int SCORE_ITERS = 4;  // descriptor groups of 4 per wave in k_select_scores
 
-// Pairwise-tree sum over the 16 lanes of a DPP row (every lane gets it):
-// lane pairs, quads, 8-lane halves, then the two halves.
-__device__ __forceinline__ float row16_tree(float v) {
-  v = v + dpp_mov<0xB1>(v);
-  v = v + dpp_mov<0x4E>(v);
-  v = v + dpp_mov<0x141>(v);
-  v = v + dpp_mov<0x140>(v);
-  return v;
-}
 
 // grid (ceil(maxd / (16 * SCORE_ITERS)), streams), 256 threads.  A 16-lane
 // row per descriptor (4 per wave), lane i of the row holding channels
@@ -130,7 +121,7 @@ __global__ __launch_bounds__(256) void k_select_scores(SelectPlan p) {
         t[2 * k + 1] = fmaxf(q1 * mx[2 * k + 1], q1 * mn[2 * k + 1]) + 0.0f;
       }
       const float v = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
-      best = fmaxf(best, row16_tree(v));
+      best = fmaxf(best, row16_sum(v));
     }
     if (cb == 0 && d < p.maxd) p.score[(uint64_t)s * p.maxd + d] = live ? best : -INFINITY;
   }

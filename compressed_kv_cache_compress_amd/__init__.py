@@ -60,6 +60,31 @@ class Layout(ctypes.Structure):
                 ("needs_scoring", ctypes.c_uint32)]
 
 
+class PipeConfig(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("mode", ctypes.c_uint32),
+                ("switch_lag", ctypes.c_uint32), ("pages", ctypes.c_uint32),
+                ("max_events", ctypes.c_uint32), ("prefix_desc", ctypes.c_uint32),
+                ("protect", ctypes.c_uint32), ("reserved0", ctypes.c_uint32),
+                ("events_offset", ctypes.c_uint64), ("pages_offset", ctypes.c_uint64),
+                ("reserved", ctypes.c_uint64 * 2)]
+
+
+class PipeLayout(ctypes.Structure):
+    _fields_ = [("desc_per_stream", ctypes.c_uint32), ("period", ctypes.c_uint32),
+                ("event_bytes", ctypes.c_uint64), ("page_bytes", ctypes.c_uint64),
+                ("stream_bytes_min", ctypes.c_uint64), ("ws_bytes", ctypes.c_uint64),
+                ("decode_splits", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+class PipeStats(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_uint64), ("tokens", ctypes.c_uint64),
+                ("events_fired", ctypes.c_uint64), ("events_switched", ctypes.c_uint64),
+                ("host_waits", ctypes.c_uint64), ("pending", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
+
+
+PIPE_ASYNC, PIPE_SYNC, PIPE_LAG = 0, 1, 2
+
 _lib = None
 
 
@@ -85,6 +110,23 @@ def lib():
         L.kv_select_segments.argtypes = [ctypes.POINTER(Params), P, P, P, P, ctypes.c_uint32, P,
                                          P, P, P]
         L.kv_select_segments.restype = ctypes.c_int
+        u32, u64 = ctypes.c_uint32, ctypes.c_uint64
+        L.kv_append.argtypes = [ctypes.POINTER(Params), P, P, u32, u32, u32, u64, P, P, P]
+        L.kv_append.restype = ctypes.c_int
+        L.kv_pipe_layout.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(PipeConfig),
+                                     ctypes.POINTER(PipeLayout)]
+        L.kv_pipe_layout.restype = ctypes.c_int
+        L.kv_pipe_create.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(PipeConfig), P, P, P,
+                                     ctypes.c_size_t, P, ctypes.POINTER(ctypes.c_void_p)]
+        L.kv_pipe_create.restype = ctypes.c_int
+        L.kv_pipe_step.argtypes = [P, P, P, u32, u64, P, P, P, P, P, P, P]
+        L.kv_pipe_step.restype = ctypes.c_int
+        L.kv_pipe_drain.argtypes = [P, P]
+        L.kv_pipe_drain.restype = ctypes.c_int
+        L.kv_pipe_get_stats.argtypes = [P, ctypes.POINTER(PipeStats)]
+        L.kv_pipe_get_stats.restype = ctypes.c_int
+        L.kv_pipe_destroy.argtypes = [P]
+        L.kv_pipe_destroy.restype = ctypes.c_int
         L.kvc_status_str.argtypes = [ctypes.c_int]
         L.kvc_status_str.restype = ctypes.c_char_p
         L.kvc_abi_version.restype = ctypes.c_int
@@ -181,6 +223,82 @@ def kv_select_segments(params, q, summary, desc, n_desc, keep, out_desc, out_n, 
                                   _ptr(score), _stream())
     if st != 0:
         raise KvcError("kv_select_segments", st)
+
+
+def kv_append(params, k_new, v_new, n_new, fill, capacity, page_offset, packed, page_desc):
+    """Enqueue the append of n_new tokens per stream to dense pages."""
+    st = lib().kv_append(ctypes.byref(params.p), _ptr(k_new), _ptr(v_new), int(n_new), int(fill),
+                         int(capacity), int(page_offset), _ptr(packed), _ptr(page_desc), _stream())
+    if st != 0:
+        raise KvcError("kv_append", st)
+
+
+def pipe_config(*, mode=PIPE_ASYNC, switch_lag=0, pages, max_events, prefix_desc=0, protect=0,
+                events_offset=0, pages_offset=0):
+    c = PipeConfig()
+    c.struct_size = ctypes.sizeof(PipeConfig)
+    c.mode, c.switch_lag, c.pages, c.max_events = mode, switch_lag, pages, max_events
+    c.prefix_desc, c.protect = prefix_desc, protect
+    c.events_offset, c.pages_offset = events_offset, pages_offset
+    return c
+
+
+def kv_pipe_layout(params, cfg, check=True):
+    """Host-only pipeline layout query -> (status, PipeLayout)."""
+    L = PipeLayout()
+    st = lib().kv_pipe_layout(ctypes.byref(params.p), ctypes.byref(cfg), ctypes.byref(L))
+    if check and st != 0:
+        raise KvcError("kv_pipe_layout", st)
+    return st, L
+
+
+class KvPipe:
+    """Owner of a kvc_pipe handle (kv_pipe_create .. kv_pipe_destroy).  The
+    tensors passed at creation are kept referenced until close()."""
+
+    def __init__(self, params, cfg, packed, desc, ws):
+        self.params, self.cfg = params, cfg
+        self._keep = (packed, desc, ws)
+        self.stream = _stream()
+        h = ctypes.c_void_p()
+        st = lib().kv_pipe_create(ctypes.byref(params.p), ctypes.byref(cfg), _ptr(packed),
+                                  _ptr(desc), _ptr(ws), ws.numel() * ws.element_size(),
+                                  self.stream, ctypes.byref(h))
+        if st != 0:
+            raise KvcError("kv_pipe_create", st)
+        self.h = h
+
+    def step(self, k_new, v_new, n_new=1, new_stride=0, win_K=None, win_V=None, win_Q=None,
+             q=None, out=None, lse=None):
+        st = lib().kv_pipe_step(self.h, _ptr(k_new), _ptr(v_new), int(n_new), int(new_stride),
+                                _ptr(win_K), _ptr(win_V), _ptr(win_Q), _ptr(q), _ptr(out),
+                                _ptr(lse), self.stream)
+        if st != 0:
+            raise KvcError("kv_pipe_step", st)
+
+    def drain(self):
+        st = lib().kv_pipe_drain(self.h, self.stream)
+        if st != 0:
+            raise KvcError("kv_pipe_drain", st)
+
+    def stats(self):
+        s = PipeStats()
+        st = lib().kv_pipe_get_stats(self.h, ctypes.byref(s))
+        if st != 0:
+            raise KvcError("kv_pipe_get_stats", st)
+        return {k: int(getattr(s, k)) for k, _ in PipeStats._fields_ if k != "reserved"}
+
+    def close(self):
+        if self.h:
+            lib().kv_pipe_destroy(self.h)
+            self.h = None
+            self._keep = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def desc_view(t):

@@ -285,7 +285,7 @@ struct Cursor {
   const uint8_t* packed;
   int di, d1, base;         // next descriptor, end, first descriptor held in the lanes
   uint32_t w0, w1, w2;      // this lane's descriptor (base + lane): offset lo/hi, n_tok|n_ch<<16
-  uint32_t w3;              // its chunk geometry: tokens per chunk | row magic << 5
+  uint32_t w3;              // its chunk geometry: tokens per chunk | row magic << 5 | page << 26
   // current segment
   const uint8_t *kmask, *kval, *vmask, *vval;  // at token 0
   int T, c, t0, ct;
@@ -304,10 +304,14 @@ __device__ __forceinline__ void fetch_descs(Cursor& cu, int lane) {
   cu.w1 = d[1];
   cu.w2 = d[2];
   // per-descriptor chunk geometry, computed once per 64 descriptors so that
-  // the chunk loop reads it with readlane instead of a memory lookup
+  // the chunk loop reads it with readlane instead of a memory lookup; a
+  // paged descriptor (flags bit2) also carries log2(seg_tokens) + 1, the
+  // token count its parts are laid out for
   const int c = (int)(d[2] >> 16) & ~7;
   const int cc = c < 8 ? 8 : (c > D ? D : c);
-  cu.w3 = (uint32_t)chunk_tokens(cc) | (row_magic(cc >> 3) << 5);
+  const uint32_t cap = d[3] >> 16;
+  const uint32_t page = ((d[3] >> 8) & KVC_DESC_PAGED) && cap ? 32u - __clz(cap) : 0u;
+  cu.w3 = (uint32_t)chunk_tokens(cc) | (row_magic(cc >> 3) << 5) | (page << 26);
 }
 
 // Advances to the next non-empty chunk; returns its description.
@@ -329,13 +333,15 @@ __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
         const uint32_t geo = __builtin_amdgcn_readlane(cu.w3, sl);
         const int c = (int)(tc >> 16);
         cu.ct = (int)(geo & 31u);
-        cu.magic = geo >> 5;
-        const uint32_t mb = c < D ? 16u * T : 0u;
+        cu.magic = (geo >> 5) & 0x1FFFFFu;
+        const uint32_t page = geo >> 26;
+        const uint32_t TL = page ? 1u << (page - 1u) : (uint32_t)T;  // tokens the parts are sized for
+        const uint32_t mb = c < D ? 16u * TL : 0u;
         const uint8_t* base = cu.packed + (((uint64_t)hi << 32) | lo);
         cu.kmask = base;
         cu.kval = base + mb;
-        cu.vmask = base + mb + 2u * T * c;
-        cu.vval = base + 2 * mb + 2u * T * c;
+        cu.vmask = base + mb + 2u * TL * c;
+        cu.vval = base + 2 * mb + 2u * TL * c;
         cu.T = T;
         cu.c = c;
         cu.t0 = 0;

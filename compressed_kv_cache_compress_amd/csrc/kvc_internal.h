@@ -82,7 +82,38 @@ struct SelectPlan {
   float* score;            // [streams][maxd]
 };
 
+// Dense pages and the descriptor switch of the compression pipeline
+// (kvc_pipe.hip).
+struct AppendPlan {
+  int streams, n_new, fill, capacity;
+  uint64_t src_stride;     // elements between streams of k_new / v_new
+  uint64_t page_offset;    // stream 0's page, bytes from packed
+  uint64_t pstride;        // bytes between streams' pages
+  uint32_t dstride;        // descriptors between streams
+  const uint16_t *k, *v;
+  uint8_t* packed;
+  kvc_seg_desc* desc;
+};
+
+struct SwitchPlan {
+  int streams;
+  uint32_t dstride;        // descriptors between streams in the list
+  int final_slot;          // list index that receives the staged descriptor (-1: none)
+  int clear_slot;          // list index emptied (the page), -1: none
+  const kvc_seg_desc* staged;  // [streams]
+  kvc_seg_desc* list;
+};
+
+struct ClearPlan {
+  int streams, first, count;   // empties list slots first .. first + count - 1
+  uint32_t dstride;
+  kvc_seg_desc* list;
+};
+
 hipError_t launch_compress(const CompressPlan& p, hipStream_t st);
+hipError_t launch_append(const AppendPlan& p, hipStream_t st);
+hipError_t launch_switch(const SwitchPlan& p, hipStream_t st);
+hipError_t launch_clear(const ClearPlan& p, hipStream_t st);
 hipError_t launch_summarize(const SummaryPlan& p, hipStream_t st);
 hipError_t launch_select(const SelectPlan& p, hipStream_t st);
 hipError_t launch_decode(const DecodePlan& p, hipStream_t st);

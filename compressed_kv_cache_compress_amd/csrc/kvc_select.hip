@@ -37,7 +37,9 @@ __global__ __launch_bounds__(64) void k_summarize(SummaryPlan p) {
   const int c = ds.n_ch;
   const uint8_t* base = p.packed + ds.offset;
   const bool hm = c < D;
-  const uint8_t* kval = base + (hm ? 16 * T : 0);
+  // a paged descriptor's parts are sized for seg_tokens tokens
+  const int TL = (ds.flags & KVC_DESC_PAGED) ? (int)ds.seg_tokens : T;
+  const uint8_t* kval = base + (hm ? 16 * TL : 0);
   float mx0 = -INFINITY, mx1 = -INFINITY, mn0 = INFINITY, mn1 = INFINITY;
   const int ch = 2 * lane, wd = lane >> 4, bit = ch & 31;
   for (int t = 0; t < T; ++t) {

@@ -121,8 +121,12 @@ typedef struct {
 /* Segment descriptor (16 bytes), one per compressed segment.
  * offset: byte offset of the segment's data from the packed base pointer.
  * flags: bit0 = all S tokens kept (no index list), bit1 = all 128 channels
- * kept (no masks), bit7 = a forced strategy was rejected (out of range or
- * over budget) and the library chose instead. */
+ * kept (no masks), bit2 = paged (KVC_DESC_PAGED: the parts below are laid out
+ * for seg_tokens tokens, a power of two >= n_tok, of which the first n_tok
+ * are filled, so tokens are appended in place; written by kv_append), bit7 =
+ * a forced strategy was rejected (out of range or over budget) and the
+ * library chose instead. */
+#define KVC_DESC_PAGED 0x04u
 typedef struct {
   uint64_t offset;
   uint16_t n_tok;
@@ -257,6 +261,139 @@ kvc_status kv_select_segments(const kvc_params* p, const uint16_t* q, const uint
                               const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
                               uint32_t keep, kvc_seg_desc* out_desc, uint32_t* out_n, float* score,
                               hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Incremental, asynchronous compression (MosaicKV review page: Fig. 1 and
+ * Fig. 5 captions -- compression runs asynchronously and, once a new segment
+ * is complete and compressed, a switch replaces its temporary form with the
+ * final one without blocking decode; Fig. 7 caption -- double compression
+ * buffering.  KARA review page, free-parameter ledger -- compression period
+ * delta and protected buffer U).
+ *
+ * Newly generated tokens are appended to dense pages (the temporary form of
+ * a segment: every token, all 128 channels).  When a page completes and
+ * `protect` more tokens follow it, that page is compressed by kv_compress on
+ * a second stream; decode keeps reading the page until the switch writes the
+ * final descriptor into its event slot and empties the page's slot, in one
+ * kernel on the decode stream.
+ * ------------------------------------------------------------------------ */
+
+/* Append n_new tokens per stream to dense paged segments.
+ *  k_new, v_new  device [streams][n_new][128] bf16, stream stride
+ *                p->kv_stream_stride elements (0 => n_new * 128).
+ *  fill          tokens already in each page; fill + n_new <= capacity.
+ *  capacity      tokens a page holds: a power of two in [1, 32768].
+ *  page_offset   byte offset of stream 0's page from `packed`; stream s's
+ *                page is at packed + page_offset + s * p->packed_stream_stride
+ *                (stride required, >= 512 * capacity, multiple of 16).
+ *  page_desc     device; stream s's descriptor at page_desc[s *
+ *                p->desc_stream_stride] (0 => 1) is overwritten with
+ *                {page offset, n_tok = fill + n_new, n_ch = 128, strategy 0,
+ *                flags = bit0 | bit1 | KVC_DESC_PAGED, seg_tokens = capacity}.
+ * Page layout: K rows [capacity][128] bf16, then V rows [capacity][128] bf16;
+ * token fill + i goes to row fill + i of both.  Uses batch, n_q_heads,
+ * n_kv_heads, head_dim and the strides of p.  Pure copy: bit-exact. */
+kvc_status kv_append(const kvc_params* p, const uint16_t* k_new, const uint16_t* v_new,
+                     uint32_t n_new, uint32_t fill, uint32_t capacity, uint64_t page_offset,
+                     void* packed, kvc_seg_desc* page_desc, hipStream_t stream);
+
+/* When a finished event's final segment replaces its page. */
+#define KVC_PIPE_ASYNC 0u /* at the first step after the host sees the event done (no wait) */
+#define KVC_PIPE_SYNC 1u  /* compress on the decode stream inside the step that fires it,
+                             switched before that step's decode: the blocking baseline */
+#define KVC_PIPE_LAG 2u   /* exactly switch_lag steps after the step that fires it (the
+                             decode stream waits for the event on the device if needed):
+                             deterministic, for tests */
+
+typedef struct {
+  uint32_t struct_size;   /* == sizeof(kvc_pipe_config) */
+  uint32_t mode;          /* KVC_PIPE_ASYNC, KVC_PIPE_SYNC or KVC_PIPE_LAG */
+  uint32_t switch_lag;    /* KVC_PIPE_LAG: steps from firing to switch, 0 .. slack
+                             (slack = (pages - protect/period - 1) * period) */
+  uint32_t pages;         /* dense pages per stream, >= protect/period + 2 */
+  uint32_t max_events;    /* event slots per stream (events beyond them: KVC_E_INVALID) */
+  uint32_t prefix_desc;   /* the caller's descriptors at the head of every stream's list */
+  uint32_t protect;       /* tokens that stay dense after the region: a multiple of period */
+  uint32_t reserved0;
+  uint64_t events_offset; /* byte offset of event slot 0 in a stream's packed slot */
+  uint64_t pages_offset;  /* byte offset of page 0 in a stream's packed slot */
+  uint64_t reserved[2];
+} kvc_pipe_config;
+
+typedef struct {
+  uint32_t desc_per_stream;  /* prefix_desc + max_events + pages: the decode list stride */
+  uint32_t period;           /* tokens per page = region tokens per event = seg_tokens */
+  uint64_t event_bytes;      /* bytes of one event slot (largest feasible segment) */
+  uint64_t page_bytes;       /* bytes of one page: 512 * period */
+  uint64_t stream_bytes_min; /* smallest packed_stream_stride that holds both areas */
+  uint64_t ws_bytes;         /* workspace: event compress + staged descriptors + decode */
+  uint32_t decode_splits;    /* split-K factor of the pipeline's decode */
+  uint32_t reserved;
+} kvc_pipe_layout;
+
+typedef struct {
+  uint64_t steps, tokens;     /* kv_pipe_step calls; tokens appended */
+  uint64_t events_fired;      /* event compressions launched */
+  uint64_t events_switched;   /* of which switched into the decode list */
+  uint64_t host_waits;        /* KVC_PIPE_ASYNC: a page was needed before its event was seen
+                                 done, so the host waited */
+  uint32_t pending;           /* fired events not yet switched */
+  uint32_t reserved;
+} kvc_pipe_stats;
+
+typedef struct kvc_pipe kvc_pipe; /* opaque pipeline state (host memory) */
+
+/* Host only.  p describes one event's compression: n_ctx = window positions
+ * scored, region_begin = n_ctx - protect - seg_tokens, region_len =
+ * seg_tokens, n_win, strategies, budget_bytes, t2c_*, scale as for
+ * kv_compress; kv_stream_stride / qw_head_stride describe the caller's window
+ * arrays; packed_stream_stride is the stride of the whole packed buffer;
+ * desc_stream_stride is 0 or desc_per_stream; decode_splits as for decode. */
+kvc_status kv_pipe_layout(const kvc_params* p, const kvc_pipe_config* cfg, kvc_pipe_layout* out);
+
+/* Creates the pipeline (host state, one non-blocking stream of default
+ * priority and its events) and enqueues on `stream` the clearing of every
+ * stream's event and page slots in desc [streams][desc_per_stream].  The
+ * caller owns packed, desc and ws (>= ws_bytes) and keeps them alive until
+ * kv_pipe_destroy; the prefix descriptors are the caller's.  Every later call
+ * on this pipeline passes the same `stream`. */
+kvc_status kv_pipe_create(const kvc_params* p, const kvc_pipe_config* cfg, void* packed,
+                          kvc_seg_desc* desc, void* ws, size_t ws_bytes, hipStream_t stream,
+                          kvc_pipe** out);
+
+/* One step: switch the events that are due, append n_new tokens per stream
+ * to the current page (a step's tokens stay within one page), fire an event
+ * when the pipeline's token count g reaches a multiple of period with g >=
+ * protect + period (its region: tokens g - protect - period .. g - protect -
+ * 1, one page), then decode q over the list (skipped when out is NULL).
+ *  k_new, v_new       device [streams][n_new][128] bf16, stream stride new_stride
+ *                     elements (0 => n_new * 128).
+ *  win_K, win_V       device: position 0 of the scoring window (the last
+ *                     p->n_ctx positions, this step's tokens included) of
+ *                     every stream, stream stride p->kv_stream_stride;
+ *  win_Q              device: the window's queries, [streams * G] rows of
+ *                     stride p->qw_head_stride, the last n_win positions;
+ *                     all three only read when an event fires (else may be
+ *                     NULL) and must stay unchanged until it is switched.
+ *  q, out, lse        as for kv_attend_decode over the pipeline's list.
+ * Events whose region would start before the pipeline's first token are not
+ * fired.  Returns KVC_E_INVALID when an event is due and the window is
+ * missing or the event slots are used up (nothing enqueued). */
+kvc_status kv_pipe_step(kvc_pipe* pipe, const uint16_t* k_new, const uint16_t* v_new,
+                        uint32_t n_new, uint64_t new_stride, const uint16_t* win_K,
+                        const uint16_t* win_V, const uint16_t* win_Q, const uint16_t* q,
+                        uint16_t* out, float* lse, hipStream_t stream);
+
+/* Switches every fired event (the decode stream waits for each on the
+ * device; the host does not block).  Afterwards the list holds every final
+ * segment and only the pages that no event covers. */
+kvc_status kv_pipe_drain(kvc_pipe* pipe, hipStream_t stream);
+
+kvc_status kv_pipe_get_stats(const kvc_pipe* pipe, kvc_pipe_stats* out);
+
+/* Waits for the pipeline's own stream, then releases its stream, events and
+ * host state.  NULL is accepted. */
+kvc_status kv_pipe_destroy(kvc_pipe* pipe);
 
 /* Static description of a status code. */
 const char* kvc_status_str(kvc_status s);

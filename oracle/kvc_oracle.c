@@ -638,6 +638,11 @@ int orc_compress_stream(const orc_params* p, const uint16_t* K, const uint16_t* 
 /* packed.  out: [G][128] fp64, lse: [G] (log of the softmax            */
 /* denominator incl. the max; -inf and out = 0 if no token is kept).     */
 /* ------------------------------------------------------------------ */
+/* Tokens a descriptor's parts are sized for: n_tok, or seg_tokens for a
+ * paged descriptor (flags bit2), whose first n_tok of seg_tokens rows are
+ * filled so that tokens can be appended in place. */
+static int layout_tokens(const orc_desc* d) { return (d->flags & 4) ? d->seg_tokens : d->n_tok; }
+
 void orc_decode_stream(int G, const uint16_t* q, const uint8_t* packed, const orc_desc* desc,
                        int n_desc, float scale, double* out, double* lse) {
   long ntok = 0;
@@ -646,10 +651,10 @@ void orc_decode_stream(int G, const uint16_t* q, const uint8_t* packed, const or
   /* pass 1: logits */
   long j = 0;
   for (int i = 0; i < n_desc; ++i) {
-    const int T = desc[i].n_tok, c = desc[i].n_ch;
+    const int T = desc[i].n_tok, c = desc[i].n_ch, TL = layout_tokens(&desc[i]);
     const uint8_t* base = packed + desc[i].offset;
     const uint8_t* kmask = base;
-    const uint8_t* kval = base + (c < ORC_D ? 16 * T : 0);
+    const uint8_t* kval = base + (c < ORC_D ? 16 * TL : 0);
     for (int t = 0; t < T; ++t, ++j) {
       const uint8_t* mk = c < ORC_D ? kmask + 16 * t : NULL;
       const uint8_t* vals = kval + (size_t)2 * c * t;
@@ -683,11 +688,11 @@ void orc_decode_stream(int G, const uint16_t* q, const uint8_t* packed, const or
     /* pass 2: weighted sum of the kept V elements */
     long jj = 0;
     for (int i = 0; i < n_desc; ++i) {
-      const int T = desc[i].n_tok, c = desc[i].n_ch;
+      const int T = desc[i].n_tok, c = desc[i].n_ch, TL = layout_tokens(&desc[i]);
       const uint8_t* base = packed + desc[i].offset;
-      const size_t kpart = (size_t)(c < ORC_D ? 16 * T : 0) + (size_t)2 * T * c;
+      const size_t kpart = (size_t)(c < ORC_D ? 16 * TL : 0) + (size_t)2 * TL * c;
       const uint8_t* vmask = base + kpart;
-      const uint8_t* vval = vmask + (c < ORC_D ? 16 * T : 0);
+      const uint8_t* vval = vmask + (c < ORC_D ? 16 * TL : 0);
       for (int t = 0; t < T; ++t, ++jj) {
         const double pr = exp(l[jj * G + g] - mx) / den;
         const uint8_t* mk = c < ORC_D ? vmask + 16 * t : NULL;
@@ -727,11 +732,11 @@ void orc_decode_stream(int G, const uint16_t* q, const uint8_t* packed, const or
 void orc_summarize_stream(const uint8_t* packed, const orc_desc* desc, int n_desc,
                           uint16_t* summary) {
   for (int i = 0; i < n_desc; ++i) {
-    const int T = desc[i].n_tok, c = desc[i].n_ch;
+    const int T = desc[i].n_tok, c = desc[i].n_ch, TL = layout_tokens(&desc[i]);
     uint16_t* smax = summary + (size_t)i * 2 * ORC_D;
     uint16_t* smin = smax + ORC_D;
     const uint8_t* base = packed + desc[i].offset;
-    const uint8_t* kval = base + (c < ORC_D ? 16 * T : 0);
+    const uint8_t* kval = base + (c < ORC_D ? 16 * TL : 0);
     float mx[ORC_D], mn[ORC_D];
     for (int ch = 0; ch < ORC_D; ++ch) {
       mx[ch] = -INFINITY;

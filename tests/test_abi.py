@@ -230,3 +230,86 @@ def test_stream_budget_layout_and_validation(monkeypatch):
     with pytest.raises(kvc.KvcError) as e:
         kvc.kv_compress(_params("tiny", budget_scope=1), a, a, a, a, a, a, None, None, None, a)
     assert e.value.status == -1
+
+
+def _pipe_params(**kw):
+    d = dict(batch=2, n_q_heads=8, n_kv_heads=2, n_ctx=128, region_begin=64, region_len=32,
+             seg_tokens=32, n_win=128, strategies=[(6, 128)], budget_bytes=4 * 32 * 128,
+             t2c_alpha=1, t2c_gamma=8, kv_stream_stride=768 * 128, qw_head_stride=768 * 128)
+    d.update(kw)
+    return kvc.KvParams(**d)
+
+
+def test_pipe_layout_and_validation():
+    """Pipeline layout: list stride, slot sizes, the smallest stream stride
+    and workspace; invalid schedules and overlapping areas are rejected on
+    the host."""
+    cfg = kvc.pipe_config(pages=4, max_events=15, prefix_desc=4, protect=32,
+                          events_offset=4 * 64 * 512, pages_offset=4 * 64 * 512 + 15 * 3632)
+    p = _pipe_params()
+    st, L = kvc.kv_pipe_layout(p, cfg)
+    assert st == 0
+    seg = 6 * 512 + 16  # 6 tokens x 512 B + index list padded to 16 B
+    assert L.desc_per_stream == 4 + 15 + 4 and L.period == 32
+    assert L.event_bytes == seg and L.page_bytes == 32 * 512
+    assert L.stream_bytes_min == cfg.pages_offset + 4 * 32 * 512
+    _, Lc = kvc.kv_layout_query(_pipe_params(max_desc_per_stream=L.desc_per_stream))
+    assert L.ws_bytes >= Lc.compress_ws_bytes + Lc.decode_ws_bytes + 4 * 4 * 16
+    assert L.decode_splits == Lc.decode_splits
+
+    def bad(params=None, **c):
+        base = dict(pages=4, max_events=15, prefix_desc=4, protect=32,
+                    events_offset=cfg.events_offset, pages_offset=cfg.pages_offset)
+        base.update(c)
+        st, _ = kvc.kv_pipe_layout(params or p, kvc.pipe_config(**base), check=False)
+        return st
+
+    assert bad(protect=16) == -1                         # not a multiple of the period
+    assert bad(pages=2) == -1                            # fewer than protect/period + 2
+    assert bad(max_events=0) == -1
+    assert bad(mode=3) == -1
+    assert bad(mode=kvc.PIPE_LAG, switch_lag=65) == -1   # beyond (4 - 1 - 1) * 32
+    assert bad(mode=kvc.PIPE_LAG, switch_lag=64) == 0
+    assert bad(pages_offset=cfg.events_offset + 16) == -1  # overlaps the event slots
+    assert bad(events_offset=8) == -5
+    assert bad(_pipe_params(region_begin=32)) == -1      # region not just before the protected tail
+    assert bad(_pipe_params(region_len=64)) == -1        # region is one page
+    assert bad(_pipe_params(desc_stream_stride=7)) == -1
+    assert bad(_pipe_params(budget_bytes=100)) == -3
+
+
+def test_append_and_pipe_validate_before_launch(monkeypatch):
+    monkeypatch.setattr(kvc, "_stream", lambda: ctypes.c_void_p(0))
+    p = kvc.KvParams(batch=1, n_q_heads=2, n_kv_heads=2)
+    p.p.packed_stream_stride = 16 * 512
+    a = _Fake(0x50000)
+
+    def append(n_new, fill, cap, page_offset=0, k=a, params=p):
+        with pytest.raises(kvc.KvcError) as e:
+            kvc.kv_append(params, k, a, n_new, fill, cap, page_offset, a, a)
+        return e.value.status
+
+    assert append(1, 0, 12) == -1          # capacity not a power of two
+    assert append(5, 12, 16) == -1         # past the capacity
+    assert append(0, 0, 16) == -1
+    assert append(1, 0, 16, k=_Fake(0x50008)) == -5
+    assert append(1, 0, 16, page_offset=8) == -5
+    assert append(1, 0, 32) == -1          # pages of 32 tokens do not fit the stream stride
+    cfg = kvc.pipe_config(pages=4, max_events=15, prefix_desc=4, protect=32,
+                          events_offset=4 * 64 * 512, pages_offset=4 * 64 * 512 + 15 * 3632)
+    pp = _pipe_params()
+    _, L = kvc.kv_pipe_layout(pp, cfg)
+    pp.p.packed_stream_stride = L.stream_bytes_min
+    h = ctypes.c_void_p()
+    L_ = kvc.lib()
+    st = L_.kv_pipe_create(ctypes.byref(pp.p), ctypes.byref(cfg), ctypes.c_void_p(0x60000),
+                           ctypes.c_void_p(0x60000), ctypes.c_void_p(0x60000), L.ws_bytes - 16,
+                           None, ctypes.byref(h))
+    assert st == -4 and not h.value
+    pp.p.packed_stream_stride = L.stream_bytes_min - 16
+    st = L_.kv_pipe_create(ctypes.byref(pp.p), ctypes.byref(cfg), ctypes.c_void_p(0x60000),
+                           ctypes.c_void_p(0x60000), ctypes.c_void_p(0x60000), L.ws_bytes,
+                           None, ctypes.byref(h))
+    assert st == -1 and not h.value
+    assert L_.kv_pipe_step(None, None, None, 1, 0, None, None, None, None, None, None, None) == -1
+    assert L_.kv_pipe_destroy(None) == 0

@@ -715,3 +715,80 @@ def test_stream_budget_compress_end_to_end(O):
     ch, _ = O.stream_choose(r["objective"], _table9_bytes(O, S), nseg * budget)
     assert list(r["desc"]["strategy"]) == list(ch)
     assert max(_table9_bytes(O, S)[i] for i in ch) > budget
+
+
+# ---------------------------------------------------------------------------
+# Incremental compression pipeline: the schedule written out from the reading
+
+def test_pipeline_schedule_golden():
+    """Hand-worked schedules (tests/golden/pipeline_schedule.json): firing
+    steps, regions, the switched set of every step (lag, and the switch forced
+    when a page is written again) and the tokens kept at full width."""
+    from oracle import pipeline as OP
+    with open(os.path.join(GOLDEN, "pipeline_schedule.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        got = OP.schedule(c["steps"], period=c["period"], protect=c["protect"], pages=c["pages"],
+                          lag=c["lag"])
+        assert [e["g"] for e in got] == c["g"]
+        assert [e["fired"] for e in got] == c["fired"]
+        assert [e["switched"] for e in got] == c["switched"]
+        assert [list(got[-1]["regions"][i]) for i in range(len(c["regions"]))] == c["regions"]
+        for i, want in c["tokens_at"].items():
+            assert [list(r) for r in OP.state_tokens(got[int(i)])] == want
+
+
+def test_pipeline_schedule_kara_counts():
+    """The Kara configuration (8192 generated tokens, an event every 64, a
+    64-token protected tail, 20 % of 64 = 13 tokens kept per event): 127
+    events, and once every event is switched only the protected tail stays
+    at full width, so a stream holds 16384 + 127 * 13 + 64 = 18099 tokens."""
+    from oracle import pipeline as OP
+    sched = OP.schedule([1] * 8192, period=64, protect=64, pages=4, lag=0)
+    last = sched[-1]
+    assert len(last["regions"]) == 127 and last["switched"] == list(range(127))
+    assert last["regions"][0] == (0, 64) and last["regions"][126] == (8064, 8128)
+    assert OP.state_tokens(last) == [(8128, 8192)]
+    T = (20 * 64 + 50) // 100
+    assert 16384 + 127 * T + sum(b - a for a, b in OP.state_tokens(last)) == 18099
+    # every step sees each appended token exactly once: either in a switched
+    # region or at full width
+    for e in sched[::97]:
+        seen = sum(b - a for a, b in OP.state_tokens(e)) + \
+            sum(e["regions"][k][1] - e["regions"][k][0] for k in e["switched"])
+        assert seen == e["g"]
+
+
+def test_paged_descriptor_decode_pins(O):
+    """A paged descriptor (parts sized for seg_tokens, first n_tok filled)
+    decodes like the dense attention over its first n_tok rows (closed form
+    in numpy), whatever the rows past n_tok hold; at n_tok == seg_tokens it
+    is the keep-all descriptor of the same bytes."""
+    rng = np.random.default_rng(3)
+    cap, n = 16, 11
+    K = rng.standard_normal((cap, 128)).astype(np.float32)
+    V = rng.standard_normal((cap, 128)).astype(np.float32)
+    q = rng.standard_normal((2, 128)).astype(np.float32)
+    bf = lambda a: (np.ascontiguousarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    Kb, Vb, qb = bf(K), bf(V), bf(q)
+    buf = np.full(512 * cap + 16, 0xFF, np.uint8)  # NaN past the filled rows
+    buf[:256 * n] = Kb[:n].view(np.uint8).reshape(-1)
+    buf[256 * cap:256 * cap + 256 * n] = Vb[:n].view(np.uint8).reshape(-1)
+    desc = np.array([(0, n, 128, 0, 0x07, cap)], O.DESC_DTYPE)
+    out, lse = O.decode_stream(qb, buf, desc, np.float32(0.125))
+    up = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    l = up(qb) @ up(Kb[:n]).T * float(np.float32(0.125))
+    m = l.max(axis=1, keepdims=True)
+    p = np.exp(l - m)
+    ref = (p / p.sum(axis=1, keepdims=True)) @ up(Vb[:n])
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(lse, m[:, 0] + np.log(p.sum(axis=1)), rtol=1e-12)
+    full = np.zeros(512 * cap + 16, np.uint8)
+    full[:256 * cap] = Kb.view(np.uint8).reshape(-1)
+    full[256 * cap:512 * cap] = Vb.view(np.uint8).reshape(-1)
+    a = O.decode_stream(qb, full, np.array([(0, cap, 128, 0, 0x07, cap)], O.DESC_DTYPE), np.float32(0.125))
+    b = O.decode_stream(qb, full, np.array([(0, cap, 128, 0, 0x03, cap)], O.DESC_DTYPE), np.float32(0.125))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    s_paged = O.summarize_stream(buf, desc)
+    s_dense = O.summarize_stream(full, np.array([(0, n, 128, 0, 0x03, n)], O.DESC_DTYPE))
+    assert np.array_equal(s_paged, s_dense)

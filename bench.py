@@ -58,6 +58,9 @@ def parse():
                          "segments kept (0 = off)")
     ap.add_argument("--no-kara", action="store_true",
                     help="skip the Kara sliding-window decode measurement beside the headline")
+    ap.add_argument("--pipe-steps", type=int, default=512,
+                    help="Kara generation steps through the compression pipeline, timed blocking "
+                         "and asynchronous beside the headline (0 = off)")
     ap.add_argument("--no-stream-budget", action="store_true",
                     help="skip the per-stream budget measurement beside the headline")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "decode_batched128k_traffic.md"),
@@ -150,6 +153,84 @@ def bench_kara(a, kvc, stream):
             "kv_tokens_per_s": B * L_ctx / t, "stored_tokens": int(n.sum()),
             "achieved_GBs": alg / t / 1e9, "pct_of_peak_hbm": 100.0 * alg / t / 1e9 / PEAK_HBM_GBS,
             "algorithmic_bytes_per_launch": alg}
+
+
+def bench_pipeline(a, kvc, stream):
+    """The last generation steps of the Kara workload through the compression
+    pipeline (kv_pipe_*), as a serving loop runs them: one decode step per
+    token, the host waiting for each step's output (a sampler needs it), an
+    event every 64 tokens.  Run twice from the same state: events compressed
+    inside the step that fires them (blocking), and on the pipeline's own
+    stream, switched in when done (asynchronous).  Reports each run's total
+    time (ending with a drain, so every event is inside it) and the latency
+    of single steps; the two final caches are compared byte for byte, and
+    one event's compression is timed on its own."""
+    from compressed_kv_cache_compress_amd import gen, kara
+    k = gen.KARA
+    dev = torch.device("cuda:0")
+    w = gen.make_kara(seed=a.seed, device=dev)
+    n = a.pipe_steps
+    prot, delta = k["protect"], k["delta"]
+    start = w["gen"] - n - prot
+    scale = float(np.float32(1.0 / math.sqrt(128.0)))
+    runs, pipes = {}, {}
+    for mode, name in ((kvc.PIPE_SYNC, "blocking"), (kvc.PIPE_ASYNC, "async")):
+        print(f"[bench] pipeline {name}: {n} steps from generated token {start}", file=sys.stderr,
+              flush=True)
+        kp = kara.KaraPipeline(w["K"], w["V"], w["Qall"], prompt=w["prompt"], start=start,
+                               window=k["window"], delta=delta, protect=prot,
+                               retention_pct=k["retention_pct"], alpha=k["alpha"],
+                               gamma=k["gamma"], scale=scale, mode=mode, steps=n + prot)
+        kp.step(prot, decode=False)
+        torch.cuda.synchronize()
+        lat = np.zeros(n)
+        t0 = time.perf_counter()
+        for i in range(n):
+            t = time.perf_counter()
+            kp.step(1)
+            stream.synchronize()
+            lat[i] = time.perf_counter() - t
+        kp.pipe.drain()
+        torch.cuda.synchronize()
+        total = time.perf_counter() - t0
+        runs[name] = dict(total_ms=total * 1e3, p50_ms=float(np.percentile(lat, 50) * 1e3),
+                          p99_ms=float(np.percentile(lat, 99) * 1e3), max_ms=float(lat.max() * 1e3),
+                          host_waits=kp.pipe.stats()["host_waits"],
+                          events=kp.pipe.stats()["events_fired"])
+        pipes[name] = kp
+    a_, b_ = pipes["blocking"], pipes["async"]
+    streams = a_.B * a_.Hkv
+    lo = a_.cfg.events_offset
+    hi = lo + a_.cfg.max_events * a_.layout.event_bytes
+    same = bool(torch.equal(a_.desc, b_.desc)) and bool(torch.equal(
+        a_.packed.view(streams, -1)[:, lo:hi], b_.packed.view(streams, -1)[:, lo:hi]))
+    # one event's compression on its own (same window shape, scratch output)
+    pe = kvc.KvParams(batch=a_.B, n_q_heads=a_.Hq, n_kv_heads=a_.Hkv, n_ctx=k["window"],
+                      region_begin=k["window"] - prot - delta, region_len=delta,
+                      seg_tokens=delta, n_win=k["window"], strategies=[(a_.T, 128)],
+                      budget_bytes=4 * delta * 128, t2c_alpha=k["alpha"], t2c_gamma=k["gamma"],
+                      scale=scale, kv_stream_stride=a_.L * 128, qw_head_stride=a_.L * 128)
+    _, Le = kvc.kv_layout_query(pe)
+    sp = torch.empty(Le.packed_bytes_max, dtype=torch.uint8, device=dev)
+    sd = torch.zeros(streams * 16, dtype=torch.uint8, device=dev)
+    sw = torch.empty(Le.compress_ws_bytes, dtype=torch.uint8, device=dev)
+    w0 = a_.L - k["window"]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(6)]
+    for e in ev:
+        e[0].record(stream)
+        kvc.kv_compress(pe, w["K"][:, :, w0:], w["V"][:, :, w0:], w["Qall"][:, :, w0:], None,
+                        sp, sd, None, None, None, sw)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    t_event = float(np.mean([e[0].elapsed_time(e[1]) for e in ev[1:]]))
+    for kp in pipes.values():
+        kp.close()
+    return {"workload": f"kara generation through the pipeline: B 64, GQA 32/8, the last {n} of "
+                        "8192 generated tokens, one decode step each with the host waiting for "
+                        "its output, an event every 64 tokens, 64-token protected tail, 4 pages",
+            "steps": n, "event_ms": t_event, "blocking": runs["blocking"],
+            "async": runs["async"], "identical_final_cache": same}
 
 
 def bench_stream_budget(a, kvc, K, V, Qw, q, B, Hq, Hkv, N, S, W, strategies, budget, scale,
@@ -387,6 +468,9 @@ def main():
         del w, K, V, Qw, packed, cws, dws
         torch.cuda.empty_cache()
         res["kara"] = bench_kara(a, kvc, stream)
+    if a.pipe_steps > 0:
+        torch.cuda.empty_cache()
+        res["pipeline"] = bench_pipeline(a, kvc, stream)
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wc, S, strategies, budget, scale)

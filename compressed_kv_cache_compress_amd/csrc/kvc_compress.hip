@@ -54,6 +54,7 @@ struct ScoreArgs {
   const uint16_t* Qw;
   uint64_t kv_stride, qw_stride;
   int hkv, hq, G, W, nq, nblk, region_begin, region_len;
+  int qper;  // window queries per wave of score_partials (all of them unless the grid is small)
   float scale;
 };
 
@@ -114,7 +115,10 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ qs, int
   }
 }
 
-// grid (nblk, streams), 64 threads: lane = token of the 64-token block.
+// grid (nblk, streams, ceil(nq / qper)), 64 threads: lane = token of the
+// 64-token block; wave z handles window queries z * qper .. (z + 1) * qper - 1
+// (each (query, block) partial is computed by exactly one wave, so the split
+// only fills the chip when a domain has few blocks).
 __global__ __launch_bounds__(64) void k_score_partials(ScoreArgs a, const float* __restrict__ qf,
                                                        float* __restrict__ part_m,
                                                        float* __restrict__ part_z) {
@@ -123,9 +127,10 @@ __global__ __launch_bounds__(64) void k_score_partials(ScoreArgs a, const float*
   float kf[D];
   load_row_f32(a.K + (uint64_t)s * a.kv_stride + (uint64_t)t * D, kf);
   const float* qs = qf + (uint64_t)s * a.nq * D;
-  int q0 = 0;
-  for (; q0 + QB <= a.nq; q0 += QB) block_partials<QB>(qs, q0, kf, a, s, blk, lane, part_m, part_z);
-  for (; q0 < a.nq; ++q0) block_partials<1>(qs, q0, kf, a, s, blk, lane, part_m, part_z);
+  int q0 = blockIdx.z * a.qper;
+  const int q1 = min(a.nq, q0 + a.qper);
+  for (; q0 + QB <= q1; q0 += QB) block_partials<QB>(qs, q0, kf, a, s, blk, lane, part_m, part_z);
+  for (; q0 < q1; ++q0) block_partials<1>(qs, q0, kf, a, s, blk, lane, part_m, part_z);
 }
 
 // grid (nq, streams), 64 threads.  m = max of the block maxima; Z = pairwise
@@ -199,6 +204,59 @@ __global__ __launch_bounds__(64) void k_token_scores(ScoreArgs a, const float* _
   for (; q0 + QB <= a.nq; q0 += QB) add_scores<QB>(qs, q0, kf, a.scale, nm, ni, sc);
   for (; q0 < a.nq; ++q0) add_scores<1>(qs, q0, kf, a.scale, nm, ni, sc);
   if (valid) {
+    scores[(uint64_t)s * a.region_len + tr] = sc;
+    if (scores_out) scores_out[(uint64_t)s * a.region_len + tr] = sc;
+  }
+}
+
+// The same scores when the region has few tokens (one wave per 64 region
+// tokens would leave most of the chip idle): TW waves share the 64 tokens,
+// wave w computing the terms fl(exp(l - m) / Z) of queries q0 + QB w ..
+// q0 + QB w + QB - 1 of each round of TW * QB queries into LDS, and wave 0
+// adding the round's terms to the score in query order.  Terms and their
+// order are those of k_token_scores, so the scores are identical.  grid
+// (ceil(region_len/64), streams), 64 * TW threads.
+template <int TW>
+__global__ __launch_bounds__(64 * TW) void k_token_scores_shared(
+    ScoreArgs a, const float* __restrict__ qf, const float* __restrict__ norm_m,
+    const float* __restrict__ norm_iz, float* __restrict__ scores, float* __restrict__ scores_out) {
+  constexpr int R = TW * QB;  // queries per round
+  __shared__ float term[2][R][64];
+  const int s = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int tr = blockIdx.x * 64 + lane;
+  const bool valid = tr < a.region_len;
+  const int t = a.region_begin + (valid ? tr : 0);
+  float kf[D];
+  load_row_f32(a.K + (uint64_t)s * a.kv_stride + (uint64_t)t * D, kf);
+  const float* qs = qf + (uint64_t)s * a.nq * D;
+  const float* nm = norm_m + (uint64_t)s * a.nq;
+  const float* ni = norm_iz + (uint64_t)s * a.nq;
+  float sc = 0.0f;
+  int buf = 0;
+  // a round's buffer is rewritten two rounds later, after every wave has
+  // passed the next barrier, which wave 0 reaches only after adding it
+  for (int q0 = 0; q0 < a.nq; q0 += R, buf ^= 1) {
+    const int qw = q0 + wv * QB;
+    if (qw + QB <= a.nq) {
+      float l[QB];
+      logits<QB>(qs + (uint64_t)qw * D, kf, a.scale, l);
+#pragma unroll
+      for (int j = 0; j < QB; ++j)
+        term[buf][wv * QB + j][lane] = spec_exp2((l[j] - nm[qw + j]) * KVC_LOG2E) * ni[qw + j];
+    } else {
+      for (int j = 0; j < QB && qw + j < a.nq; ++j) {
+        float l1;
+        logits<1>(qs + (uint64_t)(qw + j) * D, kf, a.scale, &l1);
+        term[buf][wv * QB + j][lane] = spec_exp2((l1 - nm[qw + j]) * KVC_LOG2E) * ni[qw + j];
+      }
+    }
+    __syncthreads();
+    if (wv == 0) {
+      const int n = min(R, a.nq - q0);
+      for (int j = 0; j < n; ++j) sc = sc + term[buf][j][lane];
+    }
+  }
+  if (wv == 0 && valid) {
     scores[(uint64_t)s * a.region_len + tr] = sc;
     if (scores_out) scores_out[(uint64_t)s * a.region_len + tr] = sc;
   }
@@ -702,14 +760,29 @@ hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
     sa.region_begin = p.region_begin;
     sa.region_len = p.region_len;
     sa.scale = p.scale;
+    // at least SCORE_WAVES waves per scoring kernel when the shape allows
+    constexpr int64_t SCORE_WAVES = 16384;
+    const int64_t pw = (int64_t)p.nblk * p.streams;
+    int qsplit = (int)((SCORE_WAVES + pw - 1) / pw);
+    const int max_split = (p.nq + 4 * QB - 1) / (4 * QB);  // keep >= 4 rounds of QB per wave
+    if (qsplit > max_split) qsplit = max_split;
+    if (qsplit < 1) qsplit = 1;
+    sa.qper = (((p.nq + qsplit - 1) / qsplit + QB - 1) / QB) * QB;
+    qsplit = (p.nq + sa.qper - 1) / sa.qper;
     hipLaunchKernelGGL(k_q_convert, dim3(p.nq, p.streams), dim3(64), 0, st, sa, p.qf);
-    hipLaunchKernelGGL(k_score_partials, dim3(p.nblk, p.streams), dim3(64), 0, st, sa,
+    hipLaunchKernelGGL(k_score_partials, dim3(p.nblk, p.streams, qsplit), dim3(64), 0, st, sa,
                        (const float*)p.qf, p.part_m, p.part_z);
     hipLaunchKernelGGL(k_score_normalise, dim3(p.nq, p.streams), dim3(64), 0, st, sa,
                        (const float*)p.part_m, (const float*)p.part_z, p.norm_m, p.norm_iz);
-    hipLaunchKernelGGL(k_token_scores, dim3((p.region_len + 63) / 64, p.streams), dim3(64), 0, st,
-                       sa, (const float*)p.qf, (const float*)p.norm_m, (const float*)p.norm_iz,
-                       p.scores, p.scores_out);
+    const dim3 tgrid((p.region_len + 63) / 64, p.streams);
+    const int64_t tw = (int64_t)tgrid.x * tgrid.y;
+    if (tw * 4 <= SCORE_WAVES && p.nq >= 8 * QB)
+      hipLaunchKernelGGL(k_token_scores_shared<8>, tgrid, dim3(512), 0, st, sa,
+                         (const float*)p.qf, (const float*)p.norm_m, (const float*)p.norm_iz,
+                         p.scores, p.scores_out);
+    else
+      hipLaunchKernelGGL(k_token_scores, tgrid, dim3(64), 0, st, sa, (const float*)p.qf,
+                         (const float*)p.norm_m, (const float*)p.norm_iz, p.scores, p.scores_out);
   }
   if (p.nc > 0) {
     SelectArgs se;

@@ -107,3 +107,180 @@ def oracle_decode_all(q, buf, descs, n_desc=None):
         outs.append(o)
         lses.append(l)
     return np.concatenate(outs), np.concatenate(lses)
+
+
+# ---------------------------------------------------------------------------
+# Incremental compression pipeline: the oracle's view of a pipeline state
+
+def _rows_u8(a):
+    return np.ascontiguousarray(a).view(np.uint8).reshape(-1)
+
+
+class PipelineOracle:
+    """The oracle's side of a Kara pipeline run (`kara.KaraPipeline` kp,
+    workload w, settings c with window, delta, protect, alpha, gamma):
+
+      * the prefix: the prompt at full width and the events of the generated
+        tokens before the pipeline's first token, each compressed by the
+        oracle from its own window;
+      * the pipeline's events, compressed by the oracle on demand (cached);
+      * state_decode: the fp64 decode of a step's query over the prefix, the
+        switched events' segments and every other appended token at full
+        width.
+    """
+
+    def __init__(self, w, kp, c):
+        from oracle import oracle as _O
+        self.O = _O
+        self.w, self.kp, self.c = w, kp, c
+        self.Kh, self.Vh, self.Qh = gen.u16(w["K"]), gen.u16(w["V"]), gen.u16(w["Qall"])
+        self.G = kp.Hq // kp.Hkv
+        sched, self.T = gen.kara_schedule(kp.prompt, kp.L - kp.prompt, window=c["window"],
+                                          delta=c["delta"], protect=c["protect"], seg=c["delta"],
+                                          retention_pct=c["retention_pct"])
+        self.pre = [e for e in sched if e[0] - c["protect"] <= kp.prompt + kp.g0]
+        assert len(self.pre) == kp.n_prefix_events and self.T == kp.T
+        self.cache, self.prefix_cache, self.prefix_events = {}, {}, {}
+
+    def _event(self, s, Le):
+        """Oracle compression of the event at sequence length Le for stream s."""
+        c = self.c
+        b, h = divmod(s, self.kp.Hkv)
+        G = self.G
+        w0 = Le - c["window"]
+        return self.O.compress_stream(
+            self.Kh[b, h, w0:Le], self.Vh[b, h, w0:Le], self.Qh[b, h * G:(h + 1) * G, w0:Le],
+            S=c["delta"], strategies=[(self.T, 128)], budget_bytes=4 * c["delta"] * 128,
+            scale=SCALE, region_begin=c["window"] - c["protect"] - c["delta"],
+            region_len=c["delta"], t2c_alpha=c["alpha"], t2c_gamma=c["gamma"])
+
+    def get(self, e, s, region):
+        """Pipeline event e (region = its (start, end) in pipeline tokens)."""
+        if (e, s) not in self.cache:
+            Le = self.kp.prompt + self.kp.g0 + region[1] + self.c["protect"]
+            self.cache[(e, s)] = self._event(s, Le)
+        return self.cache[(e, s)]
+
+    def prefix(self, s):
+        """(parts, descs, bytes) of the prompt at full width and the prefix events."""
+        if s not in self.prefix_cache:
+            b, h = divmod(s, self.kp.Hkv)
+            P = self.kp.prompt
+            parts = [_rows_u8(self.Kh[b, h, :P]), _rows_u8(self.Vh[b, h, :P])]
+            descs = [(0, P, 128, 0, 0x03, P)]
+            off = 512 * P
+            for (Le, w0, rb) in self.pre:
+                r = self._event(s, Le)
+                self.prefix_events[(s, Le)] = r
+                off = self._append(parts, descs, off, r)
+            self.prefix_cache[s] = (parts, descs, off)
+        return self.prefix_cache[s]
+
+    @staticmethod
+    def _append(parts, descs, off, r):
+        pk = np.concatenate([r["packed"], np.zeros((-r["used"]) % 16, np.uint8)])
+        d = r["desc"][0]
+        parts.append(pk)
+        descs.append((off + int(d["offset"]), int(d["n_tok"]), int(d["n_ch"]), int(d["strategy"]),
+                      int(d["flags"]), int(d["seg_tokens"])))
+        return off + len(pk)
+
+    def state_decode(self, s, entry, switched):
+        from oracle import pipeline as OP
+        kp = self.kp
+        b, h = divmod(s, kp.Hkv)
+        G = self.G
+        p0, d0, off = self.prefix(s)
+        parts, descs = list(p0), list(d0)
+        for e in switched:
+            off = self._append(parts, descs, off, self.get(e, s, entry["regions"][e]))
+        base = kp.prompt + kp.g0
+        for a, z in OP.state_tokens(dict(entry, switched=switched)):
+            n = z - a
+            parts += [_rows_u8(self.Kh[b, h, base + a:base + z]), _rows_u8(self.Vh[b, h, base + a:base + z])]
+            descs.append((off, n, 128, 0, 0x03, n))
+            off += 512 * n
+        L = base + entry["g"]
+        q = self.Qh[b, h * G:(h + 1) * G, L - 1]
+        return self.O.decode_stream(q, np.concatenate(parts), np.array(descs, DESC_DTYPE), SCALE)
+
+
+def run_pipeline(kp, n_steps, prefill=0, keep=None, sync=False):
+    """Runs the steps, keeping (for the steps in `keep`, default all) the
+    step's output and a copy of the descriptor list that step's decode read,
+    both enqueued on the decode stream.  sync: the host waits for every step,
+    as a serving loop does."""
+    outs, lists = {}, {}
+    if prefill:
+        kp.step(prefill, decode=False)
+    stream = torch.cuda.current_stream()
+    for i in range(n_steps):
+        out, lse = kp.step(1)
+        if keep is None or i in keep:
+            outs[i] = (out.clone(), lse.clone())
+            lists[i] = kp.desc.clone()
+        if sync:
+            stream.synchronize()
+    return outs, lists
+
+
+def switched_from_list(kp, lst, streams):
+    """Events whose slot holds a segment (the same for every stream), and the
+    list as [streams][max_desc] descriptors."""
+    d = lst.cpu().numpy().view(DESC_DTYPE).reshape(streams, kp.max_desc)
+    first = kp.cfg.prefix_desc
+    n = d[:, first:first + kp.cfg.max_events]["n_tok"] > 0
+    assert np.all(n == n[0]), "streams disagree on the switched events"
+    return [int(e) for e in np.nonzero(n[0])[0]], d
+
+
+def check_pipeline_pages(kp, d, entry, switched, streams):
+    """The list's page slots hold exactly the tokens the state keeps at full
+    width, as paged descriptors of whole pages (the last one partly filled)."""
+    from oracle import pipeline as OP
+    per_page = {}
+    for a, z in OP.state_tokens(dict(entry, switched=switched)):
+        t = a
+        while t < z:
+            pg = t // kp.delta
+            e = min(z, (pg + 1) * kp.delta)
+            assert pg not in per_page and t == pg * kp.delta
+            per_page[pg] = e - t
+            t = e
+    exp = {pg % kp.cfg.pages: n for pg, n in per_page.items()}
+    base = kp.cfg.prefix_desc + kp.cfg.max_events
+    pages = d[:, base:base + kp.cfg.pages]
+    for s in range(streams):
+        got = {}
+        for j in range(kp.cfg.pages):
+            x = pages[s, j]
+            if x["n_tok"] > 0:
+                assert int(x["flags"]) == 0x07 and int(x["seg_tokens"]) == kp.delta
+                assert int(x["offset"]) == s * kp.stream_bytes + kp.cfg.pages_offset + \
+                    j * kp.layout.page_bytes
+                got[j] = int(x["n_tok"])
+        assert got == exp, (s, got, exp)
+
+
+def check_pipeline_finals(kp, oe, entries, streams, sample=None):
+    """Every switched event's final segment (and every prefix event) is bit
+    exact against the oracle's compression of that event."""
+    packed = kp.packed.view(streams, -1)
+    d = kp.desc.cpu().numpy().view(DESC_DTYPE).reshape(streams, kp.max_desc)
+    last = entries[-1]
+    for s in (range(streams) if sample is None else sample):
+        row = packed[s].cpu().numpy()
+        checks = [(kp.cfg.prefix_desc + e, oe.get(e, s, last["regions"][e]),
+                   kp.cfg.events_offset + e * kp.layout.event_bytes) for e in range(len(last["regions"]))]
+        oe.prefix(s)
+        n_prompt = kp.cfg.prefix_desc - kp.n_prefix_events
+        ev0 = kp.cfg.events_offset - kp.n_prefix_events * kp.layout.event_bytes
+        for i, (Le, w0, rb) in enumerate(oe.pre):
+            checks.append((n_prompt + i, oe.prefix_events[(s, Le)], ev0 + i * kp.layout.event_bytes))
+        for slot, r, rel in checks:
+            gd = d[s, slot]
+            rd = r["desc"][0]
+            assert int(gd["offset"]) == s * kp.stream_bytes + rel, (s, slot)
+            for f in ("n_tok", "n_ch", "strategy", "flags", "seg_tokens"):
+                assert int(gd[f]) == int(rd[f]), (s, slot, f)
+            assert np.array_equal(row[rel:rel + r["used"]], r["packed"]), (s, slot)

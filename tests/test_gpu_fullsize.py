@@ -144,3 +144,54 @@ def test_fullsize_kara():
         ref, rlse = O.decode_stream(q, ref_buf, ref_desc, SCALE)
         check_attention(out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G], ref, rlse,
                         f"kara stream {s}")
+
+
+def test_fullsize_kara_pipeline():
+    """The Kara workload at full size through the compression pipeline, as
+    bench.py times it: B 64, the last 512 of 8192 generated tokens, the host
+    waiting for each step, events compressed on the pipeline's stream and
+    switched in when done.  Sampled steps: the switched set is admissible and
+    the page slots match it on every stream; decode of streams 0 and 301
+    against the oracle over exactly that state; every prefix and pipeline
+    event of those streams bit-exact against the oracle."""
+    from compressed_kv_cache_compress_amd import PIPE_ASYNC
+    from oracle import pipeline as OP
+    from helpers import (PipelineOracle, check_pipeline_finals, check_pipeline_pages,
+                         run_pipeline, switched_from_list)
+    k = gen.KARA
+    c = dict(window=k["window"], delta=k["delta"], protect=k["protect"], alpha=k["alpha"],
+             gamma=k["gamma"], retention_pct=k["retention_pct"])
+    say("[fullsize] kara pipeline: generating")
+    w = gen.make_kara(device="cuda")
+    n = 512
+    start = w["gen"] - n - c["protect"]
+    kp = kara.KaraPipeline(w["K"], w["V"], w["Qall"], prompt=w["prompt"], start=start,
+                           window=c["window"], delta=c["delta"], protect=c["protect"],
+                           retention_pct=c["retention_pct"], alpha=c["alpha"], gamma=c["gamma"],
+                           scale=float(SCALE), mode=PIPE_ASYNC, steps=n + c["protect"])
+    streams = kp.B * kp.Hkv
+    fired = [i for i in range(n) if (c["protect"] + i + 1) % c["delta"] == 0]
+    keep = set(range(0, n, 61)) | {n - 1} | {i + 1 for i in fired if i + 1 < n} | set(fired)
+    say(f"[fullsize] kara pipeline: {n} steps, {len(keep)} sampled")
+    outs, lists = run_pipeline(kp, n, prefill=c["protect"], keep=keep, sync=True)
+    kp.pipe.drain()
+    torch.cuda.synchronize()
+    st = kp.pipe.stats()
+    assert st["events_fired"] == st["events_switched"] == n // c["delta"]
+    forced = OP.schedule([c["protect"]] + [1] * n, period=c["delta"], protect=c["protect"],
+                         pages=kp.cfg.pages, lag=10 ** 9)[1:]
+    oe = PipelineOracle(w, kp, c)
+    G = kp.Hq // kp.Hkv
+    for i in sorted(keep):
+        entry = forced[i]
+        sw, d = switched_from_list(kp, lists[i], streams)
+        assert sw == list(entry["regions"])[:len(sw)] and set(entry["switched"]) <= set(sw), (i, sw)
+        check_pipeline_pages(kp, d, entry, sw, streams)
+        out, lse = outs[i]
+        for s in (0, 301):
+            b, h = divmod(s, kp.Hkv)
+            ro, rl = oe.state_decode(s, entry, sw)
+            check_attention(out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G], ro, rl,
+                            f"kara pipeline step {i} s={s}")
+    check_pipeline_finals(kp, oe, forced, streams, sample=(0, 301))
+    kp.close()

@@ -19,8 +19,9 @@ import torch
 
 from compressed_kv_cache_compress_amd import (DESC_DTYPE, PIPE_ASYNC, PIPE_LAG, PIPE_SYNC, KvParams,
                                               gen, kara, kv_append, runtime)
-from helpers import (SCALE, assemble_cache, check_attention, desc_to_dev, oracle_compress_all,
-                     say, to_dev_u8)
+from helpers import (SCALE, PipelineOracle, assemble_cache, check_attention, check_pipeline_finals,
+                     check_pipeline_pages, desc_to_dev, oracle_compress_all, run_pipeline, say,
+                     switched_from_list, to_dev_u8)
 from oracle import oracle as O
 from oracle import pipeline as OP
 
@@ -147,160 +148,26 @@ def _make(mode, lag=0, pages=None, start=0, steps=None, seed=0, **over):
     return w, kp, c
 
 
-class _OracleEvents:
-    """The oracle's compression of each event of the pipeline, per stream
-    (cached): the region is a page of `delta` generated tokens, scored by
-    the window ending `protect` tokens after it."""
-
-    def __init__(self, w, kp, c):
-        self.w, self.kp, self.c = w, kp, c
-        self.Kh, self.Vh, self.Qh = gen.u16(w["K"]), gen.u16(w["V"]), gen.u16(w["Qall"])
-        self.cache = {}
-
-    def get(self, e, s, region):
-        key = (e, s)
-        if key not in self.cache:
-            c, kp = self.c, self.kp
-            b, h = divmod(s, kp.Hkv)
-            G = kp.Hq // kp.Hkv
-            Le = kp.prompt + kp.g0 + region[1] + c["protect"]  # sequence length at the event
-            w0 = Le - c["window"]
-            self.cache[key] = O.compress_stream(
-                self.Kh[b, h, w0:Le], self.Vh[b, h, w0:Le], self.Qh[b, h * G:(h + 1) * G, w0:Le],
-                S=c["delta"], strategies=[(kp.T, D)], budget_bytes=4 * c["delta"] * D,
-                scale=SCALE, region_begin=c["window"] - c["protect"] - c["delta"],
-                region_len=c["delta"], t2c_alpha=c["alpha"], t2c_gamma=c["gamma"])
-        return self.cache[key]
-
-    def state_decode(self, s, entry, switched):
-        """fp64 oracle decode of the last appended token's query over the
-        prompt, the switched events' final segments and every other
-        appended token at full width."""
-        kp = self.kp
-        b, h = divmod(s, kp.Hkv)
-        G = kp.Hq // kp.Hkv
-        parts, descs, off = [], [], 0
-
-        def dense(p0, p1):
-            nonlocal off
-            n = p1 - p0
-            parts.append(_rows(self.Kh[b, h, p0:p1]))
-            parts.append(_rows(self.Vh[b, h, p0:p1]))
-            descs.append((off, n, 128, 0, 0x03, n))
-            off += 512 * n
-
-        dense(0, kp.prompt + kp.g0)  # prompt (and generated tokens before the pipeline, if any)
-        for e in switched:
-            r = self.get(e, s, entry["regions"][e])
-            d = r["desc"][0]
-            pk = r["packed"]
-            parts.append(np.concatenate([pk, np.zeros((-len(pk)) % 16, np.uint8)]))
-            descs.append((off + int(d["offset"]), int(d["n_tok"]), int(d["n_ch"]),
-                          int(d["strategy"]), int(d["flags"]), int(d["seg_tokens"])))
-            off += len(parts[-1])
-        st = dict(entry, switched=switched)
-        for a, z in OP.state_tokens(st):
-            dense(kp.prompt + kp.g0 + a, kp.prompt + kp.g0 + z)
-        buf = np.concatenate(parts) if parts else np.zeros(16, np.uint8)
-        dd = np.array(descs, DESC_DTYPE)
-        L = kp.prompt + kp.g0 + entry["g"]
-        q = self.Qh[b, h * G:(h + 1) * G, L - 1]
-        return O.decode_stream(q, buf, dd, SCALE)
-
-
-def _run_pipeline(kp, n_steps, prefill=0):
-    """Runs the steps, keeping each step's output and a copy of the list
-    that step's decode read (both enqueued on the decode stream)."""
-    outs, lists = [], []
-    if prefill:
-        kp.step(prefill, decode=False)
-    for i in range(n_steps):
-        out, lse = kp.step(1)
-        outs.append((out.clone(), lse.clone()))
-        lists.append(kp.desc.clone())
-    return outs, lists
-
-
-def _switched_from_list(kp, lst, streams):
-    """Events whose slot holds a segment, per stream (must agree)."""
-    per = kp.max_desc
-    d = lst.cpu().numpy().view(DESC_DTYPE).reshape(streams, per)
-    first = kp.cfg.prefix_desc
-    sw = [tuple(e for e in range(kp.cfg.max_events) if d[s, first + e]["n_tok"] > 0)
-          for s in range(streams)]
-    assert all(x == sw[0] for x in sw), sw
-    return list(sw[0]), d
-
-
-def _check_pages(kp, d, entry, switched, streams):
-    """The list's page slots hold exactly the tokens the state keeps at full
-    width, as paged descriptors."""
-    st = dict(entry, switched=switched)
-    want = OP.state_tokens(st)
-    per_page = {}
-    for a, z in want:
-        t = a
-        while t < z:
-            pg = t // kp.delta
-            e = min(z, (pg + 1) * kp.delta)
-            per_page.setdefault(pg, []).append((t, e))
-            t = e
-    base = kp.cfg.prefix_desc + kp.cfg.max_events
-    for s in range(streams):
-        got = {}
-        for j in range(kp.cfg.pages):
-            x = d[s, base + j]
-            if x["n_tok"] > 0:
-                assert int(x["flags"]) == 0x07 and int(x["seg_tokens"]) == kp.delta
-                rel = int(x["offset"]) - s * kp.stream_bytes - kp.cfg.pages_offset
-                assert rel == j * kp.layout.page_bytes
-                got[j] = int(x["n_tok"])
-        exp = {}
-        for pg, rs in per_page.items():
-            assert len(rs) == 1 and rs[0][0] == pg * kp.delta
-            exp[pg % kp.cfg.pages] = rs[0][1] - rs[0][0]
-        assert got == exp, (s, got, exp)
-
-
-def _check_finals(kp, oe, entries, streams):
-    """Every switched event's final segment is bit-exact against the
-    oracle's compression of that event."""
-    packed = kp.packed.cpu().numpy()
-    d = kp.desc.cpu().numpy().view(DESC_DTYPE).reshape(streams, kp.max_desc)
-    last = entries[-1]
-    for e in range(len(last["regions"])):
-        for s in range(streams):
-            r = oe.get(e, s, last["regions"][e])
-            gd = d[s, kp.cfg.prefix_desc + e]
-            rd = r["desc"][0]
-            assert int(gd["offset"]) == s * kp.stream_bytes + kp.cfg.events_offset + \
-                e * kp.layout.event_bytes
-            for f in ("n_tok", "n_ch", "strategy", "flags", "seg_tokens"):
-                assert int(gd[f]) == int(rd[f]), (e, s, f)
-            o = int(gd["offset"])
-            assert np.array_equal(packed[o:o + r["used"]], r["packed"]), (e, s)
-
-
 @pytest.mark.parametrize("mode,lag", [(PIPE_SYNC, 0), (PIPE_LAG, 0), (PIPE_LAG, 1), (PIPE_LAG, 57)])
 def test_pipeline_deterministic_modes(mode, lag):
     w, kp, c = _make(mode, lag=lag, pages=4)
     streams = kp.B * kp.Hkv
     n = c["gen"]
     say(f"[pipeline] mode={mode} lag={lag} steps={n} streams={streams}")
-    outs, lists = _run_pipeline(kp, n)
+    outs, lists = run_pipeline(kp, n)
     kp.pipe.drain()
     torch.cuda.synchronize()
     st = kp.pipe.stats()
     entries = OP.schedule([1] * n, period=c["delta"], protect=c["protect"], pages=4, lag=lag)
     assert st["events_fired"] == len(entries[-1]["regions"]) == n // c["delta"] - 1
     assert st["events_switched"] == st["events_fired"] and st["host_waits"] == 0
-    oe = _OracleEvents(w, kp, c)
+    oe = PipelineOracle(w, kp, c)
     check_all = set(range(0, n, 37)) | {n - 1} | \
         {i for i, e in enumerate(entries) if e["fired"] is not None}
     for i, entry in enumerate(entries):
-        sw, d = _switched_from_list(kp, lists[i], streams)
+        sw, d = switched_from_list(kp, lists[i], streams)
         assert sw == entry["switched"], (i, sw, entry["switched"])
-        _check_pages(kp, d, entry, sw, streams)
+        check_pipeline_pages(kp, d, entry, sw, streams)
         ss = range(streams) if i in check_all else (0, streams - 1)
         out, lse = outs[i]
         G = kp.Hq // kp.Hkv
@@ -309,7 +176,7 @@ def test_pipeline_deterministic_modes(mode, lag):
             ro, rl = oe.state_decode(s, entry, sw)
             check_attention(out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G], ro, rl,
                             f"step {i} s={s}")
-    _check_finals(kp, oe, entries, streams)
+    check_pipeline_finals(kp, oe, entries, streams)
     kp.close()
 
 
@@ -322,20 +189,20 @@ def test_pipeline_async_states_are_admissible():
     streams = kp.B * kp.Hkv
     n = c["gen"]
     say(f"[pipeline] async steps={n} streams={streams}")
-    outs, lists = _run_pipeline(kp, n)
+    outs, lists = run_pipeline(kp, n)
     kp.pipe.drain()
     torch.cuda.synchronize()
     st = kp.pipe.stats()
     say(f"  stats {st}")
     forced = OP.schedule([1] * n, period=c["delta"], protect=c["protect"], pages=3, lag=10 ** 9)
-    oe = _OracleEvents(w, kp, c)
+    oe = PipelineOracle(w, kp, c)
     G = kp.Hq // kp.Hkv
     for i, entry in enumerate(forced):
-        sw, d = _switched_from_list(kp, lists[i], streams)
+        sw, d = switched_from_list(kp, lists[i], streams)
         fired = [e for e in entry["regions"]]
         assert sw == fired[:len(sw)], (i, sw)
         assert set(entry["switched"]) <= set(sw), (i, sw, entry["switched"])
-        _check_pages(kp, d, entry, sw, streams)
+        check_pipeline_pages(kp, d, entry, sw, streams)
         if i % 29 == 0 or i == n - 1:
             out, lse = outs[i]
             for s in (0, streams - 1):
@@ -344,7 +211,7 @@ def test_pipeline_async_states_are_admissible():
                 check_attention(out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G], ro, rl,
                                 f"async step {i} s={s}")
     assert st["events_switched"] == st["events_fired"] == n // c["delta"] - 1
-    _check_finals(kp, oe, forced, streams)
+    check_pipeline_finals(kp, oe, forced, streams)
     kp.close()
 
 
@@ -358,64 +225,27 @@ def test_pipeline_resume_with_prefill_and_prefix_events():
     streams = kp.B * kp.Hkv
     n = c["gen"] - start
     say(f"[pipeline] resume prefix_events={kp.n_prefix_events} steps={n}")
-    outs, lists = _run_pipeline(kp, n, prefill=c["protect"])
+    outs, lists = run_pipeline(kp, n, prefill=c["protect"])
     kp.pipe.drain()
     torch.cuda.synchronize()
     entries = OP.schedule([c["protect"]] + [1] * n, period=c["delta"], protect=c["protect"],
                           pages=4, lag=3)[1:]
-    oe = _OracleEvents(w, kp, c)
+    oe = PipelineOracle(w, kp, c)
     G = kp.Hq // kp.Hkv
     # the prefix: prompt dense + the events of generated tokens [0, start - 32)
     assert kp.n_prefix_events == (start - 32) // c["delta"]
     for i, entry in enumerate(entries):
-        sw, d = _switched_from_list(kp, lists[i], streams)
+        sw, d = switched_from_list(kp, lists[i], streams)
         assert sw == entry["switched"], (i, sw, entry["switched"])
-        _check_pages(kp, d, entry, sw, streams)
+        check_pipeline_pages(kp, d, entry, sw, streams)
     # decode at sampled steps, against an oracle state that includes the prefix events
-    Kh, Vh, Qh = oe.Kh, oe.Vh, oe.Qh
-    sched, T = gen.kara_schedule(c["prompt"], c["gen"], window=c["window"], delta=c["delta"],
-                                 protect=c["protect"], seg=c["delta"],
-                                 retention_pct=c["retention_pct"])
-    pre = [e for e in sched if e[0] - c["protect"] <= c["prompt"] + kp.g0]
-    assert len(pre) == kp.n_prefix_events
     for i in (0, 40, n - 1):
         entry = entries[i]
-        for s in (0, streams - 1):
-            b, h = divmod(s, kp.Hkv)
-            parts, descs, off = [], [], 0
-            parts += [_rows(Kh[b, h, :c["prompt"]]), _rows(Vh[b, h, :c["prompt"]])]
-            descs.append((0, c["prompt"], 128, 0, 3, c["prompt"]))
-            off = 512 * c["prompt"]
-            for (Le, w0, rb) in pre:
-                r = O.compress_stream(Kh[b, h, w0:Le], Vh[b, h, w0:Le],
-                                      Qh[b, h * G:(h + 1) * G, w0:Le], S=c["delta"],
-                                      strategies=[(T, D)], budget_bytes=4 * c["delta"] * D,
-                                      scale=SCALE, region_begin=rb, region_len=c["delta"],
-                                      t2c_alpha=c["alpha"], t2c_gamma=c["gamma"])
-                pk = np.concatenate([r["packed"], np.zeros((-r["used"]) % 16, np.uint8)])
-                dd = r["desc"][0]
-                parts.append(pk)
-                descs.append((off + int(dd["offset"]), int(dd["n_tok"]), int(dd["n_ch"]),
-                              int(dd["strategy"]), int(dd["flags"]), int(dd["seg_tokens"])))
-                off += len(pk)
-            for e in entry["switched"]:
-                r = oe.get(e, s, entry["regions"][e])
-                pk = np.concatenate([r["packed"], np.zeros((-r["used"]) % 16, np.uint8)])
-                dd = r["desc"][0]
-                parts.append(pk)
-                descs.append((off + int(dd["offset"]), int(dd["n_tok"]), int(dd["n_ch"]),
-                              int(dd["strategy"]), int(dd["flags"]), int(dd["seg_tokens"])))
-                off += len(pk)
-            for a, z in OP.state_tokens(entry):
-                p0, p1 = c["prompt"] + kp.g0 + a, c["prompt"] + kp.g0 + z
-                parts += [_rows(Kh[b, h, p0:p1]), _rows(Vh[b, h, p0:p1])]
-                descs.append((off, p1 - p0, 128, 0, 3, p1 - p0))
-                off += 512 * (p1 - p0)
-            L = c["prompt"] + kp.g0 + entry["g"]
-            ro, rl = O.decode_stream(Qh[b, h * G:(h + 1) * G, L - 1], np.concatenate(parts),
-                                     np.array(descs, DESC_DTYPE), SCALE)
-            out, lse = outs[i]
+        out, lse = outs[i]
+        for s_ in (0, streams - 1):
+            b, h = divmod(s_, kp.Hkv)
+            ro, rl = oe.state_decode(s_, entry, entry["switched"])
             check_attention(out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G], ro, rl,
-                            f"resume step {i} s={s}")
-    _check_finals(kp, oe, entries, streams)
+                            f"resume step {i} s={s_}")
+    check_pipeline_finals(kp, oe, entries, streams)
     kp.close()

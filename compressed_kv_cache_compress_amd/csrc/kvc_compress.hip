@@ -102,16 +102,22 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ qs, int
   float l[NQ], mb[NQ], z[NQ];
   logits<NQ>(qs + (uint64_t)q0 * D, kf, a.scale, l);
 #pragma unroll
-  for (int j = 0; j < NQ; ++j) mb[j] = max64(l[j]);
+  for (int j = 0; j < NQ; ++j) mb[j] = l[j];
+  max64_n<NQ>(mb);
 #pragma unroll
-  for (int j = 0; j < NQ; ++j) z[j] = tree_sum64(spec_exp2((l[j] - mb[j]) * KVC_LOG2E));
+  for (int j = 0; j < NQ; ++j) z[j] = spec_exp2((l[j] - mb[j]) * KVC_LOG2E);
+  tree_sum64_n<NQ>(z);
+  // lane j < NQ stores query j's partials
+  float vm = mb[0], vz = z[0];
 #pragma unroll
-  for (int j = 0; j < NQ; ++j) {
-    if (lane == j) {
-      const uint64_t o = ((uint64_t)s * a.nq + q0 + j) * a.nblk + blk;
-      part_m[o] = mb[j];
-      part_z[o] = z[j];
-    }
+  for (int j = 1; j < NQ; ++j) {
+    vm = lane == j ? mb[j] : vm;
+    vz = lane == j ? z[j] : vz;
+  }
+  if (lane < NQ) {
+    const uint64_t o = ((uint64_t)s * a.nq + q0 + lane) * a.nblk + blk;
+    part_m[o] = vm;
+    part_z[o] = vz;
   }
 }
 
@@ -222,7 +228,9 @@ __global__ __launch_bounds__(64 * TW) void k_token_scores_shared(
     const float* __restrict__ norm_iz, float* __restrict__ scores, float* __restrict__ scores_out) {
   constexpr int R = TW * QB;  // queries per round
   __shared__ float term[2][R][64];
-  const int s = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // the wave index made visibly uniform, so that query rows are scalar loads
+  const int s = blockIdx.y, lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tr = blockIdx.x * 64 + lane;
   const bool valid = tr < a.region_len;
   const int t = a.region_begin + (valid ? tr : 0);

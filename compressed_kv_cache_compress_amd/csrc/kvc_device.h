@@ -105,6 +105,48 @@ __device__ __forceinline__ float max64(float v) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// max64 and tree_sum64 of N independent values at once, each step applied
+// to all of them before the next, so that the DPP moves of one value fill
+// the wait states after another's (same operations and order per value).
+template <int N>
+__device__ __forceinline__ void max64_n(float* v) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = fmaxf(v[j], dpp_mov<0xB1>(v[j]));
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = fmaxf(v[j], dpp_mov<0x4E>(v[j]));
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = fmaxf(v[j], dpp_mov<0x141>(v[j]));
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = fmaxf(v[j], dpp_mov<0x140>(v[j]));
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), 48));
+    v[j] = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+  }
+}
+template <int N>
+__device__ __forceinline__ void tree_sum64_n(float* v) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = v[j] + dpp_mov<0xB1>(v[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = v[j] + dpp_mov<0x4E>(v[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = v[j] + dpp_mov<0x141>(v[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = v[j] + dpp_mov<0x140>(v[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), 48));
+    v[j] = (r0 + r1) + (r2 + r3);
+  }
+}
+
 // Count of set bits of a 64-bit lane mask below the calling lane.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));

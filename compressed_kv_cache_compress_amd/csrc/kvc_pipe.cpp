@@ -106,6 +106,7 @@ struct kvc_pipe {
   hipEvent_t* ready;                     // [pages]: window inputs ready (decode stream)
   hipEvent_t* done;                      // [pages]: event compressed (compression stream)
   uint64_t g, steps, fired, switched, host_waits;
+  bool broken;                           // a HIP call failed inside a step: only destroy is valid
   struct Pending {
     uint64_t event, step, page;          // event number, step that fired it, its page number
   };
@@ -273,11 +274,67 @@ kvc_status kv_pipe_create(const kvc_params* p, const kvc_pipe_config* cfg, void*
   return KVC_OK;
 }
 
+namespace {
+kvc_status step_impl(kvc_pipe* pp, const uint16_t* k_new, const uint16_t* v_new, uint32_t n_new,
+                     uint64_t new_stride, const uint16_t* win_K, const uint16_t* win_V,
+                     const uint16_t* win_Q, const uint16_t* q, uint16_t* out, float* lse,
+                     hipStream_t stream, bool* enqueued);
+}  // namespace
+
 kvc_status kv_pipe_step(kvc_pipe* pp, const uint16_t* k_new, const uint16_t* v_new,
                         uint32_t n_new, uint64_t new_stride, const uint16_t* win_K,
                         const uint16_t* win_V, const uint16_t* win_Q, const uint16_t* q,
                         uint16_t* out, float* lse, hipStream_t stream) {
-  if (!pp || stream != pp->dstream || !k_new || !v_new || n_new == 0) return KVC_E_INVALID;
+  if (!pp) return KVC_E_INVALID;
+  if (pp->broken) return KVC_E_HIP;
+  bool enqueued = false;
+  const kvc_status st = step_impl(pp, k_new, v_new, n_new, new_stride, win_K, win_V, win_Q, q,
+                                  out, lse, stream, &enqueued);
+  if (st != KVC_OK && enqueued) pp->broken = true;  // part of the step is on the stream
+  return st;
+}
+
+kvc_status kv_pipe_drain(kvc_pipe* pp, hipStream_t stream) {
+  if (!pp || stream != pp->dstream) return KVC_E_INVALID;
+  if (pp->broken) return KVC_E_HIP;
+  while (!pp->pending.empty()) {
+    const kvc_status st = switch_front(pp, false);
+    if (st != KVC_OK) {
+      pp->broken = true;
+      return st;
+    }
+  }
+  return KVC_OK;
+}
+
+kvc_status kv_pipe_get_stats(const kvc_pipe* pp, kvc_pipe_stats* out) {
+  if (!pp || !out) return KVC_E_INVALID;
+  std::memset(out, 0, sizeof *out);
+  out->steps = pp->steps;
+  out->tokens = pp->g;
+  out->events_fired = pp->fired;
+  out->events_switched = pp->switched;
+  out->host_waits = pp->host_waits;
+  out->pending = (uint32_t)pp->pending.size();
+  return KVC_OK;
+}
+
+kvc_status kv_pipe_destroy(kvc_pipe* pp) {
+  release(pp);
+  return KVC_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// One step; every check that can fail without a HIP error comes before the
+// first enqueue, and *enqueued records whether anything reached the stream.
+kvc_status step_impl(kvc_pipe* pp, const uint16_t* k_new, const uint16_t* v_new, uint32_t n_new,
+                     uint64_t new_stride, const uint16_t* win_K, const uint16_t* win_V,
+                     const uint16_t* win_Q, const uint16_t* q, uint16_t* out, float* lse,
+                     hipStream_t stream, bool* enqueued) {
+  if (stream != pp->dstream || !k_new || !v_new || n_new == 0) return KVC_E_INVALID;
   const kvc_pipe_config& c = pp->cfg;
   const uint32_t period = pp->r.pl.period;
   const uint64_t fill = pp->g % period;
@@ -294,6 +351,7 @@ kvc_status kv_pipe_step(kvc_pipe* pp, const uint16_t* k_new, const uint16_t* v_n
     return KVC_E_INVALID;
 
   const uint64_t page = pp->g / period;
+  *enqueued = true;
   // 1. the page about to be written again must have been switched out
   if (fill == 0 && page >= c.pages) {
     const uint64_t old = page - c.pages;
@@ -362,30 +420,5 @@ kvc_status kv_pipe_step(kvc_pipe* pp, const uint16_t* k_new, const uint16_t* v_n
   return KVC_OK;
 }
 
-kvc_status kv_pipe_drain(kvc_pipe* pp, hipStream_t stream) {
-  if (!pp || stream != pp->dstream) return KVC_E_INVALID;
-  while (!pp->pending.empty()) {
-    const kvc_status st = switch_front(pp, false);
-    if (st != KVC_OK) return st;
-  }
-  return KVC_OK;
-}
+}  // namespace
 
-kvc_status kv_pipe_get_stats(const kvc_pipe* pp, kvc_pipe_stats* out) {
-  if (!pp || !out) return KVC_E_INVALID;
-  std::memset(out, 0, sizeof *out);
-  out->steps = pp->steps;
-  out->tokens = pp->g;
-  out->events_fired = pp->fired;
-  out->events_switched = pp->switched;
-  out->host_waits = pp->host_waits;
-  out->pending = (uint32_t)pp->pending.size();
-  return KVC_OK;
-}
-
-kvc_status kv_pipe_destroy(kvc_pipe* pp) {
-  release(pp);
-  return KVC_OK;
-}
-
-}  // extern "C"

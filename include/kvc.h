@@ -378,7 +378,10 @@ kvc_status kv_pipe_create(const kvc_params* p, const kvc_pipe_config* cfg, void*
  *  q, out, lse        as for kv_attend_decode over the pipeline's list.
  * Events whose region would start before the pipeline's first token are not
  * fired.  Returns KVC_E_INVALID when an event is due and the window is
- * missing or the event slots are used up (nothing enqueued). */
+ * missing or the event slots are used up; every such error leaves the
+ * pipeline unchanged, with nothing enqueued.  KVC_E_HIP (a failed HIP call
+ * after part of the step was enqueued) leaves it unusable: every later call
+ * but kv_pipe_destroy returns KVC_E_HIP. */
 kvc_status kv_pipe_step(kvc_pipe* pipe, const uint16_t* k_new, const uint16_t* v_new,
                         uint32_t n_new, uint64_t new_stride, const uint16_t* win_K,
                         const uint16_t* win_V, const uint16_t* win_Q, const uint16_t* q,

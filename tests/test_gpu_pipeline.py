@@ -249,3 +249,61 @@ def test_pipeline_resume_with_prefill_and_prefix_events():
                             f"resume step {i} s={s_}")
     check_pipeline_finals(kp, oe, entries, streams)
     kp.close()
+
+
+def test_pipeline_rejects_before_enqueue():
+    """Errors of kv_pipe_step are raised before anything is enqueued and
+    leave the pipeline unchanged: a due event without its window, a step
+    that would cross a page, event slots used up; the run then continues
+    and matches the deterministic schedule."""
+    import ctypes
+    from compressed_kv_cache_compress_amd import KvcError, lib
+    w, kp, c = _make(PIPE_LAG, lag=0, pages=4, steps=96)
+    streams = kp.B * kp.Hkv
+    D_ = 128
+    K, V = w["K"], w["V"]
+    # 63 single-token steps: no event yet (the first fires at token 64)
+    for _ in range(63):
+        kp.step(1, decode=False)
+    p0 = kp.length
+    with pytest.raises(KvcError) as e:     # event due, no window
+        kp.pipe.step(K[:, :, p0:], V[:, :, p0:], 1, kp.L * D_)
+    assert e.value.status == -1
+    with pytest.raises(KvcError) as e:     # 2 tokens would cross into the next page
+        kp.pipe.step(K[:, :, p0:], V[:, :, p0:], 2, kp.L * D_)
+    assert e.value.status == -1
+    st = kp.pipe.stats()
+    assert (st["steps"], st["tokens"], st["events_fired"]) == (63, 63, 0)
+    bad = ctypes.c_void_p(1)               # a different stream handle
+    assert lib().kv_pipe_step(kp.pipe.h, ctypes.c_void_p(K.data_ptr()),
+                              ctypes.c_void_p(V.data_ptr()), 1, kp.L * D_, None, None, None, None,
+                              None, None, bad) == -1
+    assert lib().kv_pipe_drain(kp.pipe.h, bad) == -1
+    kp.step(1, decode=False)               # fires event 0 with its window
+    for _ in range(32):
+        kp.step(1, decode=False)           # fires event 1 at token 96
+    st = kp.pipe.stats()
+    assert (st["steps"], st["tokens"], st["events_fired"], st["events_switched"]) == (96, 96, 2, 2)
+    torch.cuda.synchronize()
+    kp.close()
+
+
+def test_pipeline_event_slots_used_up():
+    """A pipeline sized for 2 events refuses the third before enqueueing."""
+    from compressed_kv_cache_compress_amd import KvcError
+    w, kp, c = _make(PIPE_LAG, lag=0, pages=4, steps=96)
+    assert kp.cfg.max_events == 2
+    for _ in range(127):
+        kp.step(1, decode=False)
+    assert kp.pipe.stats()["events_fired"] == 2
+    p0 = kp.length
+    wk = w["K"][:, :, p0 + 1 - c["window"]:]
+    wv = w["V"][:, :, p0 + 1 - c["window"]:]
+    wq = w["Qall"][:, :, p0 + 1 - c["window"]:]
+    with pytest.raises(KvcError) as e:     # the third event has no slot
+        kp.pipe.step(w["K"][:, :, p0:], w["V"][:, :, p0:], 1, kp.L * 128, wk, wv, wq)
+    assert e.value.status == -1
+    assert kp.pipe.stats()["tokens"] == 127
+    kp.pipe.drain()
+    torch.cuda.synchronize()
+    kp.close()

@@ -42,6 +42,7 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
+PIPE_EVENT_WAVES = 1024  # waves an event kernel may keep in flight in the capped asynchronous run
 
 
 def parse():
@@ -159,12 +160,14 @@ def bench_pipeline(a, kvc, stream):
     """The last generation steps of the Kara workload through the compression
     pipeline (kv_pipe_*), as a serving loop runs them: one decode step per
     token, the host waiting for each step's output (a sampler needs it), an
-    event every 64 tokens.  Run twice from the same state: events compressed
-    inside the step that fires them (blocking), and on the pipeline's own
-    stream, switched in when done (asynchronous).  Reports each run's total
-    time (ending with a drain, so every event is inside it) and the latency
-    of single steps; the two final caches are compared byte for byte, and
-    one event's compression is timed on its own."""
+    event every 64 tokens.  Run three times from the same state: events
+    compressed inside the step that fires them (blocking); on the pipeline's
+    own stream, switched in when done (asynchronous); the same with each event
+    kernel capped at PIPE_EVENT_WAVES waves in flight, so that decode keeps
+    most of the GPU.  Reports each run's total time (ending with a drain, so
+    every event is inside it) and the latency of single steps; the final
+    caches are compared byte for byte, and one event's compression is timed
+    on its own."""
     from compressed_kv_cache_compress_amd import gen, kara
     k = gen.KARA
     dev = torch.device("cuda:0")
@@ -174,13 +177,16 @@ def bench_pipeline(a, kvc, stream):
     start = w["gen"] - n - prot
     scale = float(np.float32(1.0 / math.sqrt(128.0)))
     runs, pipes = {}, {}
-    for mode, name in ((kvc.PIPE_SYNC, "blocking"), (kvc.PIPE_ASYNC, "async")):
+    runs_cfg = ((kvc.PIPE_SYNC, "blocking", 0), (kvc.PIPE_ASYNC, "async", 0),
+                (kvc.PIPE_ASYNC, "async_capped", PIPE_EVENT_WAVES))
+    for mode, name, cap in runs_cfg:
         print(f"[bench] pipeline {name}: {n} steps from generated token {start}", file=sys.stderr,
               flush=True)
         kp = kara.KaraPipeline(w["K"], w["V"], w["Qall"], prompt=w["prompt"], start=start,
                                window=k["window"], delta=delta, protect=prot,
                                retention_pct=k["retention_pct"], alpha=k["alpha"],
-                               gamma=k["gamma"], scale=scale, mode=mode, steps=n + prot)
+                               gamma=k["gamma"], scale=scale, mode=mode, steps=n + prot,
+                               event_max_waves=cap)
         kp.step(prot, decode=False)
         torch.cuda.synchronize()
         lat = np.zeros(n)
@@ -198,12 +204,13 @@ def bench_pipeline(a, kvc, stream):
                           host_waits=kp.pipe.stats()["host_waits"],
                           events=kp.pipe.stats()["events_fired"])
         pipes[name] = kp
-    a_, b_ = pipes["blocking"], pipes["async"]
+    a_ = pipes["blocking"]
     streams = a_.B * a_.Hkv
     lo = a_.cfg.events_offset
     hi = lo + a_.cfg.max_events * a_.layout.event_bytes
-    same = bool(torch.equal(a_.desc, b_.desc)) and bool(torch.equal(
+    same = all(bool(torch.equal(a_.desc, b_.desc)) and bool(torch.equal(
         a_.packed.view(streams, -1)[:, lo:hi], b_.packed.view(streams, -1)[:, lo:hi]))
+        for b_ in pipes.values())
     # one event's compression on its own (same window shape, scratch output)
     pe = kvc.KvParams(batch=a_.B, n_q_heads=a_.Hq, n_kv_heads=a_.Hkv, n_ctx=k["window"],
                       region_begin=k["window"] - prot - delta, region_len=delta,
@@ -230,7 +237,9 @@ def bench_pipeline(a, kvc, stream):
                         "8192 generated tokens, one decode step each with the host waiting for "
                         "its output, an event every 64 tokens, 64-token protected tail, 4 pages",
             "steps": n, "event_ms": t_event, "blocking": runs["blocking"],
-            "async": runs["async"], "identical_final_cache": same}
+            "async": runs["async"], "async_capped": dict(runs["async_capped"],
+                                                         event_max_waves=PIPE_EVENT_WAVES),
+            "identical_final_cache": same}
 
 
 def bench_stream_budget(a, kvc, K, V, Qw, q, B, Hq, Hkv, N, S, W, strategies, budget, scale,

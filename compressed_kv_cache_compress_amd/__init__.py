@@ -48,7 +48,7 @@ class Params(ctypes.Structure):
                 ("packed_stream_stride", ctypes.c_uint64), ("packed_base_offset", ctypes.c_uint64),
                 ("desc_stream_stride", ctypes.c_uint32), ("max_desc_per_stream", ctypes.c_uint32),
                 ("decode_splits", ctypes.c_uint32), ("budget_scope", ctypes.c_uint32),
-                ("reserved", ctypes.c_uint32 * 3)]
+                ("compress_max_waves", ctypes.c_uint32), ("reserved", ctypes.c_uint32 * 2)]
 
 
 class Layout(ctypes.Structure):
@@ -142,7 +142,7 @@ class KvParams:
                  budget_bytes=0, t2c_alpha=0, t2c_gamma=0, scale=0.0, kv_stream_stride=0,
                  qw_head_stride=0, packed_stream_stride=0, packed_base_offset=0,
                  desc_stream_stride=0, max_desc_per_stream=0, decode_splits=0,
-                 budget_scope=0):
+                 budget_scope=0, compress_max_waves=0):
         strategies = list(strategies)
         self._strat = (Strategy * max(1, len(strategies)))(*[Strategy(t, c) for t, c in strategies])
         if region_len is None:
@@ -162,6 +162,7 @@ class KvParams:
         p.desc_stream_stride, p.max_desc_per_stream = desc_stream_stride, max_desc_per_stream
         p.decode_splits = decode_splits
         p.budget_scope = budget_scope
+        p.compress_max_waves = compress_max_waves
         self.strategies = strategies
 
     @property

@@ -58,19 +58,38 @@ struct ScoreArgs {
   float scale;
 };
 
+// Work units of a logical grid (gx, gy, gz), walked by a 1-D launch that
+// may be capped below the unit count: workgroup b takes units b, b +
+// gridDim.x, ...; unit u is (u % gx, u / gx % gy, u / (gx gy)).  Every unit
+// is computed by exactly one workgroup whatever the cap, so results do not
+// depend on it.
+struct Units {
+  uint32_t gx, gy, total;
+};
+__device__ __forceinline__ void unit_xyz(const Units& g, uint32_t u, int& x, int& y, int& z) {
+  x = (int)(u % g.gx);
+  const uint32_t r = u / g.gx;
+  y = (int)(r % g.gy);
+  z = (int)(r / g.gy);
+}
+
 // Window queries to fp32, [stream][g * W + w][128], so that the scoring
 // kernels read them with scalar loads and no per-use conversion.
 // grid (G * W, streams), 64 threads: lane = channel pair.
-__global__ __launch_bounds__(64) void k_q_convert(ScoreArgs a, float* __restrict__ qf) {
-  const int qi = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
-  const int b = s / a.hkv, h = s - b * a.hkv;
-  const int g = qi / a.W, w = qi - g * a.W;
-  const uint16_t* src = a.Qw + (uint64_t)(b * a.hq + h * a.G + g) * a.qw_stride + (uint64_t)w * D;
-  const uint32_t v = reinterpret_cast<const uint32_t*>(src)[lane];
-  float2 o;
-  o.x = __uint_as_float(v << 16);
-  o.y = __uint_as_float(v & 0xFFFF0000u);
-  reinterpret_cast<float2*>(qf + ((uint64_t)s * a.nq + qi) * D)[lane] = o;
+__global__ __launch_bounds__(64) void k_q_convert(ScoreArgs a, Units un, float* __restrict__ qf) {
+  const int lane = threadIdx.x;
+  for (uint32_t u = blockIdx.x; u < un.total; u += gridDim.x) {
+    int qi, s, z_;
+    unit_xyz(un, u, qi, s, z_);
+    const int b = s / a.hkv, h = s - b * a.hkv;
+    const int g = qi / a.W, w = qi - g * a.W;
+    const uint16_t* src = a.Qw + (uint64_t)(b * a.hq + h * a.G + g) * a.qw_stride + (uint64_t)w * D;
+    const uint32_t v = reinterpret_cast<const uint32_t*>(src)[lane];
+    float2 o;
+    o.x = __uint_as_float(v << 16);
+    o.y = __uint_as_float(v & 0xFFFF0000u);
+    reinterpret_cast<float2*>(qf + ((uint64_t)s * a.nq + qi) * D)[lane] = o;
+  }
 }
 
 constexpr int QB = 4;  // window queries scored together (independent fma chains)
@@ -125,18 +144,23 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ qs, int
 // 64-token block; wave z handles window queries z * qper .. (z + 1) * qper - 1
 // (each (query, block) partial is computed by exactly one wave, so the split
 // only fills the chip when a domain has few blocks).
-__global__ __launch_bounds__(64) void k_score_partials(ScoreArgs a, const float* __restrict__ qf,
+__global__ __launch_bounds__(64) void k_score_partials(ScoreArgs a, Units un,
+                                                       const float* __restrict__ qf,
                                                        float* __restrict__ part_m,
                                                        float* __restrict__ part_z) {
-  const int blk = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
-  const int t = blk * BLK + lane;
-  float kf[D];
-  load_row_f32(a.K + (uint64_t)s * a.kv_stride + (uint64_t)t * D, kf);
-  const float* qs = qf + (uint64_t)s * a.nq * D;
-  int q0 = blockIdx.z * a.qper;
-  const int q1 = min(a.nq, q0 + a.qper);
-  for (; q0 + QB <= q1; q0 += QB) block_partials<QB>(qs, q0, kf, a, s, blk, lane, part_m, part_z);
-  for (; q0 < q1; ++q0) block_partials<1>(qs, q0, kf, a, s, blk, lane, part_m, part_z);
+  const int lane = threadIdx.x;
+  for (uint32_t u = blockIdx.x; u < un.total; u += gridDim.x) {
+    int blk, s, zq;
+    unit_xyz(un, u, blk, s, zq);
+    const int t = blk * BLK + lane;
+    float kf[D];
+    load_row_f32(a.K + (uint64_t)s * a.kv_stride + (uint64_t)t * D, kf);
+    const float* qs = qf + (uint64_t)s * a.nq * D;
+    int q0 = zq * a.qper;
+    const int q1 = min(a.nq, q0 + a.qper);
+    for (; q0 + QB <= q1; q0 += QB) block_partials<QB>(qs, q0, kf, a, s, blk, lane, part_m, part_z);
+    for (; q0 < q1; ++q0) block_partials<1>(qs, q0, kf, a, s, blk, lane, part_m, part_z);
+  }
 }
 
 // grid (nq, streams), 64 threads.  m = max of the block maxima; Z = pairwise
@@ -144,12 +168,17 @@ __global__ __launch_bounds__(64) void k_score_partials(ScoreArgs a, const float*
 // groups of 64 consecutive blocks are summed across lanes, then the group
 // sums are combined pairwise in LDS.
 constexpr int NORM_GROUPS = (1 << 22) / BLK / 64;  // n_ctx <= 2^22
-__global__ __launch_bounds__(64) void k_score_normalise(ScoreArgs a, const float* __restrict__ part_m,
+__global__ __launch_bounds__(64) void k_score_normalise(ScoreArgs a, Units un,
+                                                        const float* __restrict__ part_m,
                                                         const float* __restrict__ part_z,
                                                         float* __restrict__ norm_m,
                                                         float* __restrict__ norm_iz) {
   __shared__ float grp[NORM_GROUPS];
-  const int qi = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+  const int lane = threadIdx.x;
+  // one wave: its LDS accesses execute in issue order, also across units
+  for (uint32_t u = blockIdx.x; u < un.total; u += gridDim.x) {
+  int qi, s, z_;
+  unit_xyz(un, u, qi, s, z_);
   const float* pm = part_m + ((uint64_t)s * a.nq + qi) * a.nblk;
   const float* pz = part_z + ((uint64_t)s * a.nq + qi) * a.nblk;
   float mx = -INFINITY;
@@ -172,6 +201,7 @@ __global__ __launch_bounds__(64) void k_score_normalise(ScoreArgs a, const float
     norm_m[(uint64_t)s * a.nq + qi] = m;
     norm_iz[(uint64_t)s * a.nq + qi] = 1.0f / grp[0];
   }
+  }
 }
 
 // Adds the probabilities NQ window queries q0.. give this lane's key to sc,
@@ -191,13 +221,17 @@ __device__ __forceinline__ void add_scores(const float* __restrict__ qs, int q0,
 
 // grid (ceil(region_len/64), streams), 64 threads: lane = region token.  The
 // score is accumulated one window query at a time, in query order.
-__global__ __launch_bounds__(64) void k_token_scores(ScoreArgs a, const float* __restrict__ qf,
+__global__ __launch_bounds__(64) void k_token_scores(ScoreArgs a, Units un,
+                                                     const float* __restrict__ qf,
                                                      const float* __restrict__ norm_m,
                                                      const float* __restrict__ norm_iz,
                                                      float* __restrict__ scores,
                                                      float* __restrict__ scores_out) {
-  const int s = blockIdx.y, lane = threadIdx.x;
-  const int tr = blockIdx.x * 64 + lane;
+  const int lane = threadIdx.x;
+  for (uint32_t u = blockIdx.x; u < un.total; u += gridDim.x) {
+  int bx, s, z_;
+  unit_xyz(un, u, bx, s, z_);
+  const int tr = bx * 64 + lane;
   const bool valid = tr < a.region_len;
   const int t = a.region_begin + (valid ? tr : 0);
   float kf[D];
@@ -213,6 +247,7 @@ __global__ __launch_bounds__(64) void k_token_scores(ScoreArgs a, const float* _
     scores[(uint64_t)s * a.region_len + tr] = sc;
     if (scores_out) scores_out[(uint64_t)s * a.region_len + tr] = sc;
   }
+  }
 }
 
 // The same scores when the region has few tokens (one wave per 64 region
@@ -224,14 +259,17 @@ __global__ __launch_bounds__(64) void k_token_scores(ScoreArgs a, const float* _
 // (ceil(region_len/64), streams), 64 * TW threads.
 template <int TW>
 __global__ __launch_bounds__(64 * TW) void k_token_scores_shared(
-    ScoreArgs a, const float* __restrict__ qf, const float* __restrict__ norm_m,
+    ScoreArgs a, Units un, const float* __restrict__ qf, const float* __restrict__ norm_m,
     const float* __restrict__ norm_iz, float* __restrict__ scores, float* __restrict__ scores_out) {
   constexpr int R = TW * QB;  // queries per round
   __shared__ float term[2][R][64];
   // the wave index made visibly uniform, so that query rows are scalar loads
-  const int s = blockIdx.y, lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tr = blockIdx.x * 64 + lane;
+  for (uint32_t u = blockIdx.x; u < un.total; u += gridDim.x) {
+  int bx, s, z_;
+  unit_xyz(un, u, bx, s, z_);
+  const int tr = bx * 64 + lane;
   const bool valid = tr < a.region_len;
   const int t = a.region_begin + (valid ? tr : 0);
   float kf[D];
@@ -268,6 +306,8 @@ __global__ __launch_bounds__(64 * TW) void k_token_scores_shared(
     scores[(uint64_t)s * a.region_len + tr] = sc;
     if (scores_out) scores_out[(uint64_t)s * a.region_len + tr] = sc;
   }
+  __syncthreads();  // the next unit's first round rewrites a buffer wave 0 may still be adding
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -289,10 +329,13 @@ constexpr int SEL_TOKENS = 16;  // tokens per block (x2 vectors, 8 per wave)
 // NC = number of distinct channel counts; the NC threshold searches of a
 // vector run interleaved (independent ballot chains).
 template <int NC>
-__global__ __launch_bounds__(256) void k_channel_select(SelectArgs a) {
-  const int s = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+__global__ __launch_bounds__(256) void k_channel_select(SelectArgs a, Units un) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (uint32_t u = blockIdx.x; u < un.total; u += gridDim.x) {
+  int bx, s, z_;
+  unit_xyz(un, u, bx, s, z_);
   for (int r = wv; r < 2 * SEL_TOKENS; r += 4) {
-    const int tr = blockIdx.x * SEL_TOKENS + (r >> 1);
+    const int tr = bx * SEL_TOKENS + (r >> 1);
     const int kv = r & 1;
     if (tr >= a.region_len) break;  // wave-uniform
     const uint16_t* row = (kv ? a.V : a.K) + (uint64_t)s * a.kv_stride +
@@ -338,6 +381,7 @@ __global__ __launch_bounds__(256) void k_channel_select(SelectArgs a) {
         a.rho[o] = (Eall == 0.0f) ? 1.0f : Ec / Eall;
       }
     }
+  }
   }
 }
 
@@ -752,6 +796,17 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// 1-D launch over the units, at most max_waves / waves_per_group workgroups
+// (at least one) when max_waves > 0.
+static dim3 capped(const Units& u, uint32_t waves_per_group, uint32_t max_waves) {
+  uint32_t n = u.total;
+  if (max_waves) {
+    const uint32_t cap = max_waves / waves_per_group > 0 ? max_waves / waves_per_group : 1u;
+    if (n > cap) n = cap;
+  }
+  return dim3(n);
+}
+
 hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
   if (p.scoring) {
     ScoreArgs sa;
@@ -777,20 +832,23 @@ hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
     if (qsplit < 1) qsplit = 1;
     sa.qper = (((p.nq + qsplit - 1) / qsplit + QB - 1) / QB) * QB;
     qsplit = (p.nq + sa.qper - 1) / sa.qper;
-    hipLaunchKernelGGL(k_q_convert, dim3(p.nq, p.streams), dim3(64), 0, st, sa, p.qf);
-    hipLaunchKernelGGL(k_score_partials, dim3(p.nblk, p.streams, qsplit), dim3(64), 0, st, sa,
+    const Units uq{(uint32_t)p.nq, (uint32_t)p.streams, (uint32_t)p.nq * p.streams};
+    const Units up{(uint32_t)p.nblk, (uint32_t)p.streams, (uint32_t)(p.nblk * p.streams * qsplit)};
+    hipLaunchKernelGGL(k_q_convert, capped(uq, 1, p.max_waves), dim3(64), 0, st, sa, uq, p.qf);
+    hipLaunchKernelGGL(k_score_partials, capped(up, 1, p.max_waves), dim3(64), 0, st, sa, up,
                        (const float*)p.qf, p.part_m, p.part_z);
-    hipLaunchKernelGGL(k_score_normalise, dim3(p.nq, p.streams), dim3(64), 0, st, sa,
+    hipLaunchKernelGGL(k_score_normalise, capped(uq, 1, p.max_waves), dim3(64), 0, st, sa, uq,
                        (const float*)p.part_m, (const float*)p.part_z, p.norm_m, p.norm_iz);
-    const dim3 tgrid((p.region_len + 63) / 64, p.streams);
-    const int64_t tw = (int64_t)tgrid.x * tgrid.y;
-    if (tw * 4 <= SCORE_WAVES && p.nq >= 8 * QB)
-      hipLaunchKernelGGL(k_token_scores_shared<8>, tgrid, dim3(512), 0, st, sa,
+    const uint32_t tx = (uint32_t)(p.region_len + 63) / 64;
+    const Units ut{tx, (uint32_t)p.streams, tx * (uint32_t)p.streams};
+    if ((int64_t)ut.total * 4 <= SCORE_WAVES && p.nq >= 8 * QB)
+      hipLaunchKernelGGL(k_token_scores_shared<8>, capped(ut, 8, p.max_waves), dim3(512), 0, st,
+                         sa, ut, (const float*)p.qf, (const float*)p.norm_m,
+                         (const float*)p.norm_iz, p.scores, p.scores_out);
+    else
+      hipLaunchKernelGGL(k_token_scores, capped(ut, 1, p.max_waves), dim3(64), 0, st, sa, ut,
                          (const float*)p.qf, (const float*)p.norm_m, (const float*)p.norm_iz,
                          p.scores, p.scores_out);
-    else
-      hipLaunchKernelGGL(k_token_scores, tgrid, dim3(64), 0, st, sa, (const float*)p.qf,
-                         (const float*)p.norm_m, (const float*)p.norm_iz, p.scores, p.scores_out);
   }
   if (p.nc > 0) {
     SelectArgs se;
@@ -803,16 +861,18 @@ hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
     se.region_len = p.region_len;
     se.nc = p.nc;
     for (int i = 0; i < MAX_NC; ++i) se.cvals[i] = p.cvals[i];
-    const dim3 grid((p.region_len + SEL_TOKENS - 1) / SEL_TOKENS, p.streams);
+    const uint32_t sx = (uint32_t)(p.region_len + SEL_TOKENS - 1) / SEL_TOKENS;
+    const Units us{sx, (uint32_t)p.streams, sx * (uint32_t)p.streams};
+    const dim3 grid = capped(us, 4, p.max_waves);
     switch (p.nc) {
-      case 1: hipLaunchKernelGGL(k_channel_select<1>, grid, dim3(256), 0, st, se); break;
-      case 2: hipLaunchKernelGGL(k_channel_select<2>, grid, dim3(256), 0, st, se); break;
-      case 3: hipLaunchKernelGGL(k_channel_select<3>, grid, dim3(256), 0, st, se); break;
-      case 4: hipLaunchKernelGGL(k_channel_select<4>, grid, dim3(256), 0, st, se); break;
-      case 5: hipLaunchKernelGGL(k_channel_select<5>, grid, dim3(256), 0, st, se); break;
-      case 6: hipLaunchKernelGGL(k_channel_select<6>, grid, dim3(256), 0, st, se); break;
-      case 7: hipLaunchKernelGGL(k_channel_select<7>, grid, dim3(256), 0, st, se); break;
-      default: hipLaunchKernelGGL(k_channel_select<8>, grid, dim3(256), 0, st, se); break;
+      case 1: hipLaunchKernelGGL(k_channel_select<1>, grid, dim3(256), 0, st, se, us); break;
+      case 2: hipLaunchKernelGGL(k_channel_select<2>, grid, dim3(256), 0, st, se, us); break;
+      case 3: hipLaunchKernelGGL(k_channel_select<3>, grid, dim3(256), 0, st, se, us); break;
+      case 4: hipLaunchKernelGGL(k_channel_select<4>, grid, dim3(256), 0, st, se, us); break;
+      case 5: hipLaunchKernelGGL(k_channel_select<5>, grid, dim3(256), 0, st, se, us); break;
+      case 6: hipLaunchKernelGGL(k_channel_select<6>, grid, dim3(256), 0, st, se, us); break;
+      case 7: hipLaunchKernelGGL(k_channel_select<7>, grid, dim3(256), 0, st, se, us); break;
+      default: hipLaunchKernelGGL(k_channel_select<8>, grid, dim3(256), 0, st, se, us); break;
     }
   }
   ChooseArgs ca;

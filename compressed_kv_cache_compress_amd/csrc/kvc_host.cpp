@@ -255,6 +255,7 @@ kvc_status kv_compress(const kvc_params* p, const uint16_t* K, const uint16_t* V
   c.t2c_alpha = (int)p->t2c_alpha;
   c.t2c_gamma = (int)p->t2c_gamma;
   c.scoring = scoring;
+  c.max_waves = p->compress_max_waves;
   c.K = K;
   c.V = V;
   c.Qw = Qwin;

@@ -28,6 +28,7 @@ struct CompressPlan {
   int cvals[MAX_NC];
   int t2c_alpha, t2c_gamma;
   bool scoring;           // run the window-scoring kernels
+  uint32_t max_waves;     // cap on the waves of each scoring / selection kernel (0: none)
   // inputs / outputs
   const uint16_t *K, *V, *Qw;
   const uint8_t* forced;

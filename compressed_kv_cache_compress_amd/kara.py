@@ -110,6 +110,8 @@ class KaraPipeline:
     step: appended to a dense page, decoded with its own query, and every
     `delta` tokens the page `protect` tokens back is compressed on the
     pipeline's stream and switched in (when, depends on `mode`).
+    event_max_waves caps the waves an event's compression keeps in flight, so
+    that a background event leaves most of the GPU to decode.
 
     K, V: [B, Hkv, L, 128], Qall: [B, Hq, L, 128] on the GPU (L = prompt +
     generated); they are the full-resolution source of new tokens and of the
@@ -118,7 +120,7 @@ class KaraPipeline:
 
     def __init__(self, K, V, Qall, *, prompt, start=0, window=512, delta=64, protect=64,
                  retention_pct=20, alpha=3, gamma=16, prompt_seg=256, scale=0.0, mode=PIPE_ASYNC,
-                 switch_lag=0, pages=None, steps=None, decode_splits=0):
+                 switch_lag=0, pages=None, steps=None, decode_splits=0, event_max_waves=0):
         B, Hkv, L = K.shape[0], K.shape[1], K.shape[2]
         Hq = Qall.shape[1]
         assert K.is_contiguous() and V.is_contiguous() and Qall.is_contiguous()
@@ -143,7 +145,7 @@ class KaraPipeline:
                                   seg_tokens=delta, n_win=window, strategies=[(T, D)],
                                   budget_bytes=4 * delta * D, t2c_alpha=alpha, t2c_gamma=gamma,
                                   scale=scale, kv_stream_stride=L * D, qw_head_stride=L * D,
-                                  decode_splits=decode_splits)
+                                  decode_splits=decode_splits, compress_max_waves=event_max_waves)
         _, lev = kv_layout_query(self.ev_params)
         ev_bytes = (lev.seg_bytes[0] + 15) // 16 * 16
         prompt_bytes = _seg_bytes_keep_all(prompt)

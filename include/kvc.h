@@ -101,7 +101,12 @@ typedef struct {
   uint32_t decode_splits;        /* split-K factor; 0 => library choice */
   /* --- compression, continued --- */
   uint32_t budget_scope;         /* KVC_BUDGET_SEGMENT (0) or KVC_BUDGET_STREAM (1) */
-  uint32_t reserved[3];
+  uint32_t compress_max_waves;   /* 0, or a cap on the waves each scoring and channel-
+                                    selection kernel of kv_compress keeps in flight (each
+                                    workgroup then walks several work units): keeps a
+                                    compression that runs beside decode to a share of the
+                                    GPU; results do not depend on it */
+  uint32_t reserved[2];
 } kvc_params;
 
 /* budget_scope values.

@@ -13,7 +13,8 @@ pytestmark = pytest.mark.gpu
 
 
 def _compare(w, *, S, strategies, budget, region_begin=0, region_len=None, t2c_alpha=0,
-             t2c_gamma=0, forced=None, streams=None, label="", budget_scope=0):
+             t2c_gamma=0, forced=None, streams=None, label="", budget_scope=0,
+             compress_max_waves=0):
     say(f"[compress] {label} B={w['B']} Hq={w['Hq']} Hkv={w['Hkv']} N={w['N']} S={S} "
         f"W={w['W']} region=({region_begin},{region_len})")
     K, V, Qw = w["K"].cuda(), w["V"].cuda(), w["Qw"].cuda()
@@ -21,7 +22,8 @@ def _compare(w, *, S, strategies, budget, region_begin=0, region_len=None, t2c_a
     r = runtime.compress(K, V, Qw, seg_tokens=S, strategies=strategies, budget_bytes=budget,
                          region_begin=region_begin, region_len=region_len, t2c_alpha=t2c_alpha,
                          t2c_gamma=t2c_gamma, scale=float(SCALE), forced=fdev, want_scores=True,
-                         want_objective=True, budget_scope=budget_scope)
+                         want_objective=True, budget_scope=budget_scope,
+                         compress_max_waves=compress_max_waves)
     torch.cuda.synchronize()
     cap = r.layout.stream_capacity
     ref = oracle_compress_all(w, S=S, strategies=strategies, budget=budget,
@@ -190,3 +192,17 @@ def test_compress_deterministic():
     assert all(np.array_equal(a, b) for a, b in zip(outs[0][0], outs[1][0]))
     assert np.array_equal(outs[0][1], outs[1][1])
     assert np.array_equal(outs[0][2].view(np.uint32), outs[1][2].view(np.uint32))
+
+
+@pytest.mark.parametrize("waves", [1, 7, 64])
+def test_compress_wave_cap(waves):
+    """A cap on the waves in flight (each workgroup then walks several work
+    units) changes nothing: still bit-exact against the oracle, on a shape
+    that takes the shared token-score kernel and the query split of the
+    partials, and one with several channel counts."""
+    w = gen.make_workload("batched128k", B=1, N=1024)
+    _compare(w, S=128, strategies=gen.table9(128), budget=gen.budget_bytes(25, 128),
+             label=f"cap {waves} waves", compress_max_waves=waves)
+    t = gen.make_workload("tiny", N=2048)
+    _compare(t, S=64, strategies=gen.table9(64), budget=gen.budget_bytes(33, 64),
+             label=f"tiny cap {waves} waves", compress_max_waves=waves)

@@ -136,7 +136,7 @@ SMALL = dict(B=1, prompt=256, gen=512, window=128, delta=32, protect=32, prompt_
              retention_pct=20, alpha=1, gamma=8)
 
 
-def _make(mode, lag=0, pages=None, start=0, steps=None, seed=0, **over):
+def _make(mode, lag=0, pages=None, start=0, steps=None, seed=0, event_max_waves=0, **over):
     c = dict(SMALL)
     c.update(over)
     w = gen.make_kara(seed=seed, device="cuda", B=c["B"], prompt=c["prompt"], gen=c["gen"])
@@ -144,7 +144,8 @@ def _make(mode, lag=0, pages=None, start=0, steps=None, seed=0, **over):
                            window=c["window"], delta=c["delta"], protect=c["protect"],
                            retention_pct=c["retention_pct"], alpha=c["alpha"], gamma=c["gamma"],
                            prompt_seg=c["prompt_seg"], scale=float(SCALE), mode=mode,
-                           switch_lag=lag, pages=pages, steps=steps)
+                           switch_lag=lag, pages=pages, steps=steps,
+                           event_max_waves=event_max_waves)
     return w, kp, c
 
 
@@ -180,12 +181,13 @@ def test_pipeline_deterministic_modes(mode, lag):
     kp.close()
 
 
-def test_pipeline_async_states_are_admissible():
-    """The asynchronous mode: each step's list is a prefix of the fired
-    events that includes every event whose page was written again; outputs
-    match the oracle over that exact state; after drain the finals equal the
-    oracle's."""
-    w, kp, c = _make(PIPE_ASYNC, pages=3)
+@pytest.mark.parametrize("cap", [0, 64])
+def test_pipeline_async_states_are_admissible(cap):
+    """The asynchronous mode (event kernels uncapped, or capped at 64 waves in
+    flight): each step's list is a prefix of the fired events that includes
+    every event whose page was written again; outputs match the oracle over
+    that exact state; after drain the finals equal the oracle's."""
+    w, kp, c = _make(PIPE_ASYNC, pages=3, event_max_waves=cap)
     streams = kp.B * kp.Hkv
     n = c["gen"]
     say(f"[pipeline] async steps={n} streams={streams}")

@@ -377,7 +377,156 @@ typedef struct {
   float scale;
   int budget_scope;  /* 0: each segment <= budget_bytes; 1: the stream's
                         segments together <= nseg * budget_bytes */
+  int rotate;        /* 1: rotate the region's K and V vectors (SVD) before
+                        channel selection and packing */
 } orc_params;
+
+/* ------------------------------------------------------------------ */
+/* SVD rotation before the per-vector channel selection ([M] Fig. 6      */
+/* caption, Stage-1: the SVD rotation matrix R of the K and of the V     */
+/* matrix, respectively, is computed and the vectors are rotated before  */
+/* the top-r elements of each are kept; Fig. 4: after the rotation the   */
+/* important elements of the cache sit in a few channels).  Reading:     */
+/*  - one R per stream and side, from the vectors of the region one call */
+/*    compresses (a rotation per segment would cost 2 x 32 KB, more than */
+/*    the byte budget of a 128-token segment);                           */
+/*  - R = the right singular vectors of the [T x 128] matrix X, i.e. the */
+/*    eigenvectors of the Gram matrix X^T X, ordered by eigenvalue       */
+/*    (largest first, ties to the lower index), found by cyclic Jacobi   */
+/*    in fp32 with every operation fixed below;                          */
+/*  - a vector x is stored as y = R^T x rounded to bf16; decode attends  */
+/*    with R_K^T q and returns R_V times the rotated output.             */
+/* ------------------------------------------------------------------ */
+#define ORC_JACOBI_SWEEPS 10
+
+static uint16_t f2bf_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+/* C[i][j] = pairwise sum of eight partial sums, partial g = fma chain over
+ * tokens g*T/8 .. (g+1)*T/8 - 1 in order of x_t[i] * x_t[j].  T % 8 == 0. */
+void orc_gram(const uint16_t* X, int T, float* C, int n_threads) {
+  const int gT = T / 8;
+#pragma omp parallel for schedule(dynamic) num_threads(n_threads)
+  for (int i = 0; i < ORC_D; ++i) {
+    for (int j = 0; j < ORC_D; ++j) {
+      float part[8];
+      for (int g = 0; g < 8; ++g) {
+        float acc = 0.0f;
+        for (int t = g * gT; t < (g + 1) * gT; ++t)
+          acc = fmaf(bf2f(X[(size_t)t * ORC_D + i]), bf2f(X[(size_t)t * ORC_D + j]), acc);
+        part[g] = acc;
+      }
+      C[i * ORC_D + j] = ((part[0] + part[1]) + (part[2] + part[3])) +
+                         ((part[4] + part[5]) + (part[6] + part[7]));
+    }
+  }
+}
+
+/* Pair k of round r of the round-robin ordering of 128 indices: index 127
+ * meets r, and r + k meets r - k (mod 127) for k = 1..63; p < q. */
+static void jacobi_pair(int r, int k, int* p, int* q) {
+  int a, b;
+  if (k == 0) {
+    a = r;
+    b = 127;
+  } else {
+    a = (r + k) % 127;
+    b = (r - k + 127) % 127;
+  }
+  *p = a < b ? a : b;
+  *q = a < b ? b : a;
+}
+
+/* Jacobi rotation that zeroes A[p][q]: tau = (A[q][q] - A[p][p]) / (2 A[p][q]),
+ * t = sign(tau) / (|tau| + sqrt(tau^2 + 1)), c = 1 / sqrt(t^2 + 1), s = t c. */
+static void jacobi_cs(float app, float aqq, float apq, float* c, float* s) {
+  if (apq == 0.0f) {
+    *c = 1.0f;
+    *s = 0.0f;
+    return;
+  }
+  const float tau = (aqq - app) / (2.0f * apq);
+  const float t = (tau >= 0.0f ? 1.0f : -1.0f) / (fabsf(tau) + sqrtf(fmaf(tau, tau, 1.0f)));
+  const float cc = 1.0f / sqrtf(fmaf(t, t, 1.0f));
+  *c = cc;
+  *s = t * cc;
+}
+
+/* Eigenvectors of the symmetric C: ORC_JACOBI_SWEEPS sweeps of 127 rounds;
+ * in a round the 64 rotations are computed from A as it stands, then
+ * applied to the rows of A, then to its columns, then to the columns of
+ * the accumulated eigenvectors V (every element pair (a, b) of index p, q
+ * becomes (fma(c, a, -(s b)), fma(s, a, c b))).  R[i][k] = V[i][order[k]]
+ * with order sorting the diagonal of A (largest first, ties to the lower
+ * index); evals[k] = that diagonal entry. */
+void orc_jacobi(const float* C, float* R, float* evals) {
+  float* A = (float*)malloc(sizeof(float) * ORC_D * ORC_D);
+  float* V = (float*)malloc(sizeof(float) * ORC_D * ORC_D);
+  memcpy(A, C, sizeof(float) * ORC_D * ORC_D);
+  for (int i = 0; i < ORC_D * ORC_D; ++i) V[i] = 0.0f;
+  for (int i = 0; i < ORC_D; ++i) V[i * ORC_D + i] = 1.0f;
+  int P[64], Q[64];
+  float cs[64], sn[64];
+  for (int sweep = 0; sweep < ORC_JACOBI_SWEEPS; ++sweep) {
+    for (int r = 0; r < 127; ++r) {
+      for (int k = 0; k < 64; ++k) {
+        jacobi_pair(r, k, &P[k], &Q[k]);
+        jacobi_cs(A[P[k] * ORC_D + P[k]], A[Q[k] * ORC_D + Q[k]], A[P[k] * ORC_D + Q[k]], &cs[k],
+                  &sn[k]);
+      }
+      for (int k = 0; k < 64; ++k) /* rows */
+        for (int j = 0; j < ORC_D; ++j) {
+          const float a = A[P[k] * ORC_D + j], b = A[Q[k] * ORC_D + j];
+          A[P[k] * ORC_D + j] = fmaf(cs[k], a, -(sn[k] * b));
+          A[Q[k] * ORC_D + j] = fmaf(sn[k], a, cs[k] * b);
+        }
+      for (int k = 0; k < 64; ++k) /* columns */
+        for (int i = 0; i < ORC_D; ++i) {
+          const float a = A[i * ORC_D + P[k]], b = A[i * ORC_D + Q[k]];
+          A[i * ORC_D + P[k]] = fmaf(cs[k], a, -(sn[k] * b));
+          A[i * ORC_D + Q[k]] = fmaf(sn[k], a, cs[k] * b);
+        }
+      for (int k = 0; k < 64; ++k) /* eigenvectors */
+        for (int i = 0; i < ORC_D; ++i) {
+          const float a = V[i * ORC_D + P[k]], b = V[i * ORC_D + Q[k]];
+          V[i * ORC_D + P[k]] = fmaf(cs[k], a, -(sn[k] * b));
+          V[i * ORC_D + Q[k]] = fmaf(sn[k], a, cs[k] * b);
+        }
+    }
+  }
+  int order[ORC_D];
+  for (int k = 0; k < ORC_D; ++k) order[k] = k;
+  for (int a = 1; a < ORC_D; ++a) { /* insertion sort: diagonal desc, index asc */
+    const int o = order[a];
+    int b = a - 1;
+    while (b >= 0 && A[order[b] * ORC_D + order[b]] < A[o * ORC_D + o]) {
+      order[b + 1] = order[b];
+      --b;
+    }
+    order[b + 1] = o;
+  }
+  for (int k = 0; k < ORC_D; ++k) {
+    evals[k] = A[order[k] * ORC_D + order[k]];
+    for (int i = 0; i < ORC_D; ++i) R[i * ORC_D + k] = V[i * ORC_D + order[k]];
+  }
+  free(A);
+  free(V);
+}
+
+/* y = R^T x rounded to bf16: y[k] = bf16(fma chain over i ascending of
+ * x[i] R[i][k]). */
+void orc_rotate(const uint16_t* X, long T, const float* R, uint16_t* Y) {
+  for (long t = 0; t < T; ++t)
+    for (int k = 0; k < ORC_D; ++k) {
+      float acc = 0.0f;
+      for (int i = 0; i < ORC_D; ++i) acc = fmaf(bf2f(X[t * ORC_D + i]), R[i * ORC_D + k], acc);
+      Y[t * ORC_D + k] = f2bf_rne(acc);
+    }
+}
 
 /* ------------------------------------------------------------------ */
 /* Per-stream byte budget ([M] abstract: compression strategies chosen   */
@@ -447,8 +596,32 @@ int orc_compress_stream(const orc_params* p, const uint16_t* K, const uint16_t* 
                         const uint16_t* Qw, const uint8_t* forced, uint8_t* packed,
                         uint64_t base_offset, orc_desc* desc, uint64_t* used_bytes,
                         float* scores_out, float* objective_out, float* m_out,
-                        float* invZ_out, int n_threads) {
+                        float* invZ_out, float* rot_out, int n_threads) {
   orc_init();
+  /* rotation: selection and packing read the rotated region vectors
+   * (scoring keeps the original keys); KS/VS index them by token - rb */
+  const uint16_t* KS = K;
+  const uint16_t* VS = V;
+  long rb = 0;
+  uint16_t *KR = NULL, *VR = NULL;
+  if (p->rotate) {
+    if (p->region_len % 8) return -1;
+    float* C = (float*)malloc(sizeof(float) * ORC_D * ORC_D);
+    float R[2][ORC_D * ORC_D], ev[ORC_D];
+    KR = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)p->region_len * ORC_D);
+    VR = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)p->region_len * ORC_D);
+    for (int side = 0; side < 2; ++side) {
+      const uint16_t* X = (side ? V : K) + (size_t)p->region_begin * ORC_D;
+      orc_gram(X, p->region_len, C, n_threads);
+      orc_jacobi(C, R[side], ev);
+      orc_rotate(X, p->region_len, R[side], side ? VR : KR);
+      if (rot_out) memcpy(rot_out + (size_t)side * ORC_D * ORC_D, R[side], sizeof(R[side]));
+    }
+    free(C);
+    KS = KR;
+    VS = VR;
+    rb = p->region_begin;
+  }
   const int S = p->S, nseg = p->region_len / p->S, nq = p->G * p->W, ns = p->n_strat;
   if (p->budget_scope && forced) return -1;
   long* bytes = (long*)malloc(sizeof(long) * (size_t)ns);
@@ -496,8 +669,8 @@ int orc_compress_stream(const orc_params* p, const uint16_t* K, const uint16_t* 
     for (int t = 0; t < S; ++t) {
       for (int u = 0; u < ncs; ++u) {
         uint8_t mk[16];
-        orc_channel_topc(K + (size_t)(t0 + t) * ORC_D, cs[u], mk, &rhoK[t * ncs + u]);
-        orc_channel_topc(V + (size_t)(t0 + t) * ORC_D, cs[u], mk, &rhoV[t * ncs + u]);
+        orc_channel_topc(KS + (size_t)(t0 - rb + t) * ORC_D, cs[u], mk, &rhoK[t * ncs + u]);
+        orc_channel_topc(VS + (size_t)(t0 - rb + t) * ORC_D, cs[u], mk, &rhoV[t * ncs + u]);
       }
     }
     for (int i = 0; i < ns; ++i) {
@@ -581,18 +754,18 @@ int orc_compress_stream(const orc_params* p, const uint16_t* K, const uint16_t* 
         orc_top_t(s + (size_t)sg * S, S, T, keep);
       size_t pos = 0;
       for (int part = 0; part < 2; ++part) { /* 0: K, 1: V */
-        const uint16_t* X = part == 0 ? K : V;
+        const uint16_t* X = part == 0 ? KS : VS;
         if (c < ORC_D) {
           for (int t = 0; t < S; ++t) {
             if (!keep[t]) continue;
             float r;
-            orc_channel_topc(X + (size_t)(t0 + t) * ORC_D, c, out + pos, &r);
+            orc_channel_topc(X + (size_t)(t0 - rb + t) * ORC_D, c, out + pos, &r);
             pos += 16;
           }
         }
         for (int t = 0; t < S; ++t) {
           if (!keep[t]) continue;
-          const uint16_t* row = X + (size_t)(t0 + t) * ORC_D;
+          const uint16_t* row = X + (size_t)(t0 - rb + t) * ORC_D;
           uint8_t mk[16];
           float r;
           if (c < ORC_D)
@@ -626,6 +799,8 @@ int orc_compress_stream(const orc_params* p, const uint16_t* K, const uint16_t* 
   free(invZ);
   free(s);
   free(bytes);
+  free(KR);
+  free(VR);
   return 0;
 }
 
@@ -643,8 +818,44 @@ int orc_compress_stream(const orc_params* p, const uint16_t* K, const uint16_t* 
  * filled so that tokens can be appended in place. */
 static int layout_tokens(const orc_desc* d) { return (d->flags & 4) ? d->seg_tokens : d->n_tok; }
 
+static void decode_core(int G, const double* qd, const uint8_t* packed, const orc_desc* desc,
+                        int n_desc, float scale, double* out, double* lse);
+
 void orc_decode_stream(int G, const uint16_t* q, const uint8_t* packed, const orc_desc* desc,
                        int n_desc, float scale, double* out, double* lse) {
+  double* qd = (double*)malloc(sizeof(double) * (size_t)G * ORC_D);
+  for (int i = 0; i < G * ORC_D; ++i) qd[i] = (double)bf2f(q[i]);
+  decode_core(G, qd, packed, desc, n_desc, scale, out, lse);
+  free(qd);
+}
+
+/* Decode over a cache stored in the rotated bases (compressed with
+ * rotation): exact attention of q' = R_K^T q over the stored vectors, then
+ * out = R_V out', all in fp64 from the fp32 matrices. */
+void orc_decode_stream_rot(int G, const uint16_t* q, const uint8_t* packed, const orc_desc* desc,
+                           int n_desc, float scale, const float* RK, const float* RV,
+                           double* out, double* lse) {
+  double* qd = (double*)calloc((size_t)G * ORC_D + 1, sizeof(double));
+  double* o1 = (double*)calloc((size_t)G * ORC_D + 1, sizeof(double));
+  for (int g = 0; g < G; ++g)
+    for (int k = 0; k < ORC_D; ++k) {
+      double acc = 0.0;
+      for (int i = 0; i < ORC_D; ++i) acc += (double)bf2f(q[g * ORC_D + i]) * (double)RK[i * ORC_D + k];
+      qd[g * ORC_D + k] = acc;
+    }
+  decode_core(G, qd, packed, desc, n_desc, scale, o1, lse);
+  for (int g = 0; g < G; ++g)
+    for (int i = 0; i < ORC_D; ++i) {
+      double acc = 0.0;
+      for (int k = 0; k < ORC_D; ++k) acc += (double)RV[i * ORC_D + k] * o1[g * ORC_D + k];
+      out[g * ORC_D + i] = acc;
+    }
+  free(qd);
+  free(o1);
+}
+
+static void decode_core(int G, const double* qd, const uint8_t* packed, const orc_desc* desc,
+                        int n_desc, float scale, double* out, double* lse) {
   long ntok = 0;
   for (int i = 0; i < n_desc; ++i) ntok += desc[i].n_tok;
   double* l = (double*)malloc(sizeof(double) * (size_t)(ntok > 0 ? ntok : 1) * (size_t)G);
@@ -667,7 +878,7 @@ void orc_decode_stream(int G, const uint16_t* q, const uint8_t* packed, const or
           uint16_t kv;
           memcpy(&kv, vals + 2 * r, 2);
           ++r;
-          acc += (double)bf2f(q[g * ORC_D + ch]) * (double)bf2f(kv);
+          acc += qd[g * ORC_D + ch] * (double)bf2f(kv);
         }
         l[j * G + g] = acc * (double)scale;
       }

@@ -47,7 +47,12 @@ def lib():
         L.orc_token2chunk.argtypes = [P, i32, i32, i32, i32, P]
         L.orc_seg_bytes.argtypes = [i32, i32, i32]
         L.orc_seg_bytes.restype = i64
-        L.orc_compress_stream.argtypes = [P, P, P, P, P, P, ctypes.c_uint64, P, P, P, P, P, P, i32]
+        L.orc_compress_stream.argtypes = [P, P, P, P, P, P, ctypes.c_uint64, P, P, P, P, P, P, P,
+                                          i32]
+        L.orc_gram.argtypes = [P, i32, P, i32]
+        L.orc_jacobi.argtypes = [P, P, P]
+        L.orc_rotate.argtypes = [P, i64, P, P]
+        L.orc_decode_stream_rot.argtypes = [i32, P, P, P, i32, f32, P, P, P, P]
         L.orc_compress_stream.restype = i32
         L.orc_decode_stream.argtypes = [i32, P, P, P, i32, f32, P, P]
         L.orc_max_threads.restype = i32
@@ -144,18 +149,20 @@ class _Params(ctypes.Structure):
                 ("strat_T", ctypes.c_void_p), ("strat_c", ctypes.c_void_p),
                 ("budget_bytes", ctypes.c_long), ("t2c_alpha", ctypes.c_int),
                 ("t2c_gamma", ctypes.c_int), ("scale", ctypes.c_float),
-                ("budget_scope", ctypes.c_int)]
+                ("budget_scope", ctypes.c_int), ("rotate", ctypes.c_int)]
 
 
 def compress_stream(K, V, Qw, *, S, strategies, budget_bytes, scale, region_begin=0,
                     region_len=None, t2c_alpha=0, t2c_gamma=0, forced=None, base_offset=0,
-                    n_threads=0, budget_scope=0):
+                    n_threads=0, budget_scope=0, rotate=False):
     """Compress one stream.
 
     K, V: [n_ctx,128] u16; Qw: [G,W,128] u16; strategies: list of (T, c).
     budget_scope 0: every segment within budget_bytes; 1: the stream's
     segments together within n_seg * budget_bytes (Lagrangian choice).
-    Returns dict(packed, desc, used, scores, objective, m, invZ).
+    rotate: the region's K and V vectors are rotated (SVD) before selection.
+    Returns dict(packed, desc, used, scores, objective, m, invZ, rot) with rot
+    [2,128,128] fp32 (R_K, R_V) when rotating.
     """
     K, V, Qw = _u16(K), _u16(V), _u16(Qw)
     n_ctx = K.shape[0]
@@ -166,7 +173,7 @@ def compress_stream(K, V, Qw, *, S, strategies, budget_bytes, scale, region_begi
     sc = np.array([c for _, c in strategies], np.int32)
     prm = _Params(n_ctx, region_begin, region_len, S, G, W, len(strategies),
                   sT.ctypes.data, sc.ctypes.data, int(budget_bytes), t2c_alpha, t2c_gamma,
-                  np.float32(scale), int(budget_scope))
+                  np.float32(scale), int(budget_scope), int(bool(rotate)))
     cap = nseg * max(seg_bytes(t, c, S) for t, c in strategies) + 16
     packed = np.zeros(cap, np.uint8)
     desc = np.zeros(nseg, DESC_DTYPE)
@@ -176,13 +183,58 @@ def compress_stream(K, V, Qw, *, S, strategies, budget_bytes, scale, region_begi
     m = np.zeros(G * W, np.float32)
     iz = np.zeros(G * W, np.float32)
     f = None if forced is None else np.ascontiguousarray(forced, np.uint8)
+    rot = np.zeros((2, 128, 128), np.float32) if rotate else None
     rc = lib().orc_compress_stream(ctypes.byref(prm), _p(K), _p(V), _p(Qw), _p(f), _p(packed),
                                    base_offset, _p(desc), _p(used), _p(scores), _p(obj), _p(m),
-                                   _p(iz), n_threads or max_threads())
+                                   _p(iz), _p(rot), n_threads or max_threads())
     if rc != 0:
         raise ValueError(f"oracle compress failed ({rc})")
     return dict(packed=packed[: int(used[0])], desc=desc, used=int(used[0]), scores=scores,
-                objective=obj, m=m, invZ=iz)
+                objective=obj, m=m, invZ=iz, rot=rot)
+
+
+def gram(X, n_threads=0):
+    """X: [T,128] u16 (T % 8 == 0) -> Gram matrix [128,128] fp32 (eight
+    fma-chain partials over consecutive token groups, summed pairwise)."""
+    X = _u16(X)
+    C = np.zeros((128, 128), np.float32)
+    lib().orc_gram(_p(X), X.shape[0], _p(C), n_threads or max_threads())
+    return C
+
+
+def jacobi(C):
+    """Symmetric C [128,128] fp32 -> (R [128,128] eigenvectors as columns,
+    eigenvalues [128], largest first), fp32 cyclic Jacobi."""
+    C = np.ascontiguousarray(C, np.float32)
+    R = np.zeros((128, 128), np.float32)
+    ev = np.zeros(128, np.float32)
+    lib().orc_jacobi(_p(C), _p(R), _p(ev))
+    return R, ev
+
+
+def rotate(X, R):
+    """X: [T,128] u16 -> R^T x per row, rounded to bf16 (u16)."""
+    X = _u16(X)
+    R = np.ascontiguousarray(R, np.float32)
+    Y = np.zeros_like(X)
+    lib().orc_rotate(_p(X), X.shape[0], _p(R), _p(Y))
+    return Y
+
+
+def decode_stream_rot(q, packed, desc, scale, RK, RV):
+    """Decode over a rotated cache: attention of R_K^T q, output R_V out'."""
+    q = _u16(q)
+    packed = np.ascontiguousarray(packed, np.uint8)
+    desc = np.ascontiguousarray(desc, DESC_DTYPE)
+    RK = np.ascontiguousarray(RK, np.float32)
+    RV = np.ascontiguousarray(RV, np.float32)
+    G = q.shape[0]
+    out = np.zeros((G, 128), np.float64)
+    lse = np.zeros(G, np.float64)
+    buf = packed if packed.size else np.zeros(16, np.uint8)
+    lib().orc_decode_stream_rot(G, _p(q), _p(buf), _p(desc), desc.size, np.float32(scale),
+                                _p(RK), _p(RV), _p(out), _p(lse))
+    return out, lse
 
 
 def decode_stream(q, packed, desc, scale):

@@ -48,7 +48,8 @@ class Params(ctypes.Structure):
                 ("packed_stream_stride", ctypes.c_uint64), ("packed_base_offset", ctypes.c_uint64),
                 ("desc_stream_stride", ctypes.c_uint32), ("max_desc_per_stream", ctypes.c_uint32),
                 ("decode_splits", ctypes.c_uint32), ("budget_scope", ctypes.c_uint32),
-                ("compress_max_waves", ctypes.c_uint32), ("reserved", ctypes.c_uint32 * 2)]
+                ("compress_max_waves", ctypes.c_uint32), ("rotate", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32 * 1)]
 
 
 class Layout(ctypes.Structure):
@@ -111,6 +112,12 @@ def lib():
                                          P, P, P]
         L.kv_select_segments.restype = ctypes.c_int
         u32, u64 = ctypes.c_uint32, ctypes.c_uint64
+        L.kv_compress_rotated.argtypes = [ctypes.POINTER(Params), P, P, P, P, P, P, P, P, P, P, P,
+                                          ctypes.c_size_t, P]
+        L.kv_compress_rotated.restype = ctypes.c_int
+        L.kv_attend_decode_rotated.argtypes = [ctypes.POINTER(Params), P, P, P, P, P, P, P, P,
+                                               ctypes.c_size_t, P]
+        L.kv_attend_decode_rotated.restype = ctypes.c_int
         L.kv_append.argtypes = [ctypes.POINTER(Params), P, P, u32, u32, u32, u64, P, P, P]
         L.kv_append.restype = ctypes.c_int
         L.kv_pipe_layout.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(PipeConfig),
@@ -142,7 +149,7 @@ class KvParams:
                  budget_bytes=0, t2c_alpha=0, t2c_gamma=0, scale=0.0, kv_stream_stride=0,
                  qw_head_stride=0, packed_stream_stride=0, packed_base_offset=0,
                  desc_stream_stride=0, max_desc_per_stream=0, decode_splits=0,
-                 budget_scope=0, compress_max_waves=0):
+                 budget_scope=0, compress_max_waves=0, rotate=0):
         strategies = list(strategies)
         self._strat = (Strategy * max(1, len(strategies)))(*[Strategy(t, c) for t, c in strategies])
         if region_len is None:
@@ -163,6 +170,7 @@ class KvParams:
         p.decode_splits = decode_splits
         p.budget_scope = budget_scope
         p.compress_max_waves = compress_max_waves
+        p.rotate = int(bool(rotate))
         self.strategies = strategies
 
     @property
@@ -198,6 +206,28 @@ def kv_compress(params, K, V, Qwin, forced, packed, desc, used_bytes, scores, ob
                            _stream())
     if st != 0:
         raise KvcError("kv_compress", st)
+
+
+def kv_compress_rotated(params, K, V, Qwin, forced, packed, desc, used_bytes, scores, objective,
+                        rot, ws):
+    """Enqueue compression with the SVD rotation (params.rotate = 1)."""
+    st = lib().kv_compress_rotated(ctypes.byref(params.p), _ptr(K), _ptr(V), _ptr(Qwin),
+                                   _ptr(forced), _ptr(packed), _ptr(desc), _ptr(used_bytes),
+                                   _ptr(scores), _ptr(objective), _ptr(rot), _ptr(ws),
+                                   ws.numel() * ws.element_size() if ws is not None else 0,
+                                   _stream())
+    if st != 0:
+        raise KvcError("kv_compress_rotated", st)
+
+
+def kv_attend_decode_rotated(params, q, packed, desc, n_desc, rot, out, lse, ws):
+    """Enqueue decode attention over a rotated cache (params.rotate = 1)."""
+    st = lib().kv_attend_decode_rotated(ctypes.byref(params.p), _ptr(q), _ptr(packed), _ptr(desc),
+                                        _ptr(n_desc), _ptr(rot), _ptr(out), _ptr(lse), _ptr(ws),
+                                        ws.numel() * ws.element_size() if ws is not None else 0,
+                                        _stream())
+    if st != 0:
+        raise KvcError("kv_attend_decode_rotated", st)
 
 
 def kv_attend_decode(params, q, packed, desc, n_desc, out, lse, ws):

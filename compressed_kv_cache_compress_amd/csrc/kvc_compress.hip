@@ -850,14 +850,38 @@ hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
                          (const float*)p.qf, (const float*)p.norm_m, (const float*)p.norm_iz,
                          p.scores, p.scores_out);
   }
+  // selection and packing read the rotated region vectors when rotating
+  const uint16_t* selK = p.K;
+  const uint16_t* selV = p.V;
+  uint64_t sel_stride = p.kv_stride;
+  int sel_begin = p.region_begin;
+  if (p.rotate) {
+    RotatePlan rp;
+    rp.K = p.K;
+    rp.V = p.V;
+    rp.kv_stride = p.kv_stride;
+    rp.region_begin = p.region_begin;
+    rp.region_len = p.region_len;
+    rp.streams = p.streams;
+    rp.gram = p.gram;
+    rp.rot = p.rot;
+    rp.YK = p.YK;
+    rp.YV = p.YV;
+    const hipError_t e = launch_rotate(rp, st);
+    if (e != hipSuccess) return e;
+    selK = p.YK;
+    selV = p.YV;
+    sel_stride = (uint64_t)p.region_len * D;
+    sel_begin = 0;
+  }
   if (p.nc > 0) {
     SelectArgs se;
-    se.K = p.K;
-    se.V = p.V;
+    se.K = selK;
+    se.V = selV;
     se.masks = p.masks;
     se.rho = p.rho;
-    se.kv_stride = p.kv_stride;
-    se.region_begin = p.region_begin;
+    se.kv_stride = sel_stride;
+    se.region_begin = sel_begin;
     se.region_len = p.region_len;
     se.nc = p.nc;
     for (int i = 0; i < MAX_NC; ++i) se.cvals[i] = p.cvals[i];
@@ -928,17 +952,17 @@ hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
   sc.S = p.S;
   hipLaunchKernelGGL(k_offsets_scan, dim3(p.streams), dim3(64), 0, st, sc);
   PackArgs pa;
-  pa.K = p.K;
-  pa.V = p.V;
+  pa.K = selK;
+  pa.V = selV;
   pa.masks = p.masks;
   pa.keep = p.keep;
   pa.desc = p.desc;
   pa.packed = p.packed;
-  pa.kv_stride = p.kv_stride;
+  pa.kv_stride = sel_stride;
   pa.pstride = p.pstride;
   pa.pbase = p.pbase;
   pa.dstride = p.dstride;
-  pa.region_begin = p.region_begin;
+  pa.region_begin = sel_begin;
   pa.region_len = p.region_len;
   pa.S = p.S;
   pa.n_seg = p.n_seg;

@@ -83,6 +83,7 @@ constexpr int WAVES = 4;
 
 struct DecodeArgs {
   const uint16_t* q;
+  const uint16_t* q_lo;  // QLO: low bf16 parts of the queries (q + q_lo ~ the fp32 query)
   const uint8_t* packed;
   const kvc_seg_desc* desc;
   const uint32_t* n_desc;
@@ -368,7 +369,10 @@ __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
   return ch;
 }
 
-template <int JG>
+// QLO: the queries come as two bf16 parts (a rotated query in fp32 split
+// into its bf16 rounding and the rounded remainder); q.k is then the sum of
+// two MFMA products, so the query keeps about 16 bits of precision.
+template <int JG, bool QLO>
 __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_decode_split(DecodeArgs a) {
   __shared__ uint2 lut[16];
   __shared__ WaveLds<JG> wl[WAVES];
@@ -399,6 +403,16 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
     u32x4_t v = {0u, 0u, 0u, 0u};
     if (hh_ok) v = *reinterpret_cast<const u32x4_t*>(qh + 8 * (4 * kk + grp));
     qa[kk] = __builtin_bit_cast(bf16x8_t, v);
+  }
+  bf16x8_t qlo[QLO ? 4 : 1];
+  if constexpr (QLO) {
+    const uint16_t* ql = a.q_lo + ((uint64_t)(b * a.hq + h * a.G + (hh_ok ? hh : 0))) * D;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (hh_ok) v = *reinterpret_cast<const u32x4_t*>(ql + 8 * (4 * kk + grp));
+      qlo[kk] = __builtin_bit_cast(bf16x8_t, v);
+    }
   }
 
   // JG == 1: O4[half][item i] = head i, channel 64*half + lane (4x4x4 MFMA);
@@ -454,6 +468,13 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
       for (int kk = 0; kk < 4; ++kk)
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], __builtin_bit_cast(bf16x8_t, kb[kk]),
                                                        sacc, 0, 0, 0);
+      if constexpr (QLO) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qlo[kk],
+                                                         __builtin_bit_cast(bf16x8_t, kb[kk]), sacc,
+                                                         0, 0, 0);
+      }
     }
     bool resc = false;
 #pragma unroll
@@ -634,9 +655,65 @@ __global__ __launch_bounds__(128) void k_decode_reduce(const float* __restrict__
   if (lse && ch == 0) lse[r] = (M + log2f(L)) * 0.69314718055994530942f;
 }
 
+// Rotated cache: the same merge, then out = R_V o' (o' = the merged output
+// in the rotated basis, fp32) before the single bf16 rounding.  R_V of
+// row r's stream is read row by row (thread ch: row ch).
+__global__ __launch_bounds__(128) void k_decode_reduce_rot(const float* __restrict__ part_ml,
+                                                           const float* __restrict__ part_acc,
+                                                           const float* __restrict__ rot,
+                                                           uint16_t* __restrict__ out,
+                                                           float* __restrict__ lse, int splits,
+                                                           int hq, int hkv) {
+  __shared__ float o1[D];
+  const int r = blockIdx.x, ch = threadIdx.x;
+  const int b = r / hq, hd = r - b * hq;
+  const int s = b * hkv + hd / (hq / hkv);
+  const float* ml = part_ml + (uint64_t)r * splits * 2;
+  float M = -INFINITY;
+  for (int sp = 0; sp < splits; ++sp) M = fmaxf(M, ml[2 * sp]);
+  if (M == -INFINITY) {  // wave-uniform for the whole block: no barrier is skipped unevenly
+    out[(uint64_t)r * D + ch] = 0;
+    if (lse && ch == 0) lse[r] = -INFINITY;
+    return;
+  }
+  float L = 0.0f, acc = 0.0f;
+  for (int sp = 0; sp < splits; ++sp) {
+    const float w = exp2f(ml[2 * sp] - M);
+    L += ml[2 * sp + 1] * w;
+    acc += part_acc[((uint64_t)r * splits + sp) * D + ch] * w;
+  }
+  o1[ch] = acc / L;
+  __syncthreads();
+  const float* RV = rot + ((uint64_t)s * 2 + 1) * D * D + (uint64_t)ch * D;
+  float o = 0.0f;
+  for (int k = 0; k < D; ++k) o = __builtin_fmaf(RV[k], o1[k], o);
+  out[(uint64_t)r * D + ch] = (uint16_t)f2bf(o);
+  if (lse && ch == 0) lse[r] = (M + log2f(L)) * 0.69314718055994530942f;
+}
+
+// Rotated queries for a rotated cache: q'[k] = fma chain over i of
+// q[i] R_K[i][k] in fp32, stored as its bf16 rounding hi and the bf16
+// rounding of the remainder lo.  grid (batch * hq), 128 threads: thread k.
+__global__ __launch_bounds__(128) void k_rotate_q(const uint16_t* __restrict__ q,
+                                                  const float* __restrict__ rot,
+                                                  uint16_t* __restrict__ qhi,
+                                                  uint16_t* __restrict__ qlo, int hq, int hkv) {
+  const int r = blockIdx.x, k = threadIdx.x;
+  const int b = r / hq, hd = r - b * hq;
+  const int s = b * hkv + hd / (hq / hkv);
+  const float* RK = rot + (uint64_t)s * 2 * D * D;
+  const uint16_t* qr = q + (uint64_t)r * D;
+  float acc = 0.0f;
+  for (int i = 0; i < D; ++i) acc = __builtin_fmaf(bf2f(qr[i]), RK[i * D + k], acc);
+  const uint32_t hi = f2bf(acc);
+  qhi[(uint64_t)r * D + k] = (uint16_t)hi;
+  qlo[(uint64_t)r * D + k] = (uint16_t)f2bf(acc - bf2f(hi));
+}
+
 hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
   DecodeArgs a;
-  a.q = p.q;
+  a.q = p.rot ? p.qhi : p.q;
+  a.q_lo = p.rot ? p.qlo : nullptr;
   a.packed = p.packed;
   a.desc = p.desc;
   a.n_desc = p.n_desc;
@@ -650,12 +727,25 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
   a.items = p.streams * p.splits;
   a.sl2 = p.scale * KVC_LOG2E;
   const dim3 grid((a.items + WAVES - 1) / WAVES);
+  if (p.rot) {
+    hipLaunchKernelGGL(k_rotate_q, dim3(p.batch * p.hq), dim3(128), 0, st, p.q, p.rot, p.qhi,
+                       p.qlo, p.hq, p.hkv);
+    if (p.G <= 4)
+      hipLaunchKernelGGL((k_decode_split<1, true>), grid, dim3(64 * WAVES), 0, st, a);
+    else if (p.G <= 8)
+      hipLaunchKernelGGL((k_decode_split<2, true>), grid, dim3(64 * WAVES), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_decode_split<4, true>), grid, dim3(64 * WAVES), 0, st, a);
+    hipLaunchKernelGGL(k_decode_reduce_rot, dim3(p.batch * p.hq), dim3(128), 0, st, p.part_ml,
+                       p.part_acc, p.rot, p.out, p.lse, p.splits, p.hq, p.hkv);
+    return hipGetLastError();
+  }
   if (p.G <= 4)
-    hipLaunchKernelGGL((k_decode_split<1>), grid, dim3(64 * WAVES), 0, st, a);
+    hipLaunchKernelGGL((k_decode_split<1, false>), grid, dim3(64 * WAVES), 0, st, a);
   else if (p.G <= 8)
-    hipLaunchKernelGGL((k_decode_split<2>), grid, dim3(64 * WAVES), 0, st, a);
+    hipLaunchKernelGGL((k_decode_split<2, false>), grid, dim3(64 * WAVES), 0, st, a);
   else
-    hipLaunchKernelGGL((k_decode_split<4>), grid, dim3(64 * WAVES), 0, st, a);
+    hipLaunchKernelGGL((k_decode_split<4, false>), grid, dim3(64 * WAVES), 0, st, a);
   hipLaunchKernelGGL(k_decode_reduce, dim3(p.batch * p.hq), dim3(128), 0, st, p.part_ml, p.part_acc,
                      p.out, p.lse, p.splits);
   return hipGetLastError();

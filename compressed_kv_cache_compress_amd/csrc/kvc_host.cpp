@@ -50,6 +50,7 @@ kvc_status compress_layout(const kvc_params* p, const Shape& sh, kvc_layout* L, 
   if (p->n_strategies == 0 || p->n_strategies > KVC_MAX_STRATEGIES || !p->strategies)
     return KVC_E_INVALID;
   if (p->budget_scope > KVC_BUDGET_STREAM) return KVC_E_INVALID;
+  if (p->rotate > 1) return KVC_E_INVALID;
   const bool stream_scope = p->budget_scope == KVC_BUDGET_STREAM;
   const uint32_t S = p->seg_tokens;
   if (!pow2(S) || S < 16 || S > 256) return KVC_E_INVALID;
@@ -129,6 +130,11 @@ kvc_status compress_layout(const kvc_params* p, const Shape& sh, kvc_layout* L, 
     ws += align_up((uint64_t)sh.streams * n_seg * p->n_strategies * ((S + 31) / 32) * 4, kAlign);
     ws += align_up((uint64_t)sh.streams * n_seg * p->n_strategies * 4, kAlign);
   }
+  // rotation: partial Gram matrices and the rotated region vectors
+  if (p->rotate) {
+    ws += align_up((uint64_t)sh.streams * 2 * 8 * KVC_HEAD_DIM * KVC_HEAD_DIM * 4, kAlign);
+    ws += 2 * align_up((uint64_t)sh.streams * p->region_len * KVC_HEAD_DIM * 2, kAlign);
+  }
   L->compress_ws_bytes = ws;
   return nfeas ? KVC_OK : KVC_E_BUDGET;
 }
@@ -151,6 +157,9 @@ void decode_layout(const kvc_params* p, const Shape& sh, uint32_t maxd, kvc_layo
   L->decode_splits = splits;
   const uint64_t rows = (uint64_t)sh.batch * sh.hq * splits;
   L->decode_ws_bytes = align_up(rows * 2 * 4, kAlign) + align_up(rows * KVC_HEAD_DIM * 4, kAlign);
+  // rotated cache: the rotated queries' two bf16 parts
+  if (p->rotate)
+    L->decode_ws_bytes += 2 * align_up((uint64_t)sh.batch * sh.hq * KVC_HEAD_DIM * 2, kAlign);
 }
 
 uint32_t decode_maxd(const kvc_params* p) {
@@ -196,13 +205,20 @@ kvc_status kv_layout_query(const kvc_params* p, kvc_layout* out) {
   return cs;
 }
 
-kvc_status kv_compress(const kvc_params* p, const uint16_t* K, const uint16_t* V,
-                       const uint16_t* Qwin, const uint8_t* forced_strategy, void* packed,
-                       kvc_seg_desc* desc, uint64_t* used_bytes, float* scores, float* objective,
-                       void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+kvc_status compress_impl(const kvc_params* p, const uint16_t* K, const uint16_t* V,
+                         const uint16_t* Qwin, const uint8_t* forced_strategy, void* packed,
+                         kvc_seg_desc* desc, uint64_t* used_bytes, float* scores,
+                         float* objective, float* rot, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
   Shape sh;
   kvc_status st = check_shape(p, &sh);
   if (st != KVC_OK) return st;
+  if ((p->rotate != 0) != (rot != nullptr)) return KVC_E_INVALID;
+  if (!aligned16(rot)) return KVC_E_ALIGN;
   kvc_layout L;
   std::memset(&L, 0, sizeof L);
   CompressPlan c;
@@ -292,17 +308,76 @@ kvc_status kv_compress(const kvc_params* p, const uint16_t* K, const uint16_t* V
         take(S64 * c.n_seg * (uint64_t)c.n_strat * ((c.S + 31) / 32) * 4));
     c.J_all = reinterpret_cast<float*>(take(S64 * c.n_seg * (uint64_t)c.n_strat * 4));
   }
+  c.rotate = p->rotate != 0;
+  c.rot = rot;
+  c.gram = nullptr;
+  c.YK = c.YV = nullptr;
+  if (c.rotate) {
+    c.gram = reinterpret_cast<float*>(take(S64 * 2 * 8 * D * D * 4));
+    c.YK = reinterpret_cast<uint16_t*>(take(S64 * c.region_len * D * 2));
+    c.YV = reinterpret_cast<uint16_t*>(take(S64 * c.region_len * D * 2));
+  }
   if (launch_compress(c, stream) != hipSuccess) return KVC_E_HIP;
   return KVC_OK;
+}
+
+kvc_status decode_impl(const kvc_params* p, const uint16_t* q, const void* packed,
+                       const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
+                       const float* rot, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+}  // namespace
+
+extern "C" {
+
+kvc_status kv_compress(const kvc_params* p, const uint16_t* K, const uint16_t* V,
+                       const uint16_t* Qwin, const uint8_t* forced_strategy, void* packed,
+                       kvc_seg_desc* desc, uint64_t* used_bytes, float* scores, float* objective,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (p && p->struct_size == sizeof(kvc_params) && p->rotate) return KVC_E_INVALID;
+  return compress_impl(p, K, V, Qwin, forced_strategy, packed, desc, used_bytes, scores,
+                       objective, nullptr, ws, ws_bytes, stream);
+}
+
+kvc_status kv_compress_rotated(const kvc_params* p, const uint16_t* K, const uint16_t* V,
+                               const uint16_t* Qwin, const uint8_t* forced_strategy, void* packed,
+                               kvc_seg_desc* desc, uint64_t* used_bytes, float* scores,
+                               float* objective, float* rot, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  if (!p || p->struct_size != sizeof(kvc_params) || p->rotate != 1 || !rot) return KVC_E_INVALID;
+  return compress_impl(p, K, V, Qwin, forced_strategy, packed, desc, used_bytes, scores,
+                       objective, rot, ws, ws_bytes, stream);
 }
 
 kvc_status kv_attend_decode(const kvc_params* p, const uint16_t* q, const void* packed,
                             const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
                             uint16_t* out, float* lse, void* ws, size_t ws_bytes,
                             hipStream_t stream) {
+  if (p && p->struct_size == sizeof(kvc_params) && p->rotate) return KVC_E_INVALID;
+  return decode_impl(p, q, packed, desc, n_desc_per_stream, nullptr, out, lse, ws, ws_bytes,
+                     stream);
+}
+
+kvc_status kv_attend_decode_rotated(const kvc_params* p, const uint16_t* q, const void* packed,
+                                    const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
+                                    const float* rot, uint16_t* out, float* lse, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  if (!p || p->struct_size != sizeof(kvc_params) || p->rotate != 1 || !rot) return KVC_E_INVALID;
+  return decode_impl(p, q, packed, desc, n_desc_per_stream, rot, out, lse, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+kvc_status decode_impl(const kvc_params* p, const uint16_t* q, const void* packed,
+                       const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
+                       const float* rot, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
   Shape sh;
   kvc_status st = check_shape(p, &sh);
   if (st != KVC_OK) return st;
+  if (!aligned16(rot)) return KVC_E_ALIGN;
   const uint32_t maxd = decode_maxd(p);
   if (maxd == 0 || !q || !out || !desc || !packed) return KVC_E_INVALID;
   if (!aligned16(q) || !aligned16(packed) || !aligned16(desc) || !aligned16(out) || !aligned16(ws))
@@ -327,11 +402,25 @@ kvc_status kv_attend_decode(const kvc_params* p, const uint16_t* q, const void* 
   d.out = out;
   d.lse = lse;
   const uint64_t rows = (uint64_t)sh.batch * sh.hq * d.splits;
-  d.part_ml = static_cast<float*>(ws);
-  d.part_acc = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up(rows * 2 * 4, kAlign));
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  d.part_ml = reinterpret_cast<float*>(w);
+  w += align_up(rows * 2 * 4, kAlign);
+  d.part_acc = reinterpret_cast<float*>(w);
+  w += align_up(rows * KVC_HEAD_DIM * 4, kAlign);
+  d.rot = rot;
+  d.qhi = d.qlo = nullptr;
+  if (rot) {
+    const uint64_t qb = align_up((uint64_t)sh.batch * sh.hq * KVC_HEAD_DIM * 2, kAlign);
+    d.qhi = reinterpret_cast<uint16_t*>(w);
+    d.qlo = reinterpret_cast<uint16_t*>(w + qb);
+  }
   if (launch_decode(d, stream) != hipSuccess) return KVC_E_HIP;
   return KVC_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 kvc_status kv_summarize(const kvc_params* p, const void* packed, const kvc_seg_desc* desc,
                         const uint32_t* n_desc_per_stream, uint16_t* summary, hipStream_t stream) {

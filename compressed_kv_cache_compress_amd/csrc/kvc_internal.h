@@ -48,6 +48,20 @@ struct CompressPlan {
   uint32_t seg_bytes[KVC_MAX_STRATEGIES];
   uint32_t* keep_all;     // [streams][n_seg][n_strat][S/32]
   float* J_all;           // [streams][n_seg][n_strat]
+  // SVD rotation before channel selection (kvc_rotate.hip)
+  bool rotate;
+  float* rot;             // [streams][2][128][128] output: R_K, R_V
+  float* gram;            // [streams][2][8][128][128] partial Gram matrices
+  uint16_t *YK, *YV;      // [streams][region_len][128] rotated region vectors
+};
+
+struct RotatePlan {
+  const uint16_t *K, *V;
+  uint64_t kv_stride;
+  int region_begin, region_len, streams;
+  float* gram;
+  float* rot;
+  uint16_t *YK, *YV;
 };
 
 struct DecodePlan {
@@ -60,6 +74,10 @@ struct DecodePlan {
   uint16_t* out;
   float* lse;
   float *part_ml, *part_acc;
+  // rotated cache (null when not rotated): R_K, R_V per stream and the
+  // rotated queries' bf16 parts in the workspace
+  const float* rot;
+  uint16_t *qhi, *qlo;
 };
 
 // Query-aware segment selection (kvc_select.hip).
@@ -112,6 +130,7 @@ struct ClearPlan {
 };
 
 hipError_t launch_compress(const CompressPlan& p, hipStream_t st);
+hipError_t launch_rotate(const RotatePlan& p, hipStream_t st);
 hipError_t launch_append(const AppendPlan& p, hipStream_t st);
 hipError_t launch_switch(const SwitchPlan& p, hipStream_t st);
 hipError_t launch_clear(const ClearPlan& p, hipStream_t st);

@@ -7,8 +7,8 @@ data except to allocate it.
 """
 import torch
 
-from . import (DESC_DTYPE, KvParams, kv_attend_decode, kv_compress, kv_layout_query,
-               kv_select_segments, kv_summarize)
+from . import (DESC_DTYPE, KvParams, kv_attend_decode, kv_attend_decode_rotated, kv_compress,
+               kv_compress_rotated, kv_layout_query, kv_select_segments, kv_summarize)
 
 
 def _u8(n, device):
@@ -23,10 +23,11 @@ def _as_u16(t):
 class Compressed:
     """Result of compress(): packed bytes, descriptors and optional outputs."""
 
-    def __init__(self, params, layout, packed, desc, used, scores, objective):
+    def __init__(self, params, layout, packed, desc, used, scores, objective, rot=None):
         self.params, self.layout = params, layout
         self.packed, self.desc, self.used = packed, desc, used
         self.scores, self.objective = scores, objective
+        self.rot = rot  # [streams, 2, 128, 128] fp32 when compressed with rotation
 
     @property
     def n_seg(self):
@@ -47,7 +48,8 @@ def compress(K, V, Qw, *, seg_tokens, strategies, budget_bytes, region_begin=0, 
              t2c_alpha=0, t2c_gamma=0, scale=0.0, forced=None, want_scores=False,
              want_objective=False, ws=None, packed=None, desc=None, n_ctx=None,
              kv_stream_stride=0, qw_head_stride=0, packed_stream_stride=0, packed_base_offset=0,
-             desc_stream_stride=0, n_q_heads=None, budget_scope=0, compress_max_waves=0):
+             desc_stream_stride=0, n_q_heads=None, budget_scope=0, compress_max_waves=0,
+             rotate=False):
     """K, V: [B, Hkv, N, 128] bf16 (or strided views described by the stride
     arguments); Qw: [B, Hq, W, 128] bf16 or None.  budget_scope 1 shares
     n_seg * budget_bytes among a stream's segments."""
@@ -61,7 +63,8 @@ def compress(K, V, Qw, *, seg_tokens, strategies, budget_bytes, region_begin=0, 
                  kv_stream_stride=kv_stream_stride, qw_head_stride=qw_head_stride,
                  packed_stream_stride=packed_stream_stride,
                  packed_base_offset=packed_base_offset, desc_stream_stride=desc_stream_stride,
-                 budget_scope=budget_scope, compress_max_waves=compress_max_waves)
+                 budget_scope=budget_scope, compress_max_waves=compress_max_waves,
+                 rotate=rotate)
     _, L = kv_layout_query(p)
     dev = K.device
     streams = B * Hkv
@@ -76,8 +79,15 @@ def compress(K, V, Qw, *, seg_tokens, strategies, budget_bytes, region_begin=0, 
                  if want_objective else None)
     if ws is None or ws.numel() < L.compress_ws_bytes:
         ws = _u8(L.compress_ws_bytes, dev)
-    kv_compress(p, _as_u16(K), _as_u16(V), Qw, forced, packed, desc, used, scores, objective, ws)
-    return Compressed(p, L, packed, desc, used, scores, objective)
+    rot = None
+    if rotate:
+        rot = torch.empty((B * Hkv, 2, 128, 128), dtype=torch.float32, device=dev)
+        kv_compress_rotated(p, _as_u16(K), _as_u16(V), Qw, forced, packed, desc, used, scores,
+                            objective, rot, ws)
+    else:
+        kv_compress(p, _as_u16(K), _as_u16(V), Qw, forced, packed, desc, used, scores, objective,
+                    ws)
+    return Compressed(p, L, packed, desc, used, scores, objective, rot)
 
 
 def decode_params(*, batch, n_q_heads, n_kv_heads, max_desc_per_stream, decode_splits=0,
@@ -88,12 +98,15 @@ def decode_params(*, batch, n_q_heads, n_kv_heads, max_desc_per_stream, decode_s
 
 
 def decode(q, packed, desc, *, n_kv_heads, max_desc_per_stream, n_desc=None, decode_splits=0,
-           scale=0.0, want_lse=True, out=None, lse=None, ws=None, params=None):
-    """q: [B, Hq, 128] bf16 -> (out [B, Hq, 128] bf16, lse [B, Hq] fp32 or None)."""
+           scale=0.0, want_lse=True, out=None, lse=None, ws=None, params=None, rot=None):
+    """q: [B, Hq, 128] bf16 -> (out [B, Hq, 128] bf16, lse [B, Hq] fp32 or None).
+    rot: the rotations of a cache compressed with rotation."""
     B, Hq = q.shape[0], q.shape[1]
     p = params or decode_params(batch=B, n_q_heads=Hq, n_kv_heads=n_kv_heads,
                                 max_desc_per_stream=max_desc_per_stream,
                                 decode_splits=decode_splits, scale=scale)
+    if rot is not None:
+        p.p.rotate = 1
     if ws is None:
         _, L = kv_layout_query(p)
         ws = _u8(L.decode_ws_bytes, q.device)
@@ -101,7 +114,10 @@ def decode(q, packed, desc, *, n_kv_heads, max_desc_per_stream, n_desc=None, dec
         out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    kv_attend_decode(p, q, packed, desc, n_desc, out, lse, ws)
+    if rot is not None:
+        kv_attend_decode_rotated(p, q, packed, desc, n_desc, rot, out, lse, ws)
+    else:
+        kv_attend_decode(p, q, packed, desc, n_desc, out, lse, ws)
     return out, lse
 
 

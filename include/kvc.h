@@ -106,7 +106,10 @@ typedef struct {
                                     workgroup then walks several work units): keeps a
                                     compression that runs beside decode to a share of the
                                     GPU; results do not depend on it */
-  uint32_t reserved[2];
+  uint32_t rotate;               /* 1: SVD rotation before channel selection (calls
+                                    kv_compress_rotated / kv_attend_decode_rotated; sizes
+                                    their workspaces); 0: none */
+  uint32_t reserved[1];
 } kvc_params;
 
 /* budget_scope values.
@@ -208,6 +211,33 @@ kvc_status kv_compress(const kvc_params* p, const uint16_t* K, const uint16_t* V
                        kvc_seg_desc* desc, uint64_t* used_bytes, float* scores, float* objective,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Compression with an SVD rotation before the channel selection (MosaicKV
+ * review page: Fig. 6 caption, Stage-1 -- the rotation matrix R of the K and
+ * of the V matrix from their SVD, the vectors rotated before the top-r
+ * elements of each are kept; Fig. 4 -- after the rotation the important
+ * elements concentrate in a few channels).  As kv_compress (p->rotate = 1),
+ * and per stream:
+ *  1. R_K, R_V: eigenvectors of the Gram matrices X^T X of the region's K
+ *     and V vectors, ordered by eigenvalue (largest first, ties to the lower
+ *     index).  The Gram matrix is the pairwise sum of eight fp32 fma chains
+ *     over consecutive token groups; the eigenvectors come from 10 sweeps of
+ *     cyclic Jacobi in fp32 (round-robin pairing, each round's rotations
+ *     computed from the matrix as it stands, then applied to its rows, its
+ *     columns and the eigenvector columns), so R is reproducible bit for bit.
+ *  2. Every region vector x becomes y = R^T x (fp32 fma chain over input
+ *     channels, rounded to bf16); channel selection, the objective and the
+ *     packed values use y.  Window scoring uses the original keys.
+ *  rot   device [streams][2][128][128] fp32, written: R_K then R_V (row i,
+ *        column k = component i of the k-th eigenvector).
+ * One R per stream and side serves the whole region: a rotation per segment
+ * would cost more bytes than a compressed segment is allowed.  Decode the
+ * result with kv_attend_decode_rotated. */
+kvc_status kv_compress_rotated(const kvc_params* p, const uint16_t* K, const uint16_t* V,
+                               const uint16_t* Qwin, const uint8_t* forced_strategy, void* packed,
+                               kvc_seg_desc* desc, uint64_t* used_bytes, float* scores,
+                               float* objective, float* rot, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
 /* Decode attention of one query per q head over every stream's compressed
  * segments (MosaicKV Fig. 6 caption, PackedAttention): softmax over all kept
  * tokens of the stream's descriptors; a dropped channel contributes 0 to
@@ -228,6 +258,20 @@ kvc_status kv_attend_decode(const kvc_params* p, const uint16_t* q, const void* 
                             const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
                             uint16_t* out, float* lse, void* ws, size_t ws_bytes,
                             hipStream_t stream);
+
+/* Decode over a cache whose every descriptor of a stream holds vectors
+ * rotated by that stream's R (kv_compress_rotated; p->rotate = 1): each
+ * query becomes q' = R_K^T q (fp32, passed to the score product as its bf16
+ * rounding plus the bf16 rounding of the remainder, so about 16 bits of it
+ * survive), attention runs as in kv_attend_decode, and the output is R_V
+ * times the merged rotated output, in fp32, before its bf16 rounding.  rot
+ * as written by kv_compress_rotated; lse as for kv_attend_decode (the
+ * rotation does not change the logits).  Workspace from kv_layout_query
+ * with p->rotate = 1. */
+kvc_status kv_attend_decode_rotated(const kvc_params* p, const uint16_t* q, const void* packed,
+                                    const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
+                                    const float* rot, uint16_t* out, float* lse, void* ws,
+                                    size_t ws_bytes, hipStream_t stream);
 
 /* Query-aware segment selection before decode attention (MosaicKV review
  * page: Fig. 6 caption, stage 2 runs during the decode stage before each

@@ -520,6 +520,7 @@ void orc_jacobi(const float* C, float* R, float* evals) {
 /* y = R^T x rounded to bf16: y[k] = bf16(fma chain over i ascending of
  * x[i] R[i][k]). */
 void orc_rotate(const uint16_t* X, long T, const float* R, uint16_t* Y) {
+#pragma omp parallel for schedule(static)
   for (long t = 0; t < T; ++t)
     for (int k = 0; k < ORC_D; ++k) {
       float acc = 0.0f;

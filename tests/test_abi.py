@@ -313,3 +313,45 @@ def test_append_and_pipe_validate_before_launch(monkeypatch):
     assert st == -1 and not h.value
     assert L_.kv_pipe_step(None, None, None, 1, 0, None, None, None, None, None, None, None) == -1
     assert L_.kv_pipe_destroy(None) == 0
+
+
+def test_rotation_entry_points_validate(monkeypatch):
+    """rotate = 1 needs the rotated entry points (and they need it), a rot
+    buffer, and larger workspaces; everything is rejected before a launch."""
+    monkeypatch.setattr(kvc, "_stream", lambda: ctypes.c_void_p(0))
+    p0 = _params("batched128k")
+    p1 = _params("batched128k", rotate=1)
+    _, L0 = kvc.kv_layout_query(p0)
+    _, L1 = kvc.kv_layout_query(p1)
+    c = gen.CONFIGS["batched128k"]
+    streams = c["B"] * c["Hkv"]
+    extra = streams * 2 * 8 * 128 * 128 * 4 + 2 * streams * c["N"] * 256
+    assert L1.compress_ws_bytes >= L0.compress_ws_bytes + extra
+    d0 = kvc.KvParams(batch=2, n_q_heads=8, n_kv_heads=2, max_desc_per_stream=8)
+    d1 = kvc.KvParams(batch=2, n_q_heads=8, n_kv_heads=2, max_desc_per_stream=8, rotate=1)
+    _, D0 = kvc.kv_layout_query(d0)
+    _, D1 = kvc.kv_layout_query(d1)
+    assert D1.decode_ws_bytes >= D0.decode_ws_bytes + 2 * 2 * 8 * 128 * 2
+    a = _Fake(0x70000)
+    t = _params("tiny", rotate=1)
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_compress(t, a, a, a, None, a, a, None, None, None, a)
+    assert e.value.status == -1
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_compress_rotated(_params("tiny"), a, a, a, None, a, a, None, None, None, a, a)
+    assert e.value.status == -1
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_compress_rotated(t, a, a, a, None, a, a, None, None, None, None, a)
+    assert e.value.status == -1
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_compress_rotated(t, a, a, a, None, a, a, None, None, None, _Fake(0x70004), a)
+    assert e.value.status == -5
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_attend_decode(d1, a, a, a, None, a, None, a)
+    assert e.value.status == -1
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_attend_decode_rotated(d0, a, a, a, None, a, a, None, a)
+    assert e.value.status == -1
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kv_attend_decode_rotated(d1, a, a, a, None, a, a, None, _Fake(0x70000, 64))
+    assert e.value.status == -4

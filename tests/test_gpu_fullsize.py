@@ -17,7 +17,7 @@ from oracle import oracle as O
 pytestmark = pytest.mark.gpu
 
 
-def _sampled(cfg, streams_to_check, budget_scope=0):
+def _sampled(cfg, streams_to_check, budget_scope=0, rotate=False):
     c = gen.CONFIGS[cfg]
     S = c["S"]
     strat = gen.table9(S)
@@ -27,9 +27,9 @@ def _sampled(cfg, streams_to_check, budget_scope=0):
     say(f"[fullsize] {cfg}: kv_compress + kv_attend_decode")
     r = runtime.compress(w["K"], w["V"], w["Qw"], seg_tokens=S, strategies=strat,
                          budget_bytes=budget, scale=float(SCALE), want_scores=True,
-                         budget_scope=budget_scope)
+                         budget_scope=budget_scope, rotate=rotate)
     out, lse = runtime.decode(w["q"], r.packed, r.desc, n_kv_heads=c["Hkv"],
-                              max_desc_per_stream=r.n_seg, scale=float(SCALE))
+                              max_desc_per_stream=r.n_seg, scale=float(SCALE), rot=r.rot)
     torch.cuda.synchronize()
     desc = r.desc_host()
     used = r.used.cpu().numpy()
@@ -51,7 +51,9 @@ def _sampled(cfg, streams_to_check, budget_scope=0):
         Ks, Vs = gen.u16(w["K"][b, h]), gen.u16(w["V"][b, h])
         Qs = gen.u16(w["Qw"][b, h * G:(h + 1) * G])
         o = O.compress_stream(Ks, Vs, Qs, S=S, strategies=strat, budget_bytes=budget, scale=SCALE,
-                              base_offset=s * cap, budget_scope=budget_scope)
+                              base_offset=s * cap, budget_scope=budget_scope, rotate=rotate)
+        if rotate:
+            assert np.array_equal(r.rot[s].cpu().numpy().view(np.uint32), o["rot"].view(np.uint32))
         assert np.array_equal(r.scores[s].cpu().numpy().view(np.uint32), o["scores"].view(np.uint32))
         assert np.array_equal(desc[s].view(np.uint8), o["desc"].view(np.uint8))
         assert used[s] == o["used"]
@@ -60,7 +62,10 @@ def _sampled(cfg, streams_to_check, budget_scope=0):
         q = gen.u16(w["q"][b, h * G:(h + 1) * G])
         local = o["desc"].copy()
         local["offset"] -= s * cap
-        ref, rlse = O.decode_stream(q, o["packed"], local, SCALE)
+        if rotate:
+            ref, rlse = O.decode_stream_rot(q, o["packed"], local, SCALE, o["rot"][0], o["rot"][1])
+        else:
+            ref, rlse = O.decode_stream(q, o["packed"], local, SCALE)
         check_attention(out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G], ref, rlse,
                         f"{cfg} stream {s}")
     del w, r, packed
@@ -78,6 +83,11 @@ def test_fullsize_batched128k():
 def test_fullsize_batched128k_stream_budget():
     """The same workload with the budget shared by each stream's segments."""
     _sampled("batched128k", [3, 120], budget_scope=1)
+
+
+def test_fullsize_batched128k_rotated():
+    """The same workload with the SVD rotation before channel selection."""
+    _sampled("batched128k", [5, 100], rotate=True)
 
 
 def test_fullsize_million():

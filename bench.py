@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--pipe-steps", type=int, default=512,
                     help="Kara generation steps through the compression pipeline, timed blocking "
                          "and asynchronous beside the headline (0 = off)")
+    ap.add_argument("--no-rotate", action="store_true",
+                    help="skip the SVD-rotation measurement beside the headline")
     ap.add_argument("--no-stream-budget", action="store_true",
                     help="skip the per-stream budget measurement beside the headline")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "decode_batched128k_traffic.md"),
@@ -240,6 +242,57 @@ def bench_pipeline(a, kvc, stream):
             "async": runs["async"], "async_capped": dict(runs["async_capped"],
                                                          event_max_waves=PIPE_EVENT_WAVES),
             "identical_final_cache": same}
+
+
+def bench_rotation(a, kvc, K, V, Qw, q, B, Hq, Hkv, N, S, W, strategies, budget, scale, stream,
+                   plain_objective, plain_desc, steps=3):
+    """The same workload compressed with the SVD rotation before channel
+    selection (kv_compress_rotated) and decoded over the rotated cache
+    (kv_attend_decode_rotated): compress and decode times with HIP events on
+    the launch stream, and the objective (attention mass kept, weighted by
+    the vector energy kept) of the chosen strategies against the plain run."""
+    p = kvc.KvParams(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, n_ctx=N, seg_tokens=S, n_win=W,
+                     strategies=strategies, budget_bytes=budget, scale=float(scale), rotate=1)
+    _, L = kvc.kv_layout_query(p)
+    dev = q.device
+    streams = B * Hkv
+    packed = torch.empty(L.packed_bytes_max, dtype=torch.uint8, device=dev)
+    desc = torch.zeros(streams * L.n_seg * 16, dtype=torch.uint8, device=dev)
+    used = torch.zeros(streams, dtype=torch.int64, device=dev)
+    obj = torch.empty((streams, L.n_seg, len(strategies)), dtype=torch.float32, device=dev)
+    rot = torch.empty((streams, 2, 128, 128), dtype=torch.float32, device=dev)
+    cws = torch.empty(L.compress_ws_bytes, dtype=torch.uint8, device=dev)
+    dws = torch.empty(L.decode_ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(steps)]
+    kvc.kv_compress_rotated(p, K, V, Qw, None, packed, desc, used, None, obj, rot, cws)
+    for e in ev:
+        e[0].record(stream)
+        kvc.kv_compress_rotated(p, K, V, Qw, None, packed, desc, used, None, None, rot, cws)
+        e[1].record(stream)
+    dv = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(20)]
+    for i in range(23):
+        e = dv[i - 3] if i >= 3 else None
+        if e:
+            e[0].record(stream)
+        kvc.kv_attend_decode_rotated(p, q, packed, desc, None, rot, out, None, dws)
+        if e:
+            e[1].record(stream)
+    torch.cuda.synchronize()
+    dh = desc.cpu().numpy().view(kvc.DESC_DTYPE).reshape(streams, L.n_seg)
+    oh = obj.cpu().numpy()
+    chosen = np.take_along_axis(oh, dh["strategy"].astype(np.int64)[..., None], axis=2)[..., 0]
+    pc = np.take_along_axis(plain_objective, plain_desc["strategy"].astype(np.int64)[..., None],
+                            axis=2)[..., 0]
+    t_dec = float(np.mean([e[0].elapsed_time(e[1]) for e in dv])) * 1e-3
+    alg = algorithmic_decode_bytes(dh.ravel(), S, B, Hq, L.decode_splits)
+    return {"compress_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
+            "decode_us": t_dec * 1e6, "kv_tokens_per_s": B * N / t_dec,
+            "achieved_GBs": alg / t_dec / 1e9, "packed_bytes": int(used.sum().item()),
+            "strategy_histogram": np.bincount(dh["strategy"].ravel(),
+                                              minlength=len(strategies)).tolist(),
+            "objective_mean_rotated": float(chosen.mean()),
+            "objective_mean_plain": float(pc.mean())}
 
 
 def bench_stream_budget(a, kvc, K, V, Qw, q, B, Hq, Hkv, N, S, W, strategies, budget, scale,
@@ -423,6 +476,17 @@ def main():
     if not a.no_stream_budget:
         sbud = bench_stream_budget(a, kvc, K, V, Qw, q, B, Hq, Hkv, N, S, W, strategies, budget,
                                    scale, stream)
+    rotation = None
+    if not a.no_rotate:
+        print("[bench] rotation ...", file=sys.stderr, flush=True)
+        pobj = torch.empty((B * Hkv, L.n_seg, len(strategies)), dtype=torch.float32, device=dev)
+        kvc.kv_compress(p, K, V, Qw, None, packed, desc, used, None, pobj, cws)
+        torch.cuda.synchronize()
+        rotation = bench_rotation(a, kvc, K, V, Qw, q, B, Hq, Hkv, N, S, W, strategies, budget,
+                                  scale, stream, pobj.cpu().numpy(),
+                                  desc.cpu().numpy().view(kvc.DESC_DTYPE).reshape(B * Hkv, -1))
+        del pobj
+        torch.cuda.empty_cache()
     stage2 = None
     if a.select_pct > 0:
         stage2 = bench_stage2(a, kvc, p, L, q, packed, desc, B, Hq, Hkv, N, stream)
@@ -469,6 +533,8 @@ def main():
     }
     if stage2 is not None:
         res["stage2"] = stage2
+    if rotation is not None:
+        res["rotation"] = rotation
     if sbud is not None:
         res["stream_budget"] = sbud
     wc = {k: (v[:1].cpu() if torch.is_tensor(v) else v) for k, v in w.items()}

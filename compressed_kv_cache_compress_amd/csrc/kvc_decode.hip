@@ -371,7 +371,11 @@ __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
 
 // QLO: the queries come as two bf16 parts (a rotated query in fp32 split
 // into its bf16 rounding and the rounded remainder); q.k is then the sum of
-// two MFMA products, so the query keeps about 16 bits of precision.
+// two MFMA products, so the query keeps about 16 bits of precision.  For
+// groups of up to 4 heads the low part of head h takes the otherwise empty
+// A-row 4h + 1, so its product lands in accumulator item 1 of the lanes that
+// hold head h in item 0: no extra MFMA and no extra registers.  Larger
+// groups run a second set of MFMAs.
 template <int JG, bool QLO>
 __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_decode_split(DecodeArgs a) {
   __shared__ uint2 lut[16];
@@ -393,10 +397,14 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   WaveLds<JG>& L = wl[wv];
   for (int i = lane; i < 2 * 4 * JG * CT; i += 64) (&L.pl[0][0])[i] = 0;
 
-  // A operand of the score MFMA: row col holds head hh (zero if none)
-  const int hh = 4 * (col & 3) + (col >> 2);
-  const bool hh_ok = hh < a.G;
-  const uint16_t* qh = a.q + ((uint64_t)(b * a.hq + h * a.G + (hh_ok ? hh : 0))) * D;
+  // A operand of the score MFMA: row col holds head hh (zero if none); with
+  // QLO and JG == 1, row 4h + 1 holds the low part of head h
+  constexpr bool LO_ROWS = QLO && JG == 1;
+  const bool lo_row = LO_ROWS && (col & 3) == 1 && (col >> 2) < a.G;
+  const int hh = lo_row ? (col >> 2) : 4 * (col & 3) + (col >> 2);
+  const bool hh_ok = lo_row || hh < a.G;
+  const uint16_t* qh = (lo_row ? a.q_lo : a.q) +
+                       ((uint64_t)(b * a.hq + h * a.G + (hh_ok ? hh : 0))) * D;
   bf16x8_t qa[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -404,8 +412,8 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
     if (hh_ok) v = *reinterpret_cast<const u32x4_t*>(qh + 8 * (4 * kk + grp));
     qa[kk] = __builtin_bit_cast(bf16x8_t, v);
   }
-  bf16x8_t qlo[QLO ? 4 : 1];
-  if constexpr (QLO) {
+  bf16x8_t qlo[QLO && !LO_ROWS ? 4 : 1];
+  if constexpr (QLO && !LO_ROWS) {
     const uint16_t* ql = a.q_lo + ((uint64_t)(b * a.hq + h * a.G + (hh_ok ? hh : 0))) * D;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -468,7 +476,7 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
       for (int kk = 0; kk < 4; ++kk)
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], __builtin_bit_cast(bf16x8_t, kb[kk]),
                                                        sacc, 0, 0, 0);
-      if constexpr (QLO) {
+      if constexpr (QLO && !LO_ROWS) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qlo[kk],
@@ -481,7 +489,8 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
     for (int j = 0; j < JG; ++j) {
       const int hd = 4 * j + grp;
       const bool ok = col < ch.nt && hd < a.G;
-      const float x = ok ? sacc[j] * a.sl2 : -INFINITY;
+      const float sj = LO_ROWS ? sacc[0] + sacc[1] : sacc[j];  // high + low query part
+      const float x = ok ? sj * a.sl2 : -INFINITY;
       alpha[j] = 1.0f;
       if (__builtin_amdgcn_ballot_w64(x > m_run[j] + RESCALE_SLACK)) {
         const float cm = row16_max(x);

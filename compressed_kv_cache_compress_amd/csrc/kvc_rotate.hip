@@ -100,9 +100,11 @@ __device__ __forceinline__ void jacobi_pair(int r, int k, int& p, int& q) {
   q = a < b ? b : a;
 }
 
-// grid (2 sides, streams), 256 threads.  A and V live in LDS with rows of
+// grid (2 sides, streams), JT threads (16 waves, so that LDS latency is hidden
+// inside the one workgroup a CU holds).  A and V live in LDS with rows of
 // APAD floats, so that a column walk hits 32 different banks.
-__global__ __launch_bounds__(256) void k_jacobi(RotatePlan p) {
+constexpr int JT = 1024;
+__global__ __launch_bounds__(JT) void k_jacobi(RotatePlan p) {
   extern __shared__ float lds[];
   float* A = lds;                   // [128][APAD]
   float* V = lds + D * APAD;        // [128][APAD]
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(256) void k_jacobi(RotatePlan p) {
   const int side = blockIdx.x, s = blockIdx.y;
   // A = pairwise sum of the eight partials; the lower-left tile mirrors
   const float* gp = p.gram + ((uint64_t)s * 2 + side) * GGROUPS * D * D;
-  for (int e = tid; e < D * D; e += 256) {
+  for (int e = tid; e < D * D; e += JT) {
     const int i = e / D, j = e % D;
     const int src = (i >= 64 && j < 64) ? j * D + i : e;
     float v[GGROUPS];
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(256) void k_jacobi(RotatePlan p) {
       }
       __syncthreads();
       // rows p and q of A (64 pairs x 128 columns)
-      for (int e = tid; e < 64 * D; e += 256) {
+      for (int e = tid; e < 64 * D; e += JT) {
         const int k = e / D, j = e % D;
         const float c = cs[k], sv = sn[k];
         float* rp = A + P[k] * APAD + j;
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(256) void k_jacobi(RotatePlan p) {
       }
       __syncthreads();
       // columns p and q of A and of V
-      for (int e = tid; e < 64 * D; e += 256) {
+      for (int e = tid; e < 64 * D; e += JT) {
         const int k = e / D, i = e % D;
         const float c = cs[k], sv = sn[k];
         const int pp = P[k], qq = Q[k];
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(256) void k_jacobi(RotatePlan p) {
   }
   __syncthreads();
   float* R = p.rot + ((uint64_t)s * 2 + side) * D * D;
-  for (int e = tid; e < D * D; e += 256) {
+  for (int e = tid; e < D * D; e += JT) {
     const int i = e / D, o = e % D;
     R[i * D + rank[o]] = V[i * APAD + o];
   }
@@ -233,17 +235,24 @@ __global__ __launch_bounds__(128) void k_rotate_vec(RotatePlan p) {
   for (int i = 0; i < D; ++i) rc[i] = R[i * D + k];
   __syncthreads();
   uint16_t* Y = (side ? p.YV : p.YK) + ((uint64_t)s * p.region_len + t0) * D;
-  for (int t = 0; t < n; ++t) {
-    float acc = 0.0f;
+  // two tokens per pass: independent chains (n is even: region_len % 16 == 0)
+  for (int t = 0; t < n; t += 2) {
+    float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
     for (int i4 = 0; i4 < D / 4; ++i4) {
       const float4 x = xs[t * 32 + i4];
-      acc = __builtin_fmaf(x.x, rc[4 * i4], acc);
-      acc = __builtin_fmaf(x.y, rc[4 * i4 + 1], acc);
-      acc = __builtin_fmaf(x.z, rc[4 * i4 + 2], acc);
-      acc = __builtin_fmaf(x.w, rc[4 * i4 + 3], acc);
+      const float4 y = xs[(t + 1) * 32 + i4];
+      a0 = __builtin_fmaf(x.x, rc[4 * i4], a0);
+      a1 = __builtin_fmaf(y.x, rc[4 * i4], a1);
+      a0 = __builtin_fmaf(x.y, rc[4 * i4 + 1], a0);
+      a1 = __builtin_fmaf(y.y, rc[4 * i4 + 1], a1);
+      a0 = __builtin_fmaf(x.z, rc[4 * i4 + 2], a0);
+      a1 = __builtin_fmaf(y.z, rc[4 * i4 + 2], a1);
+      a0 = __builtin_fmaf(x.w, rc[4 * i4 + 3], a0);
+      a1 = __builtin_fmaf(y.w, rc[4 * i4 + 3], a1);
     }
-    Y[(uint64_t)t * D + k] = (uint16_t)f2bf(acc);
+    Y[(uint64_t)t * D + k] = (uint16_t)f2bf(a0);
+    Y[(uint64_t)(t + 1) * D + k] = (uint16_t)f2bf(a1);
   }
 }
 
@@ -256,7 +265,7 @@ hipError_t launch_rotate(const RotatePlan& p, hipStream_t st) {
                           (int)jacobi_lds_bytes()) != hipSuccess)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_gram_partial, dim3(GGROUPS * 3 * 2, p.streams), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(k_jacobi, dim3(2, p.streams), dim3(256), jacobi_lds_bytes(), st, p);
+  hipLaunchKernelGGL(k_jacobi, dim3(2, p.streams), dim3(JT), jacobi_lds_bytes(), st, p);
   hipLaunchKernelGGL(k_rotate_vec, dim3((p.region_len + 63) / 64, 2, p.streams), dim3(128), 0, st,
                      p);
   return hipGetLastError();

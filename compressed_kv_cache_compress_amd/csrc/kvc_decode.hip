@@ -47,6 +47,16 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) const uint32_t lds_u32_t;
+typedef __attribute__((address_space(1))) const u32x4_t glb_u32x4_t;
+
+// LDS byte offset of a pointer into shared memory, and back.
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_u32_t*)p;
+}
+__device__ __forceinline__ const lds_u32_t* lds_ptr(uint32_t off) {
+  return (const lds_u32_t*)(uintptr_t)off;
+}
 
 constexpr int CT = 16;  // MFMA columns: at most this many kept tokens per chunk
 #ifndef KVC_DECODE_SLOTS
@@ -124,11 +134,10 @@ static_assert(chunk_tokens(64) == CT && chunk_tokens(D) >= 12, "stage sizing");
 // order (the library is built with -fno-strict-aliasing because the staging
 // buffers are read and written through different types).
 
-// Selector table entry for a mask nibble n (channels 0..3 of the nibble):
-// dword d holds the v_perm_b32 selectors of channels 2d and 2d+1, i.e. bytes
-// (2e, 2e+1) of an 8-byte window of compact elements where e = kept channels
-// of the nibble before this one, or 0x0C (zero byte) when the channel is
-// dropped.
+// Selectors for a mask nibble n (channels 0..3 of the nibble): dword d holds
+// the v_perm_b32 selectors of channels 2d and 2d+1, i.e. bytes (2e, 2e+1) of
+// an 8-byte window of compact elements where e = kept channels of the nibble
+// before this one, or 0x0C (zero byte) when the channel is dropped.
 __device__ void build_lut_entry(uint32_t n, uint32_t* e) {
   for (int d = 0; d < 2; ++d) {
     uint32_t sel = 0;
@@ -152,51 +161,54 @@ __device__ void build_lut_entry(uint32_t n, uint32_t* e) {
 // read of a token side is in flight at once: issue() reads the mask, the
 // two 12-byte windows (low and high nibble) per byte and the two selector
 // entries; finish() aligns each window to its first element and places the
-// values with one v_perm_b32 per output dword.  Reads stay inside the staging
-// buffer for any mask, so lanes past the chunk run the same code and are
-// zeroed at the end.
+// values with one v_perm_b32 per output dword.  A window is read from the
+// dword holding its first element; v_alignbyte_b32 takes the element's byte
+// address itself as the shift (bits 1:0, 0 or 2 since rows start on 16-byte
+// boundaries).  MASKED: rows carry a 16-byte mask (c < 128); otherwise every
+// channel is kept.  Tokens past the chunk read the zero mask `zrow` (every
+// output zero) and row 0, so every read stays inside the staging buffer.
 struct Expand {
   uint32_t a[4][3], b[4][3];  // windows of the low / high nibble
-  uint32_t sa[4], sb[4];      // shift: 16 * (start & 1) in bits 4:0
+  uint32_t sa[4], sb[4];      // byte address of the first element (bits 1:0 used)
   uint2 tl[4], th[4];         // selectors of the low / high nibble
 };
 
+template <bool MASKED>
 __device__ __forceinline__ void expand_issue(const uint8_t* st, int col, int grp, int nt, int c,
-                                             const uint2* lut, Expand& e) {
-  // masked rows read their mask; dense rows (c == 128) behave as all-ones
-  // masks; tokens past the chunk behave as empty masks (all outputs zero)
-  const bool hm = c < D;
+                                             const uint2* lut, const u32x4_t* zrow, Expand& e) {
   const bool live = col < nt;
-  const int rc = live ? col : 0;  // rows past the chunk read row 0 (their mask is empty)
-  const u32x4_t ml = *reinterpret_cast<const u32x4_t*>(st + 16 * (hm ? rc : 0));
-  const uint32_t* row = reinterpret_cast<const uint32_t*>(st + (hm ? 16 * nt : 0) + (2 * c + 16) * rc);
+  const int rc = live ? col : 0;
+  u32x4_t ml = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  if (MASKED) ml = *(live ? reinterpret_cast<const u32x4_t*>(st + 16 * col) : zrow);
+  const uint32_t row = lds_off(st) + (MASKED ? 16 * nt : 0) + (2 * c + 16) * rc;
   uint32_t pre = 0;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    const uint32_t mw = hm ? ml[kk] : 0xFFFFFFFFu;
-    const uint32_t mb = live ? (mw >> (8 * grp)) & 0xFFu : 0u;
+    const uint32_t mw = ml[kk];
+    const uint32_t mb = (MASKED || live) ? (mw >> (8 * grp)) & 0xFFu : 0u;
     const uint32_t ra = pre + __popc(mw & ((1u << (8 * grp)) - 1u));
     const uint32_t rb = ra + __popc(mb & 0xFu);
     pre += __popc(mw);
-    const uint32_t* wa = row + (ra >> 1);
-    const uint32_t* wb = row + (rb >> 1);
+    const uint32_t ba = row + 2 * ra, bb = row + 2 * rb;
+    const lds_u32_t* wa = lds_ptr(ba & ~3u);
+    const lds_u32_t* wb = lds_ptr(bb & ~3u);
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       e.a[kk][i] = wa[i];
       e.b[kk][i] = wb[i];
     }
-    e.sa[kk] = ra << 4;  // alignbit uses bits 4:0, i.e. 16 * (ra & 1)
-    e.sb[kk] = rb << 4;
+    e.sa[kk] = ba;
+    e.sb[kk] = bb;
     e.tl[kk] = lut[mb & 0xFu];
     e.th[kk] = lut[mb >> 4];
   }
 }
 
 __device__ __forceinline__ u32x4_t expand_finish(const Expand& e, int kk) {
-  const uint32_t xa0 = __builtin_amdgcn_alignbit(e.a[kk][1], e.a[kk][0], e.sa[kk]);
-  const uint32_t xa1 = __builtin_amdgcn_alignbit(e.a[kk][2], e.a[kk][1], e.sa[kk]);
-  const uint32_t xb0 = __builtin_amdgcn_alignbit(e.b[kk][1], e.b[kk][0], e.sb[kk]);
-  const uint32_t xb1 = __builtin_amdgcn_alignbit(e.b[kk][2], e.b[kk][1], e.sb[kk]);
+  const uint32_t xa0 = __builtin_amdgcn_alignbyte(e.a[kk][1], e.a[kk][0], e.sa[kk]);
+  const uint32_t xa1 = __builtin_amdgcn_alignbyte(e.a[kk][2], e.a[kk][1], e.sa[kk]);
+  const uint32_t xb0 = __builtin_amdgcn_alignbyte(e.b[kk][1], e.b[kk][0], e.sb[kk]);
+  const uint32_t xb1 = __builtin_amdgcn_alignbyte(e.b[kk][2], e.b[kk][1], e.sb[kk]);
   u32x4_t o;
   o[0] = __builtin_amdgcn_perm(xa1, xa0, e.tl[kk].x);
   o[1] = __builtin_amdgcn_perm(xa1, xa0, e.tl[kk].y);
@@ -206,10 +218,11 @@ __device__ __forceinline__ u32x4_t expand_finish(const Expand& e, int kk) {
 }
 
 // The 4 x 8 dense channels of this lane's token (zero past the chunk).
+template <bool MASKED>
 __device__ __forceinline__ void expand_side(const uint8_t* st, int col, int grp, int nt, int c,
-                                            const uint2* lut, u32x4_t* o) {
+                                            const uint2* lut, const u32x4_t* zrow, u32x4_t* o) {
   Expand e;
-  expand_issue(st, col, grp, nt, c, lut, e);
+  expand_issue<MASKED>(st, col, grp, nt, c, lut, zrow, e);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) o[kk] = expand_finish(e, kk);
 }
@@ -236,12 +249,15 @@ template <int I>
 __device__ __forceinline__ void prefetch_slot(const Chunk& ch, int lane, Regs& r) {
   const int j = lane + 64 * I;
   if (j < ch.n16) {
+    // the packed buffer is device (global) memory; an unsigned 32-bit
+    // offset on a scalar base is the load's native addressing form
+    const uint32_t off = 16u * (uint32_t)j;
     if (I == 0 && j < ch.nm) {
-      r.k[I] = *reinterpret_cast<const u32x4_t*>(ch.kmask + 16 * j);
-      r.v[I] = *reinterpret_cast<const u32x4_t*>(ch.vmask + 16 * j);
+      r.k[I] = *(glb_u32x4_t*)(ch.kmask + off);
+      r.v[I] = *(glb_u32x4_t*)(ch.vmask + off);
     } else {
-      r.k[I] = *reinterpret_cast<const u32x4_t*>(ch.kval + 16 * j);
-      r.v[I] = *reinterpret_cast<const u32x4_t*>(ch.vval + 16 * j);
+      r.k[I] = *(glb_u32x4_t*)(ch.kval + off);
+      r.v[I] = *(glb_u32x4_t*)(ch.vval + off);
     }
   }
 }
@@ -315,6 +331,13 @@ __device__ __forceinline__ void fetch_descs(Cursor& cu, int lane) {
   cu.w3 = (uint32_t)chunk_tokens(cc) | (row_magic(cc >> 3) << 5) | (page << 26);
 }
 
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Advances to the next non-empty chunk; returns its description.
 __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
   Chunk ch;
@@ -355,15 +378,17 @@ __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
   const int ct = cu.ct;
   const int nt = min(ct, T - t0);
   const int nm = c < D ? nt : 0;
-  ch.kmask = cu.kmask + 16 * t0;
-  ch.vmask = cu.vmask + 16 * t0;
-  ch.kval = cu.kval + 2 * c * t0 - 16 * nm;
-  ch.vval = cu.vval + 2 * c * t0 - 16 * nm;
-  ch.nt = nt;
-  ch.c = c;
-  ch.nm = nm;
-  ch.n16 = nm + (2 * c * nt) / 16;
-  ch.magic = cu.magic;
+  // every field is wave-uniform; readfirstlane keeps them in scalar
+  // registers, so loads take a scalar base and a 32-bit lane offset
+  ch.kmask = uniform_ptr(cu.kmask + 16 * t0);
+  ch.vmask = uniform_ptr(cu.vmask + 16 * t0);
+  ch.kval = uniform_ptr(cu.kval + 2 * c * t0 - 16 * nm);
+  ch.vval = uniform_ptr(cu.vval + 2 * c * t0 - 16 * nm);
+  ch.nt = __builtin_amdgcn_readfirstlane(nt);
+  ch.c = __builtin_amdgcn_readfirstlane(c);
+  ch.nm = __builtin_amdgcn_readfirstlane(nm);
+  ch.n16 = __builtin_amdgcn_readfirstlane(nm + (2 * c * nt) / 16);
+  ch.magic = __builtin_amdgcn_readfirstlane(cu.magic);
   ch.valid = true;
   cu.t0 = t0 + ct;
   return ch;
@@ -379,12 +404,15 @@ __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
 template <int JG, bool QLO>
 __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_decode_split(DecodeArgs a) {
   __shared__ uint2 lut[16];
+  __shared__ u32x4_t zrow[1];
   __shared__ WaveLds<JG> wl[WAVES];
   const int tid = threadIdx.x;
+  static_assert(64 * WAVES == 256, "one selector entry per thread");
   if (tid < 16) {
-    uint32_t e[2];
-    build_lut_entry((uint32_t)tid, e);
-    lut[tid] = make_uint2(e[0], e[1]);
+    uint32_t lo[2];
+    build_lut_entry((uint32_t)tid, lo);
+    lut[tid] = make_uint2(lo[0], lo[1]);
+    if (tid == 0) zrow[0] = u32x4_t{0u, 0u, 0u, 0u};
   }
   __syncthreads();
 
@@ -470,7 +498,7 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
           kb[kk] = live ? r[4 * kk + grp] : z;
         }
       } else {
-        expand_side(sk8, col, grp, ch.nt, ch.c, lut, kb);
+        expand_side<true>(sk8, col, grp, ch.nt, ch.c, lut, zrow, kb);
       }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
@@ -524,7 +552,8 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
         }
       } else {
         u32x4_t vv[4];
-        expand_side(reinterpret_cast<const uint8_t*>(S.v), col, grp, ch.nt, ch.c, lut, vv);
+        expand_side<true>(reinterpret_cast<const uint8_t*>(S.v), col, grp, ch.nt, ch.c, lut, zrow,
+                          vv);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           *reinterpret_cast<u32x4_t*>(S.vt + col * VR_STRIDE + 8 * (4 * kk + grp)) = vv[kk];
@@ -544,7 +573,11 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
     } else {
       // transposed dense tile [channel][token]
       u32x4_t vv[4];
-      expand_side(reinterpret_cast<const uint8_t*>(S.v), col, grp, ch.nt, ch.c, lut, vv);
+      const uint8_t* sv8 = reinterpret_cast<const uint8_t*>(S.v);
+      if (ch.c < D)
+        expand_side<true>(sv8, col, grp, ch.nt, ch.c, lut, zrow, vv);
+      else
+        expand_side<false>(sv8, col, grp, ch.nt, ch.c, lut, zrow, vv);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         uint16_t* dst = S.vt + (8 * (4 * kk + grp)) * VT_STRIDE + col;

@@ -23,6 +23,8 @@ Printed JSON (one line):
                Kara sliding-window cache (mostly dense prompt)
   stream_budget beside the headline (not part of `value`): the same workload
                with the byte budget shared by each stream's segments
+  read_stream  the achievable-bandwidth reference: kv_read_stream (a plain
+               16-byte-load read of as many bytes as one decode reads)
   stage2       beside the headline (not part of `value`): query-aware
                selection of --select-pct percent of the segments
                (kv_summarize once, kv_select_segments + kv_attend_decode over
@@ -381,6 +383,25 @@ def bench_stage2(a, kvc, p, L, q, packed, desc, B, Hq, Hkv, N, stream):
             "kv_tokens_per_s": B * N / ((sel_us + dec_us) * 1e-6)}
 
 
+def bench_read_stream(kvc, buf, nbytes, stream, reps=20):
+    """Achievable HBM read bandwidth on this machine: kv_read_stream (a plain
+    16-byte-load stream over every CU) over as many bytes as one decode
+    reads, HIP events around `reps` back-to-back launches."""
+    nbytes = nbytes // 16 * 16
+    sink = torch.zeros(4, dtype=torch.int32, device=buf.device)
+    for _ in range(3):
+        kvc.kv_read_stream(buf, nbytes, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        kvc.kv_read_stream(buf, nbytes, sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    return {"kernel": "k_read_stream", "bytes": nbytes, "us": t * 1e6, "GBs": nbytes / t / 1e9,
+            "pct_of_peak_hbm": 100.0 * nbytes / t / 1e9 / PEAK_HBM_GBS}
+
+
 def cpu_baseline(w, S, strategies, budget, scale):
     """Oracle as it stands on a bounded sample: one stream compressed, then its
     decode timed (fp64)."""
@@ -496,6 +517,8 @@ def main():
     alg = algorithmic_decode_bytes(dh, S, B, Hq, L.decode_splits)
     t_dec = float(dec_ms.mean()) * 1e-3
     achieved = alg / t_dec / 1e9
+    print("[bench] read-stream reference ...", file=sys.stderr, flush=True)
+    rstream = bench_read_stream(kvc, packed, alg, stream)
     traffic = measured_traffic(a.traffic) if a.config == "batched128k" and not a.decode_splits else None
     packed_total = int(used.sum().item())
     res = {
@@ -527,7 +550,9 @@ def main():
         "roofline": {"kernel": "kv_attend_decode (k_decode_split + k_decode_reduce)",
                      "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": alg},
+                     "algorithmic_bytes_per_launch": alg,
+                     "frac_of_read_stream": achieved / rstream["GBs"]},
+        "read_stream": rstream,
         "value_basis": "B*context / mean decode time over the timed steps; each timed step also "
                        "runs kv_compress (compress_ms)",
     }

@@ -134,6 +134,8 @@ def lib():
         L.kv_pipe_get_stats.restype = ctypes.c_int
         L.kv_pipe_destroy.argtypes = [P]
         L.kv_pipe_destroy.restype = ctypes.c_int
+        L.kv_read_stream.argtypes = [P, u64, P, P]
+        L.kv_read_stream.restype = ctypes.c_int
         L.kvc_status_str.argtypes = [ctypes.c_int]
         L.kvc_status_str.restype = ctypes.c_char_p
         L.kvc_abi_version.restype = ctypes.c_int
@@ -254,6 +256,14 @@ def kv_select_segments(params, q, summary, desc, n_desc, keep, out_desc, out_n, 
                                   _ptr(score), _stream())
     if st != 0:
         raise KvcError("kv_select_segments", st)
+
+
+def kv_read_stream(src, nbytes, sink):
+    """Enqueue the HBM read-stream reference over the first nbytes of src
+    (a measurement, not a step of the method) on the current stream."""
+    st = lib().kv_read_stream(_ptr(src), int(nbytes), _ptr(sink), _stream())
+    if st != 0:
+        raise KvcError("kv_read_stream", st)
 
 
 def kv_append(params, k_new, v_new, n_new, fill, capacity, page_offset, packed, page_desc):

@@ -23,7 +23,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvc.so")
 SOURCES = [os.path.join(CSRC, f)
            for f in ("kvc_host.cpp", "kvc_pipe.cpp", "kvc_compress.hip", "kvc_decode.hip",
-                     "kvc_select.hip", "kvc_pipe.hip", "kvc_rotate.hip")]
+                     "kvc_select.hip", "kvc_pipe.hip", "kvc_rotate.hip",
+                     "kvc_measure.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

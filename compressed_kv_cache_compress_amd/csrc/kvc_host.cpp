@@ -441,6 +441,13 @@ kvc_status kv_summarize(const kvc_params* p, const void* packed, const kvc_seg_d
   return KVC_OK;
 }
 
+kvc_status kv_read_stream(const void* src, uint64_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0) return KVC_E_INVALID;
+  if (!aligned16(src) || !aligned16(sink)) return KVC_E_ALIGN;
+  if (launch_read_stream(src, bytes, sink, stream) != hipSuccess) return KVC_E_HIP;
+  return KVC_OK;
+}
+
 kvc_status kv_select_segments(const kvc_params* p, const uint16_t* q, const uint16_t* summary,
                               const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
                               uint32_t keep, kvc_seg_desc* out_desc, uint32_t* out_n, float* score,

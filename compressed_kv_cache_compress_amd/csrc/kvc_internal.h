@@ -135,6 +135,7 @@ hipError_t launch_append(const AppendPlan& p, hipStream_t st);
 hipError_t launch_switch(const SwitchPlan& p, hipStream_t st);
 hipError_t launch_clear(const ClearPlan& p, hipStream_t st);
 hipError_t launch_summarize(const SummaryPlan& p, hipStream_t st);
+hipError_t launch_read_stream(const void* src, uint64_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_select(const SelectPlan& p, hipStream_t st);
 hipError_t launch_decode(const DecodePlan& p, hipStream_t st);
 

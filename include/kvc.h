@@ -447,6 +447,15 @@ kvc_status kv_pipe_get_stats(const kvc_pipe* pipe, kvc_pipe_stats* out);
  * host state.  NULL is accepted. */
 kvc_status kv_pipe_destroy(kvc_pipe* pipe);
 
+/* Measurement reference, not a step of the method: reads `bytes` bytes of
+ * device memory at `src` once with 16-byte loads spread over every CU.  It
+ * writes nothing unless the XOR of all words read equals a fixed constant;
+ * then it writes that word to *sink.  Timing it on a buffer the size of a
+ * decode's reads gives the achievable HBM read bandwidth of the same box.
+ * src and sink 16-byte aligned device pointers; bytes a multiple of 16,
+ * > 0 (else KVC_E_INVALID / KVC_E_ALIGN). */
+kvc_status kv_read_stream(const void* src, uint64_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* kvc_status_str(kvc_status s);
 

@@ -355,3 +355,16 @@ def test_rotation_entry_points_validate(monkeypatch):
     with pytest.raises(kvc.KvcError) as e:
         kvc.kv_attend_decode_rotated(d1, a, a, a, None, a, a, None, _Fake(0x70000, 64))
     assert e.value.status == -4
+
+
+def test_read_stream_validates(monkeypatch):
+    """The read-stream reference rejects empty, ragged and unaligned buffers
+    before a launch."""
+    monkeypatch.setattr(kvc, "_stream", lambda: ctypes.c_void_p(0))
+    a = _Fake(0x80000)
+    for nbytes, src, sink, status in ((0, a, a, -1), (24, a, a, -1), (32, None, a, -1),
+                                      (32, a, None, -1), (32, _Fake(0x80008), a, -5),
+                                      (32, a, _Fake(0x80004), -5)):
+        with pytest.raises(kvc.KvcError) as e:
+            kvc.kv_read_stream(src, nbytes, sink)
+        assert e.value.status == status

@@ -112,14 +112,23 @@ __device__ __forceinline__ void logits(const float* __restrict__ qr, const float
 }
 
 // Block maximum and pairwise exp-sum of NQ window queries q0.. over the 64
-// tokens of a block (lane = token).
+// tokens of a block (lane = token).  With `lg`, the logits of region tokens
+// are also stored, [stream][query][region token], for the second pass.
 template <int NQ>
 __device__ __forceinline__ void block_partials(const float* __restrict__ qs, int q0, const float* kf,
                                                const ScoreArgs& a, int s, int blk, int lane,
                                                float* __restrict__ part_m,
-                                               float* __restrict__ part_z) {
+                                               float* __restrict__ part_z,
+                                               float* __restrict__ lg) {
   float l[NQ], mb[NQ], z[NQ];
   logits<NQ>(qs + (uint64_t)q0 * D, kf, a.scale, l);
+  if (lg) {
+    const int tr = blk * BLK + lane - a.region_begin;
+    if (tr >= 0 && tr < a.region_len) {
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) lg[((uint64_t)s * a.nq + q0 + j) * a.region_len + tr] = l[j];
+    }
+  }
 #pragma unroll
   for (int j = 0; j < NQ; ++j) mb[j] = l[j];
   max64_n<NQ>(mb);
@@ -147,7 +156,8 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ qs, int
 __global__ __launch_bounds__(64) void k_score_partials(ScoreArgs a, Units un,
                                                        const float* __restrict__ qf,
                                                        float* __restrict__ part_m,
-                                                       float* __restrict__ part_z) {
+                                                       float* __restrict__ part_z,
+                                                       float* __restrict__ lg) {
   const int lane = threadIdx.x;
   for (uint32_t u = blockIdx.x; u < un.total; u += gridDim.x) {
     int blk, s, zq;
@@ -158,8 +168,9 @@ __global__ __launch_bounds__(64) void k_score_partials(ScoreArgs a, Units un,
     const float* qs = qf + (uint64_t)s * a.nq * D;
     int q0 = zq * a.qper;
     const int q1 = min(a.nq, q0 + a.qper);
-    for (; q0 + QB <= q1; q0 += QB) block_partials<QB>(qs, q0, kf, a, s, blk, lane, part_m, part_z);
-    for (; q0 < q1; ++q0) block_partials<1>(qs, q0, kf, a, s, blk, lane, part_m, part_z);
+    for (; q0 + QB <= q1; q0 += QB)
+      block_partials<QB>(qs, q0, kf, a, s, blk, lane, part_m, part_z, lg);
+    for (; q0 < q1; ++q0) block_partials<1>(qs, q0, kf, a, s, blk, lane, part_m, part_z, lg);
   }
 }
 
@@ -247,6 +258,50 @@ __global__ __launch_bounds__(64) void k_token_scores(ScoreArgs a, Units un,
     scores[(uint64_t)s * a.region_len + tr] = sc;
     if (scores_out) scores_out[(uint64_t)s * a.region_len + tr] = sc;
   }
+  }
+}
+
+// The same scores from the logits the first pass stored ([stream][query]
+// [region token]): each term is computed from the same logit by the same
+// operations, in the same query order, so the scores are identical.  Logits
+// are loaded LQ queries at a time so that a wave keeps several loads in
+// flight.  grid (ceil(region_len/64), streams), 64 threads: lane = token.
+constexpr int LQ = 16;
+__global__ __launch_bounds__(64) void k_token_scores_stored(ScoreArgs a, Units un,
+                                                            const float* __restrict__ lg,
+                                                            const float* __restrict__ norm_m,
+                                                            const float* __restrict__ norm_iz,
+                                                            float* __restrict__ scores,
+                                                            float* __restrict__ scores_out) {
+  const int lane = threadIdx.x;
+  for (uint32_t u = blockIdx.x; u < un.total; u += gridDim.x) {
+    int bx, s, z_;
+    unit_xyz(un, u, bx, s, z_);
+    const int tr = bx * 64 + lane;
+    const bool valid = tr < a.region_len;
+    const float* lr = lg + (uint64_t)s * a.nq * a.region_len + (valid ? tr : 0);
+    const float* nm = norm_m + (uint64_t)s * a.nq;
+    const float* ni = norm_iz + (uint64_t)s * a.nq;
+    float sc = 0.0f;
+    int q0 = 0;
+    for (; q0 + LQ <= a.nq; q0 += LQ) {
+      float l[LQ];
+#pragma unroll
+      for (int j = 0; j < LQ; ++j) l[j] = lr[(uint64_t)(q0 + j) * a.region_len];
+#pragma unroll
+      for (int j = 0; j < LQ; ++j) {
+        const float e = spec_exp2((l[j] - nm[q0 + j]) * KVC_LOG2E);
+        sc = sc + e * ni[q0 + j];
+      }
+    }
+    for (; q0 < a.nq; ++q0) {
+      const float e = spec_exp2((lr[(uint64_t)q0 * a.region_len] - nm[q0]) * KVC_LOG2E);
+      sc = sc + e * ni[q0];
+    }
+    if (valid) {
+      scores[(uint64_t)s * a.region_len + tr] = sc;
+      if (scores_out) scores_out[(uint64_t)s * a.region_len + tr] = sc;
+    }
   }
 }
 
@@ -836,12 +891,16 @@ hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
     const Units up{(uint32_t)p.nblk, (uint32_t)p.streams, (uint32_t)(p.nblk * p.streams * qsplit)};
     hipLaunchKernelGGL(k_q_convert, capped(uq, 1, p.max_waves), dim3(64), 0, st, sa, uq, p.qf);
     hipLaunchKernelGGL(k_score_partials, capped(up, 1, p.max_waves), dim3(64), 0, st, sa, up,
-                       (const float*)p.qf, p.part_m, p.part_z);
+                       (const float*)p.qf, p.part_m, p.part_z, p.logits);
     hipLaunchKernelGGL(k_score_normalise, capped(uq, 1, p.max_waves), dim3(64), 0, st, sa, uq,
                        (const float*)p.part_m, (const float*)p.part_z, p.norm_m, p.norm_iz);
     const uint32_t tx = (uint32_t)(p.region_len + 63) / 64;
     const Units ut{tx, (uint32_t)p.streams, tx * (uint32_t)p.streams};
-    if ((int64_t)ut.total * 4 <= SCORE_WAVES && p.nq >= 8 * QB)
+    if (p.logits)
+      hipLaunchKernelGGL(k_token_scores_stored, capped(ut, 1, p.max_waves), dim3(64), 0, st, sa,
+                         ut, (const float*)p.logits, (const float*)p.norm_m,
+                         (const float*)p.norm_iz, p.scores, p.scores_out);
+    else if ((int64_t)ut.total * 4 <= SCORE_WAVES && p.nq >= 8 * QB)
       hipLaunchKernelGGL(k_token_scores_shared<8>, capped(ut, 8, p.max_waves), dim3(512), 0, st,
                          sa, ut, (const float*)p.qf, (const float*)p.norm_m,
                          (const float*)p.norm_iz, p.scores, p.scores_out);

@@ -50,7 +50,7 @@ kvc_status compress_layout(const kvc_params* p, const Shape& sh, kvc_layout* L, 
   if (p->n_strategies == 0 || p->n_strategies > KVC_MAX_STRATEGIES || !p->strategies)
     return KVC_E_INVALID;
   if (p->budget_scope > KVC_BUDGET_STREAM) return KVC_E_INVALID;
-  if (p->rotate > 1) return KVC_E_INVALID;
+  if (p->rotate > 1 || p->store_logits > 1) return KVC_E_INVALID;
   const bool stream_scope = p->budget_scope == KVC_BUDGET_STREAM;
   const uint32_t S = p->seg_tokens;
   if (!pow2(S) || S < 16 || S > 256) return KVC_E_INVALID;
@@ -125,6 +125,8 @@ kvc_status compress_layout(const kvc_params* p, const Shape& sh, kvc_layout* L, 
   ws += align_up((uint64_t)sh.streams * n_seg * ((S + 31) / 32) * 4, kAlign);
   // window queries converted to fp32 once per call
   if (p->n_win) ws += align_up((uint64_t)sh.streams * nq * KVC_HEAD_DIM * 4, kAlign);
+  // store_logits: every window-query logit of the region
+  if (p->n_win && p->store_logits) ws += align_up((uint64_t)sh.streams * nq * p->region_len * 4, kAlign);
   // stream scope: keep sets and objectives of every strategy
   if (stream_scope) {
     ws += align_up((uint64_t)sh.streams * n_seg * p->n_strategies * ((S + 31) / 32) * 4, kAlign);
@@ -298,6 +300,9 @@ kvc_status compress_impl(const kvc_params* p, const uint16_t* K, const uint16_t*
   c.rho = reinterpret_cast<float*>(take(S64 * c.region_len * (uint64_t)c.nc * 2 * 4));
   c.keep = reinterpret_cast<uint32_t*>(take(S64 * c.n_seg * ((c.S + 31) / 32) * 4));
   c.qf = p->n_win ? reinterpret_cast<float*>(take(S64 * c.nq * D * 4)) : nullptr;
+  c.logits = p->n_win && p->store_logits
+                 ? reinterpret_cast<float*>(take(S64 * c.nq * (uint64_t)c.region_len * 4))
+                 : nullptr;
   c.stream_budget = stream_scope;
   c.stream_bytes = (uint64_t)L.n_seg * p->budget_bytes;
   for (int i = 0; i < KVC_MAX_STRATEGIES; ++i) c.seg_bytes[i] = L.seg_bytes[i];

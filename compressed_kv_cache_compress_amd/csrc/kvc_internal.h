@@ -40,6 +40,7 @@ struct CompressPlan {
   // workspace carve-up (device pointers)
   float *part_m, *part_z, *norm_m, *norm_iz, *scores, *rho;
   float* qf;              // window queries in fp32, [streams][G * W][128]
+  float* logits;          // store_logits: [streams][G * W][region_len] fp32, else null
   uint32_t* masks;        // [streams][region_len][nc][2][4]
   uint32_t* keep;         // [streams][n_seg][S/32]
   // per-stream budget (budget_scope == KVC_BUDGET_STREAM)

@@ -49,7 +49,7 @@ def compress(K, V, Qw, *, seg_tokens, strategies, budget_bytes, region_begin=0, 
              want_objective=False, ws=None, packed=None, desc=None, n_ctx=None,
              kv_stream_stride=0, qw_head_stride=0, packed_stream_stride=0, packed_base_offset=0,
              desc_stream_stride=0, n_q_heads=None, budget_scope=0, compress_max_waves=0,
-             rotate=False):
+             rotate=False, store_logits=False):
     """K, V: [B, Hkv, N, 128] bf16 (or strided views described by the stride
     arguments); Qw: [B, Hq, W, 128] bf16 or None.  budget_scope 1 shares
     n_seg * budget_bytes among a stream's segments."""
@@ -64,7 +64,7 @@ def compress(K, V, Qw, *, seg_tokens, strategies, budget_bytes, region_begin=0, 
                  packed_stream_stride=packed_stream_stride,
                  packed_base_offset=packed_base_offset, desc_stream_stride=desc_stream_stride,
                  budget_scope=budget_scope, compress_max_waves=compress_max_waves,
-                 rotate=rotate)
+                 rotate=rotate, store_logits=store_logits)
     _, L = kv_layout_query(p)
     dev = K.device
     streams = B * Hkv

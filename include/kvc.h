@@ -109,7 +109,11 @@ typedef struct {
   uint32_t rotate;               /* 1: SVD rotation before channel selection (calls
                                     kv_compress_rotated / kv_attend_decode_rotated; sizes
                                     their workspaces); 0: none */
-  uint32_t reserved[1];
+  uint32_t store_logits;         /* 1: the first scoring pass keeps every window-query
+                                    logit of the region in the compress workspace
+                                    (streams x G*n_win x region_len fp32) and the second
+                                    pass reads them back instead of recomputing them;
+                                    0: the second pass recomputes them.  Same results. */
 } kvc_params;
 
 /* budget_scope values.

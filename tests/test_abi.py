@@ -107,6 +107,23 @@ def test_layout_errors():
     assert st == -1
 
 
+def test_stored_logits_layout():
+    """store_logits adds streams x G*W x region_len fp32 to the compress
+    workspace and nothing else; other values are rejected."""
+    for cfg in ("tiny", "llama8b", "batched128k", "million"):
+        c = gen.CONFIGS[cfg]
+        _, L0 = kvc.kv_layout_query(_params(cfg))
+        _, L1 = kvc.kv_layout_query(_params(cfg, store_logits=1))
+        streams, nq = c["B"] * c["Hkv"], (c["Hq"] // c["Hkv"]) * c["W"]
+        extra = (streams * nq * c["N"] * 4 + 255) // 256 * 256
+        assert L1.compress_ws_bytes == L0.compress_ws_bytes + extra
+        assert L1.packed_bytes_max == L0.packed_bytes_max
+    p = _params("tiny")
+    p.p.store_logits = 2
+    st, _ = kvc.kv_layout_query(p, check=False)
+    assert st == -1
+
+
 def test_keep_all_needs_no_scoring():
     p = kvc.KvParams(batch=2, n_q_heads=8, n_kv_heads=2, n_ctx=1024, seg_tokens=256,
                      strategies=[(256, 128)], budget_bytes=4 * 256 * 128)

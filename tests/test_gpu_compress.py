@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 def _compare(w, *, S, strategies, budget, region_begin=0, region_len=None, t2c_alpha=0,
              t2c_gamma=0, forced=None, streams=None, label="", budget_scope=0,
-             compress_max_waves=0):
+             compress_max_waves=0, store_logits=False):
     say(f"[compress] {label} B={w['B']} Hq={w['Hq']} Hkv={w['Hkv']} N={w['N']} S={S} "
         f"W={w['W']} region=({region_begin},{region_len})")
     K, V, Qw = w["K"].cuda(), w["V"].cuda(), w["Qw"].cuda()
@@ -23,7 +23,7 @@ def _compare(w, *, S, strategies, budget, region_begin=0, region_len=None, t2c_a
                          region_begin=region_begin, region_len=region_len, t2c_alpha=t2c_alpha,
                          t2c_gamma=t2c_gamma, scale=float(SCALE), forced=fdev, want_scores=True,
                          want_objective=True, budget_scope=budget_scope,
-                         compress_max_waves=compress_max_waves)
+                         compress_max_waves=compress_max_waves, store_logits=store_logits)
     torch.cuda.synchronize()
     cap = r.layout.stream_capacity
     ref = oracle_compress_all(w, S=S, strategies=strategies, budget=budget,
@@ -206,3 +206,21 @@ def test_compress_wave_cap(waves):
     t = gen.make_workload("tiny", N=2048)
     _compare(t, S=64, strategies=gen.table9(64), budget=gen.budget_bytes(33, 64),
              label=f"tiny cap {waves} waves", compress_max_waves=waves)
+
+
+def test_compress_stored_logits():
+    """store_logits: the first scoring pass keeps the logits of the region
+    and the second pass reads them back instead of recomputing them.  Every
+    output stays bit-exact: whole domain, a region that starts mid-domain
+    with a ragged query count, several channel counts, and a wave cap."""
+    w = gen.make_workload("batched128k", B=2, N=2048)
+    _compare(w, S=128, strategies=gen.table9(128), budget=gen.budget_bytes(25, 128),
+             label="stored logits", store_logits=True)
+    c = dict(gen.CONFIGS["tiny"])
+    c.update(Hq=4, Hkv=2, N=1088, S=32, W=9)
+    t = gen.make_workload(c)
+    _compare(t, S=32, strategies=gen.table9(32), budget=gen.budget_bytes(33, 32), region_begin=64,
+             region_len=960, label="stored logits, region", store_logits=True)
+    _compare(t, S=32, strategies=gen.table9(32), budget=gen.budget_bytes(33, 32), region_begin=64,
+             region_len=960, label="stored logits, capped", store_logits=True,
+             compress_max_waves=5)

@@ -17,7 +17,7 @@ from oracle import oracle as O
 pytestmark = pytest.mark.gpu
 
 
-def _sampled(cfg, streams_to_check, budget_scope=0, rotate=False):
+def _sampled(cfg, streams_to_check, budget_scope=0, rotate=False, store_logits=False):
     c = gen.CONFIGS[cfg]
     S = c["S"]
     strat = gen.table9(S)
@@ -27,7 +27,7 @@ def _sampled(cfg, streams_to_check, budget_scope=0, rotate=False):
     say(f"[fullsize] {cfg}: kv_compress + kv_attend_decode")
     r = runtime.compress(w["K"], w["V"], w["Qw"], seg_tokens=S, strategies=strat,
                          budget_bytes=budget, scale=float(SCALE), want_scores=True,
-                         budget_scope=budget_scope, rotate=rotate)
+                         budget_scope=budget_scope, rotate=rotate, store_logits=store_logits)
     out, lse = runtime.decode(w["q"], r.packed, r.desc, n_kv_heads=c["Hkv"],
                               max_desc_per_stream=r.n_seg, scale=float(SCALE), rot=r.rot)
     torch.cuda.synchronize()
@@ -78,6 +78,12 @@ def test_fullsize_llama8b():
 
 def test_fullsize_batched128k():
     _sampled("batched128k", [0, 77])
+
+
+def test_fullsize_batched128k_stored_logits():
+    """The same workload with the first scoring pass storing the logits for
+    the second (17 GB of workspace), as bench.py times it."""
+    _sampled("batched128k", [1, 90], store_logits=True)
 
 
 def test_fullsize_batched128k_stream_budget():

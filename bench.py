@@ -26,6 +26,9 @@ Printed JSON (one line):
                Kara sliding-window cache (mostly dense prompt)
   stream_budget beside the headline (not part of `value`): the same workload
                with the byte budget shared by each stream's segments
+  graph        beside the headline: decode on the Llama-3-8B-shaped layer
+               (a few microseconds per call) launched eagerly and from a
+               HIP graph of 20 calls
   read_stream  the achievable-bandwidth reference: kv_read_stream (a plain
                16-byte-load read of as many bytes as one decode reads)
   stage2       beside the headline (not part of `value`): query-aware
@@ -69,6 +72,8 @@ def parse():
                          "and asynchronous beside the headline (0 = off)")
     ap.add_argument("--no-rotate", action="store_true",
                     help="skip the SVD-rotation measurement beside the headline")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph decode measurement on the Llama-3-8B-shaped layer")
     ap.add_argument("--no-stream-budget", action="store_true",
                     help="skip the per-stream budget measurement beside the headline")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "decode_batched128k_traffic.md"),
@@ -337,6 +342,73 @@ def bench_stream_budget(a, kvc, K, V, Qw, q, B, Hq, Hkv, N, S, W, strategies, bu
             "strategy_histogram": np.bincount(dh["strategy"], minlength=len(strategies)).tolist()}
 
 
+def bench_graph(kvc, stream, reps=200, per_graph=20):
+    """Decode on the Llama-3-8B-shaped layer (B 1, GQA 32/8, 32768 tokens,
+    a few microseconds per call, so launch costs show): kv_attend_decode
+    launched eagerly `reps` times, against a HIP graph holding `per_graph`
+    decode calls replayed reps / per_graph times.  HIP events around each
+    loop; per-call time."""
+    from compressed_kv_cache_compress_amd import gen
+    cfg = gen.CONFIGS["llama8b"]
+    S = cfg["S"]
+    dev = torch.device("cuda:0")
+    w = gen.make_workload("llama8b", seed=0, device=dev)
+    strategies = gen.table9(S)
+    p = kvc.KvParams(batch=cfg["B"], n_q_heads=cfg["Hq"], n_kv_heads=cfg["Hkv"], n_ctx=cfg["N"],
+                     seg_tokens=S, n_win=cfg["W"], strategies=strategies,
+                     budget_bytes=gen.budget_bytes(cfg["budget_pct"], S),
+                     scale=float(1.0 / math.sqrt(128.0)))
+    _, L = kvc.kv_layout_query(p)
+    streams = cfg["B"] * cfg["Hkv"]
+    packed = torch.empty(L.packed_bytes_max, dtype=torch.uint8, device=dev)
+    desc = torch.zeros(streams * L.n_seg * 16, dtype=torch.uint8, device=dev)
+    used = torch.zeros(streams, dtype=torch.int64, device=dev)
+    cws = torch.empty(L.compress_ws_bytes, dtype=torch.uint8, device=dev)
+    dws = torch.empty(L.decode_ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg["B"], cfg["Hq"], 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((cfg["B"], cfg["Hq"]), dtype=torch.float32, device=dev)
+    kvc.kv_compress(p, w["K"], w["V"], w["Qw"], None, packed, desc, used, None, None, cws)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    kvc.kv_attend_decode(p, w["q"], packed, desc, None, ref, lse, dws)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s = torch.cuda.current_stream()
+        e0.record(s)
+        for _ in range(n):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    dec = lambda: kvc.kv_attend_decode(p, w["q"], packed, desc, None, out, lse, dws)  # noqa: E731
+    timed(dec, 20)
+    eager_us = timed(dec, reps) / reps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dec()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            dec()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    graph_us = timed(g.replay, reps // per_graph) / reps
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out.view(torch.uint8), ref.view(torch.uint8)))
+    del w, packed, cws, g
+    torch.cuda.empty_cache()
+    return {"workload": "llama8b", "decode_eager_us": eager_us, "decode_graph_us": graph_us,
+            "decode_calls_per_graph": per_graph, "graph_output_equals_eager": same,
+            "stored_tokens_per_stream": int(np.frombuffer(desc.cpu().numpy().tobytes(),
+                                                           dtype=kvc.DESC_DTYPE)["n_tok"].astype(np.int64).sum() // streams)}
+
+
 def bench_stage2(a, kvc, p, L, q, packed, desc, B, Hq, Hkv, N, stream):
     """Query-aware segment selection (decode-time stage 2) on the same cache:
     kv_summarize once, then per step kv_select_segments + kv_attend_decode
@@ -587,6 +659,10 @@ def main():
         del w, K, V, Qw, packed, cws, dws
         torch.cuda.empty_cache()
         res["kara"] = bench_kara(a, kvc, stream)
+    if not a.no_graph:
+        print("[bench] HIP-graph decode (Llama-3-8B-shaped layer) ...", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        res["graph"] = bench_graph(kvc, stream)
     if a.pipe_steps > 0:
         torch.cuda.empty_cache()
         res["pipeline"] = bench_pipeline(a, kvc, stream)

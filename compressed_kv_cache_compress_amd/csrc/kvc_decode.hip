@@ -673,64 +673,108 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   }
 }
 
-// grid (batch*n_q_heads), 128 threads: lane = channel.
-__global__ __launch_bounds__(128) void k_decode_reduce(const float* __restrict__ part_ml,
-                                                       const float* __restrict__ part_acc,
-                                                       uint16_t* __restrict__ out,
-                                                       float* __restrict__ lse, int splits) {
-  const int r = blockIdx.x, ch = threadIdx.x;
-  const float* ml = part_ml + (uint64_t)r * splits * 2;
+// Log-sum-exp merge of the splits of one (b, q head) row, for a slice of
+// RC channels: thread (g, c) folds splits g, g + RG, ... of channel
+// c0 + c into a group state (m, l, acc), then the RG group states are merged
+// through LDS by the threads of group 0.  Many groups keep the per-thread
+// chain of dependent loads short when there are many splits (RG 32 x RC 32
+// above 32 splits, RG 8 x RC 128 otherwise).  Returns acc / l for channel
+// c0 + c and the row's log-sum-exp (base 2); false when every split was
+// empty (the same answer on every thread of the block).
+template <int RG, int RC>
+__device__ __forceinline__ bool merge_splits(const float* __restrict__ ml,
+                                             const float* __restrict__ acc_row, int splits,
+                                             int c0, float* o, float* lse2) {
+  __shared__ float gm[RG], gl[RG], gacc[RG][RC + 1];
+  const int c = threadIdx.x % RC, g = threadIdx.x / RC;
   float M = -INFINITY;
-  for (int sp = 0; sp < splits; ++sp) M = fmaxf(M, ml[2 * sp]);
-  if (M == -INFINITY) {
-    out[(uint64_t)r * D + ch] = 0;
-    if (lse && ch == 0) lse[r] = -INFINITY;
-    return;
-  }
+  for (int sp = g; sp < splits; sp += RG) M = fmaxf(M, ml[2 * sp]);
   float L = 0.0f, acc = 0.0f;
-  for (int sp = 0; sp < splits; ++sp) {
-    const float w = exp2f(ml[2 * sp] - M);
-    L += ml[2 * sp + 1] * w;
-    acc += part_acc[((uint64_t)r * splits + sp) * D + ch] * w;
+  if (M != -INFINITY) {
+    for (int sp = g; sp < splits; sp += RG) {
+      const float w = exp2f(ml[2 * sp] - M);
+      L += ml[2 * sp + 1] * w;
+      acc += acc_row[(uint64_t)sp * D + c0 + c] * w;
+    }
   }
-  out[(uint64_t)r * D + ch] = (uint16_t)f2bf(acc / L);
-  if (lse && ch == 0) lse[r] = (M + log2f(L)) * 0.69314718055994530942f;
+  gacc[g][c] = acc;
+  if (c == 0) {
+    gm[g] = M;
+    gl[g] = L;
+  }
+  __syncthreads();
+  float Mt = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < RG; ++k) Mt = fmaxf(Mt, gm[k]);
+  if (Mt == -INFINITY) return false;
+  float Lt = 0.0f, at = 0.0f;
+  if (g == 0) {
+#pragma unroll 8
+    for (int k = 0; k < RG; ++k) {
+      const float w = gm[k] == -INFINITY ? 0.0f : exp2f(gm[k] - Mt);
+      Lt += gl[k] * w;
+      at += gacc[k][c] * w;
+    }
+  }
+  *o = at / Lt;
+  *lse2 = Mt + log2f(Lt);
+  return true;
 }
 
-// Rotated cache: the same merge, then out = R_V o' (o' = the merged output
-// in the rotated basis, fp32) before the single bf16 rounding.  R_V of
-// row r's stream is read row by row (thread ch: row ch).
-__global__ __launch_bounds__(128) void k_decode_reduce_rot(const float* __restrict__ part_ml,
+// grid (batch*n_q_heads, 128 / RC), RG * RC threads; group 0 writes.
+template <int RG, int RC>
+__global__ __launch_bounds__(RG * RC) void k_decode_reduce(const float* __restrict__ part_ml,
                                                            const float* __restrict__ part_acc,
-                                                           const float* __restrict__ rot,
                                                            uint16_t* __restrict__ out,
-                                                           float* __restrict__ lse, int splits,
-                                                           int hq, int hkv) {
+                                                           float* __restrict__ lse, int splits) {
+  const int r = blockIdx.x, c0 = blockIdx.y * RC, c = threadIdx.x % RC;
+  float o, l2;
+  const bool any = merge_splits<RG, RC>(part_ml + (uint64_t)r * splits * 2,
+                                        part_acc + (uint64_t)r * splits * D, splits, c0, &o, &l2);
+  if (threadIdx.x >= RC) return;
+  out[(uint64_t)r * D + c0 + c] = any ? (uint16_t)f2bf(o) : (uint16_t)0;
+  if (lse && blockIdx.y == 0 && c == 0) lse[r] = any ? l2 * 0.69314718055994530942f : -INFINITY;
+}
+
+// Rotated cache: the same merge over all 128 channels (grid batch*n_q_heads,
+// four slices of RC channels per block, one after the other), then
+// out = R_V o' (o' = the merged output in the rotated basis, fp32) before the
+// single bf16 rounding.  R_V of row r's stream is read row by row.
+template <int RG, int RC>
+__global__ __launch_bounds__(RG * RC) void k_decode_reduce_rot(const float* __restrict__ part_ml,
+                                                             const float* __restrict__ part_acc,
+                                                             const float* __restrict__ rot,
+                                                             uint16_t* __restrict__ out,
+                                                             float* __restrict__ lse, int splits,
+                                                             int hq, int hkv) {
   __shared__ float o1[D];
-  const int r = blockIdx.x, ch = threadIdx.x;
+  const int r = blockIdx.x, c = threadIdx.x % RC;
   const int b = r / hq, hd = r - b * hq;
   const int s = b * hkv + hd / (hq / hkv);
-  const float* ml = part_ml + (uint64_t)r * splits * 2;
-  float M = -INFINITY;
-  for (int sp = 0; sp < splits; ++sp) M = fmaxf(M, ml[2 * sp]);
-  if (M == -INFINITY) {  // wave-uniform for the whole block: no barrier is skipped unevenly
-    out[(uint64_t)r * D + ch] = 0;
-    if (lse && ch == 0) lse[r] = -INFINITY;
+  bool any = true;
+  float l2 = 0.0f;
+  for (int c0 = 0; c0 < D; c0 += RC) {
+    float o;
+    any = merge_splits<RG, RC>(part_ml + (uint64_t)r * splits * 2,
+                               part_acc + (uint64_t)r * splits * D, splits, c0, &o, &l2);
+    // `any` is uniform over the block: every thread takes the same path
+    if (!any) break;
+    if (threadIdx.x < RC) o1[c0 + c] = o;
+    __syncthreads();  // the next slice rewrites the group states
+  }
+  static_assert(RG * RC >= D, "one thread per output channel");
+  if (!any) {
+    if (threadIdx.x < D) out[(uint64_t)r * D + threadIdx.x] = 0;
+    if (lse && threadIdx.x == 0) lse[r] = -INFINITY;
     return;
   }
-  float L = 0.0f, acc = 0.0f;
-  for (int sp = 0; sp < splits; ++sp) {
-    const float w = exp2f(ml[2 * sp] - M);
-    L += ml[2 * sp + 1] * w;
-    acc += part_acc[((uint64_t)r * splits + sp) * D + ch] * w;
-  }
-  o1[ch] = acc / L;
-  __syncthreads();
+  if (threadIdx.x >= D) return;
+  const int ch = threadIdx.x;
   const float* RV = rot + ((uint64_t)s * 2 + 1) * D * D + (uint64_t)ch * D;
-  float o = 0.0f;
-  for (int k = 0; k < D; ++k) o = __builtin_fmaf(RV[k], o1[k], o);
-  out[(uint64_t)r * D + ch] = (uint16_t)f2bf(o);
-  if (lse && ch == 0) lse[r] = (M + log2f(L)) * 0.69314718055994530942f;
+  float v = 0.0f;
+  for (int k = 0; k < D; ++k) v = __builtin_fmaf(RV[k], o1[k], v);
+  out[(uint64_t)r * D + ch] = (uint16_t)f2bf(v);
+  if (lse && ch == 0) lse[r] = l2 * 0.69314718055994530942f;
 }
 
 // Rotated queries for a rotated cache: q'[k] = fma chain over i of
@@ -778,8 +822,12 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
       hipLaunchKernelGGL((k_decode_split<2, true>), grid, dim3(64 * WAVES), 0, st, a);
     else
       hipLaunchKernelGGL((k_decode_split<4, true>), grid, dim3(64 * WAVES), 0, st, a);
-    hipLaunchKernelGGL(k_decode_reduce_rot, dim3(p.batch * p.hq), dim3(128), 0, st, p.part_ml,
-                       p.part_acc, p.rot, p.out, p.lse, p.splits, p.hq, p.hkv);
+    if (p.splits > 32)
+      hipLaunchKernelGGL((k_decode_reduce_rot<32, 32>), dim3(p.batch * p.hq), dim3(1024), 0, st,
+                         p.part_ml, p.part_acc, p.rot, p.out, p.lse, p.splits, p.hq, p.hkv);
+    else
+      hipLaunchKernelGGL((k_decode_reduce_rot<8, 128>), dim3(p.batch * p.hq), dim3(1024), 0, st,
+                         p.part_ml, p.part_acc, p.rot, p.out, p.lse, p.splits, p.hq, p.hkv);
     return hipGetLastError();
   }
   if (p.G <= 4)
@@ -788,8 +836,12 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
     hipLaunchKernelGGL((k_decode_split<2, false>), grid, dim3(64 * WAVES), 0, st, a);
   else
     hipLaunchKernelGGL((k_decode_split<4, false>), grid, dim3(64 * WAVES), 0, st, a);
-  hipLaunchKernelGGL(k_decode_reduce, dim3(p.batch * p.hq), dim3(128), 0, st, p.part_ml, p.part_acc,
-                     p.out, p.lse, p.splits);
+  if (p.splits > 32)
+    hipLaunchKernelGGL((k_decode_reduce<32, 32>), dim3(p.batch * p.hq, D / 32), dim3(1024), 0, st,
+                       p.part_ml, p.part_acc, p.out, p.lse, p.splits);
+  else
+    hipLaunchKernelGGL((k_decode_reduce<8, 128>), dim3(p.batch * p.hq, 1), dim3(1024), 0, st,
+                       p.part_ml, p.part_acc, p.out, p.lse, p.splits);
   return hipGetLastError();
 }
 

@@ -193,7 +193,7 @@ __global__ __launch_bounds__(64) void k_score_normalise(ScoreArgs a, Units un,
   const float* pm = part_m + ((uint64_t)s * a.nq + qi) * a.nblk;
   const float* pz = part_z + ((uint64_t)s * a.nq + qi) * a.nblk;
   float mx = -INFINITY;
-  for (int b = lane; b < a.nblk; b += 64) mx = fmaxf(mx, pm[b]);
+  for (int b = lane; b < a.nblk; b += 64) mx = fmax_nn(mx, pm[b]);
   const float m = max64(mx);
   const int ng = (a.nblk + 63) / 64;
   int np = 1;

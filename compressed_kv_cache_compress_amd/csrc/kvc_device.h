@@ -19,6 +19,13 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 // log2(e) rounded to fp32.
 #define KVC_LOG2E 0x1.715476p+0f
 
+// Maximum of two non-NaN floats in one instruction (v_maximum3_f32).  It
+// equals fmaxf except that +0 ranks above -0; every caller subtracts the
+// maximum or compares against it, where the sign of a zero changes nothing.
+__device__ __forceinline__ float fmax_nn(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // 2^y for y <= 0 from the Taylor series of e^(f ln 2) truncated after the
 // degree-7 term (coefficients ln2^k / k! rounded to fp32), evaluated by Horner
 // with fused multiply-adds after the split y = n + f, n = rint(y), |f| <= 1/2.
@@ -27,7 +34,7 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 // IEEE machine that evaluates the same sequence.
 __device__ __forceinline__ float spec_exp2(float y) {
   // branch-free: evaluate at max(y, -125) and select
-  const float yc = fmaxf(y, -125.0f);
+  const float yc = fmax_nn(y, -125.0f);
   const float n = __builtin_rintf(yc);
   const float f = yc - n;
   float p = 0x1.ffcbfcp-17f;
@@ -58,19 +65,21 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // Cross-lane moves inside DPP rows of 16 lanes (controls: quad_perm [1,0,3,2],
-// quad_perm [2,3,0,1], row_half_mirror, row_mirror).
+// quad_perm [2,3,0,1], row_half_mirror, row_mirror).  Every lane has a valid
+// source under these controls; written as an update with bound_ctrl so that
+// the compiler folds the move into the consuming add (v_add_f32_dpp).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // Maximum and pairwise-tree sum over the 16 lanes of a DPP row (every lane
 // gets the result): lane pairs, quads, 8-lane halves, then the two halves.
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_mov<0xB1>(v));
-  v = fmaxf(v, dpp_mov<0x4E>(v));
-  v = fmaxf(v, dpp_mov<0x141>(v));
-  v = fmaxf(v, dpp_mov<0x140>(v));
+  v = fmax_nn(v, dpp_mov<0xB1>(v));
+  v = fmax_nn(v, dpp_mov<0x4E>(v));
+  v = fmax_nn(v, dpp_mov<0x141>(v));
+  v = fmax_nn(v, dpp_mov<0x140>(v));
   return v;
 }
 __device__ __forceinline__ float row16_sum(float v) {
@@ -102,7 +111,7 @@ __device__ __forceinline__ float max64(float v) {
   const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
   const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
   const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+  return fmax_nn(fmax_nn(r0, r1), fmax_nn(r2, r3));
 }
 
 // max64 and tree_sum64 of N independent values at once, each step applied
@@ -111,20 +120,20 @@ __device__ __forceinline__ float max64(float v) {
 template <int N>
 __device__ __forceinline__ void max64_n(float* v) {
 #pragma unroll
-  for (int j = 0; j < N; ++j) v[j] = fmaxf(v[j], dpp_mov<0xB1>(v[j]));
+  for (int j = 0; j < N; ++j) v[j] = fmax_nn(v[j], dpp_mov<0xB1>(v[j]));
 #pragma unroll
-  for (int j = 0; j < N; ++j) v[j] = fmaxf(v[j], dpp_mov<0x4E>(v[j]));
+  for (int j = 0; j < N; ++j) v[j] = fmax_nn(v[j], dpp_mov<0x4E>(v[j]));
 #pragma unroll
-  for (int j = 0; j < N; ++j) v[j] = fmaxf(v[j], dpp_mov<0x141>(v[j]));
+  for (int j = 0; j < N; ++j) v[j] = fmax_nn(v[j], dpp_mov<0x141>(v[j]));
 #pragma unroll
-  for (int j = 0; j < N; ++j) v[j] = fmaxf(v[j], dpp_mov<0x140>(v[j]));
+  for (int j = 0; j < N; ++j) v[j] = fmax_nn(v[j], dpp_mov<0x140>(v[j]));
 #pragma unroll
   for (int j = 0; j < N; ++j) {
     const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), 0));
     const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), 16));
     const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), 32));
     const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), 48));
-    v[j] = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+    v[j] = fmax_nn(fmax_nn(r0, r1), fmax_nn(r2, r3));
   }
 }
 template <int N>

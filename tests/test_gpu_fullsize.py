@@ -17,13 +17,14 @@ from oracle import oracle as O
 pytestmark = pytest.mark.gpu
 
 
-def _sampled(cfg, streams_to_check, budget_scope=0, rotate=False, store_logits=False):
-    c = gen.CONFIGS[cfg]
+def _sampled(cfg, streams_to_check, budget_scope=0, rotate=False, store_logits=False, **over):
+    c = dict(gen.CONFIGS[cfg])
+    c.update(over)
     S = c["S"]
     strat = gen.table9(S)
     budget = gen.budget_bytes(c["budget_pct"], S)
     say(f"[fullsize] {cfg}: generating B={c['B']} N={c['N']}")
-    w = gen.make_workload(cfg, device="cuda")
+    w = gen.make_workload(c if over else cfg, device="cuda")
     say(f"[fullsize] {cfg}: kv_compress + kv_attend_decode")
     r = runtime.compress(w["K"], w["V"], w["Qw"], seg_tokens=S, strategies=strat,
                          budget_bytes=budget, scale=float(SCALE), want_scores=True,
@@ -98,6 +99,15 @@ def test_fullsize_batched128k_rotated():
 
 def test_fullsize_million():
     _sampled("million", [3])
+
+
+def test_max_context_one_stream():
+    """The largest context the library takes (n_ctx = 2^22 tokens, 16384
+    segments of 256 and as many decode descriptors per stream): one stream
+    of the million-token generator, G = 4, every output of the stream checked
+    (offsets past 2^31 bits of K, 32-bit token and slot indices at their
+    widest)."""
+    _sampled("million", [0], Hq=4, Hkv=1, N=1 << 22)
 
 
 def test_fullsize_kara():

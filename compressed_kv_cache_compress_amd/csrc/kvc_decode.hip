@@ -678,7 +678,8 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
 // c0 + c into a group state (m, l, acc), then the RG group states are merged
 // through LDS by the threads of group 0.  Many groups keep the per-thread
 // chain of dependent loads short when there are many splits (RG 32 x RC 32
-// above 32 splits, RG 8 x RC 128 otherwise).  Returns acc / l for channel
+// above 32 splits, RG 8 x RC 128 above 8, one group of 128 threads
+// otherwise, where idle threads would cost more than the short chains).  Returns acc / l for channel
 // c0 + c and the row's log-sum-exp (base 2); false when every split was
 // empty (the same answer on every thread of the block).
 template <int RG, int RC>
@@ -825,8 +826,11 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
     if (p.splits > 32)
       hipLaunchKernelGGL((k_decode_reduce_rot<32, 32>), dim3(p.batch * p.hq), dim3(1024), 0, st,
                          p.part_ml, p.part_acc, p.rot, p.out, p.lse, p.splits, p.hq, p.hkv);
-    else
+    else if (p.splits > 8)
       hipLaunchKernelGGL((k_decode_reduce_rot<8, 128>), dim3(p.batch * p.hq), dim3(1024), 0, st,
+                         p.part_ml, p.part_acc, p.rot, p.out, p.lse, p.splits, p.hq, p.hkv);
+    else
+      hipLaunchKernelGGL((k_decode_reduce_rot<1, 128>), dim3(p.batch * p.hq), dim3(128), 0, st,
                          p.part_ml, p.part_acc, p.rot, p.out, p.lse, p.splits, p.hq, p.hkv);
     return hipGetLastError();
   }
@@ -839,8 +843,11 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
   if (p.splits > 32)
     hipLaunchKernelGGL((k_decode_reduce<32, 32>), dim3(p.batch * p.hq, D / 32), dim3(1024), 0, st,
                        p.part_ml, p.part_acc, p.out, p.lse, p.splits);
-  else
+  else if (p.splits > 8)
     hipLaunchKernelGGL((k_decode_reduce<8, 128>), dim3(p.batch * p.hq, 1), dim3(1024), 0, st,
+                       p.part_ml, p.part_acc, p.out, p.lse, p.splits);
+  else
+    hipLaunchKernelGGL((k_decode_reduce<1, 128>), dim3(p.batch * p.hq, 1), dim3(128), 0, st,
                        p.part_ml, p.part_acc, p.out, p.lse, p.splits);
   return hipGetLastError();
 }

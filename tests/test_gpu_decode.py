@@ -43,10 +43,11 @@ def test_decode_gqa_budget25_and_split_invariance():
     _, o2, l2 = _run(w, S, gen.table9(S), gen.budget_bytes(25, S), splits=7)
     d = (o1.float() - o2.float()).abs().max().item()
     say(f"  split 1 vs 7 max diff {d:.2e}")
-    # more than 32 splits per row take the wide merge (32 split groups x 32
-    # channels per workgroup); up to 32 the narrow one (8 x 128)
+    # the merge of the splits has three shapes: up to 8 splits one group of
+    # 128 threads (splits 1 and 7 above), up to 32 eight groups, beyond that
+    # 32 groups x 32 channels per workgroup
     w = gen.make_workload("batched128k", B=1, N=8192)
-    for sp in (33, 64):
+    for sp in (20, 33, 64):
         _run(w, S, gen.table9(S), gen.budget_bytes(25, S), splits=sp)
 
 

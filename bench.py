@@ -509,8 +509,9 @@ def cpu_baseline(w, S, strategies, budget, scale):
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for {a.gpus}); the "
-              "multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (asked for {a.gpus}); the "
+              "streams are independent, so batch or head sharding would need no exchange, but "
+              "no multi-GPU path is built.", file=sys.stderr)
         sys.exit(2)
     import compressed_kv_cache_compress_amd as kvc
     from compressed_kv_cache_compress_amd import gen, runtime

@@ -228,7 +228,8 @@ def bench_pipeline(a, kvc, stream):
                       region_begin=k["window"] - prot - delta, region_len=delta,
                       seg_tokens=delta, n_win=k["window"], strategies=[(a_.T, 128)],
                       budget_bytes=4 * delta * 128, t2c_alpha=k["alpha"], t2c_gamma=k["gamma"],
-                      scale=scale, kv_stream_stride=a_.L * 128, qw_head_stride=a_.L * 128)
+                      scale=scale, kv_stream_stride=a_.L * 128, qw_head_stride=a_.L * 128,
+                      store_logits=1)
     _, Le = kvc.kv_layout_query(pe)
     sp = torch.empty(Le.packed_bytes_max, dtype=torch.uint8, device=dev)
     sd = torch.zeros(streams * 16, dtype=torch.uint8, device=dev)

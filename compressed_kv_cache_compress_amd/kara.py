@@ -61,7 +61,7 @@ def build_cache(K, V, Qall, *, prompt, gen, window=512, delta=64, protect=64, se
     p_ev = KvParams(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, n_ctx=window, region_begin=window - protect - seg,
                     region_len=seg, seg_tokens=seg, n_win=window, strategies=[(T, D)],
                     budget_bytes=4 * seg * D, t2c_alpha=alpha, t2c_gamma=gamma, scale=scale,
-                    kv_stream_stride=L * D, qw_head_stride=L * D)
+                    kv_stream_stride=L * D, qw_head_stride=L * D, store_logits=1)
     _, lev = kv_layout_query(p_ev)
     ev_bytes = lev.seg_bytes[0]
     prompt_bytes = _seg_bytes_keep_all(prompt)
@@ -145,7 +145,8 @@ class KaraPipeline:
                                   seg_tokens=delta, n_win=window, strategies=[(T, D)],
                                   budget_bytes=4 * delta * D, t2c_alpha=alpha, t2c_gamma=gamma,
                                   scale=scale, kv_stream_stride=L * D, qw_head_stride=L * D,
-                                  decode_splits=decode_splits, compress_max_waves=event_max_waves)
+                                  decode_splits=decode_splits, compress_max_waves=event_max_waves,
+                                  store_logits=1)
         _, lev = kv_layout_query(self.ev_params)
         ev_bytes = (lev.seg_bytes[0] + 15) // 16 * 16
         prompt_bytes = _seg_bytes_keep_all(prompt)
@@ -185,7 +186,8 @@ class KaraPipeline:
                           region_begin=window - protect - delta, region_len=delta,
                           seg_tokens=delta, n_win=window, strategies=[(T, D)],
                           budget_bytes=4 * delta * D, t2c_alpha=alpha, t2c_gamma=gamma,
-                          scale=scale, kv_stream_stride=L * D, qw_head_stride=L * D)
+                          scale=scale, kv_stream_stride=L * D, qw_head_stride=L * D,
+                          store_logits=1)
             run(pe, K[:, :, w0:], V[:, :, w0:], Qall[:, :, w0:], prompt_bytes + e * ev_bytes,
                 n_prompt_desc + e)
         self.n_prefix_events = len(pre)

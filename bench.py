@@ -430,6 +430,7 @@ def bench_stage2(a, kvc, p, L, q, packed, desc, B, Hq, Hkv, N, stream):
     dws = torch.empty(max(Ld.decode_ws_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device=dev)
     e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    kvc.kv_summarize(ps, packed, desc, None, summary)  # first launch loads the kernel
     e0.record(stream)
     kvc.kv_summarize(ps, packed, desc, None, summary)
     e1.record(stream)

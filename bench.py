@@ -263,7 +263,8 @@ def bench_rotation(a, kvc, K, V, Qw, q, B, Hq, Hkv, N, S, W, strategies, budget,
     the launch stream, and the objective (attention mass kept, weighted by
     the vector energy kept) of the chosen strategies against the plain run."""
     p = kvc.KvParams(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, n_ctx=N, seg_tokens=S, n_win=W,
-                     strategies=strategies, budget_bytes=budget, scale=float(scale), rotate=1)
+                     strategies=strategies, budget_bytes=budget, scale=float(scale), rotate=1,
+                     store_logits=1)
     _, L = kvc.kv_layout_query(p)
     dev = q.device
     streams = B * Hkv
@@ -313,7 +314,7 @@ def bench_stream_budget(a, kvc, K, V, Qw, q, B, Hq, Hkv, N, S, W, strategies, bu
     strategies; HIP events on the launch stream."""
     p = kvc.KvParams(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, n_ctx=N, seg_tokens=S, n_win=W,
                      strategies=strategies, budget_bytes=budget, scale=float(scale),
-                     budget_scope=1)
+                     budget_scope=1, store_logits=1)
     _, L = kvc.kv_layout_query(p)
     dev = q.device
     streams = B * Hkv

@@ -366,8 +366,7 @@ __global__ __launch_bounds__(64 * TW) void k_token_scores_shared(
 }
 
 // ---------------------------------------------------------------------------
-// Per-vector channel selection (Stage-1): one wave per K or V vector, lane l
-// holding channels l and l+64.
+// Per-vector channel selection (Stage-1): 16 lanes per K or V vector.
 // ---------------------------------------------------------------------------
 struct SelectArgs {
   const uint16_t* K;
@@ -382,61 +381,114 @@ struct SelectArgs {
 constexpr int SEL_TOKENS = 16;  // tokens per block (x2 vectors, 8 per wave)
 
 // NC = number of distinct channel counts; the NC threshold searches of a
-// vector run interleaved (independent ballot chains).
+// vector run interleaved (independent chains).
+// A wave takes four vectors, one per 16-lane DPP row, and lane j of a row
+// holds channels 8j..8j+7.  The c-th largest key is found bit by bit from
+// the top: per-lane compares summed across the row with DPP (vector ALU
+// only; a ballot-and-popcount search with one vector per wave keeps the
+// shared scalar unit busy instead and measured 5 % slower).  Ties at the
+// threshold go to the lower channels (an exclusive prefix count across the
+// row).  Energies are pairwise trees: in-lane over 8 channels, then across
+// the row, i.e. the pairwise tree over the 128 channels in index order.
+__device__ __forceinline__ uint32_t row16_sum_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true);
+  return v;
+}
+// exclusive prefix sum over the lanes of a 16-lane row (row_shr 1, 2, 4, 8;
+// lanes shifted in from outside the row read 0)
+__device__ __forceinline__ uint32_t row16_excl_scan_u32(uint32_t v) {
+  uint32_t x = v;
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);
+  return x - v;
+}
+__device__ __forceinline__ float tree8(const float* v) {
+  return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+}
+
 template <int NC>
-__global__ __launch_bounds__(256) void k_channel_select(SelectArgs a, Units un) {
+__device__ __forceinline__ void select_unit_rows(const SelectArgs& a, int bx, int s) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (uint32_t u = blockIdx.x; u < un.total; u += gridDim.x) {
-  int bx, s, z_;
-  unit_xyz(un, u, bx, s, z_);
-  for (int r = wv; r < 2 * SEL_TOKENS; r += 4) {
+  const int rw = lane >> 4, j = lane & 15;
+  // the unit's 2 * SEL_TOKENS vectors, 16 per pass (4 waves x 4 rows)
+  for (int r0 = 0; r0 < 2 * SEL_TOKENS; r0 += 16) {
+    const int r = r0 + 4 * wv + rw;
     const int tr = bx * SEL_TOKENS + (r >> 1);
     const int kv = r & 1;
-    if (tr >= a.region_len) break;  // wave-uniform
+    const bool valid = tr < a.region_len;  // uniform per row
     const uint16_t* row = (kv ? a.V : a.K) + (uint64_t)s * a.kv_stride +
-                          (uint64_t)(a.region_begin + tr) * D;
-    const uint32_t b0 = row[lane], b1 = row[lane + 64];
-    const uint32_t k0 = b0 & 0x7FFFu, k1 = b1 & 0x7FFFu;
-    const float x0 = bf2f(b0), x1 = bf2f(b1);
-    const float q0 = x0 * x0, q1 = x1 * x1;
-    // tree over channels 0..127 = tree(0..63) + tree(64..127)
-    const float Eall = tree_sum64(q0) + tree_sum64(q1);
-    // the c-th largest key, bit by bit from the top
+                          (uint64_t)(a.region_begin + (valid ? tr : 0)) * D;
+    const uint4 w = *reinterpret_cast<const uint4*>(row + 8 * j);
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    uint32_t k[8];
+    float q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t b = (wd[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      k[e] = b & 0x7FFFu;
+      const float x = bf2f(b);
+      q[e] = x * x;
+    }
+    const float Eall = row16_sum(tree8(q));
     uint32_t tau[NC];
 #pragma unroll
-    for (int u = 0; u < NC; ++u) tau[u] = 0;
+    for (int v = 0; v < NC; ++v) tau[v] = 0;
     for (int bit = 14; bit >= 0; --bit) {
 #pragma unroll
-      for (int u = 0; u < NC; ++u) {
-        const uint32_t cand = tau[u] | (1u << bit);
-        const uint32_t cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand));
-        tau[u] = (cnt >= (uint32_t)a.cvals[u]) ? cand : tau[u];
+      for (int v = 0; v < NC; ++v) {
+        const uint32_t cand = tau[v] | (1u << bit);
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cnt += k[e] >= cand ? 1u : 0u;
+        cnt = row16_sum_u32(cnt);
+        tau[v] = (cnt >= (uint32_t)a.cvals[v]) ? cand : tau[v];
       }
     }
 #pragma unroll
-    for (int u = 0; u < NC; ++u) {
-      const uint32_t c = (uint32_t)a.cvals[u];
-      const uint32_t ngt = __popcll(__ballot(k0 > tau[u])) + __popcll(__ballot(k1 > tau[u]));
-      const uint32_t need = c - ngt;
-      const uint64_t e0 = __ballot(k0 == tau[u]), e1 = __ballot(k1 == tau[u]);
-      const uint32_t rk0 = lanes_below(e0);
-      const uint32_t rk1 = (uint32_t)__popcll(e0) + lanes_below(e1);
-      const bool s0 = k0 > tau[u] || (k0 == tau[u] && rk0 < need);
-      const bool s1 = k1 > tau[u] || (k1 == tau[u] && rk1 < need);
-      const uint64_t m0 = __ballot(s0), m1 = __ballot(s1);
-      const float Ec = tree_sum64(s0 ? q0 : 0.0f) + tree_sum64(s1 ? q1 : 0.0f);
-      if (lane == 0) {
-        const uint64_t o = (((uint64_t)s * a.region_len + tr) * a.nc + u) * 2 + kv;
-        uint4 w;
-        w.x = (uint32_t)m0;
-        w.y = (uint32_t)(m0 >> 32);
-        w.z = (uint32_t)m1;
-        w.w = (uint32_t)(m1 >> 32);
-        reinterpret_cast<uint4*>(a.masks)[o] = w;
-        a.rho[o] = (Eall == 0.0f) ? 1.0f : Ec / Eall;
+    for (int v = 0; v < NC; ++v) {
+      const uint32_t c = (uint32_t)a.cvals[v];
+      uint32_t gt = 0, eq = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        gt += k[e] > tau[v] ? 1u : 0u;
+        eq += k[e] == tau[v] ? 1u : 0u;
+      }
+      const uint32_t need = c - row16_sum_u32(gt);
+      uint32_t rk = row16_excl_scan_u32(eq);  // ties in lower channels of the row
+      uint32_t mb = 0;
+      float qs[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bool sel = k[e] > tau[v];
+        if (k[e] == tau[v]) {
+          sel = rk < need;
+          ++rk;
+        }
+        mb |= (sel ? 1u : 0u) << e;
+        qs[e] = sel ? q[e] : 0.0f;
+      }
+      const float Ec = row16_sum(tree8(qs));
+      if (valid) {
+        const uint64_t o = (((uint64_t)s * a.region_len + tr) * a.nc + v) * 2 + kv;
+        reinterpret_cast<uint8_t*>(a.masks)[o * 16 + j] = (uint8_t)mb;
+        if (j == 0) a.rho[o] = (Eall == 0.0f) ? 1.0f : Ec / Eall;
       }
     }
   }
+}
+
+// grid: units of SEL_TOKENS tokens of a stream (K and V vectors), 256 threads.
+template <int NC>
+__global__ __launch_bounds__(256) void k_channel_select(SelectArgs a, Units un) {
+  for (uint32_t u = blockIdx.x; u < un.total; u += gridDim.x) {
+    int bx, s, z_;
+    unit_xyz(un, u, bx, s, z_);
+    select_unit_rows<NC>(a, bx, s);
   }
 }
 

@@ -531,7 +531,7 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
       }
       const float p = (x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(x - m_run[j]);
       l_run[j] += p;
-      if (hd < a.G) L.pl[pb][hd * CT + col] = (uint16_t)f2bf(p);
+      if (hd < a.G) L.pl[pb][hd * CT + col] = __builtin_bit_cast(uint16_t, (__bf16)p);  // RNE
     }
     return resc;
   };

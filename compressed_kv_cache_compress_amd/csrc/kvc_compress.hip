@@ -869,6 +869,12 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs a) {
   const uint32_t kmask = 0, kval = hasmask ? 16u * T : 0u;
   const uint32_t vmask = kval + 2u * T * c, vval = vmask + (hasmask ? 16u * T : 0u);
   const uint32_t idxo = vval + 2u * T * c;
+  // values: 16 lanes per kept row (lane q: channels 8q..8q+7, one 16-byte
+  // load), four rows per wave; a masked row is compacted in LDS (each lane
+  // drops its kept values at the row's running rank, an exclusive prefix of
+  // the per-lane counts) and written out in 16-byte pieces
+  __shared__ uint4 s_row[16][D / 8 + 1];
+  const int rr = 4 * wv + (lane >> 4), q = lane & 15;
   for (int part = 0; part < 2; ++part) {
     const uint16_t* X = part ? a.V : a.K;
     const uint32_t mo = part ? vmask : kmask, vo = part ? vval : kval;
@@ -878,21 +884,33 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs a) {
         reinterpret_cast<uint4*>(out + mo)[j] = reinterpret_cast<const uint4*>(a.masks)[o];
       }
     }
-    for (int j = wv; j < T; j += 4) {
-      const int tr = sg * S + s_idx[j];
+    for (int j0 = 0; j0 < T; j0 += 16) {
+      const int j = j0 + rr;
+      const bool live = j < T;
+      const int tr = sg * S + s_idx[live ? j : 0];
       const uint16_t* row = X + (uint64_t)s * a.kv_stride + (uint64_t)(a.region_begin + tr) * D;
-      uint16_t* ov = reinterpret_cast<uint16_t*>(out + vo) + (uint64_t)j * c;
+      const uint4 w = *reinterpret_cast<const uint4*>(row + 8 * q);
       if (!hasmask) {
-        ov[lane] = row[lane];
-        ov[lane + 64] = row[lane + 64];
-      } else {
-        const uint64_t o = (((uint64_t)s * a.region_len + tr) * a.nc + u) * 2 + part;
-        const uint4 w = reinterpret_cast<const uint4*>(a.masks)[o];
-        const uint64_t lo = (uint64_t)w.x | ((uint64_t)w.y << 32);
-        const uint64_t hi = (uint64_t)w.z | ((uint64_t)w.w << 32);
-        if ((lo >> lane) & 1u) ov[lanes_below(lo)] = row[lane];
-        if ((hi >> lane) & 1u) ov[(uint32_t)__popcll(lo) + lanes_below(hi)] = row[lane + 64];
+        if (live) reinterpret_cast<uint4*>(out + vo + (uint64_t)j * 2 * D)[q] = w;
+        continue;
       }
+      const uint64_t o = (((uint64_t)s * a.region_len + tr) * a.nc + u) * 2 + part;
+      const uint4 m = reinterpret_cast<const uint4*>(a.masks)[o];
+      const uint32_t mw = q < 4 ? m.x : q < 8 ? m.y : q < 12 ? m.z : m.w;
+      const uint32_t mb = live ? (mw >> (8 * (q & 3))) & 0xFFu : 0u;
+      uint32_t rank = row16_excl_scan_u32((uint32_t)__popc(mb));
+      uint16_t* dst = reinterpret_cast<uint16_t*>(&s_row[rr][0]);
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if ((mb >> e) & 1u) {
+          dst[rank] = (uint16_t)(wd[e >> 1] >> (16 * (e & 1)));
+          ++rank;
+        }
+      }
+      // the row's LDS writes and reads are by the same wave, in order
+      if (live && q < c / 8)
+        reinterpret_cast<uint4*>(out + vo + (uint64_t)j * 2 * c)[q] = s_row[rr][q];
     }
   }
   if (T < S) {

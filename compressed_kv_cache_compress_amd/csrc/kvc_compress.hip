@@ -397,6 +397,19 @@ __device__ __forceinline__ uint32_t row16_sum_u32(uint32_t v) {
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true);
   return v;
 }
+// row16_sum_u32 of N values, each step applied to all before the next, so
+// that one value's DPP move fills the wait states after another's
+template <int N>
+__device__ __forceinline__ void row16_sum_u32_n(uint32_t* v) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[j], 0xB1, 0xF, 0xF, true);
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[j], 0x4E, 0xF, 0xF, true);
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[j], 0x141, 0xF, 0xF, true);
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[j], 0x140, 0xF, 0xF, true);
+}
 // exclusive prefix sum over the lanes of a 16-lane row (row_shr 1, 2, 4, 8;
 // lanes shifted in from outside the row read 0)
 __device__ __forceinline__ uint32_t row16_excl_scan_u32(uint32_t v) {
@@ -407,6 +420,7 @@ __device__ __forceinline__ uint32_t row16_excl_scan_u32(uint32_t v) {
   x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);
   return x - v;
 }
+typedef __attribute__((ext_vector_type(2))) uint16_t u16x2;
 __device__ __forceinline__ float tree8(const float* v) {
   return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
 }
@@ -435,19 +449,29 @@ __device__ __forceinline__ void select_unit_rows(const SelectArgs& a, int bx, in
       q[e] = x * x;
     }
     const float Eall = row16_sum(tree8(q));
+    // keys two to a dword: (key - cand) per 16-bit half has bit 15 set
+    // exactly when key < cand (both are below 2^15), so one packed subtract
+    // and a popcount of the two sign bits count two keys
+    u16x2 k2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k2[i] = __builtin_bit_cast(u16x2, wd[i] & 0x7FFF7FFFu);
     uint32_t tau[NC];
 #pragma unroll
     for (int v = 0; v < NC; ++v) tau[v] = 0;
     for (int bit = 14; bit >= 0; --bit) {
+      uint32_t cand[NC], lt[NC];
 #pragma unroll
       for (int v = 0; v < NC; ++v) {
-        const uint32_t cand = tau[v] | (1u << bit);
-        uint32_t cnt = 0;
+        cand[v] = tau[v] | (1u << bit);
+        const u16x2 c2 = {(uint16_t)cand[v], (uint16_t)cand[v]};
+        lt[v] = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cnt += k[e] >= cand ? 1u : 0u;
-        cnt = row16_sum_u32(cnt);
-        tau[v] = (cnt >= (uint32_t)a.cvals[v]) ? cand : tau[v];
+        for (int i = 0; i < 4; ++i)
+          lt[v] += (uint32_t)__popc(__builtin_bit_cast(uint32_t, (u16x2)(k2[i] - c2)) & 0x80008000u);
       }
+      row16_sum_u32_n<NC>(lt);  // keys below cand, of 128; the searches step together
+#pragma unroll
+      for (int v = 0; v < NC; ++v) tau[v] = (D - lt[v] >= (uint32_t)a.cvals[v]) ? cand[v] : tau[v];
     }
 #pragma unroll
     for (int v = 0; v < NC; ++v) {

@@ -54,7 +54,7 @@ struct ScoreArgs {
   const uint16_t* Qw;
   uint64_t kv_stride, qw_stride;
   int hkv, hq, G, W, nq, nblk, region_begin, region_len;
-  int qper;  // window queries per wave of score_partials (all of them unless the grid is small)
+  int qper;  // window queries per wave of score_partials (at most 64, a multiple of 4)
   float scale;
 };
 
@@ -126,33 +126,32 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ qs, int
     const int tr = blk * BLK + lane - a.region_begin;
     if (tr >= 0 && tr < a.region_len) {
 #pragma unroll
-      for (int j = 0; j < NQ; ++j) lg[((uint64_t)s * a.nq + q0 + j) * a.region_len + tr] = l[j];
+      for (int j = 0; j < NQ; ++j)
+        (lg + ((uint64_t)s * a.nq + q0 + j) * a.region_len)[(uint32_t)tr] = l[j];
     }
   }
 #pragma unroll
   for (int j = 0; j < NQ; ++j) mb[j] = l[j];
-  max64_n<NQ>(mb);
+  max64_n_last<NQ>(mb);
 #pragma unroll
   for (int j = 0; j < NQ; ++j) z[j] = spec_exp2((l[j] - mb[j]) * KVC_LOG2E);
-  tree_sum64_n<NQ>(z);
-  // lane j < NQ stores query j's partials
-  float vm = mb[0], vz = z[0];
+  tree_sum64_n_last<NQ>(z);
+  // lane 63 holds the sums
+  if (lane == 63) {
 #pragma unroll
-  for (int j = 1; j < NQ; ++j) {
-    vm = lane == j ? mb[j] : vm;
-    vz = lane == j ? z[j] : vz;
-  }
-  if (lane < NQ) {
-    const uint64_t o = ((uint64_t)s * a.nq + q0 + lane) * a.nblk + blk;
-    part_m[o] = vm;
-    part_z[o] = vz;
+    for (int j = 0; j < NQ; ++j) {
+      const uint64_t o = ((uint64_t)s * a.nq + q0 + j) * a.nblk + blk;
+      part_m[o] = mb[j];
+      part_z[o] = z[j];
+    }
   }
 }
 
 // grid (nblk, streams, ceil(nq / qper)), 64 threads: lane = token of the
 // 64-token block; wave z handles window queries z * qper .. (z + 1) * qper - 1
 // (each (query, block) partial is computed by exactly one wave, so the split
-// only fills the chip when a domain has few blocks).
+// changes no result; it fills the chip when a domain has few blocks and keeps
+// the window queries read at one time within the scalar cache).
 __global__ __launch_bounds__(64) void k_score_partials(ScoreArgs a, Units un,
                                                        const float* __restrict__ qf,
                                                        float* __restrict__ part_m,
@@ -976,6 +975,11 @@ hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
     constexpr int64_t SCORE_WAVES = 16384;
     const int64_t pw = (int64_t)p.nblk * p.streams;
     int qsplit = (int)((SCORE_WAVES + pw - 1) / pw);
+    // and at most 64 window queries per wave: the waves resident together
+    // then read one 32 KB window of the fp32 queries, most of which the
+    // scalar cache holds (all 256 queries of a stream, 128 KB, mostly miss
+    // it); the key rows are read once per wave, nq / 64 times in all
+    if (qsplit < (p.nq + 63) / 64) qsplit = (p.nq + 63) / 64;
     const int max_split = (p.nq + 4 * QB - 1) / (4 * QB);  // keep >= 4 rounds of QB per wave
     if (qsplit > max_split) qsplit = max_split;
     if (qsplit < 1) qsplit = 1;

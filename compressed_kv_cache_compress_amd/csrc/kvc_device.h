@@ -156,6 +156,63 @@ __device__ __forceinline__ void tree_sum64_n(float* v) {
   }
 }
 
+// Signed integer with the order of a non-NaN float (-0 below +0): the
+// magnitude bits of a negative float are inverted.  The map is its own
+// inverse.  Integer maxima fold into one DPP instruction per step, where a
+// float maximum needs a move and a three-operand maximum.
+__device__ __forceinline__ int32_t f_order_key(float x) {
+  const int32_t i = __float_as_int(x);
+  return i ^ (int32_t)((uint32_t)(i >> 31) >> 1);
+}
+__device__ __forceinline__ float f_order_key_inv(int32_t k) {
+  return __int_as_float(k ^ (int32_t)((uint32_t)(k >> 31) >> 1));
+}
+template <int CTRL>
+__device__ __forceinline__ int32_t dpp_mov_i(int32_t v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+
+// max64_n and tree_sum64_n with the last two steps done by the row
+// broadcasts (lane 15 of each row into the next row, then lane 31 into rows
+// 2 and 3): lane 63 ends with (r3 . r2) . (r1 . r0), the same tree as
+// (r0 . r1) . (r2 . r3) since both operations commute.  Only lane 63 holds
+// the result; the maxima are returned wave-uniform, the sums stay in lane 63.
+template <int N>
+__device__ __forceinline__ void max64_n_last(float* v) {
+  int32_t k[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) k[j] = f_order_key(v[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) k[j] = max(k[j], dpp_mov_i<0xB1>(k[j]));
+#pragma unroll
+  for (int j = 0; j < N; ++j) k[j] = max(k[j], dpp_mov_i<0x4E>(k[j]));
+#pragma unroll
+  for (int j = 0; j < N; ++j) k[j] = max(k[j], dpp_mov_i<0x141>(k[j]));
+#pragma unroll
+  for (int j = 0; j < N; ++j) k[j] = max(k[j], dpp_mov_i<0x140>(k[j]));
+#pragma unroll
+  for (int j = 0; j < N; ++j) k[j] = max(k[j], dpp_mov_i<0x142>(k[j]));
+#pragma unroll
+  for (int j = 0; j < N; ++j) k[j] = max(k[j], dpp_mov_i<0x143>(k[j]));
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = f_order_key_inv(__builtin_amdgcn_readlane(k[j], 63));
+}
+template <int N>
+__device__ __forceinline__ void tree_sum64_n_last(float* v) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = v[j] + dpp_mov<0xB1>(v[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = v[j] + dpp_mov<0x4E>(v[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = v[j] + dpp_mov<0x141>(v[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = v[j] + dpp_mov<0x140>(v[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = v[j] + dpp_mov<0x142>(v[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = v[j] + dpp_mov<0x143>(v[j]);
+}
+
 // Count of set bits of a 64-bit lane mask below the calling lane.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));

@@ -424,6 +424,111 @@ __device__ __forceinline__ float tree8(const float* v) {
   return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
 }
 
+// Ascending bitonic sort of the 128 keys of every 16-lane row.  Key x of a
+// row sits in lane x >> 3 of the row, dword x & 3, half (x >> 2) & 1 of k,
+// so the stages with partner x ^ 1 and x ^ 2 pair whole dwords, x ^ 4 pairs
+// the two halves of a dword and x ^ 8m pairs lanes m apart.  In each phase
+// the blocks that sort downwards hold complemented keys (key ^ 0x7FFF
+// reverses the order of 15-bit keys), so every compare-exchange puts the
+// minimum at the lower index.  The c-th largest key of a row is then key
+// 128 - c, whatever order equal keys end in.
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+// dwords a (lower keys) and b
+__device__ __forceinline__ void cx_dwords(uint32_t& a, uint32_t& b) {
+  const uint32_t m = pk_min_u16(a, b);
+  b = pk_max_u16(a, b);
+  a = m;
+}
+// the two halves of x (the low half holds the lower key)
+__device__ __forceinline__ uint32_t cx_halves(uint32_t x) {
+  const uint32_t sw = __builtin_amdgcn_alignbit(x, x, 16);
+  return (pk_min_u16(x, sw) & 0xFFFFu) | (pk_max_u16(x, sw) & 0xFFFF0000u);
+}
+// the same dword of the row's lane l ^ M (M = 1, 2, 4, 8)
+template <int M>
+__device__ __forceinline__ uint32_t row_partner(uint32_t x) {
+  const int xi = (int)x;
+  if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, xi, 0xB1, 0xF, 0xF, true);
+  if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, xi, 0x4E, 0xF, 0xF, true);
+  if constexpr (M == 8) return (uint32_t)__builtin_amdgcn_update_dpp(0, xi, 0x128, 0xF, 0xF, true);
+  // M == 4: lanes 0-3 and 8-11 of the row read 4 lanes up (row_shl:4),
+  // lanes 4-7 and 12-15 4 lanes down (row_shr:4)
+  const int t = __builtin_amdgcn_update_dpp(xi, xi, 0x104, 0xF, 0x5, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(t, xi, 0x114, 0xF, 0xA, false);
+}
+template <int M>
+__device__ __forceinline__ void cx_lanes(uint32_t* k, bool upper) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t p = row_partner<M>(k[d]);
+    k[d] = upper ? pk_max_u16(k[d], p) : pk_min_u16(k[d], p);
+  }
+}
+__device__ __forceinline__ void cx_in_lane(uint32_t* k, bool halves) {
+  if (halves) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) k[d] = cx_halves(k[d]);
+  }
+  cx_dwords(k[0], k[2]);
+  cx_dwords(k[1], k[3]);
+  cx_dwords(k[0], k[1]);
+  cx_dwords(k[2], k[3]);
+}
+__device__ __forceinline__ void row_sort128_u16(uint32_t* k, int lane) {
+  constexpr uint32_t F = 0x7FFF7FFFu;
+  const bool l1 = lane & 1, l2 = lane & 2, l4 = lane & 4, l8 = lane & 8;
+  // phase 2: down where x & 2 (dwords 2, 3)
+  k[2] ^= F;
+  k[3] ^= F;
+  cx_dwords(k[0], k[1]);
+  cx_dwords(k[2], k[3]);
+  // phase 4: down where x & 4 (high halves)
+  k[0] ^= 0x7FFF0000u;
+  k[1] ^= 0x7FFF0000u;
+  k[2] ^= 0x00007FFFu;
+  k[3] ^= 0x00007FFFu;
+  cx_in_lane(k, false);
+  // phases 8 .. 64: down where lane bit 0, 1, 2, 3 of the row is set
+  uint32_t f = 0x7FFF0000u ^ (l1 ? F : 0u);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) k[d] ^= f;
+  cx_in_lane(k, true);
+  f = (l1 ? F : 0u) ^ (l2 ? F : 0u);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) k[d] ^= f;
+  cx_lanes<1>(k, l1);
+  cx_in_lane(k, true);
+  f = (l2 ? F : 0u) ^ (l4 ? F : 0u);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) k[d] ^= f;
+  cx_lanes<2>(k, l2);
+  cx_lanes<1>(k, l1);
+  cx_in_lane(k, true);
+  f = (l4 ? F : 0u) ^ (l8 ? F : 0u);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) k[d] ^= f;
+  cx_lanes<4>(k, l4);
+  cx_lanes<2>(k, l2);
+  cx_lanes<1>(k, l1);
+  cx_in_lane(k, true);
+  // phase 128: all upwards
+  f = l8 ? F : 0u;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) k[d] ^= f;
+  cx_lanes<8>(k, l8);
+  cx_lanes<4>(k, l4);
+  cx_lanes<2>(k, l2);
+  cx_lanes<1>(k, l1);
+  cx_in_lane(k, true);
+}
+
 template <int NC>
 __device__ __forceinline__ void select_unit_rows(const SelectArgs& a, int bx, int s) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -455,22 +560,34 @@ __device__ __forceinline__ void select_unit_rows(const SelectArgs& a, int bx, in
 #pragma unroll
     for (int i = 0; i < 4; ++i) k2[i] = __builtin_bit_cast(u16x2, wd[i] & 0x7FFF7FFFu);
     uint32_t tau[NC];
+    if constexpr (NC >= 2) {
+      // one sort serves every channel count: c is a multiple of 8, so the
+      // c-th largest key is the low half of dword 0 in lane 16 - c / 8
+      uint32_t ks[4];
 #pragma unroll
-    for (int v = 0; v < NC; ++v) tau[v] = 0;
-    for (int bit = 14; bit >= 0; --bit) {
-      uint32_t cand[NC], lt[NC];
+      for (int i = 0; i < 4; ++i) ks[i] = __builtin_bit_cast(uint32_t, k2[i]);
+      row_sort128_u16(ks, lane);
 #pragma unroll
-      for (int v = 0; v < NC; ++v) {
-        cand[v] = tau[v] | (1u << bit);
-        const u16x2 c2 = {(uint16_t)cand[v], (uint16_t)cand[v]};
-        lt[v] = 0;
+      for (int v = 0; v < NC; ++v)
+        tau[v] = (uint32_t)__shfl((int)(ks[0] & 0xFFFFu), (lane & 48) | (16 - a.cvals[v] / 8), 64);
+    } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          lt[v] += (uint32_t)__popc(__builtin_bit_cast(uint32_t, (u16x2)(k2[i] - c2)) & 0x80008000u);
+      for (int v = 0; v < NC; ++v) tau[v] = 0;
+      for (int bit = 14; bit >= 0; --bit) {
+        uint32_t cand[NC], lt[NC];
+#pragma unroll
+        for (int v = 0; v < NC; ++v) {
+          cand[v] = tau[v] | (1u << bit);
+          const u16x2 c2 = {(uint16_t)cand[v], (uint16_t)cand[v]};
+          lt[v] = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            lt[v] += (uint32_t)__popc(__builtin_bit_cast(uint32_t, (u16x2)(k2[i] - c2)) & 0x80008000u);
+        }
+        row16_sum_u32_n<NC>(lt);  // keys below cand, of 128
+#pragma unroll
+        for (int v = 0; v < NC; ++v) tau[v] = (D - lt[v] >= (uint32_t)a.cvals[v]) ? cand[v] : tau[v];
       }
-      row16_sum_u32_n<NC>(lt);  // keys below cand, of 128; the searches step together
-#pragma unroll
-      for (int v = 0; v < NC; ++v) tau[v] = (D - lt[v] >= (uint32_t)a.cvals[v]) ? cand[v] : tau[v];
     }
 #pragma unroll
     for (int v = 0; v < NC; ++v) {

@@ -592,24 +592,26 @@ __device__ __forceinline__ void select_unit_rows(const SelectArgs& a, int bx, in
 #pragma unroll
     for (int v = 0; v < NC; ++v) {
       const uint32_t c = (uint32_t)a.cvals[v];
-      uint32_t gt = 0, eq = 0;
+      // counts of keys above and below the threshold from the packed keys
+      // (sign bit of each 16-bit difference), so that no per-key flag has
+      // to live across both loops
+      const u16x2 t2 = {(uint16_t)tau[v], (uint16_t)tau[v]};
+      uint32_t gt = 0, lt = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        gt += k[e] > tau[v] ? 1u : 0u;
-        eq += k[e] == tau[v] ? 1u : 0u;
+      for (int i = 0; i < 4; ++i) {
+        gt += (uint32_t)__popc(__builtin_bit_cast(uint32_t, (u16x2)(t2 - k2[i])) & 0x80008000u);
+        lt += (uint32_t)__popc(__builtin_bit_cast(uint32_t, (u16x2)(k2[i] - t2)) & 0x80008000u);
       }
       const uint32_t need = c - row16_sum_u32(gt);
-      uint32_t rk = row16_excl_scan_u32(eq);  // ties in lower channels of the row
+      uint32_t rk = row16_excl_scan_u32(8u - gt - lt);  // ties in lower channels of the row
       uint32_t mb = 0;
       float qs[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        bool sel = k[e] > tau[v];
-        if (k[e] == tau[v]) {
-          sel = rk < need;
-          ++rk;
-        }
-        mb |= (sel ? 1u : 0u) << e;
+        const bool eq = k[e] == tau[v];
+        const bool sel = (k[e] > tau[v]) | (eq & (rk < need));
+        rk += eq ? 1u : 0u;
+        mb |= sel ? (1u << e) : 0u;
         qs[e] = sel ? q[e] : 0.0f;
       }
       const float Ec = row16_sum(tree8(qs));

@@ -127,6 +127,37 @@ def test_compress_many_channel_counts():
     _compare(w, S=S, strategies=strat, budget=4 * S * 128, forced=forced, label="six c, forced")
 
 
+def _tie_workload(seed):
+    """Small integer K and V (many equal magnitudes in every vector)."""
+    c = dict(gen.CONFIGS["tiny"])
+    c.update(Hq=2, Hkv=1, N=512, S=64, W=4)
+    w = gen.make_workload(c)
+    g = torch.Generator().manual_seed(seed)
+    w["K"] = torch.randint(-3, 4, w["K"].shape, generator=g).to(torch.bfloat16)
+    w["V"] = torch.randint(-2, 3, w["V"].shape, generator=g).to(torch.bfloat16)
+    return w
+
+
+def test_compress_one_channel_count():
+    """A single distinct channel count below 128: the per-vector threshold is
+    found by the bit search instead of the sort (random and tied keys)."""
+    w = gen.make_workload("llama8b", B=1, N=2048)
+    strat = [(128, 128), (64, 48), (32, 48), (96, 128)]
+    _compare(w, S=128, strategies=strat, budget=gen.budget_bytes(30, 128), label="one c")
+    _compare(_tie_workload(11), S=64, strategies=[(64, 128), (32, 40), (16, 40)],
+             budget=gen.budget_bytes(30, 64), label="one c, ties")
+
+
+def test_compress_eight_channel_counts_ties():
+    """The most distinct channel counts a table may hold (8), on vectors full
+    of equal magnitudes: one sort serves all eight thresholds and ties go to
+    the lower channels."""
+    strat = [(64, 8), (48, 16), (40, 32), (32, 48), (24, 64), (16, 80), (12, 96), (8, 120),
+             (64, 128)]
+    _compare(_tie_workload(12), S=64, strategies=strat, budget=gen.budget_bytes(35, 64),
+             label="eight c, ties")
+
+
 @pytest.mark.parametrize("cfg,pct", [("tiny", 25), ("llama8b", 33), ("batched128k", 25)])
 def test_compress_stream_budget(cfg, pct):
     """Per-stream budget (Lagrangian choice over all strategies): descriptors,

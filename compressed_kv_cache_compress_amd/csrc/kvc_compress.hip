@@ -448,8 +448,12 @@ __device__ __forceinline__ void cx_dwords(uint32_t& a, uint32_t& b) {
 }
 // the two halves of x (the low half holds the lower key)
 __device__ __forceinline__ uint32_t cx_halves(uint32_t x) {
-  const uint32_t sw = __builtin_amdgcn_alignbit(x, x, 16);
-  return (pk_min_u16(x, sw) & 0xFFFFu) | (pk_max_u16(x, sw) & 0xFFFF0000u);
+  // the swapped operand folds into the packed instructions' operand selects
+  const u16x2 v = __builtin_bit_cast(u16x2, x);
+  const u16x2 sw = __builtin_shufflevector(v, v, 1, 0);
+  const uint32_t mn = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(v, sw));
+  const uint32_t mx = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, sw));
+  return (mn & 0xFFFFu) | (mx & 0xFFFF0000u);
 }
 // the same dword of the row's lane l ^ M (M = 1, 2, 4, 8)
 template <int M>

@@ -467,13 +467,19 @@ __device__ __forceinline__ uint32_t row_partner(uint32_t x) {
   const int t = __builtin_amdgcn_update_dpp(xi, xi, 0x104, 0xF, 0x5, false);
   return (uint32_t)__builtin_amdgcn_update_dpp(t, xi, 0x114, 0xF, 0xA, false);
 }
+// Lanes with bit M (of the row) hold complemented keys during this stage.
+// Each lane takes the minimum of its own value and its partner's value
+// complemented: the lower lane gets the minimum of the two keys, the upper
+// lane the complement of their maximum.  The partner's move folds into the
+// exclusive or (v_xor_b32_dpp), so a stage is two instructions per dword.
 template <int M>
-__device__ __forceinline__ void cx_lanes(uint32_t* k, bool upper) {
+__device__ __forceinline__ void cx_lanes_c(uint32_t* k, uint32_t fv) {
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t p = row_partner<M>(k[d]);
-    k[d] = upper ? pk_max_u16(k[d], p) : pk_min_u16(k[d], p);
-  }
+  for (int d = 0; d < 4; ++d) k[d] = pk_min_u16(k[d], row_partner<M>(k[d]) ^ fv);
+}
+__device__ __forceinline__ void xor_all(uint32_t* k, uint32_t f) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) k[d] ^= f;
 }
 __device__ __forceinline__ void cx_in_lane(uint32_t* k, bool halves) {
   if (halves) {
@@ -499,37 +505,44 @@ __device__ __forceinline__ void row_sort128_u16(uint32_t* k, int lane) {
   k[2] ^= 0x00007FFFu;
   k[3] ^= 0x00007FFFu;
   cx_in_lane(k, false);
-  // phases 8 .. 64: down where lane bit 0, 1, 2, 3 of the row is set
-  uint32_t f = 0x7FFF0000u ^ (l1 ? F : 0u);
-#pragma unroll
-  for (int d = 0; d < 4; ++d) k[d] ^= f;
+  // phases 8 .. 64: down where lane bit 0, 1, 2, 3 of the row is set; the
+  // exclusive ors below move between the stored forms: direction flip of
+  // the phase, complemented upper lanes of each lane stage, plain keys for
+  // the in-lane stages
+  const uint32_t c1 = l1 ? F : 0u, c2 = l2 ? F : 0u, c4 = l4 ? F : 0u, c8 = l8 ? F : 0u;
+  // the complement mask in a vector register, so that the partner's move
+  // folds into the exclusive or (a DPP operation takes no literal)
+  uint32_t fv = F;
+  asm volatile("" : "+v"(fv));
+  xor_all(k, 0x7FFF0000u ^ c1);
   cx_in_lane(k, true);
-  f = (l1 ? F : 0u) ^ (l2 ? F : 0u);
-#pragma unroll
-  for (int d = 0; d < 4; ++d) k[d] ^= f;
-  cx_lanes<1>(k, l1);
+  xor_all(k, c2);  // phase 16: key ^ c2, upper lanes of x ^ 8 complemented
+  cx_lanes_c<1>(k, fv);
+  xor_all(k, c1);
   cx_in_lane(k, true);
-  f = (l2 ? F : 0u) ^ (l4 ? F : 0u);
-#pragma unroll
-  for (int d = 0; d < 4; ++d) k[d] ^= f;
-  cx_lanes<2>(k, l2);
-  cx_lanes<1>(k, l1);
+  xor_all(k, c4);  // phase 32
+  cx_lanes_c<2>(k, fv);
+  xor_all(k, c2 ^ c1);
+  cx_lanes_c<1>(k, fv);
+  xor_all(k, c1);
   cx_in_lane(k, true);
-  f = (l4 ? F : 0u) ^ (l8 ? F : 0u);
-#pragma unroll
-  for (int d = 0; d < 4; ++d) k[d] ^= f;
-  cx_lanes<4>(k, l4);
-  cx_lanes<2>(k, l2);
-  cx_lanes<1>(k, l1);
+  xor_all(k, c8);  // phase 64
+  cx_lanes_c<4>(k, fv);
+  xor_all(k, c4 ^ c2);
+  cx_lanes_c<2>(k, fv);
+  xor_all(k, c2 ^ c1);
+  cx_lanes_c<1>(k, fv);
+  xor_all(k, c1);
   cx_in_lane(k, true);
-  // phase 128: all upwards
-  f = l8 ? F : 0u;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) k[d] ^= f;
-  cx_lanes<8>(k, l8);
-  cx_lanes<4>(k, l4);
-  cx_lanes<2>(k, l2);
-  cx_lanes<1>(k, l1);
+  // phase 128, all upwards: key ^ c8 is already the form for x ^ 64
+  cx_lanes_c<8>(k, fv);
+  xor_all(k, c8 ^ c4);
+  cx_lanes_c<4>(k, fv);
+  xor_all(k, c4 ^ c2);
+  cx_lanes_c<2>(k, fv);
+  xor_all(k, c2 ^ c1);
+  cx_lanes_c<1>(k, fv);
+  xor_all(k, c1);
   cx_in_lane(k, true);
 }
 

@@ -127,6 +127,18 @@ def test_compress_many_channel_counts():
     _compare(w, S=S, strategies=strat, budget=4 * S * 128, forced=forced, label="six c, forced")
 
 
+@pytest.mark.parametrize("hq,hkv,W", [(1, 1, 150), (4, 1, 37), (2, 2, 71)])
+def test_compress_window_query_split(hq, hkv, W):
+    """Window-query counts that do not divide into the per-wave split (a
+    wave takes at most 64 queries, four at a time, then single ones):
+    G*W = 150, 148 and 71 queries per stream."""
+    c = dict(gen.CONFIGS["tiny"])
+    c.update(Hq=hq, Hkv=hkv, N=2048, S=64, W=W)
+    w = gen.make_workload(c, seed=3)
+    _compare(w, S=64, strategies=gen.table9(64), budget=gen.budget_bytes(33, 64),
+             region_begin=256, region_len=1472, label=f"G*W={hq // hkv * W}")
+
+
 def _tie_workload(seed):
     """Small integer K and V (many equal magnitudes in every vector)."""
     c = dict(gen.CONFIGS["tiny"])

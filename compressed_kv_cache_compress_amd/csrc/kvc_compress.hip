@@ -606,6 +606,7 @@ __device__ __forceinline__ void select_unit_rows(const SelectArgs& a, int bx, in
         for (int v = 0; v < NC; ++v) tau[v] = (D - lt[v] >= (uint32_t)a.cvals[v]) ? cand[v] : tau[v];
       }
     }
+    float ec_mine = 0.0f;  // kept energy of channel count j (lanes j < NC of the row)
 #pragma unroll
     for (int v = 0; v < NC; ++v) {
       const uint32_t c = (uint32_t)a.cvals[v];
@@ -632,11 +633,17 @@ __device__ __forceinline__ void select_unit_rows(const SelectArgs& a, int bx, in
         qs[e] = sel ? q[e] : 0.0f;
       }
       const float Ec = row16_sum(tree8(qs));
+      ec_mine = j == v ? Ec : ec_mine;
       if (valid) {
         const uint64_t o = (((uint64_t)s * a.region_len + tr) * a.nc + v) * 2 + kv;
         reinterpret_cast<uint8_t*>(a.masks)[o * 16 + j] = (uint8_t)mb;
-        if (j == 0) a.rho[o] = (Eall == 0.0f) ? 1.0f : Ec / Eall;
       }
+    }
+    // lane j < NC of the row divides for channel count j: one division
+    // sequence for all counts
+    if (valid && j < NC) {
+      const uint64_t o = (((uint64_t)s * a.region_len + tr) * a.nc + j) * 2 + kv;
+      a.rho[o] = (Eall == 0.0f) ? 1.0f : ec_mine / Eall;
     }
   }
 }

@@ -82,7 +82,7 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_decode_bytes(desc, S, B, Hq, splits):
+def algorithmic_decode_bytes(desc, B, Hq, splits):
     n = desc["n_tok"].astype(np.int64)
     c = desc["n_ch"].astype(np.int64)
     masks = np.where(c < 128, 2 * 16 * n, 0)
@@ -298,7 +298,7 @@ def bench_rotation(a, kvc, K, V, Qw, q, B, Hq, Hkv, N, S, W, strategies, budget,
     pc = np.take_along_axis(plain_objective, plain_desc["strategy"].astype(np.int64)[..., None],
                             axis=2)[..., 0]
     t_dec = float(np.mean([e[0].elapsed_time(e[1]) for e in dv])) * 1e-3
-    alg = algorithmic_decode_bytes(dh.ravel(), S, B, Hq, L.decode_splits)
+    alg = algorithmic_decode_bytes(dh.ravel(), B, Hq, L.decode_splits)
     return {"compress_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
             "decode_us": t_dec * 1e6, "kv_tokens_per_s": B * N / t_dec,
             "achieved_GBs": alg / t_dec / 1e9, "packed_bytes": int(used.sum().item()),
@@ -452,13 +452,17 @@ def bench_stage2(a, kvc, p, L, q, packed, desc, B, Hq, Hkv, N, stream):
     torch.cuda.synchronize()
     sel_us = float(np.mean([x[0].elapsed_time(x[1]) for x in ev])) * 1e3
     dec_us = float(np.mean([x[1].elapsed_time(x[2]) for x in ev])) * 1e3
-    kept = np.asarray(out_desc.cpu().numpy().view(kvc.DESC_DTYPE)["n_tok"], np.int64)
+    kd = out_desc.cpu().numpy().view(kvc.DESC_DTYPE).reshape(streams, keep)
     n = out_n.cpu().numpy()
-    kept_tok = int(sum(kept.reshape(streams, keep)[s, :n[s]].sum() for s in range(streams)))
+    live = np.concatenate([kd[s, :n[s]] for s in range(streams)])
+    kept_tok = int(live["n_tok"].astype(np.int64).sum())
+    alg = algorithmic_decode_bytes(live, B, Hq, Ld.decode_splits)
     return {"keep_segments_per_stream": keep, "keep_pct": a.select_pct,
             "summarize_us_once": t_sum, "select_us": sel_us, "decode_us": dec_us,
             "select_plus_decode_us": sel_us + dec_us,
             "kept_tokens": kept_tok,
+            "decode_algorithmic_bytes": alg,
+            "decode_achieved_GBs": alg / (dec_us * 1e-6) / 1e9,
             "kv_tokens_per_s": B * N / ((sel_us + dec_us) * 1e-6)}
 
 
@@ -609,7 +613,7 @@ def main():
 
     dh = desc.cpu().numpy().view(kvc.DESC_DTYPE)
     hist = np.bincount(dh["strategy"], minlength=len(strategies)).tolist()
-    alg = algorithmic_decode_bytes(dh, S, B, Hq, L.decode_splits)
+    alg = algorithmic_decode_bytes(dh, B, Hq, L.decode_splits)
     t_dec = float(np.median(dec_ms)) * 1e-3
     achieved = alg / t_dec / 1e9
     print("[bench] read-stream reference ...", file=sys.stderr, flush=True)

@@ -331,6 +331,66 @@ __device__ __forceinline__ void fetch_descs(Cursor& cu, int lane) {
   cu.w3 = (uint32_t)chunk_tokens(cc) | (row_magic(cc >> 3) << 5) | (page << 26);
 }
 
+// Chunks of descriptor i of a stream's list (0 past nd): ceil(T / ct) with
+// ct = 12 to 16 tokens per chunk.  T / ct is a multiple of 1/ct >= 1/16 apart
+// from the next integer, so adding 31/32 to the product with the approximate
+// reciprocal and truncating gives the exact ceiling.  (The count only
+// balances the splits; any count gives the same results.)
+__device__ __forceinline__ uint32_t desc_chunks(const kvc_seg_desc* dl, int i, int nd) {
+  if (i >= nd) return 0u;
+  const uint32_t tc = reinterpret_cast<const uint32_t*>(dl + i)[2];
+  const uint32_t T = tc & 0xFFFFu;
+  const int c = (int)(tc >> 16) & ~7;
+  const float ct = (float)chunk_tokens(c < 8 ? 8 : (c > D ? D : c));
+  return (uint32_t)((float)T * __builtin_amdgcn_rcpf(ct) + 0.96875f);
+}
+// inclusive sum over the 64 lanes: rows by row_shr, then the row broadcasts
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);
+  return x;
+}
+
+// Descriptor range [di, d1) of split sp of a stream with nd descriptors.
+// With more descriptors than splits and at most 256 of them, splits take
+// equal shares of chunks: descriptor i goes to split floor(E_i * splits / W),
+// with E_i the chunks of the descriptors before i and W all chunks of the
+// stream.  That index never decreases with i, so every split takes a
+// contiguous run (possibly empty).  Few descriptors per split of different
+// sizes (a dense prompt page is 22 chunks, a Kara event segment 1) leave one
+// wave with most of a stream's work otherwise.  Over longer lists equal
+// descriptor counts balance well enough: at 1024 descriptors per stream the
+// scan cost more than it saved.
+__device__ __forceinline__ void split_range(const kvc_seg_desc* dl, int nd, int splits, int sp,
+                                            int lane, int& di, int& d1) {
+  di = (int)(((int64_t)sp * nd) / splits);
+  d1 = (int)(((int64_t)(sp + 1) * nd) / splits);
+  if (nd <= splits || nd > 256) return;
+  uint32_t part = 0;
+  for (int i = lane; i < nd; i += 64) part += desc_chunks(dl, i, nd);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_u32(part), 63);
+  if (total == 0) return;
+  // split(i) < t  <=>  E_i * splits < t * W
+  const uint32_t lo = (uint32_t)sp * total, hi = (uint32_t)(sp + 1) * total;
+  uint32_t carry = 0;
+  int nlo = 0, nhi = 0;
+  for (int i0 = 0; i0 < nd; i0 += 64) {
+    const int i = i0 + lane;
+    const uint32_t w = desc_chunks(dl, i, nd);
+    const uint32_t x = wave_incl_scan_u32(w);
+    const uint32_t e = (carry + x - w) * (uint32_t)splits;
+    carry += (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+    nlo += __popcll(__ballot(i < nd && e < lo));
+    nhi += __popcll(__ballot(i < nd && e < hi));
+  }
+  di = nlo;
+  d1 = sp == splits - 1 ? nd : nhi;
+}
+
 __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   const uint64_t v = (uint64_t)(uintptr_t)p;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -468,8 +528,7 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   Cursor cu;
   cu.dl = a.desc + (uint64_t)s * a.maxd;
   cu.packed = a.packed;
-  cu.di = (int)(((int64_t)sp * nd) / a.splits);
-  cu.d1 = (int)(((int64_t)(sp + 1) * nd) / a.splits);
+  split_range(cu.dl, nd, a.splits, sp, lane, cu.di, cu.d1);
   cu.T = 0;
   cu.c = 0;
   cu.t0 = 0;

@@ -121,15 +121,19 @@ def test_decode_ragged_descriptor_lists_and_empty_streams():
         descs[s, :len(lst)] = lst
         n_desc[s] = len(lst)
     q = w["q"].cuda()
-    out, lse = runtime.decode(q, to_dev_u8(buf), desc_to_dev(descs), n_kv_heads=w["Hkv"],
-                              max_desc_per_stream=maxd,
-                              n_desc=torch.tensor(n_desc.astype(np.int32)).cuda(),
-                              scale=float(SCALE))
-    torch.cuda.synchronize()
     ref, rlse = oracle_decode_all(w["q"], buf, descs, n_desc)
-    check_attention(out, lse, ref, rlse, "ragged")
     G = w["G"]
-    assert np.all(np.isneginf(lse.cpu().numpy().reshape(-1)[5 * G:6 * G]))
+    # default splits (at least one descriptor each), then 2 and 5 splits: more
+    # descriptors than splits, so each split takes an equal share of chunks
+    # (a dense 256-token segment is 22 chunks, a 13-token one 1)
+    for splits in (0, 2, 5):
+        out, lse = runtime.decode(q, to_dev_u8(buf), desc_to_dev(descs), n_kv_heads=w["Hkv"],
+                                  max_desc_per_stream=maxd,
+                                  n_desc=torch.tensor(n_desc.astype(np.int32)).cuda(),
+                                  decode_splits=splits, scale=float(SCALE))
+        torch.cuda.synchronize()
+        check_attention(out, lse, ref, rlse, f"ragged, splits={splits}")
+        assert np.all(np.isneginf(lse.cpu().numpy().reshape(-1)[5 * G:6 * G]))
 
 
 def test_decode_wide_rows_and_chunk_tails():

@@ -194,27 +194,6 @@ def make_kara(seed=0, device="cpu", B=None, prompt=None, gen=None):
     return dict(K=K, V=V, Qall=Qall, q=q, B=B, L=L, prompt=prompt, gen=gen, Hq=Hq, Hkv=Hkv, G=G)
 
 
-def kara_schedule(prompt, gen, window=512, delta=64, protect=64, seg=64, retention_pct=20):
-    """Compression events of the Kara workload.
-
-    Every ``delta`` generated tokens (length L after the step), the window is
-    the last ``window`` positions and the region is the ``seg`` tokens just
-    before the protected tail of ``protect`` tokens.  Events whose region lies
-    in the prompt are skipped (only generated tokens are compressed).  Returns
-    the list of (L, window_start, region_begin_in_window) plus T.
-    """
-    T = (retention_pct * seg + 50) // 100
-    ev = []
-    for e in range(1, gen // delta + 1):
-        L = prompt + delta * e
-        r0 = L - protect - seg
-        if r0 < prompt:
-            continue
-        w0 = L - window
-        ev.append((L, w0, r0 - w0))
-    return ev, T
-
-
 def u16(t):
     """bf16 tensor -> numpy uint16 bit patterns (host copy)."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

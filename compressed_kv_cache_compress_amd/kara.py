@@ -23,9 +23,24 @@ import torch
 
 from . import (PIPE_ASYNC, KvParams, KvPipe, kv_compress, kv_layout_query, kv_pipe_layout,
                pipe_config)
-from .gen import kara_schedule
 
 D = 128
+
+
+def event_schedule(prompt, generated, *, window, delta, protect, seg, retention_pct):
+    """Compression events of a Kara run, in firing order (the reading in the
+    module docstring).  Event k fires at length L = prompt + delta * k; its
+    region [L - protect - seg, L - protect) starts at or after the prompt
+    exactly when delta * k >= protect + seg, so the first event is k0 =
+    ceil((protect + seg) / delta) and the last k = generated div delta.
+    Returns ([(L, window start, region start inside the window)], T) with T =
+    round(r * seg) half up."""
+    T = (retention_pct * seg + 50) // 100
+    k0 = -(-(protect + seg) // delta)
+    rb = window - protect - seg
+    assert rb >= 0, "the window must hold the region and the protected tail"
+    return [(prompt + delta * k, prompt + delta * k - window, rb)
+            for k in range(k0, generated // delta + 1)], T
 
 
 def _seg_bytes_keep_all(tokens):
@@ -49,8 +64,8 @@ def build_cache(K, V, Qall, *, prompt, gen, window=512, delta=64, protect=64, se
     B, Hkv, L = K.shape[0], K.shape[1], K.shape[2]
     Hq = Qall.shape[1]
     assert L == prompt + gen and K.is_contiguous() and V.is_contiguous() and Qall.is_contiguous()
-    sched, T = kara_schedule(prompt, gen, window=window, delta=delta, protect=protect, seg=seg,
-                             retention_pct=retention_pct)
+    sched, T = event_schedule(prompt, gen, window=window, delta=delta, protect=protect, seg=seg,
+                              retention_pct=retention_pct)
     if events is not None:
         sched = [sched[i] for i in events]
     n_ev = len(sched)
@@ -130,8 +145,8 @@ class KaraPipeline:
         self.K, self.V, self.Qall = K, V, Qall
         self.window, self.delta, self.protect = window, delta, protect
         # prefix: events whose region ends by generated token `start`
-        sched, T = kara_schedule(prompt, gen, window=window, delta=delta, protect=protect,
-                                 seg=delta, retention_pct=retention_pct)
+        sched, T = event_schedule(prompt, gen, window=window, delta=delta, protect=protect,
+                                  seg=delta, retention_pct=retention_pct)
         pre = [e for e in sched if e[0] - protect <= prompt + start]
         self.T = T
         n_steps = gen - start if steps is None else steps

@@ -135,30 +135,36 @@ class PipelineOracle:
         self.w, self.kp, self.c = w, kp, c
         self.Kh, self.Vh, self.Qh = gen.u16(w["K"]), gen.u16(w["V"]), gen.u16(w["Qall"])
         self.G = kp.Hq // kp.Hkv
-        sched, self.T = gen.kara_schedule(kp.prompt, kp.L - kp.prompt, window=c["window"],
-                                          delta=c["delta"], protect=c["protect"], seg=c["delta"],
-                                          retention_pct=c["retention_pct"])
-        self.pre = [e for e in sched if e[0] - c["protect"] <= kp.prompt + kp.g0]
+        from oracle import kara as OK
+        sched, _ = OK.events(kp.prompt, kp.L - kp.prompt, window=c["window"], delta=c["delta"],
+                             protect=c["protect"], seg=c["delta"])
+        self.T = OK.kept_tokens(c["retention_pct"], c["delta"])
+        # events whose region ends by the pipeline's first token
+        self.pre = [e for e in sched if e["r1"] <= kp.prompt + kp.g0]
         assert len(self.pre) == kp.n_prefix_events and self.T == kp.T
         self.cache, self.prefix_cache, self.prefix_events = {}, {}, {}
 
-    def _event(self, s, Le):
-        """Oracle compression of the event at sequence length Le for stream s."""
+    def _event(self, s, L, w0, rb):
+        """Oracle compression for stream s of the event at sequence length L
+        whose window starts at w0 and whose region starts rb into it."""
         c = self.c
         b, h = divmod(s, self.kp.Hkv)
         G = self.G
-        w0 = Le - c["window"]
         return self.O.compress_stream(
-            self.Kh[b, h, w0:Le], self.Vh[b, h, w0:Le], self.Qh[b, h * G:(h + 1) * G, w0:Le],
+            self.Kh[b, h, w0:L], self.Vh[b, h, w0:L], self.Qh[b, h * G:(h + 1) * G, w0:L],
             S=c["delta"], strategies=[(self.T, 128)], budget_bytes=4 * c["delta"] * 128,
-            scale=SCALE, region_begin=c["window"] - c["protect"] - c["delta"],
-            region_len=c["delta"], t2c_alpha=c["alpha"], t2c_gamma=c["gamma"])
+            scale=SCALE, region_begin=rb, region_len=c["delta"], t2c_alpha=c["alpha"],
+            t2c_gamma=c["gamma"])
 
     def get(self, e, s, region):
-        """Pipeline event e (region = its (start, end) in pipeline tokens)."""
+        """Pipeline event e (region = its (start, end) in pipeline tokens, as
+        the oracle's pipeline schedule gives it)."""
         if (e, s) not in self.cache:
-            Le = self.kp.prompt + self.kp.g0 + region[1] + self.c["protect"]
-            self.cache[(e, s)] = self._event(s, Le)
+            base = self.kp.prompt + self.kp.g0
+            r0, r1 = base + region[0], base + region[1]
+            L = r1 + self.c["protect"]
+            w0 = L - self.c["window"]
+            self.cache[(e, s)] = self._event(s, L, w0, r0 - w0)
         return self.cache[(e, s)]
 
     def prefix(self, s):
@@ -169,9 +175,9 @@ class PipelineOracle:
             parts = [_rows_u8(self.Kh[b, h, :P]), _rows_u8(self.Vh[b, h, :P])]
             descs = [(0, P, 128, 0, 0x03, P)]
             off = 512 * P
-            for (Le, w0, rb) in self.pre:
-                r = self._event(s, Le)
-                self.prefix_events[(s, Le)] = r
+            for ev in self.pre:
+                r = self._event(s, ev["L"], ev["w0"], ev["rb"])
+                self.prefix_events[(s, ev["L"])] = r
                 off = self._append(parts, descs, off, r)
             self.prefix_cache[s] = (parts, descs, off)
         return self.prefix_cache[s]
@@ -275,8 +281,9 @@ def check_pipeline_finals(kp, oe, entries, streams, sample=None):
         oe.prefix(s)
         n_prompt = kp.cfg.prefix_desc - kp.n_prefix_events
         ev0 = kp.cfg.events_offset - kp.n_prefix_events * kp.layout.event_bytes
-        for i, (Le, w0, rb) in enumerate(oe.pre):
-            checks.append((n_prompt + i, oe.prefix_events[(s, Le)], ev0 + i * kp.layout.event_bytes))
+        for i, ev in enumerate(oe.pre):
+            checks.append((n_prompt + i, oe.prefix_events[(s, ev["L"])],
+                           ev0 + i * kp.layout.event_bytes))
         for slot, r, rel in checks:
             gd = d[s, slot]
             rd = r["desc"][0]

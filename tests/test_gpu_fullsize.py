@@ -110,11 +110,18 @@ def test_max_context_one_stream():
     _sampled("million", [0], Hq=4, Hkv=1, N=1 << 22)
 
 
+KARA_STREAMS = (0, 41, 106, 171, 244, 301, 406, 511)  # every kv head, batch entries 0..63
+
+
 def test_fullsize_kara():
     """Kara workload: B 64, GQA 32/8, prompt 16384 + 8192 generated, window 512,
     retention 20 % (13 of each 64-token region), Token2Chunk alpha 3 gamma 16,
     an event every 64 steps (127 events compress generated tokens); decode over
-    dense prompt + compressed segments + dense tail."""
+    dense prompt + compressed segments + dense tail.  The expected cache of
+    eight streams (every kv head) is built from the oracle's own event list
+    (oracle/kara.py), each event compressed by the oracle from its window, and
+    compared byte for byte with the library's cache."""
+    from oracle import kara as OK
     k = gen.KARA
     say("[fullsize] kara: generating")
     w = gen.make_kara(device="cuda")
@@ -126,16 +133,24 @@ def test_fullsize_kara():
     out, lse = runtime.decode(w["q"], cache.packed, cache.desc, n_kv_heads=w["Hkv"],
                               max_desc_per_stream=cache.max_desc, scale=float(SCALE))
     torch.cuda.synchronize()
-    assert cache.n_events == 127 and cache.T == 13
-    desc = cache.desc.cpu().numpy().view(DESC_DTYPE).reshape(w["B"] * w["Hkv"], cache.max_desc)
-    lay = cache.layout
-    assert np.all(desc[:, lay["n_prompt_desc"]:lay["n_prompt_desc"] + 127]["n_tok"] == 13)
-    assert desc["n_tok"].astype(np.int64).sum(axis=1).tolist() == [16384 + 127 * 13 + 64] * desc.shape[0]
-    G, Hkv = w["G"], w["Hkv"]
     prompt, L = w["prompt"], w["L"]
-    for s in (0, 301):
+    events, _ = OK.events(prompt, w["gen"], window=k["window"], delta=k["delta"],
+                          protect=k["protect"], seg=64)
+    T = OK.kept_tokens(k["retention_pct"], 64)
+    final = OK.final_tokens(prompt, w["gen"], delta=k["delta"], protect=k["protect"], seg=64,
+                            retention_pct=k["retention_pct"])
+    n_ev = len(events)
+    assert cache.n_events == n_ev and cache.T == T
+    n_prompt_desc = prompt // 256
+    assert cache.max_desc == n_prompt_desc + n_ev + 1
+    desc = cache.desc.cpu().numpy().view(DESC_DTYPE).reshape(w["B"] * w["Hkv"], cache.max_desc)
+    assert np.all(desc[:, n_prompt_desc:n_prompt_desc + n_ev]["n_tok"] == T)
+    assert desc["n_tok"].astype(np.int64).sum(axis=1).tolist() == [final] * desc.shape[0]
+    G, Hkv = w["G"], w["Hkv"]
+    tail = L - events[-1]["r1"]
+    for s in KARA_STREAMS:
         b, h = divmod(s, Hkv)
-        say(f"  oracle stream {s}: prompt, 127 events, tail")
+        say(f"  oracle stream {s}: prompt, {n_ev} events, tail")
         Kf, Vf = gen.u16(w["K"][b, h]), gen.u16(w["V"][b, h])
         Qf = gen.u16(w["Qall"][b, h * G:(h + 1) * G])
         zq = np.zeros((G, 1, 128), np.uint16)
@@ -144,28 +159,29 @@ def test_fullsize_kara():
         pr = O.compress_stream(Kf[:prompt], Vf[:prompt], zq, S=256, strategies=[(256, 128)],
                                budget_bytes=4 * 256 * 128, scale=SCALE)
         parts.append(pr["packed"])
-        d = pr["desc"].copy()
-        descs.append(d)
+        descs.append(pr["desc"].copy())
         off += pr["used"]
-        for (Le, w0, rb) in lay["schedule"]:
-            e = O.compress_stream(Kf[w0:w0 + 512], Vf[w0:w0 + 512], Qf[:, w0:w0 + 512], S=64,
-                                  strategies=[(13, 128)], budget_bytes=4 * 64 * 128, scale=SCALE,
-                                  region_begin=rb, region_len=64, t2c_alpha=3, t2c_gamma=16,
+        for ev in events:
+            e = O.compress_stream(Kf[ev["w0"]:ev["L"]], Vf[ev["w0"]:ev["L"]],
+                                  Qf[:, ev["w0"]:ev["L"]], S=64, strategies=[(T, 128)],
+                                  budget_bytes=4 * 64 * 128, scale=SCALE, region_begin=ev["rb"],
+                                  region_len=64, t2c_alpha=k["alpha"], t2c_gamma=k["gamma"],
                                   base_offset=off)
             parts.append(e["packed"])
             descs.append(e["desc"])
             off += e["used"]
-        tl = O.compress_stream(Kf[L - 64:], Vf[L - 64:], zq, S=64, strategies=[(64, 128)],
-                               budget_bytes=4 * 64 * 128, scale=SCALE, base_offset=off)
+        tl = O.compress_stream(Kf[L - tail:], Vf[L - tail:], zq, S=tail,
+                               strategies=[(tail, 128)], budget_bytes=4 * tail * 128,
+                               scale=SCALE, base_offset=off)
         parts.append(tl["packed"])
         descs.append(tl["desc"])
         ref_buf = np.concatenate(parts)
         ref_desc = np.concatenate(descs)
         got = cache.packed[s * cache.stream_bytes:s * cache.stream_bytes + ref_buf.size].cpu().numpy()
-        assert np.array_equal(got, ref_buf)
+        assert np.array_equal(got, ref_buf), f"kara stream {s}: packed bytes"
         gd = desc[s].copy()
         gd["offset"] -= s * cache.stream_bytes
-        assert np.array_equal(gd.view(np.uint8), ref_desc.view(np.uint8))
+        assert np.array_equal(gd.view(np.uint8), ref_desc.view(np.uint8)), f"kara stream {s}: descriptors"
         q = gen.u16(w["q"][b, h * G:(h + 1) * G])
         ref, rlse = O.decode_stream(q, ref_buf, ref_desc, SCALE)
         check_attention(out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G], ref, rlse,

@@ -465,14 +465,6 @@ def test_kara_window_scores(O):
     assert r["used"] == 13 * 512 + 32
 
 
-def test_kara_schedule():
-    ev, T = gen.kara_schedule(16384, 8192)
-    assert T == 13 and len(ev) == 127
-    L, w0, rb = ev[0]
-    assert L == 16384 + 128 and rb == 384 and w0 == L - 512
-    assert ev[-1][0] == 24576
-
-
 # ---------------------------------------------------------------------------
 # Query-aware segment selection (MosaicKV page, Fig. 6 caption: stage 2 runs
 # during decode before each attention layer; Sec. 5.3: sequence compression in

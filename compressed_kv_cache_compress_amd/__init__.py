@@ -49,7 +49,7 @@ class Params(ctypes.Structure):
                 ("desc_stream_stride", ctypes.c_uint32), ("max_desc_per_stream", ctypes.c_uint32),
                 ("decode_splits", ctypes.c_uint32), ("budget_scope", ctypes.c_uint32),
                 ("compress_max_waves", ctypes.c_uint32), ("rotate", ctypes.c_uint32),
-                ("store_logits", ctypes.c_uint32)]
+                ("store_logits", ctypes.c_uint32), ("rot_span", ctypes.c_uint32)]
 
 
 class Layout(ctypes.Structure):
@@ -151,7 +151,7 @@ class KvParams:
                  budget_bytes=0, t2c_alpha=0, t2c_gamma=0, scale=0.0, kv_stream_stride=0,
                  qw_head_stride=0, packed_stream_stride=0, packed_base_offset=0,
                  desc_stream_stride=0, max_desc_per_stream=0, decode_splits=0,
-                 budget_scope=0, compress_max_waves=0, rotate=0, store_logits=0):
+                 budget_scope=0, compress_max_waves=0, rotate=0, store_logits=0, rot_span=0):
         strategies = list(strategies)
         self._strat = (Strategy * max(1, len(strategies)))(*[Strategy(t, c) for t, c in strategies])
         if region_len is None:
@@ -174,6 +174,7 @@ class KvParams:
         p.compress_max_waves = compress_max_waves
         p.rotate = int(bool(rotate))
         p.store_logits = int(bool(store_logits))
+        p.rot_span = rot_span
         self.strategies = strategies
 
     @property

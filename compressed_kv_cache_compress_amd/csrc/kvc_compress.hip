@@ -4,8 +4,14 @@
 //
 // Pipeline per call (every kernel on the caller's stream):
 //   score_partials  per 64-token block of the domain and per window query:
-//                   block max m_b and pairwise sum z_b of exp(l - m_b)
-//   score_normalise per window query: global max m and 1/Z
+//                   the logits (stored for the later passes when asked) and
+//                   their block maximum m_b
+//   score_max       per window query: global max m = max of the m_b
+//   score_expsum    per block and window query: pairwise sum z_b of
+//                   exp(l - m) over the block's 64 tokens
+//   score_normalise per window query: Z = pairwise sum of the z_b over the
+//                   blocks (zero-padded to a power of two), i.e. the
+//                   pairwise sum of exp(l - m) over the whole domain; 1/Z
 //   token_scores    per region token: sum over the group's window queries of
 //                   exp(l - m) / Z, accumulated one query at a time
 //   channel_select  per region K and V vector and per channel count c < 128:
@@ -53,7 +59,7 @@ struct ScoreArgs {
   const uint16_t* K;
   const uint16_t* Qw;
   uint64_t kv_stride, qw_stride;
-  int hkv, hq, G, W, nq, nblk, region_begin, region_len;
+  int hkv, hq, G, W, nq, nblk, n_ctx, region_begin, region_len;
   int qper;  // window queries per wave of score_partials (at most 64, a multiple of 4)
   float scale;
 };
@@ -111,51 +117,37 @@ __device__ __forceinline__ void logits(const float* __restrict__ qr, const float
   for (int j = 0; j < NQ; ++j) l[j] = acc[j] * scale;
 }
 
-// Block maximum and pairwise exp-sum of NQ window queries q0.. over the 64
-// tokens of a block (lane = token).  With `lg`, the logits of region tokens
-// are also stored, [stream][query][region token], for the second pass.
+// Logits and block maximum of NQ window queries q0.. over the 64 tokens of a
+// block (lane = token).  With `lg`, the logits are also stored,
+// [stream][query][domain token], for the later passes.
 template <int NQ>
-__device__ __forceinline__ void block_partials(const float* __restrict__ qs, int q0, const float* kf,
-                                               const ScoreArgs& a, int s, int blk, int lane,
-                                               float* __restrict__ part_m,
-                                               float* __restrict__ part_z,
-                                               float* __restrict__ lg) {
-  float l[NQ], mb[NQ], z[NQ];
+__device__ __forceinline__ void block_max(const float* __restrict__ qs, int q0, const float* kf,
+                                          const ScoreArgs& a, int s, int blk, int lane,
+                                          float* __restrict__ part_m, float* __restrict__ lg) {
+  float l[NQ], mb[NQ];
   logits<NQ>(qs + (uint64_t)q0 * D, kf, a.scale, l);
   if (lg) {
-    const int tr = blk * BLK + lane - a.region_begin;
-    if (tr >= 0 && tr < a.region_len) {
+    const uint32_t t = (uint32_t)(blk * BLK + lane);
 #pragma unroll
-      for (int j = 0; j < NQ; ++j)
-        (lg + ((uint64_t)s * a.nq + q0 + j) * a.region_len)[(uint32_t)tr] = l[j];
-    }
+    for (int j = 0; j < NQ; ++j) (lg + ((uint64_t)s * a.nq + q0 + j) * a.n_ctx)[t] = l[j];
   }
 #pragma unroll
   for (int j = 0; j < NQ; ++j) mb[j] = l[j];
   max64_n_last<NQ>(mb);
-#pragma unroll
-  for (int j = 0; j < NQ; ++j) z[j] = spec_exp2((l[j] - mb[j]) * KVC_LOG2E);
-  tree_sum64_n_last<NQ>(z);
-  // lane 63 holds the sums
   if (lane == 63) {
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      const uint64_t o = ((uint64_t)s * a.nq + q0 + j) * a.nblk + blk;
-      part_m[o] = mb[j];
-      part_z[o] = z[j];
-    }
+    for (int j = 0; j < NQ; ++j) part_m[((uint64_t)s * a.nq + q0 + j) * a.nblk + blk] = mb[j];
   }
 }
 
 // grid (nblk, streams, ceil(nq / qper)), 64 threads: lane = token of the
 // 64-token block; wave z handles window queries z * qper .. (z + 1) * qper - 1
-// (each (query, block) partial is computed by exactly one wave, so the split
+// (each (query, block) result is computed by exactly one wave, so the split
 // changes no result; it fills the chip when a domain has few blocks and keeps
 // the window queries read at one time within the scalar cache).
 __global__ __launch_bounds__(64) void k_score_partials(ScoreArgs a, Units un,
                                                        const float* __restrict__ qf,
                                                        float* __restrict__ part_m,
-                                                       float* __restrict__ part_z,
                                                        float* __restrict__ lg) {
   const int lane = threadIdx.x;
   for (uint32_t u = blockIdx.x; u < un.total; u += gridDim.x) {
@@ -167,50 +159,130 @@ __global__ __launch_bounds__(64) void k_score_partials(ScoreArgs a, Units un,
     const float* qs = qf + (uint64_t)s * a.nq * D;
     int q0 = zq * a.qper;
     const int q1 = min(a.nq, q0 + a.qper);
-    for (; q0 + QB <= q1; q0 += QB)
-      block_partials<QB>(qs, q0, kf, a, s, blk, lane, part_m, part_z, lg);
-    for (; q0 < q1; ++q0) block_partials<1>(qs, q0, kf, a, s, blk, lane, part_m, part_z, lg);
+    for (; q0 + QB <= q1; q0 += QB) block_max<QB>(qs, q0, kf, a, s, blk, lane, part_m, lg);
+    for (; q0 < q1; ++q0) block_max<1>(qs, q0, kf, a, s, blk, lane, part_m, lg);
   }
 }
 
-// grid (nq, streams), 64 threads.  m = max of the block maxima; Z = pairwise
-// tree over the blocks (zero-padded to a power of two) of z_b exp(m_b - m):
-// groups of 64 consecutive blocks are summed across lanes, then the group
-// sums are combined pairwise in LDS.
+// grid (nq, streams), 64 threads: m = max of the block maxima of a query.
+__global__ __launch_bounds__(64) void k_score_max(ScoreArgs a, Units un,
+                                                  const float* __restrict__ part_m,
+                                                  float* __restrict__ norm_m) {
+  const int lane = threadIdx.x;
+  for (uint32_t u = blockIdx.x; u < un.total; u += gridDim.x) {
+    int qi, s, z_;
+    unit_xyz(un, u, qi, s, z_);
+    const float* pm = part_m + ((uint64_t)s * a.nq + qi) * a.nblk;
+    float mx = -INFINITY;
+    for (int b = lane; b < a.nblk; b += 64) mx = fmax_nn(mx, pm[b]);
+    const float m = max64(mx);
+    if (lane == 0) norm_m[(uint64_t)s * a.nq + qi] = m;
+  }
+}
+
+// z_b of NQ queries q0.. from their logits l (lane = token): pairwise sum of
+// exp(l - m) over the block, stored by lane 63.
+template <int NQ>
+__device__ __forceinline__ void block_expsum(const float* l, int q0, const ScoreArgs& a, int s,
+                                             int blk, int lane, const float* __restrict__ nm,
+                                             float* __restrict__ part_z) {
+  float z[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) z[j] = spec_exp2((l[j] - nm[q0 + j]) * KVC_LOG2E);
+  tree_sum64_n_last<NQ>(z);
+  if (lane == 63) {
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) part_z[((uint64_t)s * a.nq + q0 + j) * a.nblk + blk] = z[j];
+  }
+}
+
+// grid as k_score_partials: the block sums z_b with the global maximum,
+// logits recomputed (same fma chains, so the same values).
+__global__ __launch_bounds__(64) void k_score_expsum(ScoreArgs a, Units un,
+                                                     const float* __restrict__ qf,
+                                                     const float* __restrict__ norm_m,
+                                                     float* __restrict__ part_z) {
+  const int lane = threadIdx.x;
+  for (uint32_t u = blockIdx.x; u < un.total; u += gridDim.x) {
+    int blk, s, zq;
+    unit_xyz(un, u, blk, s, zq);
+    const int t = blk * BLK + lane;
+    float kf[D];
+    load_row_f32(a.K + (uint64_t)s * a.kv_stride + (uint64_t)t * D, kf);
+    const float* qs = qf + (uint64_t)s * a.nq * D;
+    const float* nm = norm_m + (uint64_t)s * a.nq;
+    int q0 = zq * a.qper;
+    const int q1 = min(a.nq, q0 + a.qper);
+    for (; q0 + QB <= q1; q0 += QB) {
+      float l[QB];
+      logits<QB>(qs + (uint64_t)q0 * D, kf, a.scale, l);
+      block_expsum<QB>(l, q0, a, s, blk, lane, nm, part_z);
+    }
+    for (; q0 < q1; ++q0) {
+      float l;
+      logits<1>(qs + (uint64_t)q0 * D, kf, a.scale, &l);
+      block_expsum<1>(&l, q0, a, s, blk, lane, nm, part_z);
+    }
+  }
+}
+
+// The same block sums from the stored logits ([stream][query][domain
+// token]), LQ queries loaded at a time.
+constexpr int LQ = 16;
+__global__ __launch_bounds__(64) void k_score_expsum_stored(ScoreArgs a, Units un,
+                                                            const float* __restrict__ lg,
+                                                            const float* __restrict__ norm_m,
+                                                            float* __restrict__ part_z) {
+  const int lane = threadIdx.x;
+  for (uint32_t u = blockIdx.x; u < un.total; u += gridDim.x) {
+    int blk, s, zq;
+    unit_xyz(un, u, blk, s, zq);
+    const float* lr = lg + (uint64_t)s * a.nq * a.n_ctx + (uint32_t)(blk * BLK + lane);
+    const float* nm = norm_m + (uint64_t)s * a.nq;
+    int q0 = zq * a.qper;
+    const int q1 = min(a.nq, q0 + a.qper);
+    for (; q0 + LQ <= q1; q0 += LQ) {
+      float l[LQ];
+#pragma unroll
+      for (int j = 0; j < LQ; ++j) l[j] = lr[(uint64_t)(q0 + j) * a.n_ctx];
+      block_expsum<LQ>(l, q0, a, s, blk, lane, nm, part_z);
+    }
+    for (; q0 < q1; ++q0) {
+      const float l = lr[(uint64_t)q0 * a.n_ctx];
+      block_expsum<1>(&l, q0, a, s, blk, lane, nm, part_z);
+    }
+  }
+}
+
+// grid (nq, streams), 64 threads.  Z = pairwise tree over the blocks
+// (zero-padded to a power of two) of z_b: groups of 64 consecutive blocks are
+// summed across lanes, then the group sums are combined pairwise in LDS.
+// Every block holds 64 tokens, so this is the pairwise tree over the domain's
+// tokens.
 constexpr int NORM_GROUPS = (1 << 22) / BLK / 64;  // n_ctx <= 2^22
 __global__ __launch_bounds__(64) void k_score_normalise(ScoreArgs a, Units un,
-                                                        const float* __restrict__ part_m,
                                                         const float* __restrict__ part_z,
-                                                        float* __restrict__ norm_m,
                                                         float* __restrict__ norm_iz) {
   __shared__ float grp[NORM_GROUPS];
   const int lane = threadIdx.x;
   // one wave: its LDS accesses execute in issue order, also across units
   for (uint32_t u = blockIdx.x; u < un.total; u += gridDim.x) {
-  int qi, s, z_;
-  unit_xyz(un, u, qi, s, z_);
-  const float* pm = part_m + ((uint64_t)s * a.nq + qi) * a.nblk;
-  const float* pz = part_z + ((uint64_t)s * a.nq + qi) * a.nblk;
-  float mx = -INFINITY;
-  for (int b = lane; b < a.nblk; b += 64) mx = fmax_nn(mx, pm[b]);
-  const float m = max64(mx);
-  const int ng = (a.nblk + 63) / 64;
-  int np = 1;
-  while (np < ng) np <<= 1;
-  for (int i = 0; i < ng; ++i) {
-    const int b = 64 * i + lane;
-    const float v = b < a.nblk ? pz[b] * spec_exp2((pm[b] - m) * KVC_LOG2E) : 0.0f;
-    const float t = tree_sum64(v);
-    if (lane == 0) grp[i] = t;
-  }
-  for (int i = ng + lane; i < np; i += 64) grp[i] = 0.0f;
-  // in-order LDS within the wave: level w reads [0, 2w) before writing [0, w)
-  for (int w = np >> 1; w >= 1; w >>= 1)
-    for (int j = lane; j < w; j += 64) grp[j] = grp[2 * j] + grp[2 * j + 1];
-  if (lane == 0) {
-    norm_m[(uint64_t)s * a.nq + qi] = m;
-    norm_iz[(uint64_t)s * a.nq + qi] = 1.0f / grp[0];
-  }
+    int qi, s, z_;
+    unit_xyz(un, u, qi, s, z_);
+    const float* pz = part_z + ((uint64_t)s * a.nq + qi) * a.nblk;
+    const int ng = (a.nblk + 63) / 64;
+    int np = 1;
+    while (np < ng) np <<= 1;
+    for (int i = 0; i < ng; ++i) {
+      const int b = 64 * i + lane;
+      const float t = tree_sum64(b < a.nblk ? pz[b] : 0.0f);
+      if (lane == 0) grp[i] = t;
+    }
+    for (int i = ng + lane; i < np; i += 64) grp[i] = 0.0f;
+    // in-order LDS within the wave: level w reads [0, 2w) before writing [0, w)
+    for (int w = np >> 1; w >= 1; w >>= 1)
+      for (int j = lane; j < w; j += 64) grp[j] = grp[2 * j] + grp[2 * j + 1];
+    if (lane == 0) norm_iz[(uint64_t)s * a.nq + qi] = 1.0f / grp[0];
   }
 }
 
@@ -261,11 +333,10 @@ __global__ __launch_bounds__(64) void k_token_scores(ScoreArgs a, Units un,
 }
 
 // The same scores from the logits the first pass stored ([stream][query]
-// [region token]): each term is computed from the same logit by the same
+// [domain token]): each term is computed from the same logit by the same
 // operations, in the same query order, so the scores are identical.  Logits
 // are loaded LQ queries at a time so that a wave keeps several loads in
 // flight.  grid (ceil(region_len/64), streams), 64 threads: lane = token.
-constexpr int LQ = 16;
 __global__ __launch_bounds__(64) void k_token_scores_stored(ScoreArgs a, Units un,
                                                             const float* __restrict__ lg,
                                                             const float* __restrict__ norm_m,
@@ -278,7 +349,7 @@ __global__ __launch_bounds__(64) void k_token_scores_stored(ScoreArgs a, Units u
     unit_xyz(un, u, bx, s, z_);
     const int tr = bx * 64 + lane;
     const bool valid = tr < a.region_len;
-    const float* lr = lg + (uint64_t)s * a.nq * a.region_len + (valid ? tr : 0);
+    const float* lr = lg + (uint64_t)s * a.nq * a.n_ctx + (uint32_t)(a.region_begin + (valid ? tr : 0));
     const float* nm = norm_m + (uint64_t)s * a.nq;
     const float* ni = norm_iz + (uint64_t)s * a.nq;
     float sc = 0.0f;
@@ -286,7 +357,7 @@ __global__ __launch_bounds__(64) void k_token_scores_stored(ScoreArgs a, Units u
     for (; q0 + LQ <= a.nq; q0 += LQ) {
       float l[LQ];
 #pragma unroll
-      for (int j = 0; j < LQ; ++j) l[j] = lr[(uint64_t)(q0 + j) * a.region_len];
+      for (int j = 0; j < LQ; ++j) l[j] = lr[(uint64_t)(q0 + j) * a.n_ctx];
 #pragma unroll
       for (int j = 0; j < LQ; ++j) {
         const float e = spec_exp2((l[j] - nm[q0 + j]) * KVC_LOG2E);
@@ -294,7 +365,7 @@ __global__ __launch_bounds__(64) void k_token_scores_stored(ScoreArgs a, Units u
       }
     }
     for (; q0 < a.nq; ++q0) {
-      const float e = spec_exp2((lr[(uint64_t)q0 * a.region_len] - nm[q0]) * KVC_LOG2E);
+      const float e = spec_exp2((lr[(uint64_t)q0 * a.n_ctx] - nm[q0]) * KVC_LOG2E);
       sc = sc + e * ni[q0];
     }
     if (valid) {
@@ -1111,6 +1182,7 @@ hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
     sa.W = p.W;
     sa.nq = p.nq;
     sa.nblk = p.nblk;
+    sa.n_ctx = p.nblk * BLK;
     sa.region_begin = p.region_begin;
     sa.region_len = p.region_len;
     sa.scale = p.scale;
@@ -1132,9 +1204,17 @@ hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
     const Units up{(uint32_t)p.nblk, (uint32_t)p.streams, (uint32_t)(p.nblk * p.streams * qsplit)};
     hipLaunchKernelGGL(k_q_convert, capped(uq, 1, p.max_waves), dim3(64), 0, st, sa, uq, p.qf);
     hipLaunchKernelGGL(k_score_partials, capped(up, 1, p.max_waves), dim3(64), 0, st, sa, up,
-                       (const float*)p.qf, p.part_m, p.part_z, p.logits);
+                       (const float*)p.qf, p.part_m, p.logits);
+    hipLaunchKernelGGL(k_score_max, capped(uq, 1, p.max_waves), dim3(64), 0, st, sa, uq,
+                       (const float*)p.part_m, p.norm_m);
+    if (p.logits)
+      hipLaunchKernelGGL(k_score_expsum_stored, capped(up, 1, p.max_waves), dim3(64), 0, st, sa,
+                         up, (const float*)p.logits, (const float*)p.norm_m, p.part_z);
+    else
+      hipLaunchKernelGGL(k_score_expsum, capped(up, 1, p.max_waves), dim3(64), 0, st, sa, up,
+                         (const float*)p.qf, (const float*)p.norm_m, p.part_z);
     hipLaunchKernelGGL(k_score_normalise, capped(uq, 1, p.max_waves), dim3(64), 0, st, sa, uq,
-                       (const float*)p.part_m, (const float*)p.part_z, p.norm_m, p.norm_iz);
+                       (const float*)p.part_z, p.norm_iz);
     const uint32_t tx = (uint32_t)(p.region_len + 63) / 64;
     const Units ut{tx, (uint32_t)p.streams, tx * (uint32_t)p.streams};
     if (p.logits)
@@ -1163,6 +1243,8 @@ hipError_t launch_compress(const CompressPlan& p, hipStream_t st) {
     rp.region_begin = p.region_begin;
     rp.region_len = p.region_len;
     rp.streams = p.streams;
+    rp.n_span = p.n_span;
+    rp.span_len = p.span_len;
     rp.gram = p.gram;
     rp.rot = p.rot;
     rp.YK = p.YK;

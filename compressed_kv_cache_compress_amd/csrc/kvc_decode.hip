@@ -100,6 +100,9 @@ struct DecodeArgs {
   float* part_ml;
   float* part_acc;
   int hkv, hq, G, maxd, splits, items;
+  // rotation spans (QLO only): descriptor i is in span i / span_desc, split
+  // sp covers span sp / spl, and the queries are [row][n_span][128]
+  int n_span, span_desc, spl;
   float sl2;  // scale * log2(e)
 };
 
@@ -482,6 +485,10 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   const int s = item / a.splits, sp = item - s * a.splits;
   const int grp = lane >> 4, col = lane & 15;
   const int b = s / a.hkv, h = s - b * a.hkv;
+  // rotation span of this split (QLO with spans): its queries are rotated by
+  // the span's R_K
+  const int span = (QLO && a.span_desc) ? sp / a.spl : 0;
+  const uint64_t qrow_mul = QLO ? (uint64_t)a.n_span : 1u;
   WaveLds<JG>& L = wl[wv];
   for (int i = lane; i < 2 * 4 * JG * CT; i += 64) (&L.pl[0][0])[i] = 0;
 
@@ -492,7 +499,7 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   const int hh = lo_row ? (col >> 2) : 4 * (col & 3) + (col >> 2);
   const bool hh_ok = lo_row || hh < a.G;
   const uint16_t* qh = (lo_row ? a.q_lo : a.q) +
-                       ((uint64_t)(b * a.hq + h * a.G + (hh_ok ? hh : 0))) * D;
+                       ((uint64_t)(b * a.hq + h * a.G + (hh_ok ? hh : 0)) * qrow_mul + span) * D;
   bf16x8_t qa[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -502,7 +509,8 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   }
   bf16x8_t qlo[QLO && !LO_ROWS ? 4 : 1];
   if constexpr (QLO && !LO_ROWS) {
-    const uint16_t* ql = a.q_lo + ((uint64_t)(b * a.hq + h * a.G + (hh_ok ? hh : 0))) * D;
+    const uint16_t* ql =
+        a.q_lo + ((uint64_t)(b * a.hq + h * a.G + (hh_ok ? hh : 0)) * qrow_mul + span) * D;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       u32x4_t v = {0u, 0u, 0u, 0u};
@@ -528,7 +536,16 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   Cursor cu;
   cu.dl = a.desc + (uint64_t)s * a.maxd;
   cu.packed = a.packed;
-  split_range(cu.dl, nd, a.splits, sp, lane, cu.di, cu.d1);
+  if (QLO && a.span_desc) {
+    // an equal share of the span's descriptors
+    const int s0 = span * a.span_desc;
+    const int n = max(0, min(nd, s0 + a.span_desc) - s0);
+    const int sub = sp - span * a.spl;
+    cu.di = s0 + (int)(((int64_t)sub * n) / a.spl);
+    cu.d1 = s0 + (int)(((int64_t)(sub + 1) * n) / a.spl);
+  } else {
+    split_range(cu.dl, nd, a.splits, sp, lane, cu.di, cu.d1);
+  }
   cu.T = 0;
   cu.c = 0;
   cu.t0 = 0;
@@ -796,64 +813,85 @@ __global__ __launch_bounds__(RG * RC) void k_decode_reduce(const float* __restri
   if (lse && blockIdx.y == 0 && c == 0) lse[r] = any ? l2 * 0.69314718055994530942f : -INFINITY;
 }
 
-// Rotated cache: the same merge over all 128 channels (grid batch*n_q_heads,
-// four slices of RC channels per block, one after the other), then
-// out = R_V o' (o' = the merged output in the rotated basis, fp32) before the
-// single bf16 rounding.  R_V of row r's stream is read row by row.
-template <int RG, int RC>
-__global__ __launch_bounds__(RG * RC) void k_decode_reduce_rot(const float* __restrict__ part_ml,
-                                                             const float* __restrict__ part_acc,
-                                                             const float* __restrict__ rot,
-                                                             uint16_t* __restrict__ out,
-                                                             float* __restrict__ lse, int splits,
-                                                             int hq, int hkv) {
+// Rotated cache: per span, the merge of the span's splits (every split
+// weighted against the maximum M over all splits of the row) over all 128
+// channels, rotated back by the span's R_V and added up; out = sum / L,
+// with L the merged denominator, then the single bf16 rounding.  grid
+// (batch*n_q_heads), 128 threads: thread c owns output channel c.  Split sp
+// belongs to span sp / spl (spl = splits when there is one span).
+__global__ __launch_bounds__(128) void k_decode_reduce_rot(const float* __restrict__ part_ml,
+                                                           const float* __restrict__ part_acc,
+                                                           const float* __restrict__ rot,
+                                                           uint16_t* __restrict__ out,
+                                                           float* __restrict__ lse, int splits,
+                                                           int spl, int n_span, int hq, int hkv) {
   __shared__ float o1[D];
-  const int r = blockIdx.x, c = threadIdx.x % RC;
+  __shared__ float red[2][D];
+  const int r = blockIdx.x, c = threadIdx.x;
   const int b = r / hq, hd = r - b * hq;
   const int s = b * hkv + hd / (hq / hkv);
-  bool any = true;
-  float l2 = 0.0f;
-  for (int c0 = 0; c0 < D; c0 += RC) {
-    float o;
-    any = merge_splits<RG, RC>(part_ml + (uint64_t)r * splits * 2,
-                               part_acc + (uint64_t)r * splits * D, splits, c0, &o, &l2);
-    // `any` is uniform over the block: every thread takes the same path
-    if (!any) break;
-    if (threadIdx.x < RC) o1[c0 + c] = o;
-    __syncthreads();  // the next slice rewrites the group states
+  const float* ml = part_ml + (uint64_t)r * splits * 2;
+  const float* acc = part_acc + (uint64_t)r * splits * D;
+  // M and L over all splits (thread c folds splits c, c + 128, ...)
+  float m = -INFINITY;
+  for (int sp = c; sp < splits; sp += D) m = fmaxf(m, ml[2 * sp]);
+  red[0][c] = m;
+  __syncthreads();
+  for (int w = D / 2; w >= 1; w >>= 1) {
+    if (c < w) red[0][c] = fmaxf(red[0][c], red[0][c + w]);
+    __syncthreads();
   }
-  static_assert(RG * RC >= D, "one thread per output channel");
-  if (!any) {
-    if (threadIdx.x < D) out[(uint64_t)r * D + threadIdx.x] = 0;
-    if (lse && threadIdx.x == 0) lse[r] = -INFINITY;
+  const float M = red[0][0];
+  if (M == -INFINITY) {
+    out[(uint64_t)r * D + c] = 0;
+    if (lse && c == 0) lse[r] = -INFINITY;
     return;
   }
-  if (threadIdx.x >= D) return;
-  const int ch = threadIdx.x;
-  const float* RV = rot + ((uint64_t)s * 2 + 1) * D * D + (uint64_t)ch * D;
+  float l = 0.0f;
+  for (int sp = c; sp < splits; sp += D) l += ml[2 * sp + 1] * exp2f(ml[2 * sp] - M);
+  red[1][c] = l;
+  __syncthreads();
+  for (int w = D / 2; w >= 1; w >>= 1) {
+    if (c < w) red[1][c] += red[1][c + w];
+    __syncthreads();
+  }
+  const float L = red[1][0];
   float v = 0.0f;
-  for (int k = 0; k < D; ++k) v = __builtin_fmaf(RV[k], o1[k], v);
-  out[(uint64_t)r * D + ch] = (uint16_t)f2bf(v);
-  if (lse && ch == 0) lse[r] = l2 * 0.69314718055994530942f;
+  for (int span = 0; span < n_span; ++span) {
+    float a = 0.0f;
+    for (int sp = span * spl; sp < (span + 1) * spl; ++sp) {
+      const float m_sp = ml[2 * sp];
+      if (m_sp != -INFINITY) a += acc[(uint64_t)sp * D + c] * exp2f(m_sp - M);
+    }
+    __syncthreads();  // the previous span's o1 is read by every thread
+    o1[c] = a;
+    __syncthreads();
+    const float* RV = rot + (((uint64_t)s * n_span + span) * 2 + 1) * D * D + (uint64_t)c * D;
+    for (int k = 0; k < D; ++k) v = __builtin_fmaf(RV[k], o1[k], v);
+  }
+  out[(uint64_t)r * D + c] = (uint16_t)f2bf(v / L);
+  if (lse && c == 0) lse[r] = (M + log2f(L)) * 0.69314718055994530942f;
 }
 
 // Rotated queries for a rotated cache: q'[k] = fma chain over i of
-// q[i] R_K[i][k] in fp32, stored as its bf16 rounding hi and the bf16
-// rounding of the remainder lo.  grid (batch * hq), 128 threads: thread k.
+// q[i] R_K[i][k] in fp32 with the R_K of each span, stored as its bf16
+// rounding hi and the bf16 rounding of the remainder lo, [row][n_span][128].
+// grid (batch * hq, n_span), 128 threads: thread k.
 __global__ __launch_bounds__(128) void k_rotate_q(const uint16_t* __restrict__ q,
                                                   const float* __restrict__ rot,
                                                   uint16_t* __restrict__ qhi,
                                                   uint16_t* __restrict__ qlo, int hq, int hkv) {
-  const int r = blockIdx.x, k = threadIdx.x;
+  const int r = blockIdx.x, span = blockIdx.y, n_span = gridDim.y, k = threadIdx.x;
   const int b = r / hq, hd = r - b * hq;
   const int s = b * hkv + hd / (hq / hkv);
-  const float* RK = rot + (uint64_t)s * 2 * D * D;
+  const float* RK = rot + ((uint64_t)s * n_span + span) * 2 * D * D;
   const uint16_t* qr = q + (uint64_t)r * D;
   float acc = 0.0f;
   for (int i = 0; i < D; ++i) acc = __builtin_fmaf(bf2f(qr[i]), RK[i * D + k], acc);
   const uint32_t hi = f2bf(acc);
-  qhi[(uint64_t)r * D + k] = (uint16_t)hi;
-  qlo[(uint64_t)r * D + k] = (uint16_t)f2bf(acc - bf2f(hi));
+  const uint64_t o = ((uint64_t)r * n_span + span) * D + k;
+  qhi[o] = (uint16_t)hi;
+  qlo[o] = (uint16_t)f2bf(acc - bf2f(hi));
 }
 
 hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
@@ -871,26 +909,22 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
   a.maxd = p.maxd;
   a.splits = p.splits;
   a.items = p.streams * p.splits;
+  a.n_span = p.n_span;
+  a.span_desc = p.span_desc;
+  a.spl = p.spl;
   a.sl2 = p.scale * KVC_LOG2E;
   const dim3 grid((a.items + WAVES - 1) / WAVES);
   if (p.rot) {
-    hipLaunchKernelGGL(k_rotate_q, dim3(p.batch * p.hq), dim3(128), 0, st, p.q, p.rot, p.qhi,
-                       p.qlo, p.hq, p.hkv);
+    hipLaunchKernelGGL(k_rotate_q, dim3(p.batch * p.hq, p.n_span), dim3(128), 0, st, p.q, p.rot,
+                       p.qhi, p.qlo, p.hq, p.hkv);
     if (p.G <= 4)
       hipLaunchKernelGGL((k_decode_split<1, true>), grid, dim3(64 * WAVES), 0, st, a);
     else if (p.G <= 8)
       hipLaunchKernelGGL((k_decode_split<2, true>), grid, dim3(64 * WAVES), 0, st, a);
     else
       hipLaunchKernelGGL((k_decode_split<4, true>), grid, dim3(64 * WAVES), 0, st, a);
-    if (p.splits > 32)
-      hipLaunchKernelGGL((k_decode_reduce_rot<32, 32>), dim3(p.batch * p.hq), dim3(1024), 0, st,
-                         p.part_ml, p.part_acc, p.rot, p.out, p.lse, p.splits, p.hq, p.hkv);
-    else if (p.splits > 8)
-      hipLaunchKernelGGL((k_decode_reduce_rot<8, 128>), dim3(p.batch * p.hq), dim3(1024), 0, st,
-                         p.part_ml, p.part_acc, p.rot, p.out, p.lse, p.splits, p.hq, p.hkv);
-    else
-      hipLaunchKernelGGL((k_decode_reduce_rot<1, 128>), dim3(p.batch * p.hq), dim3(128), 0, st,
-                         p.part_ml, p.part_acc, p.rot, p.out, p.lse, p.splits, p.hq, p.hkv);
+    hipLaunchKernelGGL(k_decode_reduce_rot, dim3(p.batch * p.hq), dim3(D), 0, st, p.part_ml,
+                       p.part_acc, p.rot, p.out, p.lse, p.splits, p.spl, p.n_span, p.hq, p.hkv);
     return hipGetLastError();
   }
   if (p.G <= 4)

@@ -51,6 +51,9 @@ kvc_status compress_layout(const kvc_params* p, const Shape& sh, kvc_layout* L, 
     return KVC_E_INVALID;
   if (p->budget_scope > KVC_BUDGET_STREAM) return KVC_E_INVALID;
   if (p->rotate > 1 || p->store_logits > 1) return KVC_E_INVALID;
+  if (p->rot_span && (!p->rotate || p->rot_span % 64 || p->rot_span % p->seg_tokens ||
+                      p->region_len % p->rot_span))
+    return KVC_E_INVALID;
   const bool stream_scope = p->budget_scope == KVC_BUDGET_STREAM;
   const uint32_t S = p->seg_tokens;
   if (!pow2(S) || S < 16 || S > 256) return KVC_E_INVALID;
@@ -125,24 +128,46 @@ kvc_status compress_layout(const kvc_params* p, const Shape& sh, kvc_layout* L, 
   ws += align_up((uint64_t)sh.streams * n_seg * ((S + 31) / 32) * 4, kAlign);
   // window queries converted to fp32 once per call
   if (p->n_win) ws += align_up((uint64_t)sh.streams * nq * KVC_HEAD_DIM * 4, kAlign);
-  // store_logits: every window-query logit of the region
-  if (p->n_win && p->store_logits) ws += align_up((uint64_t)sh.streams * nq * p->region_len * 4, kAlign);
+  // store_logits: every window-query logit of the domain
+  if (p->n_win && p->store_logits) ws += align_up((uint64_t)sh.streams * nq * p->n_ctx * 4, kAlign);
   // stream scope: keep sets and objectives of every strategy
   if (stream_scope) {
     ws += align_up((uint64_t)sh.streams * n_seg * p->n_strategies * ((S + 31) / 32) * 4, kAlign);
     ws += align_up((uint64_t)sh.streams * n_seg * p->n_strategies * 4, kAlign);
   }
-  // rotation: partial Gram matrices and the rotated region vectors
+  // rotation: the Gram matrix of every span and side, the rotated region vectors
   if (p->rotate) {
-    ws += align_up((uint64_t)sh.streams * 2 * 8 * KVC_HEAD_DIM * KVC_HEAD_DIM * 4, kAlign);
+    const uint64_t n_span = p->rot_span ? p->region_len / p->rot_span : 1;
+    ws += align_up((uint64_t)sh.streams * n_span * 2 * KVC_HEAD_DIM * KVC_HEAD_DIM * 4, kAlign);
     ws += 2 * align_up((uint64_t)sh.streams * p->region_len * KVC_HEAD_DIM * 2, kAlign);
   }
   L->compress_ws_bytes = ws;
   return nfeas ? KVC_OK : KVC_E_BUDGET;
 }
 
+// Rotation spans of a decode list: descriptor i is in span i / span_desc
+// (one span holding every descriptor when the cache has no rotation spans).
+struct DecodeSpans {
+  uint32_t n_span, span_desc;
+};
+DecodeSpans decode_spans(const kvc_params* p, uint32_t maxd) {
+  DecodeSpans d{1u, maxd};
+  if (p->rotate && p->rot_span && p->seg_tokens && p->rot_span % p->seg_tokens == 0) {
+    d.span_desc = p->rot_span / p->seg_tokens;
+    d.n_span = (maxd + d.span_desc - 1) / d.span_desc;
+  }
+  return d;
+}
+
+constexpr uint32_t kMaxSplits = 65536;  // split-K factor per stream (a caller's value included)
+
+// 0 when the caller's split count cannot be used.
 uint32_t choose_splits(const kvc_params* p, const Shape& sh, uint32_t maxd) {
-  if (p->decode_splits) return p->decode_splits;
+  const DecodeSpans sp = decode_spans(p, maxd);
+  if (p->decode_splits) {
+    if (p->decode_splits > kMaxSplits || p->decode_splits % sp.n_span) return 0;
+    return p->decode_splits;
+  }
   // one wave per (stream, split); a CU holds 12 decode waves for groups of up
   // to 4 q heads and 8 for larger groups (LDS and registers): fill 256 CUs
   // once, with at least one descriptor per split
@@ -151,17 +176,30 @@ uint32_t choose_splits(const kvc_params* p, const Shape& sh, uint32_t maxd) {
   if (want > maxd) want = maxd;
   if (want < 1) want = 1;
   if (want > 1024) want = 1024;
+  // with rotation spans, every split stays inside one span
+  if (sp.n_span > 1) {
+    uint32_t per = (want + sp.n_span - 1) / sp.n_span;
+    if (per > sp.span_desc) per = sp.span_desc;
+    want = sp.n_span * per;
+  }
   return want;
 }
 
-void decode_layout(const kvc_params* p, const Shape& sh, uint32_t maxd, kvc_layout* L) {
+// false when the split count is unusable (caller's value out of range, or
+// more (stream, split) items than an int holds).
+bool decode_layout(const kvc_params* p, const Shape& sh, uint32_t maxd, kvc_layout* L) {
   const uint32_t splits = choose_splits(p, sh, maxd ? maxd : 1);
+  if (splits == 0 || (uint64_t)sh.streams * splits > 0x7FFFFFFFull) return false;
   L->decode_splits = splits;
   const uint64_t rows = (uint64_t)sh.batch * sh.hq * splits;
   L->decode_ws_bytes = align_up(rows * 2 * 4, kAlign) + align_up(rows * KVC_HEAD_DIM * 4, kAlign);
-  // rotated cache: the rotated queries' two bf16 parts
-  if (p->rotate)
-    L->decode_ws_bytes += 2 * align_up((uint64_t)sh.batch * sh.hq * KVC_HEAD_DIM * 2, kAlign);
+  // rotated cache: the rotated queries' two bf16 parts, per span
+  if (p->rotate) {
+    const uint64_t n_span = decode_spans(p, maxd ? maxd : 1).n_span;
+    L->decode_ws_bytes +=
+        2 * align_up((uint64_t)sh.batch * sh.hq * n_span * KVC_HEAD_DIM * 2, kAlign);
+  }
+  return true;
 }
 
 uint32_t decode_maxd(const kvc_params* p) {
@@ -202,8 +240,11 @@ kvc_status kv_layout_query(const kvc_params* p, kvc_layout* out) {
     if (cs != KVC_OK && cs != KVC_E_BUDGET) return cs;
   }
   const uint32_t maxd = decode_maxd(p);
-  if (maxd) decode_layout(p, sh, maxd, out);
-  else if (p->n_strategies == 0) return KVC_E_INVALID;
+  if (maxd) {
+    if (!decode_layout(p, sh, maxd, out)) return KVC_E_INVALID;
+  } else if (p->n_strategies == 0) {
+    return KVC_E_INVALID;
+  }
   return cs;
 }
 
@@ -301,7 +342,7 @@ kvc_status compress_impl(const kvc_params* p, const uint16_t* K, const uint16_t*
   c.keep = reinterpret_cast<uint32_t*>(take(S64 * c.n_seg * ((c.S + 31) / 32) * 4));
   c.qf = p->n_win ? reinterpret_cast<float*>(take(S64 * c.nq * D * 4)) : nullptr;
   c.logits = p->n_win && p->store_logits
-                 ? reinterpret_cast<float*>(take(S64 * c.nq * (uint64_t)c.region_len * 4))
+                 ? reinterpret_cast<float*>(take(S64 * c.nq * (uint64_t)p->n_ctx * 4))
                  : nullptr;
   c.stream_budget = stream_scope;
   c.stream_bytes = (uint64_t)L.n_seg * p->budget_bytes;
@@ -318,7 +359,9 @@ kvc_status compress_impl(const kvc_params* p, const uint16_t* K, const uint16_t*
   c.gram = nullptr;
   c.YK = c.YV = nullptr;
   if (c.rotate) {
-    c.gram = reinterpret_cast<float*>(take(S64 * 2 * 8 * D * D * 4));
+    c.span_len = p->rot_span ? (int)p->rot_span : c.region_len;
+    c.n_span = c.region_len / c.span_len;
+    c.gram = reinterpret_cast<float*>(take(S64 * (uint64_t)c.n_span * 2 * D * D * 4));
     c.YK = reinterpret_cast<uint16_t*>(take(S64 * c.region_len * D * 2));
     c.YV = reinterpret_cast<uint16_t*>(take(S64 * c.region_len * D * 2));
   }
@@ -387,9 +430,11 @@ kvc_status decode_impl(const kvc_params* p, const uint16_t* q, const void* packe
   if (maxd == 0 || !q || !out || !desc || !packed) return KVC_E_INVALID;
   if (!aligned16(q) || !aligned16(packed) || !aligned16(desc) || !aligned16(out) || !aligned16(ws))
     return KVC_E_ALIGN;
+  if (p->rot_span && (!p->rotate || !p->seg_tokens || p->rot_span % p->seg_tokens))
+    return KVC_E_INVALID;
   kvc_layout L;
   std::memset(&L, 0, sizeof L);
-  decode_layout(p, sh, maxd, &L);
+  if (!decode_layout(p, sh, maxd, &L)) return KVC_E_INVALID;
   if (ws_bytes < L.decode_ws_bytes || !ws) return KVC_E_WORKSPACE;
   DecodePlan d;
   d.batch = sh.batch;
@@ -414,8 +459,18 @@ kvc_status decode_impl(const kvc_params* p, const uint16_t* q, const void* packe
   w += align_up(rows * KVC_HEAD_DIM * 4, kAlign);
   d.rot = rot;
   d.qhi = d.qlo = nullptr;
+  d.n_span = 1;
+  d.span_desc = 0;
+  d.spl = d.splits;
   if (rot) {
-    const uint64_t qb = align_up((uint64_t)sh.batch * sh.hq * KVC_HEAD_DIM * 2, kAlign);
+    const DecodeSpans sp = decode_spans(p, maxd);
+    d.n_span = (int)sp.n_span;
+    if (sp.n_span > 1) {
+      d.span_desc = (int)sp.span_desc;
+      d.spl = d.splits / d.n_span;
+    }
+    const uint64_t qb =
+        align_up((uint64_t)sh.batch * sh.hq * sp.n_span * KVC_HEAD_DIM * 2, kAlign);
     d.qhi = reinterpret_cast<uint16_t*>(w);
     d.qlo = reinterpret_cast<uint16_t*>(w + qb);
   }

@@ -40,7 +40,7 @@ struct CompressPlan {
   // workspace carve-up (device pointers)
   float *part_m, *part_z, *norm_m, *norm_iz, *scores, *rho;
   float* qf;              // window queries in fp32, [streams][G * W][128]
-  float* logits;          // store_logits: [streams][G * W][region_len] fp32, else null
+  float* logits;          // store_logits: [streams][G * W][n_ctx] fp32, else null
   uint32_t* masks;        // [streams][region_len][nc][2][4]
   uint32_t* keep;         // [streams][n_seg][S/32]
   // per-stream budget (budget_scope == KVC_BUDGET_STREAM)
@@ -51,8 +51,9 @@ struct CompressPlan {
   float* J_all;           // [streams][n_seg][n_strat]
   // SVD rotation before channel selection (kvc_rotate.hip)
   bool rotate;
-  float* rot;             // [streams][2][128][128] output: R_K, R_V
-  float* gram;            // [streams][2][8][128][128] partial Gram matrices
+  int n_span, span_len;   // rotation spans of the region (1 span: the whole region)
+  float* rot;             // [streams][n_span][2][128][128] output: R_K, R_V
+  float* gram;            // [streams][n_span][2][128][128] Gram matrices
   uint16_t *YK, *YV;      // [streams][region_len][128] rotated region vectors
 };
 
@@ -60,6 +61,7 @@ struct RotatePlan {
   const uint16_t *K, *V;
   uint64_t kv_stride;
   int region_begin, region_len, streams;
+  int n_span, span_len;
   float* gram;
   float* rot;
   uint16_t *YK, *YV;
@@ -75,10 +77,13 @@ struct DecodePlan {
   uint16_t* out;
   float* lse;
   float *part_ml, *part_acc;
-  // rotated cache (null when not rotated): R_K, R_V per stream and the
-  // rotated queries' bf16 parts in the workspace
+  // rotated cache (null when not rotated): R_K, R_V per stream and span
+  // ([streams][n_span][2][128][128]) and the rotated queries' bf16 parts in
+  // the workspace ([batch * hq][n_span][128]); descriptor i of a stream is
+  // in span i / span_desc, and split sp covers descriptors of span sp / spl
   const float* rot;
   uint16_t *qhi, *qlo;
+  int n_span, span_desc, spl;
 };
 
 // Query-aware segment selection (kvc_select.hip).

@@ -4,16 +4,19 @@
 // SVD, the vectors rotated before the top-r elements of each are kept;
 // Fig. 4: after the rotation the important elements sit in a few channels).
 //
-// One R per stream and side (K, V), from the region one call compresses:
-//   gram_partial  X^T X over eight consecutive token groups, each an fma
-//                 chain in token order (64 x 64 tiles, 4 x 4 per thread)
-//   jacobi        the eight partials summed pairwise, then cyclic Jacobi in
-//                 fp32: 127 rounds of 64 disjoint rotations per sweep, each
-//                 round's rotations computed from the matrix as it stands,
-//                 applied to its rows, its columns and the eigenvector
-//                 columns; R = eigenvectors ordered by eigenvalue (largest
-//                 first, ties to the lower index)
-//   rotate_vec    y = R^T x rounded to bf16 for every region vector
+// One R per span and side (K, V): the region one call compresses is cut into
+// spans of span_len tokens (one span when the caller asks for none):
+//   gram          X^T X of each span, every entry one fma chain over the
+//                 span's tokens in order (64 x 64 tiles, 4 x 4 per thread)
+//   jacobi        cyclic Jacobi in fp32 with the round-robin (tournament)
+//                 pair ordering of parallel Jacobi methods: 127 rounds of 64
+//                 rotations on disjoint index pairs per sweep, each round's
+//                 rotations computed from the matrix as it stands and applied
+//                 to its rows, its columns and the eigenvector columns; R =
+//                 eigenvectors ordered by eigenvalue (largest first, ties to
+//                 the lower index)
+//   rotate_vec    y = R^T x rounded to bf16 for every region vector, with the
+//                 R of its span
 // Every operation is a correctly rounded fp32 operation in a fixed order
 // (division and square root correctly rounded, no contraction), so R and
 // the rotated vectors are reproducible bit for bit.
@@ -26,27 +29,24 @@
 namespace kvc {
 
 constexpr int JSWEEPS = 10;   // Jacobi sweeps
-constexpr int GGROUPS = 8;    // token groups of the Gram matrix
 constexpr int APAD = D + 1;   // LDS row stride of the Jacobi matrices (conflict-free columns)
 
-// grid (GGROUPS * 3 tiles * 2 sides, streams), 256 threads.  Tile (bi, bj) of
+// grid (3 tiles * 2 sides, spans, streams), 256 threads.  Tile (bi, bj) of
 // 64 x 64 entries with bi <= bj (the lower-left tile is the transpose of the
 // upper-right one: fma(a, b, c) = fma(b, a, c), so the matrix is exactly
 // symmetric); thread (ti, tj) = (tid / 16, tid % 16) owns rows bi*64 + 4ti ..
-// +3 and columns bj*64 + 4tj .. +3.
-__global__ __launch_bounds__(256) void k_gram_partial(RotatePlan p) {
+// +3 and columns bj*64 + 4tj .. +3 and runs their 16 fma chains over the
+// span's tokens in order.
+__global__ __launch_bounds__(256) void k_gram(RotatePlan p) {
   __shared__ float4 xs[64 * D / 4];  // 64 tokens x 128 channels, fp32
   const int tid = threadIdx.x;
-  const int s = blockIdx.y;
-  const int side = blockIdx.x / (GGROUPS * 3);
-  const int rem = blockIdx.x - side * GGROUPS * 3;
-  const int g = rem / 3, tile = rem - g * 3;
+  const int s = blockIdx.z, span = blockIdx.y;
+  const int side = blockIdx.x / 3, tile = blockIdx.x - side * 3;
   const int bi = tile == 2 ? 1 : 0, bj = tile == 0 ? 0 : 1;
   const int ti = tid >> 4, tj = tid & 15;
   const int ri = bi * 64 + 4 * ti, rj = bj * 64 + 4 * tj;
   const uint16_t* X = (side ? p.V : p.K) + (uint64_t)s * p.kv_stride + (uint64_t)p.region_begin * D;
-  const int gT = p.region_len / GGROUPS;
-  const int t_lo = g * gT, t_hi = t_lo + gT;
+  const int t_lo = span * p.span_len, t_hi = t_lo + p.span_len;
   float acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void k_gram_partial(RotatePlan p) {
         for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fmaf(vi[a], vj[b], acc[a][b]);
     }
   }
-  float* out = p.gram + (((uint64_t)s * 2 + side) * GGROUPS + g) * D * D;
+  float* out = p.gram + (((uint64_t)s * p.n_span + span) * 2 + side) * D * D;
 #pragma unroll
   for (int a = 0; a < 4; ++a)
     *reinterpret_cast<float4*>(out + (ri + a) * D + rj) =
@@ -100,9 +100,9 @@ __device__ __forceinline__ void jacobi_pair(int r, int k, int& p, int& q) {
   q = a < b ? b : a;
 }
 
-// grid (2 sides, streams), JT threads (16 waves, so that LDS latency is hidden
-// inside the one workgroup a CU holds).  A and V live in LDS with rows of
-// APAD floats, so that a column walk hits 32 different banks.
+// grid (2 sides, spans, streams), JT threads (16 waves, so that LDS latency
+// is hidden inside the one workgroup a CU holds).  A and V live in LDS with
+// rows of APAD floats, so that a column walk hits 32 different banks.
 constexpr int JT = 1024;
 __global__ __launch_bounds__(JT) void k_jacobi(RotatePlan p) {
   extern __shared__ float lds[];
@@ -114,16 +114,14 @@ __global__ __launch_bounds__(JT) void k_jacobi(RotatePlan p) {
   int* Q = P + 64;                  // [64]
   int* rank = Q + 64;               // [128]
   const int tid = threadIdx.x;
-  const int side = blockIdx.x, s = blockIdx.y;
-  // A = pairwise sum of the eight partials; the lower-left tile mirrors
-  const float* gp = p.gram + ((uint64_t)s * 2 + side) * GGROUPS * D * D;
+  const int side = blockIdx.x, span = blockIdx.y, s = blockIdx.z;
+  const uint64_t mat = ((uint64_t)s * p.n_span + span) * 2 + side;
+  // A = the span's Gram matrix; the lower-left tile mirrors the upper-right
+  const float* gp = p.gram + mat * D * D;
   for (int e = tid; e < D * D; e += JT) {
     const int i = e / D, j = e % D;
     const int src = (i >= 64 && j < 64) ? j * D + i : e;
-    float v[GGROUPS];
-#pragma unroll
-    for (int g = 0; g < GGROUPS; ++g) v[g] = gp[(uint64_t)g * D * D + src];
-    A[i * APAD + j] = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    A[i * APAD + j] = gp[src];
     V[i * APAD + j] = i == j ? 1.0f : 0.0f;
   }
   __syncthreads();
@@ -192,7 +190,7 @@ __global__ __launch_bounds__(JT) void k_jacobi(RotatePlan p) {
     rank[tid] = rk;
   }
   __syncthreads();
-  float* R = p.rot + ((uint64_t)s * 2 + side) * D * D;
+  float* R = p.rot + mat * D * D;
   for (int e = tid; e < D * D; e += JT) {
     const int i = e / D, o = e % D;
     R[i * D + rank[o]] = V[i * APAD + o];
@@ -200,9 +198,10 @@ __global__ __launch_bounds__(JT) void k_jacobi(RotatePlan p) {
 }
 
 // grid (ceil(region_len / 64), 2 sides, streams), 128 threads: thread k
-// holds column k of R in registers and writes channel k of every rotated
-// vector of its 64 tokens; the tokens are staged in LDS as fp32 and read
-// by all lanes at once.
+// holds column k of the R of the block's span in registers (a span is a
+// multiple of 64 tokens, or the whole region) and writes channel k of every
+// rotated vector of its 64 tokens; the tokens are staged in LDS as fp32 and
+// read by all lanes at once.
 __global__ __launch_bounds__(128) void k_rotate_vec(RotatePlan p) {
   __shared__ float4 xs[64 * D / 4];
   const int k = threadIdx.x;
@@ -229,7 +228,8 @@ __global__ __launch_bounds__(128) void k_rotate_vec(RotatePlan p) {
       }
     }
   }
-  const float* R = p.rot + ((uint64_t)s * 2 + side) * D * D;
+  const int span = p.n_span > 1 ? t0 / p.span_len : 0;
+  const float* R = p.rot + (((uint64_t)s * p.n_span + span) * 2 + side) * D * D;
   float rc[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) rc[i] = R[i * D + k];
@@ -264,8 +264,8 @@ hipError_t launch_rotate(const RotatePlan& p, hipStream_t st) {
                           hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)jacobi_lds_bytes()) != hipSuccess)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_gram_partial, dim3(GGROUPS * 3 * 2, p.streams), dim3(256), 0, st, p);
-  hipLaunchKernelGGL(k_jacobi, dim3(2, p.streams), dim3(JT), jacobi_lds_bytes(), st, p);
+  hipLaunchKernelGGL(k_gram, dim3(3 * 2, p.n_span, p.streams), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(k_jacobi, dim3(2, p.n_span, p.streams), dim3(JT), jacobi_lds_bytes(), st, p);
   hipLaunchKernelGGL(k_rotate_vec, dim3((p.region_len + 63) / 64, 2, p.streams), dim3(128), 0, st,
                      p);
   return hipGetLastError();

@@ -27,7 +27,7 @@ class Compressed:
         self.params, self.layout = params, layout
         self.packed, self.desc, self.used = packed, desc, used
         self.scores, self.objective = scores, objective
-        self.rot = rot  # [streams, 2, 128, 128] fp32 when compressed with rotation
+        self.rot = rot  # [streams, n_span, 2, 128, 128] fp32 when compressed with rotation
 
     @property
     def n_seg(self):
@@ -49,10 +49,11 @@ def compress(K, V, Qw, *, seg_tokens, strategies, budget_bytes, region_begin=0, 
              want_objective=False, ws=None, packed=None, desc=None, n_ctx=None,
              kv_stream_stride=0, qw_head_stride=0, packed_stream_stride=0, packed_base_offset=0,
              desc_stream_stride=0, n_q_heads=None, budget_scope=0, compress_max_waves=0,
-             rotate=False, store_logits=False):
+             rotate=False, store_logits=False, rot_span=0):
     """K, V: [B, Hkv, N, 128] bf16 (or strided views described by the stride
     arguments); Qw: [B, Hq, W, 128] bf16 or None.  budget_scope 1 shares
-    n_seg * budget_bytes among a stream's segments."""
+    n_seg * budget_bytes among a stream's segments.  rotate: one SVD
+    rotation per span of rot_span tokens (0: per stream)."""
     B, Hkv = K.shape[0], K.shape[1]
     N = K.shape[2] if n_ctx is None else n_ctx
     Hq = Qw.shape[1] if Qw is not None else (n_q_heads or Hkv)
@@ -64,7 +65,7 @@ def compress(K, V, Qw, *, seg_tokens, strategies, budget_bytes, region_begin=0, 
                  packed_stream_stride=packed_stream_stride,
                  packed_base_offset=packed_base_offset, desc_stream_stride=desc_stream_stride,
                  budget_scope=budget_scope, compress_max_waves=compress_max_waves,
-                 rotate=rotate, store_logits=store_logits)
+                 rotate=rotate, store_logits=store_logits, rot_span=rot_span)
     _, L = kv_layout_query(p)
     dev = K.device
     streams = B * Hkv
@@ -81,7 +82,8 @@ def compress(K, V, Qw, *, seg_tokens, strategies, budget_bytes, region_begin=0, 
         ws = _u8(L.compress_ws_bytes, dev)
     rot = None
     if rotate:
-        rot = torch.empty((B * Hkv, 2, 128, 128), dtype=torch.float32, device=dev)
+        n_span = p.p.region_len // (rot_span or p.p.region_len)
+        rot = torch.empty((B * Hkv, n_span, 2, 128, 128), dtype=torch.float32, device=dev)
         kv_compress_rotated(p, _as_u16(K), _as_u16(V), Qw, forced, packed, desc, used, scores,
                             objective, rot, ws)
     else:
@@ -98,15 +100,19 @@ def decode_params(*, batch, n_q_heads, n_kv_heads, max_desc_per_stream, decode_s
 
 
 def decode(q, packed, desc, *, n_kv_heads, max_desc_per_stream, n_desc=None, decode_splits=0,
-           scale=0.0, want_lse=True, out=None, lse=None, ws=None, params=None, rot=None):
+           scale=0.0, want_lse=True, out=None, lse=None, ws=None, params=None, rot=None,
+           seg_tokens=0, rot_span=0):
     """q: [B, Hq, 128] bf16 -> (out [B, Hq, 128] bf16, lse [B, Hq] fp32 or None).
-    rot: the rotations of a cache compressed with rotation."""
+    rot: the rotations of a cache compressed with rotation (per span of
+    rot_span tokens of seg_tokens-token segments when rot_span > 0)."""
     B, Hq = q.shape[0], q.shape[1]
     p = params or decode_params(batch=B, n_q_heads=Hq, n_kv_heads=n_kv_heads,
                                 max_desc_per_stream=max_desc_per_stream,
                                 decode_splits=decode_splits, scale=scale)
     if rot is not None:
         p.p.rotate = 1
+        if rot_span:
+            p.p.seg_tokens, p.p.rot_span = seg_tokens, rot_span
     if ws is None:
         _, L = kv_layout_query(p)
         ws = _u8(L.decode_ws_bytes, q.device)

@@ -110,10 +110,14 @@ typedef struct {
                                     kv_compress_rotated / kv_attend_decode_rotated; sizes
                                     their workspaces); 0: none */
   uint32_t store_logits;         /* 1: the first scoring pass keeps every window-query
-                                    logit of the region in the compress workspace
-                                    (streams x G*n_win x region_len fp32) and the second
-                                    pass reads them back instead of recomputing them;
-                                    0: the second pass recomputes them.  Same results. */
+                                    logit of the domain in the compress workspace
+                                    (streams x G*n_win x n_ctx fp32) and the later
+                                    passes read them back instead of recomputing them;
+                                    0: they recompute them.  Same results. */
+  uint32_t rot_span;             /* rotate = 1: tokens per rotation span; every span of
+                                    the region has its own R_K, R_V.  0 => the whole
+                                    region (one R per stream).  Otherwise a multiple of
+                                    seg_tokens and of 64 that divides region_len. */
 } kvc_params;
 
 /* budget_scope values.
@@ -216,26 +220,31 @@ kvc_status kv_compress(const kvc_params* p, const uint16_t* K, const uint16_t* V
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Compression with an SVD rotation before the channel selection (MosaicKV
- * review page: Fig. 6 caption, Stage-1 -- the rotation matrix R of the K and
- * of the V matrix from their SVD, the vectors rotated before the top-r
- * elements of each are kept; Fig. 4 -- after the rotation the important
- * elements concentrate in a few channels).  As kv_compress (p->rotate = 1),
- * and per stream:
- *  1. R_K, R_V: eigenvectors of the Gram matrices X^T X of the region's K
- *     and V vectors, ordered by eigenvalue (largest first, ties to the lower
- *     index).  The Gram matrix is the pairwise sum of eight fp32 fma chains
- *     over consecutive token groups; the eigenvectors come from 10 sweeps of
- *     cyclic Jacobi in fp32 (round-robin pairing, each round's rotations
- *     computed from the matrix as it stands, then applied to its rows, its
- *     columns and the eigenvector columns), so R is reproducible bit for bit.
- *  2. Every region vector x becomes y = R^T x (fp32 fma chain over input
- *     channels, rounded to bf16); channel selection, the objective and the
- *     packed values use y.  Window scoring uses the original keys.
- *  rot   device [streams][2][128][128] fp32, written: R_K then R_V (row i,
- *        column k = component i of the k-th eigenvector).
- * One R per stream and side serves the whole region: a rotation per segment
- * would cost more bytes than a compressed segment is allowed.  Decode the
- * result with kv_attend_decode_rotated. */
+ * review page: Fig. 6 caption, Stage-1 -- the rotation matrix R of the
+ * current segment's K and of its V matrix from their SVD, the vectors rotated
+ * before the top-r elements of each are kept; Fig. 4 -- after the rotation
+ * the important elements concentrate in a few channels).  As kv_compress
+ * (p->rotate = 1), and per stream and span of p->rot_span tokens (the whole
+ * region when rot_span = 0):
+ *  1. R_K, R_V: eigenvectors of the Gram matrices X^T X of the span's K and
+ *     V vectors, ordered by eigenvalue (largest first, ties to the lower
+ *     index).  Every Gram entry is one fp32 fma chain over the span's tokens
+ *     in order; the eigenvectors come from 10 sweeps of cyclic Jacobi in
+ *     fp32 with the round-robin pair ordering of parallel Jacobi methods
+ *     (each round's 64 rotations act on disjoint index pairs, are computed
+ *     from the matrix as it stands and applied to its rows, its columns and
+ *     the eigenvector columns), so R is reproducible bit for bit.
+ *  2. Every region vector x becomes y = R^T x with the R of its span (fp32
+ *     fma chain over input channels, rounded to bf16); channel selection,
+ *     the objective and the packed values use y.  Window scoring uses the
+ *     original keys.
+ *  rot   device [streams][n_span][2][128][128] fp32, written: R_K then R_V
+ *        of each span (row i, column k = component i of the k-th
+ *        eigenvector); n_span = region_len / rot_span (1 when rot_span = 0).
+ * The rotations are part of what a cache stores: 128 KB per span and
+ * stream in fp32, beside the packed bytes (a span of one 128-token segment
+ * would need more for its two matrices than its compressed vectors may
+ * occupy).  Decode the result with kv_attend_decode_rotated. */
 kvc_status kv_compress_rotated(const kvc_params* p, const uint16_t* K, const uint16_t* V,
                                const uint16_t* Qwin, const uint8_t* forced_strategy, void* packed,
                                kvc_seg_desc* desc, uint64_t* used_bytes, float* scores,
@@ -263,15 +272,20 @@ kvc_status kv_attend_decode(const kvc_params* p, const uint16_t* q, const void* 
                             uint16_t* out, float* lse, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
-/* Decode over a cache whose every descriptor of a stream holds vectors
- * rotated by that stream's R (kv_compress_rotated; p->rotate = 1): each
- * query becomes q' = R_K^T q (fp32, passed to the score product as its bf16
- * rounding plus the bf16 rounding of the remainder, so about 16 bits of it
- * survive), attention runs as in kv_attend_decode, and the output is R_V
- * times the merged rotated output, in fp32, before its bf16 rounding.  rot
- * as written by kv_compress_rotated; lse as for kv_attend_decode (the
- * rotation does not change the logits).  Workspace from kv_layout_query
- * with p->rotate = 1. */
+/* Decode over a cache compressed by kv_compress_rotated (p->rotate = 1):
+ * descriptor i of a stream holds vectors rotated by the R of span
+ * i / (rot_span / seg_tokens) (one span when rot_span = 0).  Each query
+ * becomes q' = R_K^T q per span (fp32, passed to the score product as its
+ * bf16 rounding plus the bf16 rounding of the remainder, so about 16 bits of
+ * it survive), attention runs as in kv_attend_decode with the logits of a
+ * token taken against its span's q', and the output is the sum over spans of
+ * R_V times the span's share of the merged rotated output, in fp32, before
+ * its bf16 rounding.  Every split covers descriptors of one span, so the
+ * split count is a multiple of the span count (decode_splits, when given,
+ * must be).  rot as written by kv_compress_rotated; lse as for
+ * kv_attend_decode (the rotation does not change the logits).  Uses
+ * seg_tokens and rot_span besides the fields kv_attend_decode uses;
+ * workspace from kv_layout_query with p->rotate = 1. */
 kvc_status kv_attend_decode_rotated(const kvc_params* p, const uint16_t* q, const void* packed,
                                     const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
                                     const float* rot, uint16_t* out, float* lse, void* ws,

@@ -39,7 +39,6 @@
 #include <omp.h>
 
 #define ORC_D 128           /* head dimension handled by the oracle */
-#define ORC_BLK 64          /* tokens per normalisation partial block */
 
 /* ------------------------------------------------------------------ */
 /* fp32 helpers                                                         */
@@ -131,42 +130,27 @@ void orc_exp2_coeffs(float* c8, float* log2e) {
 /*  the G q-heads of its group and the W window queries.               */
 /* ------------------------------------------------------------------ */
 /* Qw: [nq][128] bf16, query index qi = g*W + w.  K: [n_ctx][128].
- * Outputs m[nq], invZ[nq] (global max and 1/Z of each query). */
+ * Outputs m[nq], invZ[nq]: for each query, m = the largest of its n_ctx
+ * logits and Z = the pairwise sum (zero-padded to a power of two) over all
+ * n_ctx tokens of exp(l - m); invZ = 1/Z. */
 void orc_normalisers(int n_ctx, int nq, const uint16_t* K, const uint16_t* Qw,
                      float scale, float* m_out, float* invZ_out, int n_threads) {
   orc_init();
-  const int nblk = n_ctx / ORC_BLK;
 #pragma omp parallel for schedule(dynamic) num_threads(n_threads)
   for (int qi = 0; qi < nq; ++qi) {
     float q[ORC_D];
     for (int ch = 0; ch < ORC_D; ++ch) q[ch] = bf2f(Qw[(size_t)qi * ORC_D + ch]);
-    float* mb = (float*)malloc(sizeof(float) * (size_t)nblk);
-    float* zb = (float*)malloc(sizeof(float) * (size_t)nblk);
-    float l[ORC_BLK], e[ORC_BLK];
-    for (int b = 0; b < nblk; ++b) {
-      /* partial of one 64-token block: its max and the pairwise sum of
-       * exp(l - max) */
-      float mx = -INFINITY;
-      for (int i = 0; i < ORC_BLK; ++i) {
-        const uint16_t* k = K + ((size_t)b * ORC_BLK + i) * ORC_D;
-        l[i] = dot_chain(q, k) * scale;
-        if (l[i] > mx) mx = l[i];
-      }
-      for (int i = 0; i < ORC_BLK; ++i) e[i] = orc_exp2((l[i] - mx) * LOG2E_F);
-      mb[b] = mx;
-      zb[b] = tree_pow2(e, ORC_BLK);
-    }
+    float* l = (float*)malloc(sizeof(float) * (size_t)n_ctx);
     float m = -INFINITY;
-    for (int b = 0; b < nblk; ++b)
-      if (mb[b] > m) m = mb[b];
-    float* t = (float*)malloc(sizeof(float) * (size_t)nblk);
-    for (int b = 0; b < nblk; ++b) t[b] = zb[b] * orc_exp2((mb[b] - m) * LOG2E_F);
-    float Z = tree_any(t, nblk);
+    for (int t = 0; t < n_ctx; ++t) {
+      l[t] = dot_chain(q, K + (size_t)t * ORC_D) * scale;
+      if (l[t] > m) m = l[t];
+    }
+    for (int t = 0; t < n_ctx; ++t) l[t] = orc_exp2((l[t] - m) * LOG2E_F);
+    const float Z = tree_any(l, n_ctx);
     m_out[qi] = m;
     invZ_out[qi] = 1.0f / Z;
-    free(t);
-    free(mb);
-    free(zb);
+    free(l);
   }
 }
 
@@ -379,6 +363,7 @@ typedef struct {
                         segments together <= nseg * budget_bytes */
   int rotate;        /* 1: rotate the region's K and V vectors (SVD) before
                         channel selection and packing */
+  int rot_span;      /* tokens per rotation span (0: the whole region) */
 } orc_params;
 
 /* ------------------------------------------------------------------ */
@@ -387,15 +372,23 @@ typedef struct {
 /* matrix, respectively, is computed and the vectors are rotated before  */
 /* the top-r elements of each are kept; Fig. 4: after the rotation the   */
 /* important elements of the cache sit in a few channels).  Reading:     */
-/*  - one R per stream and side, from the vectors of the region one call */
-/*    compresses (a rotation per segment would cost 2 x 32 KB, more than */
-/*    the byte budget of a 128-token segment);                           */
-/*  - R = the right singular vectors of the [T x 128] matrix X, i.e. the */
-/*    eigenvectors of the Gram matrix X^T X, ordered by eigenvalue       */
-/*    (largest first, ties to the lower index), found by cyclic Jacobi   */
-/*    in fp32 with every operation fixed below;                          */
+/*  - the region is cut into spans of rot_span tokens (one span = the    */
+/*    whole region when rot_span is 0); each span has its own R for K    */
+/*    and for V, from that span's vectors;                               */
+/*  - R = the right singular vectors of the span's [T x 128] matrix X,   */
+/*    i.e. the eigenvectors of the Gram matrix X^T X, ordered by          */
+/*    eigenvalue (largest first, ties to the lower index);               */
+/*  - a Gram entry is the dot product of two columns of X, computed like */
+/*    every other dot product here: one fmaf chain in ascending token    */
+/*    order;                                                             */
+/*  - the eigenvectors come from cyclic Jacobi in fp32 with the          */
+/*    round-robin (tournament) pair ordering of parallel Jacobi methods: */
+/*    the 64 rotations of a round touch disjoint index pairs, so they are */
+/*    all computed from the matrix as it stands and then applied as one  */
+/*    similarity transform (rows, then columns), every operation fixed;  */
 /*  - a vector x is stored as y = R^T x rounded to bf16; decode attends  */
-/*    with R_K^T q and returns R_V times the rotated output.             */
+/*    with R_K^T q in the span's basis and returns the sum over spans of */
+/*    R_V times the span's share of the rotated output.                  */
 /* ------------------------------------------------------------------ */
 #define ORC_JACOBI_SWEEPS 10
 
@@ -406,22 +399,16 @@ static uint16_t f2bf_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-/* C[i][j] = pairwise sum of eight partial sums, partial g = fma chain over
- * tokens g*T/8 .. (g+1)*T/8 - 1 in order of x_t[i] * x_t[j].  T % 8 == 0. */
+/* C[i][j] = sum over the T tokens of x_t[i] * x_t[j] as one fma chain in
+ * ascending token order (a dot product of columns i and j of X). */
 void orc_gram(const uint16_t* X, int T, float* C, int n_threads) {
-  const int gT = T / 8;
 #pragma omp parallel for schedule(dynamic) num_threads(n_threads)
   for (int i = 0; i < ORC_D; ++i) {
     for (int j = 0; j < ORC_D; ++j) {
-      float part[8];
-      for (int g = 0; g < 8; ++g) {
-        float acc = 0.0f;
-        for (int t = g * gT; t < (g + 1) * gT; ++t)
-          acc = fmaf(bf2f(X[(size_t)t * ORC_D + i]), bf2f(X[(size_t)t * ORC_D + j]), acc);
-        part[g] = acc;
-      }
-      C[i * ORC_D + j] = ((part[0] + part[1]) + (part[2] + part[3])) +
-                         ((part[4] + part[5]) + (part[6] + part[7]));
+      float acc = 0.0f;
+      for (int t = 0; t < T; ++t)
+        acc = fmaf(bf2f(X[(size_t)t * ORC_D + i]), bf2f(X[(size_t)t * ORC_D + j]), acc);
+      C[i * ORC_D + j] = acc;
     }
   }
 }
@@ -606,19 +593,27 @@ int orc_compress_stream(const orc_params* p, const uint16_t* K, const uint16_t* 
   long rb = 0;
   uint16_t *KR = NULL, *VR = NULL;
   if (p->rotate) {
-    if (p->region_len % 8) return -1;
+    const int span = p->rot_span ? p->rot_span : p->region_len;
+    if (span <= 0 || p->region_len % span) return -1;
     float* C = (float*)malloc(sizeof(float) * ORC_D * ORC_D);
-    float R[2][ORC_D * ORC_D], ev[ORC_D];
+    float* R = (float*)malloc(sizeof(float) * ORC_D * ORC_D);
+    float ev[ORC_D];
     KR = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)p->region_len * ORC_D);
     VR = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)p->region_len * ORC_D);
-    for (int side = 0; side < 2; ++side) {
-      const uint16_t* X = (side ? V : K) + (size_t)p->region_begin * ORC_D;
-      orc_gram(X, p->region_len, C, n_threads);
-      orc_jacobi(C, R[side], ev);
-      orc_rotate(X, p->region_len, R[side], side ? VR : KR);
-      if (rot_out) memcpy(rot_out + (size_t)side * ORC_D * ORC_D, R[side], sizeof(R[side]));
+    for (int sp = 0; sp < p->region_len / span; ++sp) {
+      for (int side = 0; side < 2; ++side) {
+        const size_t t0 = (size_t)sp * span;
+        const uint16_t* X = (side ? V : K) + ((size_t)p->region_begin + t0) * ORC_D;
+        orc_gram(X, span, C, n_threads);
+        orc_jacobi(C, R, ev);
+        orc_rotate(X, span, R, (side ? VR : KR) + t0 * ORC_D);
+        if (rot_out)
+          memcpy(rot_out + ((size_t)sp * 2 + side) * ORC_D * ORC_D, R,
+                 sizeof(float) * ORC_D * ORC_D);
+      }
     }
     free(C);
+    free(R);
     KS = KR;
     VS = VR;
     rb = p->region_begin;
@@ -831,28 +826,101 @@ void orc_decode_stream(int G, const uint16_t* q, const uint8_t* packed, const or
 }
 
 /* Decode over a cache stored in the rotated bases (compressed with
- * rotation): exact attention of q' = R_K^T q over the stored vectors, then
- * out = R_V out', all in fp64 from the fp32 matrices. */
+ * rotation): rot holds [n_span][2][128][128] fp32 (R_K, R_V of each span),
+ * descriptor i belongs to span i / desc_per_span.  Exact attention over the
+ * stored vectors with the logits of token t taken against q' = R_K^T q of
+ * t's span; out = sum over spans of R_V times the softmax-weighted sum of
+ * that span's stored V vectors; all in fp64 from the fp32 matrices. */
 void orc_decode_stream_rot(int G, const uint16_t* q, const uint8_t* packed, const orc_desc* desc,
-                           int n_desc, float scale, const float* RK, const float* RV,
+                           int n_desc, float scale, const float* rot, int desc_per_span,
                            double* out, double* lse) {
-  double* qd = (double*)calloc((size_t)G * ORC_D + 1, sizeof(double));
+  const int n_span = (n_desc + desc_per_span - 1) / desc_per_span;
+  double* qd = (double*)calloc((size_t)n_span * G * ORC_D + 1, sizeof(double));
+  for (int sp = 0; sp < n_span; ++sp) {
+    const float* RK = rot + (size_t)sp * 2 * ORC_D * ORC_D;
+    for (int g = 0; g < G; ++g)
+      for (int k = 0; k < ORC_D; ++k) {
+        double acc = 0.0;
+        for (int i = 0; i < ORC_D; ++i)
+          acc += (double)bf2f(q[g * ORC_D + i]) * (double)RK[i * ORC_D + k];
+        qd[((size_t)sp * G + g) * ORC_D + k] = acc;
+      }
+  }
+  /* logits of every kept token against its span's rotated query */
+  long ntok = 0;
+  for (int i = 0; i < n_desc; ++i) ntok += desc[i].n_tok;
+  double* l = (double*)malloc(sizeof(double) * (size_t)(ntok > 0 ? ntok : 1) * (size_t)G);
+  long j = 0;
+  for (int i = 0; i < n_desc; ++i) {
+    const double* qs = qd + (size_t)(i / desc_per_span) * G * ORC_D;
+    const int T = desc[i].n_tok, c = desc[i].n_ch, TL = layout_tokens(&desc[i]);
+    const uint8_t* base = packed + desc[i].offset;
+    const uint8_t* kval = base + (c < ORC_D ? 16 * TL : 0);
+    for (int t = 0; t < T; ++t, ++j) {
+      const uint8_t* mk = c < ORC_D ? base + 16 * t : NULL;
+      const uint8_t* vals = kval + (size_t)2 * c * t;
+      for (int g = 0; g < G; ++g) {
+        double acc = 0.0;
+        int r = 0;
+        for (int ch = 0; ch < ORC_D; ++ch) {
+          if (mk && !((mk[ch >> 3] >> (ch & 7)) & 1)) continue;
+          uint16_t u;
+          memcpy(&u, vals + 2 * r, 2);
+          ++r;
+          acc += qs[g * ORC_D + ch] * (double)bf2f(u);
+        }
+        l[(size_t)j * G + g] = acc * (double)scale;
+      }
+    }
+  }
   double* o1 = (double*)calloc((size_t)G * ORC_D + 1, sizeof(double));
-  for (int g = 0; g < G; ++g)
-    for (int k = 0; k < ORC_D; ++k) {
-      double acc = 0.0;
-      for (int i = 0; i < ORC_D; ++i) acc += (double)bf2f(q[g * ORC_D + i]) * (double)RK[i * ORC_D + k];
-      qd[g * ORC_D + k] = acc;
+  for (int g = 0; g < G; ++g) {
+    double mx = -INFINITY;
+    for (long t = 0; t < ntok; ++t) mx = l[t * G + g] > mx ? l[t * G + g] : mx;
+    for (int i = 0; i < ORC_D; ++i) out[g * ORC_D + i] = 0.0;
+    if (ntok == 0) {
+      lse[g] = -INFINITY;
+      continue;
     }
-  decode_core(G, qd, packed, desc, n_desc, scale, o1, lse);
-  for (int g = 0; g < G; ++g)
-    for (int i = 0; i < ORC_D; ++i) {
-      double acc = 0.0;
-      for (int k = 0; k < ORC_D; ++k) acc += (double)RV[i * ORC_D + k] * o1[g * ORC_D + k];
-      out[g * ORC_D + i] = acc;
+    double den = 0.0;
+    for (long t = 0; t < ntok; ++t) den += exp(l[t * G + g] - mx);
+    lse[g] = mx + log(den);
+    /* per span: the weighted sum of its stored V vectors, then R_V times it */
+    j = 0;
+    for (int sp = 0; sp < n_span; ++sp) {
+      for (int k = 0; k < ORC_D; ++k) o1[k] = 0.0;
+      const int i1 = (sp + 1) * desc_per_span < n_desc ? (sp + 1) * desc_per_span : n_desc;
+      for (int i = sp * desc_per_span; i < i1; ++i) {
+        const int T = desc[i].n_tok, c = desc[i].n_ch, TL = layout_tokens(&desc[i]);
+        const uint8_t* base = packed + desc[i].offset;
+        const size_t mb = c < ORC_D ? (size_t)16 * TL : 0;
+        const uint8_t* vmask = base + mb + (size_t)2 * TL * c;
+        const uint8_t* vval = vmask + mb;
+        for (int t = 0; t < T; ++t, ++j) {
+          const double pw = exp(l[(size_t)j * G + g] - mx) / den;
+          const uint8_t* mk = c < ORC_D ? vmask + 16 * t : NULL;
+          const uint8_t* vals = vval + (size_t)2 * c * t;
+          int r = 0;
+          for (int ch = 0; ch < ORC_D; ++ch) {
+            if (mk && !((mk[ch >> 3] >> (ch & 7)) & 1)) continue;
+            uint16_t u;
+            memcpy(&u, vals + 2 * r, 2);
+            ++r;
+            o1[ch] += pw * (double)bf2f(u);
+          }
+        }
+      }
+      const float* RV = rot + ((size_t)sp * 2 + 1) * ORC_D * ORC_D;
+      for (int i = 0; i < ORC_D; ++i) {
+        double acc = 0.0;
+        for (int k = 0; k < ORC_D; ++k) acc += (double)RV[i * ORC_D + k] * o1[k];
+        out[g * ORC_D + i] += acc;
+      }
     }
-  free(qd);
+  }
   free(o1);
+  free(l);
+  free(qd);
 }
 
 static void decode_core(int G, const double* qd, const uint8_t* packed, const orc_desc* desc,

@@ -27,7 +27,7 @@ def say(*a):
 
 def oracle_compress_all(w, *, S, strategies, budget, region_begin=0, region_len=None, t2c_alpha=0,
                         t2c_gamma=0, forced=None, streams=None, capacity=None, K=None, V=None,
-                        Qw=None, budget_scope=0, rotate=False):
+                        Qw=None, budget_scope=0, rotate=False, rot_span=0):
     """Oracle compression of every (or the listed) stream of workload `w`.
 
     Returns dict stream -> oracle result, with descriptor offsets laid out as
@@ -47,7 +47,7 @@ def oracle_compress_all(w, *, S, strategies, budget, region_begin=0, region_len=
                                    scale=SCALE, region_begin=region_begin, region_len=region_len,
                                    t2c_alpha=t2c_alpha, t2c_gamma=t2c_gamma, forced=f,
                                    base_offset=(s * capacity if capacity is not None else 0),
-                                   budget_scope=budget_scope, rotate=rotate)
+                                   budget_scope=budget_scope, rotate=rotate, rot_span=rot_span)
     return res
 
 

@@ -108,7 +108,7 @@ def test_layout_errors():
 
 
 def test_stored_logits_layout():
-    """store_logits adds streams x G*W x region_len fp32 to the compress
+    """store_logits adds streams x G*W x n_ctx fp32 to the compress
     workspace and nothing else; other values are rejected."""
     for cfg in ("tiny", "llama8b", "batched128k", "million"):
         c = gen.CONFIGS[cfg]
@@ -342,8 +342,11 @@ def test_rotation_entry_points_validate(monkeypatch):
     _, L1 = kvc.kv_layout_query(p1)
     c = gen.CONFIGS["batched128k"]
     streams = c["B"] * c["Hkv"]
-    extra = streams * 2 * 8 * 128 * 128 * 4 + 2 * streams * c["N"] * 256
+    extra = streams * 2 * 128 * 128 * 4 + 2 * streams * c["N"] * 256
     assert L1.compress_ws_bytes >= L0.compress_ws_bytes + extra
+    # one Gram matrix per span and side
+    _, L2 = kvc.kv_layout_query(_params("batched128k", rotate=1, rot_span=4096))
+    assert L2.compress_ws_bytes == L1.compress_ws_bytes + streams * 31 * 2 * 128 * 128 * 4
     d0 = kvc.KvParams(batch=2, n_q_heads=8, n_kv_heads=2, max_desc_per_stream=8)
     d1 = kvc.KvParams(batch=2, n_q_heads=8, n_kv_heads=2, max_desc_per_stream=8, rotate=1)
     _, D0 = kvc.kv_layout_query(d0)
@@ -385,3 +388,41 @@ def test_read_stream_validates(monkeypatch):
         with pytest.raises(kvc.KvcError) as e:
             kvc.kv_read_stream(src, nbytes, sink)
         assert e.value.status == status
+
+
+def test_rotation_span_validation():
+    """rot_span needs rotate = 1, must be a multiple of seg_tokens and of 64
+    and divide region_len; a rotated decode over spans splits every span
+    alike, so a caller's split count must be a multiple of the span count."""
+    for bad in (100, 192 * 3, 64):  # not a multiple of 128, not dividing 131072, not of S
+        st, _ = kvc.kv_layout_query(_params("batched128k", rotate=1, rot_span=bad), check=False)
+        assert st == -1, bad
+    st, _ = kvc.kv_layout_query(_params("batched128k", rot_span=4096), check=False)
+    assert st == -1  # no rotation
+    st, L = kvc.kv_layout_query(_params("batched128k", rotate=1, rot_span=4096))
+    assert st == 0
+    d = dict(batch=2, n_q_heads=8, n_kv_heads=2, max_desc_per_stream=64, rotate=1,
+             seg_tokens=128, rot_span=1024)  # 8 descriptors per span, 8 spans
+    st, D = kvc.kv_layout_query(kvc.KvParams(**d))
+    assert st == 0 and D.decode_splits % 8 == 0 and D.decode_splits >= 8
+    assert D.decode_ws_bytes >= 2 * 2 * 8 * 8 * 128 * 2
+    st, _ = kvc.kv_layout_query(kvc.KvParams(**d, decode_splits=12), check=False)
+    assert st == -1
+    st, D = kvc.kv_layout_query(kvc.KvParams(**d, decode_splits=16))
+    assert st == 0 and D.decode_splits == 16
+
+
+def test_decode_split_count_is_bounded():
+    """A caller's split count above 65536, or one that makes streams x splits
+    exceed an int, is rejected by the layout query and by decode."""
+    st, _ = kvc.kv_layout_query(kvc.KvParams(batch=1, n_q_heads=4, n_kv_heads=1,
+                                             max_desc_per_stream=8, decode_splits=65537),
+                                check=False)
+    assert st == -1
+    st, L = kvc.kv_layout_query(kvc.KvParams(batch=1, n_q_heads=4, n_kv_heads=1,
+                                             max_desc_per_stream=8, decode_splits=65536))
+    assert st == 0 and L.decode_splits == 65536
+    st, _ = kvc.kv_layout_query(kvc.KvParams(batch=4095, n_q_heads=16, n_kv_heads=16,
+                                             max_desc_per_stream=8, decode_splits=40000),
+                                check=False)
+    assert st == -1  # 65520 streams x 40000 splits

@@ -1,8 +1,9 @@
 """GPU parity of the SVD rotation before channel selection
 (kv_compress_rotated, kv_attend_decode_rotated) against the CPU oracle:
-rotation matrices, scores, objectives, descriptors and the whole packed byte
-range of every stream bit-exact; decode over the rotated cache within the
-attention tolerance of the oracle's fp64 rotated decode."""
+rotation matrices (one per stream, or one per span of rot_span tokens),
+scores, objectives, descriptors and the whole packed byte range of every
+stream bit-exact; decode over the rotated cache within the attention
+tolerance of the oracle's fp64 rotated decode."""
 import numpy as np
 import pytest
 import torch
@@ -15,17 +16,17 @@ pytestmark = pytest.mark.gpu
 
 
 def _check(w, *, S, strategies, budget, region_begin=0, region_len=None, label="", streams=None,
-           decode=True):
-    say(f"[rotate] {label} B={w['B']} Hq={w['Hq']} Hkv={w['Hkv']} N={w['N']} S={S}")
+           decode=True, rot_span=0, decode_splits=0):
+    say(f"[rotate] {label} B={w['B']} Hq={w['Hq']} Hkv={w['Hkv']} N={w['N']} S={S} span={rot_span}")
     K, V, Qw = w["K"].cuda(), w["V"].cuda(), w["Qw"].cuda()
     r = runtime.compress(K, V, Qw, seg_tokens=S, strategies=strategies, budget_bytes=budget,
                          region_begin=region_begin, region_len=region_len, scale=float(SCALE),
-                         want_scores=True, want_objective=True, rotate=True)
+                         want_scores=True, want_objective=True, rotate=True, rot_span=rot_span)
     torch.cuda.synchronize()
     cap = r.layout.stream_capacity
     ref = oracle_compress_all(w, S=S, strategies=strategies, budget=budget,
                               region_begin=region_begin, region_len=region_len, streams=streams,
-                              capacity=cap, rotate=True)
+                              capacity=cap, rotate=True, rot_span=rot_span)
     rot = r.rot.cpu().numpy()
     packed = r.packed.cpu().numpy()
     desc = r.desc_host()
@@ -45,7 +46,8 @@ def _check(w, *, S, strategies, budget, region_begin=0, region_len=None, label="
         q = w["q"].cuda()
         maxd = desc.shape[1]
         out, lse = runtime.decode(q, r.packed, r.desc, n_kv_heads=w["Hkv"], max_desc_per_stream=maxd,
-                                  scale=float(SCALE), rot=r.rot)
+                                  scale=float(SCALE), rot=r.rot, seg_tokens=S, rot_span=rot_span,
+                                  decode_splits=decode_splits)
         torch.cuda.synchronize()
         qn = gen.u16(w["q"])
         G = w["G"]
@@ -54,7 +56,7 @@ def _check(w, *, S, strategies, budget, region_begin=0, region_len=None, label="
             buf = np.zeros(s * cap + o["used"] + 16, np.uint8)
             buf[s * cap:s * cap + o["used"]] = o["packed"]
             ro, rl = O.decode_stream_rot(qn[b, h * G:(h + 1) * G], buf, o["desc"], SCALE,
-                                         o["rot"][0], o["rot"][1])
+                                         o["rot"], (rot_span // S) if rot_span else None)
             check_attention(out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G], ro, rl,
                             f"{label} rotated decode s={s}")
     return r, ref
@@ -93,5 +95,28 @@ def test_rotate_keep_all_matches_dense_attention():
     rot = r.rot.cpu().numpy().astype(np.float64)
     for s in range(rot.shape[0]):
         for side in range(2):
-            R = rot[s, side]
+            R = rot[s, 0, side]
             assert np.abs(R.T @ R - np.eye(128)).max() < 1e-4
+
+
+def test_rotate_per_span():
+    """One rotation per span of 512 tokens (four 128-token segments): every
+    span's R_K and R_V bit-exact, vectors rotated by their span's R; decode
+    takes each token's logits against its span's rotated query and rotates
+    each span's share of the output back with the span's R_V."""
+    w = gen.make_workload("batched128k", B=2, N=2048)
+    _check(w, S=128, strategies=gen.table9(128), budget=gen.budget_bytes(25, 128),
+           label="spans of 512", rot_span=512)
+
+
+def test_rotate_per_span_region_and_splits():
+    """Spans over a region that starts mid-domain (64-token spans of four
+    16-token segments, G = 8), decoded with the library's split count and
+    with three splits per span (a split never crosses a span)."""
+    c = dict(gen.CONFIGS["tiny"])
+    c.update(Hq=16, Hkv=2, N=1024, S=16, W=4)
+    w = gen.make_workload(c)
+    for splits in (0, 3 * 4):
+        _check(w, S=16, strategies=gen.table9(16), budget=gen.budget_bytes(33, 16),
+               region_begin=512, region_len=256, label=f"spans of 64, splits {splits}",
+               rot_span=64, decode_splits=splits)

@@ -809,6 +809,25 @@ def test_gram_exact_on_integer_data(O):
     assert np.array_equal(C.astype(np.float64), ref)
 
 
+def test_gram_is_a_chain_in_token_order(O):
+    """Each Gram entry is one fma chain over the tokens in ascending order: a
+    column (2^12, 1, 1, ..., 1) squares to 2^24 followed by 63 ones, and
+    2^24 + 1 rounds back to 2^24 (ties to even), so the diagonal entry is
+    exactly 2^24.  Summing the ones first (reversed order, or a pairwise
+    tree) would give 2^24 + 64 (16777279 rounded).  The off-diagonal entry
+    with a column of ones, 2^12 + 63, is exact in any order."""
+    X = np.zeros((64, 128), np.float32)
+    X[:, 5] = 1.0
+    X[0, 5] = 4096.0
+    X[:, 9] = 1.0
+    C = O.gram(_bf16(X))
+    assert C[5, 5] == np.float32(2.0 ** 24)
+    assert C[5, 9] == C[9, 5] == np.float32(4096 + 63)
+    assert C[9, 9] == np.float32(64.0)
+    Cr = O.gram(_bf16(X[::-1]))
+    assert Cr[5, 5] == np.float32(16777280.0)
+
+
 def test_jacobi_against_numpy_eigh(O):
     """Eigenvalues within 1e-4 of the largest of numpy's fp64 eigh, sorted
     largest first; R orthogonal; R^T C R diagonal to 1e-5 of the largest."""
@@ -898,7 +917,7 @@ def test_rotated_decode_pins(O):
                           budget_bytes=4 * S * 128, scale=np.float32(0.125))
     I = np.eye(128, dtype=np.float32)
     a = O.decode_stream(q, r["packed"], r["desc"], np.float32(0.125))
-    b = O.decode_stream_rot(q, r["packed"], r["desc"], np.float32(0.125), I, I)
+    b = O.decode_stream_rot(q, r["packed"], r["desc"], np.float32(0.125), np.stack([I, I]))
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     pk, pv = rng.permutation(128), rng.permutation(128)
     PK = np.zeros((128, 128), np.float32)
@@ -907,7 +926,7 @@ def test_rotated_decode_pins(O):
     PV[pv, np.arange(128)] = 1.0
     rp = O.compress_stream(K[:, pk], V[:, pv], np.zeros((4, 1, 128), np.uint16), S=S,
                            strategies=[(S, 128)], budget_bytes=4 * S * 128, scale=np.float32(0.125))
-    o, l = O.decode_stream_rot(q, rp["packed"], rp["desc"], np.float32(0.125), PK, PV)
+    o, l = O.decode_stream_rot(q, rp["packed"], rp["desc"], np.float32(0.125), np.stack([PK, PV]))
     Kf, Vf, qf = _f32(K).astype(np.float64), _f32(V).astype(np.float64), _f32(q).astype(np.float64)
     lg = qf @ Kf.T * 0.125
     m = lg.max(axis=1, keepdims=True)
@@ -931,16 +950,83 @@ def test_compress_with_rotation_stores_rotated_vectors(O):
                           budget_bytes=4 * S * 128, scale=np.float32(0.125), rotate=True)
     RK, _ = O.jacobi(O.gram(K))
     RV, _ = O.jacobi(O.gram(V))
-    assert np.array_equal(r["rot"][0], RK) and np.array_equal(r["rot"][1], RV)
+    assert r["rot"].shape == (1, 2, 128, 128)
+    assert np.array_equal(r["rot"][0, 0], RK) and np.array_equal(r["rot"][0, 1], RV)
     seg = 2 * S * 256
     YK, YV = O.rotate(K, RK), O.rotate(V, RV)
     for sg in range(N // S):
         blk = r["packed"][sg * seg:(sg + 1) * seg]
         assert np.array_equal(blk[:S * 256].view(np.uint16).reshape(S, 128), YK[sg * S:(sg + 1) * S])
         assert np.array_equal(blk[S * 256:].view(np.uint16).reshape(S, 128), YV[sg * S:(sg + 1) * S])
-    o, l = O.decode_stream_rot(q, r["packed"], r["desc"], np.float32(0.125), RK, RV)
+    o, l = O.decode_stream_rot(q, r["packed"], r["desc"], np.float32(0.125), r["rot"])
     Kf, Vf, qf = _f32(K).astype(np.float64), _f32(V).astype(np.float64), _f32(q).astype(np.float64)
     lg = qf @ Kf.T * 0.125
     p = np.exp(lg - lg.max(axis=1, keepdims=True))
     ref = (p / p.sum(axis=1, keepdims=True)) @ Vf
     assert np.abs(o - ref).max() <= 2e-2 * np.linalg.norm(ref, axis=1).max()
+
+
+def test_rotation_per_span(O):
+    """With rot_span, every span of the region has its own R_K and R_V: R of
+    span j is the Jacobi rotation of span j's own Gram matrix, the span's
+    vectors are stored rotated by it, and the rotations of different spans
+    differ when their vectors do."""
+    rng = np.random.default_rng(18)
+    S, N, span = 64, 256, 128
+    K = _bf16(rng.standard_normal((N, 128)) * np.repeat(rng.uniform(0.5, 4.0, (N // span, 128)), span, 0))
+    V = _bf16(rng.standard_normal((N, 128)))
+    r = O.compress_stream(K, V, np.zeros((2, 1, 128), np.uint16), S=S, strategies=[(S, 128)],
+                          budget_bytes=4 * S * 128, scale=np.float32(0.125), rotate=True,
+                          rot_span=span)
+    assert r["rot"].shape == (N // span, 2, 128, 128)
+    seg = 2 * S * 256
+    for j in range(N // span):
+        Ks, Vs = K[j * span:(j + 1) * span], V[j * span:(j + 1) * span]
+        RK, _ = O.jacobi(O.gram(Ks))
+        RV, _ = O.jacobi(O.gram(Vs))
+        assert np.array_equal(r["rot"][j, 0], RK) and np.array_equal(r["rot"][j, 1], RV)
+        YK, YV = O.rotate(Ks, RK), O.rotate(Vs, RV)
+        for sg in range(span // S):
+            g = j * (span // S) + sg
+            blk = r["packed"][g * seg:(g + 1) * seg]
+            assert np.array_equal(blk[:S * 256].view(np.uint16).reshape(S, 128), YK[sg * S:(sg + 1) * S])
+            assert np.array_equal(blk[S * 256:].view(np.uint16).reshape(S, 128), YV[sg * S:(sg + 1) * S])
+    assert not np.array_equal(r["rot"][0, 0], r["rot"][1, 0])
+
+
+def test_rotated_decode_per_span_permutations(O):
+    """Decode over spans with their own rotations: a keep-all cache whose
+    span j holds K and V with its own channel permutation, decoded with
+    those permutation matrices, equals dense attention over the original
+    vectors (a span taking another span's matrices would not); identity
+    matrices in every span give the plain decode exactly."""
+    rng = np.random.default_rng(19)
+    S, N, dps = 32, 128, 2  # four segments, two spans of two segments
+    K = _bf16(rng.standard_normal((N, 128)))
+    V = _bf16(rng.standard_normal((N, 128)))
+    q = _bf16(rng.standard_normal((3, 128)))
+    span = S * dps
+    rot = np.zeros((N // span, 2, 128, 128), np.float32)
+    Kp, Vp = K.copy(), V.copy()
+    for j in range(N // span):
+        for side, (X, Xp) in enumerate(((K, Kp), (V, Vp))):
+            perm = rng.permutation(128)
+            rot[j, side][perm, np.arange(128)] = 1.0
+            Xp[j * span:(j + 1) * span] = X[j * span:(j + 1) * span][:, perm]
+    r = O.compress_stream(Kp, Vp, np.zeros((3, 1, 128), np.uint16), S=S, strategies=[(S, 128)],
+                          budget_bytes=4 * S * 128, scale=np.float32(0.125))
+    o, l = O.decode_stream_rot(q, r["packed"], r["desc"], np.float32(0.125), rot, dps)
+    Kf, Vf, qf = _f32(K).astype(np.float64), _f32(V).astype(np.float64), _f32(q).astype(np.float64)
+    lg = qf @ Kf.T * 0.125
+    m = lg.max(axis=1, keepdims=True)
+    p = np.exp(lg - m)
+    ref = (p / p.sum(axis=1, keepdims=True)) @ Vf
+    assert np.allclose(o, ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(l, m[:, 0] + np.log(p.sum(axis=1)), rtol=1e-12)
+    swapped = O.decode_stream_rot(q, r["packed"], r["desc"], np.float32(0.125), rot[::-1], dps)[0]
+    assert not np.allclose(swapped, ref, rtol=1e-6, atol=1e-6)
+    I = np.eye(128, dtype=np.float32)
+    eye = np.broadcast_to(I, (N // span, 2, 128, 128))
+    a = O.decode_stream(q, r["packed"], r["desc"], np.float32(0.125))
+    b = O.decode_stream_rot(q, r["packed"], r["desc"], np.float32(0.125), eye, dps)
+    assert np.allclose(a[0], b[0], rtol=1e-13, atol=1e-13) and np.array_equal(a[1], b[1])

@@ -194,6 +194,26 @@ def make_kara(seed=0, device="cpu", B=None, prompt=None, gen=None):
     return dict(K=K, V=V, Qall=Qall, q=q, B=B, L=L, prompt=prompt, gen=gen, Hq=Hq, Hkv=Hkv, G=G)
 
 
+def offaxis_blocks(X, block, seed=1):
+    """X: [B, Hkv, N, D] bf16 -> a copy in which every `block`-token block of
+    every stream is multiplied by its own seeded random orthogonal matrix
+    (QR of a Gaussian matrix) and rounded to bf16 again.  The outlier
+    channels and heavy-token directions of the recipe then sit along
+    directions that differ from block to block instead of along channels
+    (an input transformation only)."""
+    B, H, N, _ = X.shape
+    g = _gen(seed, X.device)
+    out = torch.empty_like(X)
+    nb = (N + block - 1) // block
+    for b in range(B):
+        Q, _ = torch.linalg.qr(_randn(g, (H * nb, D, D), X.device).cpu())
+        Q = Q.to(X.device).view(H, nb, D, D)
+        for j in range(nb):
+            t0, t1 = j * block, min(N, (j + 1) * block)
+            out[b, :, t0:t1] = (X[b, :, t0:t1].float() @ Q[:, j]).to(torch.bfloat16)
+    return out
+
+
 def u16(t):
     """bf16 tensor -> numpy uint16 bit patterns (host copy)."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

@@ -1,10 +1,13 @@
 """Parity at the workloads' full sizes, in the launch configuration bench.py
-times (library-chosen split count), on sampled streams the oracle computes
-one by one: every selection output of a sampled stream is compared bit for
-bit (scores, descriptors, the stream's whole packed byte range) and its
-decode output within the attention tolerance.  Properties that hold at any
-size are checked on all streams (descriptor sanity, used bytes within the
-budget, score mass = G * W per stream)."""
+times (library-chosen split count), on streams the oracle computes one by
+one: every selection output of a checked stream is compared bit for bit
+(scores, descriptors, the stream's whole packed byte range) and its decode
+output within the attention tolerance.  The Llama-3-8B-shaped layer and the
+million-token request are checked on every stream, the batched 128k workload
+on 32 of its 128 streams (every kv head four times, every batch entry), the
+Kara workload on eight streams (one per kv head).  Properties that hold at
+any size are checked on all streams (descriptor sanity, used bytes within
+the budget, score mass = G * W per stream)."""
 import numpy as np
 import pytest
 import torch
@@ -17,7 +20,8 @@ from oracle import oracle as O
 pytestmark = pytest.mark.gpu
 
 
-def _sampled(cfg, streams_to_check, budget_scope=0, rotate=False, store_logits=False, **over):
+def _sampled(cfg, streams_to_check, budget_scope=0, rotate=False, store_logits=False, rot_span=0,
+             **over):
     c = dict(gen.CONFIGS[cfg])
     c.update(over)
     S = c["S"]
@@ -28,9 +32,11 @@ def _sampled(cfg, streams_to_check, budget_scope=0, rotate=False, store_logits=F
     say(f"[fullsize] {cfg}: kv_compress + kv_attend_decode")
     r = runtime.compress(w["K"], w["V"], w["Qw"], seg_tokens=S, strategies=strat,
                          budget_bytes=budget, scale=float(SCALE), want_scores=True,
-                         budget_scope=budget_scope, rotate=rotate, store_logits=store_logits)
+                         budget_scope=budget_scope, rotate=rotate, store_logits=store_logits,
+                         rot_span=rot_span)
     out, lse = runtime.decode(w["q"], r.packed, r.desc, n_kv_heads=c["Hkv"],
-                              max_desc_per_stream=r.n_seg, scale=float(SCALE), rot=r.rot)
+                              max_desc_per_stream=r.n_seg, scale=float(SCALE), rot=r.rot,
+                              seg_tokens=S, rot_span=rot_span)
     torch.cuda.synchronize()
     desc = r.desc_host()
     used = r.used.cpu().numpy()
@@ -52,7 +58,8 @@ def _sampled(cfg, streams_to_check, budget_scope=0, rotate=False, store_logits=F
         Ks, Vs = gen.u16(w["K"][b, h]), gen.u16(w["V"][b, h])
         Qs = gen.u16(w["Qw"][b, h * G:(h + 1) * G])
         o = O.compress_stream(Ks, Vs, Qs, S=S, strategies=strat, budget_bytes=budget, scale=SCALE,
-                              base_offset=s * cap, budget_scope=budget_scope, rotate=rotate)
+                              base_offset=s * cap, budget_scope=budget_scope, rotate=rotate,
+                              rot_span=rot_span)
         if rotate:
             assert np.array_equal(r.rot[s].cpu().numpy().view(np.uint32), o["rot"].view(np.uint32))
         assert np.array_equal(r.scores[s].cpu().numpy().view(np.uint32), o["scores"].view(np.uint32))
@@ -64,7 +71,8 @@ def _sampled(cfg, streams_to_check, budget_scope=0, rotate=False, store_logits=F
         local = o["desc"].copy()
         local["offset"] -= s * cap
         if rotate:
-            ref, rlse = O.decode_stream_rot(q, o["packed"], local, SCALE, o["rot"][0], o["rot"][1])
+            ref, rlse = O.decode_stream_rot(q, o["packed"], local, SCALE, o["rot"],
+                                            (rot_span // S) if rot_span else None)
         else:
             ref, rlse = O.decode_stream(q, o["packed"], local, SCALE)
         check_attention(out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G], ref, rlse,
@@ -73,12 +81,20 @@ def _sampled(cfg, streams_to_check, budget_scope=0, rotate=False, store_logits=F
     torch.cuda.empty_cache()
 
 
+# 32 of the 128 streams: s = 9 i mod 128 runs through every kv head (s mod 8)
+# four times and every batch entry (s div 8)
+BATCHED_STREAMS = sorted({(9 * i) % 128 for i in range(32)})
+
+
 def test_fullsize_llama8b():
-    _sampled("llama8b", [0, 5])
+    _sampled("llama8b", list(range(8)))
 
 
 def test_fullsize_batched128k():
-    _sampled("batched128k", [0, 77])
+    assert len(BATCHED_STREAMS) == 32
+    assert {s % 8 for s in BATCHED_STREAMS} == set(range(8))
+    assert {s // 8 for s in BATCHED_STREAMS} == set(range(16))
+    _sampled("batched128k", BATCHED_STREAMS)
 
 
 def test_fullsize_batched128k_stored_logits():
@@ -97,8 +113,14 @@ def test_fullsize_batched128k_rotated():
     _sampled("batched128k", [5, 100], rotate=True)
 
 
+def test_fullsize_batched128k_rotated_spans():
+    """The same workload with one rotation per 4096-token span (32 spans per
+    stream), as the rotation measurement beside the headline runs it."""
+    _sampled("batched128k", [7], rotate=True, rot_span=4096)
+
+
 def test_fullsize_million():
-    _sampled("million", [3])
+    _sampled("million", list(range(8)))
 
 
 def test_max_context_one_stream():

@@ -106,6 +106,8 @@ def lib():
         L.kv_attend_decode.argtypes = [ctypes.POINTER(Params), P, P, P, P, P, P, P,
                                        ctypes.c_size_t, P]
         L.kv_attend_decode.restype = ctypes.c_int
+        L.kv_attend_decode_noalloc.argtypes = [ctypes.POINTER(Params), P, P, P, P, P, P, P]
+        L.kv_attend_decode_noalloc.restype = ctypes.c_int
         L.kv_summarize.argtypes = [ctypes.POINTER(Params), P, P, P, P, P]
         L.kv_summarize.restype = ctypes.c_int
         L.kv_select_segments.argtypes = [ctypes.POINTER(Params), P, P, P, P, ctypes.c_uint32, P,
@@ -241,6 +243,18 @@ def kv_attend_decode(params, q, packed, desc, n_desc, out, lse, ws):
                                 ws.numel() * ws.element_size() if ws is not None else 0, _stream())
     if st != 0:
         raise KvcError("kv_attend_decode", st)
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def kv_attend_decode_noalloc(params, q, packed, desc, n_desc, out, lse):
+    """Decode attention with the library's fixed scratch instead of a
+    workspace (nothing is allocated; calls on one GPU must not overlap)."""
+    st = lib().kv_attend_decode_noalloc(ctypes.byref(params.p), _ptr(q), _ptr(packed), _ptr(desc),
+                                        _ptr(n_desc), _ptr(out), _ptr(lse), _stream())
+    if st != 0:
+        raise KvcError("kv_attend_decode_noalloc", st)
 
 
 def kv_summarize(params, packed, desc, n_desc, summary):

@@ -36,6 +36,7 @@
 // l reads row 4*sg + ((l & 15) >> 2), channels 64*half + 16*(l >> 4) + 4*(l & 3).
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <mutex>
 
 #include "kvc_device.h"
 #include "kvc_internal.h"
@@ -892,6 +893,32 @@ __global__ __launch_bounds__(128) void k_rotate_q(const uint16_t* __restrict__ q
   const uint64_t o = ((uint64_t)r * n_span + span) * D + k;
   qhi[o] = (uint16_t)hi;
   qlo[o] = (uint16_t)f2bf(acc - bf2f(hi));
+}
+
+// Fixed decode scratch for kv_attend_decode_noalloc: the split partials of
+// a call live here instead of in a caller's workspace.  Every GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// the name is only a stand-in; the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[KVC_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {

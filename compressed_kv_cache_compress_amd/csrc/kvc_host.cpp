@@ -406,6 +406,25 @@ kvc_status kv_attend_decode(const kvc_params* p, const uint16_t* q, const void* 
                      stream);
 }
 
+kvc_status kv_attend_decode_noalloc(const kvc_params* p, const uint16_t* q, const void* packed,
+                                    const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
+                                    uint16_t* out, float* lse, hipStream_t stream) {
+  if (p && p->struct_size == sizeof(kvc_params) && p->rotate) return KVC_E_INVALID;
+  Shape sh;
+  kvc_status st = check_shape(p, &sh);
+  if (st != KVC_OK) return st;
+  const uint32_t maxd = decode_maxd(p);
+  if (maxd == 0) return KVC_E_INVALID;
+  kvc_layout L;
+  std::memset(&L, 0, sizeof L);
+  if (!decode_layout(p, sh, maxd, &L)) return KVC_E_INVALID;
+  if (L.decode_ws_bytes > KVC_NOALLOC_SCRATCH_BYTES) return KVC_E_WORKSPACE;
+  void* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess || !ws) return KVC_E_HIP;
+  return decode_impl(p, q, packed, desc, n_desc_per_stream, nullptr, out, lse, ws,
+                     KVC_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 kvc_status kv_attend_decode_rotated(const kvc_params* p, const uint16_t* q, const void* packed,
                                     const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
                                     const float* rot, uint16_t* out, float* lse, void* ws,

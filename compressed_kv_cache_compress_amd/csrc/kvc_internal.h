@@ -144,5 +144,8 @@ hipError_t launch_summarize(const SummaryPlan& p, hipStream_t st);
 hipError_t launch_read_stream(const void* src, uint64_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_select(const SelectPlan& p, hipStream_t st);
 hipError_t launch_decode(const DecodePlan& p, hipStream_t st);
+// Device address of the fixed decode scratch on the current device (looked
+// up once per device).
+hipError_t noalloc_scratch(void** ptr);
 
 }  // namespace kvc

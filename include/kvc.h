@@ -272,6 +272,22 @@ kvc_status kv_attend_decode(const kvc_params* p, const uint16_t* q, const void* 
                             uint16_t* out, float* lse, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): kv_attend_decode without
+ * a workspace argument.  The split partials go to a fixed device array of
+ * KVC_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, held until the
+ * process ends); the call allocates nothing.  Same kernels and results as
+ * kv_attend_decode with the same p.  Returns KVC_E_WORKSPACE when the
+ * workspace kv_layout_query reports for p (decode_ws_bytes) exceeds
+ * KVC_NOALLOC_SCRATCH_BYTES, KVC_E_HIP when the array cannot be located on
+ * the current device.  Every call on one GPU uses the same array: calls that
+ * overlap on one GPU (on different streams or host threads) race and must
+ * be ordered by the caller. */
+#define KVC_NOALLOC_SCRATCH_BYTES (16u << 20)
+kvc_status kv_attend_decode_noalloc(const kvc_params* p, const uint16_t* q, const void* packed,
+                                    const kvc_seg_desc* desc, const uint32_t* n_desc_per_stream,
+                                    uint16_t* out, float* lse, hipStream_t stream);
+
 /* Decode over a cache compressed by kv_compress_rotated (p->rotate = 1):
  * descriptor i of a stream holds vectors rotated by the R of span
  * i / (rot_span / seg_tokens) (one span when rot_span = 0).  Each query

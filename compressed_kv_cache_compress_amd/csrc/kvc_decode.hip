@@ -815,63 +815,89 @@ __global__ __launch_bounds__(RG * RC) void k_decode_reduce(const float* __restri
 }
 
 // Rotated cache: per span, the merge of the span's splits (every split
-// weighted against the maximum M over all splits of the row) over all 128
+// weighted against the maximum M over all splits of its row) over all 128
 // channels, rotated back by the span's R_V and added up; out = sum / L,
 // with L the merged denominator, then the single bf16 rounding.  grid
-// (batch*n_q_heads), 128 threads: thread c owns output channel c.  Split sp
-// belongs to span sp / spl (spl = splits when there is one span).
+// (streams), 128 threads: thread c owns output channel c of the G rows (q
+// heads) of the stream, so each span's R_V is read once for all of them.
+// Split sp belongs to span sp / spl (spl = splits when there is one span).
+constexpr int RMAXG = 16;
 __global__ __launch_bounds__(128) void k_decode_reduce_rot(const float* __restrict__ part_ml,
                                                            const float* __restrict__ part_acc,
                                                            const float* __restrict__ rot,
                                                            uint16_t* __restrict__ out,
                                                            float* __restrict__ lse, int splits,
                                                            int spl, int n_span, int hq, int hkv) {
-  __shared__ float o1[D];
-  __shared__ float red[2][D];
-  const int r = blockIdx.x, c = threadIdx.x;
-  const int b = r / hq, hd = r - b * hq;
-  const int s = b * hkv + hd / (hq / hkv);
-  const float* ml = part_ml + (uint64_t)r * splits * 2;
-  const float* acc = part_acc + (uint64_t)r * splits * D;
-  // M and L over all splits (thread c folds splits c, c + 128, ...)
-  float m = -INFINITY;
-  for (int sp = c; sp < splits; sp += D) m = fmaxf(m, ml[2 * sp]);
-  red[0][c] = m;
-  __syncthreads();
-  for (int w = D / 2; w >= 1; w >>= 1) {
-    if (c < w) red[0][c] = fmaxf(red[0][c], red[0][c + w]);
+  __shared__ float o1[RMAXG][D];
+  __shared__ float red[D];
+  __shared__ float Mg[RMAXG], Lg[RMAXG];
+  const int s = blockIdx.x, c = threadIdx.x;
+  const int G = hq / hkv;
+  const int b = s / hkv, h = s - b * hkv;
+  const int row0 = b * hq + h * G;
+  // M and L of every row (thread c folds splits c, c + 128, ...)
+  for (int g = 0; g < G; ++g) {
+    const float* ml = part_ml + (uint64_t)(row0 + g) * splits * 2;
+    float m = -INFINITY;
+    for (int sp = c; sp < splits; sp += D) m = fmaxf(m, ml[2 * sp]);
+    red[c] = m;
     __syncthreads();
-  }
-  const float M = red[0][0];
-  if (M == -INFINITY) {
-    out[(uint64_t)r * D + c] = 0;
-    if (lse && c == 0) lse[r] = -INFINITY;
-    return;
-  }
-  float l = 0.0f;
-  for (int sp = c; sp < splits; sp += D) l += ml[2 * sp + 1] * exp2f(ml[2 * sp] - M);
-  red[1][c] = l;
-  __syncthreads();
-  for (int w = D / 2; w >= 1; w >>= 1) {
-    if (c < w) red[1][c] += red[1][c + w];
-    __syncthreads();
-  }
-  const float L = red[1][0];
-  float v = 0.0f;
-  for (int span = 0; span < n_span; ++span) {
-    float a = 0.0f;
-    for (int sp = span * spl; sp < (span + 1) * spl; ++sp) {
-      const float m_sp = ml[2 * sp];
-      if (m_sp != -INFINITY) a += acc[(uint64_t)sp * D + c] * exp2f(m_sp - M);
+    for (int w = D / 2; w >= 1; w >>= 1) {
+      if (c < w) red[c] = fmaxf(red[c], red[c + w]);
+      __syncthreads();
     }
-    __syncthreads();  // the previous span's o1 is read by every thread
-    o1[c] = a;
+    const float M = red[0];
+    __syncthreads();
+    float l = 0.0f;
+    if (M != -INFINITY)
+      for (int sp = c; sp < splits; sp += D) l += ml[2 * sp + 1] * exp2f(ml[2 * sp] - M);
+    red[c] = l;
+    __syncthreads();
+    for (int w = D / 2; w >= 1; w >>= 1) {
+      if (c < w) red[c] += red[c + w];
+      __syncthreads();
+    }
+    if (c == 0) {
+      Mg[g] = M;
+      Lg[g] = red[0];
+    }
+    __syncthreads();
+  }
+  float v[RMAXG];
+#pragma unroll
+  for (int g = 0; g < RMAXG; ++g) v[g] = 0.0f;
+  for (int span = 0; span < n_span; ++span) {
+    for (int g = 0; g < G; ++g) {
+      const float* ml = part_ml + (uint64_t)(row0 + g) * splits * 2;
+      const float* acc = part_acc + (uint64_t)(row0 + g) * splits * D;
+      const float M = Mg[g];
+      float a = 0.0f;
+      for (int sp = span * spl; sp < (span + 1) * spl; ++sp) {
+        const float m_sp = ml[2 * sp];
+        if (m_sp != -INFINITY) a += acc[(uint64_t)sp * D + c] * exp2f(m_sp - M);
+      }
+      o1[g][c] = a;
+    }
     __syncthreads();
     const float* RV = rot + (((uint64_t)s * n_span + span) * 2 + 1) * D * D + (uint64_t)c * D;
-    for (int k = 0; k < D; ++k) v = __builtin_fmaf(RV[k], o1[k], v);
+    for (int k = 0; k < D; ++k) {
+      const float rv = RV[k];
+#pragma unroll
+      for (int g = 0; g < RMAXG; ++g)
+        if (g < G) v[g] = __builtin_fmaf(rv, o1[g][k], v[g]);
+    }
+    __syncthreads();  // the next span rewrites o1
   }
-  out[(uint64_t)r * D + c] = (uint16_t)f2bf(v / L);
-  if (lse && c == 0) lse[r] = (M + log2f(L)) * 0.69314718055994530942f;
+#pragma unroll
+  for (int g = 0; g < RMAXG; ++g) {
+    if (g < G) {
+      const int r = row0 + g;
+      const bool any = Mg[g] != -INFINITY;
+      out[(uint64_t)r * D + c] = any ? (uint16_t)f2bf(v[g] / Lg[g]) : (uint16_t)0;
+      if (lse && c == 0)
+        lse[r] = any ? (Mg[g] + log2f(Lg[g])) * 0.69314718055994530942f : -INFINITY;
+    }
+  }
 }
 
 // Rotated queries for a rotated cache: q'[k] = fma chain over i of
@@ -950,7 +976,7 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
       hipLaunchKernelGGL((k_decode_split<2, true>), grid, dim3(64 * WAVES), 0, st, a);
     else
       hipLaunchKernelGGL((k_decode_split<4, true>), grid, dim3(64 * WAVES), 0, st, a);
-    hipLaunchKernelGGL(k_decode_reduce_rot, dim3(p.batch * p.hq), dim3(D), 0, st, p.part_ml,
+    hipLaunchKernelGGL(k_decode_reduce_rot, dim3(p.streams), dim3(D), 0, st, p.part_ml,
                        p.part_acc, p.rot, p.out, p.lse, p.splits, p.spl, p.n_span, p.hq, p.hkv);
     return hipGetLastError();
   }

@@ -21,7 +21,9 @@
  *    aligned, owned by the caller.  bf16 tensors are uint16_t bit patterns.
  *  - Work is enqueued on the caller's `stream`; nothing is synchronised and
  *    the library never allocates or frees device memory.  All scratch space
- *    comes from the caller's workspace `ws` (size from kv_layout_query).
+ *    comes from the caller's workspace `ws` (size from kv_layout_query),
+ *    except for kv_attend_decode_noalloc, which uses a fixed array the
+ *    library holds on each device.
  *  - Arguments are validated on the host first; on any error nothing is
  *    enqueued and the call returns a negative kvc_status.  Device faults
  *    surface at the caller's next synchronisation.
@@ -98,7 +100,7 @@ typedef struct {
   uint32_t desc_stream_stride;   /* descriptors between streams; 0 => region_len/seg_tokens */
   /* --- decode (kv_attend_decode) --- */
   uint32_t max_desc_per_stream;  /* descriptor stride per stream for decode; 0 => region_len/seg_tokens */
-  uint32_t decode_splits;        /* split-K factor; 0 => library choice */
+  uint32_t decode_splits;        /* split-K factor, 1 .. 65536; 0 => library choice */
   /* --- compression, continued --- */
   uint32_t budget_scope;         /* KVC_BUDGET_SEGMENT (0) or KVC_BUDGET_STREAM (1) */
   uint32_t compress_max_waves;   /* 0, or a cap on the waves each scoring and channel-
@@ -180,8 +182,16 @@ typedef struct {
 } kvc_layout;
 
 /* Host only (no device call).  Validates p and reports byte costs, feasible
- * strategies, buffer and workspace sizes.  Returns KVC_E_BUDGET when no
- * strategy fits budget_bytes (the layout is still filled). */
+ * strategies, buffer and workspace sizes: the packed bytes of one segment
+ * under each strategy of the table (MosaicKV review page, Fig. 6 caption:
+ * packed KV format, bitmask plus the kept bf16 elements of each vector;
+ * abstract and Fig. 5 caption: a strategy per segment under the memory
+ * target), which strategies fit the budget, and the split-K factor decode
+ * will use.  Returns KVC_E_BUDGET when no strategy fits budget_bytes (the
+ * layout is still filled), KVC_E_INVALID for malformed parameters,
+ * including a decode_splits above 65536 or one that makes streams x splits
+ * exceed INT_MAX (or, for a rotated decode over spans, that is no multiple of
+ * the span count). */
 kvc_status kv_layout_query(const kvc_params* p, kvc_layout* out);
 
 /* Compress the region of every stream (MosaicKV: dynamic two-D compression;

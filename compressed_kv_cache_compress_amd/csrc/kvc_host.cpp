@@ -51,12 +51,12 @@ kvc_status compress_layout(const kvc_params* p, const Shape& sh, kvc_layout* L, 
     return KVC_E_INVALID;
   if (p->budget_scope > KVC_BUDGET_STREAM) return KVC_E_INVALID;
   if (p->rotate > 1 || p->store_logits > 1) return KVC_E_INVALID;
-  if (p->rot_span && (!p->rotate || p->rot_span % 64 || p->rot_span % p->seg_tokens ||
-                      p->region_len % p->rot_span))
-    return KVC_E_INVALID;
   const bool stream_scope = p->budget_scope == KVC_BUDGET_STREAM;
   const uint32_t S = p->seg_tokens;
   if (!pow2(S) || S < 16 || S > 256) return KVC_E_INVALID;
+  if (p->rot_span && (!p->rotate || p->rot_span % 64 || p->rot_span % S ||
+                      p->region_len % p->rot_span))
+    return KVC_E_INVALID;
   if (p->n_ctx == 0 || p->n_ctx % BLK || p->n_ctx > (1u << 22)) return KVC_E_INVALID;
   if (p->region_len == 0 || p->region_len % S) return KVC_E_INVALID;
   if ((uint64_t)p->region_begin + p->region_len > p->n_ctx) return KVC_E_INVALID;

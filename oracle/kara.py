@@ -53,6 +53,7 @@ def final_tokens(prompt, generated, *, delta, protect, seg, retention_pct):
     """Tokens per stream once every event has run: the dense prompt, T per
     event and the dense tokens no event covers (the protected tail and any
     generated tokens past the last region)."""
+    assert delta == seg, "one region per period: the regions tile the generated tokens"
     ev, _ = events(prompt, generated, window=protect + seg, delta=delta, protect=protect, seg=seg)
     T = kept_tokens(retention_pct, seg)
     covered = len(ev) * seg

@@ -399,6 +399,9 @@ def test_rotation_span_validation():
         assert st == -1, bad
     st, _ = kvc.kv_layout_query(_params("batched128k", rot_span=4096), check=False)
     assert st == -1  # no rotation
+    st, _ = kvc.kv_layout_query(_params("batched128k", rotate=1, rot_span=4096, seg_tokens=0),
+                                check=False)
+    assert st == -1  # no segment size: rejected before any division by it
     st, L = kvc.kv_layout_query(_params("batched128k", rotate=1, rot_span=4096))
     assert st == 0
     d = dict(batch=2, n_q_heads=8, n_kv_heads=2, max_desc_per_stream=64, rotate=1,

@@ -337,8 +337,8 @@ kvc_status kv_summarize(const kvc_params* p, const void* packed, const kvc_seg_d
 
 /* kv_select_segments: for each stream, every non-empty descriptor d below
  * n_desc gets score(d) = max over the group's q heads g of the pairwise-tree
- * fp32 sum over channels 0..127 (each half of a range summed separately,
- * then added) of max(q_g kmax, q_g kmin) + 0 (exact bf16 products; -0 taken
+ * fp32 sum over channels 0..127 (the same tree as every selection sum) of
+ * max(q_g kmax, q_g kmin) + 0 (exact bf16 products; -0 taken
  * as +0), an upper bound of q_g . k over the descriptor's kept keys (scale
  * omitted: it does not change the order).  The keep best by (score desc, index asc)
  * are written to out_desc in index order.

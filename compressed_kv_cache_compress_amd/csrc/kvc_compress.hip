@@ -1111,10 +1111,62 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs a) {
   // drops its kept values at the row's running rank, an exclusive prefix of
   // the per-lane counts) and written out in 16-byte pieces
   __shared__ uint4 s_row[16][D / 8 + 1];
+  __shared__ uint32_t s_vm[4][32];  // one transposed V block's mask bits per wave
   const int rr = 4 * wv + (lane >> 4), q = lane & 15;
   for (int part = 0; part < 2; ++part) {
     const uint16_t* X = part ? a.V : a.K;
     const uint32_t mo = part ? vmask : kmask, vo = part ? vval : kval;
+    if (part == 1 && hasmask) {
+      // V of a masked segment: transposed blocks of 8 kept tokens, wave wv
+      // takes blocks wv, wv + 4, ...  Lane l holds channels l (h 0) and
+      // 64 + l (h 1): its 2 nb mask bits (bit nb h + t: token t keeps the
+      // channel) go to bit 2 nb l of the block's mask bytes, its kept values
+      // (h, t order) to the block's value bytes at the running rank, an
+      // exclusive prefix of the lanes' counts.
+      const uint16_t* Xs = X + (uint64_t)s * a.kv_stride + (uint64_t)a.region_begin * D;
+      for (int bk = wv; 8 * bk < T; bk += 4) {
+        const int nb = min(8, T - 8 * bk);
+        uint32_t field = 0;
+        uint16_t v0[8], v1[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          v0[t] = 0;
+          v1[t] = 0;
+          if (t < nb) {
+            const int tr = sg * S + s_idx[8 * bk + t];
+            const uint64_t o = (((uint64_t)s * a.region_len + tr) * a.nc + u) * 2 + 1;
+            const uint4 m = reinterpret_cast<const uint4*>(a.masks)[o];
+            const uint32_t b0 = ((lane < 32 ? m.x : m.y) >> (lane & 31)) & 1u;
+            const uint32_t b1 = ((lane < 32 ? m.z : m.w) >> (lane & 31)) & 1u;
+            field |= (b0 << t) | (b1 << (nb + t));
+            const uint16_t* row = Xs + (uint64_t)tr * D;
+            v0[t] = row[lane];
+            v1[t] = row[64 + lane];
+          }
+        }
+        const uint32_t cnt = (uint32_t)__popc(field);
+        uint32_t k = wave_incl_scan_u32(cnt) - cnt;
+        uint16_t* bv = reinterpret_cast<uint16_t*>(out + vo + (uint64_t)16 * c * bk);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (t < nb && ((field >> t) & 1u)) bv[k++] = v0[t];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (t < nb && ((field >> (nb + t)) & 1u)) bv[k++] = v1[t];
+        // mask bits: 2 nb bits at bit 2 nb l, assembled in LDS (the wave's
+        // own words, written and read in order by the same wave)
+        if (lane < 32) s_vm[wv][lane] = 0u;
+        const uint32_t bit = 2u * (uint32_t)nb * (uint32_t)lane;
+        if (field) {
+          atomicOr(&s_vm[wv][bit >> 5], field << (bit & 31u));
+          if ((bit & 31u) + 2u * (uint32_t)nb > 32u)
+            atomicOr(&s_vm[wv][(bit >> 5) + 1u], field >> (32u - (bit & 31u)));
+        }
+        if (lane < 4 * nb)
+          reinterpret_cast<uint32_t*>(out + mo + (uint64_t)128 * bk)[lane] = s_vm[wv][lane];
+      }
+      continue;
+    }
     if (hasmask) {
       for (int j = tid; j < T; j += 256) {
         const uint64_t o = (((uint64_t)s * a.region_len + sg * S + s_idx[j]) * a.nc + u) * 2 + part;

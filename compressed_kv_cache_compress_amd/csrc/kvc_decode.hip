@@ -5,35 +5,34 @@
 // Work split: one wave per (stream, split); a split is a contiguous range of
 // the stream's descriptors.  Four independent waves share a workgroup only to
 // share one LDS table.  Each wave walks its descriptors in chunks of up to 16
-// kept tokens (fewer for rows wider than 96 channels):
+// kept tokens (8 for masked rows wider than 88 channels, 12 for dense rows):
 //   * the next chunk's K and V bytes (masks + compact values) are loaded into
 //     registers while the current chunk is computed, then written to LDS;
-//   * every kept vector is expanded from (bitmask, compact bf16 values) to a
-//     dense 128-channel row, one mask byte (8 channels) per lane and step,
+//   * every kept K vector is expanded from (bitmask, compact bf16 values) to
+//     a dense 128-channel row, one mask byte (8 channels) per lane and step,
 //     one nibble (4 channels) at a time: the nibble's candidate values are
 //     the 4 compact elements starting at its rank (an 8-byte window, shifted
 //     by one element when the rank is odd), and one v_perm_b32 per output
 //     dword places them (or zero) using a 16-entry selector table indexed by
-//     the nibble;
-//   * staged rows are padded by 16 bytes so that the 16 tokens of a chunk
-//     start on different LDS banks;
+//     the nibble; staged K rows are padded by 16 bytes so that the 16 tokens
+//     of a chunk start on different LDS banks;
+//   * the V side of a masked segment is stored in transposed blocks of 8
+//     tokens (per channel, the tokens that keep it), so the same nibble
+//     expansion over a channel's token mask yields 4 tokens of one channel:
+//     exactly the B operand the p.v product takes, with no dense V tile in
+//     between;
 //   * q.k of the 16 tokens and p.v run on MFMA (bf16 inputs, fp32
 //     accumulation); the softmax is online, in base 2, with DPP row
 //     reductions.
 // A second kernel merges the splits (log-sum-exp) and rounds to bf16.
 //
-// MFMA row mapping: q head h of the group is A-row 4*(h & 3) + (h >> 2), so
-// in the 16x16 accumulator layout (lane l, item j <-> row 4*(l>>4)+j, column
-// l&15) lane l's item j belongs to head 4*j+(l>>4) and to token/channel l&15;
-// for G <= 4 every head lives in item 0 of its own 16-lane row.  For G <= 4
-// the p.v product uses the 16-block 4x4x4 MFMA instead (block b = lanes
-// 4b..4b+3; A[i][k] at lane 4b+i item k, B[k][j] at lane 4b+j item k, D[i][j]
-// at lane 4b+j item i): head i x channel (64*half + lane) accumulates over 4
-// tokens per instruction, so the output needs 8 instead of 32 registers.  Its
-// B operand (4 tokens x 1 channel per lane) comes from the row-major dense V
-// tile through ds_read_b64_tr_b16: within each 16-lane group, element r of
-// lane i is element (i & 3) of the 8 bytes read by lane 4r + (i >> 2), so lane
-// l reads row 4*sg + ((l & 15) >> 2), channels 64*half + 16*(l >> 4) + 4*(l & 3).
+// MFMA row mapping of q.k: q head h of the group is A-row 4*(h & 3) + (h >> 2),
+// so in the 16x16 accumulator layout (lane l, item j <-> row 4*(l>>4)+j,
+// column l&15) lane l's item j belongs to head 4*j+(l>>4) and to token l&15.
+// p.v uses the 16-block 4x4x4 MFMA (block b = lanes 4b..4b+3; A[i][k] at lane
+// 4b+i item k, B[k][j] at lane 4b+j item k, D[i][j] at lane 4b+j item i):
+// head 4 jg + i x channel (64*half + lane) accumulates over 4 tokens per
+// instruction, so a group of 4 heads needs 8 output registers.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <mutex>
@@ -45,6 +44,7 @@ namespace kvc {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
@@ -60,33 +60,47 @@ __device__ __forceinline__ const lds_u32_t* lds_ptr(uint32_t off) {
 }
 
 constexpr int CT = 16;  // MFMA columns: at most this many kept tokens per chunk
+constexpr int VB = 8;   // tokens per transposed V block of a masked segment
 #ifndef KVC_DECODE_SLOTS
 #define KVC_DECODE_SLOTS 3
 #endif
 // uint4 prefetch slots per lane and side: a chunk side (masks + values) is at
 // most 64 * NPF slots of 16 bytes.
 constexpr int NPF = KVC_DECODE_SLOTS;
-// Tokens per chunk for c kept channels: at most CT, at most what the prefetch
-// slots hold, and at most 3584 staged bytes (16 tokens up to c = 96), so that
-// wide rows do not set the staging size.  Narrow rows get 16 tokens; dense
-// rows 12.
 constexpr int slots_per_token(int c) { return (c < D ? 1 : 0) + c / 8; }
-constexpr int staged_per_token(int c) { return (c < D ? 16 : 0) + 2 * c + 16; }
-constexpr int cmin(int x, int y) { return x < y ? x : y; }
-constexpr int cmax(int x, int y) { return x > y ? x : y; }
+// Tokens per chunk for c kept channels.  Masked rows: two V blocks (16
+// tokens) while the prefetch slots hold them (c <= 88), else one (8); a
+// chunk of a masked segment therefore always starts on a V block.  Dense
+// rows: 12.
 constexpr int chunk_tokens(int c) {
-  return cmin(CT, cmin(64 * NPF / slots_per_token(c), 3584 / staged_per_token(c)));
+  return c >= D ? 12 : (2 * VB * slots_per_token(c) <= 64 * NPF ? 2 * VB : VB);
 }
-constexpr int stage_bytes() {
+constexpr int cmax(int x, int y) { return x > y ? x : y; }
+// Staging of one chunk side.  K: [masks 16 nt][rows (2c + 16) nt] (each row
+// padded by 16 bytes); dense V likewise (the rows are the tile the
+// transposing reads take, whole 4-token groups of them); masked V: [masks
+// 16 nt][values 2 c nt] as stored.  + pad: a window may read 12 bytes past
+// the last element, and an absent second V block is addressed 16 c bytes
+// past the first.
+constexpr int VR_STRIDE = 136;  // u16 per staged dense row (2 * 128 + 16 bytes)
+constexpr int kstage_bytes() {
   int m = 0;
-  for (int c = 8; c <= D; c += 8) m = cmax(m, chunk_tokens(c) * staged_per_token(c));
-  return m + 32;  // + pad: a window may read 12 bytes past a row's last element
+  for (int c = 8; c <= D; c += 8)
+    m = cmax(m, chunk_tokens(c) * ((c < D ? 16 : 0) + 2 * c + 16));
+  return m + 32;
 }
-// Staging bytes of one side of a chunk: [masks 16 * nt][rows (2c + 16) * nt].
-constexpr int STAGE = (stage_bytes() + 15) / 16 * 16;
+constexpr int vstage_bytes() {
+  int m = 4 * ((chunk_tokens(D) + 3) / 4) * 2 * VR_STRIDE;
+  for (int c = 8; c < D; c += 8) {
+    const int nt = chunk_tokens(c);
+    m = cmax(m, nt * (16 + 2 * c) + 32);
+    m = cmax(m, 16 * nt + 2 * c * VB + 32);
+  }
+  return m;
+}
+constexpr int KSTAGE = (kstage_bytes() + 15) / 16 * 16;
+constexpr int VSTAGE = (vstage_bytes() + 15) / 16 * 16;
 constexpr float RESCALE_SLACK = 8.0f;             // log2 units the running max may lag
-constexpr int VT_STRIDE = 20;                     // u16 per channel row of the transposed V tile (G > 4)
-constexpr int VR_STRIDE = 136;                    // u16 per token row of the row-major V tile (G <= 4)
 constexpr int WAVES = 4;
 #ifndef KVC_DECODE_MIN_BLOCKS
 #define KVC_DECODE_MIN_BLOCKS 2  // workgroups per CU the register budget is sized for
@@ -109,26 +123,21 @@ struct DecodeArgs {
 
 // Per-wave LDS.  The loop is software-pipelined: while the K side of chunk
 // i+1 is computed, the V side of chunk i is, so V stages and probabilities
-// are double-buffered.  A V stage's dense tile is written from the registers
-// its own reads produced, so the two share storage.
-// JG == 1: row-major dense V tile [token][VR_STRIDE]; otherwise transposed
-// [channel][VT_STRIDE].  Either is written over the V stage it is expanded from.
-template <int JG>
-struct VStage {
-  static constexpr int BYTES = cmax(STAGE, JG == 1 ? CT * VR_STRIDE * 2 : D * VT_STRIDE * 2);
-  union {
-    u32x4_t v[BYTES / 16];
-    uint16_t vt[BYTES / 2];
-  };
+// are double-buffered.
+union VStage {
+  u32x4_t v[VSTAGE / 16];
+  uint16_t vt[VSTAGE / 2];
 };
 template <int JG>
 struct WaveLds {
-  u32x4_t k[STAGE / 16];
-  VStage<JG> vs[2];               // chunk i's V side and chunk i+1's, alternating
+  u32x4_t k[KSTAGE / 16];
+  VStage vs[2];                   // chunk i's V side and chunk i+1's, alternating
   uint16_t pl[2][4 * JG * CT];    // probabilities, [head][token], alternating
 };
 
-static_assert(chunk_tokens(64) == CT && chunk_tokens(D) >= 12, "stage sizing");
+static_assert(chunk_tokens(64) == CT && chunk_tokens(88) == CT && chunk_tokens(96) == VB &&
+              chunk_tokens(D) == 12, "chunk sizing");
+static_assert(64 * NPF >= 12 * slots_per_token(D), "dense chunks fit the prefetch slots");
 
 
 // Ordering of a wave's LDS accesses, and why the chunk loop needs no fence:
@@ -231,6 +240,74 @@ __device__ __forceinline__ void expand_side(const uint8_t* st, int col, int grp,
   for (int kk = 0; kk < 4; ++kk) o[kk] = expand_finish(e, kk);
 }
 
+// V side of a masked chunk, staged as [masks 16 nt][values 2 c nt] in
+// transposed blocks of VB tokens (block bk = tokens 8 bk .. of the chunk,
+// mask bytes at 128 bk, values at 16 c bk; in a block of nb tokens, bit
+// nb (2 l + h) + t says token t keeps channel 64 h + l, and the values run
+// in (l, h, t) order).  Lane l takes channels l (h = 0) and 64 + l (h = 1):
+// its 2 nb bits of each block, an exclusive prefix of the lanes' counts for
+// the rank of its first value, and per nibble of a channel's block mask (4
+// tokens) one window and one v_perm_b32 per output dword -- the 4 tokens'
+// elements of the channel, which is the B operand of the 4x4x4 p.v product
+// for that token group as it stands.  Two phases like Expand.
+struct VExpand {
+  uint32_t w[4][2][3];  // [token group sg = 2 bk + n][h] windows
+  uint32_t sa[4][2];    // byte address of the first element (bits 1:0 used)
+  uint2 sel[4][2];
+};
+
+__device__ __forceinline__ void vexpand_issue(const uint8_t* st, int lane, int nt, int c,
+                                              const uint2* lut, VExpand& e) {
+  const uint32_t base = lds_off(st);
+  uint32_t chm[2][2];
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk) {
+    const int nb = min(max(nt - VB * bk, 0), VB);  // wave-uniform
+    uint32_t x = 0u;
+    if (nb > 0) {
+      const uint32_t bit = 2u * (uint32_t)nb * (uint32_t)lane;
+      const lds_u32_t* m = lds_ptr(base + 128u * bk + 4u * (bit >> 5));
+      x = __builtin_amdgcn_alignbit(m[1], m[0], bit & 31u);
+    }
+    chm[bk][0] = __builtin_amdgcn_ubfe(x, 0u, (uint32_t)nb);
+    chm[bk][1] = __builtin_amdgcn_ubfe(x, (uint32_t)nb, (uint32_t)nb);
+  }
+  const uint32_t p00 = __popc(chm[0][0]), p10 = __popc(chm[1][0]);
+  const uint32_t cnt = (p00 + __popc(chm[0][1])) | ((p10 + __popc(chm[1][1])) << 16);
+  const uint32_t ex = wave_incl_scan_u32(cnt) - cnt;  // two 16-bit prefixes
+  const uint32_t vb = base + 16u * (uint32_t)nt;
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk) {
+    const uint32_t r0 = bk ? ex >> 16 : ex & 0xFFFFu;
+    const uint32_t blk = vb + 16u * (uint32_t)c * bk;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t m = chm[bk][h];
+      const uint32_t ra = r0 + (h ? (bk ? p10 : p00) : 0u);
+      const uint32_t rb = ra + __popc(m & 0xFu);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int sg = 2 * bk + n;
+        const uint32_t ba = blk + 2u * (n ? rb : ra);
+        const lds_u32_t* w = lds_ptr(ba & ~3u);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) e.w[sg][h][i] = w[i];
+        e.sa[sg][h] = ba;
+        e.sel[sg][h] = lut[n ? m >> 4 : m & 0xFu];
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ s16x4_t vexpand_finish(const VExpand& e, int sg, int h) {
+  const uint32_t x0 = __builtin_amdgcn_alignbyte(e.w[sg][h][1], e.w[sg][h][0], e.sa[sg][h]);
+  const uint32_t x1 = __builtin_amdgcn_alignbyte(e.w[sg][h][2], e.w[sg][h][1], e.sa[sg][h]);
+  u32x2_t o;
+  o[0] = __builtin_amdgcn_perm(x1, x0, e.sel[sg][h].x);
+  o[1] = __builtin_amdgcn_perm(x1, x0, e.sel[sg][h].y);
+  return __builtin_bit_cast(s16x4_t, o);
+}
+
 // One chunk to stream: K part and V part each = [masks 16*nt][values 2*c*nt]
 // in global memory.  Uniform bases: the value stream of a side is addressed
 // as val + 16*j for stream slot j >= nm (val already offset by -16*nm).
@@ -274,8 +351,10 @@ __device__ __forceinline__ void prefetch(const Chunk& ch, int lane, Regs& r) {
   if constexpr (NPF > 3) prefetch_slot<3>(ch, lane, r);
 }
 
-// Slot j of the [masks | values] stream goes to LDS slot j (masks) or, for
-// value slot v = j - nm, to nm + v + v / (c/8): one 16-byte pad per row.
+// Slot j of the [masks | values] stream of the K side goes to LDS slot j
+// (masks) or, for value slot v = j - nm, to nm + v + v / (c/8): one 16-byte
+// pad per row.  The V side of a masked chunk is staged as stored (slot j);
+// dense V rows are padded like K rows.
 template <int I>
 __device__ __forceinline__ void commit_slot(const Chunk& ch, int lane, const Regs& r, u32x4_t* sk,
                                             u32x4_t* sv) {
@@ -284,7 +363,7 @@ __device__ __forceinline__ void commit_slot(const Chunk& ch, int lane, const Reg
     const uint32_t v = (uint32_t)(j - ch.nm);
     const int dst = (I == 0 && j < ch.nm) ? j : j + (int)(__umul24(v, ch.magic) >> 20);
     sk[dst] = r.k[I];
-    sv[dst] = r.v[I];
+    sv[ch.nm ? j : dst] = r.v[I];
   }
 }
 
@@ -348,17 +427,6 @@ __device__ __forceinline__ uint32_t desc_chunks(const kvc_seg_desc* dl, int i, i
   const float ct = (float)chunk_tokens(c < 8 ? 8 : (c > D ? D : c));
   return (uint32_t)((float)T * __builtin_amdgcn_rcpf(ct) + 0.96875f);
 }
-// inclusive sum over the 64 lanes: rows by row_shr, then the row broadcasts
-__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);
-  return x;
-}
-
 // Descriptor range [di, d1) of split sp of a stream with nd descriptors.
 // With more descriptors than splits and at most 256 of them, splits take
 // equal shares of chunks: descriptor i goes to split floor(E_i * splits / W),
@@ -520,12 +588,12 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
     }
   }
 
-  // JG == 1: O4[half][item i] = head i, channel 64*half + lane (4x4x4 MFMA);
-  // otherwise O[nn] is the 16x16 tile of channels 16*nn .. +15
-  constexpr int NO = JG == 1 ? 2 : 8;
-  f32x4_t O[NO];
+  // O4[half][jg] item i = head 4 jg + i, channel 64 half + lane (4x4x4 MFMA)
+  f32x4_t O4[2][JG];
 #pragma unroll
-  for (int nn = 0; nn < NO; ++nn) O[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int jg = 0; jg < JG; ++jg) O4[hf][jg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run[JG], l_run[JG];
 #pragma unroll
   for (int j = 0; j < JG; ++j) {
@@ -612,82 +680,72 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
     }
     return resc;
   };
-  // V side of a chunk staged in L.vs[vb]: dense V tile (over the stage),
-  // then O += P V with the probabilities in L.pl[vb].
+  // V side of a chunk staged in L.vs[vb]: O += P V with the probabilities
+  // in L.pl[vb], one 4x4x4 product per token group of 4, channel half and
+  // group of 4 heads.  Its B operand (4 tokens of the lane's channel) comes
+  // from the transposed-block expansion (masked rows) or from the staged
+  // dense rows through ds_read_b64_tr_b16: within each 16-lane group,
+  // element r of lane i is element (i & 3) of the 8 bytes read by lane
+  // 4r + (i >> 2), so lane l reads row 4 sg + ((l & 15) >> 2), channels
+  // 64 half + 16 (l >> 4) + 4 (l & 3).  Token groups past the chunk are
+  // skipped.
   auto v_side = [&](const Chunk& ch, int vb) {
-    VStage<JG>& S = L.vs[vb];
-    if (JG == 1) {
-      // row-major dense tile [token][channel], row stride VR_STRIDE
+    VStage& S = L.vs[vb];
+    const int nsg = (ch.nt + 3) >> 2;
+    s16x4_t bop[4][2];
+    if (ch.c == D) {
       static_assert(2 * VR_STRIDE == 2 * D + 16, "dense staged rows are the tile rows");
-      if (ch.c == D) {
-        // dense rows are staged exactly as the tile; rows past the chunk may
-        // hold older data (their probabilities are 0, but 0 * NaN is NaN)
-        const int nz = (CT - ch.nt) * (VR_STRIDE / 8);
-        for (int i = lane; i < nz; i += 64) {
-          const u32x4_t z = {0u, 0u, 0u, 0u};
-          S.v[ch.nt * (VR_STRIDE / 8) + i] = z;
-        }
-      } else {
-        u32x4_t vv[4];
-        expand_side<true>(reinterpret_cast<const uint8_t*>(S.v), col, grp, ch.nt, ch.c, lut, zrow,
-                          vv);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          *reinterpret_cast<u32x4_t*>(S.vt + col * VR_STRIDE + 8 * (4 * kk + grp)) = vv[kk];
+      // rows nt .. 4 nsg - 1 may hold older data (their probabilities are 0,
+      // but 0 * NaN is NaN)
+      const int nz = (4 * nsg - ch.nt) * (VR_STRIDE / 8);
+      for (int i = lane; i < nz; i += 64) {
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        S.v[ch.nt * (VR_STRIDE / 8) + i] = z;
       }
       const int trow = (lane & 15) >> 2, tcol = 16 * (lane >> 4) + 4 * (lane & 3);
 #pragma unroll
       for (int sg = 0; sg < CT / 4; ++sg) {
-        // A: head (lane & 3) x tokens 4sg..4sg+3; B: tokens x channel 64*hf + lane
-        const s16x4_t pa = *reinterpret_cast<const s16x4_t*>(L.pl[vb] + (lane & 3) * CT + 4 * sg);
+        if (sg < nsg) {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const uint16_t* src = S.vt + (4 * sg + trow) * VR_STRIDE + 64 * hf + tcol;
-          const s16x4_t w = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)src);
-          O[hf] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(pa, w, O[hf], 0, 0, 0);
+          for (int hf = 0; hf < 2; ++hf) {
+            const uint16_t* src = S.vt + (4 * sg + trow) * VR_STRIDE + 64 * hf + tcol;
+            bop[sg][hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)src);
+          }
         }
       }
     } else {
-      // transposed dense tile [channel][token]
-      u32x4_t vv[4];
-      const uint8_t* sv8 = reinterpret_cast<const uint8_t*>(S.v);
-      if (ch.c < D)
-        expand_side<true>(sv8, col, grp, ch.nt, ch.c, lut, zrow, vv);
-      else
-        expand_side<false>(sv8, col, grp, ch.nt, ch.c, lut, zrow, vv);
+      VExpand e;
+      vexpand_issue(reinterpret_cast<const uint8_t*>(S.v), lane, ch.nt, ch.c, lut, e);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        uint16_t* dst = S.vt + (8 * (4 * kk + grp)) * VT_STRIDE + col;
+      for (int sg = 0; sg < CT / 4; ++sg)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dst[(2 * i) * VT_STRIDE] = (uint16_t)(vv[kk][i] & 0xFFFFu);
-          dst[(2 * i + 1) * VT_STRIDE] = (uint16_t)(vv[kk][i] >> 16);
+        for (int hf = 0; hf < 2; ++hf) bop[sg][hf] = vexpand_finish(e, sg, hf);
+    }
+#pragma unroll
+    for (int sg = 0; sg < CT / 4; ++sg) {
+      if (sg < nsg) {
+#pragma unroll
+        for (int jg = 0; jg < JG; ++jg) {
+          // A: head 4 jg + (lane & 3) x tokens 4sg..4sg+3
+          const s16x4_t pa =
+              *reinterpret_cast<const s16x4_t*>(L.pl[vb] + (4 * jg + (lane & 3)) * CT + 4 * sg);
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            O4[hf][jg] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(pa, bop[sg][hf], O4[hf][jg], 0, 0, 0);
         }
-      }
-      s16x4_t pa = {0, 0, 0, 0};
-      if (hh_ok) pa = *reinterpret_cast<const s16x4_t*>(L.pl[vb] + hh * CT + 4 * grp);
-#pragma unroll
-      for (int nn = 0; nn < NO; ++nn) {
-        const s16x4_t w = *reinterpret_cast<const s16x4_t*>(S.vt + (16 * nn + col) * VT_STRIDE + 4 * grp);
-        O[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, w, O[nn], 0, 0, 0);
       }
     }
   };
+  // alpha[j] of the lanes of row i (lane 16 i) belongs to head 4 j + i
   auto rescale = [&](const float* alpha) {
-    if (JG == 1) {
-      // every lane holds all four heads: alpha of head i sits in row i
+#pragma unroll
+    for (int jg = 0; jg < JG; ++jg)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float ai = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[0]), 16 * i));
-        O[0][i] *= ai;
-        O[1][i] *= ai;
+        const float ai = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[jg]), 16 * i));
+        O4[0][jg][i] *= ai;
+        O4[1][jg][i] *= ai;
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < JG; ++j)
-#pragma unroll
-        for (int nn = 0; nn < NO; ++nn) O[nn][j] *= alpha[j];
-    }
   };
 
   static_assert((NPF == 3 || NPF == 4) && CT == 16, "prefetch slots are unrolled by hand; masks fit slot 0");
@@ -728,26 +786,17 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
       a.part_ml[2 * pi + 1] = l_run[j];
     }
   }
-  if (JG == 1) {
+#pragma unroll
+  for (int jg = 0; jg < JG; ++jg)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (i < a.G) {
-        const uint64_t pi = (uint64_t)(b * a.hq + h * a.G + i) * a.splits + sp;
-        a.part_acc[pi * D + lane] = O[0][i];
-        a.part_acc[pi * D + 64 + lane] = O[1][i];
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < JG; ++j) {
-      const int hd = 4 * j + grp;
+      const int hd = 4 * jg + i;
       if (hd < a.G) {
         const uint64_t pi = (uint64_t)(b * a.hq + h * a.G + hd) * a.splits + sp;
-#pragma unroll
-        for (int nn = 0; nn < NO; ++nn) a.part_acc[pi * D + 16 * nn + col] = O[nn][j];
+        a.part_acc[pi * D + lane] = O4[0][jg][i];
+        a.part_acc[pi * D + 64 + lane] = O4[1][jg][i];
       }
     }
-  }
 }
 
 // Log-sum-exp merge of the splits of one (b, q head) row, for a slice of

@@ -154,15 +154,23 @@ typedef struct {
   uint16_t seg_tokens;
 } kvc_seg_desc;
 
-/* Packed segment layout (MosaicKV Fig. 6 caption: packed KV format), parts
- * in this order, each starting 16-byte aligned:
+/* Packed segment layout (MosaicKV Fig. 6 caption: packed KV format, a
+ * bitmask and the kept values of every vector), parts in this order, each
+ * starting 16-byte aligned:
  *   K masks  [n_tok] x 16 B   (only if n_ch < 128; channel c = byte c/8, bit c%8)
  *   K values [n_tok][n_ch] bf16, kept channels in ascending order
- *   V masks  [n_tok] x 16 B   (only if n_ch < 128)
- *   V values [n_tok][n_ch] bf16
+ *   V masks  16 * n_tok B     (only if n_ch < 128)
+ *   V values 2 * n_tok * n_ch B
  *   indices  [n_tok] u16 ascending, position in the segment (only if n_tok < S),
  *            zero-padded to a multiple of 16 bytes.
- * Decode never reads the index list. */
+ * V with n_ch < 128 is stored transposed in blocks of 8 tokens: block b
+ * holds tokens 8b .. 8b+nb-1 (nb = min(8, n_tok - 8b)); its mask bits fill
+ * bytes [128 b, 128 b + 16 nb) of the V masks, bit nb*(2l + h) + t (LSB
+ * first) set iff token 8b+t keeps channel 64h + l (l = 0..63, h = 0, 1),
+ * and its kept values fill bytes [16 n_ch b, 16 n_ch b + 2 n_ch nb) of the
+ * V values in (l, h, t) order.  Same bytes as a per-token layout; decode
+ * expands a channel's tokens straight into its p.v operand.  Dense V
+ * (n_ch = 128) is [n_tok][128].  Decode never reads the index list. */
 
 typedef struct {
   uint32_t seg_bytes[KVC_MAX_STRATEGIES]; /* packed bytes of one segment per strategy */

@@ -320,19 +320,92 @@ void orc_token2chunk(const float* s, int S, int T, int alpha, int gamma, uint8_t
 }
 
 /* ------------------------------------------------------------------ */
-/* Packed segment layout ([M] Fig. 6 caption: packed KV format; the     */
-/* spec layout is bf16 values + per-vector channel bitmask +      */
-/* token index list).  Parts, each starting 16-byte aligned:            */
+/* Packed segment layout ([M] Fig. 6 caption: packed KV format, bf16   */
+/* values + per-vector channel bitmask + token index list).  Parts,     */
+/* each starting 16-byte aligned:                                       */
 /*   K masks [T] x 16 B (only if c < 128), K values [T][c] bf16,        */
 /*   V masks (only if c < 128), V values, token indices [T] u16 (only   */
 /*   if T < S) zero-padded to 16 B.                                     */
+/* K rows are token-major: token t's 16-byte mask (bit ch of byte ch/8, */
+/* LSB first), and its kept values in channel order.                    */
+/* V with c < 128 is grouped in blocks of 8 kept tokens (block b =      */
+/* tokens 8b .. 8b+nb-1, nb = min(8, T - 8b)), each block transposed:   */
+/* its mask bits fill bytes [128 b, 128 b + 16 nb) of the V mask part,  */
+/* bit nb (2 l + h) + t (LSB first) set iff token 8b+t keeps channel    */
+/* 64 h + l (l = 0..63, h = 0, 1); its values fill bytes                */
+/* [16 c b, 16 c b + 2 c nb) of the V value part, the kept elements in  */
+/* (l, h, t) order.  The page fixes the content (mask + kept values),   */
+/* not the byte order; every part keeps the size above.  Dense V        */
+/* (c = 128) is token-major.                                            */
 /* ------------------------------------------------------------------ */
+#define ORC_VBLK 8 /* tokens per transposed V block */
 long orc_seg_bytes(int T, int c, int S) {
   if (T <= 0) return 0;
   long mk = (c < ORC_D) ? 16L * T : 0;
   long vals = 2L * T * c;
   long idx = (T < S) ? ((2L * T + 15) / 16) * 16 : 0;
   return 2 * mk + 2 * vals + idx;
+}
+
+/* V part of a masked segment in transposed 8-token blocks (layout above).
+ * X: the segment's S rows [S][128] bf16; keep: S flags, T of them set;
+ * out: 16 T mask bytes then 2 T c value bytes. */
+static void orc_pack_v_blocks(const uint16_t* X, const uint8_t* keep, int S, int T, int c,
+                              uint8_t* out) {
+  int* tok = (int*)malloc(sizeof(int) * (size_t)T);
+  uint8_t* mk = (uint8_t*)malloc((size_t)16 * T);
+  int j = 0;
+  for (int t = 0; t < S; ++t)
+    if (keep[t]) tok[j++] = t;
+  for (j = 0; j < T; ++j) {
+    float r;
+    orc_channel_topc(X + (size_t)tok[j] * ORC_D, c, mk + 16 * j, &r);
+  }
+  uint8_t* vm = out;
+  uint8_t* vv = out + (size_t)16 * T;
+  memset(vm, 0, (size_t)16 * T);
+  for (int b = 0; ORC_VBLK * b < T; ++b) {
+    const int nb = T - ORC_VBLK * b < ORC_VBLK ? T - ORC_VBLK * b : ORC_VBLK;
+    uint8_t* bm = vm + (size_t)16 * ORC_VBLK * b;
+    uint8_t* bv = vv + (size_t)2 * c * ORC_VBLK * b;
+    int r = 0;
+    for (int l = 0; l < 64; ++l)
+      for (int h = 0; h < 2; ++h)
+        for (int t = 0; t < nb; ++t) {
+          const int jt = ORC_VBLK * b + t, ch = 64 * h + l;
+          if (!((mk[16 * jt + (ch >> 3)] >> (ch & 7)) & 1)) continue;
+          const int bit = nb * (2 * l + h) + t;
+          bm[bit >> 3] |= (uint8_t)(1u << (bit & 7));
+          memcpy(bv + 2 * r, &X[(size_t)tok[jt] * ORC_D + ch], 2);
+          ++r;
+        }
+  }
+  free(mk);
+  free(tok);
+}
+
+/* Dense V rows [T][128] (bf16 bits, 0 where dropped) of a segment's V part:
+ * vmask = the V mask part (masked segments), vval = the V value part. */
+static void orc_v_dense(const uint8_t* vmask, const uint8_t* vval, int T, int c, uint16_t* out) {
+  memset(out, 0, sizeof(uint16_t) * (size_t)T * ORC_D);
+  if (c >= ORC_D) {
+    memcpy(out, vval, sizeof(uint16_t) * (size_t)T * ORC_D);
+    return;
+  }
+  for (int b = 0; ORC_VBLK * b < T; ++b) {
+    const int nb = T - ORC_VBLK * b < ORC_VBLK ? T - ORC_VBLK * b : ORC_VBLK;
+    const uint8_t* bm = vmask + (size_t)16 * ORC_VBLK * b;
+    const uint8_t* bv = vval + (size_t)2 * c * ORC_VBLK * b;
+    int r = 0;
+    for (int l = 0; l < 64; ++l)
+      for (int h = 0; h < 2; ++h)
+        for (int t = 0; t < nb; ++t) {
+          const int bit = nb * (2 * l + h) + t;
+          if (!((bm[bit >> 3] >> (bit & 7)) & 1)) continue;
+          memcpy(&out[(size_t)(ORC_VBLK * b + t) * ORC_D + 64 * h + l], bv + 2 * r, 2);
+          ++r;
+        }
+  }
 }
 
 /* Descriptor, 16 bytes, same field order as the library's. */
@@ -751,6 +824,11 @@ int orc_compress_stream(const orc_params* p, const uint16_t* K, const uint16_t* 
       size_t pos = 0;
       for (int part = 0; part < 2; ++part) { /* 0: K, 1: V */
         const uint16_t* X = part == 0 ? KS : VS;
+        if (part == 1 && c < ORC_D) {
+          orc_pack_v_blocks(X + (size_t)(t0 - rb) * ORC_D, keep, S, T, c, out + pos);
+          pos += (size_t)16 * T + (size_t)2 * T * c;
+          continue;
+        }
         if (c < ORC_D) {
           for (int t = 0; t < S; ++t) {
             if (!keep[t]) continue;
@@ -813,6 +891,11 @@ int orc_compress_stream(const orc_params* p, const uint16_t* K, const uint16_t* 
  * paged descriptor (flags bit2), whose first n_tok of seg_tokens rows are
  * filled so that tokens can be appended in place. */
 static int layout_tokens(const orc_desc* d) { return (d->flags & 4) ? d->seg_tokens : d->n_tok; }
+static int max_tok(const orc_desc* d, int n) {
+  int m = 0;
+  for (int i = 0; i < n; ++i) m = d[i].n_tok > m ? d[i].n_tok : m;
+  return m;
+}
 
 static void decode_core(int G, const double* qd, const uint8_t* packed, const orc_desc* desc,
                         int n_desc, float scale, double* out, double* lse);
@@ -874,50 +957,50 @@ void orc_decode_stream_rot(int G, const uint16_t* q, const uint8_t* packed, cons
     }
   }
   double* o1 = (double*)calloc((size_t)G * ORC_D + 1, sizeof(double));
+  uint16_t* vd = (uint16_t*)malloc(sizeof(uint16_t) * ORC_D * (size_t)(max_tok(desc, n_desc) + 1));
+  double* mx = (double*)malloc(sizeof(double) * (size_t)G);
+  double* den = (double*)malloc(sizeof(double) * (size_t)G);
   for (int g = 0; g < G; ++g) {
-    double mx = -INFINITY;
-    for (long t = 0; t < ntok; ++t) mx = l[t * G + g] > mx ? l[t * G + g] : mx;
     for (int i = 0; i < ORC_D; ++i) out[g * ORC_D + i] = 0.0;
+    mx[g] = -INFINITY;
+    den[g] = 0.0;
     if (ntok == 0) {
       lse[g] = -INFINITY;
       continue;
     }
-    double den = 0.0;
-    for (long t = 0; t < ntok; ++t) den += exp(l[t * G + g] - mx);
-    lse[g] = mx + log(den);
-    /* per span: the weighted sum of its stored V vectors, then R_V times it */
-    j = 0;
-    for (int sp = 0; sp < n_span; ++sp) {
-      for (int k = 0; k < ORC_D; ++k) o1[k] = 0.0;
-      const int i1 = (sp + 1) * desc_per_span < n_desc ? (sp + 1) * desc_per_span : n_desc;
-      for (int i = sp * desc_per_span; i < i1; ++i) {
-        const int T = desc[i].n_tok, c = desc[i].n_ch, TL = layout_tokens(&desc[i]);
-        const uint8_t* base = packed + desc[i].offset;
-        const size_t mb = c < ORC_D ? (size_t)16 * TL : 0;
-        const uint8_t* vmask = base + mb + (size_t)2 * TL * c;
-        const uint8_t* vval = vmask + mb;
-        for (int t = 0; t < T; ++t, ++j) {
-          const double pw = exp(l[(size_t)j * G + g] - mx) / den;
-          const uint8_t* mk = c < ORC_D ? vmask + 16 * t : NULL;
-          const uint8_t* vals = vval + (size_t)2 * c * t;
-          int r = 0;
-          for (int ch = 0; ch < ORC_D; ++ch) {
-            if (mk && !((mk[ch >> 3] >> (ch & 7)) & 1)) continue;
-            uint16_t u;
-            memcpy(&u, vals + 2 * r, 2);
-            ++r;
-            o1[ch] += pw * (double)bf2f(u);
-          }
+    for (long t = 0; t < ntok; ++t) mx[g] = l[t * G + g] > mx[g] ? l[t * G + g] : mx[g];
+    for (long t = 0; t < ntok; ++t) den[g] += exp(l[t * G + g] - mx[g]);
+    lse[g] = mx[g] + log(den[g]);
+  }
+  /* per span: the weighted sum of its stored V vectors, then R_V times it */
+  j = 0;
+  for (int sp = 0; ntok > 0 && sp < n_span; ++sp) {
+    for (int k = 0; k < G * ORC_D; ++k) o1[k] = 0.0;
+    const int i1 = (sp + 1) * desc_per_span < n_desc ? (sp + 1) * desc_per_span : n_desc;
+    for (int i = sp * desc_per_span; i < i1; ++i) {
+      const int T = desc[i].n_tok, c = desc[i].n_ch, TL = layout_tokens(&desc[i]);
+      const uint8_t* base = packed + desc[i].offset;
+      const size_t mb = c < ORC_D ? (size_t)16 * TL : 0;
+      const uint8_t* vmask = base + mb + (size_t)2 * TL * c;
+      orc_v_dense(vmask, vmask + mb, T, c, vd);
+      for (int t = 0; t < T; ++t, ++j)
+        for (int g = 0; g < G; ++g) {
+          const double pw = exp(l[(size_t)j * G + g] - mx[g]) / den[g];
+          for (int ch = 0; ch < ORC_D; ++ch)
+            o1[g * ORC_D + ch] += pw * (double)bf2f(vd[(size_t)t * ORC_D + ch]);
         }
-      }
-      const float* RV = rot + ((size_t)sp * 2 + 1) * ORC_D * ORC_D;
+    }
+    const float* RV = rot + ((size_t)sp * 2 + 1) * ORC_D * ORC_D;
+    for (int g = 0; g < G; ++g)
       for (int i = 0; i < ORC_D; ++i) {
         double acc = 0.0;
-        for (int k = 0; k < ORC_D; ++k) acc += (double)RV[i * ORC_D + k] * o1[k];
+        for (int k = 0; k < ORC_D; ++k) acc += (double)RV[i * ORC_D + k] * o1[g * ORC_D + k];
         out[g * ORC_D + i] += acc;
       }
-    }
   }
+  free(den);
+  free(mx);
+  free(vd);
   free(o1);
   free(l);
   free(qd);
@@ -928,6 +1011,7 @@ static void decode_core(int G, const double* qd, const uint8_t* packed, const or
   long ntok = 0;
   for (int i = 0; i < n_desc; ++i) ntok += desc[i].n_tok;
   double* l = (double*)malloc(sizeof(double) * (size_t)(ntok > 0 ? ntok : 1) * (size_t)G);
+  uint16_t* vd = (uint16_t*)malloc(sizeof(uint16_t) * ORC_D * (size_t)(max_tok(desc, n_desc) + 1));
   /* pass 1: logits */
   long j = 0;
   for (int i = 0; i < n_desc; ++i) {
@@ -953,42 +1037,40 @@ static void decode_core(int G, const double* qd, const uint8_t* packed, const or
       }
     }
   }
+  double* mx = (double*)malloc(sizeof(double) * (size_t)G);
+  double* den = (double*)malloc(sizeof(double) * (size_t)G);
   for (int g = 0; g < G; ++g) {
     for (int ch = 0; ch < ORC_D; ++ch) out[g * ORC_D + ch] = 0.0;
+    mx[g] = -INFINITY;
+    den[g] = 0.0;
     if (ntok == 0) {
       lse[g] = -INFINITY;
       continue;
     }
-    double mx = -INFINITY;
     for (long t = 0; t < ntok; ++t)
-      if (l[t * G + g] > mx) mx = l[t * G + g];
-    double den = 0.0;
-    for (long t = 0; t < ntok; ++t) den += exp(l[t * G + g] - mx);
-    lse[g] = mx + log(den);
-    /* pass 2: weighted sum of the kept V elements */
-    long jj = 0;
-    for (int i = 0; i < n_desc; ++i) {
-      const int T = desc[i].n_tok, c = desc[i].n_ch, TL = layout_tokens(&desc[i]);
-      const uint8_t* base = packed + desc[i].offset;
-      const size_t kpart = (size_t)(c < ORC_D ? 16 * TL : 0) + (size_t)2 * TL * c;
-      const uint8_t* vmask = base + kpart;
-      const uint8_t* vval = vmask + (c < ORC_D ? 16 * TL : 0);
-      for (int t = 0; t < T; ++t, ++jj) {
-        const double pr = exp(l[jj * G + g] - mx) / den;
-        const uint8_t* mk = c < ORC_D ? vmask + 16 * t : NULL;
-        const uint8_t* vals = vval + (size_t)2 * c * t;
-        int r = 0;
-        for (int ch = 0; ch < ORC_D; ++ch) {
-          int on = mk ? ((mk[ch >> 3] >> (ch & 7)) & 1) : 1;
-          if (!on) continue;
-          uint16_t vv;
-          memcpy(&vv, vals + 2 * r, 2);
-          ++r;
-          out[g * ORC_D + ch] += pr * (double)bf2f(vv);
-        }
-      }
-    }
+      if (l[t * G + g] > mx[g]) mx[g] = l[t * G + g];
+    for (long t = 0; t < ntok; ++t) den[g] += exp(l[t * G + g] - mx[g]);
+    lse[g] = mx[g] + log(den[g]);
   }
+  /* pass 2: weighted sum of the kept V elements, token by token (a dropped
+   * element is a stored zero, which adds nothing) */
+  long jj = 0;
+  for (int i = 0; i < n_desc; ++i) {
+    const int T = desc[i].n_tok, c = desc[i].n_ch, TL = layout_tokens(&desc[i]);
+    const uint8_t* base = packed + desc[i].offset;
+    const size_t kpart = (size_t)(c < ORC_D ? 16 * TL : 0) + (size_t)2 * TL * c;
+    const uint8_t* vmask = base + kpart;
+    orc_v_dense(vmask, vmask + (c < ORC_D ? 16 * TL : 0), T, c, vd);
+    for (int t = 0; t < T; ++t, ++jj)
+      for (int g = 0; g < G; ++g) {
+        const double pr = exp(l[jj * G + g] - mx[g]) / den[g];
+        for (int ch = 0; ch < ORC_D; ++ch)
+          out[g * ORC_D + ch] += pr * (double)bf2f(vd[(size_t)t * ORC_D + ch]);
+      }
+  }
+  free(den);
+  free(mx);
+  free(vd);
   free(l);
 }
 

@@ -257,10 +257,34 @@ def unpack_segment(buf, d, S):
             out[t, m[t]] = v[t]
         return out
 
+    def v_blocks():
+        # V of a masked segment: blocks of 8 tokens, each transposed: bit
+        # nb*(2l + h) + t of the block's mask bytes is (token t, channel
+        # 64h + l); its values follow in (l, h, t) order
+        nonlocal pos
+        mpos, vpos = pos, pos + 16 * T
+        m = np.zeros((T, 128), bool)
+        out = np.zeros((T, 128), np.uint16)
+        for b in range(0, T, 8):
+            nb = min(8, T - b)
+            bits = np.unpackbits(buf[mpos + 16 * b:mpos + 16 * (b + nb)], bitorder="little")
+            lht = bits.reshape(64, 2, nb).astype(bool)  # [l][h][t]
+            cnt = int(lht.sum())
+            v = buf[vpos + 2 * c * b:vpos + 2 * c * b + 2 * cnt].view(np.uint16)
+            ll, hh, tt = np.nonzero(lht)  # (l, h, t) order
+            ch = 64 * hh + ll
+            m[b + tt, ch] = True
+            out[b + tt, ch] = v
+        pos += 16 * T + 2 * T * c
+        return m, out
+
     mk = masks()
     Kd = vals(mk)
-    mv = masks()
-    Vd = vals(mv)
+    if c < 128:
+        mv, Vd = v_blocks()
+    else:
+        mv = masks()
+        Vd = vals(mv)
     if T < S:
         idx = buf[pos:pos + 2 * T].view(np.uint16).astype(np.int64)
         pad_end = off + int(O_seg_bytes(T, c, S))
@@ -306,6 +330,40 @@ def test_pack_round_trip(O):
         assert np.array_equal(Vd, np.where(mv, V[rows], 0))
         off += O.seg_bytes(T, c, S)
     assert r["used"] == off
+
+
+def test_pack_v_blocks_partial_and_bit_positions(O):
+    """Masked V parts are stored in transposed 8-token blocks (the last one
+    partial when T is not a multiple of 8): every kept element round-trips
+    through the independent unpacker, and one hand-placed element sits at the
+    bit and value position the layout names."""
+    K, V, Qw = _small_stream(21, N=256)
+    S = 64
+    strat = [(13, 40), (20, 64), (5, 8), (64, 120)]
+    r = O.compress_stream(K, V, Qw, S=S, strategies=strat, budget_bytes=4 * S * 128,
+                          scale=SCALE, forced=np.array([0, 1, 2, 3], np.uint8))
+    buf = r["packed"]
+    for sg, d in enumerate(r["desc"]):
+        T, c = strat[sg]
+        assert (int(d["n_tok"]), int(d["n_ch"])) == (T, c)
+        idx, Kd, Vd, mk, mv = unpack_segment(buf, d, S)
+        rows = sg * S + idx
+        assert np.all(mv.sum(axis=1) == c)
+        assert np.array_equal(Vd, np.where(mv, V[rows], 0))
+    # segment 0 (T 13, c 40): block 1 holds tokens 8..12 (nb 5); its first
+    # kept element in (l, h, t) order is the block's first value
+    d = r["desc"][0]
+    T, c = 13, 40
+    idx, _, _, _, mv = unpack_segment(buf, d, S)
+    vmask = int(d["offset"]) + 16 * T + 2 * T * c
+    vval = vmask + 16 * T
+    nb = 5
+    lht = [(l, h, t) for l in range(64) for h in range(2) for t in range(nb) if mv[8 + t, 64 * h + l]]
+    l, h, t = lht[0]
+    bit = nb * (2 * l + h) + t
+    assert (buf[vmask + 128 + bit // 8] >> (bit % 8)) & 1
+    first = buf[vval + 2 * c * 8:vval + 2 * c * 8 + 2].view(np.uint16)[0]
+    assert first == V[idx[8 + t], 64 * h + l]
 
 
 def test_keep_all_pack_is_the_dense_cache(O):

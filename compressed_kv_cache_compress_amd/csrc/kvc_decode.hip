@@ -317,6 +317,7 @@ struct Chunk {
   const uint8_t* vmask;
   const uint8_t* vval;
   int nt, c, nm, n16;
+  uint32_t delta;  // kval - kmask = vval - vmask
   uint32_t magic;  // ceil(2^20 / (c/8)): value slot -> row by multiply-shift
   bool valid;
 };
@@ -328,18 +329,21 @@ struct Regs {
 
 template <int I>
 __device__ __forceinline__ void prefetch_slot(const Chunk& ch, int lane, Regs& r) {
-  const int j = lane + 64 * I;
-  if (j < ch.n16) {
-    // the packed buffer is device (global) memory; an unsigned 32-bit
-    // offset on a scalar base is the load's native addressing form
+  // Lanes past the chunk load its last slot again, so no branch surrounds
+  // the loads (a branch there makes the compiler wait for every load in
+  // flight before the next one); commit skips those lanes.  The packed
+  // buffer is device (global) memory: each load takes a scalar base and an
+  // unsigned 32-bit lane offset, its native addressing form; in slot 0 the
+  // value slots sit delta bytes past the masks.
+  const int j = min(lane + 64 * I, ch.n16 - 1);
+  if (I == 0) {
+    const uint32_t off = 16u * (uint32_t)j + (j < ch.nm ? 0u : ch.delta);
+    r.k[I] = *(glb_u32x4_t*)(ch.kmask + off);
+    r.v[I] = *(glb_u32x4_t*)(ch.vmask + off);
+  } else {
     const uint32_t off = 16u * (uint32_t)j;
-    if (I == 0 && j < ch.nm) {
-      r.k[I] = *(glb_u32x4_t*)(ch.kmask + off);
-      r.v[I] = *(glb_u32x4_t*)(ch.vmask + off);
-    } else {
-      r.k[I] = *(glb_u32x4_t*)(ch.kval + off);
-      r.v[I] = *(glb_u32x4_t*)(ch.vval + off);
-    }
+    r.k[I] = *(glb_u32x4_t*)(ch.kval + off);
+    r.v[I] = *(glb_u32x4_t*)(ch.vval + off);
   }
 }
 
@@ -516,6 +520,7 @@ __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
   ch.vmask = uniform_ptr(cu.vmask + 16 * t0);
   ch.kval = uniform_ptr(cu.kval + 2 * c * t0 - 16 * nm);
   ch.vval = uniform_ptr(cu.vval + 2 * c * t0 - 16 * nm);
+  ch.delta = __builtin_amdgcn_readfirstlane((uint32_t)(ch.kval - ch.kmask));
   ch.nt = __builtin_amdgcn_readfirstlane(nt);
   ch.c = __builtin_amdgcn_readfirstlane(c);
   ch.nm = __builtin_amdgcn_readfirstlane(nm);
@@ -549,7 +554,9 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   __syncthreads();
 
   const int lane = tid & 63, wv = tid >> 6;
-  const int item = blockIdx.x * WAVES + wv;
+  // wave-uniform (the compiler cannot tell that tid >> 6 is), so the
+  // descriptor walk and the chunk addresses live in scalar registers
+  const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * WAVES + wv);
   if (item >= a.items) return;
   const int s = item / a.splits, sp = item - s * a.splits;
   const int grp = lane >> 4, col = lane & 15;
@@ -761,10 +768,10 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
     int vb = 0;
     // iteration: stage chunk i+1, load chunk i+2, K side of i+1, V side of i
     while (nxt.valid) {
-        commit(nxt, lane, rg, L.k, L.vs[vb ^ 1].v);
+      commit(nxt, lane, rg, L.k, L.vs[vb ^ 1].v);
       const Chunk far = next_chunk(cu, lane);
       prefetch(far, lane, rg);
-        const bool resc = k_side(nxt, vb ^ 1, alpha);
+      const bool resc = k_side(nxt, vb ^ 1, alpha);
       v_side(cur, vb);
       if (resc) rescale(alpha);
       cur = nxt;

@@ -49,6 +49,7 @@ typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) const uint32_t lds_u32_t;
+typedef __attribute__((address_space(3))) const uint16_t lds_u16_t;
 typedef __attribute__((address_space(1))) const u32x4_t glb_u32x4_t;
 
 // LDS byte offset of a pointer into shared memory, and back.
@@ -263,14 +264,23 @@ __device__ __forceinline__ void vexpand_issue(const uint8_t* st, int lane, int n
 #pragma unroll
   for (int bk = 0; bk < 2; ++bk) {
     const int nb = min(max(nt - VB * bk, 0), VB);  // wave-uniform
-    uint32_t x = 0u;
-    if (nb > 0) {
-      const uint32_t bit = 2u * (uint32_t)nb * (uint32_t)lane;
-      const lds_u32_t* m = lds_ptr(base + 128u * bk + 4u * (bit >> 5));
-      x = __builtin_amdgcn_alignbit(m[1], m[0], bit & 31u);
+    if (nb == VB) {
+      // a whole block: the lane's two channel masks are byte 0 and 1 of
+      // halfword l
+      const uint32_t x = *reinterpret_cast<const lds_u16_t*>(
+          (uintptr_t)(base + 128u * bk + 2u * (uint32_t)lane));
+      chm[bk][0] = x & 0xFFu;
+      chm[bk][1] = x >> 8;
+    } else {
+      uint32_t x = 0u;
+      if (nb > 0) {
+        const uint32_t bit = 2u * (uint32_t)nb * (uint32_t)lane;
+        const lds_u32_t* m = lds_ptr(base + 128u * bk + 4u * (bit >> 5));
+        x = __builtin_amdgcn_alignbit(m[1], m[0], bit & 31u);
+      }
+      chm[bk][0] = __builtin_amdgcn_ubfe(x, 0u, (uint32_t)nb);
+      chm[bk][1] = __builtin_amdgcn_ubfe(x, (uint32_t)nb, (uint32_t)nb);
     }
-    chm[bk][0] = __builtin_amdgcn_ubfe(x, 0u, (uint32_t)nb);
-    chm[bk][1] = __builtin_amdgcn_ubfe(x, (uint32_t)nb, (uint32_t)nb);
   }
   const uint32_t p00 = __popc(chm[0][0]), p10 = __popc(chm[1][0]);
   const uint32_t cnt = (p00 + __popc(chm[0][1])) | ((p10 + __popc(chm[1][1])) << 16);

@@ -880,111 +880,182 @@ __global__ __launch_bounds__(RG * RC) void k_decode_reduce(const float* __restri
   if (lse && blockIdx.y == 0 && c == 0) lse[r] = any ? l2 * 0.69314718055994530942f : -INFINITY;
 }
 
-// Rotated cache: per span, the merge of the span's splits (every split
-// weighted against the maximum M over all splits of its row) over all 128
-// channels, rotated back by the span's R_V and added up; out = sum / L,
-// with L the merged denominator, then the single bf16 rounding.  grid
-// (streams), 128 threads: thread c owns output channel c of the G rows (q
-// heads) of the stream, so each span's R_V is read once for all of them.
-// Split sp belongs to span sp / spl (spl = splits when there is one span).
+// Rotated cache, first pass: per (stream, span), the span's share of the
+// merged rotated output of every q head of the group, rotated back by the
+// span's R_V:  y[g][c] = sum_k R_V[c][k] o1[g][k] with o1[g][k] = sum over
+// the span's splits of acc[sp][k] exp2(m_sp - M_g), M_g the maximum over all
+// splits of the row.  grid (streams, n_span, 4), 128 threads: workgroup z
+// produces channels 32 z .. 32 z + 31 (a stream with one span still gets 4
+// workgroups); thread t first merges channel t of o1, then four threads
+// share an output channel (t >> 2), each summing 32 of its k, added within
+// the quad.  The 32 rows of R_V are staged in LDS by coalesced rows (padded
+// to 132 floats).  Split sp belongs to span sp / spl.
 constexpr int RMAXG = 16;
-__global__ __launch_bounds__(128) void k_decode_reduce_rot(const float* __restrict__ part_ml,
-                                                           const float* __restrict__ part_acc,
-                                                           const float* __restrict__ rot,
-                                                           uint16_t* __restrict__ out,
-                                                           float* __restrict__ lse, int splits,
-                                                           int spl, int n_span, int hq, int hkv) {
-  __shared__ float o1[RMAXG][D];
-  __shared__ float red[D];
-  __shared__ float Mg[RMAXG], Lg[RMAXG];
-  const int s = blockIdx.x, c = threadIdx.x;
+constexpr int RV_ROWS = 32;
+constexpr int RV_STRIDE = D + 4;
+__global__ __launch_bounds__(128) void k_decode_span_rot(const float* __restrict__ part_ml,
+                                                         const float* __restrict__ part_acc,
+                                                         const float* __restrict__ rot,
+                                                         float* __restrict__ span_out, int splits,
+                                                         int spl, int hq, int hkv) {
+  __shared__ float rv[RV_ROWS * RV_STRIDE];
+  __shared__ float o1[RMAXG * D], red[RMAXG];
+  const int s = blockIdx.x, span = blockIdx.y, n_span = gridDim.y, t = threadIdx.x;
+  const int c0 = RV_ROWS * blockIdx.z;
   const int G = hq / hkv;
   const int b = s / hkv, h = s - b * hkv;
   const int row0 = b * hq + h * G;
-  // M and L of every row (thread c folds splits c, c + 128, ...)
-  for (int g = 0; g < G; ++g) {
-    const float* ml = part_ml + (uint64_t)(row0 + g) * splits * 2;
-    float m = -INFINITY;
-    for (int sp = c; sp < splits; sp += D) m = fmaxf(m, ml[2 * sp]);
-    red[c] = m;
-    __syncthreads();
-    for (int w = D / 2; w >= 1; w >>= 1) {
-      if (c < w) red[c] = fmaxf(red[c], red[c + w]);
-      __syncthreads();
-    }
-    const float M = red[0];
-    __syncthreads();
-    float l = 0.0f;
-    if (M != -INFINITY)
-      for (int sp = c; sp < splits; sp += D) l += ml[2 * sp + 1] * exp2f(ml[2 * sp] - M);
-    red[c] = l;
-    __syncthreads();
-    for (int w = D / 2; w >= 1; w >>= 1) {
-      if (c < w) red[c] += red[c + w];
-      __syncthreads();
-    }
-    if (c == 0) {
-      Mg[g] = M;
-      Lg[g] = red[0];
-    }
-    __syncthreads();
-  }
-  float v[RMAXG];
+  const float4* RV4 = reinterpret_cast<const float4*>(
+      rot + (((uint64_t)s * n_span + span) * 2 + 1) * D * D + (uint64_t)c0 * D);
+  // the R_V rows' loads go out first and land in LDS after the maxima, so
+  // that their latency overlaps the split loads
+  constexpr int NRV = RV_ROWS * D / 4 / D;
+  float4 rvr[NRV];
 #pragma unroll
-  for (int g = 0; g < RMAXG; ++g) v[g] = 0.0f;
-  for (int span = 0; span < n_span; ++span) {
-    for (int g = 0; g < G; ++g) {
+  for (int u = 0; u < NRV; ++u) rvr[u] = RV4[t + D * u];
+  // M_g of every head: 32 threads per head, four heads per pass
+  for (int g0 = 0; g0 < G; g0 += 4) {
+    const int g = g0 + (t >> 5);
+    float m = -INFINITY;
+    if (g < G) {
       const float* ml = part_ml + (uint64_t)(row0 + g) * splits * 2;
-      const float* acc = part_acc + (uint64_t)(row0 + g) * splits * D;
-      const float M = Mg[g];
-      float a = 0.0f;
+      for (int sp = t & 31; sp < splits; sp += 32) m = fmaxf(m, ml[2 * sp]);
+    }
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if ((t & 31) == 0 && g < G) red[g] = m;
+  }
+#pragma unroll
+  for (int u = 0; u < NRV; ++u) {
+    const int i = t + D * u;
+    *reinterpret_cast<float4*>(rv + (i >> 5) * RV_STRIDE + 4 * (i & 31)) = rvr[u];
+  }
+  __syncthreads();
+  for (int g = 0; g < G; ++g) {
+    const float M = red[g];
+    const float* ml = part_ml + (uint64_t)(row0 + g) * splits * 2;
+    const float* acc = part_acc + (uint64_t)(row0 + g) * splits * D;
+    float a = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll 8
       for (int sp = span * spl; sp < (span + 1) * spl; ++sp) {
         const float m_sp = ml[2 * sp];
-        if (m_sp != -INFINITY) a += acc[(uint64_t)sp * D + c] * exp2f(m_sp - M);
+        if (m_sp != -INFINITY) a += acc[(uint64_t)sp * D + t] * exp2f(m_sp - M);
       }
-      o1[g][c] = a;
     }
-    __syncthreads();
-    const float* RV = rot + (((uint64_t)s * n_span + span) * 2 + 1) * D * D + (uint64_t)c * D;
-    for (int k = 0; k < D; ++k) {
-      const float rv = RV[k];
+    o1[g * D + t] = a;
+  }
+  __syncthreads();
+  const int row = t >> 2, k0 = (D / 4) * (t & 3);
+  float y[RMAXG];
 #pragma unroll
-      for (int g = 0; g < RMAXG; ++g)
-        if (g < G) v[g] = __builtin_fmaf(rv, o1[g][k], v[g]);
-    }
-    __syncthreads();  // the next span rewrites o1
+  for (int g = 0; g < RMAXG; ++g) y[g] = 0.0f;
+  const float* r = rv + row * RV_STRIDE + k0;
+#pragma unroll 4
+  for (int j = 0; j < D / 4; ++j) {
+    const float rk = r[j];
+#pragma unroll
+    for (int g = 0; g < RMAXG; ++g)
+      if (g < G) y[g] = __builtin_fmaf(rk, o1[g * D + k0 + j], y[g]);
   }
 #pragma unroll
   for (int g = 0; g < RMAXG; ++g) {
     if (g < G) {
-      const int r = row0 + g;
-      const bool any = Mg[g] != -INFINITY;
-      out[(uint64_t)r * D + c] = any ? (uint16_t)f2bf(v[g] / Lg[g]) : (uint16_t)0;
-      if (lse && c == 0)
-        lse[r] = any ? (Mg[g] + log2f(Lg[g])) * 0.69314718055994530942f : -INFINITY;
+      float v = y[g] + __shfl_xor(y[g], 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      if ((t & 3) == 0) span_out[((uint64_t)(row0 + g) * n_span + span) * D + c0 + row] = v;
     }
   }
 }
 
-// Rotated queries for a rotated cache: q'[k] = fma chain over i of
-// q[i] R_K[i][k] in fp32 with the R_K of each span, stored as its bf16
-// rounding hi and the bf16 rounding of the remainder lo, [row][n_span][128].
-// grid (batch * hq, n_span), 128 threads: thread k.
+// Rotated cache, second pass: out = (sum over spans, in span order, of the
+// first pass's y) / L, with L the merged denominator, then the single bf16
+// rounding; lse from M and L.  grid (batch * hq), 128 threads.
+__global__ __launch_bounds__(128) void k_decode_rot_final(const float* __restrict__ part_ml,
+                                                          const float* __restrict__ span_out,
+                                                          uint16_t* __restrict__ out,
+                                                          float* __restrict__ lse, int splits,
+                                                          int n_span) {
+  __shared__ float red[D];
+  const int r = blockIdx.x, c = threadIdx.x;
+  const float* ml = part_ml + (uint64_t)r * splits * 2;
+  float m = -INFINITY;
+  for (int sp = c; sp < splits; sp += D) m = fmaxf(m, ml[2 * sp]);
+  red[c] = m;
+  __syncthreads();
+  for (int w = D / 2; w >= 1; w >>= 1) {
+    if (c < w) red[c] = fmaxf(red[c], red[c + w]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float l = 0.0f;
+  if (M != -INFINITY)
+    for (int sp = c; sp < splits; sp += D) l += ml[2 * sp + 1] * exp2f(ml[2 * sp] - M);
+  red[c] = l;
+  __syncthreads();
+  for (int w = D / 2; w >= 1; w >>= 1) {
+    if (c < w) red[c] += red[c + w];
+    __syncthreads();
+  }
+  const float L = red[0];
+  const bool any = M != -INFINITY;
+  float v = 0.0f;
+  for (int span = 0; span < n_span; ++span) v += span_out[((uint64_t)r * n_span + span) * D + c];
+  out[(uint64_t)r * D + c] = any ? (uint16_t)f2bf(v / L) : (uint16_t)0;
+  if (lse && c == 0) lse[r] = any ? (M + log2f(L)) * 0.69314718055994530942f : -INFINITY;
+}
+
+// Rotated queries for a rotated cache: q'[k] = sum over i of q[i] R_K[i][k]
+// in fp32 with the R_K of each span (four fma chains over quarters of i,
+// then added), stored as its bf16 rounding hi and the bf16 rounding of the
+// remainder lo, [row][n_span][128].  grid (streams, n_span), 128 threads:
+// thread t takes k = 4 (t & 31) .. +3 over the quarter t >> 5 of i, for every
+// q head of the group (R_K read once per stream and span, 16 bytes per lane).
 __global__ __launch_bounds__(128) void k_rotate_q(const uint16_t* __restrict__ q,
                                                   const float* __restrict__ rot,
                                                   uint16_t* __restrict__ qhi,
                                                   uint16_t* __restrict__ qlo, int hq, int hkv) {
-  const int r = blockIdx.x, span = blockIdx.y, n_span = gridDim.y, k = threadIdx.x;
-  const int b = r / hq, hd = r - b * hq;
-  const int s = b * hkv + hd / (hq / hkv);
-  const float* RK = rot + ((uint64_t)s * n_span + span) * 2 * D * D;
-  const uint16_t* qr = q + (uint64_t)r * D;
-  float acc = 0.0f;
-  for (int i = 0; i < D; ++i) acc = __builtin_fmaf(bf2f(qr[i]), RK[i * D + k], acc);
-  const uint32_t hi = f2bf(acc);
-  const uint64_t o = ((uint64_t)r * n_span + span) * D + k;
-  qhi[o] = (uint16_t)hi;
-  qlo[o] = (uint16_t)f2bf(acc - bf2f(hi));
+  __shared__ float qs[RMAXG][D];
+  __shared__ float part[4][RMAXG][D];
+  const int s = blockIdx.x, span = blockIdx.y, n_span = gridDim.y, t = threadIdx.x;
+  const int G = hq / hkv;
+  const int b = s / hkv, h = s - b * hkv;
+  const int row0 = b * hq + h * G;
+  for (int g = 0; g < G; ++g) qs[g][t] = bf2f(q[(uint64_t)(row0 + g) * D + t]);
+  __syncthreads();
+  const int kq = t & 31, iq = t >> 5;
+  const float4* RK4 =
+      reinterpret_cast<const float4*>(rot + ((uint64_t)s * n_span + span) * 2 * D * D) + kq;
+  float4 acc[RMAXG];
+#pragma unroll
+  for (int g = 0; g < RMAXG; ++g) acc[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int j = 0; j < D / 4; ++j) {
+    const int i = (D / 4) * iq + j;
+    const float4 r = RK4[i * (D / 4)];
+#pragma unroll
+    for (int g = 0; g < RMAXG; ++g) {
+      if (g < G) {
+        const float qi = qs[g][i];
+        acc[g].x = __builtin_fmaf(qi, r.x, acc[g].x);
+        acc[g].y = __builtin_fmaf(qi, r.y, acc[g].y);
+        acc[g].z = __builtin_fmaf(qi, r.z, acc[g].z);
+        acc[g].w = __builtin_fmaf(qi, r.w, acc[g].w);
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < RMAXG; ++g)
+    if (g < G) *reinterpret_cast<float4*>(&part[iq][g][4 * kq]) = acc[g];
+  __syncthreads();
+  for (int g = 0; g < G; ++g) {
+    const float v = (part[0][g][t] + part[1][g][t]) + (part[2][g][t] + part[3][g][t]);
+    const uint32_t hi = f2bf(v);
+    const uint64_t o = ((uint64_t)(row0 + g) * n_span + span) * D + t;
+    qhi[o] = (uint16_t)hi;
+    qlo[o] = (uint16_t)f2bf(v - bf2f(hi));
+  }
 }
 
 // Fixed decode scratch for kv_attend_decode_noalloc: the split partials of
@@ -1034,7 +1105,7 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
   a.sl2 = p.scale * KVC_LOG2E;
   const dim3 grid((a.items + WAVES - 1) / WAVES);
   if (p.rot) {
-    hipLaunchKernelGGL(k_rotate_q, dim3(p.batch * p.hq, p.n_span), dim3(128), 0, st, p.q, p.rot,
+    hipLaunchKernelGGL(k_rotate_q, dim3(p.streams, p.n_span), dim3(128), 0, st, p.q, p.rot,
                        p.qhi, p.qlo, p.hq, p.hkv);
     if (p.G <= 4)
       hipLaunchKernelGGL((k_decode_split<1, true>), grid, dim3(64 * WAVES), 0, st, a);
@@ -1042,8 +1113,10 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
       hipLaunchKernelGGL((k_decode_split<2, true>), grid, dim3(64 * WAVES), 0, st, a);
     else
       hipLaunchKernelGGL((k_decode_split<4, true>), grid, dim3(64 * WAVES), 0, st, a);
-    hipLaunchKernelGGL(k_decode_reduce_rot, dim3(p.streams), dim3(D), 0, st, p.part_ml,
-                       p.part_acc, p.rot, p.out, p.lse, p.splits, p.spl, p.n_span, p.hq, p.hkv);
+    hipLaunchKernelGGL(k_decode_span_rot, dim3(p.streams, p.n_span, D / RV_ROWS), dim3(D), 0, st,
+                       p.part_ml, p.part_acc, p.rot, p.span_out, p.splits, p.spl, p.hq, p.hkv);
+    hipLaunchKernelGGL(k_decode_rot_final, dim3(p.batch * p.hq), dim3(D), 0, st, p.part_ml,
+                       p.span_out, p.out, p.lse, p.splits, p.n_span);
     return hipGetLastError();
   }
   if (p.G <= 4)

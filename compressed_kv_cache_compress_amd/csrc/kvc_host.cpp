@@ -176,10 +176,21 @@ uint32_t choose_splits(const kvc_params* p, const Shape& sh, uint32_t maxd) {
   if (want > maxd) want = maxd;
   if (want < 1) want = 1;
   if (want > 1024) want = 1024;
-  // with rotation spans, every split stays inside one span
+  // with rotation spans, every split stays inside one span: per splits per
+  // span, chosen (up to 8, at most a span's descriptors) so that the waves
+  // fill whole rounds of the CU slots (rounds per unit of work,
+  // ceil(items * per / waves) / per, is smallest)
   if (sp.n_span > 1) {
-    uint32_t per = (want + sp.n_span - 1) / sp.n_span;
-    if (per > sp.span_desc) per = sp.span_desc;
+    const uint64_t items = (uint64_t)sh.streams * sp.n_span;
+    uint32_t per = 1;
+    double best = 1e30;
+    for (uint32_t c = 1; c <= 8 && c <= sp.span_desc; ++c) {
+      const double rounds = (double)((items * c + waves - 1) / waves) / (double)c;
+      if (rounds < best - 1e-9) {
+        best = rounds;
+        per = c;
+      }
+    }
     want = sp.n_span * per;
   }
   return want;
@@ -193,11 +204,12 @@ bool decode_layout(const kvc_params* p, const Shape& sh, uint32_t maxd, kvc_layo
   L->decode_splits = splits;
   const uint64_t rows = (uint64_t)sh.batch * sh.hq * splits;
   L->decode_ws_bytes = align_up(rows * 2 * 4, kAlign) + align_up(rows * KVC_HEAD_DIM * 4, kAlign);
-  // rotated cache: the rotated queries' two bf16 parts, per span
+  // rotated cache: the rotated queries' two bf16 parts and each span's
+  // rotated-back share of the output (fp32), per row and span
   if (p->rotate) {
     const uint64_t n_span = decode_spans(p, maxd ? maxd : 1).n_span;
-    L->decode_ws_bytes +=
-        2 * align_up((uint64_t)sh.batch * sh.hq * n_span * KVC_HEAD_DIM * 2, kAlign);
+    const uint64_t per = (uint64_t)sh.batch * sh.hq * n_span * KVC_HEAD_DIM;
+    L->decode_ws_bytes += 2 * align_up(per * 2, kAlign) + align_up(per * 4, kAlign);
   }
   return true;
 }
@@ -478,6 +490,7 @@ kvc_status decode_impl(const kvc_params* p, const uint16_t* q, const void* packe
   w += align_up(rows * KVC_HEAD_DIM * 4, kAlign);
   d.rot = rot;
   d.qhi = d.qlo = nullptr;
+  d.span_out = nullptr;
   d.n_span = 1;
   d.span_desc = 0;
   d.spl = d.splits;
@@ -488,10 +501,11 @@ kvc_status decode_impl(const kvc_params* p, const uint16_t* q, const void* packe
       d.span_desc = (int)sp.span_desc;
       d.spl = d.splits / d.n_span;
     }
-    const uint64_t qb =
-        align_up((uint64_t)sh.batch * sh.hq * sp.n_span * KVC_HEAD_DIM * 2, kAlign);
+    const uint64_t per = (uint64_t)sh.batch * sh.hq * sp.n_span * KVC_HEAD_DIM;
+    const uint64_t qb = align_up(per * 2, kAlign);
     d.qhi = reinterpret_cast<uint16_t*>(w);
     d.qlo = reinterpret_cast<uint16_t*>(w + qb);
+    d.span_out = reinterpret_cast<float*>(w + 2 * qb);
   }
   if (launch_decode(d, stream) != hipSuccess) return KVC_E_HIP;
   return KVC_OK;

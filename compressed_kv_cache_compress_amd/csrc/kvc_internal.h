@@ -78,11 +78,13 @@ struct DecodePlan {
   float* lse;
   float *part_ml, *part_acc;
   // rotated cache (null when not rotated): R_K, R_V per stream and span
-  // ([streams][n_span][2][128][128]) and the rotated queries' bf16 parts in
-  // the workspace ([batch * hq][n_span][128]); descriptor i of a stream is
-  // in span i / span_desc, and split sp covers descriptors of span sp / spl
+  // ([streams][n_span][2][128][128]) and, in the workspace, the rotated
+  // queries' bf16 parts ([batch * hq][n_span][128]) and each span's share of
+  // the output; descriptor i of a stream is in span i / span_desc, and split
+  // sp covers descriptors of span sp / spl
   const float* rot;
   uint16_t *qhi, *qlo;
+  float* span_out;  // [batch * hq][n_span][128]: each span's rotated-back share
   int n_span, span_desc, spl;
 };
 

@@ -1112,6 +1112,7 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs a) {
   // the per-lane counts) and written out in 16-byte pieces
   __shared__ uint4 s_row[16][D / 8 + 1];
   __shared__ uint32_t s_vm[4][32];  // one transposed V block's mask bits per wave
+  __shared__ __align__(16) uint16_t s_vv[4][8 * (D - 8)];  // and its values (c <= 120)
   const int rr = 4 * wv + (lane >> 4), q = lane & 15;
   for (int part = 0; part < 2; ++part) {
     const uint16_t* X = part ? a.V : a.K;
@@ -1146,13 +1147,19 @@ __global__ __launch_bounds__(256) void k_pack(PackArgs a) {
         }
         const uint32_t cnt = (uint32_t)__popc(field);
         uint32_t k = wave_incl_scan_u32(cnt) - cnt;
-        uint16_t* bv = reinterpret_cast<uint16_t*>(out + vo + (uint64_t)16 * c * bk);
+        // the block's values are gathered in LDS (the wave's own words,
+        // written and read in order by the same wave) and written out in
+        // 16-byte pieces: 2 c nb bytes, a multiple of 16
+        uint16_t* sv = s_vv[wv];
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-          if (t < nb && ((field >> t) & 1u)) bv[k++] = v0[t];
+          if (t < nb && ((field >> t) & 1u)) sv[k++] = v0[t];
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-          if (t < nb && ((field >> (nb + t)) & 1u)) bv[k++] = v1[t];
+          if (t < nb && ((field >> (nb + t)) & 1u)) sv[k++] = v1[t];
+        const int n16 = (2 * c * nb) / 16;
+        uint4* bv = reinterpret_cast<uint4*>(out + vo + (uint64_t)16 * c * bk);
+        for (int i = lane; i < n16; i += 64) bv[i] = reinterpret_cast<const uint4*>(sv)[i];
         // mask bits: 2 nb bits at bit 2 nb l, assembled in LDS (the wave's
         // own words, written and read in order by the same wave)
         if (lane < 32) s_vm[wv][lane] = 0u;

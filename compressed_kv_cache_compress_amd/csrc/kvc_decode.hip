@@ -429,18 +429,20 @@ __device__ __forceinline__ void fetch_descs(Cursor& cu, int lane) {
 }
 
 // Chunks of descriptor i of a stream's list (0 past nd): ceil(T / ct) with
-// ct = 12 to 16 tokens per chunk.  T / ct is a multiple of 1/ct >= 1/16 apart
+// ct = 8, 12 or 16 tokens per chunk.  T / ct is a multiple of 1/ct >= 1/16 apart
 // from the next integer, so adding 31/32 to the product with the approximate
 // reciprocal and truncating gives the exact ceiling.  (The count only
 // balances the splits; any count gives the same results.)
 __device__ __forceinline__ uint32_t desc_chunks(const kvc_seg_desc* dl, int i, int nd) {
-  if (i >= nd) return 0u;
-  const uint32_t tc = reinterpret_cast<const uint32_t*>(dl + i)[2];
+  // the load is unconditional (a clamped index), so that a wave's loads for
+  // several descriptors go out together
+  const uint32_t tc = reinterpret_cast<const uint32_t*>(dl + min(i, nd - 1))[2];
   const uint32_t T = tc & 0xFFFFu;
   const int c = (int)(tc >> 16) & ~7;
   const float ct = (float)chunk_tokens(c < 8 ? 8 : (c > D ? D : c));
-  return (uint32_t)((float)T * __builtin_amdgcn_rcpf(ct) + 0.96875f);
+  return i < nd ? (uint32_t)((float)T * __builtin_amdgcn_rcpf(ct) + 0.96875f) : 0u;
 }
+
 // Descriptor range [di, d1) of split sp of a stream with nd descriptors.
 // With more descriptors than splits and at most 256 of them, splits take
 // equal shares of chunks: descriptor i goes to split floor(E_i * splits / W),
@@ -450,28 +452,34 @@ __device__ __forceinline__ uint32_t desc_chunks(const kvc_seg_desc* dl, int i, i
 // sizes (a dense prompt page is 22 chunks, a Kara event segment 1) leave one
 // wave with most of a stream's work otherwise.  Over longer lists equal
 // descriptor counts balance well enough: at 1024 descriptors per stream the
-// scan cost more than it saved.
+// scan cost more than it saved.  The chunk counts of all (at most four)
+// batches of 64 descriptors are loaded at once and kept in registers.
 __device__ __forceinline__ void split_range(const kvc_seg_desc* dl, int nd, int splits, int sp,
                                             int lane, int& di, int& d1) {
   di = (int)(((int64_t)sp * nd) / splits);
   d1 = (int)(((int64_t)(sp + 1) * nd) / splits);
   if (nd <= splits || nd > 256) return;
-  uint32_t part = 0;
-  for (int i = lane; i < nd; i += 64) part += desc_chunks(dl, i, nd);
-  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_u32(part), 63);
+  uint32_t w[4], e[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = desc_chunks(dl, lane + 64 * k, nd);
+  uint32_t carry = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t x = wave_incl_scan_u32(w[k]);
+    e[k] = carry + x - w[k];  // chunks before descriptor lane + 64 k
+    carry += (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+  }
+  const uint32_t total = carry;
   if (total == 0) return;
   // split(i) < t  <=>  E_i * splits < t * W
   const uint32_t lo = (uint32_t)sp * total, hi = (uint32_t)(sp + 1) * total;
-  uint32_t carry = 0;
   int nlo = 0, nhi = 0;
-  for (int i0 = 0; i0 < nd; i0 += 64) {
-    const int i = i0 + lane;
-    const uint32_t w = desc_chunks(dl, i, nd);
-    const uint32_t x = wave_incl_scan_u32(w);
-    const uint32_t e = (carry + x - w) * (uint32_t)splits;
-    carry += (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
-    nlo += __popcll(__ballot(i < nd && e < lo));
-    nhi += __popcll(__ballot(i < nd && e < hi));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = lane + 64 * k;
+    const uint32_t ek = e[k] * (uint32_t)splits;
+    nlo += __popcll(__ballot(i < nd && ek < lo));
+    nhi += __popcll(__ballot(i < nd && ek < hi));
   }
   di = nlo;
   d1 = sp == splits - 1 ? nd : nhi;

@@ -213,8 +213,9 @@ __device__ __forceinline__ void expand_issue(const uint8_t* st, int col, int grp
     }
     e.sa[kk] = ba;
     e.sb[kk] = bb;
-    e.tl[kk] = lut[mb & 0xFu];
-    e.th[kk] = lut[mb >> 4];
+    // lut[2 n] is the selector entry of nibble n (16-byte entries)
+    e.tl[kk] = lut[2 * (mb & 0xFu)];
+    e.th[kk] = lut[2 * (mb >> 4)];
   }
 }
 
@@ -303,7 +304,7 @@ __device__ __forceinline__ void vexpand_issue(const uint8_t* st, int lane, int n
 #pragma unroll
         for (int i = 0; i < 3; ++i) e.w[sg][h][i] = w[i];
         e.sa[sg][h] = ba;
-        e.sel[sg][h] = lut[n ? m >> 4 : m & 0xFu];
+        e.sel[sg][h] = lut[2 * (n ? m >> 4 : m & 0xFu)];
       }
     }
   }
@@ -558,7 +559,10 @@ __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
 // groups run a second set of MFMAs.
 template <int JG, bool QLO>
 __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_decode_split(DecodeArgs a) {
-  __shared__ uint2 lut[16];
+  // selector table, one 16-byte entry per nibble (its first 8 bytes used):
+  // the entry of a high nibble is then at byte offset (mask byte & 0xF0)
+  __shared__ uint4 lut4[16];
+  const uint2* lut = reinterpret_cast<const uint2*>(lut4);
   __shared__ u32x4_t zrow[1];
   __shared__ WaveLds<JG> wl[WAVES];
   const int tid = threadIdx.x;
@@ -566,7 +570,7 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   if (tid < 16) {
     uint32_t lo[2];
     build_lut_entry((uint32_t)tid, lo);
-    lut[tid] = make_uint2(lo[0], lo[1]);
+    lut4[tid] = make_uint4(lo[0], lo[1], 0u, 0u);
     if (tid == 0) zrow[0] = u32x4_t{0u, 0u, 0u, 0u};
   }
   __syncthreads();

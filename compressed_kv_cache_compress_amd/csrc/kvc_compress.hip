@@ -98,7 +98,7 @@ __global__ __launch_bounds__(64) void k_q_convert(ScoreArgs a, Units un, float* 
   }
 }
 
-constexpr int QB = 4;  // window queries scored together (independent fma chains)
+constexpr int QB = 8;  // window queries scored together (independent fma chains)
 
 // Logits of NQ consecutive window queries (rows qr, qr + 128, ...) against
 // this lane's key: one fma chain per query over ascending channels, times

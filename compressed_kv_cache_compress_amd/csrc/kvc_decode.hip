@@ -902,16 +902,17 @@ __global__ __launch_bounds__(RG * RC) void k_decode_reduce(const float* __restri
 // share an output channel (t >> 2), each summing 32 of its k, added within
 // the quad.  The 32 rows of R_V are staged in LDS by coalesced rows (padded
 // to 132 floats).  Split sp belongs to span sp / spl.
-constexpr int RMAXG = 16;
 constexpr int RV_ROWS = 32;
 constexpr int RV_STRIDE = D + 4;
+// NG: the group size rounded up to 4, 8 or 16 (registers and LDS sized by it)
+template <int NG>
 __global__ __launch_bounds__(128) void k_decode_span_rot(const float* __restrict__ part_ml,
                                                          const float* __restrict__ part_acc,
                                                          const float* __restrict__ rot,
                                                          float* __restrict__ span_out, int splits,
                                                          int spl, int hq, int hkv) {
   __shared__ float rv[RV_ROWS * RV_STRIDE];
-  __shared__ float o1[RMAXG * D], red[RMAXG];
+  __shared__ float o1[NG * D], red[NG];
   const int s = blockIdx.x, span = blockIdx.y, n_span = gridDim.y, t = threadIdx.x;
   const int c0 = RV_ROWS * blockIdx.z;
   const int G = hq / hkv;
@@ -931,7 +932,15 @@ __global__ __launch_bounds__(128) void k_decode_span_rot(const float* __restrict
     float m = -INFINITY;
     if (g < G) {
       const float* ml = part_ml + (uint64_t)(row0 + g) * splits * 2;
-      for (int sp = t & 31; sp < splits; sp += 32) m = fmaxf(m, ml[2 * sp]);
+      // four loads in flight per pass (a clamped index repeats a split,
+      // which leaves the maximum unchanged)
+      for (int sp0 = t & 31; sp0 < splits; sp0 += 128) {
+        float mm[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mm[u] = ml[2 * min(sp0 + 32 * u, splits - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) m = fmaxf(m, mm[u]);
+      }
     }
 #pragma unroll
     for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
@@ -949,29 +958,38 @@ __global__ __launch_bounds__(128) void k_decode_span_rot(const float* __restrict
     const float* acc = part_acc + (uint64_t)(row0 + g) * splits * D;
     float a = 0.0f;
     if (M != -INFINITY) {
-#pragma unroll 8
-      for (int sp = span * spl; sp < (span + 1) * spl; ++sp) {
-        const float m_sp = ml[2 * sp];
-        if (m_sp != -INFINITY) a += acc[(uint64_t)sp * D + t] * exp2f(m_sp - M);
+      // eight splits' loads in flight per pass, clamped to the span
+      const int sp1 = (span + 1) * spl;
+      for (int sp0 = span * spl; sp0 < sp1; sp0 += 8) {
+        float mv[8], av[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int sp = min(sp0 + u, sp1 - 1);
+          mv[u] = ml[2 * sp];
+          av[u] = acc[(uint64_t)sp * D + t];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (sp0 + u < sp1 && mv[u] != -INFINITY) a += av[u] * exp2f(mv[u] - M);
       }
     }
     o1[g * D + t] = a;
   }
   __syncthreads();
   const int row = t >> 2, k0 = (D / 4) * (t & 3);
-  float y[RMAXG];
+  float y[NG];
 #pragma unroll
-  for (int g = 0; g < RMAXG; ++g) y[g] = 0.0f;
+  for (int g = 0; g < NG; ++g) y[g] = 0.0f;
   const float* r = rv + row * RV_STRIDE + k0;
 #pragma unroll 4
   for (int j = 0; j < D / 4; ++j) {
     const float rk = r[j];
 #pragma unroll
-    for (int g = 0; g < RMAXG; ++g)
+    for (int g = 0; g < NG; ++g)
       if (g < G) y[g] = __builtin_fmaf(rk, o1[g * D + k0 + j], y[g]);
   }
 #pragma unroll
-  for (int g = 0; g < RMAXG; ++g) {
+  for (int g = 0; g < NG; ++g) {
     if (g < G) {
       float v = y[g] + __shfl_xor(y[g], 1, 64);
       v += __shfl_xor(v, 2, 64);
@@ -1024,12 +1042,13 @@ __global__ __launch_bounds__(128) void k_decode_rot_final(const float* __restric
 // remainder lo, [row][n_span][128].  grid (streams, n_span), 128 threads:
 // thread t takes k = 4 (t & 31) .. +3 over the quarter t >> 5 of i, for every
 // q head of the group (R_K read once per stream and span, 16 bytes per lane).
+template <int NG>
 __global__ __launch_bounds__(128) void k_rotate_q(const uint16_t* __restrict__ q,
                                                   const float* __restrict__ rot,
                                                   uint16_t* __restrict__ qhi,
                                                   uint16_t* __restrict__ qlo, int hq, int hkv) {
-  __shared__ float qs[RMAXG][D];
-  __shared__ float part[4][RMAXG][D];
+  __shared__ float qs[NG][D];
+  __shared__ float part[4][NG][D];
   const int s = blockIdx.x, span = blockIdx.y, n_span = gridDim.y, t = threadIdx.x;
   const int G = hq / hkv;
   const int b = s / hkv, h = s - b * hkv;
@@ -1039,15 +1058,15 @@ __global__ __launch_bounds__(128) void k_rotate_q(const uint16_t* __restrict__ q
   const int kq = t & 31, iq = t >> 5;
   const float4* RK4 =
       reinterpret_cast<const float4*>(rot + ((uint64_t)s * n_span + span) * 2 * D * D) + kq;
-  float4 acc[RMAXG];
+  float4 acc[NG];
 #pragma unroll
-  for (int g = 0; g < RMAXG; ++g) acc[g] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
+  for (int g = 0; g < NG; ++g) acc[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 16
   for (int j = 0; j < D / 4; ++j) {
     const int i = (D / 4) * iq + j;
     const float4 r = RK4[i * (D / 4)];
 #pragma unroll
-    for (int g = 0; g < RMAXG; ++g) {
+    for (int g = 0; g < NG; ++g) {
       if (g < G) {
         const float qi = qs[g][i];
         acc[g].x = __builtin_fmaf(qi, r.x, acc[g].x);
@@ -1058,7 +1077,7 @@ __global__ __launch_bounds__(128) void k_rotate_q(const uint16_t* __restrict__ q
     }
   }
 #pragma unroll
-  for (int g = 0; g < RMAXG; ++g)
+  for (int g = 0; g < NG; ++g)
     if (g < G) *reinterpret_cast<float4*>(&part[iq][g][4 * kq]) = acc[g];
   __syncthreads();
   for (int g = 0; g < G; ++g) {
@@ -1117,16 +1136,29 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
   a.sl2 = p.scale * KVC_LOG2E;
   const dim3 grid((a.items + WAVES - 1) / WAVES);
   if (p.rot) {
-    hipLaunchKernelGGL(k_rotate_q, dim3(p.streams, p.n_span), dim3(128), 0, st, p.q, p.rot,
-                       p.qhi, p.qlo, p.hq, p.hkv);
+    const dim3 gq(p.streams, p.n_span);
+    if (p.G <= 4)
+      hipLaunchKernelGGL(k_rotate_q<4>, gq, dim3(128), 0, st, p.q, p.rot, p.qhi, p.qlo, p.hq, p.hkv);
+    else if (p.G <= 8)
+      hipLaunchKernelGGL(k_rotate_q<8>, gq, dim3(128), 0, st, p.q, p.rot, p.qhi, p.qlo, p.hq, p.hkv);
+    else
+      hipLaunchKernelGGL(k_rotate_q<16>, gq, dim3(128), 0, st, p.q, p.rot, p.qhi, p.qlo, p.hq, p.hkv);
     if (p.G <= 4)
       hipLaunchKernelGGL((k_decode_split<1, true>), grid, dim3(64 * WAVES), 0, st, a);
     else if (p.G <= 8)
       hipLaunchKernelGGL((k_decode_split<2, true>), grid, dim3(64 * WAVES), 0, st, a);
     else
       hipLaunchKernelGGL((k_decode_split<4, true>), grid, dim3(64 * WAVES), 0, st, a);
-    hipLaunchKernelGGL(k_decode_span_rot, dim3(p.streams, p.n_span, D / RV_ROWS), dim3(D), 0, st,
-                       p.part_ml, p.part_acc, p.rot, p.span_out, p.splits, p.spl, p.hq, p.hkv);
+    const dim3 gs(p.streams, p.n_span, D / RV_ROWS);
+    if (p.G <= 4)
+      hipLaunchKernelGGL(k_decode_span_rot<4>, gs, dim3(D), 0, st, p.part_ml, p.part_acc, p.rot,
+                         p.span_out, p.splits, p.spl, p.hq, p.hkv);
+    else if (p.G <= 8)
+      hipLaunchKernelGGL(k_decode_span_rot<8>, gs, dim3(D), 0, st, p.part_ml, p.part_acc, p.rot,
+                         p.span_out, p.splits, p.spl, p.hq, p.hkv);
+    else
+      hipLaunchKernelGGL(k_decode_span_rot<16>, gs, dim3(D), 0, st, p.part_ml, p.part_acc, p.rot,
+                         p.span_out, p.splits, p.spl, p.hq, p.hkv);
     hipLaunchKernelGGL(k_decode_rot_final, dim3(p.batch * p.hq), dim3(D), 0, st, p.part_ml,
                        p.span_out, p.out, p.lse, p.splits, p.n_span);
     return hipGetLastError();

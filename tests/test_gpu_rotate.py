@@ -120,3 +120,16 @@ def test_rotate_per_span_region_and_splits():
         _check(w, S=16, strategies=gen.table9(16), budget=gen.budget_bytes(33, 16),
                region_begin=512, region_len=256, label=f"spans of 64, splits {splits}",
                rot_span=64, decode_splits=splits)
+
+
+@pytest.mark.parametrize("Hq", [12, 16])
+def test_rotate_large_groups(Hq):
+    """Groups of 12 and 16 q heads per kv head, one R per stream and one per
+    64-token span: the rotation kernels' largest instantiation (and a group
+    that fills it only partly)."""
+    c = dict(gen.CONFIGS["tiny"])
+    c.update(Hq=Hq, Hkv=1, N=512, S=16, W=4)
+    w = gen.make_workload(c)
+    for span in (0, 64):
+        _check(w, S=16, strategies=gen.table9(16), budget=gen.budget_bytes(33, 16),
+               region_begin=128, region_len=256, label=f"G={Hq} span {span}", rot_span=span)

@@ -445,45 +445,56 @@ __device__ __forceinline__ uint32_t desc_chunks(const kvc_seg_desc* dl, int i, i
 }
 
 // Descriptor range [di, d1) of split sp of a stream with nd descriptors.
-// With more descriptors than splits and at most 256 of them, splits take
+// With more descriptors than splits and at most 1024 of them, splits take
 // equal shares of chunks: descriptor i goes to split floor(E_i * splits / W),
 // with E_i the chunks of the descriptors before i and W all chunks of the
 // stream.  That index never decreases with i, so every split takes a
-// contiguous run (possibly empty).  Few descriptors per split of different
-// sizes (a dense prompt page is 22 chunks, a Kara event segment 1) leave one
-// wave with most of a stream's work otherwise.  Over longer lists equal
-// descriptor counts balance well enough: at 1024 descriptors per stream the
-// scan cost more than it saved.  The chunk counts of all (at most four)
-// batches of 64 descriptors are loaded at once and kept in registers.
+// contiguous run (possibly empty).  Equal descriptor counts leave some waves
+// with far more chunks than others: a dense prompt page is 22 chunks and a
+// Kara event segment 1, and even over 1024 segments of 2 and 4 chunks the
+// busiest of 24 waves took 20 % more than the mean.  Lane l sums the chunks
+// of PER consecutive descriptors (loads issued together), one wave scan
+// gives its first E_i, and one wave sum of two packed 16-bit counts gives
+// di and d1.  Longer lists keep equal descriptor counts.
+template <int PER>
+__device__ __forceinline__ void chunk_balanced_range(const kvc_seg_desc* dl, int nd, int splits,
+                                                     int sp, int lane, int& di, int& d1) {
+  const int per = (nd + 63) >> 6;  // descriptors per lane, <= PER
+  uint32_t w[PER], tot = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const uint32_t x = desc_chunks(dl, lane * per + k, nd);
+    w[k] = k < per ? x : 0u;
+    tot += w[k];
+  }
+  const uint32_t inc = wave_incl_scan_u32(tot);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  if (total == 0) return;
+  // split(i) < t  <=>  E_i * splits < t * W
+  const uint64_t lo = (uint64_t)sp * total, hi = (uint64_t)(sp + 1) * total;
+  uint32_t e = inc - tot, cnt = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const bool ok = k < per && lane * per + k < nd;
+    const uint64_t ek = (uint64_t)e * (uint32_t)splits;
+    cnt += (ok && ek < lo ? 1u : 0u) + (ok && ek < hi ? 0x10000u : 0u);
+    e += w[k];
+  }
+  // nd <= 1024: neither 16-bit count carries
+  const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_u32(cnt), 63);
+  di = (int)(all & 0xFFFFu);
+  d1 = sp == splits - 1 ? nd : (int)(all >> 16);
+}
+
 __device__ __forceinline__ void split_range(const kvc_seg_desc* dl, int nd, int splits, int sp,
                                             int lane, int& di, int& d1) {
   di = (int)(((int64_t)sp * nd) / splits);
   d1 = (int)(((int64_t)(sp + 1) * nd) / splits);
-  if (nd <= splits || nd > 256) return;
-  uint32_t w[4], e[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) w[k] = desc_chunks(dl, lane + 64 * k, nd);
-  uint32_t carry = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t x = wave_incl_scan_u32(w[k]);
-    e[k] = carry + x - w[k];  // chunks before descriptor lane + 64 k
-    carry += (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
-  }
-  const uint32_t total = carry;
-  if (total == 0) return;
-  // split(i) < t  <=>  E_i * splits < t * W
-  const uint32_t lo = (uint32_t)sp * total, hi = (uint32_t)(sp + 1) * total;
-  int nlo = 0, nhi = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int i = lane + 64 * k;
-    const uint32_t ek = e[k] * (uint32_t)splits;
-    nlo += __popcll(__ballot(i < nd && ek < lo));
-    nhi += __popcll(__ballot(i < nd && ek < hi));
-  }
-  di = nlo;
-  d1 = sp == splits - 1 ? nd : nhi;
+  if (nd <= splits || nd > 1024) return;
+  if (nd <= 256)
+    chunk_balanced_range<4>(dl, nd, splits, sp, lane, di, d1);
+  else
+    chunk_balanced_range<16>(dl, nd, splits, sp, lane, di, d1);
 }
 
 __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {

@@ -410,6 +410,15 @@ struct Cursor {
 // ceil(2^20 / k): value slot v of a stage with k slots per row is in row
 // (v * magic) >> 20 for v < 16 * k.
 constexpr uint32_t row_magic(int k) { return (1048576u + (uint32_t)k - 1u) / (uint32_t)k; }
+// The fields of the packed chunk geometry hold every value they take: tokens
+// per chunk in 5 bits (a chunk of 0 tokens would never advance and would
+// address slot -1), the row magic in 21, log2(seg_tokens) + 1 <= 17 in 6.
+constexpr bool geo_fields_fit() {
+  for (int c = 8; c <= D; c += 8)
+    if (chunk_tokens(c) < 1 || chunk_tokens(c) > 31 || row_magic(c >> 3) > 0x1FFFFFu) return false;
+  return true;
+}
+static_assert(geo_fields_fit(), "chunk geometry fields");
 
 __device__ __forceinline__ void fetch_descs(Cursor& cu, int lane) {
   cu.base = cu.di;

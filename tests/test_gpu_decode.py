@@ -139,13 +139,15 @@ def test_decode_ragged_descriptor_lists_and_empty_streams():
 def test_decode_wide_rows_and_chunk_tails():
     """Masked rows up to 88 channels take 16 tokens per chunk (88 fills the
     prefetch slots exactly), wider masked rows 8 (one transposed V block) and
-    dense rows 12: every channel-count class (8, 56, 88, 96, 104, 112, 120,
-    dense) with token counts that leave ragged chunk tails and partial V
-    blocks, forced per segment, at several split counts."""
+    dense rows 12: every channel-count class (8, 16, 24, 32, 56, 88, 96, 104,
+    112, 120, dense) with token counts that leave ragged chunk tails and
+    partial V blocks (tails of 5, 14, 1 and 16 tokens among them), forced per
+    segment, at several split counts."""
     w = gen.make_workload("llama8b", B=1, N=2048)
     S = 128
     strategies = [(37, 8), (100, 56), (17, 96), (128, 104), (45, 112), (99, 120), (77, 128),
-                  (128, 128), (1, 120), (29, 104), (53, 88)]
+                  (128, 128), (1, 120), (29, 104), (53, 88), (21, 32), (30, 24), (16, 16),
+                  (49, 32)]
     streams = w["B"] * w["Hkv"]
     n_seg = w["N"] // S
     forced = np.array([[(s + 3 * j) % len(strategies) for j in range(n_seg)] for s in range(streams)],

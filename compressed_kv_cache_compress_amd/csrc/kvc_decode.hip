@@ -399,6 +399,9 @@ struct Cursor {
   const kvc_seg_desc* dl;
   const uint8_t* packed;
   int di, d1, base;         // next descriptor, end, first descriptor held in the lanes
+  // a split may start and end inside a segment: descriptor dfirst is walked
+  // from token tfirst, descriptor dlast up to token tlast (-1: none)
+  int dfirst, tfirst, dlast, tlast;
   uint32_t w0, w1, w2;      // this lane's descriptor (base + lane): offset lo/hi, n_tok|n_ch<<16
   uint32_t w3;              // its chunk geometry: tokens per chunk | row magic << 5 | page << 26
   // current segment
@@ -443,67 +446,87 @@ __device__ __forceinline__ void fetch_descs(Cursor& cu, int lane) {
 // from the next integer, so adding 31/32 to the product with the approximate
 // reciprocal and truncating gives the exact ceiling.  (The count only
 // balances the splits; any count gives the same results.)
-__device__ __forceinline__ uint32_t desc_chunks(const kvc_seg_desc* dl, int i, int nd) {
+__device__ __forceinline__ uint32_t desc_chunks(const kvc_seg_desc* dl, int i, int nd,
+                                                uint32_t& ct) {
   // the load is unconditional (a clamped index), so that a wave's loads for
   // several descriptors go out together
   const uint32_t tc = reinterpret_cast<const uint32_t*>(dl + min(i, nd - 1))[2];
   const uint32_t T = tc & 0xFFFFu;
   const int c = (int)(tc >> 16) & ~7;
-  const float ct = (float)chunk_tokens(c < 8 ? 8 : (c > D ? D : c));
-  return i < nd ? (uint32_t)((float)T * __builtin_amdgcn_rcpf(ct) + 0.96875f) : 0u;
+  ct = (uint32_t)chunk_tokens(c < 8 ? 8 : (c > D ? D : c));
+  return i < nd ? (uint32_t)((float)T * __builtin_amdgcn_rcpf((float)ct) + 0.96875f) : 0u;
 }
 
-// Descriptor range [di, d1) of split sp of a stream with nd descriptors.
-// With more descriptors than splits and at most 1024 of them, splits take
-// equal shares of chunks: descriptor i goes to split floor(E_i * splits / W),
-// with E_i the chunks of the descriptors before i and W all chunks of the
-// stream.  That index never decreases with i, so every split takes a
-// contiguous run (possibly empty).  Equal descriptor counts leave some waves
-// with far more chunks than others: a dense prompt page is 22 chunks and a
-// Kara event segment 1, and even over 1024 segments of 2 and 4 chunks the
-// busiest of 24 waves took 20 % more than the mean.  Lane l sums the chunks
-// of PER consecutive descriptors (loads issued together), one wave scan
-// gives its first E_i, and one wave sum of two packed 16-bit counts gives
-// di and d1.  Longer lists keep equal descriptor counts.
+// Chunk range of split sp of a stream with nd descriptors: with W the
+// stream's chunks, chunks floor(sp W / splits) .. floor((sp + 1) W / splits)
+// - 1 in walking order, so that every split of a stream takes the same
+// number of chunks to within one, starting and ending inside a segment
+// where the share falls there.  A segment is 2 to 22 chunks here; whole
+// segments per split left the busiest of 24 waves 20 % (1024 segments of 2
+// and 4 chunks) to 25 % (128 such segments) above the mean.  Lane l takes
+// descriptors PER l .. PER l + PER - 1 (their loads issued together), one
+// wave scan gives each lane the chunks before its first, and the lanes that
+// hold the first and the last chunk of the share are found by ballot.  Lists
+// of more than 1024 descriptors take equal descriptor counts.
 template <int PER>
-__device__ __forceinline__ void chunk_balanced_range(const kvc_seg_desc* dl, int nd, int splits,
-                                                     int sp, int lane, int& di, int& d1) {
+__device__ __forceinline__ void chunk_balanced_range(int nd, int splits, int sp, int lane,
+                                                     Cursor& cu) {
   const int per = (nd + 63) >> 6;  // descriptors per lane, <= PER
-  uint32_t w[PER], tot = 0;
+  uint32_t w[PER], ct[PER], tot = 0;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const uint32_t x = desc_chunks(dl, lane * per + k, nd);
+    const uint32_t x = desc_chunks(cu.dl, lane * per + k, nd, ct[k]);
     w[k] = k < per ? x : 0u;
     tot += w[k];
   }
   const uint32_t inc = wave_incl_scan_u32(tot);
   const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
-  if (total == 0) return;
-  // split(i) < t  <=>  E_i * splits < t * W
-  const uint64_t lo = (uint64_t)sp * total, hi = (uint64_t)(sp + 1) * total;
-  uint32_t e = inc - tot, cnt = 0;
+  const uint32_t c0 = (uint32_t)(((uint64_t)sp * total) / (uint32_t)splits);
+  const uint32_t c1 = (uint32_t)(((uint64_t)(sp + 1) * total) / (uint32_t)splits);
+  cu.di = cu.d1 = 0;
+  if (c0 >= c1) return;  // no chunks for this split
+  // the descriptors holding chunk c0 and chunk c1 - 1 (each non-empty, so
+  // one lane and slot each), and the tokens before / through them
+  uint32_t e = inc - tot;
+  int f0 = -1, f1 = -1;
+  uint32_t t0 = 0, t1 = 0;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const bool ok = k < per && lane * per + k < nd;
-    const uint64_t ek = (uint64_t)e * (uint32_t)splits;
-    cnt += (ok && ek < lo ? 1u : 0u) + (ok && ek < hi ? 0x10000u : 0u);
+    const int i = lane * per + k;
+    const bool in0 = w[k] > 0u && e <= c0 && c0 < e + w[k];
+    const bool in1 = w[k] > 0u && e < c1 && c1 <= e + w[k];
+    if (in0) {
+      f0 = i;
+      t0 = (c0 - e) * ct[k];
+    }
+    if (in1) {
+      f1 = i;
+      t1 = (c1 - e) * ct[k];
+    }
     e += w[k];
   }
-  // nd <= 1024: neither 16-bit count carries
-  const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_u32(cnt), 63);
-  di = (int)(all & 0xFFFFu);
-  d1 = sp == splits - 1 ? nd : (int)(all >> 16);
+  const uint64_t b0 = __ballot(f0 >= 0), b1 = __ballot(f1 >= 0);
+  if (b0 == 0u || b1 == 0u) return;
+  const int l0 = (int)__builtin_ctzll(b0), l1 = (int)__builtin_ctzll(b1);
+  cu.di = __builtin_amdgcn_readlane(f0, l0);
+  cu.tfirst = __builtin_amdgcn_readlane((int)t0, l0);
+  cu.dlast = __builtin_amdgcn_readlane(f1, l1);
+  cu.tlast = __builtin_amdgcn_readlane((int)t1, l1);
+  cu.dfirst = cu.di;
+  cu.d1 = cu.dlast + 1;
 }
 
-__device__ __forceinline__ void split_range(const kvc_seg_desc* dl, int nd, int splits, int sp,
-                                            int lane, int& di, int& d1) {
-  di = (int)(((int64_t)sp * nd) / splits);
-  d1 = (int)(((int64_t)(sp + 1) * nd) / splits);
-  if (nd <= splits || nd > 1024) return;
+// Descriptor range of split sp: chunk shares above for lists of up to 1024
+// descriptors, else an equal share of the descriptors.
+__device__ __forceinline__ void split_range(int nd, int splits, int sp, int lane, Cursor& cu) {
+  cu.dfirst = cu.dlast = -1;
+  cu.di = (int)(((int64_t)sp * nd) / splits);
+  cu.d1 = (int)(((int64_t)(sp + 1) * nd) / splits);
+  if (nd <= 0 || nd > 1024) return;
   if (nd <= 256)
-    chunk_balanced_range<4>(dl, nd, splits, sp, lane, di, d1);
+    chunk_balanced_range<4>(nd, splits, sp, lane, cu);
   else
-    chunk_balanced_range<16>(dl, nd, splits, sp, lane, di, d1);
+    chunk_balanced_range<16>(nd, splits, sp, lane, cu);
 }
 
 __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
@@ -525,8 +548,11 @@ __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
       const int sl = cu.di - cu.base;
       const uint32_t tc = __builtin_amdgcn_readlane(cu.w2, sl);
       const int T = (int)(tc & 0xFFFFu);
+      // tokens [tb, te) of this segment belong to the split
+      const int tb = cu.di == cu.dfirst ? cu.tfirst : 0;
+      const int te = cu.di == cu.dlast ? min(T, cu.tlast) : T;
       ++cu.di;
-      if (T > 0) {
+      if (te > tb) {
         const uint32_t lo = __builtin_amdgcn_readlane(cu.w0, sl);
         const uint32_t hi = __builtin_amdgcn_readlane(cu.w1, sl);
         const uint32_t geo = __builtin_amdgcn_readlane(cu.w3, sl);
@@ -541,9 +567,9 @@ __device__ __forceinline__ Chunk next_chunk(Cursor& cu, int lane) {
         cu.kval = base + mb;
         cu.vmask = base + mb + 2u * TL * c;
         cu.vval = base + 2 * mb + 2u * TL * c;
-        cu.T = T;
+        cu.T = te;
         cu.c = c;
-        cu.t0 = 0;
+        cu.t0 = tb;
         break;
       }
     }
@@ -661,8 +687,9 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
     const int sub = sp - span * a.spl;
     cu.di = s0 + (int)(((int64_t)sub * n) / a.spl);
     cu.d1 = s0 + (int)(((int64_t)(sub + 1) * n) / a.spl);
+    cu.dfirst = cu.dlast = -1;
   } else {
-    split_range(cu.dl, nd, a.splits, sp, lane, cu.di, cu.d1);
+    split_range(nd, a.splits, sp, lane, cu);
   }
   cu.T = 0;
   cu.c = 0;

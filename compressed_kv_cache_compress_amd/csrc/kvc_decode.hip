@@ -891,13 +891,40 @@ __device__ __forceinline__ bool merge_splits(const float* __restrict__ ml,
   __shared__ float gm[RG], gl[RG], gacc[RG][RC + 1];
   const int c = threadIdx.x % RC, g = threadIdx.x / RC;
   float M = -INFINITY;
-  for (int sp = g; sp < splits; sp += RG) M = fmaxf(M, ml[2 * sp]);
   float L = 0.0f, acc = 0.0f;
-  if (M != -INFINITY) {
-    for (int sp = g; sp < splits; sp += RG) {
-      const float w = exp2f(ml[2 * sp] - M);
-      L += ml[2 * sp + 1] * w;
-      acc += acc_row[(uint64_t)sp * D + c0 + c] * w;
+  constexpr int NPT = 4;  // splits per thread loaded at once
+  if (splits <= NPT * RG) {
+    // every load of the thread in one round trip (clamped indices; a split
+    // past the end weighs 0, which adds nothing to the sums)
+    float mv[NPT], lv[NPT], av[NPT];
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      const int sp = min(g + RG * k, splits - 1);
+      mv[k] = ml[2 * sp];
+      lv[k] = ml[2 * sp + 1];
+      av[k] = acc_row[(uint64_t)sp * D + c0 + c];
+    }
+#pragma unroll
+    for (int k = 0; k < NPT; ++k)
+      if (g + RG * k < splits) M = fmaxf(M, mv[k]);
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < NPT; ++k) {
+        if (g + RG * k < splits) {
+          const float w = exp2f(mv[k] - M);
+          L += lv[k] * w;
+          acc += av[k] * w;
+        }
+      }
+    }
+  } else {
+    for (int sp = g; sp < splits; sp += RG) M = fmaxf(M, ml[2 * sp]);
+    if (M != -INFINITY) {
+      for (int sp = g; sp < splits; sp += RG) {
+        const float w = exp2f(ml[2 * sp] - M);
+        L += ml[2 * sp + 1] * w;
+        acc += acc_row[(uint64_t)sp * D + c0 + c] * w;
+      }
     }
   }
   gacc[g][c] = acc;

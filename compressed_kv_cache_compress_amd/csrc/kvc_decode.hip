@@ -423,6 +423,18 @@ constexpr bool geo_fields_fit() {
 }
 static_assert(geo_fields_fit(), "chunk geometry fields");
 
+// Chunk geometry of a descriptor (words 2 and 3), computed once per 64
+// descriptors so that the chunk loop reads it with readlane instead of a
+// memory lookup; a paged descriptor (flags bit2) also carries
+// log2(seg_tokens) + 1, the token count its parts are laid out for.
+__device__ __forceinline__ uint32_t desc_geometry(uint32_t d2, uint32_t d3) {
+  const int c = (int)(d2 >> 16) & ~7;
+  const int cc = c < 8 ? 8 : (c > D ? D : c);
+  const uint32_t cap = d3 >> 16;
+  const uint32_t page = ((d3 >> 8) & KVC_DESC_PAGED) && cap ? 32u - __clz(cap) : 0u;
+  return (uint32_t)chunk_tokens(cc) | (row_magic(cc >> 3) << 5) | (page << 26);
+}
+
 __device__ __forceinline__ void fetch_descs(Cursor& cu, int lane) {
   cu.base = cu.di;
   const int i = min(cu.di + lane, cu.d1 - 1);
@@ -430,15 +442,7 @@ __device__ __forceinline__ void fetch_descs(Cursor& cu, int lane) {
   cu.w0 = d[0];
   cu.w1 = d[1];
   cu.w2 = d[2];
-  // per-descriptor chunk geometry, computed once per 64 descriptors so that
-  // the chunk loop reads it with readlane instead of a memory lookup; a
-  // paged descriptor (flags bit2) also carries log2(seg_tokens) + 1, the
-  // token count its parts are laid out for
-  const int c = (int)(d[2] >> 16) & ~7;
-  const int cc = c < 8 ? 8 : (c > D ? D : c);
-  const uint32_t cap = d[3] >> 16;
-  const uint32_t page = ((d[3] >> 8) & KVC_DESC_PAGED) && cap ? 32u - __clz(cap) : 0u;
-  cu.w3 = (uint32_t)chunk_tokens(cc) | (row_magic(cc >> 3) << 5) | (page << 26);
+  cu.w3 = desc_geometry(d[2], d[3]);
 }
 
 // Chunks of descriptor i of a stream's list (0 past nd): ceil(T / ct) with
@@ -446,15 +450,13 @@ __device__ __forceinline__ void fetch_descs(Cursor& cu, int lane) {
 // from the next integer, so adding 31/32 to the product with the approximate
 // reciprocal and truncating gives the exact ceiling.  (The count only
 // balances the splits; any count gives the same results.)
-__device__ __forceinline__ uint32_t desc_chunks(const kvc_seg_desc* dl, int i, int nd,
-                                                uint32_t& ct) {
-  // the load is unconditional (a clamped index), so that a wave's loads for
-  // several descriptors go out together
-  const uint32_t tc = reinterpret_cast<const uint32_t*>(dl + min(i, nd - 1))[2];
+// Chunks of a descriptor from its word 2 (n_tok | n_ch << 16), and its
+// tokens per chunk.
+__device__ __forceinline__ uint32_t desc_chunks(uint32_t tc, uint32_t& ct) {
   const uint32_t T = tc & 0xFFFFu;
   const int c = (int)(tc >> 16) & ~7;
   ct = (uint32_t)chunk_tokens(c < 8 ? 8 : (c > D ? D : c));
-  return i < nd ? (uint32_t)((float)T * __builtin_amdgcn_rcpf((float)ct) + 0.96875f) : 0u;
+  return (uint32_t)((float)T * __builtin_amdgcn_rcpf((float)ct) + 0.96875f);
 }
 
 // Chunk range of split sp of a stream with nd descriptors: with W the
@@ -463,20 +465,18 @@ __device__ __forceinline__ uint32_t desc_chunks(const kvc_seg_desc* dl, int i, i
 // number of chunks to within one, starting and ending inside a segment
 // where the share falls there.  A segment is 2 to 22 chunks here; whole
 // segments per split left the busiest of 24 waves 20 % (1024 segments of 2
-// and 4 chunks) to 25 % (128 such segments) above the mean.  Lane l takes
-// descriptors PER l .. PER l + PER - 1 (their loads issued together), one
+// and 4 chunks) to 25 % (128 such segments) above the mean.  Lane l holds
+// word 2 of descriptors per l .. per l + per - 1 (tc[k]; per <= PER), one
 // wave scan gives each lane the chunks before its first, and the lanes that
-// hold the first and the last chunk of the share are found by ballot.  Lists
-// of more than 1024 descriptors take equal descriptor counts.
+// hold the first and the last chunk of the share are found by ballot.
 template <int PER>
-__device__ __forceinline__ void chunk_balanced_range(int nd, int splits, int sp, int lane,
-                                                     Cursor& cu) {
-  const int per = (nd + 63) >> 6;  // descriptors per lane, <= PER
+__device__ __forceinline__ void balanced_core(const uint32_t (&tc)[PER], int per, int nd,
+                                              int splits, int sp, int lane, Cursor& cu) {
   uint32_t w[PER], ct[PER], tot = 0;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const uint32_t x = desc_chunks(cu.dl, lane * per + k, nd, ct[k]);
-    w[k] = k < per ? x : 0u;
+    const uint32_t x = desc_chunks(tc[k], ct[k]);
+    w[k] = k < per && lane * per + k < nd ? x : 0u;
     tot += w[k];
   }
   const uint32_t inc = wave_incl_scan_u32(tot);
@@ -516,17 +516,63 @@ __device__ __forceinline__ void chunk_balanced_range(int nd, int splits, int sp,
   cu.d1 = cu.dlast + 1;
 }
 
-// Descriptor range of split sp: chunk shares above for lists of up to 1024
-// descriptors, else an equal share of the descriptors.
-__device__ __forceinline__ void split_range(int nd, int splits, int sp, int lane, Cursor& cu) {
+// Descriptor range of split sp, with the cursor's first 64 descriptors in
+// place when it returns true.  Lists of at most 256 descriptors (by capacity
+// maxd): every lane loads its up to four whole descriptors in the round trip
+// that also brings the query and the list length (the layout follows maxd,
+// not nd, so the loads wait for nothing), the chunk share is taken from
+// their word 2, and lane j then takes descriptor di + j from the lane that
+// holds it by cross-lane permutes -- one memory round trip where counting,
+// then fetching took two more.  Up to 1024 descriptors: word 2 of each is
+// loaded for the share and the cursor fetches its descriptors after.
+// Longer lists take an equal share of the descriptors.
+__device__ __forceinline__ bool split_range(int nd, int maxd, int splits, int sp, int lane,
+                                            Cursor& cu) {
   cu.dfirst = cu.dlast = -1;
   cu.di = (int)(((int64_t)sp * nd) / splits);
   cu.d1 = (int)(((int64_t)(sp + 1) * nd) / splits);
-  if (nd <= 0 || nd > 1024) return;
-  if (nd <= 256)
-    chunk_balanced_range<4>(nd, splits, sp, lane, cu);
-  else
-    chunk_balanced_range<16>(nd, splits, sp, lane, cu);
+  if (maxd <= 256) {
+    constexpr int PER = 4;
+    const int per = (maxd + 63) >> 6;
+    u32x4_t dd[PER];
+    uint32_t tc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      // unconditional loads of clamped indices go out together
+      dd[k] = *reinterpret_cast<const u32x4_t*>(cu.dl + min(lane * per + k, maxd - 1));
+      tc[k] = dd[k][2];
+    }
+    if (nd <= 0) return false;
+    balanced_core<PER>(tc, per, nd, splits, sp, lane, cu);
+    if (cu.di >= cu.d1) return false;
+    // lane j takes descriptor i = di + j (clamped to the range), held by lane
+    // i / per in slot i % per
+    const int i = min(cu.di + lane, cu.d1 - 1);
+    const int src = i / per, slot = i - src * per;
+    uint32_t g[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t x = (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)dd[k][q]);
+        g[q] = slot == k ? x : g[q];
+      }
+    cu.base = cu.di;
+    cu.w0 = g[0];
+    cu.w1 = g[1];
+    cu.w2 = g[2];
+    cu.w3 = desc_geometry(g[2], g[3]);
+    return true;
+  }
+  if (nd <= 0 || nd > 1024) return false;
+  constexpr int PER = 16;
+  const int per = (nd + 63) >> 6;
+  uint32_t tc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    tc[k] = reinterpret_cast<const uint32_t*>(cu.dl + min(lane * per + k, nd - 1))[2];
+  balanced_core<PER>(tc, per, nd, splits, sp, lane, cu);
+  return false;
 }
 
 __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
@@ -680,6 +726,7 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   Cursor cu;
   cu.dl = a.desc + (uint64_t)s * a.maxd;
   cu.packed = a.packed;
+  bool placed = false;
   if (QLO && a.span_desc) {
     // an equal share of the span's descriptors
     const int s0 = span * a.span_desc;
@@ -689,12 +736,12 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
     cu.d1 = s0 + (int)(((int64_t)(sub + 1) * n) / a.spl);
     cu.dfirst = cu.dlast = -1;
   } else {
-    split_range(nd, a.splits, sp, lane, cu);
+    placed = split_range(nd, a.maxd, a.splits, sp, lane, cu);
   }
   cu.T = 0;
   cu.c = 0;
   cu.t0 = 0;
-  if (cu.di < cu.d1) fetch_descs(cu, lane);
+  if (cu.di < cu.d1 && !placed) fetch_descs(cu, lane);
 
   const uint8_t* sk8 = reinterpret_cast<const uint8_t*>(L.k);
 

@@ -155,3 +155,22 @@ def test_decode_wide_rows_and_chunk_tails():
     for splits in (0, 3):
         worst, _, _ = _run(w, S, strategies, 4 * S * 128, splits=splits, forced=forced)
         say(f"  splits={splits} worst rel err {worst:.2e}")
+
+
+def test_decode_long_ragged_lists():
+    """Lists of up to 512 descriptors (capacity 512: the path that loads each
+    descriptor's token and channel counts for the chunk shares, then fetches
+    the descriptors) with per-stream lengths 0, 1, 257, 300, 384, 450, 511
+    and 512, at the library's split count and at 7 and 24 splits; a split's
+    share may start and end inside a segment."""
+    c = dict(gen.CONFIGS["llama8b"])
+    c.update(B=1, N=8192)
+    w = gen.make_workload(c)
+    S = 16
+    n_desc = [512, 300, 257, 511, 0, 384, 1, 450]
+    for splits in (0, 7, 24):
+        worst, _, lse = _run(w, S, gen.table9(S), gen.budget_bytes(33, S), splits=splits,
+                             n_desc=n_desc)
+        G = w["G"]
+        assert np.all(np.isneginf(lse.cpu().numpy().reshape(-1)[4 * G:5 * G]))
+        say(f"  splits={splits} worst rel err {worst:.2e}")

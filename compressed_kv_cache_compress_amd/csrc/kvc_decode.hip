@@ -728,13 +728,14 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   cu.packed = a.packed;
   bool placed = false;
   if (QLO && a.span_desc) {
-    // an equal share of the span's descriptors
+    // a share of the span's chunks: the span's descriptors are a list of
+    // their own (the cursor's base moves to its first)
     const int s0 = span * a.span_desc;
     const int n = max(0, min(nd, s0 + a.span_desc) - s0);
+    const int cap = min(a.span_desc, a.maxd - s0);
     const int sub = sp - span * a.spl;
-    cu.di = s0 + (int)(((int64_t)sub * n) / a.spl);
-    cu.d1 = s0 + (int)(((int64_t)(sub + 1) * n) / a.spl);
-    cu.dfirst = cu.dlast = -1;
+    cu.dl += s0;
+    placed = split_range(n, cap, a.spl, sub, lane, cu);
   } else {
     placed = split_range(nd, a.maxd, a.splits, sp, lane, cu);
   }

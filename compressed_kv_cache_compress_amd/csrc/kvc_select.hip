@@ -79,54 +79,73 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int SCORE_ITERS = 4;  // descriptor groups of 4 per wave in k_select_scores
+static_assert(sizeof(kvc_seg_desc) == 16, "descriptors move as one 16-byte word");
 
+constexpr int SCORE_ITERS = 4;  // descriptor groups of 4 per wave and pass
 
-// grid (ceil(maxd / (16 * SCORE_ITERS)), streams), 256 threads.  A 16-lane
-// row per descriptor (4 per wave), lane i of the row holding channels
-// 8i .. 8i+7.  score = max over the group's q heads of the pairwise-tree sum
-// over channels of max(q kmax, q kmin) + 0 (8 channels in the lane, then the
-// row), -inf for an empty descriptor or one past n_desc.
-__global__ __launch_bounds__(256) void k_select_scores(SelectPlan p) {
-  const int s = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int row = lane >> 4, cb = lane & 15;
+// Scores of NI descriptors dd[i] of stream s, one per 16-lane row (lane cb of
+// the row holding channels 8cb .. 8cb+7): max over the group's q heads of
+// the pairwise-tree sum over channels of max(q kmax, q kmin) + 0 (8 channels
+// in the lane, then the row), -inf for an empty descriptor or one past nd.
+// Every load comes first (clamped indices): a store between them, which the
+// compiler must assume could alias, would make each wait for it.
+template <int NI>
+__device__ __forceinline__ void score_rows(const SelectPlan& p, int s, int cb, int nd,
+                                           const int (&dd)[NI], float (&out)[NI]) {
   const int b = s / p.hkv, h = s - b * p.hkv;
   const int G = p.G;
-  const int nd = p.n_desc ? min((int)p.n_desc[s], p.maxd) : p.maxd;
   const uint16_t* qg = p.q + (uint64_t)(b * p.hq + h * G) * D + 8 * cb;
-  for (int it = 0; it < SCORE_ITERS; ++it) {
-    const int d = ((blockIdx.x * SCORE_ITERS + it) * 4 + wv) * 4 + row;
-    const bool live = d < nd && p.desc[(uint64_t)s * p.maxd + min(d, p.maxd - 1)].n_tok > 0;
-    float mx[8], mn[8];
-    {
-      const uint16_t* sm = p.summary + ((uint64_t)s * p.maxd + min(d, p.maxd - 1)) * 2 * D + 8 * cb;
-      const uint4 a = *reinterpret_cast<const uint4*>(sm);
-      const uint4 c = *reinterpret_cast<const uint4*>(sm + D);
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, cw[4] = {c.x, c.y, c.z, c.w};
+  uint32_t ntok[NI];
+  uint4 sa[NI], sc[NI];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        mx[2 * k] = bf2f(aw[k] & 0xFFFFu);
-        mx[2 * k + 1] = bf2f(aw[k] >> 16);
-        mn[2 * k] = bf2f(cw[k] & 0xFFFFu);
-        mn[2 * k + 1] = bf2f(cw[k] >> 16);
-      }
-    }
-    float best = -INFINITY;
-    for (int g = 0; g < G; ++g) {
-      const uint4 qv = *reinterpret_cast<const uint4*>(qg + (uint64_t)g * D);
-      const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+  for (int it = 0; it < NI; ++it) {
+    const int di = min(dd[it], p.maxd - 1);
+    ntok[it] = p.desc[(uint64_t)s * p.maxd + di].n_tok;
+    const uint16_t* sm = p.summary + ((uint64_t)s * p.maxd + di) * 2 * D + 8 * cb;
+    sa[it] = *reinterpret_cast<const uint4*>(sm);
+    sc[it] = *reinterpret_cast<const uint4*>(sm + D);
+  }
+  float best[NI];
+#pragma unroll
+  for (int it = 0; it < NI; ++it) best[it] = -INFINITY;
+  for (int g = 0; g < G; ++g) {
+    const uint4 qv = *reinterpret_cast<const uint4*>(qg + (uint64_t)g * D);
+    const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const uint32_t aw[4] = {sa[it].x, sa[it].y, sa[it].z, sa[it].w};
+      const uint32_t cw[4] = {sc[it].x, sc[it].y, sc[it].z, sc[it].w};
       float t[8];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float q0 = bf2f(qw[k] & 0xFFFFu), q1 = bf2f(qw[k] >> 16);
-        t[2 * k] = fmaxf(q0 * mx[2 * k], q0 * mn[2 * k]) + 0.0f;
-        t[2 * k + 1] = fmaxf(q1 * mx[2 * k + 1], q1 * mn[2 * k + 1]) + 0.0f;
+        t[2 * k] = fmaxf(q0 * bf2f(aw[k] & 0xFFFFu), q0 * bf2f(cw[k] & 0xFFFFu)) + 0.0f;
+        t[2 * k + 1] = fmaxf(q1 * bf2f(aw[k] >> 16), q1 * bf2f(cw[k] >> 16)) + 0.0f;
       }
       const float v = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
-      best = fmaxf(best, row16_sum(v));
+      best[it] = fmaxf(best[it], row16_sum(v));
     }
-    if (cb == 0 && d < p.maxd) p.score[(uint64_t)s * p.maxd + d] = live ? best : -INFINITY;
   }
+#pragma unroll
+  for (int it = 0; it < NI; ++it)
+    out[it] = (dd[it] < nd && ntok[it] > 0) ? best[it] : -INFINITY;
+}
+
+// grid (ceil(maxd / (16 * SCORE_ITERS)), streams), 256 threads: four rows
+// per wave, SCORE_ITERS descriptors per row.
+__global__ __launch_bounds__(256) void k_select_scores(SelectPlan p) {
+  const int s = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row = lane >> 4, cb = lane & 15;
+  const int nd = p.n_desc ? min((int)p.n_desc[s], p.maxd) : p.maxd;
+  int dd[SCORE_ITERS];
+#pragma unroll
+  for (int it = 0; it < SCORE_ITERS; ++it)
+    dd[it] = ((blockIdx.x * SCORE_ITERS + it) * 4 + wv) * 4 + row;
+  float sc[SCORE_ITERS];
+  score_rows<SCORE_ITERS>(p, s, cb, nd, dd, sc);
+#pragma unroll
+  for (int it = 0; it < SCORE_ITERS; ++it)
+    if (cb == 0 && dd[it] < p.maxd) p.score[(uint64_t)s * p.maxd + dd[it]] = sc[it];
 }
 
 // Sum of a small non-negative integer over the 64 lanes of a full wave
@@ -135,16 +154,25 @@ __device__ __forceinline__ uint32_t wave_count(uint32_t v) {
   return (uint32_t)tree_sum64((float)v);
 }
 
-// grid (streams), one wave: the keep best live descriptors by (score desc,
+// One wave: the keep best live descriptors of stream s by (score desc,
 // index asc), written in index order.  KPL keys per lane in registers
-// (descriptor d = 64 i + lane in slot i; maxd <= 64 KPL); counts are lane
-// counts summed once per step, ranks are ballots and mbcnt, so there is no
-// barrier.
+// (descriptor d = 64 i + lane in slot i; maxd <= 64 KPL); counts are ballots
+// counted on the scalar unit, ranks are ballots and mbcnt, so there is no
+// barrier.  `score` is the stream's row (global memory or LDS).
 template <int KPL>
-__global__ __launch_bounds__(64) void k_select_topk(SelectPlan p) {
-  const int s = blockIdx.x, lane = threadIdx.x;
+__device__ __forceinline__ void topk_wave(const SelectPlan& p, int s, int lane,
+                                          const float* score) {
   const int maxd = p.maxd;
-  const float* score = p.score + (uint64_t)s * maxd;
+  const kvc_seg_desc* dl = p.desc + (uint64_t)s * maxd;
+  // short lists: every descriptor is loaded before any store (a store that
+  // might alias would make the loads after it wait), overlapping the search
+  constexpr bool PRELOAD = KPL <= 16;
+  uint4 dv[PRELOAD ? KPL : 1];
+  if constexpr (PRELOAD) {
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+      dv[i] = *reinterpret_cast<const uint4*>(dl + min(64 * i + lane, maxd - 1));
+  }
   uint32_t key[KPL];
   uint32_t live = 0u;
 #pragma unroll
@@ -160,10 +188,12 @@ __global__ __launch_bounds__(64) void k_select_topk(SelectPlan p) {
   if (kk > 0) {
     for (int bt = 31; bt >= 0; --bt) {
       const uint32_t cand = tau | (1u << bt);
+      // keys at or above cand over the wave: one ballot per slot, counted on
+      // the scalar unit (no cross-lane reduction in the chain)
       uint32_t c = 0u;
 #pragma unroll
-      for (int i = 0; i < KPL; ++i) c += key[i] >= cand ? 1u : 0u;
-      if (wave_count(c) >= kk) tau = cand;
+      for (int i = 0; i < KPL; ++i) c += (uint32_t)__popcll(__ballot(key[i] >= cand));
+      if (c >= kk) tau = cand;
     }
   }
   uint32_t c = 0u;
@@ -171,8 +201,7 @@ __global__ __launch_bounds__(64) void k_select_topk(SelectPlan p) {
   for (int i = 0; i < KPL; ++i) c += (kk > 0 && key[i] > tau) ? 1u : 0u;
   const uint32_t need = kk - wave_count(c);
   // compaction in index order: keys above tau, then the first `need` equal to tau
-  const kvc_seg_desc* dl = p.desc + (uint64_t)s * maxd;
-  kvc_seg_desc* od = p.out_desc + (uint64_t)s * p.keep;
+  uint4* od = reinterpret_cast<uint4*>(p.out_desc + (uint64_t)s * p.keep);
   uint32_t eq_before = 0u, out_before = 0u;
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
@@ -183,11 +212,24 @@ __global__ __launch_bounds__(64) void k_select_topk(SelectPlan p) {
       const bool on = k != 0u && (k > tau || (eq && eq_before + lanes_below(be) < need));
       eq_before += (uint32_t)__popcll(be);
       const uint64_t bo = __ballot(on);
-      if (on) od[out_before + lanes_below(bo)] = dl[64 * i + lane];
+      if (on) {
+        uint4 v;
+        if constexpr (PRELOAD)
+          v = dv[i];
+        else
+          v = *reinterpret_cast<const uint4*>(dl + 64 * i + lane);
+        od[out_before + lanes_below(bo)] = v;
+      }
       out_before += (uint32_t)__popcll(bo);
     }
   }
   if (lane == 0) p.out_n[s] = kk;
+}
+
+// grid (streams), one wave.
+template <int KPL>
+__global__ __launch_bounds__(64) void k_select_topk(SelectPlan p) {
+  topk_wave<KPL>(p, blockIdx.x, threadIdx.x, p.score + (uint64_t)blockIdx.x * p.maxd);
 }
 
 hipError_t launch_summarize(const SummaryPlan& p, hipStream_t st) {

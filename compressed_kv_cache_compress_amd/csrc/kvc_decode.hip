@@ -1048,6 +1048,27 @@ __global__ __launch_bounds__(128) void k_decode_span_rot(const float* __restrict
   float4 rvr[NRV];
 #pragma unroll
   for (int u = 0; u < NRV; ++u) rvr[u] = RV4[t + D * u];
+  // groups of up to 4 heads over at most 8 splits per span (the per-span
+  // case): the span's own partial rows go out with them too, so that one
+  // round trip brings every operand (their weights wait for the maxima)
+  constexpr int PSP = 8;
+  const int sp_lo = span * spl;
+  const bool pre = NG == 4 && spl <= PSP;  // block-uniform
+  float pm[NG == 4 ? 4 : 1][PSP], pa[NG == 4 ? 4 : 1][PSP];
+  if constexpr (NG == 4) {
+    if (pre) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int gr = row0 + min(g, G - 1);
+#pragma unroll
+        for (int u = 0; u < PSP; ++u) {
+          const int sp = sp_lo + min(u, spl - 1);
+          pm[g][u] = part_ml[((uint64_t)gr * splits + sp) * 2];
+          pa[g][u] = part_acc[((uint64_t)gr * splits + sp) * D + t];
+        }
+      }
+    }
+  }
   // M_g of every head: 32 threads per head, four heads per pass
   for (int g0 = 0; g0 < G; g0 += 4) {
     const int g = g0 + (t >> 5);
@@ -1074,7 +1095,24 @@ __global__ __launch_bounds__(128) void k_decode_span_rot(const float* __restrict
     *reinterpret_cast<float4*>(rv + (i >> 5) * RV_STRIDE + 4 * (i & 31)) = rvr[u];
   }
   __syncthreads();
-  for (int g = 0; g < G; ++g) {
+  if constexpr (NG == 4) {
+    if (pre) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (g < G) {
+          const float M = red[g];
+          float a = 0.0f;
+          if (M != -INFINITY) {
+#pragma unroll
+            for (int u = 0; u < PSP; ++u)
+              if (u < spl && pm[g][u] != -INFINITY) a += pa[g][u] * exp2f(pm[g][u] - M);
+          }
+          o1[g * D + t] = a;
+        }
+      }
+    }
+  }
+  for (int g = 0; g < (pre ? 0 : G); ++g) {
     const float M = red[g];
     const float* ml = part_ml + (uint64_t)(row0 + g) * splits * 2;
     const float* acc = part_acc + (uint64_t)(row0 + g) * splits * D;

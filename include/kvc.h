@@ -272,11 +272,15 @@ kvc_status kv_compress_rotated(const kvc_params* p, const uint16_t* K, const uin
 /* Decode attention of one query per q head over every stream's compressed
  * segments (MosaicKV Fig. 6 caption, PackedAttention): softmax over all kept
  * tokens of the stream's descriptors; a dropped channel contributes 0 to
- * q.k and to the output; fp32 accumulation.  Split-K over descriptors, then a
+ * q.k and to the output; fp32 accumulation.  Split-K over each stream's
+ * chunks of kept tokens (the splits of a stream take equal shares of its
+ * chunks to within one, a share may start and end inside a segment; lists
+ * of more than 1024 descriptors are split by descriptor count), then a
  * log-sum-exp merge.
  *  q                 device [batch][n_q_heads][128] bf16.
  *  packed            device base that descriptor offsets index.
- *  desc              device [streams][max_desc_per_stream].
+ *  desc              device [streams][max_desc_per_stream]; entries past a
+ *                    stream's n_desc may be read but are never used.
  *  n_desc_per_stream device [streams] u32 or NULL (= max_desc_per_stream each).
  *  out               device [batch][n_q_heads][128] bf16 (RNE), overwritten;
  *                    zero for a stream with no kept token.

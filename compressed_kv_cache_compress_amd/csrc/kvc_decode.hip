@@ -883,12 +883,24 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
     float alpha[JG];
     if (k_side(cur, 0, alpha)) rescale(alpha);
     int vb = 0;
-    // iteration: stage chunk i+1, load chunk i+2, K side of i+1, V side of i
+    // iteration: stage chunk i+1, load chunk i+2, K side of i+1, V side of i.
+    // Wave priorities order the work of the waves sharing a SIMD by how soon
+    // other work waits for it: the commit first (its loads have landed, and
+    // staging them frees the prefetch registers for the next loads), then the
+    // walk and those loads, then the K side (its probabilities feed the next
+    // V side), and the V side last, which only adds into this wave's
+    // accumulators and may trail.  The arbiter then keeps the chunk chain of
+    // each wave moving and fills the gaps with V work.
+    constexpr int PRIO_COMMIT = 3, PRIO_LOAD = 2, PRIO_K = 1, PRIO_V = 0;
     while (nxt.valid) {
+      __builtin_amdgcn_s_setprio(PRIO_COMMIT);
       commit(nxt, lane, rg, L.k, L.vs[vb ^ 1].v);
+      __builtin_amdgcn_s_setprio(PRIO_LOAD);
       const Chunk far = next_chunk(cu, lane);
       prefetch(far, lane, rg);
+      __builtin_amdgcn_s_setprio(PRIO_K);
       const bool resc = k_side(nxt, vb ^ 1, alpha);
+      __builtin_amdgcn_s_setprio(PRIO_V);
       v_side(cur, vb);
       if (resc) rescale(alpha);
       cur = nxt;

@@ -86,14 +86,21 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_decode_bytes(desc, B, Hq, splits):
+def decode_partials(splits, rotated=False):
+    """Partial rows per (b, q head) a decode writes and its merge reads: the
+    four waves of a workgroup, consecutive splits of one stream, merge their
+    states first when the split count is a multiple of 4 (unrotated decode)."""
+    return splits if rotated or splits % 4 else splits // 4
+
+
+def algorithmic_decode_bytes(desc, B, Hq, splits, rotated=False):
     n = desc["n_tok"].astype(np.int64)
     c = desc["n_ch"].astype(np.int64)
     masks = np.where(c < 128, 2 * 16 * n, 0)
     vals = 2 * 2 * n * c
     seg = (16 + masks + vals).sum()  # descriptor + masks + values (index lists unread)
     q = out = B * Hq * 128 * 2
-    partials = 2 * B * Hq * splits * (2 + 128) * 4
+    partials = 2 * B * Hq * decode_partials(splits, rotated) * (2 + 128) * 4
     return int(seg + q + out + partials)
 
 
@@ -163,7 +170,7 @@ def bench_kara(a, kvc, stream):
     n = dh["n_tok"].astype(np.int64)
     c = dh["n_ch"].astype(np.int64)
     alg = int((16 + np.where(c < 128, 32 * n, 0) + 4 * n * c).sum()) + 2 * B * Hq * 256 + \
-        2 * B * Hq * L.decode_splits * 520
+        2 * B * Hq * decode_partials(L.decode_splits) * 520
     L_ctx = w["prompt"] + w["gen"]
     return {"workload": "kara: B 64, GQA 32/8, prompt 16384 + 8192 generated, window 512, "
                         "retention 20 %, Token2Chunk alpha 3 gamma 16, an event every 64 steps",
@@ -303,7 +310,7 @@ def _rotated_run(kvc, K, V, Qw, q, B, Hq, Hkv, N, S, W, strategies, budget, scal
     oh = obj.cpu().numpy()
     chosen = np.take_along_axis(oh, dh["strategy"].astype(np.int64)[..., None], axis=2)[..., 0]
     t_dec = float(np.mean([e[0].elapsed_time(e[1]) for e in dv])) * 1e-3
-    alg = algorithmic_decode_bytes(dh.ravel(), B, Hq, L.decode_splits)
+    alg = algorithmic_decode_bytes(dh.ravel(), B, Hq, L.decode_splits, rotated=True)
     packed_bytes = int(used.sum().item())
     rot_bytes = streams * n_span * 2 * 128 * 128 * 4
     return {"rot_span": rot_span or N, "spans_per_stream": n_span,

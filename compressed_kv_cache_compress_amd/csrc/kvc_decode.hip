@@ -119,6 +119,10 @@ struct DecodeArgs {
   // rotation spans (QLO only): descriptor i is in span i / span_desc, split
   // sp covers span sp / spl, and the queries are [row][n_span][128]
   int n_span, span_desc, spl;
+  // the four waves of a workgroup hold consecutive splits of one stream
+  // (splits a multiple of 4, no rotation): they merge their states and the
+  // workgroup writes one partial, split index sp / 4 of splits / 4
+  int wg_merge;
   float sl2;  // scale * log2(e)
 };
 
@@ -913,6 +917,61 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   // partial state of this split
 #pragma unroll
   for (int j = 0; j < JG; ++j) l_run[j] = row16_sum(l_run[j]);
+  if (!QLO && a.wg_merge) {
+    // Each wave writes its state into its own (now idle) staging, the
+    // workgroup waits for all four, then wave wv merges the heads hd with
+    // hd % 4 == wv over the four waves in order (log-sum-exp, base 2) and
+    // writes them as one partial.  No wave of such a launch returned early:
+    // its wave count is a multiple of 4.
+    constexpr int NH = 4 * JG;  // head slots per wave
+    float* mine = reinterpret_cast<float*>(&L);  // [NH][2] (m, l), then [NH][D] acc
+#pragma unroll
+    for (int j = 0; j < JG; ++j)
+      if (col == 0) {
+        mine[2 * (4 * j + grp)] = m_run[j];
+        mine[2 * (4 * j + grp) + 1] = l_run[j];
+      }
+#pragma unroll
+    for (int jg = 0; jg < JG; ++jg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mine[2 * NH + (4 * jg + i) * D + lane] = O4[0][jg][i];
+        mine[2 * NH + (4 * jg + i) * D + 64 + lane] = O4[1][jg][i];
+      }
+    static_assert((2 + D) * NH * 4 <= sizeof(WaveLds<JG>), "wave states fit the staging");
+    __syncthreads();
+    const int splits4 = a.splits >> 2, sp4 = sp >> 2;
+#pragma unroll
+    for (int jg = 0; jg < JG; ++jg) {
+      const int hd = 4 * jg + wv;
+      if (hd >= a.G) continue;
+      float mu[WAVES], M = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < WAVES; ++u) {
+        mu[u] = reinterpret_cast<const float*>(&wl[u])[2 * hd];
+        M = fmaxf(M, mu[u]);
+      }
+      float Ls = 0.0f, a0 = 0.0f, a1 = 0.0f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int u = 0; u < WAVES; ++u) {
+          const float* st = reinterpret_cast<const float*>(&wl[u]);
+          const float w = mu[u] == -INFINITY ? 0.0f : exp2f(mu[u] - M);
+          Ls += st[2 * hd + 1] * w;
+          a0 += st[2 * NH + hd * D + lane] * w;
+          a1 += st[2 * NH + hd * D + 64 + lane] * w;
+        }
+      }
+      const uint64_t pi = (uint64_t)(b * a.hq + h * a.G + hd) * splits4 + sp4;
+      if (lane == 0) {
+        a.part_ml[2 * pi] = M;
+        a.part_ml[2 * pi + 1] = Ls;
+      }
+      a.part_acc[pi * D + lane] = a0;
+      a.part_acc[pi * D + 64 + lane] = a1;
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < JG; ++j) {
     const int hd = 4 * j + grp;
@@ -952,7 +1011,7 @@ __device__ __forceinline__ bool merge_splits(const float* __restrict__ ml,
   const int c = threadIdx.x % RC, g = threadIdx.x / RC;
   float M = -INFINITY;
   float L = 0.0f, acc = 0.0f;
-  constexpr int NPT = 4;  // splits per thread loaded at once
+  constexpr int NPT = RG == 1 ? 8 : 4;  // splits per thread loaded at once
   if (splits <= NPT * RG) {
     // every load of the thread in one round trip (clamped indices; a split
     // past the end weighs 0, which adds nothing to the sums)
@@ -1306,6 +1365,7 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
   a.span_desc = p.span_desc;
   a.spl = p.spl;
   a.sl2 = p.scale * KVC_LOG2E;
+  a.wg_merge = (!p.rot && p.splits % WAVES == 0) ? 1 : 0;
   const dim3 grid((a.items + WAVES - 1) / WAVES);
   if (p.rot) {
     const dim3 gq(p.streams, p.n_span);
@@ -1341,15 +1401,16 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
     hipLaunchKernelGGL((k_decode_split<2, false>), grid, dim3(64 * WAVES), 0, st, a);
   else
     hipLaunchKernelGGL((k_decode_split<4, false>), grid, dim3(64 * WAVES), 0, st, a);
-  if (p.splits > 32)
+  const int parts = a.wg_merge ? p.splits / WAVES : p.splits;  // partials per row
+  if (parts > 32)
     hipLaunchKernelGGL((k_decode_reduce<32, 32>), dim3(p.batch * p.hq, D / 32), dim3(1024), 0, st,
-                       p.part_ml, p.part_acc, p.out, p.lse, p.splits);
-  else if (p.splits > 8)
+                       p.part_ml, p.part_acc, p.out, p.lse, parts);
+  else if (parts > 8)
     hipLaunchKernelGGL((k_decode_reduce<8, 128>), dim3(p.batch * p.hq, 1), dim3(1024), 0, st,
-                       p.part_ml, p.part_acc, p.out, p.lse, p.splits);
+                       p.part_ml, p.part_acc, p.out, p.lse, parts);
   else
     hipLaunchKernelGGL((k_decode_reduce<1, 128>), dim3(p.batch * p.hq, 1), dim3(128), 0, st,
-                       p.part_ml, p.part_acc, p.out, p.lse, p.splits);
+                       p.part_ml, p.part_acc, p.out, p.lse, parts);
   return hipGetLastError();
 }
 

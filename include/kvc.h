@@ -276,7 +276,8 @@ kvc_status kv_compress_rotated(const kvc_params* p, const uint16_t* K, const uin
  * chunks of kept tokens (the splits of a stream take equal shares of its
  * chunks to within one, a share may start and end inside a segment; lists
  * of more than 1024 descriptors are split by descriptor count), then a
- * log-sum-exp merge.
+ * log-sum-exp merge (when the split count is a multiple of 4, the four
+ * splits of a workgroup are merged first, in the split kernel).
  *  q                 device [batch][n_q_heads][128] bf16.
  *  packed            device base that descriptor offsets index.
  *  desc              device [streams][max_desc_per_stream]; entries past a

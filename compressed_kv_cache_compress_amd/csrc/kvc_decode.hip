@@ -103,6 +103,7 @@ constexpr int KSTAGE = (kstage_bytes() + 15) / 16 * 16;
 constexpr int VSTAGE = (vstage_bytes() + 15) / 16 * 16;
 constexpr float RESCALE_SLACK = 8.0f;             // log2 units the running max may lag
 constexpr int WAVES = 4;
+constexpr int XCDS = 8;  // accelerator complex dies of the chip, one L2 each
 #ifndef KVC_DECODE_MIN_BLOCKS
 #define KVC_DECODE_MIN_BLOCKS 2  // workgroups per CU the register budget is sized for
 #endif
@@ -674,7 +675,16 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   const int lane = tid & 63, wv = tid >> 6;
   // wave-uniform (the compiler cannot tell that tid >> 6 is), so the
   // descriptor walk and the chunk addresses live in scalar registers
-  const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * WAVES + wv);
+  // Workgroups are handed to the 8 XCDs in turn (workgroup b to XCD b mod
+  // 8), and each XCD has an L2 of its own.  Renumbered so that consecutive
+  // work items, the splits of one stream, run on one XCD: the stream's
+  // query and descriptor list, read by every one of its splits, then come
+  // from HBM once per stream rather than once per XCD.  A permutation of the
+  // workgroups whenever their count is a multiple of 8 (else the identity).
+  const int nb = (int)gridDim.x;
+  const int bx = (nb % XCDS == 0) ? (int)(blockIdx.x % XCDS) * (nb / XCDS) + (int)(blockIdx.x / XCDS)
+                                   : (int)blockIdx.x;
+  const int item = __builtin_amdgcn_readfirstlane(bx * WAVES + wv);
   if (item >= a.items) return;
   const int s = item / a.splits, sp = item - s * a.splits;
   const int grp = lane >> 4, col = lane & 15;

@@ -673,8 +673,6 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   __syncthreads();
 
   const int lane = tid & 63, wv = tid >> 6;
-  // wave-uniform (the compiler cannot tell that tid >> 6 is), so the
-  // descriptor walk and the chunk addresses live in scalar registers
   // Workgroups are handed to the 8 XCDs in turn (workgroup b to XCD b mod
   // 8), and each XCD has an L2 of its own.  Renumbered so that consecutive
   // work items, the splits of one stream, run on one XCD: the stream's
@@ -684,6 +682,8 @@ __global__ __launch_bounds__(256, JG == 1 ? KVC_DECODE_MIN_BLOCKS : 2) void k_de
   const int nb = (int)gridDim.x;
   const int bx = (nb % XCDS == 0) ? (int)(blockIdx.x % XCDS) * (nb / XCDS) + (int)(blockIdx.x / XCDS)
                                    : (int)blockIdx.x;
+  // wave-uniform (the compiler cannot tell that tid >> 6 is), so the
+  // descriptor walk and the chunk addresses live in scalar registers
   const int item = __builtin_amdgcn_readfirstlane(bx * WAVES + wv);
   if (item >= a.items) return;
   const int s = item / a.splits, sp = item - s * a.splits;

@@ -88,6 +88,20 @@ def test_decode_group_sizes(G):
     _run(w, 64, gen.table9(64), gen.budget_bytes(33, 64))
 
 
+@pytest.mark.parametrize("G", [2, 3])
+def test_decode_workgroup_merge_and_numbering(G):
+    """Groups of 2 and 3 q heads (some waves of a workgroup merge no head)
+    at split counts that are multiples of 4 (the four splits of a workgroup
+    merged in the split kernel: 4, 12, 16) and that are not (6), with
+    workgroup counts that are multiples of 8 (renumbered across the XCDs: 16
+    splits x 2 streams = 8 workgroups) and that are not (4 and 12 splits)."""
+    c = dict(gen.CONFIGS["tiny"])
+    c.update(Hq=2 * G, Hkv=2, N=1024, S=64, W=4)
+    w = gen.make_workload(c)
+    for splits in (4, 6, 12, 16):
+        _run(w, 64, gen.table9(64), gen.budget_bytes(33, 64), splits=splits)
+
+
 def test_decode_ragged_descriptor_lists_and_empty_streams():
     """Per-stream descriptor counts differ (one stream has none), segments hold
     13 tokens (a ragged 16-token chunk) or all 256 (dense)."""
